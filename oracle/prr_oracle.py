@@ -1,0 +1,272 @@
+"""Plain, slow fp64 CPU oracle for one decode step of PRR's dynamic sparse attention.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke entry point and the benchmark's CPU-baseline leg may import this
+module. The HIP library never uses it, and it shares no code with the HIP library: it reads plain numpy arrays and
+computes every quantity from its definition in float64.
+
+Sources (the pages describing "Predict, Reuse, and Repair: Accelerating Dynamic Sparse Attention for Long-Context
+LLM Decoding", arXiv 2606.30389):
+  * PRR abstract: decoding attends only to the top-K KV blocks relevant to each query; an EMA-based predictor
+    forecasts the blocks; attention is speculated over them while selection runs; missed blocks are folded into the
+    partial attention state with online-softmax statistics once the true set is known.
+  * PRR summary page (arxivlens), Summary / Key findings / Contributions: the repair covers exactly the missed
+    blocks and the result keeps standard DSA accuracy (full top-K coverage); Limitations: the budget comes from
+    profiled latency grids plus polynomial regression off the grid.
+  * PRR reference list: Quest (query-aware block scores from per-block elementwise key min/max), FlashAttention-2
+    (online softmax), PagedAttention (paged KV cache with a block table).
+
+Readings where the pages are silent (each is listed in the design notes):
+  * score: Quest's per-head upper bound sum_d max(q_d * kmin_d, q_d * kmax_d), summed over the query heads of the
+    KV group (one selection per sequence and KV head);
+  * top-K ties go to the lower block index; index lists are reported in ascending order;
+  * the EMA averages block scores: e_0 = s_0, e_t = alpha * e_{t-1} + (1 - alpha) * s_t; step 0 has no prediction;
+    the prediction for step t is the top-K' of e_{t-1} with the same tie rule;
+  * softmax scale 1/sqrt(D);
+  * budget: K'* is the largest profiled K' whose speculation time does not exceed the selection time predicted for
+    the target block count (a least-squares polynomial in the block count when that count is off the grid).
+
+Layouts: K/V caches [n_pages, Hkv, page, D]; block table int32 [B, pages_per_seq]; logical token i of sequence b sits
+in physical page table[b, i // page] at row i % page.
+"""
+from __future__ import annotations
+
+import math
+from itertools import combinations
+
+import numpy as np
+
+# ------------------------------------------------------------------------------------------------------------------
+# paged KV cache (PagedAttention, in the PRR reference list)
+# ------------------------------------------------------------------------------------------------------------------
+
+
+def logical_tokens(cache: np.ndarray, table: np.ndarray, b: int, g: int, n_tokens: int) -> np.ndarray:
+    """Keys (or values) of sequence b, KV head g in logical token order, as float64 [n_tokens, D]."""
+    page = cache.shape[2]
+    i = np.arange(n_tokens)
+    return np.asarray(cache[table[b, i // page], g, i % page], dtype=np.float64)
+
+
+# ------------------------------------------------------------------------------------------------------------------
+# Quest block summaries and scores (Quest, in the PRR reference list)
+# ------------------------------------------------------------------------------------------------------------------
+
+
+def block_summaries(keys: np.ndarray, block_size: int):
+    """Elementwise min and max of the keys of each block: kmin, kmax [N, D] (exact: comparisons only)."""
+    n_tok, d = keys.shape
+    kb = keys.reshape(n_tok // block_size, block_size, d)
+    return kb.min(axis=1), kb.max(axis=1)
+
+
+def quest_scores(q_group: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> np.ndarray:
+    """s[n] = sum over the group's heads h and dims d of max(q_hd * kmin_nd, q_hd * kmax_nd)  (plain max form).
+
+    For one head this bounds max_i q . k_i over the block's tokens from above."""
+    s = np.zeros(kmin.shape[0], dtype=np.float64)
+    for h in range(q_group.shape[0]):
+        q = q_group[h].astype(np.float64)
+        s += np.maximum(kmin * q, kmax * q).sum(axis=1)
+    return s
+
+
+def quest_scores_signsplit(q_group: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> np.ndarray:
+    """Same value as quest_scores via max(q*a, q*b) = max(q,0)*b + min(q,0)*a for a <= b (faster; used for large
+    sampled checks; pinned against the plain form)."""
+    qp = np.maximum(q_group, 0.0).sum(axis=0)
+    qn = np.minimum(q_group, 0.0).sum(axis=0)
+    return kmax @ qp + kmin @ qn
+
+
+# ------------------------------------------------------------------------------------------------------------------
+# top-K block selection (PRR abstract: attend only to the top-K blocks)
+# ------------------------------------------------------------------------------------------------------------------
+
+
+def top_k(values: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest values, ties to the lower index; returned ascending (int64)."""
+    n = len(values)
+    order = np.lexsort((np.arange(n), -np.asarray(values, dtype=np.float64)))
+    return np.sort(order[:k])
+
+
+def boundary_gap(values: np.ndarray, k: int):
+    """(v_(k), v_(k+1), relative gap (v_(k) - v_(k+1)) / |v_(k)|) of the sorted values; gap = inf when k == n."""
+    v = np.sort(np.asarray(values, dtype=np.float64))[::-1]
+    if k >= len(v):
+        return float(v[k - 1]), -math.inf, math.inf
+    a, b = float(v[k - 1]), float(v[k])
+    return a, b, (a - b) / abs(a) if a != 0 else (math.inf if a > b else 0.0)
+
+
+# ------------------------------------------------------------------------------------------------------------------
+# attention over a block set: the definition of the output (standard DSA over the true top-K set)
+# ------------------------------------------------------------------------------------------------------------------
+
+
+def block_tokens(blocks, block_size: int) -> np.ndarray:
+    return np.concatenate([np.arange(n * block_size, (n + 1) * block_size) for n in blocks]) if len(blocks) else \
+        np.zeros((0,), dtype=np.int64)
+
+
+def attention_over_blocks(q_group, keys, values, blocks, block_size: int, scale: float) -> np.ndarray:
+    """o[h] = softmax(scale * q_h . k_i) weighted sum of v_i over the tokens of ``blocks``; two-pass softmax
+    (max first, then the sum), float64. Returns [G, D]."""
+    idx = block_tokens(blocks, block_size)
+    k = keys[idx]
+    v = values[idx]
+    out = np.empty((q_group.shape[0], keys.shape[1]), dtype=np.float64)
+    for h in range(q_group.shape[0]):
+        z = scale * (k @ q_group[h].astype(np.float64))
+        zmax = z.max()
+        w = np.exp(z - zmax)
+        out[h] = (w @ v) / w.sum()
+    return out
+
+
+# ------------------------------------------------------------------------------------------------------------------
+# online-softmax partial states and their merge (FlashAttention-2 in the reference list; PRR abstract: the repair
+# folds missed blocks into the partial attention state using online-softmax statistics)
+# ------------------------------------------------------------------------------------------------------------------
+
+
+def block_partial(q_h, k_blk, v_blk, scale: float):
+    """(m, l, O) of one head over one block: m = max z, l = sum exp(z - m), O = sum exp(z - m) v."""
+    z = scale * (k_blk @ np.asarray(q_h, dtype=np.float64))
+    m = z.max()
+    p = np.exp(z - m)
+    return float(m), float(p.sum()), p @ v_blk
+
+
+def merge(a, b):
+    """Online-softmax merge of two partial states over disjoint token sets."""
+    (m1, l1, o1), (m2, l2, o2) = a, b
+    m = max(m1, m2)
+    c1, c2 = math.exp(m1 - m), math.exp(m2 - m)
+    return m, l1 * c1 + l2 * c2, o1 * c1 + o2 * c2
+
+
+def finalize(state) -> np.ndarray:
+    m, l, o = state
+    return o / l
+
+
+def prr_output(q_group, keys, values, true_set, pred_set, block_size: int, scale: float):
+    """Reference speculate-reuse-repair pipeline for one (sequence, KV head).
+
+    Speculation leaves one partial per predicted block; repair computes partials for the missed blocks M = T \\ P;
+    the output merges, in ascending block order, the speculated partials of T n P and the repaired partials of M.
+    Predicted blocks outside T never enter. Returns (o [G, D], missed ascending, wasted ascending)."""
+    keys = np.asarray(keys, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64)
+    T = [int(n) for n in true_set]
+    P = {int(n) for n in pred_set}
+    spec = {}
+    for n in P:                                   # speculation over every predicted block
+        sl = slice(n * block_size, (n + 1) * block_size)
+        spec[n] = [block_partial(q_group[h], keys[sl], values[sl], scale) for h in range(q_group.shape[0])]
+    missed = [n for n in T if n not in P]
+    out = np.empty((q_group.shape[0], keys.shape[1]), dtype=np.float64)
+    for h in range(q_group.shape[0]):
+        state = None
+        for n in sorted(T):
+            if n in P:
+                part = spec[n][h]
+            else:                                 # repair: a missed block
+                sl = slice(n * block_size, (n + 1) * block_size)
+                part = block_partial(q_group[h], keys[sl], values[sl], scale)
+            state = part if state is None else merge(state, part)
+        out[h] = finalize(state)
+    wasted = sorted(P - set(T))
+    return out, np.asarray(missed, dtype=np.int64), np.asarray(wasted, dtype=np.int64)
+
+
+# ------------------------------------------------------------------------------------------------------------------
+# EMA score predictor (PRR abstract: "lightweight EMA-based predictor"; summary page: forecasts the top-K blocks)
+# ------------------------------------------------------------------------------------------------------------------
+
+
+def ema_update(ema_prev, scores, alpha: float, first: bool) -> np.ndarray:
+    s = np.asarray(scores, dtype=np.float64)
+    if first:
+        return s.copy()
+    return alpha * np.asarray(ema_prev, dtype=np.float64) + (1.0 - alpha) * s
+
+
+def predict(ema, k_spec: int) -> np.ndarray:
+    """Predicted set for the next step: top-K' of the EMA with the selection's tie rule (ascending)."""
+    return top_k(ema, k_spec)
+
+
+# ------------------------------------------------------------------------------------------------------------------
+# profiling-guided speculation budget (PRR abstract; summary page, Limitations: polynomial regression off the grid)
+# ------------------------------------------------------------------------------------------------------------------
+
+
+def choose_budget(n_grid, t_sel, kspec_grid, t_spec, n_target: float, degree: int = 2) -> int:
+    """Largest profiled K' whose measured speculation time is at most the selection time at n_target blocks.
+
+    The selection time at n_target is the measured one when n_target is on the grid, else a least-squares polynomial
+    of ``degree`` in the block count. K' = 0 is always admissible."""
+    n_grid = np.asarray(n_grid, dtype=np.float64)
+    t_sel = np.asarray(t_sel, dtype=np.float64)
+    hit = np.flatnonzero(n_grid == n_target)
+    if len(hit):
+        t_target = float(t_sel[hit[0]])
+    else:
+        coef = np.polyfit(n_grid, t_sel, min(degree, len(n_grid) - 1))
+        t_target = float(np.polyval(coef, n_target))
+    best = 0
+    for k, t in zip(kspec_grid, t_spec):
+        if t <= t_target and k > best:
+            best = int(k)
+    return best
+
+
+# ------------------------------------------------------------------------------------------------------------------
+# one (sequence, KV head) through a whole decode run: selection, prediction, output, statistics
+# ------------------------------------------------------------------------------------------------------------------
+
+
+def select_row(q_group, keys, block_size: int, top_k_blocks: int):
+    """(scores [N], T ascending, gap) for one (sequence, KV head) and one query group."""
+    kmin, kmax = block_summaries(keys, block_size)
+    s = quest_scores(q_group, kmin, kmax)
+    return s, top_k(s, top_k_blocks), boundary_gap(s, top_k_blocks)[2]
+
+
+def decode_row(q_steps, keys_at, values, block_size: int, top_k_blocks: int, k_spec: int, alpha: float,
+               scale: float, steps=None):
+    """Run the PRR reference pipeline over decode steps for one (sequence, KV head).
+
+    q_steps: [steps, G, D] queries; keys_at(t) -> [ctx, D] keys in force at step t (drift may change them).
+    Yields per step a dict with scores, T, P (None at step 0), output, missed, wasted, gaps."""
+    ema = None
+    P = None
+    n_steps = len(q_steps) if steps is None else steps
+    for t in range(n_steps):
+        keys = keys_at(t)
+        s, T, gap = select_row(q_steps[t], keys, block_size, top_k_blocks)
+        Pt = np.zeros((0,), dtype=np.int64) if (P is None or k_spec == 0) else P
+        o, missed, wasted = prr_output(q_steps[t], keys, values, T, Pt, block_size, scale)
+        ema = ema_update(ema, s, alpha, first=(t == 0))
+        ema_gap = boundary_gap(ema, k_spec)[2] if k_spec else math.inf
+        P_next = predict(ema, k_spec) if k_spec else np.zeros((0,), dtype=np.int64)
+        yield dict(t=t, scores=s, T=T, P=None if P is None else Pt, out=o, missed=missed, wasted=wasted, gap=gap,
+                   ema=ema.copy(), ema_gap_next=ema_gap, P_next=P_next)
+        P = P_next
+
+
+# ------------------------------------------------------------------------------------------------------------------
+# brute force (tiny inputs only): used by the pins
+# ------------------------------------------------------------------------------------------------------------------
+
+
+def brute_force_top_k(values, k: int):
+    """Among all k-subsets, the one with the largest sum; ties to the lexicographically smallest ascending tuple."""
+    best, best_sum = None, -math.inf
+    for c in combinations(range(len(values)), k):
+        s = float(sum(values[i] for i in c))
+        if s > best_sum or (s == best_sum and c < best):
+            best, best_sum = c, s
+    return np.asarray(best, dtype=np.int64)

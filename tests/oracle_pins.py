@@ -1,0 +1,260 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle module ``o`` disagrees with:
+  * a library special case (all blocks selected = dense attention, checked against torch's
+    scaled_dot_product_attention in float64 on the CPU),
+  * brute force on tiny inputs (every K-subset),
+  * closed forms (zero query, constant values, one-token blocks, EMA of a linear ramp, linear latency tables),
+  * invariants stated by the pages (repair covers exactly the missed blocks and the output equals standard DSA over
+    the true set, whatever was predicted: PRR summary page, Summary and Key findings),
+  * the hand-worked example in tests/golden.
+They take the module as an argument so that tests/test_oracle_mutants.py can show that planted mistakes fail them.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_problem(rng, n_blocks=6, bs=3, d=5, g=2):
+    keys = rng.standard_normal((n_blocks * bs, d))
+    values = rng.standard_normal((n_blocks * bs, d))
+    q = rng.standard_normal((g, d))
+    return q, keys, values
+
+
+def pin_dense_equivalence(o):
+    """K = N: attention over every block equals dense softmax attention (torch SDPA, fp64, CPU)."""
+    rng = np.random.default_rng(11)
+    for (nb, bs, d, g) in [(4, 8, 16, 4), (7, 3, 5, 1), (16, 32, 64, 4)]:
+        q, k, v = _rand_problem(rng, nb, bs, d, g)
+        scale = 1.0 / math.sqrt(d)
+        got = o.attention_over_blocks(q, k, v, np.arange(nb), bs, scale)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, :, None, :], torch.from_numpy(k)[None, None].expand(1, g, -1, -1),
+            torch.from_numpy(v)[None, None].expand(1, g, -1, -1), scale=scale)[0, :, 0, :].numpy()
+        assert np.allclose(got, ref, rtol=0, atol=1e-13), np.abs(got - ref).max()
+        # the speculate-reuse-repair pipeline with an arbitrary prediction gives the same dense result
+        pred = rng.choice(nb, size=max(1, nb // 2), replace=False)
+        got2, _, _ = o.prr_output(q, k, v, np.arange(nb), pred, bs, scale)
+        assert np.allclose(got2, ref, rtol=0, atol=1e-13)
+
+
+def pin_brute_force_selection(o):
+    """Tiny inputs: the selected set maximises the summed score over all K-subsets (ties: lowest indices)."""
+    rng = np.random.default_rng(12)
+    for trial in range(60):
+        nb = int(rng.integers(2, 9))
+        bs = int(rng.integers(1, 5))
+        d = int(rng.integers(1, 9))
+        g = int(rng.integers(1, 3))
+        k = int(rng.integers(1, nb + 1))
+        q, keys, _ = _rand_problem(rng, nb, bs, d, g)
+        if trial % 3 == 0:   # integer-valued data: exact ties in the scores
+            q = np.round(q * 2)
+            keys = np.round(keys)
+        kmin, kmax = o.block_summaries(keys, bs)
+        # summaries against a per-token scan
+        for n in range(nb):
+            blk = keys[n * bs:(n + 1) * bs]
+            for dd in range(d):
+                assert kmin[n, dd] == min(blk[:, dd]) and kmax[n, dd] == max(blk[:, dd])
+        s = o.quest_scores(q, kmin, kmax)
+        # score against its element-by-element definition
+        for n in range(nb):
+            ref = sum(max(q[h, dd] * kmin[n, dd], q[h, dd] * kmax[n, dd]) for h in range(g) for dd in range(d))
+            assert abs(s[n] - ref) <= 1e-12 * max(1.0, abs(ref))
+        got = o.top_k(s, k)
+        ref = o.brute_force_top_k(list(s), k)
+        assert list(got) == list(ref), (s, got, ref)
+
+
+def pin_quest_upper_bound(o):
+    """Per head, the block score bounds the largest exact q.k over the block's tokens from above; with one token per
+    block it equals the exact dot product (summed over the group's heads)."""
+    rng = np.random.default_rng(13)
+    for _ in range(20):
+        q, keys, _ = _rand_problem(rng, 8, 4, 16, 1)
+        kmin, kmax = o.block_summaries(keys, 4)
+        s = o.quest_scores(q, kmin, kmax)
+        exact = (keys @ q[0]).reshape(8, 4).max(axis=1)
+        assert np.all(s >= exact - 1e-12)
+        qg, keys1, _ = _rand_problem(rng, 10, 1, 16, 4)
+        kmin, kmax = o.block_summaries(keys1, 1)
+        s1 = o.quest_scores(qg, kmin, kmax)
+        assert np.allclose(s1, keys1 @ qg.sum(axis=0), rtol=0, atol=1e-12)
+
+
+def pin_signsplit(o):
+    rng = np.random.default_rng(14)
+    q, keys, _ = _rand_problem(rng, 64, 8, 32, 4)
+    kmin, kmax = o.block_summaries(keys, 8)
+    a = o.quest_scores(q, kmin, kmax)
+    b = o.quest_scores_signsplit(q, kmin, kmax)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def pin_merge_order_free(o):
+    """Merging per-block partials in any order and bracketing equals the two-pass softmax over their union."""
+    rng = np.random.default_rng(15)
+    q, k, v = _rand_problem(rng, 9, 5, 8, 1)
+    k = k * 3.0   # spread the logits so the rescaling matters
+    scale = 0.7
+    parts = [o.block_partial(q[0], k[n * 5:(n + 1) * 5], v[n * 5:(n + 1) * 5], scale) for n in range(9)]
+    ref = o.attention_over_blocks(q, k, v, np.arange(9), 5, scale)[0]
+    for trial in range(20):
+        order = rng.permutation(9)
+        pool = [parts[i] for i in order]
+        while len(pool) > 1:   # random bracketing
+            i = int(rng.integers(len(pool) - 1))
+            pool[i:i + 2] = [o.merge(pool[i], pool[i + 1])]
+        got = o.finalize(pool[0])
+        assert np.allclose(got, ref, rtol=0, atol=1e-13), np.abs(got - ref).max()
+    # a partial's own fields against their definitions; the merged m is the running maximum of every logit
+    m, l, O = parts[0]
+    z = scale * (k[:5] @ q[0])
+    assert abs(m - z.max()) < 1e-15 and abs(l - np.exp(z - z.max()).sum()) < 1e-13
+    zall = scale * (k @ q[0])
+    m_all = o.merge(o.merge(parts[3], parts[0]), parts[7])[0]
+    assert m_all == max(zall[15:20].max(), zall[0:5].max(), zall[35:40].max())
+    # logits hundreds apart: the merge must not overflow (weights relative to the running maximum)
+    big = [o.block_partial(q[0], 400.0 * n * np.tile(q[0], (5, 1)) / (q[0] @ q[0]), v[n * 5:(n + 1) * 5], 1.0)
+           for n in range(3)]
+    st = o.merge(o.merge(big[2], big[0]), big[1])
+    assert np.all(np.isfinite(o.finalize(st))) and np.allclose(o.finalize(st), v[10:15].mean(axis=0), atol=1e-12)
+
+
+def pin_repair_invariants(o):
+    """P = T needs no repair; P = {} repairs everything; any P (random, disjoint, poisoned) gives the same output."""
+    rng = np.random.default_rng(16)
+    nb, bs, d, g, K = 12, 4, 8, 2, 5
+    q, keys, vals = _rand_problem(rng, nb, bs, d, g)
+    kmin, kmax = o.block_summaries(keys, bs)
+    T = o.top_k(o.quest_scores(q, kmin, kmax), K)
+    scale = 1 / math.sqrt(d)
+    ref = o.attention_over_blocks(q, keys, vals, T, bs, scale)
+    out, missed, wasted = o.prr_output(q, keys, vals, T, T, bs, scale)
+    assert len(missed) == 0 and len(wasted) == 0 and np.allclose(out, ref, rtol=0, atol=1e-13)
+    out, missed, wasted = o.prr_output(q, keys, vals, T, [], bs, scale)
+    assert list(missed) == list(T) and len(wasted) == 0 and np.allclose(out, ref, rtol=0, atol=1e-13)
+    outside = [n for n in range(nb) if n not in set(T)]
+    for P in [rng.choice(nb, 7, replace=False), outside, list(T[:2]) + outside[:3]]:
+        out, missed, wasted = o.prr_output(q, keys, vals, T, P, bs, scale)
+        assert sorted(set(missed) | (set(T) & set(P))) == sorted(T)
+        assert sorted(wasted) == sorted(set(P) - set(T))
+        assert np.allclose(out, ref, rtol=0, atol=1e-13)
+    # a poison block (keys aligned with every query, huge logits) that is predicted but not selected must not leak
+    pk = keys.copy()
+    pois = outside[0]
+    pk[pois * bs:(pois + 1) * bs] = 100.0 * q.sum(axis=0) / np.linalg.norm(q.sum(axis=0))
+    ref_p = o.attention_over_blocks(q, pk, vals, T, bs, scale)
+    out, _, wasted = o.prr_output(q, pk, vals, T, [pois] + list(T), bs, scale)
+    assert list(wasted) == [pois] and np.allclose(out, ref_p, rtol=0, atol=1e-13)
+    assert np.allclose(ref_p, ref)
+
+
+def pin_closed_forms(o):
+    rng = np.random.default_rng(17)
+    nb, bs, d, g, K = 10, 4, 6, 3, 4
+    _, keys, vals = _rand_problem(rng, nb, bs, d, g)
+    # q = 0: all scores 0, T = first K blocks, uniform weights -> mean of V over T
+    q0 = np.zeros((g, d))
+    kmin, kmax = o.block_summaries(keys, bs)
+    s = o.quest_scores(q0, kmin, kmax)
+    T = o.top_k(s, K)
+    assert list(T) == list(range(K))
+    out = o.attention_over_blocks(q0, keys, vals, T, bs, 0.5)
+    assert np.allclose(out, vals[:K * bs].mean(axis=0)[None], rtol=0, atol=1e-14)
+    # constant V: the output is that constant
+    q = rng.standard_normal((g, d))
+    c = rng.standard_normal(d)
+    out = o.attention_over_blocks(q, keys, np.tile(c, (nb * bs, 1)), [1, 4, 7], bs, 0.3)
+    assert np.allclose(out, c[None], rtol=0, atol=1e-14)
+    # one-token blocks, K = 1: the output is v of the token with the largest group-summed dot product
+    k1 = rng.standard_normal((nb, d))
+    v1 = rng.standard_normal((nb, d))
+    q1 = rng.standard_normal((1, d))
+    kmin, kmax = o.block_summaries(k1, 1)
+    T = o.top_k(o.quest_scores(q1, kmin, kmax), 1)
+    assert T[0] == int(np.argmax(k1 @ q1[0]))
+    assert np.allclose(o.attention_over_blocks(q1, k1, v1, T, 1, 0.125)[0], v1[T[0]], rtol=0, atol=1e-15)
+
+
+def pin_hand_example(o):
+    ex = json.load(open(os.path.join(GOLDEN, "hand_worked_example.json")))
+    q = np.asarray(ex["q"], dtype=np.float64)
+    keys = np.asarray(ex["keys"], dtype=np.float64)
+    vals = np.asarray(ex["values"], dtype=np.float64)
+    bs, K = ex["block_size"], ex["top_k"]
+    kmin, kmax = o.block_summaries(keys, bs)
+    assert kmin.tolist() == ex["kmin"] and kmax.tolist() == ex["kmax"]
+    s = o.quest_scores(q, kmin, kmax)
+    assert s.tolist() == ex["scores"]
+    T = o.top_k(s, K)
+    assert T.tolist() == ex["selected"]
+    out = o.attention_over_blocks(q, keys, vals, T, bs, math.log(2.0))
+    assert np.allclose(out[0] * 12.0, ex["out_numerator_over_12"], rtol=0, atol=1e-12)
+    out2, missed, wasted = o.prr_output(q, keys, vals, T, ex["pred"], bs, math.log(2.0))
+    assert missed.tolist() == ex["missed"] and wasted.tolist() == ex["wasted"]
+    assert np.allclose(out2, out, rtol=0, atol=1e-13)
+
+
+def pin_ema_closed_form(o):
+    """EMA of a linear ramp s_t = (t0 + t) c started at e_0 = s_0: the constant t0 c passes through unchanged and the
+    ramp part gives e_t = (t0 + t - a/(1-a) + a^(t+1)/(1-a)) c."""
+    t0 = 5.0
+    for a in (0.9, 0.7, 0.5):
+        c = np.array([1.0, -2.0, 0.5])
+        e = None
+        for t in range(30):
+            e = o.ema_update(e, (t0 + t) * c, a, first=(t == 0))
+            ref = (t0 + t - a / (1 - a) + a ** (t + 1) / (1 - a)) * c
+            assert np.allclose(e, ref, rtol=0, atol=1e-12), (t, e, ref)
+    # prediction uses the same tie rule as selection
+    assert o.predict(np.array([1.0, 3.0, 3.0, 2.0, 3.0]), 2).tolist() == [1, 2]
+
+
+def pin_budget_closed_form(o):
+    """Linear latency tables: t_sel(N) = 2 + 0.01 N, t_spec(K') = 1 + 0.05 K'. At N = 1000 (off the grid),
+    t_sel = 12, so the largest admissible K' on the grid {0, 64, ..., 384} is the largest with 1 + 0.05 K' <= 12,
+    i.e. K' <= 220 -> 192. At N = 4096 (on the grid) t_sel = 42.96 -> K' <= 839.2 -> 384."""
+    n_grid = [256, 512, 2048, 4096, 8192]
+    t_sel = [2 + 0.01 * n for n in n_grid]
+    ks = [0, 64, 128, 192, 256, 320, 384]
+    t_spec = [1 + 0.05 * k for k in ks]
+    assert o.choose_budget(n_grid, t_sel, ks, t_spec, 1000) == 192
+    assert o.choose_budget(n_grid, t_sel, ks, t_spec, 4096) == 384
+    assert o.choose_budget(n_grid, t_sel, ks, [100.0] * len(ks), 1000) == 0
+    # a quadratic table is reproduced exactly off the grid: t_sel = 1 + N^2 / 1e6 -> at 3000: 10 -> K' <= 180 -> 128
+    t_q = [1 + n * n / 1e6 for n in n_grid]
+    assert o.choose_budget(n_grid, t_q, ks, t_spec, 3000) == 128
+
+
+def pin_paged_gather(o):
+    """Logical token order through a permuted page table, against a hand-built cache: page p of sequence b holds
+    tokens [p * page, (p + 1) * page), so entry (phys, g, r) of the cache is token table[b].index(phys) * page + r."""
+    B, Hkv, page, D, pps = 2, 3, 4, 2, 5
+    table = np.array([[7, 2, 9, 0, 4], [1, 8, 3, 6, 5]], dtype=np.int32)
+    cache = np.zeros((B * pps, Hkv, page, D))
+    for b in range(B):
+        for p in range(pps):
+            for g in range(Hkv):
+                for r in range(page):
+                    tok = p * page + r
+                    cache[table[b, p], g, r] = [1000 * b + 100 * g + tok, -tok]
+    for b in range(B):
+        for g in range(Hkv):
+            got = o.logical_tokens(cache, table, b, g, pps * page)
+            ref = np.array([[1000 * b + 100 * g + i, -i] for i in range(pps * page)], dtype=np.float64)
+            assert np.array_equal(got, ref)
+
+
+ALL_PINS = [pin_dense_equivalence, pin_brute_force_selection, pin_quest_upper_bound, pin_signsplit,
+            pin_merge_order_free, pin_repair_invariants, pin_closed_forms, pin_hand_example, pin_ema_closed_form,
+            pin_budget_closed_form, pin_paged_gather]

@@ -1,0 +1,108 @@
+"""The seeded input generator: determinism, hot-block planting, drift, paging (CPU)."""
+import numpy as np
+import torch
+
+from dynamic_sparse_attention_decode_amd.inputs import WORKLOADS, make_inputs, query_stream, block_table
+
+
+def _small(name, **kw):
+    w = WORKLOADS[name]
+    base = dict(ctx=w.block_size * 64, steps=9, hot_blocks=min(w.hot_blocks, 8) if w.hot_blocks else 0,
+                top_k=min(w.top_k, 16), k_spec=tuple(min(k, 20) for k in w.k_spec))
+    base.update(kw)
+    return w.replace(**base)
+
+
+def test_workload_shapes():
+    for w in WORKLOADS.values():
+        w.validate()
+    w = WORKLOADS["million_token"]
+    assert w.n_blocks == 32768 and w.group == 8 and w.k_spec == (0, 128, 256, 384)
+    w = WORKLOADS["paged_b32_64k"]
+    assert w.n_blocks == 4096 and w.shuffle_pages and w.page_size == 16
+
+
+def test_determinism_same_bytes():
+    w = _small("llama3_8b_32k", batch=2)
+    a = make_inputs(w)
+    b = make_inputs(w)
+    assert torch.equal(a.k_cache.view(torch.int16), b.k_cache.view(torch.int16))
+    assert torch.equal(a.v_cache.view(torch.int16), b.v_cache.view(torch.int16))
+    assert torch.equal(a.q.view(torch.int16), b.q.view(torch.int16))
+    c = make_inputs(w.replace(seed=w.seed + 1))
+    assert not torch.equal(a.k_cache.view(torch.int16), c.k_cache.view(torch.int16))
+
+
+def test_query_ar1_process():
+    w = WORKLOADS["paged_b32_64k"].replace(steps=4000, batch=1, n_q_heads=8, n_kv_heads=2)
+    q = query_stream(w)
+    # stationary unit variance and lag-1 correlation rho
+    x = q[100:].reshape(q.shape[0] - 100, -1)
+    assert abs(x.var() - 1.0) < 0.05
+    r = (x[1:] * x[:-1]).mean() / x.var()
+    assert abs(r - w.rho) < 0.03
+
+
+def test_hot_blocks_planted():
+    w = _small("llama3_8b_32k", batch=1, n_q_heads=8, n_kv_heads=2)
+    inp = make_inputs(w)
+    G = w.group
+    for g in range(w.n_kv_heads):
+        for n in inp.hot[0, g]:
+            k = inp.block_keys(0, g, int(n)).float()
+            # the bias direction dominates the mean key of a hot block
+            mean = k.mean(dim=0).numpy()
+            assert mean @ inp.qhat[0, g] > 1.0   # bias 2, noise std 0.25
+    # qhat is the unit group-summed first query
+    q0 = inp.q[0, 0].float().numpy()
+    s = q0[:G].sum(axis=0)
+    assert np.allclose(inp.qhat[0, 0], s / np.linalg.norm(s), atol=2e-2)
+
+
+def test_page_table_permutation():
+    w = _small("paged_b32_64k", batch=3)
+    t = block_table(w)
+    assert t.shape == (3, w.pages_per_seq)
+    assert sorted(t.ravel().tolist()) == list(range(w.n_pages))
+    assert not np.array_equal(t.ravel(), np.arange(w.n_pages))
+    w2 = _small("llama3_8b_32k", batch=2)
+    assert np.array_equal(block_table(w2).ravel(), np.arange(w2.n_pages))
+
+
+def test_bf16_cast_is_round_to_nearest_even():
+    x = torch.tensor([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8)], dtype=torch.float32)
+    y = x.to(torch.bfloat16).float()
+    assert y.tolist() == [1.0, 1.0 + 2 ** -6, -1.0]
+
+
+def test_drift_moves_one_block_per_row():
+    w = _small("long_ctx_131k_b4", batch=2)
+    inp = make_inputs(w)
+    before_hot = inp.hot.copy()
+    k_before = inp.k_cache.clone()
+    assert len(inp.drift(3)) == 0
+    changed = inp.drift(4)
+    assert len(changed) == 2 * w.batch * w.n_kv_heads
+    after = inp.hot
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            assert len(set(before_hot[b, g]) ^ set(after[b, g])) == 2
+    # only the keys of the changed blocks moved
+    N = w.n_blocks
+    moved = set()
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            for n in range(N):
+                if not torch.equal(inp.block_keys(b, g, n), _keys(k_before, inp, b, g, n)):
+                    moved.add((b * w.n_kv_heads + g) * N + n)
+    assert moved == set(changed.tolist())
+    # a block that loses the bias gets back exactly its unbiased keys: moving it back and forth is lossless
+    inp2 = make_inputs(w)
+    for t in (4, 8, 12):
+        inp2.drift(t)
+    assert len(inp2.saved) == w.batch * w.n_kv_heads * w.hot_blocks
+
+
+def _keys(cache, inp, b, g, n):
+    pages = torch.as_tensor(inp._pages_of_block(b, n), dtype=torch.long)
+    return cache[pages, g].reshape(inp.w.block_size, inp.w.head_dim)

@@ -1,0 +1,178 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail at least one pin.
+
+Each mutant replaces one oracle function with a plausible wrong version (a dropped term, a wrong sign or index, a
+transposed operand, a wrong tie rule); the test asserts that running all pins against the mutated oracle raises."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import prr_oracle as O
+from tests.oracle_pins import ALL_PINS
+
+
+def _quest_drop_kmin(q_group, kmin, kmax):
+    return sum((kmax * q_group[h]).sum(axis=1) for h in range(q_group.shape[0]))
+
+
+def _quest_min_not_max(q_group, kmin, kmax):
+    return sum(np.minimum(kmin * q_group[h], kmax * q_group[h]).sum(axis=1) for h in range(q_group.shape[0]))
+
+
+def _quest_first_head_only(q_group, kmin, kmax):
+    q = q_group[0]
+    return np.maximum(kmin * q, kmax * q).sum(axis=1)
+
+
+def _signsplit_swapped(q_group, kmin, kmax):
+    qp = np.maximum(q_group, 0.0).sum(axis=0)
+    qn = np.minimum(q_group, 0.0).sum(axis=0)
+    return kmin @ qp + kmax @ qn
+
+
+def _summaries_swapped(keys, bs):
+    kb = keys.reshape(-1, bs, keys.shape[1])
+    return kb.max(axis=1), kb.min(axis=1)
+
+
+def _topk_high_ties(values, k):
+    n = len(values)
+    order = np.lexsort((-np.arange(n), -np.asarray(values, dtype=np.float64)))
+    return np.sort(order[:k])
+
+
+def _topk_off_by_one(values, k):
+    n = len(values)
+    order = np.lexsort((np.arange(n), -np.asarray(values, dtype=np.float64)))
+    return np.sort(order[1:k + 1]) if k < n else np.sort(order[:k])
+
+
+def _topk_unsorted(values, k):
+    n = len(values)
+    return np.lexsort((np.arange(n), -np.asarray(values, dtype=np.float64)))[:k]
+
+
+def _attn_no_scale(q_group, keys, values, blocks, block_size, scale):
+    return _orig["attention_over_blocks"](q_group, keys, values, blocks, block_size, 1.0)
+
+
+def _attn_keys_as_values(q_group, keys, values, blocks, block_size, scale):
+    return _orig["attention_over_blocks"](q_group, keys, keys, blocks, block_size, scale)
+
+
+def _attn_block_index_shift(q_group, keys, values, blocks, block_size, scale):
+    idx = np.concatenate([np.arange(n * block_size + 1, (n + 1) * block_size + 1) % len(keys) for n in blocks])
+    k, v = keys[idx], values[idx]
+    out = np.empty((q_group.shape[0], keys.shape[1]))
+    for h in range(q_group.shape[0]):
+        z = scale * (k @ q_group[h])
+        w = np.exp(z - z.max())
+        out[h] = (w @ v) / w.sum()
+    return out
+
+
+def _merge_no_rescale_l(a, b):
+    (m1, l1, o1), (m2, l2, o2) = a, b
+    m = max(m1, m2)
+    c1, c2 = math.exp(m1 - m), math.exp(m2 - m)
+    return m, l1 * c1 + l2, o1 * c1 + o2 * c2
+
+
+def _merge_min(a, b):
+    (m1, l1, o1), (m2, l2, o2) = a, b
+    m = min(m1, m2)
+    c1, c2 = math.exp(m1 - m), math.exp(m2 - m)
+    return m, l1 * c1 + l2 * c2, o1 * c1 + o2 * c2
+
+
+def _partial_unshifted(q_h, k_blk, v_blk, scale):
+    z = scale * (k_blk @ q_h)
+    p = np.exp(z)
+    return float(z.max()), float(p.sum()), p @ v_blk
+
+
+def _prr_keeps_wasted(q_group, keys, values, true_set, pred_set, block_size, scale):
+    allb = sorted(set(int(n) for n in true_set) | set(int(n) for n in pred_set))
+    out = _orig["attention_over_blocks"](q_group, keys, values, allb, block_size, scale)
+    _, missed, wasted = _orig["prr_output"](q_group, keys, values, true_set, pred_set, block_size, scale)
+    return out, missed, wasted
+
+
+def _prr_skips_repair(q_group, keys, values, true_set, pred_set, block_size, scale):
+    hit = [n for n in true_set if n in set(int(p) for p in pred_set)]
+    _, missed, wasted = _orig["prr_output"](q_group, keys, values, true_set, pred_set, block_size, scale)
+    if not hit:
+        hit = list(true_set[:1])
+    return _orig["attention_over_blocks"](q_group, keys, values, hit, block_size, scale), missed, wasted
+
+
+def _ema_swapped(ema_prev, scores, alpha, first):
+    return _orig["ema_update"](ema_prev, scores, 1.0 - alpha, first)
+
+
+def _ema_no_init(ema_prev, scores, alpha, first):
+    prev = np.zeros_like(np.asarray(scores, dtype=np.float64)) if first else ema_prev
+    return alpha * prev + (1 - alpha) * np.asarray(scores, dtype=np.float64)
+
+
+def _budget_strict(n_grid, t_sel, kspec_grid, t_spec, n_target, degree=2):
+    return _orig["choose_budget"](n_grid, t_sel, kspec_grid, [t * 1.0000001 + 1e-9 for t in t_spec], n_target,
+                                  degree) if False else _budget_linear(n_grid, t_sel, kspec_grid, t_spec, n_target)
+
+
+def _budget_linear(n_grid, t_sel, kspec_grid, t_spec, n_target, degree=2):
+    return _orig["choose_budget"](n_grid, t_sel, kspec_grid, t_spec, n_target, 1)
+
+
+def _budget_smallest(n_grid, t_sel, kspec_grid, t_spec, n_target, degree=2):
+    best = _orig["choose_budget"](n_grid, t_sel, kspec_grid, t_spec, n_target, degree)
+    ok = [k for k in kspec_grid if 0 < k <= best]
+    return min(ok) if ok else 0
+
+
+def _gather_identity(cache, table, b, g, n_tokens):
+    page = cache.shape[2]
+    i = np.arange(n_tokens)
+    return np.asarray(cache[b * table.shape[1] + i // page, g, i % page], dtype=np.float64)
+
+
+_orig = {k: getattr(O, k) for k in ["attention_over_blocks", "prr_output", "ema_update", "choose_budget"]}
+
+MUTANTS = {
+    "quest_drop_kmin": ("quest_scores", _quest_drop_kmin),
+    "quest_min_not_max": ("quest_scores", _quest_min_not_max),
+    "quest_first_head_only": ("quest_scores", _quest_first_head_only),
+    "signsplit_swapped": ("quest_scores_signsplit", _signsplit_swapped),
+    "summaries_swapped": ("block_summaries", _summaries_swapped),
+    "topk_high_ties": ("top_k", _topk_high_ties),
+    "topk_off_by_one": ("top_k", _topk_off_by_one),
+    "topk_unsorted": ("top_k", _topk_unsorted),
+    "attn_no_scale": ("attention_over_blocks", _attn_no_scale),
+    "attn_keys_as_values": ("attention_over_blocks", _attn_keys_as_values),
+    "attn_block_index_shift": ("attention_over_blocks", _attn_block_index_shift),
+    "merge_no_rescale_l": ("merge", _merge_no_rescale_l),
+    "merge_min": ("merge", _merge_min),
+    "partial_unshifted": ("block_partial", _partial_unshifted),
+    "prr_keeps_wasted": ("prr_output", _prr_keeps_wasted),
+    "prr_skips_repair": ("prr_output", _prr_skips_repair),
+    "ema_swapped_alpha": ("ema_update", _ema_swapped),
+    "ema_no_init": ("ema_update", _ema_no_init),
+    "budget_linear_fit": ("choose_budget", _budget_linear),
+    "budget_smallest": ("choose_budget", _budget_smallest),
+    "gather_ignores_table": ("logical_tokens", _gather_identity),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failures = 0
+    for pin in ALL_PINS:
+        try:
+            pin(O)
+        except AssertionError:
+            failures += 1
+        except Exception:   # a crash inside a pin also counts as caught
+            failures += 1
+    assert failures > 0, f"mutant {name} passed every pin"
