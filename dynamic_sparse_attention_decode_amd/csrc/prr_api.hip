@@ -1,0 +1,398 @@
+// C ABI of libprr: argument validation, launch configuration, the two-stream decode step, and status strings.
+// Every check happens on the host before any launch; nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <atomic>
+#include <new>
+
+#include "prr_device.h"
+#include "prr_launch.h"
+
+namespace prr {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+prr_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: launch failed: %s", what, hipGetErrorString(e));
+    return PRR_ELAUNCH;
+  }
+  return PRR_OK;
+}
+
+// ---- kernel tracing ------------------------------------------------------------------------------------------------
+
+}  // namespace prr
+
+struct prr_trace {
+  int32_t capacity = 0;
+  uint32_t mask = 0;
+  int32_t count[PRR_KERNEL_COUNT] = {};
+  hipEvent_t* ev0[PRR_KERNEL_COUNT] = {};
+  hipEvent_t* ev1[PRR_KERNEL_COUNT] = {};
+};
+
+namespace prr {
+
+static std::atomic<prr_trace*> g_trace{nullptr};
+
+void trace_begin(int kid, hipStream_t stream) {
+  prr_trace* t = g_trace.load(std::memory_order_acquire);
+  if (!t || !(t->mask & (1u << kid)) || t->count[kid] >= t->capacity) return;
+  (void)hipEventRecord(t->ev0[kid][t->count[kid]], stream);
+}
+
+void trace_end(int kid, hipStream_t stream) {
+  prr_trace* t = g_trace.load(std::memory_order_acquire);
+  if (!t || !(t->mask & (1u << kid)) || t->count[kid] >= t->capacity) return;
+  (void)hipEventRecord(t->ev1[kid][t->count[kid]], stream);
+  ++t->count[kid];
+}
+
+// ---- benchmark helper kernels ------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void flush_kernel(uint4* __restrict__ p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, (uint32_t)i, 0u, 0u);
+}
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, int64_t n16,
+                                                          float* __restrict__ sink) {
+  uint32_t acc = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] ^= red[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sink[blockIdx.x] = __uint_as_float(red[0] & 0x007fffffu);   // finite value
+}
+
+prr_status launch_flush(void* buf, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return PRR_OK;
+  const int64_t blocks = (n16 + 255) / 256;
+  flush_kernel<<<dim3((unsigned)(blocks < 16384 ? blocks : 16384)), dim3(256), 0, stream>>>(static_cast<uint4*>(buf),
+                                                                                            n16);
+  return check_launch("flush_write");
+}
+
+prr_status launch_stream_read(const void* buf, size_t bytes, float* sink, hipStream_t stream) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return PRR_OK;
+  const int64_t blocks = (n16 + 255) / 256;
+  stream_read_kernel<<<dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream>>>(
+      static_cast<const uint4*>(buf), n16, sink);
+  return check_launch("stream_read");
+}
+
+// ---- validation ------------------------------------------------------------------------------------------------------
+
+static prr_status check_shape(const prr_shape* s) {
+  if (!s) { set_error("shape is NULL"); return PRR_EINVAL; }
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->head_dim < 1 || s->block_size < 1 ||
+      s->page_size < 1 || s->n_blocks < 1 || s->pages_per_seq < 1) {
+    set_error("shape has a non-positive size");
+    return PRR_EINVAL;
+  }
+  if (s->n_q_heads % s->n_kv_heads) { set_error("n_q_heads %% n_kv_heads != 0"); return PRR_EINVAL; }
+  const int G = s->n_q_heads / s->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) { set_error("group size %d not in {1,2,4,8}", G); return PRR_EUNSUPPORTED; }
+  if (s->dtype != kF32 && s->dtype != kBF16 && s->dtype != kF16) { set_error("unknown dtype %d", s->dtype); return PRR_EINVAL; }
+  const bool row256 = (s->dtype == kF32 && s->head_dim == 64) || (s->dtype != kF32 && s->head_dim == 128);
+  if (!row256) {
+    set_error("unsupported dtype/head_dim combination (%d, %d): need f32 x 64 or bf16/f16 x 128", s->dtype,
+              s->head_dim);
+    return PRR_EUNSUPPORTED;
+  }
+  if (s->block_size % 4) { set_error("block_size %% 4 != 0"); return PRR_EUNSUPPORTED; }
+  if (s->block_size % s->page_size) { set_error("block_size %% page_size != 0"); return PRR_EINVAL; }
+  if ((int64_t)s->pages_per_seq * s->page_size != (int64_t)s->n_blocks * s->block_size) {
+    set_error("pages_per_seq * page_size != n_blocks * block_size");
+    return PRR_EINVAL;
+  }
+  if (s->n_blocks > 65536) { set_error("n_blocks > 65536"); return PRR_EUNSUPPORTED; }
+  if (!(s->softmax_scale > 0.f) || !isfinite(s->softmax_scale)) { set_error("softmax_scale must be finite and > 0"); return PRR_EINVAL; }
+  return PRR_OK;
+}
+
+#define PRR_REQUIRE(cond, ...)            \
+  do {                                    \
+    if (!(cond)) {                        \
+      set_error(__VA_ARGS__);             \
+      return PRR_EINVAL;                  \
+    }                                     \
+  } while (0)
+
+#define PRR_TRY(expr)                  \
+  do {                                 \
+    const prr_status st_ = (expr);     \
+    if (st_ != PRR_OK) return st_;     \
+  } while (0)
+
+static prr_status check_topk_n(const prr_shape* s) {
+  if (s->n_blocks > 32768) { set_error("n_blocks > 32768 is not supported by the top-K kernels"); return PRR_EUNSUPPORTED; }
+  return PRR_OK;
+}
+
+static inline hipStream_t as_stream(void* p) { return static_cast<hipStream_t>(p); }
+
+}  // namespace prr
+
+using namespace prr;
+
+struct prr_step_ctx {
+  hipEvent_t q_ready, spec_done, sel_done, spec_tail;
+};
+
+extern "C" {
+
+prr_status prr_build_summaries(const prr_shape* shape, const void* k_cache, const int32_t* block_table,
+                               const int32_t* block_ids, int32_t n_block_ids, void* summaries, void* stream) {
+  PRR_TRY(check_shape(shape));
+  PRR_REQUIRE(k_cache && block_table && summaries, "build_summaries: null pointer");
+  int64_t jobs = (int64_t)shape->batch * shape->n_kv_heads * shape->n_blocks;
+  if (block_ids) {
+    PRR_REQUIRE(n_block_ids >= 0, "build_summaries: n_block_ids < 0");
+    jobs = n_block_ids;
+  }
+  return launch_summaries(*shape, k_cache, block_table, block_ids, jobs, summaries, as_stream(stream));
+}
+
+prr_status prr_score_select(const prr_shape* shape, const void* q, const void* summaries, int32_t top_k,
+                            float* scores, int32_t* sel_idx, void* stream) {
+  PRR_TRY(check_shape(shape));
+  PRR_TRY(check_topk_n(shape));
+  PRR_REQUIRE(q && summaries && scores && sel_idx, "score_select: null pointer");
+  PRR_REQUIRE(top_k >= 1 && top_k <= shape->n_blocks, "score_select: top_k %d not in [1, %d]", top_k,
+              shape->n_blocks);
+  PRR_TRY(launch_score(*shape, q, summaries, scores, as_stream(stream)));
+  return launch_topk(*shape, scores, nullptr, 0.f, 0, top_k, sel_idx, as_stream(stream));
+}
+
+prr_status prr_ema_predict(const prr_shape* shape, const float* scores, float* ema, float alpha, int32_t first_step,
+                           int32_t k_spec, int32_t* pred_idx_next, void* stream) {
+  PRR_TRY(check_shape(shape));
+  PRR_TRY(check_topk_n(shape));
+  PRR_REQUIRE(scores && ema && pred_idx_next, "ema_predict: null pointer");
+  PRR_REQUIRE(k_spec >= 1 && k_spec <= shape->n_blocks, "ema_predict: k_spec %d not in [1, %d]", k_spec,
+              shape->n_blocks);
+  PRR_REQUIRE(alpha >= 0.f && alpha <= 1.f, "ema_predict: alpha not in [0, 1]");
+  return launch_topk(*shape, scores, ema, alpha, first_step ? 1 : 0, k_spec, pred_idx_next, as_stream(stream));
+}
+
+prr_status prr_speculate(const prr_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* pred_idx, int32_t k_spec, float* partials,
+                         void* stream) {
+  PRR_TRY(check_shape(shape));
+  PRR_REQUIRE(k_spec >= 0 && k_spec <= shape->n_blocks, "speculate: k_spec %d not in [0, %d]", k_spec,
+              shape->n_blocks);
+  if (k_spec == 0) return PRR_OK;
+  PRR_REQUIRE(q && k_cache && v_cache && block_table && pred_idx && partials, "speculate: null pointer");
+  return launch_speculate(*shape, q, k_cache, v_cache, block_table, pred_idx, k_spec, partials, as_stream(stream));
+}
+
+prr_status prr_repair_merge(const prr_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, const int32_t* sel_idx, int32_t top_k,
+                            const int32_t* pred_idx, int32_t k_spec, const float* partials, float* out,
+                            int32_t* n_missed, void* workspace, void* stream) {
+  PRR_TRY(check_shape(shape));
+  PRR_REQUIRE(q && k_cache && v_cache && block_table && sel_idx && out && n_missed && workspace,
+              "repair_merge: null pointer");
+  PRR_REQUIRE(top_k >= 1 && top_k <= shape->n_blocks, "repair_merge: top_k %d not in [1, %d]", top_k,
+              shape->n_blocks);
+  PRR_REQUIRE(k_spec >= 0 && k_spec <= shape->n_blocks, "repair_merge: k_spec %d not in [0, %d]", k_spec,
+              shape->n_blocks);
+  if (k_spec > 0) PRR_REQUIRE(pred_idx && partials, "repair_merge: k_spec > 0 needs pred_idx and partials");
+  return launch_repair(*shape, q, k_cache, v_cache, block_table, sel_idx, top_k, k_spec ? pred_idx : nullptr,
+                       k_spec, k_spec ? partials : nullptr, out, n_missed, workspace, as_stream(stream));
+}
+
+size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec) {
+  if (check_shape(shape) != PRR_OK || k_spec <= 0) return 0;
+  const int G = shape->n_q_heads / shape->n_kv_heads;
+  return (size_t)shape->batch * shape->n_kv_heads * (size_t)k_spec * (size_t)rec_floats(G, shape->head_dim) *
+         sizeof(float);
+}
+
+size_t prr_workspace_bytes(const prr_shape* shape, int32_t top_k) {
+  if (check_shape(shape) != PRR_OK || top_k <= 0) return 0;
+  return repair_workspace_bytes(*shape, top_k);
+}
+
+prr_status prr_step_ctx_create(prr_step_ctx** out) {
+  if (!out) { set_error("step_ctx_create: null pointer"); return PRR_EINVAL; }
+  auto* c = new (std::nothrow) prr_step_ctx{};
+  if (!c) { set_error("step_ctx_create: out of host memory"); return PRR_EINVAL; }
+  hipEvent_t* ev[4] = {&c->q_ready, &c->spec_done, &c->sel_done, &c->spec_tail};
+  for (int i = 0; i < 4; ++i) {
+    if (hipEventCreateWithFlags(ev[i], hipEventDisableTiming) != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(*ev[j]);
+      delete c;
+      set_error("step_ctx_create: hipEventCreateWithFlags failed");
+      return PRR_ELAUNCH;
+    }
+  }
+  *out = c;
+  return PRR_OK;
+}
+
+void prr_step_ctx_destroy(prr_step_ctx* ctx) {
+  if (!ctx) return;
+  (void)hipEventDestroy(ctx->q_ready);
+  (void)hipEventDestroy(ctx->spec_done);
+  (void)hipEventDestroy(ctx->sel_done);
+  (void)hipEventDestroy(ctx->spec_tail);
+  delete ctx;
+}
+
+static prr_status hip_ok(hipError_t e, const char* what) {
+  if (e != hipSuccess) {
+    set_error("%s: %s", what, hipGetErrorString(e));
+    return PRR_ELAUNCH;
+  }
+  return PRR_OK;
+}
+
+prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_step_args* a, int32_t mode,
+                           int32_t join, void* stream_sel, void* stream_spec) {
+  PRR_TRY(check_shape(shape));
+  PRR_REQUIRE(a, "decode_step: args is NULL");
+  PRR_REQUIRE(mode >= PRR_MODE_SERIALIZED && mode <= PRR_MODE_TWO_STREAM, "decode_step: unknown mode %d", mode);
+  PRR_REQUIRE(mode != PRR_MODE_TWO_STREAM || ctx, "decode_step: two-stream mode needs a step context");
+  const hipStream_t s1 = as_stream(stream_sel);
+  const hipStream_t s2 = as_stream(stream_spec);
+  const int kc = mode == PRR_MODE_SERIALIZED ? 0 : a->k_spec_cur;
+  const int kn = mode == PRR_MODE_SERIALIZED ? 0 : a->k_spec_next;
+  PRR_REQUIRE(kc >= 0 && kn >= 0, "decode_step: negative k_spec");
+
+  if (mode != PRR_MODE_TWO_STREAM) {
+    if (kc > 0) PRR_TRY(prr_speculate(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->pred_cur, kc,
+                                      a->partials, s1));
+    PRR_TRY(prr_score_select(shape, a->q, a->summaries, a->top_k, a->scores, a->sel_idx, s1));
+    PRR_TRY(prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
+                             kc, a->partials, a->out, a->n_missed, a->workspace, s1));
+    if (kn > 0) PRR_TRY(prr_ema_predict(shape, a->scores, a->ema, a->alpha, a->first_step, kn, a->pred_next, s1));
+    return PRR_OK;
+  }
+  PRR_TRY(hip_ok(hipEventRecord(ctx->q_ready, s1), "decode_step: record q_ready"));
+  PRR_TRY(hip_ok(hipStreamWaitEvent(s2, ctx->q_ready, 0), "decode_step: wait q_ready"));
+  if (kc > 0) PRR_TRY(prr_speculate(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->pred_cur, kc,
+                                    a->partials, s2));
+  PRR_TRY(hip_ok(hipEventRecord(ctx->spec_done, s2), "decode_step: record spec_done"));
+  PRR_TRY(prr_score_select(shape, a->q, a->summaries, a->top_k, a->scores, a->sel_idx, s1));
+  PRR_TRY(hip_ok(hipEventRecord(ctx->sel_done, s1), "decode_step: record sel_done"));
+  PRR_TRY(hip_ok(hipStreamWaitEvent(s1, ctx->spec_done, 0), "decode_step: wait spec_done"));
+  PRR_TRY(prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
+                           kc, a->partials, a->out, a->n_missed, a->workspace, s1));
+  if (kn > 0) {
+    PRR_TRY(hip_ok(hipStreamWaitEvent(s2, ctx->sel_done, 0), "decode_step: wait sel_done"));
+    PRR_TRY(prr_ema_predict(shape, a->scores, a->ema, a->alpha, a->first_step, kn, a->pred_next, s2));
+  }
+  if (join) {
+    PRR_TRY(hip_ok(hipEventRecord(ctx->spec_tail, s2), "decode_step: record spec_tail"));
+    PRR_TRY(hip_ok(hipStreamWaitEvent(s1, ctx->spec_tail, 0), "decode_step: wait spec_tail"));
+  }
+  return PRR_OK;
+}
+
+prr_status prr_trace_create(prr_trace** out, int32_t capacity) {
+  if (!out || capacity < 1) { set_error("trace_create: null pointer or capacity < 1"); return PRR_EINVAL; }
+  auto* t = new (std::nothrow) prr_trace{};
+  if (!t) { set_error("trace_create: out of host memory"); return PRR_EINVAL; }
+  t->capacity = capacity;
+  for (int k = 0; k < PRR_KERNEL_COUNT; ++k) {
+    t->ev0[k] = new (std::nothrow) hipEvent_t[capacity]();
+    t->ev1[k] = new (std::nothrow) hipEvent_t[capacity]();
+    if (!t->ev0[k] || !t->ev1[k]) { prr_trace_destroy(t); set_error("trace_create: out of host memory"); return PRR_EINVAL; }
+    for (int i = 0; i < capacity; ++i) {
+      if (hipEventCreate(&t->ev0[k][i]) != hipSuccess || hipEventCreate(&t->ev1[k][i]) != hipSuccess) {
+        prr_trace_destroy(t);
+        set_error("trace_create: hipEventCreate failed");
+        return PRR_ELAUNCH;
+      }
+    }
+  }
+  *out = t;
+  return PRR_OK;
+}
+
+void prr_trace_destroy(prr_trace* t) {
+  if (!t) return;
+  prr_trace* expected = t;
+  g_trace.compare_exchange_strong(expected, nullptr);
+  for (int k = 0; k < PRR_KERNEL_COUNT; ++k) {
+    for (int i = 0; i < t->capacity; ++i) {
+      if (t->ev0[k] && t->ev0[k][i]) (void)hipEventDestroy(t->ev0[k][i]);
+      if (t->ev1[k] && t->ev1[k][i]) (void)hipEventDestroy(t->ev1[k][i]);
+    }
+    delete[] t->ev0[k];
+    delete[] t->ev1[k];
+  }
+  delete t;
+}
+
+prr_status prr_trace_enable(prr_trace* t, uint32_t mask) {
+  if (!t || mask == 0) { g_trace.store(nullptr, std::memory_order_release); return PRR_OK; }
+  t->mask = mask;
+  for (int k = 0; k < PRR_KERNEL_COUNT; ++k) t->count[k] = 0;
+  g_trace.store(t, std::memory_order_release);
+  return PRR_OK;
+}
+
+int32_t prr_trace_read(prr_trace* t, int32_t kernel, float* ms_out, int32_t cap) {
+  if (!t || kernel < 0 || kernel >= PRR_KERNEL_COUNT || (cap > 0 && !ms_out)) {
+    set_error("trace_read: invalid argument");
+    return PRR_EINVAL;
+  }
+  const int n = t->count[kernel] < cap ? t->count[kernel] : cap;
+  for (int i = 0; i < n; ++i) {
+    if (hipEventSynchronize(t->ev1[kernel][i]) != hipSuccess ||
+        hipEventElapsedTime(&ms_out[i], t->ev0[kernel][i], t->ev1[kernel][i]) != hipSuccess) {
+      set_error("trace_read: event query failed");
+      return PRR_ELAUNCH;
+    }
+  }
+  return n;
+}
+
+prr_status prr_flush_write(void* buf, size_t bytes, void* stream) {
+  PRR_REQUIRE(buf && bytes % 16 == 0, "flush_write: null buffer or size not a multiple of 16");
+  return launch_flush(buf, bytes, as_stream(stream));
+}
+
+prr_status prr_stream_read(const void* buf, size_t bytes, float* sink, void* stream) {
+  PRR_REQUIRE(buf && sink && bytes % 16 == 0, "stream_read: null pointer or size not a multiple of 16");
+  return launch_stream_read(buf, bytes, sink, as_stream(stream));
+}
+
+const char* prr_status_string(prr_status s) {
+  switch (s) {
+    case PRR_OK: return "PRR_OK";
+    case PRR_EINVAL: return "PRR_EINVAL: invalid argument";
+    case PRR_EUNSUPPORTED: return "PRR_EUNSUPPORTED: unsupported shape or dtype";
+    case PRR_ELAUNCH: return "PRR_ELAUNCH: HIP runtime error";
+  }
+  return "unknown prr_status";
+}
+
+const char* prr_last_error(void) { return g_err; }
+
+const char* prr_version(void) { return "libprr 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// prr_launch.h — host-side declarations shared by the kernel translation units and the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/prr.h"
+
+namespace prr {
+
+// Thread-local error message for prr_last_error().
+void set_error(const char* fmt, ...);
+// Checks hipGetLastError() after a launch; on failure records the message and returns PRR_ELAUNCH.
+prr_status check_launch(const char* what);
+
+// Record of a partial attention state for one (b, g, slot): m[G] (log2 units), l[G], padding to a multiple of 4
+// floats, then O[G][D]. Records are 16-byte aligned.
+__host__ __device__ constexpr int rec_ml(int G) { return (2 * G + 3) & ~3; }
+__host__ __device__ constexpr int64_t rec_floats(int G, int D) { return (int64_t)rec_ml(G) + (int64_t)G * D; }
+
+// Kernel tracing hooks: record the armed trace's start/end events around a launch of kernel `kid` on `stream`.
+void trace_begin(int kid, hipStream_t stream);
+void trace_end(int kid, hipStream_t stream);
+
+prr_status launch_summaries(const prr_shape& s, const void* k_cache, const int32_t* table, const int32_t* ids,
+                            int64_t n_jobs, void* summ, hipStream_t stream);
+prr_status launch_score(const prr_shape& s, const void* q, const void* summ, float* scores, hipStream_t stream);
+prr_status launch_topk(const prr_shape& s, const float* values, float* ema, float alpha, int first, int k,
+                       int32_t* out_idx, hipStream_t stream);
+prr_status launch_speculate(const prr_shape& s, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* table, const int32_t* pred, int k_spec, float* partials,
+                            hipStream_t stream);
+prr_status launch_repair(const prr_shape& s, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* table, const int32_t* sel, int top_k, const int32_t* pred, int k_spec,
+                         const float* partials, float* out, int32_t* n_missed, void* workspace, hipStream_t stream);
+size_t repair_workspace_bytes(const prr_shape& s, int top_k);
+prr_status launch_flush(void* buf, size_t bytes, hipStream_t stream);
+prr_status launch_stream_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
+
+}  // namespace prr

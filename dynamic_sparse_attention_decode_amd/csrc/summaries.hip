@@ -1,0 +1,80 @@
+// Quest block summaries (PRR reference list, Quest): per (sequence b, KV head g, block n) the elementwise min and
+// max of the block's keys, read through the paged block table (PagedAttention, PRR reference list).
+//
+// One wave per block: each load instruction reads 4 token rows (16 lanes x 16 B per 256-byte row); lanes keep
+// running min/max, then fold the 4 rows with permlane swaps. Rows 0 and 1 of the wave write the min and max rows.
+// Pure HBM streaming: reads bs * 256 B per block, writes 512 B.
+#include "prr_device.h"
+#include "prr_launch.h"
+
+namespace prr {
+
+template <int DT>
+__global__ __launch_bounds__(256) void summaries_kernel(const uint8_t* __restrict__ k_cache,
+                                                        const int32_t* __restrict__ table,
+                                                        const int32_t* __restrict__ ids, int64_t n_jobs,
+                                                        int64_t n_total, uint8_t* __restrict__ summ, int Hkv, int N,
+                                                        int bs, int page, int pps) {
+  using V = Vec<DT>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t job = (int64_t)blockIdx.x * 4 + wave;
+  if (job >= n_jobs) return;
+  const int64_t flat = ids ? (int64_t)ids[job] : job;   // (b * Hkv + g) * N + n
+  if (flat < 0 || flat >= n_total) return;                 // ids outside the summaries are ignored
+  const int n = (int)(flat % N);
+  const int64_t bg = flat / N;
+  const int g = (int)(bg % Hkv);
+  const int b = (int)(bg / Hkv);
+  const int row = lane >> 4, col = lane & 15;
+  const int32_t* trow = table + (int64_t)b * pps;
+
+  float mn[V::n], mx[V::n];
+#pragma unroll
+  for (int e = 0; e < V::n; ++e) { mn[e] = __builtin_huge_valf(); mx[e] = -__builtin_huge_valf(); }
+
+  const int tok0 = n * bs;
+#pragma unroll 4
+  for (int t = 0; t < bs; t += 4) {
+    const int tok = tok0 + t + row;
+    const int64_t phys = trow[tok / page];
+    const uint8_t* p = k_cache + ((phys * Hkv + g) * page + (tok % page)) * (int64_t)kRowBytes + col * 16;
+    float x[V::n];
+    V::to_f32(ld16(p), x);
+#pragma unroll
+    for (int e = 0; e < V::n; ++e) { mn[e] = fminf(mn[e], x[e]); mx[e] = fmaxf(mx[e], x[e]); }
+  }
+#pragma unroll
+  for (int e = 0; e < V::n; ++e) {
+    Pair p = swap16(mn[e], mn[e]); mn[e] = fminf(p.a, p.b);
+    p = swap32(mn[e], mn[e]);      mn[e] = fminf(p.a, p.b);
+    p = swap16(mx[e], mx[e]);      mx[e] = fmaxf(p.a, p.b);
+    p = swap32(mx[e], mx[e]);      mx[e] = fmaxf(p.a, p.b);
+  }
+  if (row < 2) {
+    uint8_t* dst = summ + (flat * 2 + row) * (int64_t)kRowBytes + col * 16;
+    st16(dst, V::from_f32(row == 0 ? mn : mx));
+  }
+}
+
+prr_status launch_summaries(const prr_shape& s, const void* k_cache, const int32_t* table, const int32_t* ids,
+                            int64_t n_jobs, void* summ, hipStream_t stream) {
+  if (n_jobs == 0) return PRR_OK;
+  const dim3 grid((unsigned)((n_jobs + 3) / 4)), block(256);
+  const auto* kc = static_cast<const uint8_t*>(k_cache);
+  auto* sm = static_cast<uint8_t*>(summ);
+  const int64_t n_total = (int64_t)s.batch * s.n_kv_heads * s.n_blocks;
+  trace_begin(PRR_KERNEL_SUMMARIES, stream);
+  switch (s.dtype) {
+    case kF32: summaries_kernel<kF32><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads, s.n_blocks,
+                                                                  s.block_size, s.page_size, s.pages_per_seq); break;
+    case kBF16: summaries_kernel<kBF16><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads,
+                                                                    s.n_blocks, s.block_size, s.page_size,
+                                                                    s.pages_per_seq); break;
+    default: summaries_kernel<kF16><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads, s.n_blocks,
+                                                                s.block_size, s.page_size, s.pages_per_seq); break;
+  }
+  trace_end(PRR_KERNEL_SUMMARIES, stream);
+  return check_launch("build_summaries");
+}
+
+}  // namespace prr

@@ -1,0 +1,198 @@
+/*
+ * prr.h — C ABI of libprr: one decode step of PRR's dynamic sparse attention for one attention layer on one
+ * MI355X (gfx950).
+ *
+ * Method: "Predict, Reuse, and Repair: Accelerating Dynamic Sparse Attention for Long-Context LLM Decoding"
+ * (arXiv 2606.30389). PRR abstract: decoding attends to the top-K KV blocks of each query; an EMA-based predictor
+ * forecasts those blocks, attention is speculated over them while the true selection is in flight, and once the
+ * true set is known the missed blocks are folded into the partial attention state with online-softmax statistics.
+ * PRR summary page (Key findings, Contributions): the repair covers exactly the missed blocks, so the result equals
+ * standard DSA over the true top-K set.
+ *
+ * Conventions for every entry point
+ *  - All tensor arguments are DEVICE pointers to contiguous row-major buffers that the caller allocates, owns and
+ *    frees. The library never allocates device memory, never synchronises the host, and launches only on the
+ *    stream(s) it is given (a hipStream_t passed as void*; NULL = the null stream).
+ *  - Calls are asynchronous: they validate their arguments on the host, enqueue kernels and return. A non-zero
+ *    status means nothing was enqueued (PRR_EINVAL, PRR_EUNSUPPORTED) or a launch failed (PRR_ELAUNCH);
+ *    prr_last_error() then gives a thread-local message. Device faults surface at the caller's next sync.
+ *  - Inputs must be finite (no NaN/Inf in q, K, V).
+ *  - No state lives in the library: the EMA vector, index lists and partials are caller buffers, so any number of
+ *    layers (each with its own buffers) may share the library.
+ *
+ * Notation: B batch, Hq query heads, Hkv KV heads, G = Hq / Hkv (query head h uses KV head h / G), D head_dim,
+ * bs block_size (tokens per selection block), N n_blocks = ctx / bs, K top_k, K' k_spec (speculation budget).
+ * The storage dtype (prr_dtype) applies to q, the K/V caches and the summaries; all scores, EMA values, partials
+ * and outputs are fp32.
+ *
+ * Layouts
+ *  q          [B, Hq, D]
+ *  k/v cache  [n_pages, Hkv, page_size, D]   (PagedAttention, PRR reference list); token i of sequence b lives in
+ *             physical page block_table[b, i / page_size], row i % page_size
+ *  block_table int32 [B, pages_per_seq], pages_per_seq = N * bs / page_size
+ *  summaries  [B, Hkv, N, 2, D]   row 0 = elementwise min of the block's keys, row 1 = max (Quest)
+ *  scores     f32 [B, Hkv, N]
+ *  ema        f32 [B, Hkv, N]
+ *  sel_idx    int32 [B, Hkv, K]   ascending block ids of the true top-K set
+ *  pred_idx   int32 [B, Hkv, K']  ascending block ids of the predicted set
+ *  partials   f32 buffer of prr_partials_bytes(): one record per (b, kv head, predicted slot), layout
+ *             [B, Hkv, K'] x {m[G], l[G], zero padding to a multiple of 4 floats, O[G][D]}; m is the block's
+ *             largest logit in log2 units (softmax_scale * q.k * log2 e), l = sum of 2^(z - m), O = sum of
+ *             2^(z - m) v (unnormalised); records are 16-byte aligned
+ *  out        f32 [B, Hq, D]      softmax attention over the tokens of the true top-K blocks
+ *  n_missed   int32 [B, Hkv]      |T \ P| of the last repair
+ */
+#ifndef PRR_H_
+#define PRR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PRR_OK = 0,
+  PRR_EINVAL = -1,        /* a null pointer, a size out of range or inconsistent shapes */
+  PRR_EUNSUPPORTED = -2,  /* a valid but unsupported combination (dtype x head_dim, group size) */
+  PRR_ELAUNCH = -3        /* the HIP runtime reported an error when enqueuing */
+} prr_status;
+
+typedef enum { PRR_F32 = 0, PRR_BF16 = 1, PRR_F16 = 2 } prr_dtype;
+
+/* Shape of one attention layer's decode state. Supported: (dtype F32, head_dim 64) and (dtype BF16 or F16,
+ * head_dim 128) — one 256-byte row per token; group size G in {1, 2, 4, 8}; block_size a multiple of page_size and
+ * of 4; 1 <= n_blocks <= 65536 (and n_blocks <= 32768 for the top-K kernels). */
+typedef struct {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim;
+  int32_t block_size, page_size;
+  int32_t n_blocks, pages_per_seq;
+  int32_t dtype;        /* prr_dtype */
+  float softmax_scale;  /* typically 1/sqrt(head_dim) */
+} prr_shape;
+
+/* Quest block summaries (PRR reference list, Quest): for every (b, kv head g, block n), the elementwise min and max
+ * over the block's tokens of the keys, read through the page table; exact in every dtype.
+ * block_ids: NULL rebuilds every block; otherwise n_block_ids flat ids f = (b * Hkv + g) * N + n (e.g. the blocks
+ * whose keys changed) are rebuilt and the rest of `summaries` is left untouched. */
+prr_status prr_build_summaries(const prr_shape* shape, const void* k_cache, const int32_t* block_table,
+                               const int32_t* block_ids, int32_t n_block_ids, void* summaries, void* stream);
+
+/* Query-aware block scores and exact top-K selection (PRR abstract: attend only to the top-K blocks relevant to
+ * each query). scores[b,g,n] = sum over the query heads h of KV head g and dims d of
+ * max(q[b,h,d]*kmin[d], q[b,h,d]*kmax[d]) (fp32); sel_idx[b,g,:] = the top_k largest scores, ties to the lower
+ * block index, ascending. Requires 1 <= top_k <= N. */
+prr_status prr_score_select(const prr_shape* shape, const void* q, const void* summaries, int32_t top_k,
+                            float* scores, int32_t* sel_idx, void* stream);
+
+/* EMA score predictor (PRR abstract: "lightweight EMA-based predictor"): ema = scores when first_step != 0, else
+ * ema = alpha * ema + (1 - alpha) * scores (in place); then pred_idx_next[b,g,:] = top-k_spec of ema, ties to the
+ * lower index, ascending — the predicted set for the next decode step. Requires 1 <= k_spec <= N. */
+prr_status prr_ema_predict(const prr_shape* shape, const float* scores, float* ema, float alpha, int32_t first_step,
+                           int32_t k_spec, int32_t* pred_idx_next, void* stream);
+
+/* Speculative attention (PRR abstract: speculate the attention over the predicted blocks while selection is in
+ * flight): for every (b, g) and predicted slot j < k_spec, with n = pred_idx[b,g,j] and each query head h of the
+ * group, z_i = softmax_scale * q[b,h] . k_i over the block's tokens; the block's partial state m = max z,
+ * l = sum exp(z - m), O = sum exp(z - m) v_i is stored as the record (b, g, j) of `partials`, in the base-2 form
+ * given under Layouts (m2 = m * log2 e, the same l and O). k_spec == 0 enqueues nothing. */
+prr_status prr_speculate(const prr_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* pred_idx, int32_t k_spec, float* partials,
+                         void* stream);
+
+/* Repair and merge (PRR abstract: repair the missed blocks once the true set is known; folds them into the partial
+ * state with online-softmax statistics). For every (b, g): the blocks of T = sel_idx[b,g,:] that are in
+ * P = pred_idx[b,g,:k_spec] reuse their speculated partials; the missed blocks M = T \ P are computed here; blocks of
+ * P \ T never enter. out[b,h] = O / l of the merged state; n_missed[b,g] = |M|. k_spec == 0 (or pred_idx NULL)
+ * computes attention over all of T (the serialized select-then-attend path). `workspace` holds
+ * prr_workspace_bytes() bytes of scratch (no initialisation needed). */
+prr_status prr_repair_merge(const prr_shape* shape, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, const int32_t* sel_idx, int32_t top_k,
+                            const int32_t* pred_idx, int32_t k_spec, const float* partials, float* out,
+                            int32_t* n_missed, void* workspace, void* stream);
+
+/* Bytes of the partials buffer for a speculation budget k_spec (0 for k_spec == 0). */
+size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec);
+/* Bytes of the repair workspace for top_k. */
+size_t prr_workspace_bytes(const prr_shape* shape, int32_t top_k);
+
+/* ---- one decode step on two streams (the runtime around the calls above) ------------------------------------ */
+
+typedef enum {
+  PRR_MODE_SERIALIZED = 0,  /* stream_sel: score_select -> repair_merge over all of T (no prediction)            */
+  PRR_MODE_ONE_STREAM = 1,  /* stream_sel: speculate -> score_select -> repair_merge -> ema_predict                */
+  PRR_MODE_TWO_STREAM = 2   /* stream_spec: speculate || stream_sel: score_select; then repair_merge on stream_sel
+                               while ema_predict runs on stream_spec                                            */
+} prr_mode;
+
+typedef struct {
+  const void* q; const void* k_cache; const void* v_cache; const int32_t* block_table; const void* summaries;
+  float* scores;               /* written by score_select, read by ema_predict; double-buffer it across steps   */
+  int32_t* sel_idx;
+  float* ema;
+  const int32_t* pred_cur;     /* P_t (k_spec_cur entries; ignored when k_spec_cur == 0)                          */
+  int32_t* pred_next;          /* P_{t+1} (k_spec_next entries), written by ema_predict                          */
+  float* partials;             /* speculation partials for P_t; double-buffer it across steps                   */
+  float* out; int32_t* n_missed; void* workspace;
+  int32_t top_k, k_spec_cur, k_spec_next, first_step;
+  float alpha;
+} prr_step_args;
+
+/* Opaque host object holding the events that order the two streams (no device memory). */
+typedef struct prr_step_ctx prr_step_ctx;
+prr_status prr_step_ctx_create(prr_step_ctx** out);
+void prr_step_ctx_destroy(prr_step_ctx* ctx);
+
+/* Enqueue one PRR decode step. Two-stream order (PRR abstract: speculation runs while selection is in flight):
+ *   stream_sel:  [record q-ready] score_select [record sel-done] [wait spec-done] repair_merge
+ *   stream_spec: [wait q-ready] speculate(P_t) [record spec-done] [wait sel-done] ema_predict -> P_{t+1}
+ * `out` is complete on stream_sel when the call's work there finishes; P_{t+1} is complete on stream_spec, and the
+ * next call's speculation is ordered after it. Pass join != 0 to make stream_sel also wait for stream_spec's work
+ * (needed at the end of a graph capture). In PRR_MODE_ONE_STREAM and PRR_MODE_SERIALIZED only stream_sel is used. */
+prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_step_args* args, int32_t mode,
+                           int32_t join, void* stream_sel, void* stream_spec);
+
+/* Profiling-guided speculation budget (PRR abstract; PRR summary page, Limitations: polynomial regression outside
+ * the profiled grid). Returns the largest kspec_grid[i] with t_spec[i] <= t_sel(n_target), where t_sel(n_target)
+ * is t_sel[j] if n_grid[j] == n_target, else a least-squares polynomial of degree poly_degree (clamped to
+ * n_pts_sel - 1, at most 4) fitted to (n_grid, t_sel). Returns 0 when no positive budget qualifies and -1 on
+ * invalid arguments (null arrays, n_pts_sel < 1). Host-only; safe without a GPU. */
+int32_t prr_choose_budget(const double* n_grid, const double* t_sel, int32_t n_pts_sel, const double* kspec_grid,
+                          const double* t_spec, int32_t n_pts_spec, double n_target, int32_t poly_degree);
+
+/* ---- kernel tracing ------------------------------------------------------------------------------------------ */
+/* Per-kernel launch timing with HIP events recorded on the stream each kernel is launched on, for measuring the
+ * achieved bandwidth of one kernel inside a running decode loop. A trace holds `capacity` event pairs per kernel
+ * id; while enabled (process-wide, one trace at a time) every launch of a kernel in `kernel_mask` (bit i = kernel
+ * id i) records an event immediately before and after it, until that kernel's pool is full. Reading synchronises
+ * on the events. */
+typedef enum {
+  PRR_KERNEL_SUMMARIES = 0, PRR_KERNEL_SCORE = 1, PRR_KERNEL_SELECT_TOPK = 2, PRR_KERNEL_EMA_TOPK = 3,
+  PRR_KERNEL_SPECULATE = 4, PRR_KERNEL_REPAIR = 5, PRR_KERNEL_FINALIZE = 6, PRR_KERNEL_COUNT = 7
+} prr_kernel_id;
+typedef struct prr_trace prr_trace;
+prr_status prr_trace_create(prr_trace** out, int32_t capacity);
+void prr_trace_destroy(prr_trace* trace);
+/* Enable `trace` for the kernels in kernel_mask (0 or a NULL trace disables tracing); resets its counters. */
+prr_status prr_trace_enable(prr_trace* trace, uint32_t kernel_mask);
+/* Copy up to `cap` per-launch durations (ms) of `kernel` into ms_out; returns the count (>= 0) or a negative
+ * prr_status. Synchronises on the recorded events. */
+int32_t prr_trace_read(prr_trace* trace, int32_t kernel, float* ms_out, int32_t cap);
+
+/* ---- benchmark helpers ----------------------------------------------------------------------------------- */
+/* Write `bytes` (multiple of 16) of `buf` with a streaming kernel (evicts caches before cold-cache timing). */
+prr_status prr_flush_write(void* buf, size_t bytes, void* stream);
+/* Stream-read `bytes` (multiple of 16) of `buf`, writing one float per workgroup to `sink` (>= 65536 floats);
+ * measures the achievable read bandwidth. */
+prr_status prr_stream_read(const void* buf, size_t bytes, float* sink, void* stream);
+
+const char* prr_status_string(prr_status s);
+const char* prr_last_error(void);
+/* Library version string. */
+const char* prr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PRR_H_ */

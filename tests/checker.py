@@ -1,0 +1,43 @@
+"""Comparison rules between the HIP path and the fp64 oracle.
+
+Selection (several answers can be correct at near-ties): a GPU set T_g of K distinct ascending ids is valid when its
+smallest oracle score is at least the largest excluded oracle score minus eps = rel * |s_(K)|. Where the oracle's
+relative gap at the K-th/(K+1)-th boundary exceeds rel, the only valid set is the oracle's own, so validity is then
+bit-exact equality. The GPU computes scores in fp32 (relative error ~1e-6), far inside rel = 1e-4.
+
+Outputs are compared with the oracle's attention over the GPU's own (validated) set, element by element, with the
+stated max-abs tolerance: 1e-5 for fp32 storage, 2e-2 for bf16/fp16 storage.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import prr_oracle as O
+
+REL_GAP = 1e-4
+TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2}
+
+
+def check_selection(gpu_idx, oracle_scores, k: int, rel: float = REL_GAP):
+    """Returns (exact_required, banded_ok). Raises AssertionError if the GPU set is invalid."""
+    g = np.asarray(gpu_idx, dtype=np.int64)
+    s = np.asarray(oracle_scores, dtype=np.float64)
+    assert g.shape == (k,), g.shape
+    assert np.all(np.diff(g) > 0), "indices not strictly ascending"
+    assert g.min() >= 0 and g.max() < len(s), "index out of range"
+    ref = O.top_k(s, k)
+    _, _, gap = O.boundary_gap(s, k)
+    if gap > rel:
+        assert np.array_equal(g, ref), f"selection differs where the gap {gap:.3e} > {rel}: {set(g) ^ set(ref)}"
+        return True
+    eps = rel * abs(O.boundary_gap(s, k)[0])
+    mask = np.zeros(len(s), dtype=bool)
+    mask[g] = True
+    inside_min = s[mask].min()
+    outside_max = s[~mask].max() if (~mask).any() else -np.inf
+    assert inside_min >= outside_max - eps, (inside_min, outside_max, eps)
+    return False
+
+
+def max_abs(a, b) -> float:
+    return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64))))

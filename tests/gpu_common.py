@@ -1,0 +1,75 @@
+"""Shared helpers of the GPU parity tests: reduced workloads, oracle views of the generated inputs."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from dynamic_sparse_attention_decode_amd import _lib as L
+from dynamic_sparse_attention_decode_amd.inputs import WORKLOADS, Workload
+
+requires_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+
+
+def small(name: str) -> Workload:
+    """Reduced versions of the five workloads: the oracle finishes them in seconds, yet they span several tiles of
+    every kernel and end on ragged tails (block counts, K and K' that are not multiples of the tile sizes)."""
+    w = WORKLOADS[name]
+    if name == "tiny_f32_4k":
+        return w
+    if name == "llama3_8b_32k":
+        return w.replace(ctx=w.block_size * 250, top_k=30, k_spec=(37,), steps=10, hot_blocks=12)
+    if name == "long_ctx_131k_b4":
+        return w.replace(batch=2, ctx=w.block_size * 130, top_k=14, k_spec=(19,), steps=10, hot_blocks=10)
+    if name == "paged_b32_64k":
+        return w.replace(batch=3, ctx=w.block_size * 300, top_k=33, k_spec=(33,), steps=8)
+    if name == "million_token":
+        return w.replace(ctx=w.block_size * 2100, top_k=61, k_spec=(0, 29, 61, 93), steps=8, hot_blocks=40)
+    raise KeyError(name)
+
+
+SMALL = ["tiny_f32_4k", "llama3_8b_32k", "long_ctx_131k_b4", "paged_b32_64k", "million_token"]
+
+
+def shape_of(w: Workload) -> L.Shape:
+    return L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, w.n_blocks,
+                        {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[w.dtype], w.scale)
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+class OracleView:
+    """fp64 host copies of one (b, g) row's logical keys/values, gathered through the page table by the oracle."""
+
+    def __init__(self, inp):
+        self.inp = inp
+        self.w = inp.w
+        self.table = inp.table_np
+        self._k = {}
+        self._v = {}
+
+    def _cache_row(self, cache: torch.Tensor, b: int, g: int) -> np.ndarray:
+        from oracle import prr_oracle as O
+        pages = torch.as_tensor(self.table[b], device=cache.device, dtype=torch.long)
+        sub = cache[pages, g].float().cpu().numpy()            # [pps, page, D] (plain page copy)
+        local_table = np.arange(len(self.table[b]), dtype=np.int64)[None, :]
+        return O.logical_tokens(sub[:, None], local_table, 0, 0, self.w.ctx)
+
+    def keys(self, b: int, g: int) -> np.ndarray:
+        if (b, g) not in self._k:
+            self._k[(b, g)] = self._cache_row(self.inp.k_cache, b, g)
+        return self._k[(b, g)]
+
+    def values(self, b: int, g: int) -> np.ndarray:
+        if (b, g) not in self._v:
+            self._v[(b, g)] = self._cache_row(self.inp.v_cache, b, g)
+        return self._v[(b, g)]
+
+    def invalidate_keys(self):
+        self._k.clear()
+
+    def q_group(self, t: int, b: int, g: int) -> np.ndarray:
+        G = self.w.group
+        return np64(self.inp.q[t, b, g * G:(g + 1) * G])

@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every entry point that include/prr.h declares, and validates arguments on the host
+(no device call is made: these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dynamic_sparse_attention_decode_amd import _lib as L
+from oracle import prr_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "prr.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(prr_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.lib()
+    declared = _declared()
+    assert set(declared) == set(L.EXPORTS), (set(declared) ^ set(L.EXPORTS))
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert L.version().startswith("libprr")
+
+
+def _shape(**kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, block_size=16, page_size=16, n_blocks=2048,
+                dtype=L.BF16)
+    base.update(kw)
+    return L.make_shape(**base)
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n_q_heads=30), L.lib and -1),           # Hq % Hkv != 0
+    (dict(n_q_heads=24, n_kv_heads=2), -2),       # G = 12 unsupported
+    (dict(head_dim=64), -2),                      # bf16 x 64 unsupported
+    (dict(dtype=L.F32), -2),                      # f32 x 128 unsupported
+    (dict(dtype=7), -1),                          # unknown dtype
+    (dict(block_size=18, page_size=2), -2),       # block_size % 4 != 0
+    (dict(block_size=16, page_size=32), -1),      # block_size % page_size != 0
+    (dict(n_blocks=0), -1),
+    (dict(n_blocks=40000), -2),                   # top-K kernels support N <= 32768
+])
+def test_shape_validation(bad, code):
+    lib = L.lib()
+    s = _shape(**bad)
+    nz = ctypes.c_void_p(16)
+    st = lib.prr_score_select(ctypes.byref(s), nz, nz, 8, nz, nz, None)
+    assert st == code, (bad, st, lib.prr_last_error())
+    assert lib.prr_last_error()
+
+
+def test_argument_validation_without_launch():
+    lib = L.lib()
+    s = _shape()
+    nz = ctypes.c_void_p(16)
+    assert lib.prr_score_select(ctypes.byref(s), None, nz, 8, nz, nz, None) == -1          # null q
+    assert lib.prr_score_select(ctypes.byref(s), nz, nz, 0, nz, nz, None) == -1            # K < 1
+    assert lib.prr_score_select(ctypes.byref(s), nz, nz, 2049, nz, nz, None) == -1         # K > N
+    assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 0.9, 0, 0, nz, None) == -1        # K' < 1
+    assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 1.5, 0, 8, nz, None) == -1        # alpha > 1
+    assert lib.prr_speculate(ctypes.byref(s), nz, nz, nz, nz, nz, -1, nz, None) == -1      # K' < 0
+    assert lib.prr_speculate(ctypes.byref(s), None, None, None, None, None, 0, None, None) == 0   # K' = 0: no-op
+    assert lib.prr_repair_merge(ctypes.byref(s), nz, nz, nz, nz, nz, 8, None, 4, None, nz, nz, nz, None) == -1
+    assert lib.prr_build_summaries(None, nz, nz, None, 0, nz, None) == -1
+    assert lib.prr_decode_step(None, ctypes.byref(s), None, 2, 0, None, None) == -1
+    assert lib.prr_flush_write(nz, 17, None) == -1
+    assert b"null" in lib.prr_status_string(-1).lower() or lib.prr_status_string(-1)
+
+
+def test_buffer_sizes():
+    s = _shape()
+    G, D = 4, 128
+    rec = (2 * G + 3) // 4 * 4 + G * D
+    assert L.partials_bytes(s, 160) == 1 * 8 * 160 * rec * 4
+    assert L.partials_bytes(s, 0) == 0
+    assert L.workspace_bytes(s, 128) > 0
+    s1 = _shape(n_q_heads=8, n_kv_heads=8)   # G = 1: records padded to 16 bytes
+    assert L.partials_bytes(s1, 3) == 8 * 3 * (4 + 128) * 4
+
+
+def test_budget_chooser_matches_oracle_and_closed_forms():
+    n_grid = [256, 512, 2048, 4096, 8192]
+    ks = [0, 64, 128, 192, 256, 320, 384]
+    t_spec = [1 + 0.05 * k for k in ks]
+    t_lin = [2 + 0.01 * n for n in n_grid]
+    t_quad = [1 + n * n / 1e6 for n in n_grid]
+    assert L.choose_budget(n_grid, t_lin, ks, t_spec, 1000) == 192
+    assert L.choose_budget(n_grid, t_lin, ks, t_spec, 4096) == 384
+    assert L.choose_budget(n_grid, t_quad, ks, t_spec, 3000) == 128
+    assert L.choose_budget(n_grid, t_lin, ks, [100.0] * len(ks), 1000) == 0
+    import numpy as np
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        ts = sorted(rng.uniform(1, 50, size=5))
+        tp = sorted(rng.uniform(0, 60, size=len(ks)))
+        nt = float(rng.uniform(100, 9000))
+        for deg in (1, 2, 3):
+            a = L.choose_budget(n_grid, ts, ks, tp, nt, deg)
+            b = O.choose_budget(n_grid, ts, ks, tp, nt, deg)
+            if a != b:   # only a near-tie between fitted time and a table entry may differ
+                tt = np.polyval(np.polyfit(n_grid, ts, deg), nt)
+                k = max(a, b)
+                assert abs(tp[ks.index(k)] - tt) < 1e-9 * max(1, abs(tt))

@@ -1,0 +1,124 @@
+"""Whole decode runs through the two-stream step (libprr's prr_decode_step) against the fp64 oracle, on reduced
+workloads: every step's selection (tie-band rule), output (stated tolerance), missed count, and the predictor's
+sets; the three modes; EMA save and restore."""
+import numpy as np
+import pytest
+import torch
+
+from dynamic_sparse_attention_decode_amd.inputs import make_inputs
+from dynamic_sparse_attention_decode_amd.runtime import PRRLayer
+from oracle import prr_oracle as O
+from tests.checker import TOL, check_selection, max_abs
+from tests.gpu_common import SMALL, OracleView, np64, requires_gpu, shape_of, small
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def run_layer(w, inp, k_spec, mode, steps=None, check=True, ov=None):
+    """Run the layer over the steps; returns per-step (out, sel, pred, n_missed) host copies and stats."""
+    steps = w.steps if steps is None else steps
+    layer = PRRLayer(shape_of(w), w.top_k, k_spec, w.alpha, mode=mode)
+    layer.build(inp.k_cache, inp.v_cache, inp.table)
+    hist = []
+    ema_ref = {}
+    for t in range(steps):
+        ids = inp.drift(t)
+        if len(ids):
+            layer.rebuild_blocks(torch.as_tensor(ids, device="cuda"))
+            if ov is not None:
+                ov.invalidate_keys()
+        out = layer.step(inp.q[t].contiguous())
+        torch.cuda.synchronize()
+        hist.append(dict(out=np64(out), sel=layer.sel_idx.cpu().numpy().copy(),
+                         pred=None if (t == 0 or layer.k_spec == 0) else layer.pred_current.cpu().numpy().copy(),
+                         nm=layer.n_missed.cpu().numpy().copy(), ema=np64(layer.ema)))
+        if check:
+            _check_step(w, ov, t, hist[-1], layer.k_spec, ema_ref)
+    layer.close()
+    return hist
+
+
+def _check_step(w, ov, t, h, k_spec, ema_ref):
+    G = w.group
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            qg = ov.q_group(t, b, g)
+            keys = ov.keys(b, g)
+            kmin, kmax = O.block_summaries(keys, w.block_size)
+            s = O.quest_scores(qg, kmin, kmax)
+            check_selection(h["sel"][b, g], s, w.top_k)
+            ref = O.attention_over_blocks(qg, keys, ov.values(b, g), h["sel"][b, g], w.block_size, w.scale)
+            e = max_abs(h["out"][b, g * G:(g + 1) * G], ref)
+            assert e <= TOL[w.dtype], (t, b, g, e)
+            # oracle EMA over the oracle's scores; the GPU's predicted set must be valid for it
+            prev = ema_ref.get((b, g)) if t > 0 else None
+            if t > 0 and k_spec:
+                check_selection(h["pred"][b, g], prev, k_spec)
+                missed = len(set(h["sel"][b, g]) - set(h["pred"][b, g]))
+                assert h["nm"][b, g] == missed
+            elif t == 0 or not k_spec:
+                assert h["nm"][b, g] == w.top_k
+            ema_ref[(b, g)] = O.ema_update(prev, s, w.alpha, t == 0)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_decode_two_stream_vs_oracle(name):
+    w = small(name)
+    for kp in w.k_spec:
+        print(f"[case] decode {name} K'={kp}", flush=True)
+        inp = make_inputs(w, device="cuda")
+        ov = OracleView(inp)
+        hist = run_layer(w, inp, kp, "prr_2stream", ov=ov)
+        if kp:
+            ov_steps = [len(set(h["sel"][b, g]) & set(h["pred"][b, g])) / w.top_k
+                        for h in hist[1:] for b in range(w.batch) for g in range(w.n_kv_heads)]
+            print(f"[result] {name} K'={kp}: mean overlap {np.mean(ov_steps):.3f}, "
+                  f"mean missed {np.mean([h['nm'].mean() for h in hist[1:]]):.2f}")
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_32k", "paged_b32_64k", "tiny_f32_4k"])
+def test_modes_agree(name):
+    """Two-stream and one-stream runs are bitwise identical (same kernels, same inputs); the serialized
+    select-then-attend run matches within the output tolerance."""
+    w = small(name)
+    kp = max(w.k_spec)
+    runs = {}
+    for mode in ("prr_2stream", "prr_1stream", "serialized"):
+        inp = make_inputs(w, device="cuda")
+        runs[mode] = run_layer(w, inp, kp, mode, check=False)
+    for a, b in zip(runs["prr_2stream"], runs["prr_1stream"]):
+        assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["sel"], b["sel"])
+        assert np.array_equal(a["nm"], b["nm"])
+    for a, b in zip(runs["prr_2stream"], runs["serialized"]):
+        assert np.array_equal(a["sel"], b["sel"])
+        assert max_abs(a["out"], b["out"]) <= TOL[w.dtype]
+        assert np.all(b["nm"] == w.top_k)
+
+
+def test_ema_state_save_restore():
+    """The EMA vector and the next predicted set are the only cross-step state: restoring them into a fresh layer
+    reproduces the remaining predicted sets and outputs exactly."""
+    w = small("llama3_8b_32k")
+    kp = w.k_spec[0]
+    inp = make_inputs(w, device="cuda")
+    full = run_layer(w, inp, kp, "prr_2stream", check=False)
+    inp = make_inputs(w, device="cuda")
+    layer = PRRLayer(shape_of(w), w.top_k, kp, w.alpha)
+    layer.build(inp.k_cache, inp.v_cache, inp.table)
+    cut = 4
+    for t in range(cut):
+        layer.step(inp.q[t].contiguous())
+    torch.cuda.synchronize()
+    saved = dict(ema=layer.ema.cpu().clone(), pred=layer.pred_next.cpu().clone(), t=layer.t)
+    layer.close()
+    fresh = PRRLayer(shape_of(w), w.top_k, kp, w.alpha)
+    fresh.build(inp.k_cache, inp.v_cache, inp.table)
+    fresh.ema.copy_(saved["ema"].cuda())
+    fresh.t = saved["t"]
+    fresh.pred[fresh.t % 2][..., :kp].copy_(saved["pred"].cuda())
+    for t in range(cut, w.steps):
+        out = fresh.step(inp.q[t].contiguous())
+        torch.cuda.synchronize()
+        assert np.array_equal(np64(out), full[t]["out"])
+        assert np.array_equal(fresh.pred_current.cpu().numpy(), full[t]["pred"])
+    fresh.close()

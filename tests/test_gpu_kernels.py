@@ -1,0 +1,266 @@
+"""Kernel-by-kernel parity of the HIP path (through the C ABI) against the fp64 oracle, on reduced workloads.
+
+Every call goes through libprr's C entry points; nothing here computes the method on the device with torch."""
+import numpy as np
+import pytest
+import torch
+
+from dynamic_sparse_attention_decode_amd import _lib as L
+from dynamic_sparse_attention_decode_amd.inputs import make_inputs
+from oracle import prr_oracle as O
+from tests.checker import TOL, check_selection, max_abs
+from tests.gpu_common import SMALL, OracleView, np64, requires_gpu, shape_of, small
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _setup(name, seed_shift=0):
+    w = small(name)
+    if seed_shift:
+        w = w.replace(seed=w.seed + seed_shift)
+    print(f"[case] {name} B={w.batch} N={w.n_blocks} K={w.top_k} K'={w.k_spec}", flush=True)
+    inp = make_inputs(w, device="cuda")
+    s = shape_of(w)
+    summ = torch.zeros((w.batch, w.n_kv_heads, w.n_blocks, 2, w.head_dim), dtype=w.torch_dtype, device="cuda")
+    L.build_summaries(s, inp.k_cache, inp.table, summ)
+    torch.cuda.synchronize()
+    return w, inp, s, summ, OracleView(inp)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_summaries_exact(name):
+    w, inp, s, summ, ov = _setup(name)
+    got = np64(summ)
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            kmin, kmax = O.block_summaries(ov.keys(b, g), w.block_size)
+            assert np.array_equal(got[b, g, :, 0], kmin), (b, g)
+            assert np.array_equal(got[b, g, :, 1], kmax), (b, g)
+
+
+def test_summaries_block_ids_after_drift():
+    w, inp, s, summ, ov = _setup("long_ctx_131k_b4")
+    changed = inp.drift(4)
+    assert len(changed)
+    ids = torch.as_tensor(changed, device="cuda")
+    L.build_summaries(s, inp.k_cache, inp.table, summ, block_ids=ids)
+    full = torch.zeros_like(summ)
+    L.build_summaries(s, inp.k_cache, inp.table, full)
+    torch.cuda.synchronize()
+    assert torch.equal(summ.view(torch.int16), full.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_score_select(name):
+    w, inp, s, summ, ov = _setup(name)
+    B, Hkv, N, K = w.batch, w.n_kv_heads, w.n_blocks, w.top_k
+    scores = torch.zeros((B, Hkv, N), dtype=torch.float32, device="cuda")
+    sel = torch.full((B, Hkv, K), -1, dtype=torch.int32, device="cuda")
+    exact = banded = 0
+    for t in range(min(w.steps, 4)):
+        L.score_select(s, inp.q[t].contiguous(), summ, K, scores, sel)
+        torch.cuda.synchronize()
+        gs, gi = np64(scores), sel.cpu().numpy()
+        for b in range(B):
+            for g in range(Hkv):
+                kmin, kmax = O.block_summaries(ov.keys(b, g), w.block_size)
+                ref = O.quest_scores(ov.q_group(t, b, g), kmin, kmax)
+                err = np.max(np.abs(gs[b, g] - ref)) / max(1.0, np.max(np.abs(ref)))
+                assert err < 2e-6, (t, b, g, err)
+                if check_selection(gi[b, g], ref, K):
+                    exact += 1
+                else:
+                    banded += 1
+    print(f"[result] {name}: exact {exact} banded {banded}")
+    assert exact > 0
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_32k", "million_token", "tiny_f32_4k"])
+def test_topk_ties_and_extremes(name):
+    """Exact ties, constant rows, K = 1, K = N, negative values: the selection equals the oracle's tie rule."""
+    w, inp, s, summ, ov = _setup(name)
+    B, Hkv, N = w.batch, w.n_kv_heads, w.n_blocks
+    rng = np.random.default_rng(3)
+    cases = [
+        np.round(rng.standard_normal((B, Hkv, N)) * 2),          # many exact ties
+        np.zeros((B, Hkv, N)),                                   # all equal
+        -np.abs(rng.standard_normal((B, Hkv, N))) * 1e3,         # negative
+        rng.standard_normal((B, Hkv, N)) * 1e-30,                # tiny
+    ]
+    ema = torch.zeros((B, Hkv, N), dtype=torch.float32, device="cuda")
+    for vals in cases:
+        v32 = vals.astype(np.float32)
+        for k in sorted({1, 2, 7, N // 3, N - 1, N}):
+            out = torch.full((B, Hkv, k), -1, dtype=torch.int32, device="cuda")
+            L.ema_predict(s, torch.as_tensor(v32, device="cuda"), ema, 0.5, True, k, out)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            for b in range(B):
+                for g in range(Hkv):
+                    ref = O.top_k(v32[b, g].astype(np.float64), k)
+                    assert np.array_equal(got[b, g], ref), (k, b, g)
+            assert np.array_equal(ema.cpu().numpy(), v32)       # first step: ema = scores
+
+
+def test_ema_update_matches_oracle():
+    w, inp, s, summ, ov = _setup("llama3_8b_32k")
+    B, Hkv, N, Kp = w.batch, w.n_kv_heads, w.n_blocks, w.k_spec[0]
+    rng = np.random.default_rng(4)
+    ema = torch.zeros((B, Hkv, N), dtype=torch.float32, device="cuda")
+    pred = torch.zeros((B, Hkv, Kp), dtype=torch.int32, device="cuda")
+    e_ref = None
+    for t in range(6):
+        sc = (rng.standard_normal((B, Hkv, N)) * 50 + 500).astype(np.float32)
+        L.ema_predict(s, torch.as_tensor(sc, device="cuda"), ema, w.alpha, t == 0, Kp, pred)
+        torch.cuda.synchronize()
+        e_ref = O.ema_update(e_ref, sc.astype(np.float64), w.alpha, t == 0)
+        got = np64(ema)
+        assert np.max(np.abs(got - e_ref) / np.abs(e_ref)) < 1e-6
+        for b in range(B):
+            for g in range(Hkv):
+                check_selection(pred.cpu().numpy()[b, g], e_ref[b, g], Kp)
+
+
+def _records(part, w, k_spec):
+    G, D = w.group, w.head_dim
+    ml = (2 * G + 3) // 4 * 4
+    r = np64(part).reshape(w.batch, w.n_kv_heads, k_spec, ml + G * D)
+    return r[..., :G], r[..., G:2 * G], r[..., ml:].reshape(w.batch, w.n_kv_heads, k_spec, G, D)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_speculate_partials(name):
+    w, inp, s, summ, ov = _setup(name)
+    B, Hkv, N = w.batch, w.n_kv_heads, w.n_blocks
+    Kp = max(w.k_spec)
+    rng = np.random.default_rng(7)
+    pred_np = np.stack([np.stack([np.sort(rng.choice(N, Kp, replace=False)) for _ in range(Hkv)])
+                        for _ in range(B)]).astype(np.int32)
+    pred = torch.as_tensor(pred_np, device="cuda")
+    part = torch.zeros((L.partials_bytes(s, Kp) // 4,), dtype=torch.float32, device="cuda")
+    t = 1
+    L.speculate(s, inp.q[t].contiguous(), inp.k_cache, inp.v_cache, inp.table, pred, Kp, part)
+    torch.cuda.synchronize()
+    m, l, o = _records(part, w, Kp)
+    bs = w.block_size
+    worst = 0.0
+    for b in range(B):
+        for g in range(Hkv):
+            qg = ov.q_group(t, b, g)
+            k, v = ov.keys(b, g), ov.values(b, g)
+            for j in range(0, Kp, max(1, Kp // 7)):
+                n = pred_np[b, g, j]
+                for h in range(w.group):
+                    rm, rl, ro = O.block_partial(qg[h], k[n * bs:(n + 1) * bs], v[n * bs:(n + 1) * bs], w.scale)
+                    assert abs(m[b, g, j, h] * np.log(2.0) - rm) < 1e-5 * max(1, abs(rm))
+                    assert abs(l[b, g, j, h] - rl) < 1e-5 * rl
+                    e = max_abs(o[b, g, j, h] / l[b, g, j, h], ro / rl)
+                    worst = max(worst, e)
+    print(f"[result] {name}: worst partial O/l error {worst:.3e}")
+    assert worst < 1e-5
+
+
+def _forced_sets(rng, T, N, Kp_list):
+    T = list(T)
+    outside = [n for n in range(N) if n not in set(T)]
+    sets = {"empty": [], "equal": T, "random": sorted(rng.choice(N, min(N, len(T) + 5), replace=False).tolist()),
+            "disjoint": sorted(rng.choice(outside, min(len(outside), len(T)), replace=False).tolist()),
+            "superset": sorted(set(T) | set(rng.choice(outside, 7, replace=False).tolist())),
+            "half": sorted(T[::2] + rng.choice(outside, 3, replace=False).tolist())}
+    return sets
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_repair_merge_forced_predictions(name):
+    """Whatever the predicted set (empty, equal, random, disjoint, superset, partial), the repaired output equals
+    attention over the true set and the missed count is |T \\ P| (PRR summary page, Key findings)."""
+    w, inp, s, summ, ov = _setup(name)
+    B, Hkv, N, K, G = w.batch, w.n_kv_heads, w.n_blocks, w.top_k, w.group
+    t = 2
+    q = inp.q[t].contiguous()
+    scores = torch.zeros((B, Hkv, N), dtype=torch.float32, device="cuda")
+    sel = torch.zeros((B, Hkv, K), dtype=torch.int32, device="cuda")
+    L.score_select(s, q, summ, K, scores, sel)
+    torch.cuda.synchronize()
+    sel_np = sel.cpu().numpy()
+    rng = np.random.default_rng(9)
+    ref = {}
+    for b in range(B):
+        for g in range(Hkv):
+            ref[(b, g)] = O.attention_over_blocks(ov.q_group(t, b, g), ov.keys(b, g), ov.values(b, g),
+                                                  sel_np[b, g], w.block_size, w.scale)
+    ws = torch.zeros((L.workspace_bytes(s, K) // 4 + 1,), dtype=torch.float32, device="cuda")
+    out = torch.zeros((B, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    nm = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+    kinds = list(_forced_sets(rng, sel_np[0, 0], N, None))
+    worst = 0.0
+    for kind in kinds:
+        sets = [[_forced_sets(np.random.default_rng(100 * b + g), sel_np[b, g], N, None)[kind] for g in range(Hkv)]
+                for b in range(B)]
+        kp = max(1, max(len(x) for row in sets for x in row))
+        if kind == "empty":
+            kp = 0
+        # pad each list to kp entries with blocks outside T (extra wrongly predicted blocks)
+        pred_np = np.zeros((B, Hkv, max(kp, 1)), dtype=np.int32)
+        for b in range(B):
+            for g in range(Hkv):
+                p = list(sets[b][g])
+                pool = [n for n in range(N) if n not in set(p) and n not in set(sel_np[b, g])]
+                while len(p) < kp:
+                    p.append(pool.pop())
+                pred_np[b, g, :kp] = np.sort(p)
+        pred = torch.as_tensor(pred_np, device="cuda")
+        part = torch.zeros((max(L.partials_bytes(s, kp), 16) // 4,), dtype=torch.float32, device="cuda")
+        L.speculate(s, q, inp.k_cache, inp.v_cache, inp.table, pred, kp, part)
+        L.repair_merge(s, q, inp.k_cache, inp.v_cache, inp.table, sel, K, pred if kp else None, kp,
+                       part if kp else None, out, nm, ws)
+        torch.cuda.synchronize()
+        got = np64(out)
+        nmn = nm.cpu().numpy()
+        for b in range(B):
+            for g in range(Hkv):
+                e = max_abs(got[b, g * G:(g + 1) * G], ref[(b, g)])
+                worst = max(worst, e)
+                assert e <= TOL[w.dtype], (kind, b, g, e)
+                missed = len(set(sel_np[b, g]) - set(pred_np[b, g, :kp]))
+                assert nmn[b, g] == missed, (kind, b, g, nmn[b, g], missed)
+    print(f"[result] {name}: worst forced-P output error {worst:.3e}")
+
+
+def test_poison_block_excluded():
+    """A predicted block outside the true set whose keys align with the queries (logits far above every selected
+    token) must not leak into the output."""
+    w, inp, s, summ, ov = _setup("llama3_8b_32k")
+    B, Hkv, N, K, G = w.batch, w.n_kv_heads, w.n_blocks, w.top_k, w.group
+    t = 1
+    q = inp.q[t].contiguous()
+    scores = torch.zeros((B, Hkv, N), dtype=torch.float32, device="cuda")
+    sel = torch.zeros((B, Hkv, K), dtype=torch.int32, device="cuda")
+    L.score_select(s, q, summ, K, scores, sel)
+    torch.cuda.synchronize()
+    sel_np = sel.cpu().numpy()
+    pred_np = np.zeros((B, Hkv, K + 1), dtype=np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            outside = [n for n in range(N) if n not in set(sel_np[b, g])]
+            pois = outside[len(outside) // 2]
+            qs = ov.q_group(t, b, g).sum(axis=0)
+            keys = torch.as_tensor(np.tile(40.0 * qs / np.linalg.norm(qs), (w.block_size, 1)), dtype=torch.float32)
+            inp.set_block_keys(b, g, pois, keys.cuda())
+            pred_np[b, g] = np.sort(np.append(sel_np[b, g], pois))
+    ov.invalidate_keys()
+    pred = torch.as_tensor(pred_np, device="cuda")
+    part = torch.zeros((L.partials_bytes(s, K + 1) // 4,), dtype=torch.float32, device="cuda")
+    ws = torch.zeros((L.workspace_bytes(s, K) // 4 + 1,), dtype=torch.float32, device="cuda")
+    out = torch.zeros((B, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    nm = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+    L.speculate(s, q, inp.k_cache, inp.v_cache, inp.table, pred, K + 1, part)
+    L.repair_merge(s, q, inp.k_cache, inp.v_cache, inp.table, sel, K, pred, K + 1, part, out, nm, ws)
+    torch.cuda.synchronize()
+    got = np64(out)
+    for b in range(B):
+        for g in range(Hkv):
+            ref = O.attention_over_blocks(ov.q_group(t, b, g), ov.keys(b, g), ov.values(b, g), sel_np[b, g],
+                                          w.block_size, w.scale)
+            assert max_abs(got[b, g * G:(g + 1) * G], ref) <= TOL[w.dtype]
+    assert int(nm.sum()) == 0
