@@ -4,8 +4,8 @@ achieved HBM bandwidth of the dominant kernel against the 8 TB/s peak.
 A "step" is one decode step of one attention layer: score_select, speculate over the predicted blocks, repair and
 merge, and the EMA prediction for the next step (the whole hot path), on synthetic inputs resident in HBM. So that
 consecutive steps do not run out of the 256 MB Infinity Cache, the timed loop rotates over L copies of the layer's
-KV cache (distinct memory, like the layers of a model), with L chosen so the working set exceeds 512 MiB; the
-reported time is per (step, layer).
+KV cache (distinct memory, like the layers of a model), with L (at most 8) chosen so the working set exceeds
+512 MiB where 8 copies suffice; the reported time is per (step, layer).
 
 Prints ONE JSON line. `python bench.py --gpus N` with N > 1 exits: this build runs on one GPU only.
 """
@@ -28,12 +28,13 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b_32k")
     ap.add_argument("--kspec", type=int, default=None, help="speculation budget (default: the workload's largest)")
     ap.add_argument("--layers", type=int, default=0, help="KV copies to rotate over (0 = auto)")
-    ap.add_argument("--mode", default="prr_2stream", choices=["prr_2stream", "prr_1stream", "serialized"])
+    ap.add_argument("--mode", default="prr_2stream", choices=["prr_2stream", "prr_fused", "prr_1stream", "serialized"])
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--detail-out", default=None, help="also append the JSON line to this file")
@@ -64,7 +65,7 @@ def main():
     e = w.elem_bytes
     kv_layer = 2 * w.n_pages * w.n_kv_heads * w.page_size * w.head_dim * e
     summ_layer = w.batch * w.n_kv_heads * w.n_blocks * 2 * w.head_dim * e
-    n_layers = a.layers or max(1, math.ceil(512 * 2 ** 20 / (kv_layer + summ_layer)))
+    n_layers = a.layers or min(8, max(1, math.ceil(512 * 2 ** 20 / (kv_layer + summ_layer))))
     kvs = [(inp.k_cache, inp.v_cache)] + [(inp.k_cache.clone(), inp.v_cache.clone()) for _ in range(n_layers - 1)]
     streams = (torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev))
     qs = [inp.q[t].contiguous() for t in range(w.steps)]
@@ -82,13 +83,6 @@ def main():
         for _ in range(n):
             for lay in layers:
                 lay.enqueue(qs[lay.t % w.steps])
-
-    def timed(layers, n):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        run(layers, n)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / (n * len(layers)) * 1e6
 
     # bytes each kernel must move per launch
     rows = w.batch * w.n_kv_heads
@@ -110,63 +104,100 @@ def main():
             overlap.append(float(1.0 - nm.mean() / w.top_k))
     stat.close()
     mean_missed = float(np.mean(missed)) if missed else float(w.top_k)
-    alg["repair"] = rows * mean_missed * blk_kv if a.mode != "serialized" else rows * w.top_k * blk_kv
+    prr_mode = a.mode != "serialized"
+    alg["repair"] = rows * (mean_missed if prr_mode else w.top_k) * blk_kv
+    if a.mode == "prr_fused":   # one launch scores and speculates
+        alg["score"] += alg["speculate"]
 
-    # ---- per-kernel breakdown (traced pass) ------------------------------------------------------------------------
-    layers = make_layers(a.mode)
-    run(layers, a.warmup)
-    cap = 64 * n_layers
-    tr = L.Trace(cap)
-    kern = ["score", "select_topk", "speculate", "repair", "finalize", "ema_topk"]
-    tr.enable(kern)
-    run(layers, 32)
-    torch.cuda.synchronize()
-    tr.disable()
-    per_kernel = {}
-    for k in kern:
-        d = tr.read(k)
-        if d:
-            per_kernel[k] = float(np.mean(d[len(d) // 4:]) * 1e3)
-    dominant = max((k for k in per_kernel if k in alg), key=lambda k: per_kernel[k])
+    kern = ["score", "select_topk", "speculate", "repair", "ema_topk"]
 
-    # ---- timed loop (headline mode), dominant kernel traced live on its own stream ---------------------------------
-    tr.close()
-    tr = L.Trace(a.steps * n_layers + 8)
-    tr.enable([dominant])
-    us = timed(layers, a.steps)
-    tr.disable()
-    d = tr.read(dominant)
-    tr.close()
-    dom_ms = float(np.mean(d)) if d else float("nan")
-    achieved = alg[dominant] / (dom_ms * 1e-3) / 1e9
-    for lay in layers:
-        lay.close()
-
-    # ---- the other modes for comparison ------------------------------------------------------------------------
-    other = {}
-    for mode in ("prr_2stream", "prr_1stream", "serialized"):
-        if mode == a.mode:
-            continue
+    def measure(mode, trace_kernels=None):
+        """Warm up eagerly, capture exactly a.steps steps (x layers) in a HIP graph, replay once untimed and once
+        timed. Returns (us per step, per-kernel launch durations from the timed replay)."""
         ls = make_layers(mode)
         run(ls, a.warmup)
-        other[mode] = timed(ls, a.steps)
+        torch.cuda.synchronize()
+        tr = None
+        if trace_kernels:
+            tr = L.Trace(min(4096, a.steps * len(ls) + 8))
+            tr.enable(trace_kernels)
+        if a.eager:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            run(ls, a.steps)
+            torch.cuda.synchronize()
+            us_ = (time.perf_counter() - t0) / (a.steps * len(ls)) * 1e6
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=streams[0]):
+                for i in range(a.steps):
+                    for li, lay in enumerate(ls):
+                        lay.enqueue(qs[lay.t % w.steps], join=(i == a.steps - 1 and li == len(ls) - 1))
+            if tr:
+                tr.disable()
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            us_ = (time.perf_counter() - t0) / (a.steps * len(ls)) * 1e6
+        durs = {}
+        if tr:
+            tr.disable()
+            try:
+                for k in trace_kernels:
+                    d = tr.read(k)
+                    if d:
+                        durs[k] = float(np.mean(d)) * 1e3
+            except L.PRRError as ex:
+                print(f"[bench] kernel trace unavailable in this run: {ex}", file=sys.stderr, flush=True)
+                durs = {}
+            tr.close()
         for lay in ls:
             lay.close()
+        return us_, durs
 
-    attn_ms = (per_kernel.get("speculate", 0.0) + per_kernel.get("repair", 0.0)) * 1e-3
-    attn_bytes = alg["speculate"] + alg["repair"] if a.mode != "serialized" else alg["repair"]
+    # per-kernel breakdown (traced), then the headline timed replay with only the dominant kernel traced
+    _, per_kernel = measure(a.mode, kern)
+    if not per_kernel:
+        eager_flag, a.eager = a.eager, True
+        _, per_kernel = measure(a.mode, kern)
+        a.eager = eager_flag
+    dominant = max((k for k in per_kernel if k in alg), key=lambda k: per_kernel[k])
+    us, dom = measure(a.mode, [dominant])
+    dom_where = "timed region"
+    if dominant not in dom:   # events could not be recorded inside the graph: time that kernel in an eager pass
+        eager_flag, a.eager = a.eager, True
+        _, dom = measure(a.mode, [dominant])
+        a.eager = eager_flag
+        dom_where = "eager pass of the same steps"
+    dom_us = dom.get(dominant, float("nan"))
+    achieved = alg[dominant] / (dom_us * 1e-6) / 1e9
+    other = {}
+    for mode in ("prr_fused", "prr_2stream", "prr_1stream", "serialized"):
+        if mode != a.mode:
+            other[mode] = measure(mode)[0]
+
+    if a.mode == "prr_fused":
+        attn_us = per_kernel.get("repair", 0.0)   # speculation runs inside the scoring launch
+        attn_bytes = alg["repair"]
+    else:
+        attn_us = per_kernel.get("speculate", 0.0) + per_kernel.get("repair", 0.0)
+        attn_bytes = (alg["speculate"] if prr_mode else 0) + alg["repair"]
     detail = {
         "us_per_step": {a.mode: us, **other},
+        "timing": "eager" if a.eager else "hip graph of all timed steps",
+        "dominant_kernel_timed_in": dom_where,
         "kernel_us": per_kernel,
-        "attention_path_GBps": attn_bytes / (attn_ms * 1e-3) / 1e9 if attn_ms else None,
-        "attention_path_frac": (attn_bytes / (attn_ms * 1e-3) / 1e9) / HBM_PEAK_GBS if attn_ms else None,
-        "step_alg_bytes": alg["score"] + attn_bytes,
-        "step_GBps": (alg["score"] + attn_bytes) / (us * 1e-6) / 1e9,
+        "attention_path_GBps": attn_bytes / (attn_us * 1e-6) / 1e9 if attn_us else None,
+        "attention_path_frac": (attn_bytes / (attn_us * 1e-6) / 1e9) / HBM_PEAK_GBS if attn_us else None,
+        "step_alg_bytes": rows * w.n_blocks * 2 * w.head_dim * e + attn_bytes,
         "predictor_overlap": float(np.mean(overlap)) if overlap else None,
         "repaired_blocks_mean": mean_missed,
         "layers_rotated": n_layers,
         "working_set_MiB": n_layers * (kv_layer + summ_layer) / 2 ** 20,
     }
+    detail["step_GBps"] = detail["step_alg_bytes"] / (us * 1e-6) / 1e9
     print(f"[bench] {json.dumps(detail)}", file=sys.stderr, flush=True)
 
     cpu = None if a.no_cpu else cpu_baseline(w, inp, kspec, a.cpu_seconds)
@@ -180,7 +211,7 @@ def main():
                    "layers_rotated": n_layers, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "alg_bytes_per_launch": alg[dominant], "avg_launch_us": round(dom_ms * 1e3, 3)},
+                     "alg_bytes_per_launch": alg[dominant], "avg_launch_us": round(dom_us, 3)},
         "cpu_baseline": cpu,
         "detail": detail,
     }

@@ -1,0 +1,207 @@
+// attn_wave.h — the block-sparse decode-attention tile routine shared by speculation and repair.
+//
+// Work unit: one wave processes one (sequence b, KV head g, block) for all G query heads of the group. Each load
+// instruction reads 4 token rows of K (16 lanes x 16 B per 256-byte row, lane = 16*row + col) and the same 4 rows
+// of V, coalesced, through the paged block table (PagedAttention, PRR reference list). Per token the group's G
+// logits are full 16-lane DPP sums; the running max is kept uniform across the wave, while l and the O accumulator
+// stay per-lane partial sums over the lane's token rows until the end, when two permlane swaps fold the 4 rows (each
+// lane then owns G*VE/4 outputs). Logits are kept in log2 units (q pre-scaled by softmax_scale * log2 e) so every
+// exponential is one exp2 (online softmax, FlashAttention-2 in the PRR reference list).
+//
+// Partial record (per (b, g, slot)): m[G] (log2 units), l[G], zero padding to a multiple of 4 floats, then O[G][D]
+// (unnormalised), fp32; records are 16-byte aligned.
+#pragma once
+#include "prr_device.h"
+#include "prr_launch.h"
+
+namespace prr {
+
+template <int DT, int G>
+struct AttnWave {
+  using V = Vec<DT>;
+  static constexpr int VE = V::n;       // elements per 16-byte load
+  static constexpr int D = 16 * VE;     // head_dim
+  static constexpr int NV = G * VE;     // accumulator values per lane
+  static constexpr int NK = NV / 4;     // values per lane after folding the 4 rows
+  static constexpr int ML = rec_ml(G);  // offset of O in a record (floats)
+
+  float q[G][VE];
+  float m[G];      // running max, log2 units, uniform across the wave
+  float l[G];      // per-lane partial sum over this lane's token rows
+  float acc[G][VE];
+  int lane, row, col;
+
+  __device__ void init(int lane_) {
+    lane = lane_;
+    row = lane >> 4;
+    col = lane & 15;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -__builtin_huge_valf();
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[h][e] = 0.f;
+    }
+  }
+
+  __device__ void load_q(const uint8_t* qg, float qscale) {   // qg = q + (b*Hq + g*G) * 256
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float x[VE];
+      V::to_f32(ld16(qg + h * kRowBytes + col * 16), x);
+#pragma unroll
+      for (int e = 0; e < VE; ++e) q[h][e] = x[e] * qscale;
+    }
+  }
+
+  // Fold one block of bs tokens (bs % 4 == 0) into the running state.
+  __device__ void block(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                        const int32_t* __restrict__ trow, int n, int bs, int page, int Hkv, int g) {
+    const int64_t tok0 = (int64_t)n * bs;
+    for (int t0 = 0; t0 < bs; t0 += 16) {
+      uint4 kv[4], vv[4];
+      bool ok[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ok[j] = t0 + 4 * j < bs;
+        const int64_t tok = tok0 + t0 + 4 * j + row;
+        if (ok[j]) {
+          const int64_t phys = trow[tok / page];
+          const int64_t off = ((phys * Hkv + g) * page + tok % page) * (int64_t)kRowBytes + col * 16;
+          kv[j] = ld16(kc + off);
+          vv[j] = ld16(vc + off);
+        } else {
+          kv[j] = make_uint4(0, 0, 0, 0);
+          vv[j] = make_uint4(0, 0, 0, 0);
+        }
+      }
+      float z[4][G];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float x[VE];
+        V::to_f32(kv[j], x);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) s = fmaf(q[h][e], x[e], s);
+          s = row_sum16(s);
+          z[j][h] = ok[j] ? s : -__builtin_huge_valf();
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mc = fmaxf(fmaxf(z[0][h], z[1][h]), fmaxf(z[2][h], z[3][h]));
+        mc = max_xor32(max_xor16(mc));
+        const float mn = fmaxf(m[h], mc);
+        const float corr = exp2f(m[h] - mn);
+        m[h] = mn;
+        l[h] *= corr;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[h][e] *= corr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          z[j][h] = exp2f(z[j][h] - mn);
+          l[h] += z[j][h];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float y[VE];
+        V::to_f32(vv[j], y);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[h][e] = fmaf(z[j][h], y[e], acc[h][e]);
+        }
+      }
+    }
+  }
+
+  // Merge a stored partial record (m[G] log2, l[G], O[G][D]) into the running state. The record's l and O are
+  // added by one row only (row h % 4), since the rows are summed when the state is folded.
+  __device__ void merge_record(const float* __restrict__ rec) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mr = rec[h];
+      const float lr = rec[G + h];
+      const float mn = fmaxf(m[h], mr);
+      const float c_old = exp2f(m[h] - mn);
+      const float c_new = exp2f(mr - mn);
+      m[h] = mn;
+      const bool mine = row == (h & 3);
+      l[h] = l[h] * c_old + (mine ? lr * c_new : 0.f);
+      float o[VE] = {};
+      if (mine) {
+        const float* src = rec + ML + h * D + col * VE;
+#pragma unroll
+        for (int e = 0; e < VE; e += 4) {
+          const float4 t = *reinterpret_cast<const float4*>(src + e);
+          o[e] = t.x; o[e + 1] = t.y; o[e + 2] = t.z; o[e + 3] = t.w;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[h][e] = acc[h][e] * c_old + (mine ? o[e] * c_new : 0.f);
+    }
+  }
+
+  // Fold the 4 rows: l becomes the wave total (uniform); out[i] holds flat accumulator f = row*NK + i.
+  __device__ void fold(float* out) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) l[h] = sum_xor32(sum_xor16(l[h]));
+    float t[NV / 2];
+#pragma unroll
+    for (int f = 0; f < NV / 2; ++f) {
+      const int f2 = f + NV / 2;
+      t[f] = fold32(acc[f / VE][f % VE], acc[f2 / VE][f2 % VE]);
+    }
+#pragma unroll
+    for (int f = 0; f < NK; ++f) out[f] = fold16(t[f], t[f + NK]);
+  }
+
+  // Write the folded state as a record.
+  __device__ void write_record(float* __restrict__ rec, const float* folded) {
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) { rec[h] = m[h]; rec[G + h] = l[h]; }
+    }
+    float* o = rec + ML;
+    if constexpr (NK % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < NK; i += 4) {
+        const int f = row * NK + i;
+        const int h = f / VE, e = f % VE;
+        *reinterpret_cast<float4*>(o + h * D + col * VE + e) =
+            make_float4(folded[i], folded[i + 1], folded[i + 2], folded[i + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const int f = row * NK + i;
+        o[(f / VE) * D + col * VE + (f % VE)] = folded[i];
+      }
+    }
+  }
+};
+
+// Speculation of one predicted slot s = (b * Hkv + g) * k_spec + j by one wave: the block's partial record.
+template <int DT, int G>
+__device__ inline void speculate_slot(int64_t s, int lane, const uint8_t* __restrict__ q,
+                                      const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                                      const int32_t* __restrict__ table, const int32_t* __restrict__ pred, int k_spec,
+                                      float* __restrict__ partials, int Hq, int Hkv, int N, int bs, int page, int pps,
+                                      float qscale) {
+  using W = AttnWave<DT, G>;
+  const int64_t rowid = s / k_spec;
+  const int b = (int)(rowid / Hkv), g = (int)(rowid % Hkv);
+  const int n = min(max(pred[s], 0), N - 1);   // ids outside [0, N) are clamped: wrong output, never a fault
+  W st;
+  st.init(lane);
+  st.load_q(q + ((int64_t)b * Hq + (int64_t)g * G) * kRowBytes, qscale);
+  st.block(kc, vc, table + (int64_t)b * pps, n, bs, page, Hkv, g);
+  float folded[W::NK];
+  st.fold(folded);
+  st.write_record(partials + s * rec_floats(G, W::D), folded);
+}
+
+}  // namespace prr

@@ -37,6 +37,7 @@ prr_status check_launch(const char* what) {
 struct prr_trace {
   int32_t capacity = 0;
   uint32_t mask = 0;
+  char failure[256] = "";   // first failed record (tracing never changes the status of a launch)
   int32_t count[PRR_KERNEL_COUNT] = {};
   hipEvent_t* ev0[PRR_KERNEL_COUNT] = {};
   hipEvent_t* ev1[PRR_KERNEL_COUNT] = {};
@@ -46,16 +47,32 @@ namespace prr {
 
 static std::atomic<prr_trace*> g_trace{nullptr};
 
+// Under stream capture the record becomes an external event node of the graph, so every replay records it. A
+// failed record is noted on the trace and cleared from HIP's last-error state.
+static void record(prr_trace* t, hipEvent_t e, hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t err = hipStreamIsCapturing(stream, &cs);
+  if (err == hipSuccess)
+    err = cs == hipStreamCaptureStatusActive ? hipEventRecordWithFlags(e, stream, hipEventRecordExternal)
+                                             : hipEventRecord(e, stream);
+  if (err != hipSuccess) {
+    if (!t->failure[0])
+      snprintf(t->failure, sizeof(t->failure), "event record failed (capture status %d): %s", (int)cs,
+               hipGetErrorString(err));
+    (void)hipGetLastError();
+  }
+}
+
 void trace_begin(int kid, hipStream_t stream) {
   prr_trace* t = g_trace.load(std::memory_order_acquire);
   if (!t || !(t->mask & (1u << kid)) || t->count[kid] >= t->capacity) return;
-  (void)hipEventRecord(t->ev0[kid][t->count[kid]], stream);
+  record(t, t->ev0[kid][t->count[kid]], stream);
 }
 
 void trace_end(int kid, hipStream_t stream) {
   prr_trace* t = g_trace.load(std::memory_order_acquire);
   if (!t || !(t->mask & (1u << kid)) || t->count[kid] >= t->capacity) return;
-  (void)hipEventRecord(t->ev1[kid][t->count[kid]], stream);
+  record(t, t->ev1[kid][t->count[kid]], stream);
   ++t->count[kid];
 }
 
@@ -223,6 +240,36 @@ prr_status prr_repair_merge(const prr_shape* shape, const void* q, const void* k
                        k_spec, k_spec ? partials : nullptr, out, n_missed, workspace, as_stream(stream));
 }
 
+prr_status prr_score_speculate(const prr_shape* shape, const void* q, const void* summaries, float* scores,
+                               const void* k_cache, const void* v_cache, const int32_t* block_table,
+                               const int32_t* pred_idx, int32_t k_spec, float* partials, void* stream) {
+  PRR_TRY(check_shape(shape));
+  PRR_REQUIRE(q && summaries && scores, "score_speculate: null pointer");
+  PRR_REQUIRE(k_spec >= 0 && k_spec <= shape->n_blocks, "score_speculate: k_spec %d not in [0, %d]", k_spec,
+              shape->n_blocks);
+  if (k_spec > 0)
+    PRR_REQUIRE(k_cache && v_cache && block_table && pred_idx && partials, "score_speculate: null pointer");
+  return launch_score_spec(*shape, q, summaries, scores, k_cache, v_cache, block_table, pred_idx, k_spec, partials,
+                           as_stream(stream));
+}
+
+prr_status prr_select_predict(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
+                              float* ema, float alpha, int32_t first_step, int32_t k_spec_next,
+                              int32_t* pred_idx_next, void* stream) {
+  PRR_TRY(check_shape(shape));
+  PRR_TRY(check_topk_n(shape));
+  PRR_REQUIRE(scores && sel_idx, "select_predict: null pointer");
+  PRR_REQUIRE(top_k >= 1 && top_k <= shape->n_blocks, "select_predict: top_k %d not in [1, %d]", top_k,
+              shape->n_blocks);
+  PRR_REQUIRE(k_spec_next >= 0 && k_spec_next <= shape->n_blocks, "select_predict: k_spec_next %d not in [0, %d]",
+              k_spec_next, shape->n_blocks);
+  if (k_spec_next == 0) return launch_topk(*shape, scores, nullptr, 0.f, 0, top_k, sel_idx, as_stream(stream));
+  PRR_REQUIRE(ema && pred_idx_next, "select_predict: null pointer");
+  PRR_REQUIRE(alpha >= 0.f && alpha <= 1.f, "select_predict: alpha not in [0, 1]");
+  return launch_topk_pair(*shape, scores, top_k, sel_idx, ema, alpha, first_step ? 1 : 0, k_spec_next,
+                          pred_idx_next, as_stream(stream));
+}
+
 size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec) {
   if (check_shape(shape) != PRR_OK || k_spec <= 0) return 0;
   const int G = shape->n_q_heads / shape->n_kv_heads;
@@ -273,7 +320,7 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
                            int32_t join, void* stream_sel, void* stream_spec) {
   PRR_TRY(check_shape(shape));
   PRR_REQUIRE(a, "decode_step: args is NULL");
-  PRR_REQUIRE(mode >= PRR_MODE_SERIALIZED && mode <= PRR_MODE_TWO_STREAM, "decode_step: unknown mode %d", mode);
+  PRR_REQUIRE(mode >= PRR_MODE_SERIALIZED && mode <= PRR_MODE_FUSED, "decode_step: unknown mode %d", mode);
   PRR_REQUIRE(mode != PRR_MODE_TWO_STREAM || ctx, "decode_step: two-stream mode needs a step context");
   const hipStream_t s1 = as_stream(stream_sel);
   const hipStream_t s2 = as_stream(stream_spec);
@@ -281,6 +328,14 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
   const int kn = mode == PRR_MODE_SERIALIZED ? 0 : a->k_spec_next;
   PRR_REQUIRE(kc >= 0 && kn >= 0, "decode_step: negative k_spec");
 
+  if (mode == PRR_MODE_FUSED) {
+    PRR_TRY(prr_score_speculate(shape, a->q, a->summaries, a->scores, a->k_cache, a->v_cache, a->block_table,
+                                a->pred_cur, kc, a->partials, s1));
+    PRR_TRY(prr_select_predict(shape, a->scores, a->top_k, a->sel_idx, a->ema, a->alpha, a->first_step, kn,
+                               a->pred_next, s1));
+    return prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
+                            kc, a->partials, a->out, a->n_missed, a->workspace, s1);
+  }
   if (mode != PRR_MODE_TWO_STREAM) {
     if (kc > 0) PRR_TRY(prr_speculate(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->pred_cur, kc,
                                       a->partials, s1));
@@ -350,6 +405,7 @@ void prr_trace_destroy(prr_trace* t) {
 prr_status prr_trace_enable(prr_trace* t, uint32_t mask) {
   if (!t || mask == 0) { g_trace.store(nullptr, std::memory_order_release); return PRR_OK; }
   t->mask = mask;
+  t->failure[0] = 0;
   for (int k = 0; k < PRR_KERNEL_COUNT; ++k) t->count[k] = 0;
   g_trace.store(t, std::memory_order_release);
   return PRR_OK;
@@ -360,11 +416,17 @@ int32_t prr_trace_read(prr_trace* t, int32_t kernel, float* ms_out, int32_t cap)
     set_error("trace_read: invalid argument");
     return PRR_EINVAL;
   }
+  if (t->failure[0]) {
+    set_error("trace_read: %s", t->failure);
+    return PRR_ELAUNCH;
+  }
   const int n = t->count[kernel] < cap ? t->count[kernel] : cap;
   for (int i = 0; i < n; ++i) {
-    if (hipEventSynchronize(t->ev1[kernel][i]) != hipSuccess ||
-        hipEventElapsedTime(&ms_out[i], t->ev0[kernel][i], t->ev1[kernel][i]) != hipSuccess) {
-      set_error("trace_read: event query failed");
+    hipError_t e = hipEventSynchronize(t->ev1[kernel][i]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms_out[i], t->ev0[kernel][i], t->ev1[kernel][i]);
+    if (e != hipSuccess) {
+      set_error("trace_read: event query failed: %s", hipGetErrorString(e));
+      (void)hipGetLastError();
       return PRR_ELAUNCH;
     }
   }

@@ -21,6 +21,34 @@ __host__ __device__ constexpr int64_t rec_floats(int G, int D) { return (int64_t
 void trace_begin(int kid, hipStream_t stream);
 void trace_end(int kid, hipStream_t stream);
 
+// Calls FN<dtype, G>(args...) for the shape's storage dtype and group size (shape variable `s`).
+#define PRR_DISPATCH_DT_G(FN, ...)                                      \
+  do {                                                                  \
+    const int G_ = s.n_q_heads / s.n_kv_heads;                          \
+    if (s.dtype == 0) {                                              \
+      switch (G_) {                                                     \
+        case 1: FN<0, 1>(__VA_ARGS__); break;                        \
+        case 2: FN<0, 2>(__VA_ARGS__); break;                        \
+        case 4: FN<0, 4>(__VA_ARGS__); break;                        \
+        default: FN<0, 8>(__VA_ARGS__); break;                       \
+      }                                                                 \
+    } else if (s.dtype == 1) {                                      \
+      switch (G_) {                                                     \
+        case 1: FN<1, 1>(__VA_ARGS__); break;                       \
+        case 2: FN<1, 2>(__VA_ARGS__); break;                       \
+        case 4: FN<1, 4>(__VA_ARGS__); break;                       \
+        default: FN<1, 8>(__VA_ARGS__); break;                      \
+      }                                                                 \
+    } else {                                                            \
+      switch (G_) {                                                     \
+        case 1: FN<2, 1>(__VA_ARGS__); break;                        \
+        case 2: FN<2, 2>(__VA_ARGS__); break;                        \
+        case 4: FN<2, 4>(__VA_ARGS__); break;                        \
+        default: FN<2, 8>(__VA_ARGS__); break;                       \
+      }                                                                 \
+    }                                                                   \
+  } while (0)
+
 prr_status launch_summaries(const prr_shape& s, const void* k_cache, const int32_t* table, const int32_t* ids,
                             int64_t n_jobs, void* summ, hipStream_t stream);
 prr_status launch_score(const prr_shape& s, const void* q, const void* summ, float* scores, hipStream_t stream);
@@ -33,6 +61,11 @@ prr_status launch_repair(const prr_shape& s, const void* q, const void* k_cache,
                          const int32_t* table, const int32_t* sel, int top_k, const int32_t* pred, int k_spec,
                          const float* partials, float* out, int32_t* n_missed, void* workspace, hipStream_t stream);
 size_t repair_workspace_bytes(const prr_shape& s, int top_k);
+prr_status launch_score_spec(const prr_shape& s, const void* q, const void* summ, float* scores, const void* kc,
+                             const void* vc, const int32_t* table, const int32_t* pred, int k_spec, float* partials,
+                             hipStream_t stream);
+prr_status launch_topk_pair(const prr_shape& s, const float* scores, int k, int32_t* sel, float* ema, float alpha,
+                            int first, int kp, int32_t* pred, hipStream_t stream);
 prr_status launch_flush(void* buf, size_t bytes, hipStream_t stream);
 prr_status launch_stream_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 

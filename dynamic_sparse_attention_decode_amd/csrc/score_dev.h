@@ -1,0 +1,68 @@
+// score_dev.h — Quest block scoring as a streaming GEMV (PRR reference list, Quest), shared by the scoring kernel
+// and the fused scoring + speculation kernel.
+//
+// s[b,g,n] = sum_d Qpos_d * kmax[n,d] + Qneg_d * kmin[n,d] with Qpos_d = sum_h max(q_hd, 0) and
+// Qneg_d = sum_h min(q_hd, 0) over the group's query heads. Because kmin <= kmax, max(q*kmin, q*kmax) equals
+// max(q,0)*kmax + min(q,0)*kmin exactly, so this is Quest's group-summed score read in one pass over the summaries
+// (2*D elements per block), HBM-bound. Each wave load covers two blocks (32 lanes per [min;max] pair); the block's
+// dot product is folded with DPP inside 16-lane rows and one permlane16 swap.
+#pragma once
+#include "prr_device.h"
+#include "prr_launch.h"
+
+namespace prr {
+
+// Scores of blocks [bx * chunk, (bx + 1) * chunk) of row bg = b * Hkv + g, by one 256-thread workgroup.
+template <int DT, int G>
+__device__ inline void score_chunk(int bx, int bg, const uint8_t* __restrict__ q, const uint8_t* __restrict__ summ,
+                                   float* __restrict__ scores, int Hq, int Hkv, int N, int chunk) {
+  using V = Vec<DT>;
+  constexpr int U = 8;   // wave loads in flight per lane
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int col = lane & 15, half = (lane >> 4) & 1, pair = lane >> 5;
+
+  float coef[V::n];
+#pragma unroll
+  for (int e = 0; e < V::n; ++e) coef[e] = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float x[V::n];
+    V::to_f32(ld16(q + ((int64_t)b * Hq + g * G + h) * kRowBytes + col * 16), x);
+#pragma unroll
+    for (int e = 0; e < V::n; ++e) coef[e] += half ? fmaxf(x[e], 0.f) : fminf(x[e], 0.f);
+  }
+
+  const int c0 = bx * chunk;
+  const int c1 = min(N, c0 + chunk);
+  const uint8_t* base = summ + (int64_t)bg * N * (2 * kRowBytes) + half * kRowBytes + col * 16;
+  float* srow = scores + (int64_t)bg * N;
+  for (int n0 = c0 + wave * 2 + pair; n0 < c1; n0 += 8 * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int n = n0 + 8 * u;
+      v[u] = n < c1 ? ld16(base + (int64_t)n * (2 * kRowBytes)) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float x[V::n];
+      V::to_f32(v[u], x);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < V::n; ++e) s = fmaf(coef[e], x[e], s);
+      s = sum_xor16(row_sum16(s));
+      const int n = n0 + 8 * u;
+      if ((lane & 31) == 0 && n < c1) srow[n] = s;
+    }
+  }
+}
+
+// Blocks per scoring workgroup: a multiple of 64 (one unrolled wave round), sized for about 2048 workgroups.
+inline int score_chunk_size(const prr_shape& s) {
+  const int64_t total = (int64_t)s.batch * s.n_kv_heads * s.n_blocks;
+  const int chunk = (int)((total / 2048 + 63) / 64 * 64);
+  return chunk < 64 ? 64 : chunk;
+}
+
+}  // namespace prr

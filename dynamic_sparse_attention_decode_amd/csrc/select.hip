@@ -2,11 +2,7 @@
 // query; PRR reference list, Quest: block scores from per-block key min/max), and the EMA predictor's update and
 // top-K' (PRR abstract: "lightweight EMA-based predictor").
 //
-// score_kernel: s[b,g,n] = sum_d Qpos_d * kmax[n,d] + Qneg_d * kmin[n,d] with Qpos_d = sum_h max(q_hd, 0) and
-//   Qneg_d = sum_h min(q_hd, 0) over the group's query heads. Because kmin <= kmax, max(q*kmin, q*kmax) equals
-//   max(q,0)*kmax + min(q,0)*kmin exactly, so this is Quest's group-summed score as a streaming GEMV: one pass over
-//   the summaries (2*D elements per block), HBM-bound. Each wave load covers two blocks (32 lanes per [min;max]
-//   pair); the block's dot product is folded with DPP inside 16-lane rows and one permlane16 swap.
+// score_kernel: Quest's group-summed block score as a streaming GEMV (score_dev.h).
 //
 // topk_kernel: one 1024-thread workgroup per (b, g) row holds the row's N values in registers as order-preserving
 //   uint32 keys (thread t owns indices [t*KPT, (t+1)*KPT)). A most-significant-digit radix select finds the K-th
@@ -14,55 +10,14 @@
 //   histogram, early exit when a whole digit bin is taken. Compaction takes every key above the threshold class and
 //   the lowest-index keys of the threshold class; one workgroup-wide scan gives each thread its output offset, so
 //   the output comes out in ascending block order. Optionally updates the EMA in the same pass.
-#include "prr_device.h"
-#include "prr_launch.h"
+#include "score_dev.h"
 
 namespace prr {
 
 template <int DT, int G>
 __global__ __launch_bounds__(256) void score_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ summ,
                                                     float* __restrict__ scores, int Hq, int Hkv, int N, int chunk) {
-  using V = Vec<DT>;
-  constexpr int U = 8;   // wave loads in flight per lane
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int bg = blockIdx.y;
-  const int b = bg / Hkv, g = bg % Hkv;
-  const int col = lane & 15, half = (lane >> 4) & 1, pair = lane >> 5;
-
-  float coef[V::n];
-#pragma unroll
-  for (int e = 0; e < V::n; ++e) coef[e] = 0.f;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float x[V::n];
-    V::to_f32(ld16(q + ((int64_t)b * Hq + g * G + h) * kRowBytes + col * 16), x);
-#pragma unroll
-    for (int e = 0; e < V::n; ++e) coef[e] += half ? fmaxf(x[e], 0.f) : fminf(x[e], 0.f);
-  }
-
-  const int c0 = blockIdx.x * chunk;
-  const int c1 = min(N, c0 + chunk);
-  const uint8_t* base = summ + (int64_t)bg * N * (2 * kRowBytes) + half * kRowBytes + col * 16;
-  float* srow = scores + (int64_t)bg * N;
-  for (int n0 = c0 + wave * 2 + pair; n0 < c1; n0 += 8 * U) {
-    uint4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int n = n0 + 8 * u;
-      v[u] = n < c1 ? ld16(base + (int64_t)n * (2 * kRowBytes)) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float x[V::n];
-      V::to_f32(v[u], x);
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < V::n; ++e) s = fmaf(coef[e], x[e], s);
-      s = sum_xor16(row_sum16(s));
-      const int n = n0 + 8 * u;
-      if ((lane & 31) == 0 && n < c1) srow[n] = s;
-    }
-  }
+  score_chunk<DT, G>(blockIdx.x, blockIdx.y, q, summ, scores, Hq, Hkv, N, chunk);
 }
 
 // ---- workgroup helpers for the 1024-thread top-K kernel ----------------------------------------------------------
@@ -87,18 +42,16 @@ __device__ inline uint32_t wave_suffix_incl(uint32_t x, int lane) {
 
 __device__ inline uint32_t shr(uint32_t x, int s) { return s >= 32 ? 0u : x >> s; }
 
+// Top-K of one row of N values (optionally after the EMA update e = alpha e + (1 - alpha) v, written back), by one
+// 1024-thread workgroup; out_row receives K ascending indices.
 template <int KPT, bool EMA>
-__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ vals, float* __restrict__ ema,
-                                                    float alpha, int first, int N, int K,
-                                                    int32_t* __restrict__ out) {
+__device__ void topk_row(const float* __restrict__ v, float* __restrict__ e_row, float alpha, int first, int N, int K,
+                         int32_t* __restrict__ orow) {
   __shared__ uint32_t hist[256];
   __shared__ float red_f[2][16];
   __shared__ uint32_t red_u[16];
   __shared__ uint32_t bc[3];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row = blockIdx.x;
-  const float* v = vals + row * N;
-  float* e_row = EMA ? ema + row * N : nullptr;
   const int i0 = tid * KPT;
 
   // ---- load (and EMA update) --------------------------------------------------------------------------------
@@ -222,7 +175,6 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ va
   const uint32_t pre_g = excl >> 16, pre_e = excl & 0xffffu;
   uint32_t pos = pre_g + (pre_e < krem ? pre_e : krem);
   uint32_t le = pre_e;
-  int32_t* orow = out + row * K;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const int i = i0 + k;
@@ -242,6 +194,28 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ va
   }
 }
 
+template <int KPT, bool EMA>
+__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ vals, float* __restrict__ ema,
+                                                    float alpha, int first, int N, int K,
+                                                    int32_t* __restrict__ out) {
+  const int64_t row = blockIdx.x;
+  topk_row<KPT, EMA>(vals + row * N, EMA ? ema + row * N : nullptr, alpha, first, N, K, out + row * K);
+}
+
+// True top-K (workgroups [0, rows)) and the EMA update + top-K' prediction (workgroups [rows, 2 rows)) in one
+// launch: both read the same scores, so the prediction costs no extra step on the critical path.
+template <int KPT>
+__global__ __launch_bounds__(1024) void topk_pair_kernel(const float* __restrict__ scores, int K,
+                                                         int32_t* __restrict__ sel, float* __restrict__ ema,
+                                                         float alpha, int first, int Kp,
+                                                         int32_t* __restrict__ pred, int N, int rows) {
+  const int64_t r = blockIdx.x;
+  if (r < rows)
+    topk_row<KPT, false>(scores + r * N, nullptr, alpha, first, N, K, sel + r * K);
+  else
+    topk_row<KPT, true>(scores + (r - rows) * N, ema + (r - rows) * N, alpha, first, N, Kp, pred + (r - rows) * Kp);
+}
+
 // ---- launchers -----------------------------------------------------------------------------------------------------
 
 template <int DT>
@@ -259,10 +233,7 @@ static void score_dispatch(const prr_shape& s, dim3 grid, const uint8_t* q, cons
 
 prr_status launch_score(const prr_shape& s, const void* q, const void* summ, float* scores, hipStream_t stream) {
   const int rows = s.batch * s.n_kv_heads;
-  // Blocks per workgroup: a multiple of 64 (one unrolled wave round), sized for about 2048 workgroups in total.
-  const int64_t total = (int64_t)rows * s.n_blocks;
-  int chunk = (int)((total / 2048 + 63) / 64 * 64);
-  if (chunk < 64) chunk = 64;
+  const int chunk = score_chunk_size(s);
   const dim3 grid((unsigned)((s.n_blocks + chunk - 1) / chunk), (unsigned)rows);
   const auto* qq = static_cast<const uint8_t*>(q);
   const auto* sm = static_cast<const uint8_t*>(summ);
@@ -290,10 +261,15 @@ static void topk_dispatch(int kpt, dim3 grid, const float* vals, float* ema, flo
   }
 }
 
-prr_status launch_topk(const prr_shape& s, const float* values, float* ema, float alpha, int first, int k,
-                       int32_t* out_idx, hipStream_t stream) {
+static int topk_kpt(const prr_shape& s) {
   int kpt = 1;
   while (kpt * 1024 < s.n_blocks) kpt *= 2;
+  return kpt;
+}
+
+prr_status launch_topk(const prr_shape& s, const float* values, float* ema, float alpha, int first, int k,
+                       int32_t* out_idx, hipStream_t stream) {
+  const int kpt = topk_kpt(s);
   const dim3 grid((unsigned)(s.batch * s.n_kv_heads));
   const int kid = ema ? PRR_KERNEL_EMA_TOPK : PRR_KERNEL_SELECT_TOPK;
   trace_begin(kid, stream);
@@ -303,6 +279,28 @@ prr_status launch_topk(const prr_shape& s, const float* values, float* ema, floa
     topk_dispatch<false>(kpt, grid, values, nullptr, alpha, first, s.n_blocks, k, out_idx, stream);
   trace_end(kid, stream);
   return check_launch(ema ? "ema_predict" : "select_topk");
+}
+
+}  // namespace prr
+
+namespace prr {
+
+prr_status launch_topk_pair(const prr_shape& s, const float* scores, int k, int32_t* sel, float* ema, float alpha,
+                            int first, int kp, int32_t* pred, hipStream_t stream) {
+  const int rows = s.batch * s.n_kv_heads;
+  const dim3 grid((unsigned)(2 * rows)), blk(1024);
+  const int N = s.n_blocks;
+  trace_begin(PRR_KERNEL_SELECT_TOPK, stream);
+  switch (topk_kpt(s)) {
+    case 1: topk_pair_kernel<1><<<grid, blk, 0, stream>>>(scores, k, sel, ema, alpha, first, kp, pred, N, rows); break;
+    case 2: topk_pair_kernel<2><<<grid, blk, 0, stream>>>(scores, k, sel, ema, alpha, first, kp, pred, N, rows); break;
+    case 4: topk_pair_kernel<4><<<grid, blk, 0, stream>>>(scores, k, sel, ema, alpha, first, kp, pred, N, rows); break;
+    case 8: topk_pair_kernel<8><<<grid, blk, 0, stream>>>(scores, k, sel, ema, alpha, first, kp, pred, N, rows); break;
+    case 16: topk_pair_kernel<16><<<grid, blk, 0, stream>>>(scores, k, sel, ema, alpha, first, kp, pred, N, rows); break;
+    default: topk_pair_kernel<32><<<grid, blk, 0, stream>>>(scores, k, sel, ema, alpha, first, kp, pred, N, rows); break;
+  }
+  trace_end(PRR_KERNEL_SELECT_TOPK, stream);
+  return check_launch("select_predict");
 }
 
 }  // namespace prr

@@ -19,7 +19,8 @@ import torch
 
 from . import _lib as L
 
-MODES = {"serialized": L.MODE_SERIALIZED, "prr_1stream": L.MODE_ONE_STREAM, "prr_2stream": L.MODE_TWO_STREAM}
+MODES = {"serialized": L.MODE_SERIALIZED, "prr_1stream": L.MODE_ONE_STREAM, "prr_2stream": L.MODE_TWO_STREAM,
+         "prr_fused": L.MODE_FUSED}
 
 
 class PRRLayer:

@@ -106,11 +106,24 @@ prr_status prr_speculate(const prr_shape* shape, const void* q, const void* k_ca
  * P = pred_idx[b,g,:k_spec] reuse their speculated partials; the missed blocks M = T \ P are computed here; blocks of
  * P \ T never enter. out[b,h] = O / l of the merged state; n_missed[b,g] = |M|. k_spec == 0 (or pred_idx NULL)
  * computes attention over all of T (the serialized select-then-attend path). `workspace` holds
- * prr_workspace_bytes() bytes of scratch (no initialisation needed). */
+ * prr_workspace_bytes() bytes of scratch (no initialisation needed); calls sharing one workspace must not overlap. */
 prr_status prr_repair_merge(const prr_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_table, const int32_t* sel_idx, int32_t top_k,
                             const int32_t* pred_idx, int32_t k_spec, const float* partials, float* out,
                             int32_t* n_missed, void* workspace, void* stream);
+
+/* Scoring and speculation in ONE launch: the scores of prr_score_select plus the partials of prr_speculate
+ * (workgroups of the two roles run concurrently, so speculation overlaps selection without a second stream).
+ * k_spec == 0 only scores. Same layouts and requirements as the two calls it combines. */
+prr_status prr_score_speculate(const prr_shape* shape, const void* q, const void* summaries, float* scores,
+                               const void* k_cache, const void* v_cache, const int32_t* block_table,
+                               const int32_t* pred_idx, int32_t k_spec, float* partials, void* stream);
+
+/* The true top-K from `scores` (as in prr_score_select) and, when k_spec_next > 0, the EMA update and top-K'
+ * prediction of prr_ema_predict, in ONE launch (both only read the scores). k_spec_next == 0 selects only. */
+prr_status prr_select_predict(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
+                              float* ema, float alpha, int32_t first_step, int32_t k_spec_next,
+                              int32_t* pred_idx_next, void* stream);
 
 /* Bytes of the partials buffer for a speculation budget k_spec (0 for k_spec == 0). */
 size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec);
@@ -122,8 +135,9 @@ size_t prr_workspace_bytes(const prr_shape* shape, int32_t top_k);
 typedef enum {
   PRR_MODE_SERIALIZED = 0,  /* stream_sel: score_select -> repair_merge over all of T (no prediction)            */
   PRR_MODE_ONE_STREAM = 1,  /* stream_sel: speculate -> score_select -> repair_merge -> ema_predict                */
-  PRR_MODE_TWO_STREAM = 2   /* stream_spec: speculate || stream_sel: score_select; then repair_merge on stream_sel
+  PRR_MODE_TWO_STREAM = 2,  /* stream_spec: speculate || stream_sel: score_select; then repair_merge on stream_sel
                                while ema_predict runs on stream_spec                                            */
+  PRR_MODE_FUSED = 3        /* stream_sel only: score_speculate -> select_predict -> repair_merge (3 launches)   */
 } prr_mode;
 
 typedef struct {
@@ -166,7 +180,8 @@ int32_t prr_choose_budget(const double* n_grid, const double* t_sel, int32_t n_p
  * achieved bandwidth of one kernel inside a running decode loop. A trace holds `capacity` event pairs per kernel
  * id; while enabled (process-wide, one trace at a time) every launch of a kernel in `kernel_mask` (bit i = kernel
  * id i) records an event immediately before and after it, until that kernel's pool is full. Reading synchronises
- * on the events. */
+ * on the events. Under stream capture the records become external event nodes of the graph (each replay records
+ * them again), so a captured decode loop can be traced too. */
 typedef enum {
   PRR_KERNEL_SUMMARIES = 0, PRR_KERNEL_SCORE = 1, PRR_KERNEL_SELECT_TOPK = 2, PRR_KERNEL_EMA_TOPK = 3,
   PRR_KERNEL_SPECULATE = 4, PRR_KERNEL_REPAIR = 5, PRR_KERNEL_FINALIZE = 6, PRR_KERNEL_COUNT = 7

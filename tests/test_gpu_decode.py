@@ -76,19 +76,22 @@ def test_decode_two_stream_vs_oracle(name):
                   f"mean missed {np.mean([h['nm'].mean() for h in hist[1:]]):.2f}")
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_32k", "paged_b32_64k", "tiny_f32_4k"])
+@pytest.mark.parametrize("name", ["llama3_8b_32k", "paged_b32_64k", "tiny_f32_4k", "million_token"])
 def test_modes_agree(name):
-    """Two-stream and one-stream runs are bitwise identical (same kernels, same inputs); the serialized
-    select-then-attend run matches within the output tolerance."""
+    """Two-stream, one-stream and fused (role-specialised single-stream launches) runs are bitwise identical (same
+    arithmetic in the same order); the serialized select-then-attend run matches within the output tolerance."""
     w = small(name)
     kp = max(w.k_spec)
     runs = {}
-    for mode in ("prr_2stream", "prr_1stream", "serialized"):
+    for mode in ("prr_2stream", "prr_fused", "prr_1stream", "serialized"):
         inp = make_inputs(w, device="cuda")
         runs[mode] = run_layer(w, inp, kp, mode, check=False)
-    for a, b in zip(runs["prr_2stream"], runs["prr_1stream"]):
-        assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["sel"], b["sel"])
-        assert np.array_equal(a["nm"], b["nm"])
+    for other in ("prr_1stream", "prr_fused"):
+        for a, b in zip(runs["prr_2stream"], runs[other]):
+            assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["sel"], b["sel"]), other
+            assert np.array_equal(a["nm"], b["nm"]), other
+            if a["pred"] is not None:
+                assert np.array_equal(a["pred"], b["pred"]), other
     for a, b in zip(runs["prr_2stream"], runs["serialized"]):
         assert np.array_equal(a["sel"], b["sel"])
         assert max_abs(a["out"], b["out"]) <= TOL[w.dtype]
@@ -122,3 +125,41 @@ def test_ema_state_save_restore():
         assert np.array_equal(np64(out), full[t]["out"])
         assert np.array_equal(fresh.pred_current.cpu().numpy(), full[t]["pred"])
     fresh.close()
+
+
+@pytest.mark.parametrize("mode", ["prr_2stream", "prr_fused"])
+def test_graph_replay_matches_eager(mode):
+    """Steps captured in a HIP graph and replayed several times (with eager work and synchronisation between the
+    replays) give the same outputs, selections and missed counts as the same steps run eagerly."""
+    w = small("llama3_8b_32k")
+    kp = w.k_spec[0]
+    inp = make_inputs(w, device="cuda")
+    qs = [inp.q[t].contiguous() for t in range(w.steps)]
+    seq = [0] + [1, 2, 3, 4] * 3
+    eager = PRRLayer(shape_of(w), w.top_k, kp, w.alpha, mode=mode)
+    eager.build(inp.k_cache, inp.v_cache, inp.table)
+    ref = []
+    for t in seq:
+        out = eager.step(qs[t])
+        torch.cuda.synchronize()
+        ref.append((np64(out), eager.sel_idx.cpu().numpy().copy(), eager.n_missed.cpu().numpy().copy()))
+    eager.close()
+    lay = PRRLayer(shape_of(w), w.top_k, kp, w.alpha, mode=mode)
+    lay.build(inp.k_cache, inp.v_cache, inp.table)
+    lay.step(qs[0])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=lay.s_sel):
+        outs = [lay.enqueue(qs[t], join=(t == 4)) for t in (1, 2, 3, 4)]
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        scratch = torch.randn(1 << 16, device="cuda").sum()   # unrelated eager work between replays
+        torch.cuda.synchronize()
+        base = 1 + 4 * r
+        for i in (2, 3):   # the two output buffers hold the last two steps of the replay
+            assert np.array_equal(np64(outs[i]), ref[base + i][0]), (r, i)
+        assert np.array_equal(lay.sel_idx.cpu().numpy(), ref[base + 3][1])
+        assert np.array_equal(lay.n_missed.cpu().numpy(), ref[base + 3][2])
+        del scratch
+    lay.close()
