@@ -15,7 +15,7 @@
 namespace prr {
 
 template <int DT, int G>
-__global__ __launch_bounds__(256) void speculate_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
+__global__ __launch_bounds__(256, 3) void speculate_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
                                                         const uint8_t* __restrict__ vc,
                                                         const int32_t* __restrict__ table,
                                                         const int32_t* __restrict__ pred, int k_spec,
@@ -110,7 +110,7 @@ __device__ void finalize_row(const float* __restrict__ recs, const int32_t* __re
 }
 
 template <int DT, int G>
-__global__ __launch_bounds__(256) void repair_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
+__global__ __launch_bounds__(256, 2) void repair_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
                                                      const uint8_t* __restrict__ vc,
                                                      const int32_t* __restrict__ table,
                                                      const int32_t* __restrict__ sel, int top_k,
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void repair_kernel(const uint8_t* __restrict__
                                                      const float* __restrict__ partials, float* __restrict__ ws_rec,
                                                      int32_t* __restrict__ ws_miss, int Hq, int Hkv, int N, int bs,
                                                      int page, int pps, float qscale, int epw) {
-  using W = AttnWave<DT, G>;
+  using W = Tile<DT, G>;
   constexpr int D = W::D;
   constexpr int RF = rec_floats(G, D);
   constexpr int ML = rec_ml(G);
@@ -159,11 +159,8 @@ __global__ __launch_bounds__(256) void repair_kernel(const uint8_t* __restrict__
   }
   float folded[W::NK];
   st.fold(folded);
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) { s_ml[wave][h] = st.m[h]; s_ml[wave][G + h] = st.l[h]; }
-    s_miss[wave] = misses;
-  }
+  st.store_ml(&s_ml[wave][0]);
+  if (lane == 0) s_miss[wave] = misses;
 #pragma unroll
   for (int i = 0; i < W::NK; ++i) {
     const int f = st.row * W::NK + i;

@@ -1,0 +1,224 @@
+// attn_mfma.h — block-sparse decode-attention tile for 16-bit K/V on gfx950: logits on the matrix cores, p.V on the
+// vector ALUs in fp32.
+//
+// Per chunk of 16 tokens of one block and the G query heads of one KV head:
+//  * S^T = K . Q^T with four v_mfma_f32_16x16x32_{bf16,f16} (k = 128 head dims in 4 slices of 32). The A operand is
+//    the K tile as stored (lane l: token l%16, 8 dims at 8*(l/16) + 32*kk), the B operand the group's queries (lane l:
+//    head l%16, zero beyond G), loaded once. Products of 16-bit values are exact in fp32, so the logits keep the
+//    precision of an fp32 dot product. The result lands with lane l holding tokens 4*(l/16)+r of head l%16.
+//  * Online softmax per head in log2 units (m uniform over the wave's rows after two permlane max-swaps).
+//  * O += p . V in fp32 on the vector ALUs: lane (row, col) loads V rows 4*row+r, dims 8*col.., and takes p of head
+//    h from lane 16*row + h of its row with a ds_swizzle broadcast.
+// Compared with an all-VALU tile this removes the K-side conversions, FMAs and DPP reductions (about two thirds of
+// the vector instructions per byte), which otherwise bound the tile below the HBM rate.
+#pragma once
+#include "prr_device.h"
+#include "prr_launch.h"
+
+namespace prr {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ inline floatx4_t mfma16x16x32(const uint4 a, const uint4 b, floatx4_t c) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+}
+
+// value of `x` in lane 16*(lane/16) + h (broadcast within each 16-lane row)
+template <int H>
+__device__ inline float row_bcast(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x10 | (H << 5)));
+}
+
+template <int DT, int G>
+struct AttnWaveM {
+  using V = Vec<DT>;
+  static constexpr int VE = V::n;       // 8
+  static constexpr int D = 16 * VE;     // 128
+  static constexpr int NV = G * VE;
+  static constexpr int NK = NV / 4;
+  static_assert(DT != kF32, "matrix-core tile is for 16-bit storage");
+
+  uint4 qb[4];        // B operand: query head l%16 (zero beyond G), dims 8*(l/16) + 32*kk
+  float qscale;
+  float m_l, l_l;     // running max (log2 units) and partial sum of head l%16 over this lane's tokens
+  float acc[G][VE];   // partial O over this lane's row tokens, dims 8*col..
+  int lane, row, col;
+
+  __device__ void init(int lane_) {
+    lane = lane_;
+    row = lane >> 4;
+    col = lane & 15;
+    m_l = -__builtin_huge_valf();
+    l_l = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[h][e] = 0.f;
+  }
+
+  __device__ void load_q(const uint8_t* qg, float qs) {   // qg = q + (b*Hq + g*G) * 256
+    qscale = qs;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qb[kk] = col < G ? ld16(qg + col * kRowBytes + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
+  }
+
+  __device__ void block(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                        const int32_t* __restrict__ trow, int n, int bs, int page, int Hkv, int g) {
+    const int64_t tok0 = (int64_t)n * bs;
+    const bool chunk_pages = (page & 15) == 0;
+    for (int t0 = 0; t0 < bs; t0 += 16) {
+      // ---- loads: K (A operand) for token col, V rows 4*row + r -----------------------------------------------
+      uint4 ka[4], vv[4];
+      const bool kok = t0 + col < bs;
+      if (chunk_pages) {
+        const int64_t tc = tok0 + t0;
+        const int64_t phys = trow[tc / page];
+        const uint8_t* base_k = kc + ((phys * Hkv + g) * page + tc % page) * (int64_t)kRowBytes;
+        const uint8_t* base_v = vc + ((phys * Hkv + g) * page + tc % page) * (int64_t)kRowBytes;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          ka[kk] = kok ? ld16(base_k + col * kRowBytes + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 4 * row + r;
+          vv[r] = t0 + t < bs ? ld16(base_v + t * kRowBytes + 16 * col) : make_uint4(0, 0, 0, 0);
+        }
+      } else {
+        const int64_t tk = tok0 + t0 + col;
+        const int64_t pk = kok ? trow[tk / page] : 0;
+        const uint8_t* base_k = kc + ((pk * Hkv + g) * page + tk % page) * (int64_t)kRowBytes;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          ka[kk] = kok ? ld16(base_k + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 4 * row + r;
+          const int64_t tv = tok0 + t0 + t;
+          if (t0 + t < bs) {
+            const int64_t pv = trow[tv / page];
+            vv[r] = ld16(vc + ((pv * Hkv + g) * page + tv % page) * (int64_t)kRowBytes + 16 * col);
+          } else {
+            vv[r] = make_uint4(0, 0, 0, 0);
+          }
+        }
+      }
+      // ---- logits on the matrix cores ------------------------------------------------------------------------
+      floatx4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) c = mfma16x16x32<DT>(ka[kk], qb[kk], c);
+      float z[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) z[r] = t0 + 4 * row + r < bs ? c[r] * qscale : -__builtin_huge_valf();
+      // ---- online softmax for head col ------------------------------------------------------------------------
+      float mc = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+      mc = max_xor32(max_xor16(mc));
+      const float mn = fmaxf(m_l, mc);
+      const float corr = exp2f(m_l - mn);
+      m_l = mn;
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = exp2f(z[r] - mn);
+      l_l = l_l * corr + ((p[0] + p[1]) + (p[2] + p[3]));
+      // ---- O += p . V (fp32) --------------------------------------------------------------------------------
+      float y[4][VE];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) V::to_f32(vv[r], y[r]);
+      accumulate<0>(corr, p, y);
+    }
+  }
+
+  template <int H>
+  __device__ inline void accumulate(float corr, const float* p, float (*y)[VE]) {
+    if constexpr (H < G) {
+      const float ch = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), H));
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[H][e] *= ch;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ph = row_bcast<H>(p[r]);
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[H][e] = fmaf(ph, y[r][e], acc[H][e]);
+      }
+      accumulate<H + 1>(corr, p, y);
+    }
+  }
+
+  // Merge a stored record (m[G] log2, l[G], O[G][D]); its l and O enter through one row only.
+  __device__ void merge_record(const float* __restrict__ rec) {
+    constexpr int ML = rec_ml(G);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mr = rec[h];
+      const float lr = rec[G + h];
+      const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_l), h));
+      const float mn = fmaxf(mh, mr);
+      const float c_old = exp2f(mh - mn);
+      const float c_new = exp2f(mr - mn);
+      if (col == h) {
+        m_l = mn;
+        l_l = l_l * c_old + (row == 0 ? lr * c_new : 0.f);
+      }
+      const bool mine = row == (h & 3);
+      float o[VE] = {};
+      if (mine) {
+        const float* src = rec + ML + h * D + col * VE;
+#pragma unroll
+        for (int e = 0; e < VE; e += 4) {
+          const float4 t = *reinterpret_cast<const float4*>(src + e);
+          o[e] = t.x; o[e + 1] = t.y; o[e + 2] = t.z; o[e + 3] = t.w;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[h][e] = acc[h][e] * c_old + (mine ? o[e] * c_new : 0.f);
+    }
+  }
+
+  // Fold the 4 rows: l_l becomes the total of head col; out[i] holds flat accumulator f = row*NK + i.
+  __device__ void fold(float* out) {
+    l_l = sum_xor32(sum_xor16(l_l));
+    float t[NV / 2];
+#pragma unroll
+    for (int f = 0; f < NV / 2; ++f) {
+      const int f2 = f + NV / 2;
+      t[f] = fold32(acc[f / VE][f % VE], acc[f2 / VE][f2 % VE]);
+    }
+#pragma unroll
+    for (int f = 0; f < NK; ++f) out[f] = fold16(t[f], t[f + NK]);
+  }
+
+  // m[h], l[h] of the folded state into dst[0..G), dst[G..2G).
+  __device__ void store_ml(float* dst) const {
+    if (lane < G) { dst[lane] = m_l; dst[G + lane] = l_l; }
+  }
+
+  __device__ void write_record(float* __restrict__ rec, const float* folded) const {
+    store_ml(rec);
+    float* o = rec + rec_ml(G);
+    if constexpr (NK % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < NK; i += 4) {
+        const int f = row * NK + i;
+        const int h = f / VE, e = f % VE;
+        *reinterpret_cast<float4*>(o + h * D + col * VE + e) =
+            make_float4(folded[i], folded[i + 1], folded[i + 2], folded[i + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const int f = row * NK + i;
+        o[(f / VE) * D + col * VE + (f % VE)] = folded[i];
+      }
+    }
+  }
+};
+
+}  // namespace prr

@@ -11,6 +11,9 @@
 // Partial record (per (b, g, slot)): m[G] (log2 units), l[G], zero padding to a multiple of 4 floats, then O[G][D]
 // (unnormalised), fp32; records are 16-byte aligned.
 #pragma once
+#include <type_traits>
+
+#include "attn_mfma.h"
 #include "prr_device.h"
 #include "prr_launch.h"
 
@@ -159,12 +162,17 @@ struct AttnWave {
     for (int f = 0; f < NK; ++f) out[f] = fold16(t[f], t[f + NK]);
   }
 
-  // Write the folded state as a record.
-  __device__ void write_record(float* __restrict__ rec, const float* folded) {
+  // m[h], l[h] of the folded state into dst[0..G), dst[G..2G).
+  __device__ void store_ml(float* dst) const {
     if (lane == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) { rec[h] = m[h]; rec[G + h] = l[h]; }
+      for (int h = 0; h < G; ++h) { dst[h] = m[h]; dst[G + h] = l[h]; }
     }
+  }
+
+  // Write the folded state as a record.
+  __device__ void write_record(float* __restrict__ rec, const float* folded) {
+    store_ml(rec);
     float* o = rec + ML;
     if constexpr (NK % 4 == 0) {
 #pragma unroll
@@ -184,6 +192,10 @@ struct AttnWave {
   }
 };
 
+// The tile used for a storage dtype: matrix-core logits for 16-bit K/V, all-VALU for fp32.
+template <int DT, int G>
+using Tile = std::conditional_t<DT == kF32, AttnWave<DT, G>, AttnWaveM<(DT == kF32 ? kBF16 : DT), G>>;
+
 // Speculation of one predicted slot s = (b * Hkv + g) * k_spec + j by one wave: the block's partial record.
 template <int DT, int G>
 __device__ inline void speculate_slot(int64_t s, int lane, const uint8_t* __restrict__ q,
@@ -191,7 +203,7 @@ __device__ inline void speculate_slot(int64_t s, int lane, const uint8_t* __rest
                                       const int32_t* __restrict__ table, const int32_t* __restrict__ pred, int k_spec,
                                       float* __restrict__ partials, int Hq, int Hkv, int N, int bs, int page, int pps,
                                       float qscale) {
-  using W = AttnWave<DT, G>;
+  using W = Tile<DT, G>;
   const int64_t rowid = s / k_spec;
   const int b = (int)(rowid / Hkv), g = (int)(rowid % Hkv);
   const int n = min(max(pred[s], 0), N - 1);   // ids outside [0, N) are clamped: wrong output, never a fault

@@ -264,3 +264,37 @@ def test_poison_block_excluded():
                                           w.block_size, w.scale)
             assert max_abs(got[b, g * G:(g + 1) * G], ref) <= TOL[w.dtype]
     assert int(nm.sum()) == 0
+
+
+@pytest.mark.parametrize("n_blocks", [32768, 5000, 1000])
+def test_topk_large_rows(n_blocks):
+    """Rows up to 32768 values (the largest row the top-K kernels take): random values, massive ties, constant rows,
+    a few distinct levels, and rows whose evenly spaced entries hold the extremes. For every K the selection equals
+    the oracle's tie rule (lowest index first among equal values, ascending output)."""
+    s = L.make_shape(1, 16, 2, 128, 16, 16, n_blocks, L.BF16)
+    N, rows = n_blocks, 2
+    rng = np.random.default_rng(21)
+    stride = max(1, N // 1024)
+    cases = {
+        "normal": rng.standard_normal((rows, N)),
+        "constant": np.full((rows, N), 3.5),
+        "few_levels": rng.integers(0, 3, size=(rows, N)).astype(np.float64),
+        "rounded": np.round(rng.standard_normal((rows, N)) * 4),
+    }
+    hi = rng.standard_normal((rows, N))
+    hi[:, ::stride] = 100.0 + rng.random((rows, len(range(0, N, stride))))
+    cases["strided_high"] = hi
+    lo = rng.standard_normal((rows, N)) + 50.0
+    lo[:, ::stride] = -100.0
+    cases["strided_low"] = lo
+    ema = torch.zeros((1, rows, N), dtype=torch.float32, device="cuda")
+    for name, vals in cases.items():
+        v32 = vals.astype(np.float32)
+        for k in sorted({1, 64, 256, min(N, 2000), N}):
+            out = torch.full((1, rows, k), -1, dtype=torch.int32, device="cuda")
+            L.ema_predict(s, torch.as_tensor(v32[None], device="cuda").contiguous(), ema, 0.5, True, k, out)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()[0]
+            for r in range(rows):
+                ref = O.top_k(v32[r].astype(np.float64), k)
+                assert np.array_equal(got[r], ref), (name, k, r)
