@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--detail-out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--other-modes", default="all",
+                    help="comma list of further modes to time beside --mode ('all' or 'none')")
     return ap.parse_args()
 
 
@@ -174,7 +176,9 @@ def main():
     dom_us = dom.get(dominant, float("nan"))
     achieved = alg[dominant] / (dom_us * 1e-6) / 1e9
     other = {}
-    for mode in ("prr_fused", "prr_2stream", "prr_1stream", "serialized"):
+    others = ("prr_fused", "prr_2stream", "prr_1stream", "serialized") if a.other_modes == "all" else \
+        tuple(m for m in a.other_modes.split(",") if m and m != "none")
+    for mode in others:
         if mode != a.mode:
             other[mode] = measure(mode)[0]
 

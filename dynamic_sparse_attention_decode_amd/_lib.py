@@ -19,7 +19,7 @@ _DT_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 # every entry point of include/prr.h
 EXPORTS = ["prr_build_summaries", "prr_score_select", "prr_ema_predict", "prr_speculate", "prr_repair_merge",
-           "prr_score_speculate", "prr_select_predict",
+           "prr_score", "prr_select_speculate",
            "prr_partials_bytes", "prr_workspace_bytes", "prr_step_ctx_create", "prr_step_ctx_destroy",
            "prr_decode_step", "prr_choose_budget", "prr_trace_create", "prr_trace_destroy", "prr_trace_enable",
            "prr_trace_read", "prr_flush_write", "prr_stream_read", "prr_status_string", "prr_last_error",
@@ -85,8 +85,8 @@ def lib():
         "prr_ema_predict": (i32, [sp, vp, vp, f32, i32, i32, vp, vp]),
         "prr_speculate": (i32, [sp, vp, vp, vp, vp, vp, i32, vp, vp]),
         "prr_repair_merge": (i32, [sp, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp]),
-        "prr_score_speculate": (i32, [sp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
-        "prr_select_predict": (i32, [sp, vp, i32, vp, vp, f32, i32, i32, vp, vp]),
+        "prr_score": (i32, [sp, vp, vp, vp, vp, f32, i32, vp]),
+        "prr_select_speculate": (i32, [sp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
         "prr_partials_bytes": (sz, [sp, i32]),
         "prr_workspace_bytes": (sz, [sp, i32]),
         "prr_step_ctx_create": (i32, [ctypes.POINTER(vp)]),
@@ -180,22 +180,23 @@ def repair_merge(shape: Shape, q, k_cache, v_cache, block_table, sel_idx, top_k:
                                   _s(stream)), "repair_merge")
 
 
-def score_speculate(shape: Shape, q, summaries, scores, k_cache=None, v_cache=None, block_table=None, pred_idx=None,
-                    k_spec: int = 0, partials=None, stream=None) -> None:
+def score(shape: Shape, q, summaries, scores, ema=None, alpha: float = 0.0, first_step=False, stream=None) -> None:
     dt = shape.torch_dtype
-    _check(lib().prr_score_speculate(ctypes.byref(shape), _p(q, dt, "q"), _p(summaries, dt, "summaries"),
-                                     _p(scores, torch.float32, "scores"), _p(k_cache, dt, "k_cache"),
-                                     _p(v_cache, dt, "v_cache"), _p(block_table, torch.int32, "block_table"),
-                                     _p(pred_idx, torch.int32, "pred_idx"), k_spec,
-                                     _p(partials, torch.float32, "partials"), _s(stream)), "score_speculate")
+    _check(lib().prr_score(ctypes.byref(shape), _p(q, dt, "q"), _p(summaries, dt, "summaries"),
+                           _p(scores, torch.float32, "scores"), _p(ema, torch.float32, "ema"), alpha,
+                           int(bool(first_step)), _s(stream)), "score")
 
 
-def select_predict(shape: Shape, scores, top_k: int, sel_idx, ema=None, alpha: float = 0.0, first_step=False,
-                   k_spec_next: int = 0, pred_idx_next=None, stream=None) -> None:
-    _check(lib().prr_select_predict(ctypes.byref(shape), _p(scores, torch.float32, "scores"), top_k,
-                                    _p(sel_idx, torch.int32, "sel_idx"), _p(ema, torch.float32, "ema"), alpha,
-                                    int(bool(first_step)), k_spec_next,
-                                    _p(pred_idx_next, torch.int32, "pred_idx_next"), _s(stream)), "select_predict")
+def select_speculate(shape: Shape, scores, top_k: int, sel_idx, ema=None, k_spec_next: int = 0, pred_idx_next=None,
+                     q=None, k_cache=None, v_cache=None, block_table=None, pred_idx=None, k_spec: int = 0,
+                     partials=None, stream=None) -> None:
+    dt = shape.torch_dtype
+    _check(lib().prr_select_speculate(ctypes.byref(shape), _p(scores, torch.float32, "scores"), top_k,
+                                      _p(sel_idx, torch.int32, "sel_idx"), _p(ema, torch.float32, "ema"), k_spec_next,
+                                      _p(pred_idx_next, torch.int32, "pred_idx_next"), _p(q, dt, "q"),
+                                      _p(k_cache, dt, "k_cache"), _p(v_cache, dt, "v_cache"),
+                                      _p(block_table, torch.int32, "block_table"), _p(pred_idx, torch.int32, "pred_idx"),
+                                      k_spec, _p(partials, torch.float32, "partials"), _s(stream)), "select_speculate")
 
 
 def partials_bytes(shape: Shape, k_spec: int) -> int:

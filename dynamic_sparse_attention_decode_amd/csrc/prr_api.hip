@@ -198,7 +198,7 @@ prr_status prr_score_select(const prr_shape* shape, const void* q, const void* s
   PRR_REQUIRE(q && summaries && scores && sel_idx, "score_select: null pointer");
   PRR_REQUIRE(top_k >= 1 && top_k <= shape->n_blocks, "score_select: top_k %d not in [1, %d]", top_k,
               shape->n_blocks);
-  PRR_TRY(launch_score(*shape, q, summaries, scores, as_stream(stream)));
+  PRR_TRY(launch_score(*shape, q, summaries, scores, nullptr, 0.f, 0, as_stream(stream)));
   return launch_topk(*shape, scores, nullptr, 0.f, 0, top_k, sel_idx, as_stream(stream));
 }
 
@@ -240,34 +240,36 @@ prr_status prr_repair_merge(const prr_shape* shape, const void* q, const void* k
                        k_spec, k_spec ? partials : nullptr, out, n_missed, workspace, as_stream(stream));
 }
 
-prr_status prr_score_speculate(const prr_shape* shape, const void* q, const void* summaries, float* scores,
-                               const void* k_cache, const void* v_cache, const int32_t* block_table,
-                               const int32_t* pred_idx, int32_t k_spec, float* partials, void* stream) {
+prr_status prr_score(const prr_shape* shape, const void* q, const void* summaries, float* scores, float* ema,
+                     float alpha, int32_t first_step, void* stream) {
   PRR_TRY(check_shape(shape));
-  PRR_REQUIRE(q && summaries && scores, "score_speculate: null pointer");
-  PRR_REQUIRE(k_spec >= 0 && k_spec <= shape->n_blocks, "score_speculate: k_spec %d not in [0, %d]", k_spec,
-              shape->n_blocks);
-  if (k_spec > 0)
-    PRR_REQUIRE(k_cache && v_cache && block_table && pred_idx && partials, "score_speculate: null pointer");
-  return launch_score_spec(*shape, q, summaries, scores, k_cache, v_cache, block_table, pred_idx, k_spec, partials,
-                           as_stream(stream));
+  PRR_REQUIRE(q && summaries && scores, "score: null pointer");
+  if (ema) PRR_REQUIRE(alpha >= 0.f && alpha <= 1.f, "score: alpha not in [0, 1]");
+  return launch_score(*shape, q, summaries, scores, ema, alpha, first_step ? 1 : 0, as_stream(stream));
 }
 
-prr_status prr_select_predict(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
-                              float* ema, float alpha, int32_t first_step, int32_t k_spec_next,
-                              int32_t* pred_idx_next, void* stream) {
+prr_status prr_select_speculate(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
+                                const float* ema, int32_t k_spec_next, int32_t* pred_idx_next, const void* q,
+                                const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                const int32_t* pred_idx, int32_t k_spec, float* partials, void* stream) {
   PRR_TRY(check_shape(shape));
   PRR_TRY(check_topk_n(shape));
-  PRR_REQUIRE(scores && sel_idx, "select_predict: null pointer");
-  PRR_REQUIRE(top_k >= 1 && top_k <= shape->n_blocks, "select_predict: top_k %d not in [1, %d]", top_k,
+  PRR_REQUIRE(scores && sel_idx, "select_speculate: null pointer");
+  PRR_REQUIRE(top_k >= 1 && top_k <= shape->n_blocks, "select_speculate: top_k %d not in [1, %d]", top_k,
               shape->n_blocks);
-  PRR_REQUIRE(k_spec_next >= 0 && k_spec_next <= shape->n_blocks, "select_predict: k_spec_next %d not in [0, %d]",
+  PRR_REQUIRE(k_spec_next >= 0 && k_spec_next <= shape->n_blocks, "select_speculate: k_spec_next %d not in [0, %d]",
               k_spec_next, shape->n_blocks);
-  if (k_spec_next == 0) return launch_topk(*shape, scores, nullptr, 0.f, 0, top_k, sel_idx, as_stream(stream));
-  PRR_REQUIRE(ema && pred_idx_next, "select_predict: null pointer");
-  PRR_REQUIRE(alpha >= 0.f && alpha <= 1.f, "select_predict: alpha not in [0, 1]");
-  return launch_topk_pair(*shape, scores, top_k, sel_idx, ema, alpha, first_step ? 1 : 0, k_spec_next,
-                          pred_idx_next, as_stream(stream));
+  PRR_REQUIRE(k_spec >= 0 && k_spec <= shape->n_blocks, "select_speculate: k_spec %d not in [0, %d]", k_spec,
+              shape->n_blocks);
+  if (k_spec_next > 0) PRR_REQUIRE(ema && pred_idx_next, "select_speculate: k_spec_next > 0 needs ema and pred_idx_next");
+  if (k_spec > 0)
+    PRR_REQUIRE(q && k_cache && v_cache && block_table && pred_idx && partials, "select_speculate: null pointer");
+  if (k_spec > 0 && k_spec_next > 0 && pred_idx == pred_idx_next) {
+    set_error("select_speculate: pred_idx and pred_idx_next must be different buffers");
+    return PRR_EINVAL;
+  }
+  return launch_select_spec(*shape, scores, top_k, sel_idx, ema, k_spec_next, pred_idx_next, q, k_cache, v_cache,
+                            block_table, pred_idx, k_spec, partials, as_stream(stream));
 }
 
 size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec) {
@@ -329,10 +331,9 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
   PRR_REQUIRE(kc >= 0 && kn >= 0, "decode_step: negative k_spec");
 
   if (mode == PRR_MODE_FUSED) {
-    PRR_TRY(prr_score_speculate(shape, a->q, a->summaries, a->scores, a->k_cache, a->v_cache, a->block_table,
-                                a->pred_cur, kc, a->partials, s1));
-    PRR_TRY(prr_select_predict(shape, a->scores, a->top_k, a->sel_idx, a->ema, a->alpha, a->first_step, kn,
-                               a->pred_next, s1));
+    PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step, s1));
+    PRR_TRY(prr_select_speculate(shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,
+                                 a->v_cache, a->block_table, a->pred_cur, kc, a->partials, s1));
     return prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
                             kc, a->partials, a->out, a->n_missed, a->workspace, s1);
   }

@@ -51,7 +51,9 @@ void trace_end(int kid, hipStream_t stream);
 
 prr_status launch_summaries(const prr_shape& s, const void* k_cache, const int32_t* table, const int32_t* ids,
                             int64_t n_jobs, void* summ, hipStream_t stream);
-prr_status launch_score(const prr_shape& s, const void* q, const void* summ, float* scores, hipStream_t stream);
+// Scores; with ema != nullptr also the EMA update (first != 0: ema = scores).
+prr_status launch_score(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema, float alpha,
+                        int first, hipStream_t stream);
 prr_status launch_topk(const prr_shape& s, const float* values, float* ema, float alpha, int first, int k,
                        int32_t* out_idx, hipStream_t stream);
 prr_status launch_speculate(const prr_shape& s, const void* q, const void* k_cache, const void* v_cache,
@@ -61,11 +63,10 @@ prr_status launch_repair(const prr_shape& s, const void* q, const void* k_cache,
                          const int32_t* table, const int32_t* sel, int top_k, const int32_t* pred, int k_spec,
                          const float* partials, float* out, int32_t* n_missed, void* workspace, hipStream_t stream);
 size_t repair_workspace_bytes(const prr_shape& s, int top_k);
-prr_status launch_score_spec(const prr_shape& s, const void* q, const void* summ, float* scores, const void* kc,
-                             const void* vc, const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                             hipStream_t stream);
-prr_status launch_topk_pair(const prr_shape& s, const float* scores, int k, int32_t* sel, float* ema, float alpha,
-                            int first, int kp, int32_t* pred, hipStream_t stream);
+prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
+                              int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
+                              const int32_t* table, const int32_t* pred, int k_spec, float* partials,
+                              hipStream_t stream);
 prr_status launch_flush(void* buf, size_t bytes, hipStream_t stream);
 prr_status launch_stream_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 

@@ -1,5 +1,5 @@
-// score_dev.h — Quest block scoring as a streaming GEMV (PRR reference list, Quest), shared by the scoring kernel
-// and the fused scoring + speculation kernel.
+// score_dev.h — Quest block scoring as a streaming GEMV (PRR reference list, Quest), optionally fused with the EMA
+// predictor's update (PRR abstract: "lightweight EMA-based predictor").
 //
 // s[b,g,n] = sum_d Qpos_d * kmax[n,d] + Qneg_d * kmin[n,d] with Qpos_d = sum_h max(q_hd, 0) and
 // Qneg_d = sum_h min(q_hd, 0) over the group's query heads. Because kmin <= kmax, max(q*kmin, q*kmax) equals
@@ -12,10 +12,12 @@
 
 namespace prr {
 
-// Scores of blocks [bx * chunk, (bx + 1) * chunk) of row bg = b * Hkv + g, by one 256-thread workgroup.
-template <int DT, int G>
+// Scores of blocks [bx * chunk, (bx + 1) * chunk) of row bg = b * Hkv + g, by one 256-thread workgroup. With EMA
+// the same pass updates the row's average in place: e = s on the first step, else alpha e + (1 - alpha) s.
+template <int DT, int G, bool EMA>
 __device__ inline void score_chunk(int bx, int bg, const uint8_t* __restrict__ q, const uint8_t* __restrict__ summ,
-                                   float* __restrict__ scores, int Hq, int Hkv, int N, int chunk) {
+                                   float* __restrict__ scores, int Hq, int Hkv, int N, int chunk,
+                                   float* __restrict__ ema, float alpha, int first) {
   using V = Vec<DT>;
   constexpr int U = 8;   // wave loads in flight per lane
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -37,12 +39,16 @@ __device__ inline void score_chunk(int bx, int bg, const uint8_t* __restrict__ q
   const int c1 = min(N, c0 + chunk);
   const uint8_t* base = summ + (int64_t)bg * N * (2 * kRowBytes) + half * kRowBytes + col * 16;
   float* srow = scores + (int64_t)bg * N;
+  float* erow = EMA ? ema + (int64_t)bg * N : nullptr;
+  const bool owner = (lane & 31) == 0;   // lanes 0 and 32 hold their block's score after the fold
   for (int n0 = c0 + wave * 2 + pair; n0 < c1; n0 += 8 * U) {
     uint4 v[U];
+    float e_old[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int n = n0 + 8 * u;
       v[u] = n < c1 ? ld16(base + (int64_t)n * (2 * kRowBytes)) : make_uint4(0, 0, 0, 0);
+      e_old[u] = (EMA && !first && owner && n < c1) ? erow[n] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -53,7 +59,10 @@ __device__ inline void score_chunk(int bx, int bg, const uint8_t* __restrict__ q
       for (int e = 0; e < V::n; ++e) s = fmaf(coef[e], x[e], s);
       s = sum_xor16(row_sum16(s));
       const int n = n0 + 8 * u;
-      if ((lane & 31) == 0 && n < c1) srow[n] = s;
+      if (owner && n < c1) {
+        srow[n] = s;
+        if (EMA) erow[n] = first ? s : fmaf(alpha, e_old[u], (1.f - alpha) * s);
+      }
     }
   }
 }

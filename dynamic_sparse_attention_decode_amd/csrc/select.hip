@@ -2,196 +2,19 @@
 // query; PRR reference list, Quest: block scores from per-block key min/max), and the EMA predictor's update and
 // top-K' (PRR abstract: "lightweight EMA-based predictor").
 //
-// score_kernel: Quest's group-summed block score as a streaming GEMV (score_dev.h).
-//
-// topk_kernel: one 1024-thread workgroup per (b, g) row holds the row's N values in registers as order-preserving
-//   uint32 keys (thread t owns indices [t*KPT, (t+1)*KPT)). A most-significant-digit radix select finds the K-th
-//   largest key: the first digit starts at the highest bit in which the row's keys differ, 8-bit digits, LDS
-//   histogram, early exit when a whole digit bin is taken. Compaction takes every key above the threshold class and
-//   the lowest-index keys of the threshold class; one workgroup-wide scan gives each thread its output offset, so
-//   the output comes out in ascending block order. Optionally updates the EMA in the same pass.
+// score_kernel: Quest's group-summed block score as a streaming GEMV over all CUs (score_dev.h); optionally updates
+//   the EMA in the same pass.
+// topk_kernel: one 1024-thread workgroup per (b, g) row (topk_dev.h); optionally updates the EMA first.
 #include "score_dev.h"
+#include "topk_dev.h"
 
 namespace prr {
 
-template <int DT, int G>
+template <int DT, int G, bool EMA>
 __global__ __launch_bounds__(256) void score_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ summ,
-                                                    float* __restrict__ scores, int Hq, int Hkv, int N, int chunk) {
-  score_chunk<DT, G>(blockIdx.x, blockIdx.y, q, summ, scores, Hq, Hkv, N, chunk);
-}
-
-// ---- workgroup helpers for the 1024-thread top-K kernel ----------------------------------------------------------
-
-__device__ inline uint32_t wave_incl_scan(uint32_t x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t t = __shfl_up(x, d);
-    if (lane >= d) x += t;
-  }
-  return x;
-}
-
-__device__ inline uint32_t wave_suffix_incl(uint32_t x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t t = __shfl_down(x, d);
-    if (lane + d < 64) x += t;
-  }
-  return x;
-}
-
-__device__ inline uint32_t shr(uint32_t x, int s) { return s >= 32 ? 0u : x >> s; }
-
-// Top-K of one row of N values (optionally after the EMA update e = alpha e + (1 - alpha) v, written back), by one
-// 1024-thread workgroup; out_row receives K ascending indices.
-template <int KPT, bool EMA>
-__device__ void topk_row(const float* __restrict__ v, float* __restrict__ e_row, float alpha, int first, int N, int K,
-                         int32_t* __restrict__ orow) {
-  __shared__ uint32_t hist[256];
-  __shared__ float red_f[2][16];
-  __shared__ uint32_t red_u[16];
-  __shared__ uint32_t bc[3];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i0 = tid * KPT;
-
-  // ---- load (and EMA update) --------------------------------------------------------------------------------
-  float x[KPT];
-  if (KPT % 4 == 0 && (N & 3) == 0 && i0 + KPT <= N) {
-#pragma unroll
-    for (int k = 0; k < KPT; k += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(v + i0 + k);
-      x[k] = a.x; x[k + 1] = a.y; x[k + 2] = a.z; x[k + 3] = a.w;
-    }
-    if (EMA) {
-#pragma unroll
-      for (int k = 0; k < KPT; k += 4) {
-        float4 o = *reinterpret_cast<const float4*>(e_row + i0 + k);
-        if (!first) {
-          o.x = fmaf(alpha, o.x, (1.f - alpha) * x[k]);
-          o.y = fmaf(alpha, o.y, (1.f - alpha) * x[k + 1]);
-          o.z = fmaf(alpha, o.z, (1.f - alpha) * x[k + 2]);
-          o.w = fmaf(alpha, o.w, (1.f - alpha) * x[k + 3]);
-        } else {
-          o = make_float4(x[k], x[k + 1], x[k + 2], x[k + 3]);
-        }
-        *reinterpret_cast<float4*>(e_row + i0 + k) = o;
-        x[k] = o.x; x[k + 1] = o.y; x[k + 2] = o.z; x[k + 3] = o.w;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-      const int i = i0 + k;
-      if (i < N) {
-        float s = v[i];
-        if (EMA) {
-          s = first ? s : fmaf(alpha, e_row[i], (1.f - alpha) * s);
-          e_row[i] = s;
-        }
-        x[k] = s;
-      } else {
-        x[k] = 0.f;
-      }
-    }
-  }
-
-  // ---- row range of the keys --------------------------------------------------------------------------------
-  float lmax = -__builtin_huge_valf(), lmin = __builtin_huge_valf();
-  uint32_t key[KPT];
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const bool ok = i0 + k < N;
-    key[k] = ok ? f2key(x[k]) : 0u;
-    if (ok) { lmax = fmaxf(lmax, x[k]); lmin = fminf(lmin, x[k]); }
-  }
-  lmax = wave_max(lmax);
-  lmin = -wave_max(-lmin);
-  if (lane == 0) { red_f[0][wave] = lmax; red_f[1][wave] = lmin; }
-  __syncthreads();
-  float gmax = red_f[0][0], gmin = red_f[1][0];
-#pragma unroll
-  for (int w = 1; w < 16; ++w) { gmax = fmaxf(gmax, red_f[0][w]); gmin = fminf(gmin, red_f[1][w]); }
-  const uint32_t kmax = f2key(gmax), kmin = f2key(gmin);
-
-  // ---- MSD radix select ---------------------------------------------------------------------------------------
-  uint32_t prefix = kmax;
-  int shift = 0;
-  uint32_t krem = (uint32_t)K;
-  if (kmax != kmin) {
-    const int hb = 31 - __clz(kmax ^ kmin);
-    shift = hb + 1;
-    prefix = shift >= 32 ? 0u : (kmax >> shift) << shift;
-  }
-  while (shift > 0) {
-    const int db = shift < 8 ? shift : 8;
-    const int ns = shift - db;
-    if (tid < 256) hist[tid] = 0u;
-    __syncthreads();
-    const uint32_t pk = shr(prefix, shift);
-    const uint32_t dmask = (1u << db) - 1u;
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-      if (i0 + k < N && shr(key[k], shift) == pk) atomicAdd(&hist[(key[k] >> ns) & dmask], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t c[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) c[j] = hist[4 * lane + j];
-      const uint32_t lsum = c[0] + c[1] + c[2] + c[3];
-      uint32_t above = wave_suffix_incl(lsum, lane) - lsum;
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (above < krem && krem <= above + c[j]) { bc[0] = 4 * lane + j; bc[1] = above; bc[2] = c[j]; }
-        above += c[j];
-      }
-    }
-    __syncthreads();
-    const uint32_t bin = bc[0];
-    krem -= bc[1];
-    prefix |= bin << ns;
-    shift = ns;
-    if (bc[2] == krem) break;   // the whole bin is selected: no further digits needed
-  }
-
-  // ---- compaction in ascending index order ---------------------------------------------------------------------
-  const uint32_t pk = shr(prefix, shift);
-  uint32_t cg = 0, ce = 0;
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    if (i0 + k < N) {
-      const uint32_t hk = shr(key[k], shift);
-      cg += hk > pk;
-      ce += hk == pk;
-    }
-  }
-  const uint32_t packed = (cg << 16) | ce;
-  const uint32_t incl = wave_incl_scan(packed, lane);
-  if (lane == 63) red_u[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int w = 0; w < wave; ++w) before += red_u[w];
-  const uint32_t excl = before + incl - packed;
-  const uint32_t pre_g = excl >> 16, pre_e = excl & 0xffffu;
-  uint32_t pos = pre_g + (pre_e < krem ? pre_e : krem);
-  uint32_t le = pre_e;
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int i = i0 + k;
-    if (i < N) {
-      const uint32_t hk = shr(key[k], shift);
-      if (hk > pk) {
-        if (pos < (uint32_t)K) orow[pos] = i;   // pos < K always holds; the guard keeps a logic error in bounds
-        ++pos;
-      } else if (hk == pk) {
-        if (le < krem) {
-          if (pos < (uint32_t)K) orow[pos] = i;
-          ++pos;
-        }
-        ++le;
-      }
-    }
-  }
+                                                    float* __restrict__ scores, int Hq, int Hkv, int N, int chunk,
+                                                    float* __restrict__ ema, float alpha, int first) {
+  score_chunk<DT, G, EMA>(blockIdx.x, blockIdx.y, q, summ, scores, Hq, Hkv, N, chunk, ema, alpha, first);
 }
 
 template <int KPT, bool EMA>
@@ -202,47 +25,28 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ va
   topk_row<KPT, EMA>(vals + row * N, EMA ? ema + row * N : nullptr, alpha, first, N, K, out + row * K);
 }
 
-// True top-K (workgroups [0, rows)) and the EMA update + top-K' prediction (workgroups [rows, 2 rows)) in one
-// launch: both read the same scores, so the prediction costs no extra step on the critical path.
-template <int KPT>
-__global__ __launch_bounds__(1024) void topk_pair_kernel(const float* __restrict__ scores, int K,
-                                                         int32_t* __restrict__ sel, float* __restrict__ ema,
-                                                         float alpha, int first, int Kp,
-                                                         int32_t* __restrict__ pred, int N, int rows) {
-  const int64_t r = blockIdx.x;
-  if (r < rows)
-    topk_row<KPT, false>(scores + r * N, nullptr, alpha, first, N, K, sel + r * K);
-  else
-    topk_row<KPT, true>(scores + (r - rows) * N, ema + (r - rows) * N, alpha, first, N, Kp, pred + (r - rows) * Kp);
-}
-
 // ---- launchers -----------------------------------------------------------------------------------------------------
 
-template <int DT>
-static void score_dispatch(const prr_shape& s, dim3 grid, const uint8_t* q, const uint8_t* sm, float* scores,
-                           int chunk, hipStream_t st) {
-  const int G = s.n_q_heads / s.n_kv_heads;
-  const dim3 blk(256);
-  switch (G) {
-    case 1: score_kernel<DT, 1><<<grid, blk, 0, st>>>(q, sm, scores, s.n_q_heads, s.n_kv_heads, s.n_blocks, chunk); break;
-    case 2: score_kernel<DT, 2><<<grid, blk, 0, st>>>(q, sm, scores, s.n_q_heads, s.n_kv_heads, s.n_blocks, chunk); break;
-    case 4: score_kernel<DT, 4><<<grid, blk, 0, st>>>(q, sm, scores, s.n_q_heads, s.n_kv_heads, s.n_blocks, chunk); break;
-    default: score_kernel<DT, 8><<<grid, blk, 0, st>>>(q, sm, scores, s.n_q_heads, s.n_kv_heads, s.n_blocks, chunk); break;
-  }
-}
-
-prr_status launch_score(const prr_shape& s, const void* q, const void* summ, float* scores, hipStream_t stream) {
+template <int DT, int G>
+static void score_launch(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema, float alpha,
+                         int first, hipStream_t st) {
   const int rows = s.batch * s.n_kv_heads;
   const int chunk = score_chunk_size(s);
-  const dim3 grid((unsigned)((s.n_blocks + chunk - 1) / chunk), (unsigned)rows);
+  const dim3 grid((unsigned)((s.n_blocks + chunk - 1) / chunk), (unsigned)rows), blk(256);
   const auto* qq = static_cast<const uint8_t*>(q);
   const auto* sm = static_cast<const uint8_t*>(summ);
+  if (ema)
+    score_kernel<DT, G, true><<<grid, blk, 0, st>>>(qq, sm, scores, s.n_q_heads, s.n_kv_heads, s.n_blocks, chunk,
+                                                    ema, alpha, first);
+  else
+    score_kernel<DT, G, false><<<grid, blk, 0, st>>>(qq, sm, scores, s.n_q_heads, s.n_kv_heads, s.n_blocks, chunk,
+                                                     nullptr, 0.f, 0);
+}
+
+prr_status launch_score(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema, float alpha,
+                        int first, hipStream_t stream) {
   trace_begin(PRR_KERNEL_SCORE, stream);
-  switch (s.dtype) {
-    case kF32: score_dispatch<kF32>(s, grid, qq, sm, scores, chunk, stream); break;
-    case kBF16: score_dispatch<kBF16>(s, grid, qq, sm, scores, chunk, stream); break;
-    default: score_dispatch<kF16>(s, grid, qq, sm, scores, chunk, stream); break;
-  }
+  PRR_DISPATCH_DT_G(score_launch, s, q, summ, scores, ema, alpha, first, stream);
   trace_end(PRR_KERNEL_SCORE, stream);
   return check_launch("score");
 }
@@ -261,15 +65,10 @@ static void topk_dispatch(int kpt, dim3 grid, const float* vals, float* ema, flo
   }
 }
 
-static int topk_kpt(const prr_shape& s) {
-  int kpt = 1;
-  while (kpt * 1024 < s.n_blocks) kpt *= 2;
-  return kpt;
-}
 
 prr_status launch_topk(const prr_shape& s, const float* values, float* ema, float alpha, int first, int k,
                        int32_t* out_idx, hipStream_t stream) {
-  const int kpt = topk_kpt(s);
+  const int kpt = topk_kpt(s.n_blocks);
   const dim3 grid((unsigned)(s.batch * s.n_kv_heads));
   const int kid = ema ? PRR_KERNEL_EMA_TOPK : PRR_KERNEL_SELECT_TOPK;
   trace_begin(kid, stream);
@@ -279,28 +78,6 @@ prr_status launch_topk(const prr_shape& s, const float* values, float* ema, floa
     topk_dispatch<false>(kpt, grid, values, nullptr, alpha, first, s.n_blocks, k, out_idx, stream);
   trace_end(kid, stream);
   return check_launch(ema ? "ema_predict" : "select_topk");
-}
-
-}  // namespace prr
-
-namespace prr {
-
-prr_status launch_topk_pair(const prr_shape& s, const float* scores, int k, int32_t* sel, float* ema, float alpha,
-                            int first, int kp, int32_t* pred, hipStream_t stream) {
-  const int rows = s.batch * s.n_kv_heads;
-  const dim3 grid((unsigned)(2 * rows)), blk(1024);
-  const int N = s.n_blocks;
-  trace_begin(PRR_KERNEL_SELECT_TOPK, stream);
-  switch (topk_kpt(s)) {
-    case 1: topk_pair_kernel<1><<<grid, blk, 0, stream>>>(scores, k, sel, ema, alpha, first, kp, pred, N, rows); break;
-    case 2: topk_pair_kernel<2><<<grid, blk, 0, stream>>>(scores, k, sel, ema, alpha, first, kp, pred, N, rows); break;
-    case 4: topk_pair_kernel<4><<<grid, blk, 0, stream>>>(scores, k, sel, ema, alpha, first, kp, pred, N, rows); break;
-    case 8: topk_pair_kernel<8><<<grid, blk, 0, stream>>>(scores, k, sel, ema, alpha, first, kp, pred, N, rows); break;
-    case 16: topk_pair_kernel<16><<<grid, blk, 0, stream>>>(scores, k, sel, ema, alpha, first, kp, pred, N, rows); break;
-    default: topk_pair_kernel<32><<<grid, blk, 0, stream>>>(scores, k, sel, ema, alpha, first, kp, pred, N, rows); break;
-  }
-  trace_end(PRR_KERNEL_SELECT_TOPK, stream);
-  return check_launch("select_predict");
 }
 
 }  // namespace prr

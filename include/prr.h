@@ -112,18 +112,21 @@ prr_status prr_repair_merge(const prr_shape* shape, const void* q, const void* k
                             const int32_t* pred_idx, int32_t k_spec, const float* partials, float* out,
                             int32_t* n_missed, void* workspace, void* stream);
 
-/* Scoring and speculation in ONE launch: the scores of prr_score_select plus the partials of prr_speculate
- * (workgroups of the two roles run concurrently, so speculation overlaps selection without a second stream).
- * k_spec == 0 only scores. Same layouts and requirements as the two calls it combines. */
-prr_status prr_score_speculate(const prr_shape* shape, const void* q, const void* summaries, float* scores,
-                               const void* k_cache, const void* v_cache, const int32_t* block_table,
-                               const int32_t* pred_idx, int32_t k_spec, float* partials, void* stream);
+/* Block scores alone (as in prr_score_select) and, when ema != NULL, the EMA update of prr_ema_predict in the same
+ * pass over the summaries (ema = scores when first_step != 0, else alpha * ema + (1 - alpha) * scores, in place). The
+ * first half of the fused single-stream step; prr_select_speculate is the second. */
+prr_status prr_score(const prr_shape* shape, const void* q, const void* summaries, float* scores, float* ema,
+                     float alpha, int32_t first_step, void* stream);
 
-/* The true top-K from `scores` (as in prr_score_select) and, when k_spec_next > 0, the EMA update and top-K'
- * prediction of prr_ema_predict, in ONE launch (both only read the scores). k_spec_next == 0 selects only. */
-prr_status prr_select_predict(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
-                              float* ema, float alpha, int32_t first_step, int32_t k_spec_next,
-                              int32_t* pred_idx_next, void* stream);
+/* In ONE launch: the true top-K of `scores` into sel_idx (as prr_score_select); when k_spec_next > 0 the next
+ * step's predicted set pred_idx_next = top-k_spec_next of `ema` (already updated by prr_score; ties to the lower
+ * index, ascending); and the speculation of prr_speculate over pred_idx (k_spec slots) into `partials`.
+ * Selection occupies one workgroup per row and is bound by latency, so speculation runs in its shadow (PRR
+ * abstract: speculation overlaps selection). pred_idx and pred_idx_next must be different buffers. */
+prr_status prr_select_speculate(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
+                                const float* ema, int32_t k_spec_next, int32_t* pred_idx_next, const void* q,
+                                const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                const int32_t* pred_idx, int32_t k_spec, float* partials, void* stream);
 
 /* Bytes of the partials buffer for a speculation budget k_spec (0 for k_spec == 0). */
 size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec);
@@ -137,7 +140,8 @@ typedef enum {
   PRR_MODE_ONE_STREAM = 1,  /* stream_sel: speculate -> score_select -> repair_merge -> ema_predict                */
   PRR_MODE_TWO_STREAM = 2,  /* stream_spec: speculate || stream_sel: score_select; then repair_merge on stream_sel
                                while ema_predict runs on stream_spec                                            */
-  PRR_MODE_FUSED = 3        /* stream_sel only: score_speculate -> select_predict -> repair_merge (3 launches)   */
+  PRR_MODE_FUSED = 3        /* stream_sel only: score (+ EMA update) -> select_speculate (T, P_{t+1} and the
+                               speculation over P_t in one launch) -> repair_merge                              */
 } prr_mode;
 
 typedef struct {

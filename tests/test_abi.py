@@ -65,6 +65,14 @@ def test_argument_validation_without_launch():
     assert lib.prr_score_select(ctypes.byref(s), None, nz, 8, nz, nz, None) == -1          # null q
     assert lib.prr_score_select(ctypes.byref(s), nz, nz, 0, nz, nz, None) == -1            # K < 1
     assert lib.prr_score_select(ctypes.byref(s), nz, nz, 2049, nz, nz, None) == -1         # K > N
+    assert lib.prr_score(ctypes.byref(s), nz, None, nz, None, 0.5, 0, None) == -1         # null summaries
+    assert lib.prr_score(ctypes.byref(s), nz, nz, nz, nz, -0.5, 0, None) == -1            # alpha < 0 with an EMA
+    # select_speculate: prediction needs the EMA; speculation needs its buffers; P_t and P_{t+1} buffers differ
+    assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, None, 8, nz, None, None, None, None, None, 0, None,
+                                    None) == -1
+    assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, None, 0, None, nz, None, nz, nz, nz, 4, nz,
+                                    None) == -1
+    assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, nz, 8, nz, nz, nz, nz, nz, nz, 8, nz, None) == -1
     assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 0.9, 0, 0, nz, None) == -1        # K' < 1
     assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 1.5, 0, 8, nz, None) == -1        # alpha > 1
     assert lib.prr_speculate(ctypes.byref(s), nz, nz, nz, nz, nz, -1, nz, None) == -1      # K' < 0

@@ -298,3 +298,35 @@ def test_topk_large_rows(n_blocks):
             for r in range(rows):
                 ref = O.top_k(v32[r].astype(np.float64), k)
                 assert np.array_equal(got[r], ref), (name, k, r)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_fused_launches_match_separate(name):
+    """prr_score (with the EMA update) followed by prr_select_speculate produce, bit for bit, the scores, EMA, true
+    set, next predicted set and speculation partials of the separate calls (score_select, ema_predict, speculate)."""
+    w, inp, s, summ, ov = _setup(name)
+    B, Hkv, N, K = w.batch, w.n_kv_heads, w.n_blocks, w.top_k
+    Kp = max(w.k_spec) or K
+    dev = "cuda"
+    sc_a, sc_b = (torch.zeros((B, Hkv, N), dtype=torch.float32, device=dev) for _ in range(2))
+    em_a, em_b = (torch.zeros((B, Hkv, N), dtype=torch.float32, device=dev) for _ in range(2))
+    sel_a, sel_b = (torch.full((B, Hkv, K), -1, dtype=torch.int32, device=dev) for _ in range(2))
+    pn_a, pn_b = (torch.full((B, Hkv, Kp), -1, dtype=torch.int32, device=dev) for _ in range(2))
+    pb = L.partials_bytes(s, Kp) // 4
+    pa_a, pa_b = (torch.zeros((pb,), dtype=torch.float32, device=dev) for _ in range(2))
+    rng = np.random.default_rng(11)
+    for t in range(3):
+        q = inp.q[t].contiguous()
+        cur = torch.as_tensor(np.stack([np.sort(rng.choice(N, Kp, replace=False)) for _ in range(B * Hkv)])
+                              .reshape(B, Hkv, Kp).astype(np.int32), device=dev)
+        L.score_select(s, q, summ, K, sc_a, sel_a)
+        L.ema_predict(s, sc_a, em_a, w.alpha, t == 0, Kp, pn_a)
+        L.speculate(s, q, inp.k_cache, inp.v_cache, inp.table, cur, Kp, pa_a)
+        L.score(s, q, summ, sc_b, em_b, w.alpha, t == 0)
+        L.select_speculate(s, sc_b, K, sel_b, em_b, Kp, pn_b, q, inp.k_cache, inp.v_cache, inp.table, cur, Kp, pa_b)
+        torch.cuda.synchronize()
+        assert torch.equal(sc_a, sc_b), t
+        assert torch.equal(em_a.view(torch.int32), em_b.view(torch.int32)), t
+        assert torch.equal(sel_a, sel_b), t
+        assert torch.equal(pn_a, pn_b), t
+        assert torch.equal(pa_a.view(torch.int32), pa_b.view(torch.int32)), t
