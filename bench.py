@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_32k")
     ap.add_argument("--kspec", type=int, default=None, help="speculation budget (default: the workload's largest)")
     ap.add_argument("--layers", type=int, default=0, help="KV copies to rotate over (0 = auto)")
-    ap.add_argument("--mode", default="prr_2stream", choices=["prr_2stream", "prr_fused", "prr_1stream", "serialized"])
+    ap.add_argument("--mode", default="prr_fused", choices=["prr_fused", "prr_2stream", "prr_1stream", "serialized"])
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -86,13 +86,12 @@ def main():
             for lay in layers:
                 lay.enqueue(qs[lay.t % w.steps])
 
-    # bytes each kernel must move per launch
+    # bytes each kernel must move per launch (algorithmic: what the method reads and writes; partial-state records
+    # are implementation overhead and not counted)
     rows = w.batch * w.n_kv_heads
     blk_kv = w.block_size * 2 * w.head_dim * e
-    alg = {"score": rows * w.n_blocks * 2 * w.head_dim * e,
-           "select_topk": rows * w.n_blocks * 4,
-           "ema_topk": rows * w.n_blocks * 12,
-           "speculate": rows * kspec * blk_kv}
+    summ_b = rows * w.n_blocks * 2 * w.head_dim * e
+    row_f32 = rows * w.n_blocks * 4
 
     # ---- statistics pass: overlap, missed blocks (untimed, per-step syncs) ---------------------------------------
     stat = make_layers(a.mode)[0]
@@ -107,11 +106,21 @@ def main():
     stat.close()
     mean_missed = float(np.mean(missed)) if missed else float(w.top_k)
     prr_mode = a.mode != "serialized"
-    alg["repair"] = rows * (mean_missed if prr_mode else w.top_k) * blk_kv
-    if a.mode == "prr_fused":   # one launch scores and speculates
-        alg["score"] += alg["speculate"]
 
-    kern = ["score", "select_topk", "speculate", "repair", "ema_topk"]
+    def alg_bytes(mode):
+        """Algorithmic bytes per launch of each traced kernel in `mode`."""
+        spec = rows * kspec * blk_kv
+        rep = rows * (w.top_k if mode == "serialized" else mean_missed) * blk_kv
+        if mode == "prr_fused":
+            # scoring also updates the EMA; the selection launch reads scores and EMA and speculates
+            return {"score": summ_b + 3 * row_f32, "select_topk": 2 * row_f32 + spec, "repair": rep}
+        d = {"score": summ_b + row_f32, "select_topk": row_f32, "repair": rep}
+        if mode != "serialized":
+            d.update({"speculate": spec, "ema_topk": 3 * row_f32})
+        return d
+
+    alg = alg_bytes(a.mode)
+    kern = list(alg) + ["finalize"]
 
     def measure(mode, trace_kernels=None):
         """Warm up eagerly, capture exactly a.steps steps (x layers) in a HIP graph, replay once untimed and once
@@ -182,12 +191,14 @@ def main():
         if mode != a.mode:
             other[mode] = measure(mode)[0]
 
+    # selected-KV attention path: speculation + repair in the PRR modes, attend(T) (the repair launch with an empty
+    # prediction) in the serialized mode; the fused mode speculates inside the selection launch, so its path time is
+    # the whole selection launch
     if a.mode == "prr_fused":
-        attn_us = per_kernel.get("repair", 0.0)   # speculation runs inside the scoring launch
-        attn_bytes = alg["repair"]
+        attn_us = per_kernel.get("select_topk", 0.0) + per_kernel.get("repair", 0.0)
     else:
         attn_us = per_kernel.get("speculate", 0.0) + per_kernel.get("repair", 0.0)
-        attn_bytes = (alg["speculate"] if prr_mode else 0) + alg["repair"]
+    attn_bytes = (rows * kspec * blk_kv if prr_mode else 0) + alg["repair"]
     detail = {
         "us_per_step": {a.mode: us, **other},
         "timing": "eager" if a.eager else "hip graph of all timed steps",
@@ -195,7 +206,7 @@ def main():
         "kernel_us": per_kernel,
         "attention_path_GBps": attn_bytes / (attn_us * 1e-6) / 1e9 if attn_us else None,
         "attention_path_frac": (attn_bytes / (attn_us * 1e-6) / 1e9) / HBM_PEAK_GBS if attn_us else None,
-        "step_alg_bytes": rows * w.n_blocks * 2 * w.head_dim * e + attn_bytes,
+        "step_alg_bytes": summ_b + attn_bytes,
         "predictor_overlap": float(np.mean(overlap)) if overlap else None,
         "repaired_blocks_mean": mean_missed,
         "layers_rotated": n_layers,

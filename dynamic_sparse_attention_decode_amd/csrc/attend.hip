@@ -8,8 +8,8 @@
 // repair_kernel: grid (records per row, rows). Each wave walks `epw` consecutive entries of the true set T; an entry
 // found in the predicted set P merges its speculated record, a missed entry is computed from the KV cache; entries
 // of P outside T are never read. The 4 wave states merge in LDS into one record per workgroup.
-// finalize_kernel: one workgroup per row merges the row's records, normalises, and writes out = O / l and the
-// missed count.
+// finalize_kernel: one workgroup per (row, head) merges that head's part of the row's records, normalises, and
+// writes out = O / l; the missed count is summed alongside.
 #include "attn_wave.h"
 
 namespace prr {
@@ -29,84 +29,62 @@ __global__ __launch_bounds__(256, 3) void speculate_kernel(const uint8_t* __rest
 
 constexpr int kMaxRecords = 256;   // records per row (bounded through entries per wave)
 
+// Merge one head's part of a row's records (m log2, l, O[D] of head h in every record), normalise, and write
+// out[h][:]. One 256-thread workgroup: the n_rec (m, l) pairs are reduced with wave operations, then 256 / (D/4)
+// record groups accumulate float4 slices of O with 8 loads in flight per thread.
 template <int G, int D>
-struct FinalSmem {
-  static constexpr int S = G * D / 4;                 // float4 slots of O[G][D]
-  static constexpr int P = S >= 256 ? 1 : 256 / S;   // record groups summed in parallel
-  static constexpr int floats = 2 * G * kMaxRecords + 2 * G + 4 + 4 * P * S + 4;
-};
-
-// Merge the row's records (m[G] log2, l[G], O[G][D]), normalise, and write out[G][D] and the missed count.
-template <int G, int D>
-__device__ void finalize_row(const float* __restrict__ recs, const int32_t* __restrict__ miss, int n_rec,
-                             float* __restrict__ out_g, int32_t* __restrict__ n_missed, float* smem) {
+__device__ void finalize_head(const float* __restrict__ recs, int n_rec, int h, float* __restrict__ out_h) {
   constexpr int RF = rec_floats(G, D), ML = rec_ml(G);
-  using F = FinalSmem<G, D>;
-  float* sm = smem;                       // [n_rec][G]
-  float* sl = sm + G * kMaxRecords;       // [n_rec][G]
-  float* sML = sl + G * kMaxRecords;      // M[G], 1/L[G]
-  float4* red = reinterpret_cast<float4*>(sML + ((2 * G + 3) & ~3));   // [P][S]; offset is a multiple of 4 floats
-  int* s_miss = reinterpret_cast<int*>(red + F::P * F::S);
+  constexpr int S = D / 4;          // float4 slots of one head's O
+  constexpr int P = 256 / S;        // record groups summed in parallel
+  __shared__ float s_w[kMaxRecords];
+  __shared__ float s_red[2][4];
+  __shared__ float4 s_acc[P][S];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  if (t == 0) *s_miss = 0;
-  for (int i = t; i < n_rec * G; i += 256) {
-    const int r = i / G, h = i % G;
-    sm[i] = recs[(int64_t)r * RF + h];
-    sl[i] = recs[(int64_t)r * RF + G + h];
-  }
+  // weights w_r = exp2(m_r - M) and L = sum_r l_r w_r
+  const float mr = t < n_rec ? recs[(int64_t)t * RF + h] : -__builtin_huge_valf();
+  const float lr = t < n_rec ? recs[(int64_t)t * RF + G + h] : 0.f;
+  const float wm = wave_max(mr);
+  if (lane == 0) s_red[0][wave] = wm;
   __syncthreads();
-  for (int h = wave; h < G; h += 4) {
-    float M = -__builtin_huge_valf();
-    for (int r = lane; r < n_rec; r += 64) M = fmaxf(M, sm[r * G + h]);
-    M = wave_max(M);
-    float L = 0.f;
-    for (int r = lane; r < n_rec; r += 64) L += sl[r * G + h] * exp2f(sm[r * G + h] - M);
-    L = wave_sum(L);
-    if (lane == 0) { sML[h] = M; sML[G + h] = 1.f / L; }
-  }
-  {
-    int c = 0;
-    for (int r = t; r < n_rec; r += 256) c += miss[r];
-    c = (int)wave_sum((float)c);   // exact: counts are far below 2^24
-    if (lane == 0) atomicAdd(s_miss, c);
-  }
+  const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  const float wgt = t < n_rec ? exp2f(mr - M) : 0.f;
+  s_w[t] = wgt;
+  const float ls = wave_sum(lr * wgt);
+  if (lane == 0) s_red[1][wave] = ls;
   __syncthreads();
-  const int slot = t % F::S, p = t / F::S;
-  if (p < F::P) {
-    const int h = slot * 4 / D;
-    const float M = sML[h];
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    constexpr int U = 8;   // record loads in flight per thread
-    for (int r0 = p; r0 < n_rec; r0 += U * F::P) {
-      float4 o[U];
+  const float L = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
+  const int slot = t % S, p = t / S;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  constexpr int U = 8;
+  for (int r0 = p; r0 < n_rec; r0 += U * P) {
+    float4 o[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int r = r0 + u * F::P;
-        o[u] = r < n_rec ? *reinterpret_cast<const float4*>(recs + (int64_t)r * RF + ML + slot * 4)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int r = r0 + u * F::P;
-        const float wgt = r < n_rec ? exp2f(sm[r * G + h] - M) : 0.f;
-        acc.x = fmaf(o[u].x, wgt, acc.x); acc.y = fmaf(o[u].y, wgt, acc.y);
-        acc.z = fmaf(o[u].z, wgt, acc.z); acc.w = fmaf(o[u].w, wgt, acc.w);
-      }
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u * P;
+      o[u] = r < n_rec ? *reinterpret_cast<const float4*>(recs + (int64_t)r * RF + ML + h * D + slot * 4)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    red[p * F::S + slot] = acc;
-  }
-  __syncthreads();
-  if (t < F::S) {
-    float4 a = red[t];
 #pragma unroll
-    for (int p2 = 1; p2 < F::P; ++p2) {
-      const float4 b = red[p2 * F::S + t];
-      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    for (int u = 0; u < U; ++u) {
+      const int r = r0 + u * P;
+      const float wr = r < n_rec ? s_w[r] : 0.f;
+      acc.x = fmaf(o[u].x, wr, acc.x); acc.y = fmaf(o[u].y, wr, acc.y);
+      acc.z = fmaf(o[u].z, wr, acc.z); acc.w = fmaf(o[u].w, wr, acc.w);
     }
-    const float il = sML[G + t * 4 / D];
-    *reinterpret_cast<float4*>(out_g + t * 4) = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
   }
-  if (t == 0) *n_missed = *s_miss;
+  s_acc[p][slot] = acc;
+  __syncthreads();
+  if (t < S) {
+    float4 a = s_acc[0][t];
+#pragma unroll
+    for (int p2 = 1; p2 < P; ++p2) {
+      const float4 c = s_acc[p2][t];
+      a.x += c.x; a.y += c.y; a.z += c.z; a.w += c.w;
+    }
+    const float il = 1.f / L;
+    *reinterpret_cast<float4*>(out_h + t * 4) = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+  }
 }
 
 template <int DT, int G>
@@ -122,9 +100,11 @@ __global__ __launch_bounds__(256, 2) void repair_kernel(const uint8_t* __restric
   constexpr int D = W::D;
   constexpr int RF = rec_floats(G, D);
   constexpr int ML = rec_ml(G);
+  constexpr int kPredLds = 2048;   // predicted sets up to this size are searched in LDS
   __shared__ float s_ml[4][2 * G];
   __shared__ float s_o[4 * G * D];
   __shared__ int s_miss[4];
+  __shared__ int32_t s_pred[kPredLds];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t rowid = blockIdx.y;
   const int rec = blockIdx.x;
@@ -134,10 +114,14 @@ __global__ __launch_bounds__(256, 2) void repair_kernel(const uint8_t* __restric
   const int32_t* prow = pred ? pred + rowid * k_spec : nullptr;
   const float* part_row = partials ? partials + rowid * k_spec * (int64_t)RF : nullptr;
 
+  const bool pred_lds = k_spec <= kPredLds;
+  if (prow && pred_lds)
+    for (int i = threadIdx.x; i < k_spec; i += 256) s_pred[i] = prow[i];
   W st;
   st.init(lane);
   st.load_q(q + ((int64_t)b * Hq + (int64_t)g * G) * kRowBytes, qscale);
   const int32_t* trow = table + (int64_t)b * pps;
+  __syncthreads();
   int misses = 0;
   const int j0 = (rec * 4 + wave) * epw;
   const int j1 = min(top_k, j0 + epw);
@@ -146,7 +130,7 @@ __global__ __launch_bounds__(256, 2) void repair_kernel(const uint8_t* __restric
     int slot = -1;
     for (int c = 0; c < k_spec; c += 64) {
       const int i = c + lane;
-      const int pv = i < k_spec ? prow[i] : -1;
+      const int pv = i < k_spec ? (pred_lds ? s_pred[i] : prow[i]) : -1;
       const unsigned long long hit = __ballot(pv == n);
       if (hit) { slot = c + __ffsll(hit) - 1; break; }
     }
@@ -189,19 +173,26 @@ __global__ __launch_bounds__(256, 2) void repair_kernel(const uint8_t* __restric
   if (threadIdx.x == 0) ws_miss[rowid * n_rec + rec] = s_miss[0] + s_miss[1] + s_miss[2] + s_miss[3];
 }
 
-// Merge each row's records into the normalised output (one workgroup per row). A kernel boundary separates it from
-// repair_kernel: cross-workgroup visibility through device-scope fences (an L2 write-back and invalidate per
-// workgroup on this multi-XCD part) cost far more than one extra launch.
+// Merge each row's records into the normalised output: one workgroup per (row, head); the head-0 workgroup also sums
+// the missed count. A kernel boundary separates it from repair_kernel: cross-workgroup visibility through
+// device-scope fences (an L2 write-back and invalidate per workgroup on this multi-XCD part) cost far more than one
+// extra launch.
 template <int G, int D>
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ ws_rec,
                                                        const int32_t* __restrict__ ws_miss, int n_rec,
                                                        float* __restrict__ out, int32_t* __restrict__ n_missed,
                                                        int Hq, int Hkv) {
-  __shared__ __align__(16) float smem[FinalSmem<G, D>::floats];
   const int64_t rowid = blockIdx.x;
+  const int h = blockIdx.y;
   const int b = (int)(rowid / Hkv), g = (int)(rowid % Hkv);
-  finalize_row<G, D>(ws_rec + rowid * n_rec * rec_floats(G, D), ws_miss + rowid * n_rec, n_rec,
-                     out + ((int64_t)b * Hq + (int64_t)g * G) * D, n_missed + rowid, smem);
+  finalize_head<G, D>(ws_rec + rowid * n_rec * rec_floats(G, D), n_rec, h,
+                      out + ((int64_t)b * Hq + (int64_t)g * G + h) * D);
+  if (h == 0 && threadIdx.x < 64) {
+    int c = 0;
+    for (int r = threadIdx.x; r < n_rec; r += 64) c += ws_miss[rowid * n_rec + r];
+    c = (int)wave_sum((float)c);   // exact: counts are far below 2^24
+    if (threadIdx.x == 0) n_missed[rowid] = c;
+  }
 }
 
 // ---- launchers -----------------------------------------------------------------------------------------------------
@@ -268,8 +259,9 @@ static void repair_launch(const prr_shape& s, const void* q, const void* kc, con
   trace_end(PRR_KERNEL_REPAIR, st);
   constexpr int D = 16 * Vec<DT>::n;
   trace_begin(PRR_KERNEL_FINALIZE, st);
-  finalize_kernel<G, D><<<dim3((unsigned)rows), dim3(256), 0, st>>>(ws.rec, ws.miss, nrec, out, n_missed,
-                                                                    s.n_q_heads, s.n_kv_heads);
+  finalize_kernel<G, D><<<dim3((unsigned)rows, (unsigned)G), dim3(256), 0, st>>>(ws.rec, ws.miss, nrec, out,
+                                                                                 n_missed, s.n_q_heads,
+                                                                                 s.n_kv_heads);
   trace_end(PRR_KERNEL_FINALIZE, st);
 }
 

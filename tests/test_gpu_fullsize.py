@@ -1,0 +1,62 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark times (fused single-stream PRR step
+with the workload's largest speculation budget): a few decode steps through libprr, and for sampled (sequence, KV
+head) rows the fp64 oracle recomputes that row alone (summaries, scores, selection, attention over the selected
+blocks, EMA and the predicted set) and the GPU's row is checked against it with the same rules as the reduced tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+from dynamic_sparse_attention_decode_amd.inputs import WORKLOADS, make_inputs
+from dynamic_sparse_attention_decode_amd.runtime import PRRLayer
+from oracle import prr_oracle as O
+from tests.checker import TOL, check_selection, max_abs
+from tests.gpu_common import OracleView, np64, requires_gpu, shape_of
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+STEPS = 3
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_full_size_sampled_rows(name):
+    w = WORKLOADS[name]
+    k_spec = max(w.k_spec)
+    rng = np.random.default_rng(5)
+    rows = sorted({(0, 0), (w.batch - 1, w.n_kv_heads - 1),
+                   (int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads)))})
+    print(f"[case] full-size {name} K={w.top_k} K'={k_spec} rows {rows}", flush=True)
+    inp = make_inputs(w, device="cuda", steps=STEPS)
+    ov = OracleView(inp)
+    layer = PRRLayer(shape_of(w), w.top_k, k_spec, w.alpha, mode="prr_fused")
+    layer.build(inp.k_cache, inp.v_cache, inp.table)
+    ema = {}
+    G = w.group
+    worst = 0.0
+    for t in range(STEPS):
+        ids = inp.drift(t)
+        if len(ids):
+            layer.rebuild_blocks(torch.as_tensor(ids, device="cuda"))
+            ov.invalidate_keys()
+        out = layer.step(inp.q[t].contiguous())
+        torch.cuda.synchronize()
+        out_h, sel, nm = np64(out), layer.sel_idx.cpu().numpy(), layer.n_missed.cpu().numpy()
+        pred = layer.pred_current.cpu().numpy() if t > 0 else None
+        for (b, g) in rows:
+            qg = ov.q_group(t, b, g)
+            keys = ov.keys(b, g)
+            kmin, kmax = O.block_summaries(keys, w.block_size)
+            s = O.quest_scores_signsplit(qg, kmin, kmax)
+            check_selection(sel[b, g], s, w.top_k)
+            ref = O.attention_over_blocks(qg, keys, ov.values(b, g), sel[b, g], w.block_size, w.scale)
+            e = max_abs(out_h[b, g * G:(g + 1) * G], ref)
+            worst = max(worst, e)
+            assert e <= TOL[w.dtype], (t, b, g, e)
+            if t > 0:
+                check_selection(pred[b, g], ema[(b, g)], k_spec)
+                assert nm[b, g] == len(set(sel[b, g]) - set(pred[b, g])), (t, b, g)
+            else:
+                assert nm[b, g] == w.top_k
+            ema[(b, g)] = O.ema_update(ema.get((b, g)), s, w.alpha, t == 0)
+    layer.close()
+    print(f"[result] full-size {name}: worst output error {worst:.3e}", flush=True)
