@@ -14,17 +14,22 @@
 
 namespace prr {
 
-template <int DT, int G>
+// One wave per `spw` consecutive predicted slots of one row (wpr waves per row).
+template <int DT, int G, bool P16>
 __global__ __launch_bounds__(256, 3) void speculate_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
                                                         const uint8_t* __restrict__ vc,
                                                         const int32_t* __restrict__ table,
                                                         const int32_t* __restrict__ pred, int k_spec,
                                                         float* __restrict__ partials, int Hq, int Hkv, int N, int bs,
-                                                        int page, int pps, float qscale, int64_t total) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t s = (int64_t)blockIdx.x * 4 + wave;
-  if (s < total)
-    speculate_slot<DT, G>(s, lane, q, kc, vc, table, pred, k_spec, partials, Hq, Hkv, N, bs, page, pps, qscale);
+                                                        int page, int pps, float qscale, int spw, int wpr,
+                                                        int64_t total_waves) {
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= total_waves) return;
+  const int64_t rowid = w / wpr;
+  const int j0 = (int)(w - rowid * wpr) * spw;
+  const int j1 = min(k_spec, j0 + spw);
+  speculate_slots<DT, G, P16>(rowid, j0, j1, threadIdx.x & 63, q, kc, vc, table, pred, k_spec, partials, Hq, Hkv, N, bs,
+                         page, pps, qscale);
 }
 
 constexpr int kMaxRecords = 256;   // records per row (bounded through entries per wave)
@@ -87,8 +92,8 @@ __device__ void finalize_head(const float* __restrict__ recs, int n_rec, int h, 
   }
 }
 
-template <int DT, int G>
-__global__ __launch_bounds__(256, 2) void repair_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
+template <int DT, int G, bool P16>
+__global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
                                                      const uint8_t* __restrict__ vc,
                                                      const int32_t* __restrict__ table,
                                                      const int32_t* __restrict__ sel, int top_k,
@@ -105,6 +110,7 @@ __global__ __launch_bounds__(256, 2) void repair_kernel(const uint8_t* __restric
   __shared__ float s_o[4 * G * D];
   __shared__ int s_miss[4];
   __shared__ int32_t s_pred[kPredLds];
+  __shared__ int32_t s_mid[4][8];   // missed block ids of the current group of entries, per wave
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t rowid = blockIdx.y;
   const int rec = blockIdx.x;
@@ -125,21 +131,28 @@ __global__ __launch_bounds__(256, 2) void repair_kernel(const uint8_t* __restric
   int misses = 0;
   const int j0 = (rec * 4 + wave) * epw;
   const int j1 = min(top_k, j0 + epw);
-  for (int j = j0; j < j1; ++j) {
-    const int n = min(max(srow[j], 0), N - 1);
-    int slot = -1;
-    for (int c = 0; c < k_spec; c += 64) {
-      const int i = c + lane;
-      const int pv = i < k_spec ? (pred_lds ? s_pred[i] : prow[i]) : -1;
-      const unsigned long long hit = __ballot(pv == n);
-      if (hit) { slot = c + __ffsll(hit) - 1; break; }
+  for (int jb = j0; jb < j1; jb += 8) {
+    // look up up to 8 entries: merge the speculated ones, collect the missed ones
+    int nm = 0;
+    for (int j = jb; j < min(j1, jb + 8); ++j) {
+      const int n = min(max(srow[j], 0), N - 1);
+      int slot = -1;
+      for (int c = 0; c < k_spec; c += 64) {
+        const int i = c + lane;
+        const int pv = i < k_spec ? (pred_lds ? s_pred[i] : prow[i]) : -1;
+        const unsigned long long hit = __ballot(pv == n);
+        if (hit) { slot = c + __ffsll(hit) - 1; break; }
+      }
+      if (slot >= 0) {
+        st.merge_record(part_row + (int64_t)slot * RF);
+      } else {
+        if (lane == 0) s_mid[wave][nm] = n;
+        ++nm;
+      }
     }
-    if (slot >= 0) {
-      st.merge_record(part_row + (int64_t)slot * RF);
-    } else {
-      st.block(kc, vc, trow, n, bs, page, Hkv, g);
-      ++misses;
-    }
+    misses += nm;
+    // compute the missed blocks with the next chunk's loads in flight
+    run_blocks<P16>(st, nm, [&](int i) { return s_mid[wave][i]; }, [](int) {}, kc, vc, trow, bs, page, Hkv, g);
   }
   float folded[W::NK];
   st.fold(folded);
@@ -197,9 +210,18 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
 
 // ---- launchers -----------------------------------------------------------------------------------------------------
 
+// Entries of T per repair wave: enough to keep records per row <= kMaxRecords; on the pipelined path about four
+// 16-token chunks per wave while at least 4096 waves remain.
 static int repair_epw(const prr_shape& s, int top_k) {
-  const int need = (top_k + 4 * kMaxRecords - 1) / (4 * kMaxRecords);   // keeps records per row <= kMaxRecords
-  return need > 1 ? need : 1;
+  const int need = (top_k + 4 * kMaxRecords - 1) / (4 * kMaxRecords);
+  int e = 1;
+  if ((s.page_size & 15) == 0 && s.block_size <= 128) {
+    const int cpb = (s.block_size + 15) / 16;
+    e = cpb >= 4 ? 1 : 4 / cpb;
+    const int64_t rows = (int64_t)s.batch * s.n_kv_heads;
+    while (e > 1 && rows * ((top_k + e - 1) / e) < 4096) e >>= 1;
+  }
+  return e > need ? e : need;
 }
 
 static int repair_records(const prr_shape& s, int top_k) {
@@ -228,16 +250,32 @@ static size_t ws_layout(const prr_shape& s, int top_k, void* base, RepairWs* out
 
 size_t repair_workspace_bytes(const prr_shape& s, int top_k) { return ws_layout(s, top_k, nullptr, nullptr); }
 
+// The resolved-page pipelined path: 16-token chunks never straddle a page, and a wave's group of at most 8 entries
+// (or 4 speculation slots) spans at most 64 chunks.
+static bool p16_path(const prr_shape& s) { return (s.page_size & 15) == 0 && s.block_size <= 128; }
+
+// Slots per speculation wave: about four 16-token chunks per wave, while keeping at least 4096 waves in flight.
+static int spec_spw(const prr_shape& s, int k_spec) {
+  const int cpb = (s.block_size + 15) / 16;
+  int spw = cpb >= 4 ? 1 : 4 / cpb;
+  const int64_t rows = (int64_t)s.batch * s.n_kv_heads;
+  while (spw > 1 && rows * ((k_spec + spw - 1) / spw) < 4096) spw >>= 1;
+  return spw;
+}
+
 template <int DT, int G>
 static void spec_launch(const prr_shape& s, const void* q, const void* kc, const void* vc, const int32_t* table,
                         const int32_t* pred, int k_spec, float* partials, hipStream_t st) {
-  const int64_t total = (int64_t)s.batch * s.n_kv_heads * k_spec;
+  const int spw = spec_spw(s, k_spec);
+  const int wpr = (k_spec + spw - 1) / spw;
+  const int64_t total = (int64_t)s.batch * s.n_kv_heads * wpr;
   const float qscale = s.softmax_scale * kLog2e;
   trace_begin(PRR_KERNEL_SPECULATE, st);
-  speculate_kernel<DT, G><<<dim3((unsigned)((total + 3) / 4)), dim3(256), 0, st>>>(
+  auto kern = p16_path(s) ? speculate_kernel<DT, G, true> : speculate_kernel<DT, G, false>;
+  kern<<<dim3((unsigned)((total + 3) / 4)), dim3(256), 0, st>>>(
       static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, pred,
       k_spec, partials, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size, s.pages_per_seq, qscale,
-      total);
+      spw, wpr, total);
   trace_end(PRR_KERNEL_SPECULATE, st);
 }
 
@@ -252,7 +290,8 @@ static void repair_launch(const prr_shape& s, const void* q, const void* kc, con
   ws_layout(s, top_k, workspace, &ws);
   const float qscale = s.softmax_scale * kLog2e;
   trace_begin(PRR_KERNEL_REPAIR, st);
-  repair_kernel<DT, G><<<dim3((unsigned)nrec, (unsigned)rows), dim3(256), 0, st>>>(
+  auto kern = p16_path(s) ? repair_kernel<DT, G, true> : repair_kernel<DT, G, false>;
+  kern<<<dim3((unsigned)nrec, (unsigned)rows), dim3(256), 0, st>>>(
       static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, sel,
       top_k, pred, k_spec, partials, ws.rec, ws.miss, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size,
       s.page_size, s.pages_per_seq, qscale, epw);

@@ -45,6 +45,7 @@ struct AttnWaveM {
   static constexpr int NV = G * VE;
   static constexpr int NK = NV / 4;
   static_assert(DT != kF32, "matrix-core tile is for 16-bit storage");
+  static constexpr bool kPipelined = G <= 4;   // two chunk buffers fit the register budget
 
   uint4 qb[4];        // B operand: query head l%16 (zero beyond G), dims 8*(l/16) + 32*kk
   float qscale;
@@ -71,84 +72,121 @@ struct AttnWaveM {
       qb[kk] = col < G ? ld16(qg + col * kRowBytes + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
   }
 
-  __device__ void block(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
-                        const int32_t* __restrict__ trow, int n, int bs, int page, int Hkv, int g) {
+  // Loads of one chunk of 16 tokens: K as the A operand (token col, 8 dims at 8*row + 32*kk) and V rows 4*row + r.
+  struct Chunk {
+    uint4 ka[4], vv[4];
+  };
+
+  __device__ void load_chunk(Chunk& c, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                             const int32_t* __restrict__ trow, int n, int t0, int bs, int page, int Hkv,
+                             int g) const {
     const int64_t tok0 = (int64_t)n * bs;
-    const bool chunk_pages = (page & 15) == 0;
-    for (int t0 = 0; t0 < bs; t0 += 16) {
-      // ---- loads: K (A operand) for token col, V rows 4*row + r -----------------------------------------------
-      uint4 ka[4], vv[4];
-      const bool kok = t0 + col < bs;
-      if (chunk_pages) {
-        const int64_t tc = tok0 + t0;
-        const int64_t phys = trow[tc / page];
-        const uint8_t* base_k = kc + ((phys * Hkv + g) * page + tc % page) * (int64_t)kRowBytes;
-        const uint8_t* base_v = vc + ((phys * Hkv + g) * page + tc % page) * (int64_t)kRowBytes;
+    const bool kok = t0 + col < bs;
+    if ((page & 15) == 0) {   // the 16 tokens share one page
+      const int64_t tc = tok0 + t0;
+      const int64_t phys = trow[tc / page];
+      const uint8_t* base_k = kc + ((phys * Hkv + g) * page + tc % page) * (int64_t)kRowBytes;
+      const uint8_t* base_v = vc + ((phys * Hkv + g) * page + tc % page) * (int64_t)kRowBytes;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          ka[kk] = kok ? ld16(base_k + col * kRowBytes + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk)
+        c.ka[kk] = kok ? ld16(base_k + col * kRowBytes + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 4 * row + r;
-          vv[r] = t0 + t < bs ? ld16(base_v + t * kRowBytes + 16 * col) : make_uint4(0, 0, 0, 0);
-        }
-      } else {
-        const int64_t tk = tok0 + t0 + col;
-        const int64_t pk = kok ? trow[tk / page] : 0;
-        const uint8_t* base_k = kc + ((pk * Hkv + g) * page + tk % page) * (int64_t)kRowBytes;
+      for (int r = 0; r < 4; ++r) {
+        const int tt = 4 * row + r;
+        c.vv[r] = t0 + tt < bs ? ld16(base_v + tt * kRowBytes + 16 * col) : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      const int64_t tk = tok0 + t0 + col;
+      const int64_t pk = kok ? trow[tk / page] : 0;
+      const uint8_t* base_k = kc + ((pk * Hkv + g) * page + tk % page) * (int64_t)kRowBytes;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          ka[kk] = kok ? ld16(base_k + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
+      for (int kk = 0; kk < 4; ++kk)
+        c.ka[kk] = kok ? ld16(base_k + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 4 * row + r;
-          const int64_t tv = tok0 + t0 + t;
-          if (t0 + t < bs) {
-            const int64_t pv = trow[tv / page];
-            vv[r] = ld16(vc + ((pv * Hkv + g) * page + tv % page) * (int64_t)kRowBytes + 16 * col);
-          } else {
-            vv[r] = make_uint4(0, 0, 0, 0);
-          }
+      for (int r = 0; r < 4; ++r) {
+        const int tt = 4 * row + r;
+        const int64_t tv = tok0 + t0 + tt;
+        if (t0 + tt < bs) {
+          const int64_t pv = trow[tv / page];
+          c.vv[r] = ld16(vc + ((pv * Hkv + g) * page + tv % page) * (int64_t)kRowBytes + 16 * col);
+        } else {
+          c.vv[r] = make_uint4(0, 0, 0, 0);
         }
       }
-      // ---- logits on the matrix cores ------------------------------------------------------------------------
-      floatx4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) c = mfma16x16x32<DT>(ka[kk], qb[kk], c);
-      float z[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) z[r] = t0 + 4 * row + r < bs ? c[r] * qscale : -__builtin_huge_valf();
-      // ---- online softmax for head col ------------------------------------------------------------------------
-      float mc = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      mc = max_xor32(max_xor16(mc));
-      const float mn = fmaxf(m_l, mc);
-      const float corr = exp2f(m_l - mn);
-      m_l = mn;
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = exp2f(z[r] - mn);
-      l_l = l_l * corr + ((p[0] + p[1]) + (p[2] + p[3]));
-      // ---- O += p . V (fp32) --------------------------------------------------------------------------------
-      float y[4][VE];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) V::to_f32(vv[r], y[r]);
-      accumulate<0>(corr, p, y);
     }
   }
 
+  // Loads of one chunk whose 16 token rows are contiguous from base_k / base_v (nvalid of them exist).
+  __device__ void load_chunk_at(Chunk& c, const uint8_t* __restrict__ base_k, const uint8_t* __restrict__ base_v,
+                                int nvalid) const {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      c.ka[kk] = col < nvalid ? ld16(base_k + col * kRowBytes + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tt = 4 * row + r;
+      c.vv[r] = tt < nvalid ? ld16(base_v + tt * kRowBytes + 16 * col) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // Fold one loaded chunk (tokens t0 .. t0 + 15 of a block of bs tokens) into the running state.
+  __device__ void compute_chunk(const Chunk& c, int t0, int bs) {
+    // ---- logits on the matrix cores --------------------------------------------------------------------------
+    floatx4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) s = mfma16x16x32<DT>(c.ka[kk], qb[kk], s);
+    float z[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = t0 + 4 * row + r < bs ? s[r] * qscale : -__builtin_huge_valf();
+    // ---- online softmax for head col --------------------------------------------------------------------------
+    float mc = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mc = max_xor32(max_xor16(mc));
+    const float mn = fmaxf(m_l, mc);
+    const float corr = exp2f(m_l - mn);
+    m_l = mn;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = exp2f(z[r] - mn);
+    l_l = l_l * corr + ((p[0] + p[1]) + (p[2] + p[3]));
+    // ---- O = O * corr + p . V (fp32), one V row at a time ---------------------------------------------------
+    rescale<0>(corr);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float y[VE];
+      V::to_f32(c.vv[r], y);
+      accumulate_row<0>(p[r], y);
+    }
+  }
+
+  // Fold one block of bs tokens into the running state.
+  __device__ void block(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                        const int32_t* __restrict__ trow, int n, int bs, int page, int Hkv, int g) {
+    for (int t0 = 0; t0 < bs; t0 += 16) {
+      Chunk c;
+      load_chunk(c, kc, vc, trow, n, t0, bs, page, Hkv, g);
+      compute_chunk(c, t0, bs);
+    }
+  }
+
+  // acc[h] *= corr of head h (held by lane h)
   template <int H>
-  __device__ inline void accumulate(float corr, const float* p, float (*y)[VE]) {
+  __device__ inline void rescale(float corr) {
     if constexpr (H < G) {
       const float ch = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(corr), H));
 #pragma unroll
       for (int e = 0; e < VE; ++e) acc[H][e] *= ch;
+      rescale<H + 1>(corr);
+    }
+  }
+
+  // acc[h] += p(head h, token row r) * y, p of head h taken from lane 16*row + h
+  template <int H>
+  __device__ inline void accumulate_row(float pr, const float* y) {
+    if constexpr (H < G) {
+      const float ph = row_bcast<H>(pr);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ph = row_bcast<H>(p[r]);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) acc[H][e] = fmaf(ph, y[r][e], acc[H][e]);
-      }
-      accumulate<H + 1>(corr, p, y);
+      for (int e = 0; e < VE; ++e) acc[H][e] = fmaf(ph, y[e], acc[H][e]);
+      accumulate_row<H + 1>(pr, y);
     }
   }
 

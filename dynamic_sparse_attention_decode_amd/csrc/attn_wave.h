@@ -28,6 +28,8 @@ struct AttnWave {
   static constexpr int NK = NV / 4;     // values per lane after folding the 4 rows
   static constexpr int ML = rec_ml(G);  // offset of O in a record (floats)
 
+  static constexpr bool kPipelined = G <= 4;   // two chunk buffers fit the register budget
+
   float q[G][VE];
   float m[G];      // running max, log2 units, uniform across the wave
   float l[G];      // per-lane partial sum over this lane's token rows
@@ -57,67 +59,93 @@ struct AttnWave {
     }
   }
 
+  // Loads of one chunk of 16 tokens: rows 4*j + row of K and V (j < 4).
+  struct Chunk {
+    uint4 kv[4], vv[4];
+  };
+
+  __device__ void load_chunk(Chunk& c, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                             const int32_t* __restrict__ trow, int n, int t0, int bs, int page, int Hkv,
+                             int g) const {
+    const int64_t tok0 = (int64_t)n * bs;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t tok = tok0 + t0 + 4 * j + row;
+      if (t0 + 4 * j < bs) {
+        const int64_t phys = trow[tok / page];
+        const int64_t off = ((phys * Hkv + g) * page + tok % page) * (int64_t)kRowBytes + col * 16;
+        c.kv[j] = ld16(kc + off);
+        c.vv[j] = ld16(vc + off);
+      } else {
+        c.kv[j] = make_uint4(0, 0, 0, 0);
+        c.vv[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+
+  // Loads of one chunk whose 16 token rows are contiguous from base_k / base_v (nvalid of them exist).
+  __device__ void load_chunk_at(Chunk& c, const uint8_t* __restrict__ base_k, const uint8_t* __restrict__ base_v,
+                                int nvalid) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int off = (4 * j + row) * kRowBytes + col * 16;
+      c.kv[j] = 4 * j < nvalid ? ld16(base_k + off) : make_uint4(0, 0, 0, 0);
+      c.vv[j] = 4 * j < nvalid ? ld16(base_v + off) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // Fold one loaded chunk (tokens t0 .. t0 + 15 of a block of bs tokens, bs % 4 == 0) into the running state.
+  __device__ void compute_chunk(const Chunk& c, int t0, int bs) {
+    float z[4][G];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = t0 + 4 * j < bs;
+      float x[VE];
+      V::to_f32(c.kv[j], x);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) s = fmaf(q[h][e], x[e], s);
+        s = row_sum16(s);
+        z[j][h] = ok ? s : -__builtin_huge_valf();
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mc = fmaxf(fmaxf(z[0][h], z[1][h]), fmaxf(z[2][h], z[3][h]));
+      mc = max_xor32(max_xor16(mc));
+      const float mn = fmaxf(m[h], mc);
+      const float corr = exp2f(m[h] - mn);
+      m[h] = mn;
+      l[h] *= corr;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc[h][e] *= corr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        z[j][h] = exp2f(z[j][h] - mn);
+        l[h] += z[j][h];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float y[VE];
+      V::to_f32(c.vv[j], y);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < VE; ++e) acc[h][e] = fmaf(z[j][h], y[e], acc[h][e]);
+      }
+    }
+  }
+
   // Fold one block of bs tokens (bs % 4 == 0) into the running state.
   __device__ void block(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                         const int32_t* __restrict__ trow, int n, int bs, int page, int Hkv, int g) {
-    const int64_t tok0 = (int64_t)n * bs;
     for (int t0 = 0; t0 < bs; t0 += 16) {
-      uint4 kv[4], vv[4];
-      bool ok[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ok[j] = t0 + 4 * j < bs;
-        const int64_t tok = tok0 + t0 + 4 * j + row;
-        if (ok[j]) {
-          const int64_t phys = trow[tok / page];
-          const int64_t off = ((phys * Hkv + g) * page + tok % page) * (int64_t)kRowBytes + col * 16;
-          kv[j] = ld16(kc + off);
-          vv[j] = ld16(vc + off);
-        } else {
-          kv[j] = make_uint4(0, 0, 0, 0);
-          vv[j] = make_uint4(0, 0, 0, 0);
-        }
-      }
-      float z[4][G];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x[VE];
-        V::to_f32(kv[j], x);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float s = 0.f;
-#pragma unroll
-          for (int e = 0; e < VE; ++e) s = fmaf(q[h][e], x[e], s);
-          s = row_sum16(s);
-          z[j][h] = ok[j] ? s : -__builtin_huge_valf();
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float mc = fmaxf(fmaxf(z[0][h], z[1][h]), fmaxf(z[2][h], z[3][h]));
-        mc = max_xor32(max_xor16(mc));
-        const float mn = fmaxf(m[h], mc);
-        const float corr = exp2f(m[h] - mn);
-        m[h] = mn;
-        l[h] *= corr;
-#pragma unroll
-        for (int e = 0; e < VE; ++e) acc[h][e] *= corr;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          z[j][h] = exp2f(z[j][h] - mn);
-          l[h] += z[j][h];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float y[VE];
-        V::to_f32(vv[j], y);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-#pragma unroll
-          for (int e = 0; e < VE; ++e) acc[h][e] = fmaf(z[j][h], y[e], acc[h][e]);
-        }
-      }
+      Chunk c;
+      load_chunk(c, kc, vc, trow, n, t0, bs, page, Hkv, g);
+      compute_chunk(c, t0, bs);
     }
   }
 
@@ -195,6 +223,91 @@ struct AttnWave {
 // The tile used for a storage dtype: matrix-core logits for 16-bit K/V, all-VALU for fp32.
 template <int DT, int G>
 using Tile = std::conditional_t<DT == kF32, AttnWave<DT, G>, AttnWaveM<(DT == kF32 ? kBF16 : DT), G>>;
+
+// Attention of one wave over `cnt` blocks (ids from id_of(i)), chunk by chunk, with the next chunk's loads issued
+// before the current chunk's arithmetic so that two chunks of K/V are in flight. done(i) runs after block i's last
+// chunk (for example to write block i's record and reset the state). When every chunk of 16 tokens lies in one page
+// (P16: page size a multiple of 16, at most 64 chunks per call), lane k first resolves chunk k's block id and page;
+// the chunk loads then need no dependent address load, which would otherwise stall on the loads in flight.
+template <bool P16, typename W, typename IdFn, typename DoneFn>
+__device__ inline void run_blocks(W& st, int cnt, IdFn&& id_of, DoneFn&& done, const uint8_t* __restrict__ kc,
+                                  const uint8_t* __restrict__ vc, const int32_t* __restrict__ trow, int bs,
+                                  int page, int Hkv, int g) {
+  const int cpb = (bs + 15) >> 4;   // chunks per block
+  const int total = cnt * cpb;
+  if (total <= 0) return;
+  if constexpr (!P16) {   // general path (pages smaller than 16 tokens, or large blocks): one chunk at a time
+    for (int i = 0; i < cnt; ++i) {
+      st.block(kc, vc, trow, id_of(i), bs, page, Hkv, g);
+      done(i);
+    }
+    return;
+  }
+  // P16: the page size is a multiple of 16 and the caller keeps cnt * chunks per block <= 64
+  const int lane = threadIdx.x & 63;
+  int my_phys = 0, my_off = 0;
+  if (lane < total) {
+    const int i = lane / cpb;
+    const int64_t tc = (int64_t)id_of(i) * bs + ((lane - i * cpb) << 4);
+    my_phys = trow[tc / page];
+    my_off = (int)(tc % page);
+  }
+  // two register buffers used alternately (no copies, so the loads of one stay in flight while the other is used)
+  typename W::Chunk ca, cb;
+  auto load = [&](typename W::Chunk& c, int k) {
+    const int phys = __builtin_amdgcn_readlane(my_phys, k);
+    const int off = __builtin_amdgcn_readlane(my_off, k);
+    const int t0 = (k - (k / cpb) * cpb) << 4;
+    const int64_t r = ((int64_t)phys * Hkv + g) * page + off;
+    st.load_chunk_at(c, kc + r * kRowBytes, vc + r * kRowBytes, bs - t0);
+  };
+  auto compute = [&](const typename W::Chunk& c, int k) {
+    const int i = k / cpb, t0 = (k - i * cpb) << 4;
+    st.compute_chunk(c, t0, bs);
+    if (t0 + 16 >= bs) done(i);
+  };
+  if constexpr (W::kPipelined) {
+    load(ca, 0);
+    for (int k = 0; k < total; k += 2) {
+      if (k + 1 < total) load(cb, k + 1);
+      compute(ca, k);
+      if (k + 1 < total) {
+        if (k + 2 < total) load(ca, k + 2);
+        compute(cb, k + 1);
+      }
+    }
+  } else {   // tiles too large for two register buffers: one chunk at a time
+    for (int k = 0; k < total; ++k) {
+      load(ca, k);
+      compute(ca, k);
+    }
+  }
+}
+
+// Speculation of the predicted slots [j0, j1) of row `rowid` by one wave: one partial record per slot.
+template <int DT, int G, bool P16>
+__device__ inline void speculate_slots(int64_t rowid, int j0, int j1, int lane, const uint8_t* __restrict__ q,
+                                       const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                                       const int32_t* __restrict__ table, const int32_t* __restrict__ pred,
+                                       int k_spec, float* __restrict__ partials, int Hq, int Hkv, int N, int bs,
+                                       int page, int pps, float qscale) {
+  using W = Tile<DT, G>;
+  const int b = (int)(rowid / Hkv), g = (int)(rowid % Hkv);
+  const int32_t* prow = pred + rowid * k_spec;
+  W st;
+  st.init(lane);
+  st.load_q(q + ((int64_t)b * Hq + (int64_t)g * G) * kRowBytes, qscale);
+  run_blocks<P16>(
+      st, j1 - j0,
+      [&](int i) { return min(max(prow[j0 + i], 0), N - 1); },   // ids outside [0, N) are clamped, never a fault
+      [&](int i) {
+        float folded[W::NK];
+        st.fold(folded);
+        st.write_record(partials + (rowid * k_spec + j0 + i) * rec_floats(G, W::D), folded);
+        st.init(lane);
+      },
+      kc, vc, table + (int64_t)b * pps, bs, page, Hkv, g);
+}
 
 // Speculation of one predicted slot s = (b * Hkv + g) * k_spec + j by one wave: the block's partial record.
 template <int DT, int G>
