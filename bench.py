@@ -33,7 +33,8 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_32k")
     ap.add_argument("--kspec", type=int, default=None, help="speculation budget (default: the workload's largest)")
     ap.add_argument("--layers", type=int, default=0, help="KV copies to rotate over (0 = auto)")
-    ap.add_argument("--mode", default="prr_fused", choices=["prr_fused", "prr_2stream", "prr_1stream", "serialized"])
+    ap.add_argument("--mode", default="prr_fused",
+                    choices=["prr_fused", "prr_2stream", "prr_1stream", "serialized", "serialized_fused"])
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
@@ -105,15 +106,18 @@ def main():
             overlap.append(float(1.0 - nm.mean() / w.top_k))
     stat.close()
     mean_missed = float(np.mean(missed)) if missed else float(w.top_k)
-    prr_mode = a.mode != "serialized"
+    prr_mode = not a.mode.startswith("serialized")
 
     def alg_bytes(mode):
         """Algorithmic bytes per launch of each traced kernel in `mode`."""
         spec = rows * kspec * blk_kv
-        rep = rows * (w.top_k if mode == "serialized" else mean_missed) * blk_kv
+        rep = rows * (w.top_k if mode.startswith("serialized") else mean_missed) * blk_kv
         if mode == "prr_fused":
-            # scoring also updates the EMA; the selection launch reads scores and EMA and speculates
-            return {"score": summ_b + 3 * row_f32, "select_topk": 2 * row_f32 + spec, "repair": rep}
+            # two launches: scores + EMA update + speculation, then selection (true and next predicted sets) with the
+            # row-wise repair and merge
+            return {"score": summ_b + 3 * row_f32 + spec, "repair": 2 * row_f32 + rep}
+        if mode == "serialized_fused":
+            return {"score": summ_b + row_f32, "repair": row_f32 + rep}
         d = {"score": summ_b + row_f32, "select_topk": row_f32, "repair": rep}
         if mode != "serialized":
             d.update({"speculate": spec, "ema_topk": 3 * row_f32})
@@ -185,7 +189,8 @@ def main():
     dom_us = dom.get(dominant, float("nan"))
     achieved = alg[dominant] / (dom_us * 1e-6) / 1e9
     other = {}
-    others = ("prr_fused", "prr_2stream", "prr_1stream", "serialized") if a.other_modes == "all" else \
+    others = ("prr_fused", "prr_2stream", "prr_1stream", "serialized", "serialized_fused") \
+        if a.other_modes == "all" else \
         tuple(m for m in a.other_modes.split(",") if m and m != "none")
     for mode in others:
         if mode != a.mode:
@@ -194,11 +199,11 @@ def main():
     # selected-KV attention path: speculation + repair in the PRR modes, attend(T) (the repair launch with an empty
     # prediction) in the serialized mode; the fused mode speculates inside the selection launch, so its path time is
     # the whole selection launch
-    if a.mode == "prr_fused":
-        attn_us = per_kernel.get("select_topk", 0.0) + per_kernel.get("repair", 0.0)
+    if a.mode in ("prr_fused", "serialized_fused"):   # the repair launch also selects; speculation is in "score"
+        attn_us = per_kernel.get("repair", 0.0)
     else:
         attn_us = per_kernel.get("speculate", 0.0) + per_kernel.get("repair", 0.0)
-    attn_bytes = (rows * kspec * blk_kv if prr_mode else 0) + alg["repair"]
+    attn_bytes = alg.get("speculate", 0) + alg["repair"]
     detail = {
         "us_per_step": {a.mode: us, **other},
         "timing": "eager" if a.eager else "hip graph of all timed steps",

@@ -14,12 +14,12 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libprr.so")
 
 F32, BF16, F16 = 0, 1, 2
-MODE_SERIALIZED, MODE_ONE_STREAM, MODE_TWO_STREAM, MODE_FUSED = 0, 1, 2, 3
+MODE_SERIALIZED, MODE_ONE_STREAM, MODE_TWO_STREAM, MODE_FUSED, MODE_SERIALIZED_FUSED = 0, 1, 2, 3, 4
 _DT_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 # every entry point of include/prr.h
 EXPORTS = ["prr_build_summaries", "prr_score_select", "prr_ema_predict", "prr_speculate", "prr_repair_merge",
-           "prr_score", "prr_select_speculate",
+           "prr_score", "prr_select_speculate", "prr_score_speculate", "prr_select_repair",
            "prr_partials_bytes", "prr_workspace_bytes", "prr_step_ctx_create", "prr_step_ctx_destroy",
            "prr_decode_step", "prr_choose_budget", "prr_trace_create", "prr_trace_destroy", "prr_trace_enable",
            "prr_trace_read", "prr_flush_write", "prr_stream_read", "prr_status_string", "prr_last_error",
@@ -87,6 +87,8 @@ def lib():
         "prr_repair_merge": (i32, [sp, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp]),
         "prr_score": (i32, [sp, vp, vp, vp, vp, f32, i32, vp]),
         "prr_select_speculate": (i32, [sp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
+        "prr_score_speculate": (i32, [sp, vp, vp, vp, vp, f32, i32, vp, vp, vp, vp, i32, vp, vp]),
+        "prr_select_repair": (i32, [sp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]),
         "prr_partials_bytes": (sz, [sp, i32]),
         "prr_workspace_bytes": (sz, [sp, i32]),
         "prr_step_ctx_create": (i32, [ctypes.POINTER(vp)]),
@@ -197,6 +199,30 @@ def select_speculate(shape: Shape, scores, top_k: int, sel_idx, ema=None, k_spec
                                       _p(k_cache, dt, "k_cache"), _p(v_cache, dt, "v_cache"),
                                       _p(block_table, torch.int32, "block_table"), _p(pred_idx, torch.int32, "pred_idx"),
                                       k_spec, _p(partials, torch.float32, "partials"), _s(stream)), "select_speculate")
+
+
+def score_speculate(shape: Shape, q, summaries, scores, ema=None, alpha: float = 0.0, first_step=False,
+                    k_cache=None, v_cache=None, block_table=None, pred_idx=None, k_spec: int = 0, partials=None,
+                    stream=None) -> None:
+    dt = shape.torch_dtype
+    _check(lib().prr_score_speculate(ctypes.byref(shape), _p(q, dt, "q"), _p(summaries, dt, "summaries"),
+                                     _p(scores, torch.float32, "scores"), _p(ema, torch.float32, "ema"), alpha,
+                                     int(bool(first_step)), _p(k_cache, dt, "k_cache"), _p(v_cache, dt, "v_cache"),
+                                     _p(block_table, torch.int32, "block_table"), _p(pred_idx, torch.int32, "pred_idx"),
+                                     k_spec, _p(partials, torch.float32, "partials"), _s(stream)), "score_speculate")
+
+
+def select_repair(shape: Shape, scores, top_k: int, sel_idx, q, k_cache, v_cache, block_table, out, n_missed,
+                  ema=None, k_spec_next: int = 0, pred_idx_next=None, pred_idx=None, k_spec: int = 0, partials=None,
+                  stream=None) -> None:
+    dt = shape.torch_dtype
+    _check(lib().prr_select_repair(ctypes.byref(shape), _p(scores, torch.float32, "scores"), top_k,
+                                   _p(sel_idx, torch.int32, "sel_idx"), _p(ema, torch.float32, "ema"), k_spec_next,
+                                   _p(pred_idx_next, torch.int32, "pred_idx_next"), _p(q, dt, "q"),
+                                   _p(k_cache, dt, "k_cache"), _p(v_cache, dt, "v_cache"),
+                                   _p(block_table, torch.int32, "block_table"), _p(pred_idx, torch.int32, "pred_idx"),
+                                   k_spec, _p(partials, torch.float32, "partials"), _p(out, torch.float32, "out"),
+                                   _p(n_missed, torch.int32, "n_missed"), _s(stream)), "select_repair")
 
 
 def partials_bytes(shape: Shape, k_spec: int) -> int:

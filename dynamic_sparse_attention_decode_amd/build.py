@@ -19,7 +19,7 @@ LIB = os.path.join(LIBDIR, "libprr.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["prr_api.hip", "summaries.hip", "select.hip", "attend.hip", "fused.hip"]
+HIP_SOURCES = ["prr_api.hip", "summaries.hip", "select.hip", "attend.hip", "fused.hip", "two_launch.hip"]
 CXX_SOURCES = ["budget.cpp"]
 
 # Packed fp32 ops are switched off for all device code.

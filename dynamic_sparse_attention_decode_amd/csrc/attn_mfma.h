@@ -46,6 +46,7 @@ struct AttnWaveM {
   static constexpr int NK = NV / 4;
   static_assert(DT != kF32, "matrix-core tile is for 16-bit storage");
   static constexpr bool kPipelined = G <= 4;   // two chunk buffers fit the register budget
+  static constexpr int kRecBatch = G >= 8 ? 2 : 4;   // record loads in flight
 
   uint4 qb[4];        // B operand: query head l%16 (zero beyond G), dims 8*(l/16) + 32*kk
   float qscale;
@@ -190,34 +191,56 @@ struct AttnWaveM {
     }
   }
 
-  // Merge a stored record (m[G] log2, l[G], O[G][D]); its l and O enter through one row only.
-  __device__ void merge_record(const float* __restrict__ rec) {
+  // A stored record's values as one lane needs them: m[G], l[G] and the O slices of the heads this lane's row adds
+  // (heads h with h % 4 == row), 8 dims at 8*col.
+  struct Rec {
+    float m[G], l[G];
+    float4 o[(G + 3) / 4][VE / 4];
+  };
+
+  __device__ void load_record(Rec& r, const float* __restrict__ rec) const {
     constexpr int ML = rec_ml(G);
 #pragma unroll
+    for (int h = 0; h < G; ++h) { r.m[h] = rec[h]; r.l[h] = rec[G + h]; }
+#pragma unroll
+    for (int k = 0; k < (G + 3) / 4; ++k) {
+      const int h = row + 4 * k;
+#pragma unroll
+      for (int v = 0; v < VE / 4; ++v)
+        r.o[k][v] = h < G ? *reinterpret_cast<const float4*>(rec + ML + h * D + col * VE + 4 * v)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+
+  // Merge a loaded record; its l and O enter through one row only.
+  __device__ void apply_record(const Rec& r) {
+#pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mr = rec[h];
-      const float lr = rec[G + h];
       const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_l), h));
-      const float mn = fmaxf(mh, mr);
+      const float mn = fmaxf(mh, r.m[h]);
       const float c_old = exp2f(mh - mn);
-      const float c_new = exp2f(mr - mn);
+      const float c_new = exp2f(r.m[h] - mn);
       if (col == h) {
         m_l = mn;
-        l_l = l_l * c_old + (row == 0 ? lr * c_new : 0.f);
+        l_l = l_l * c_old + (row == 0 ? r.l[h] * c_new : 0.f);
       }
       const bool mine = row == (h & 3);
-      float o[VE] = {};
-      if (mine) {
-        const float* src = rec + ML + h * D + col * VE;
+      float o[VE];
 #pragma unroll
-        for (int e = 0; e < VE; e += 4) {
-          const float4 t = *reinterpret_cast<const float4*>(src + e);
-          o[e] = t.x; o[e + 1] = t.y; o[e + 2] = t.z; o[e + 3] = t.w;
-        }
+      for (int v = 0; v < VE / 4; ++v) {
+        const float4 t4 = r.o[h >> 2][v];
+        o[4 * v] = t4.x; o[4 * v + 1] = t4.y; o[4 * v + 2] = t4.z; o[4 * v + 3] = t4.w;
       }
 #pragma unroll
       for (int e = 0; e < VE; ++e) acc[h][e] = acc[h][e] * c_old + (mine ? o[e] * c_new : 0.f);
     }
+  }
+
+  // Merge a stored record (m[G] log2, l[G], O[G][D]).
+  __device__ void merge_record(const float* __restrict__ rec) {
+    Rec r;
+    load_record(r, rec);
+    apply_record(r);
   }
 
   // Fold the 4 rows: l_l becomes the total of head col; out[i] holds flat accumulator f = row*NK + i.

@@ -29,6 +29,7 @@ struct AttnWave {
   static constexpr int ML = rec_ml(G);  // offset of O in a record (floats)
 
   static constexpr bool kPipelined = G <= 4;   // two chunk buffers fit the register budget
+  static constexpr int kRecBatch = G >= 8 ? 2 : 4;   // record loads in flight
 
   float q[G][VE];
   float m[G];      // running max, log2 units, uniform across the wave
@@ -149,31 +150,53 @@ struct AttnWave {
     }
   }
 
-  // Merge a stored partial record (m[G] log2, l[G], O[G][D]) into the running state. The record's l and O are
-  // added by one row only (row h % 4), since the rows are summed when the state is folded.
-  __device__ void merge_record(const float* __restrict__ rec) {
+  // A stored record's values as one lane needs them: m[G], l[G] and the O slices of the heads this lane's row adds
+  // (heads h with h % 4 == row), VE dims at VE*col.
+  struct Rec {
+    float m[G], l[G];
+    float4 o[(G + 3) / 4][VE / 4];
+  };
+
+  __device__ void load_record(Rec& r, const float* __restrict__ rec) const {
+#pragma unroll
+    for (int h = 0; h < G; ++h) { r.m[h] = rec[h]; r.l[h] = rec[G + h]; }
+#pragma unroll
+    for (int k = 0; k < (G + 3) / 4; ++k) {
+      const int h = row + 4 * k;
+#pragma unroll
+      for (int v = 0; v < VE / 4; ++v)
+        r.o[k][v] = h < G ? *reinterpret_cast<const float4*>(rec + ML + h * D + col * VE + 4 * v)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+
+  // Merge a loaded record into the running state. The record's l and O are added by one row only (row h % 4), since
+  // the rows are summed when the state is folded.
+  __device__ void apply_record(const Rec& r) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mr = rec[h];
-      const float lr = rec[G + h];
-      const float mn = fmaxf(m[h], mr);
+      const float mn = fmaxf(m[h], r.m[h]);
       const float c_old = exp2f(m[h] - mn);
-      const float c_new = exp2f(mr - mn);
+      const float c_new = exp2f(r.m[h] - mn);
       m[h] = mn;
       const bool mine = row == (h & 3);
-      l[h] = l[h] * c_old + (mine ? lr * c_new : 0.f);
-      float o[VE] = {};
-      if (mine) {
-        const float* src = rec + ML + h * D + col * VE;
+      l[h] = l[h] * c_old + (mine ? r.l[h] * c_new : 0.f);
+      float o[VE];
 #pragma unroll
-        for (int e = 0; e < VE; e += 4) {
-          const float4 t = *reinterpret_cast<const float4*>(src + e);
-          o[e] = t.x; o[e + 1] = t.y; o[e + 2] = t.z; o[e + 3] = t.w;
-        }
+      for (int v = 0; v < VE / 4; ++v) {
+        const float4 t4 = r.o[h >> 2][v];
+        o[4 * v] = t4.x; o[4 * v + 1] = t4.y; o[4 * v + 2] = t4.z; o[4 * v + 3] = t4.w;
       }
 #pragma unroll
       for (int e = 0; e < VE; ++e) acc[h][e] = acc[h][e] * c_old + (mine ? o[e] * c_new : 0.f);
     }
+  }
+
+  // Merge a stored partial record (m[G] log2, l[G], O[G][D]) into the running state.
+  __device__ void merge_record(const float* __restrict__ rec) {
+    Rec r;
+    load_record(r, rec);
+    apply_record(r);
   }
 
   // Fold the 4 rows: l becomes the wave total (uniform); out[i] holds flat accumulator f = row*NK + i.
@@ -281,6 +304,22 @@ __device__ inline void run_blocks(W& st, int cnt, IdFn&& id_of, DoneFn&& done, c
       load(ca, k);
       compute(ca, k);
     }
+  }
+}
+
+// Merge `cnt` stored records (wave-uniform addresses from rec_of(i)) into a wave's state, several record loads in
+// flight at a time (four, or two for the 8-head tile).
+template <typename W, typename RecFn>
+__device__ inline void run_records(W& st, int cnt, RecFn&& rec_of) {
+  constexpr int R = W::kRecBatch;
+  for (int i = 0; i < cnt; i += R) {
+    typename W::Rec r[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+      if (i + u < cnt) st.load_record(r[u], rec_of(i + u));
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+      if (i + u < cnt) st.apply_record(r[u]);
   }
 }
 

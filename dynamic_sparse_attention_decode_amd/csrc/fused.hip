@@ -1,7 +1,7 @@
 // Speculation co-scheduled with selection inside one launch (PRR abstract: speculate over the predicted blocks while
 // selection is in flight), so the overlap needs no second queue and no cross-stream synchronisation.
 //
-// select_spec_kernel (1024 threads per workgroup): workgroups [0, rows) select the true top-K of the scores,
+// select_spec_kernel (512 threads per workgroup): workgroups [0, rows) select the true top-K of the scores,
 // [rows, 2 rows) the next step's predicted set (top-K' of the EMA, which the scoring launch has already updated), and
 // the rest run speculation over the current predicted set, one wave per slot. Selection keeps one workgroup per row
 // busy and is bound by latency, so the speculative loads use bandwidth that would otherwise sit idle.
@@ -10,8 +10,10 @@
 
 namespace prr {
 
+constexpr int kSelSpecThreads = 512;   // 8 waves: room for the speculation tile's registers
+
 template <int KPT, int DT, int G>
-__global__ __launch_bounds__(1024) void select_spec_kernel(const float* __restrict__ scores, int K,
+__global__ __launch_bounds__(kSelSpecThreads) void select_spec_kernel(const float* __restrict__ scores, int K,
                                                            int32_t* __restrict__ sel, const float* __restrict__ ema,
                                                            int Kp_next, int32_t* __restrict__ pred_next, int n_sel_wg,
                                                            const uint8_t* __restrict__ q,
@@ -25,12 +27,13 @@ __global__ __launch_bounds__(1024) void select_spec_kernel(const float* __restri
   const int64_t r = blockIdx.x;
   if (r < n_sel_wg) {
     if (r < rows)
-      topk_row<KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K);
+      topk_row<kSelSpecThreads, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K);
     else
-      topk_row<KPT, false>(ema + (r - rows) * N, nullptr, 0.f, 0, N, Kp_next, pred_next + (r - rows) * Kp_next);
+      topk_row<kSelSpecThreads, KPT, false>(ema + (r - rows) * N, nullptr, 0.f, 0, N, Kp_next,
+                                            pred_next + (r - rows) * Kp_next);
     return;
   }
-  const int64_t s = (r - n_sel_wg) * 16 + (threadIdx.x >> 6);
+  const int64_t s = (r - n_sel_wg) * (kSelSpecThreads / 64) + (threadIdx.x >> 6);
   if (s < spec_total)
     speculate_slot<DT, G>(s, threadIdx.x & 63, q, kc, vc, table, pred, k_spec, partials, Hq, Hkv, N, bs, page, pps,
                           qscale);
@@ -44,8 +47,9 @@ static void select_spec_launch(const prr_shape& s, const float* scores, int K, i
   const int rows = s.batch * s.n_kv_heads;
   const int n_sel_wg = kp_next > 0 ? 2 * rows : rows;
   const int64_t spec_total = (int64_t)rows * k_spec;
-  const int n_spec_wg = (int)((spec_total + 15) / 16);
-  const dim3 grid((unsigned)(n_sel_wg + n_spec_wg)), blk(1024);
+  constexpr int WPG = kSelSpecThreads / 64;
+  const int n_spec_wg = (int)((spec_total + WPG - 1) / WPG);
+  const dim3 grid((unsigned)(n_sel_wg + n_spec_wg)), blk(kSelSpecThreads);
   const auto* qq = static_cast<const uint8_t*>(q);
   const auto* kk = static_cast<const uint8_t*>(kc);
   const auto* vv = static_cast<const uint8_t*>(vc);
@@ -55,14 +59,13 @@ static void select_spec_launch(const prr_shape& s, const float* scores, int K, i
                                                        table, pred, k_spec, partials, spec_total, s.n_q_heads,       \
                                                        s.n_kv_heads, s.n_blocks, s.block_size, s.page_size,          \
                                                        s.pages_per_seq, qs, rows)
-  switch (topk_kpt(s.n_blocks)) {
-    case 1: PRR_SELSPEC(1); break;
-    case 2: PRR_SELSPEC(2); break;
-    case 4: PRR_SELSPEC(4); break;
-    case 8: PRR_SELSPEC(8); break;
-    case 16: PRR_SELSPEC(16); break;
-    default: PRR_SELSPEC(32); break;
-  }
+  // values per thread: a few register sizes cover every row length (larger than needed is correct, just slower)
+  if (s.n_blocks <= 4 * kSelSpecThreads)
+    PRR_SELSPEC(4);
+  else if (s.n_blocks <= 16 * kSelSpecThreads)
+    PRR_SELSPEC(16);
+  else
+    PRR_SELSPEC(64);
 #undef PRR_SELSPEC
 }
 

@@ -272,6 +272,51 @@ prr_status prr_select_speculate(const prr_shape* shape, const float* scores, int
                             block_table, pred_idx, k_spec, partials, as_stream(stream));
 }
 
+prr_status prr_score_speculate(const prr_shape* shape, const void* q, const void* summaries, float* scores, float* ema,
+                               float alpha, int32_t first_step, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* pred_idx, int32_t k_spec, float* partials,
+                               void* stream) {
+  PRR_TRY(check_shape(shape));
+  PRR_REQUIRE(q && summaries && scores, "score_speculate: null pointer");
+  if (ema) PRR_REQUIRE(alpha >= 0.f && alpha <= 1.f, "score_speculate: alpha not in [0, 1]");
+  PRR_REQUIRE(k_spec >= 0 && k_spec <= shape->n_blocks, "score_speculate: k_spec %d not in [0, %d]", k_spec,
+              shape->n_blocks);
+  if (k_spec > 0)
+    PRR_REQUIRE(k_cache && v_cache && block_table && pred_idx && partials, "score_speculate: null pointer");
+  return launch_score_spec(*shape, q, summaries, scores, ema, alpha, first_step ? 1 : 0, k_cache, v_cache,
+                           block_table, pred_idx, k_spec, partials, as_stream(stream));
+}
+
+prr_status prr_select_repair(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
+                             const float* ema, int32_t k_spec_next, int32_t* pred_idx_next, const void* q,
+                             const void* k_cache, const void* v_cache, const int32_t* block_table,
+                             const int32_t* pred_idx, int32_t k_spec, const float* partials, float* out,
+                             int32_t* n_missed, void* stream) {
+  PRR_TRY(check_shape(shape));
+  PRR_TRY(check_topk_n(shape));
+  PRR_REQUIRE(scores && sel_idx && q && k_cache && v_cache && block_table && out && n_missed,
+              "select_repair: null pointer");
+  PRR_REQUIRE(top_k >= 1 && top_k <= shape->n_blocks, "select_repair: top_k %d not in [1, %d]", top_k,
+              shape->n_blocks);
+  PRR_REQUIRE(k_spec >= 0 && k_spec <= shape->n_blocks, "select_repair: k_spec %d not in [0, %d]", k_spec,
+              shape->n_blocks);
+  PRR_REQUIRE(k_spec_next >= 0 && k_spec_next <= shape->n_blocks, "select_repair: k_spec_next %d not in [0, %d]",
+              k_spec_next, shape->n_blocks);
+  if (k_spec > 0) PRR_REQUIRE(pred_idx && partials, "select_repair: k_spec > 0 needs pred_idx and partials");
+  if (k_spec_next > 0) PRR_REQUIRE(ema && pred_idx_next, "select_repair: k_spec_next > 0 needs ema and pred_idx_next");
+  if (k_spec > 0 && k_spec_next > 0 && pred_idx == pred_idx_next) {
+    set_error("select_repair: pred_idx and pred_idx_next must be different buffers");
+    return PRR_EINVAL;
+  }
+  if (!two_launch_supported(*shape, top_k, k_spec, k_spec_next)) {
+    set_error("select_repair: needs page_size %% 16 == 0, block_size <= 128 and top_k, k_spec, k_spec_next <= 2048");
+    return PRR_EUNSUPPORTED;
+  }
+  return launch_select_repair(*shape, scores, top_k, sel_idx, ema, k_spec_next, pred_idx_next, q, k_cache, v_cache,
+                              block_table, k_spec ? pred_idx : nullptr, k_spec, k_spec ? partials : nullptr, out,
+                              n_missed, as_stream(stream));
+}
+
 size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec) {
   if (check_shape(shape) != PRR_OK || k_spec <= 0) return 0;
   const int G = shape->n_q_heads / shape->n_kv_heads;
@@ -322,14 +367,25 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
                            int32_t join, void* stream_sel, void* stream_spec) {
   PRR_TRY(check_shape(shape));
   PRR_REQUIRE(a, "decode_step: args is NULL");
-  PRR_REQUIRE(mode >= PRR_MODE_SERIALIZED && mode <= PRR_MODE_FUSED, "decode_step: unknown mode %d", mode);
+  PRR_REQUIRE(mode >= PRR_MODE_SERIALIZED && mode <= PRR_MODE_SERIALIZED_FUSED, "decode_step: unknown mode %d", mode);
   PRR_REQUIRE(mode != PRR_MODE_TWO_STREAM || ctx, "decode_step: two-stream mode needs a step context");
   const hipStream_t s1 = as_stream(stream_sel);
   const hipStream_t s2 = as_stream(stream_spec);
-  const int kc = mode == PRR_MODE_SERIALIZED ? 0 : a->k_spec_cur;
-  const int kn = mode == PRR_MODE_SERIALIZED ? 0 : a->k_spec_next;
+  const bool serial = mode == PRR_MODE_SERIALIZED || mode == PRR_MODE_SERIALIZED_FUSED;
+  const int kc = serial ? 0 : a->k_spec_cur;
+  const int kn = serial ? 0 : a->k_spec_next;
   PRR_REQUIRE(kc >= 0 && kn >= 0, "decode_step: negative k_spec");
 
+  // select-then-attend in two launches pays off only when the rows alone fill the chip (one workgroup per row
+  // attends over the row's whole true set); otherwise the spread-out attention launches are faster
+  if (mode == PRR_MODE_SERIALIZED_FUSED) {
+    if (two_launch_supported(*shape, a->top_k, 0, 0) && (int64_t)shape->batch * shape->n_kv_heads >= 128) {
+      PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, nullptr, 0.f, 0, s1));
+      return prr_select_repair(shape, a->scores, a->top_k, a->sel_idx, nullptr, 0, nullptr, a->q, a->k_cache,
+                               a->v_cache, a->block_table, nullptr, 0, nullptr, a->out, a->n_missed, s1);
+    }
+    mode = PRR_MODE_SERIALIZED;
+  }
   if (mode == PRR_MODE_FUSED) {
     PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step, s1));
     PRR_TRY(prr_select_speculate(shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,

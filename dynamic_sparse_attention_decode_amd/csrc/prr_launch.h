@@ -67,6 +67,15 @@ prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, in
                               int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                               const int32_t* table, const int32_t* pred, int k_spec, float* partials,
                               hipStream_t stream);
+// The two-launch step: scores (+ EMA) with speculation, then selection with the row-wise repair and merge.
+bool two_launch_supported(const prr_shape& s, int top_k, int k_spec, int k_spec_next);
+prr_status launch_score_spec(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema,
+                             float alpha, int first, const void* kc, const void* vc, const int32_t* table,
+                             const int32_t* pred, int k_spec, float* partials, hipStream_t stream);
+prr_status launch_select_repair(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
+                                int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
+                                const int32_t* table, const int32_t* pred, int k_spec, const float* partials,
+                                float* out, int32_t* n_missed, hipStream_t stream);
 prr_status launch_flush(void* buf, size_t bytes, hipStream_t stream);
 prr_status launch_stream_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 

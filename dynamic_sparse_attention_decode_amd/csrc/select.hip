@@ -22,7 +22,7 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ va
                                                     float alpha, int first, int N, int K,
                                                     int32_t* __restrict__ out) {
   const int64_t row = blockIdx.x;
-  topk_row<KPT, EMA>(vals + row * N, EMA ? ema + row * N : nullptr, alpha, first, N, K, out + row * K);
+  topk_row<1024, KPT, EMA>(vals + row * N, EMA ? ema + row * N : nullptr, alpha, first, N, K, out + row * K);
 }
 
 // ---- launchers -----------------------------------------------------------------------------------------------------

@@ -1,4 +1,4 @@
-// topk_dev.h — exact top-K of one row of N <= 32768 fp32 values by one 1024-thread workgroup, lowest index first
+// topk_dev.h — exact top-K of one row of N <= 32768 fp32 values by one workgroup, lowest index first
 // among equal values, written as ascending indices (PRR abstract: attend only to the top-K blocks; the same routine
 // forms the EMA predictor's top-K').
 //
@@ -35,14 +35,17 @@ __device__ inline uint32_t wave_suffix_incl(uint32_t x, int lane) {
 
 __device__ inline uint32_t shr(uint32_t x, int s) { return s >= 32 ? 0u : x >> s; }
 
-// Top-K of one row of N values (optionally after the EMA update e = alpha e + (1 - alpha) v, written back), by one
-// 1024-thread workgroup; out_row receives K ascending indices.
-template <int KPT, bool EMA>
+// Top-K of one row of N <= NT * KPT values (optionally after the EMA update e = alpha e + (1 - alpha) v, written
+// back), by one workgroup of NT threads (256 <= NT <= 1024); orow (and lds_out, an LDS copy, when given) receives K
+// ascending indices.
+template <int NT, int KPT, bool EMA>
 __device__ void topk_row(const float* __restrict__ v, float* __restrict__ e_row, float alpha, int first, int N, int K,
-                         int32_t* __restrict__ orow) {
+                         int32_t* __restrict__ orow, int32_t* lds_out = nullptr) {
+  static_assert(NT >= 256 && NT <= 1024 && NT % 64 == 0, "workgroup size");
+  constexpr int NW = NT / 64;
   __shared__ uint32_t hist[256];
-  __shared__ float red_f[2][16];
-  __shared__ uint32_t red_u[16];
+  __shared__ float red_f[2][NW];
+  __shared__ uint32_t red_u[NW];
   __shared__ uint32_t bc[3];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i0 = tid * KPT;
@@ -103,7 +106,7 @@ __device__ void topk_row(const float* __restrict__ v, float* __restrict__ e_row,
   __syncthreads();
   float gmax = red_f[0][0], gmin = red_f[1][0];
 #pragma unroll
-  for (int w = 1; w < 16; ++w) { gmax = fmaxf(gmax, red_f[0][w]); gmin = fminf(gmin, red_f[1][w]); }
+  for (int w = 1; w < NW; ++w) { gmax = fmaxf(gmax, red_f[0][w]); gmin = fminf(gmin, red_f[1][w]); }
   const uint32_t kmax = f2key(gmax), kmin = f2key(gmin);
 
   // ---- MSD radix select ---------------------------------------------------------------------------------------
@@ -174,11 +177,17 @@ __device__ void topk_row(const float* __restrict__ v, float* __restrict__ e_row,
     if (i < N) {
       const uint32_t hk = shr(key[k], shift);
       if (hk > pk) {
-        if (pos < (uint32_t)K) orow[pos] = i;   // pos < K always holds; the guard keeps a logic error in bounds
+        if (pos < (uint32_t)K) {   // pos < K always holds; the guard keeps a logic error in bounds
+          orow[pos] = i;
+          if (lds_out) lds_out[pos] = i;
+        }
         ++pos;
       } else if (hk == pk) {
         if (le < krem) {
-          if (pos < (uint32_t)K) orow[pos] = i;
+          if (pos < (uint32_t)K) {
+            orow[pos] = i;
+            if (lds_out) lds_out[pos] = i;
+          }
           ++pos;
         }
         ++le;
@@ -187,7 +196,7 @@ __device__ void topk_row(const float* __restrict__ v, float* __restrict__ e_row,
   }
 }
 
-// Values per thread for a row of N values (N <= 32768).
+// Values per thread of a 1024-thread workgroup for a row of N values (N <= 32768).
 inline int topk_kpt(int n) {
   int kpt = 1;
   while (kpt * 1024 < n) kpt *= 2;

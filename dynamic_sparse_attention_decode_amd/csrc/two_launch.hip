@@ -1,0 +1,273 @@
+// The PRR decode step in two launches (PRR abstract: speculate over the predicted blocks while selection is in
+// flight, then repair the missed blocks once the true set is known).
+//
+// score_spec_kernel: workgroups [0, n_spec_wg) speculate over P_t (per-block partial records, one wave per few
+//   slots); the rest compute the block scores (and update the EMA). Scoring reads the summaries and speculation reads
+//   the predicted blocks, concurrently, so the speculative loads fill bandwidth that selection leaves unused.
+// select_repair_kernel (512 threads): workgroup r < rows selects the true top-K of row r and then, in the same
+//   workgroup, merges that row's attention: blocks of T found in P_t merge their speculated records, missed blocks
+//   are computed from the KV cache, blocks of P_t outside T never enter. The 8 wave states merge in LDS and the
+//   normalised output is written directly, so no separate merge launch follows. Workgroups [rows, 2 rows) compute
+//   the next predicted set (top-K' of the updated EMA).
+// With P_t empty the same launch is select-then-attend (the serialized path in two launches).
+#include "attn_wave.h"
+#include "score_dev.h"
+#include "topk_dev.h"
+
+namespace prr {
+
+template <int DT, int G, bool EMA, bool P16>
+__global__ __launch_bounds__(256, 3) void score_spec_kernel(const uint8_t* __restrict__ q,
+                                                         const uint8_t* __restrict__ summ, float* __restrict__ scores,
+                                                         int chunk, int score_gx, float* __restrict__ ema, float alpha,
+                                                         int first, const uint8_t* __restrict__ kc,
+                                                         const uint8_t* __restrict__ vc,
+                                                         const int32_t* __restrict__ table,
+                                                         const int32_t* __restrict__ pred, int k_spec,
+                                                         float* __restrict__ partials, int n_spec_wg, int spw, int wpr,
+                                                         int64_t spec_waves, int Hq, int Hkv, int N, int bs, int page,
+                                                         int pps, float qscale) {
+  if ((int)blockIdx.x < n_spec_wg) {
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w < spec_waves) {
+      const int64_t rowid = w / wpr;
+      const int j0 = (int)(w - rowid * wpr) * spw;
+      speculate_slots<DT, G, P16>(rowid, j0, min(k_spec, j0 + spw), threadIdx.x & 63, q, kc, vc, table, pred,
+                                  k_spec, partials, Hq, Hkv, N, bs, page, pps, qscale);
+    }
+    return;
+  }
+  const int sb = (int)blockIdx.x - n_spec_wg;
+  score_chunk<DT, G, EMA>(sb % score_gx, sb / score_gx, q, summ, scores, Hq, Hkv, N, chunk, ema, alpha, first);
+}
+
+constexpr int kSRThreads = 512;   // 8 waves: the attention tile keeps its full register budget
+constexpr int kSRMaxK = 2048;     // largest top-K and predicted set handled in LDS
+
+template <int KPT, int DT, int G>
+__global__ __launch_bounds__(kSRThreads) void select_repair_kernel(
+    const float* __restrict__ scores, int K, int32_t* __restrict__ sel, const float* __restrict__ ema, int Kp_next,
+    int32_t* __restrict__ pred_next, const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
+    const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, const int32_t* __restrict__ pred, int k_spec,
+    const float* __restrict__ partials, float* __restrict__ out, int32_t* __restrict__ n_missed, int Hq, int Hkv,
+    int N, int bs, int page, int pps, float qscale, int rows) {
+  using W = Tile<DT, G>;
+  constexpr int NW = kSRThreads / 64;
+  constexpr int D = W::D;
+  constexpr int RF = rec_floats(G, D);
+  __shared__ int32_t s_T[kSRMaxK];
+  __shared__ int32_t s_P[kSRMaxK];
+  __shared__ int32_t s_list[kSRMaxK];   // slots of the hits, then ids of the missed blocks
+  __shared__ uint32_t s_scan[NW];
+  __shared__ int s_unsorted;
+  __shared__ float s_ml[NW][2 * G];
+  __shared__ float s_o[NW][G * D];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (r >= rows) {   // next step's predicted set
+    const int64_t rr = r - rows;
+    topk_row<kSRThreads, KPT, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp_next, pred_next + rr * Kp_next);
+    return;
+  }
+  topk_row<kSRThreads, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, s_T);
+
+  // ---- T against P_t: slot of every entry of T in P_t (binary search when P_t is ascending) --------------------
+  const int b = (int)(r / Hkv), g = (int)(r % Hkv);
+  const int32_t* prow = k_spec ? pred + r * k_spec : nullptr;
+  if (tid == 0) s_unsorted = 0;
+  for (int i = tid; i < k_spec; i += kSRThreads) s_P[i] = prow[i];
+  __syncthreads();
+  for (int i = tid; i + 1 < k_spec; i += kSRThreads)
+    if (s_P[i] >= s_P[i + 1]) s_unsorted = 1;
+  __syncthreads();
+  const bool sorted = s_unsorted == 0;
+  constexpr int EPT = kSRMaxK / kSRThreads;   // entries per thread (4)
+  int slot[EPT];
+  uint32_t nh_local = 0;
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) {
+    const int j = tid * EPT + u;
+    slot[u] = -1;
+    if (j < K && k_spec > 0) {
+      const int n = s_T[j];
+      if (sorted) {
+        int lo = 0, hi = k_spec;   // first index with s_P[idx] >= n
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_P[mid] < n) lo = mid + 1; else hi = mid;
+        }
+        if (lo < k_spec && s_P[lo] == n) slot[u] = lo;
+      } else {
+        for (int i = 0; i < k_spec; ++i)
+          if (s_P[i] == n) { slot[u] = i; break; }
+      }
+    }
+    nh_local += slot[u] >= 0;
+  }
+  // exclusive scan of the hit counts over the workgroup
+  uint32_t incl = nh_local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_scan[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, nh = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t c = s_scan[w];
+    before += w < wave ? c : 0u;
+    nh += c;
+  }
+  uint32_t ph = before + incl - nh_local;   // hits before this thread's entries
+#pragma unroll
+  for (int u = 0; u < EPT; ++u) {
+    const int j = tid * EPT + u;
+    if (j < K) {
+      if (slot[u] >= 0) {
+        s_list[ph++] = slot[u];
+      } else {
+        s_list[nh + (uint32_t)j - ph] = s_T[j];   // misses before entry j = j - hits before j
+      }
+    }
+  }
+  __syncthreads();
+  const int nm = K - (int)nh;
+
+  // ---- the row's attention: each wave merges a share of the hits and computes a share of the misses ------------
+  W st;
+  st.init(lane);
+  st.load_q(q + ((int64_t)b * Hq + (int64_t)g * G) * kRowBytes, qscale);
+  const float* part_row = partials ? partials + r * k_spec * (int64_t)RF : nullptr;
+  const int h0 = (int)((int64_t)nh * wave / NW), h1 = (int)((int64_t)nh * (wave + 1) / NW);
+  run_records(st, h1 - h0, [&](int i) {
+    return part_row + (int64_t)__builtin_amdgcn_readfirstlane(s_list[h0 + i]) * RF;   // uniform: scalar m, l loads
+  });
+  const int m0 = (int)((int64_t)nm * wave / NW), m1 = (int)((int64_t)nm * (wave + 1) / NW);
+  const int32_t* trow = table + (int64_t)b * pps;
+  const int cap = 64 / ((bs + 15) >> 4);   // blocks per pipelined call
+  for (int i0 = m0; i0 < m1; i0 += cap) {
+    const int base = nh + i0;
+    run_blocks<true>(st, min(cap, m1 - i0), [&](int i) { return s_list[base + i]; }, [](int) {}, kc, vc, trow, bs,
+                     page, Hkv, g);
+  }
+  float folded[W::NK];
+  st.fold(folded);
+  st.store_ml(&s_ml[wave][0]);
+#pragma unroll
+  for (int i = 0; i < W::NK; ++i) {
+    const int f = st.row * W::NK + i;
+    s_o[wave][(f / W::VE) * D + st.col * W::VE + (f % W::VE)] = folded[i];
+  }
+  __syncthreads();
+  float* orow = out + ((int64_t)b * Hq + (int64_t)g * G) * D;
+  for (int f = tid; f < G * D; f += kSRThreads) {
+    const int h = f / D;
+    float M = s_ml[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h]);
+    float o = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float c = exp2f(s_ml[w][h] - M);
+      o += s_o[w][f] * c;
+      l += s_ml[w][G + h] * c;
+    }
+    orow[f] = o / l;
+  }
+  if (tid == 0) n_missed[r] = nm;
+}
+
+// ---- launchers -----------------------------------------------------------------------------------------------------
+
+bool two_launch_supported(const prr_shape& s, int top_k, int k_spec, int k_spec_next) {
+  return (s.page_size & 15) == 0 && s.block_size <= 128 && top_k <= kSRMaxK && k_spec <= kSRMaxK &&
+         k_spec_next <= kSRMaxK && s.n_blocks <= 64 * kSRThreads;
+}
+
+static int spec_spw2(const prr_shape& s, int k_spec) {
+  const int cpb = (s.block_size + 15) / 16;
+  int spw = cpb >= 4 ? 1 : 4 / cpb;
+  const int64_t rows = (int64_t)s.batch * s.n_kv_heads;
+  while (spw > 1 && rows * ((k_spec + spw - 1) / spw) < 4096) spw >>= 1;
+  return spw;
+}
+
+template <int DT, int G>
+static void score_spec_launch(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema,
+                              float alpha, int first, const void* kc, const void* vc, const int32_t* table,
+                              const int32_t* pred, int k_spec, float* partials, hipStream_t st) {
+  const int rows = s.batch * s.n_kv_heads;
+  const int chunk = score_chunk_size(s);
+  const int gx = (s.n_blocks + chunk - 1) / chunk;
+  const int spw = k_spec > 0 ? spec_spw2(s, k_spec) : 1;
+  const int wpr = (k_spec + spw - 1) / spw;
+  const int64_t spec_waves = (int64_t)rows * wpr;
+  const int n_spec_wg = (int)((spec_waves + 3) / 4);
+  const unsigned grid = (unsigned)(n_spec_wg + (int64_t)gx * rows);
+  const auto* qq = static_cast<const uint8_t*>(q);
+  const auto* sm = static_cast<const uint8_t*>(summ);
+  const auto* kk = static_cast<const uint8_t*>(kc);
+  const auto* vv = static_cast<const uint8_t*>(vc);
+  const float qs = s.softmax_scale * kLog2e;
+  const bool p16 = (s.page_size & 15) == 0 && s.block_size <= 128;
+#define PRR_SCORESPEC(EMA_, P16_)                                                                                   \
+  score_spec_kernel<DT, G, EMA_, P16_><<<dim3(grid), dim3(256), 0, st>>>(                                          \
+      qq, sm, scores, chunk, gx, ema, alpha, first, kk, vv, table, pred, k_spec, partials, n_spec_wg, spw, wpr,    \
+      spec_waves, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size, s.pages_per_seq, qs)
+  if (ema) {
+    if (p16) PRR_SCORESPEC(true, true); else PRR_SCORESPEC(true, false);
+  } else {
+    if (p16) PRR_SCORESPEC(false, true); else PRR_SCORESPEC(false, false);
+  }
+#undef PRR_SCORESPEC
+}
+
+prr_status launch_score_spec(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema,
+                             float alpha, int first, const void* kc, const void* vc, const int32_t* table,
+                             const int32_t* pred, int k_spec, float* partials, hipStream_t stream) {
+  trace_begin(PRR_KERNEL_SCORE, stream);
+  PRR_DISPATCH_DT_G(score_spec_launch, s, q, summ, scores, ema, alpha, first, kc, vc, table, pred, k_spec, partials,
+                    stream);
+  trace_end(PRR_KERNEL_SCORE, stream);
+  return check_launch("score_speculate");
+}
+
+template <int DT, int G>
+static void select_repair_launch(const prr_shape& s, const float* scores, int K, int32_t* sel, const float* ema,
+                                 int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
+                                 const int32_t* table, const int32_t* pred, int k_spec, const float* partials,
+                                 float* out, int32_t* n_missed, hipStream_t st) {
+  const int rows = s.batch * s.n_kv_heads;
+  const dim3 grid((unsigned)(kp_next > 0 ? 2 * rows : rows)), blk(kSRThreads);
+  const auto* qq = static_cast<const uint8_t*>(q);
+  const auto* kk = static_cast<const uint8_t*>(kc);
+  const auto* vv = static_cast<const uint8_t*>(vc);
+  const float qs = s.softmax_scale * kLog2e;
+#define PRR_SELREP(KPT)                                                                                            \
+  select_repair_kernel<KPT, DT, G><<<grid, blk, 0, st>>>(scores, K, sel, ema, kp_next, pred_next, qq, kk, vv,       \
+                                                         table, pred, k_spec, partials, out, n_missed, s.n_q_heads, \
+                                                         s.n_kv_heads, s.n_blocks, s.block_size, s.page_size,       \
+                                                         s.pages_per_seq, qs, rows)
+  if (s.n_blocks <= 4 * kSRThreads)
+    PRR_SELREP(4);
+  else if (s.n_blocks <= 16 * kSRThreads)
+    PRR_SELREP(16);
+  else
+    PRR_SELREP(64);
+#undef PRR_SELREP
+}
+
+prr_status launch_select_repair(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
+                                int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
+                                const int32_t* table, const int32_t* pred, int k_spec, const float* partials,
+                                float* out, int32_t* n_missed, hipStream_t stream) {
+  trace_begin(PRR_KERNEL_REPAIR, stream);
+  PRR_DISPATCH_DT_G(select_repair_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
+                    partials, out, n_missed, stream);
+  trace_end(PRR_KERNEL_REPAIR, stream);
+  return check_launch("select_repair");
+}
+
+}  // namespace prr

@@ -20,7 +20,7 @@ import torch
 from . import _lib as L
 
 MODES = {"serialized": L.MODE_SERIALIZED, "prr_1stream": L.MODE_ONE_STREAM, "prr_2stream": L.MODE_TWO_STREAM,
-         "prr_fused": L.MODE_FUSED}
+         "prr_fused": L.MODE_FUSED, "serialized_fused": L.MODE_SERIALIZED_FUSED}
 
 
 class PRRLayer:
@@ -30,7 +30,7 @@ class PRRLayer:
             raise ValueError(f"mode must be one of {list(MODES)}")
         self.shape = shape
         self.top_k = int(top_k)
-        self.k_spec = int(k_spec) if mode != "serialized" else 0
+        self.k_spec = int(k_spec) if mode not in ("serialized", "serialized_fused") else 0
         self.alpha = float(alpha)
         self.mode = mode
         self.device = torch.device(device)

@@ -166,7 +166,8 @@ def _forced_sets(rng, T, N, Kp_list):
     sets = {"empty": [], "equal": T, "random": sorted(rng.choice(N, min(N, len(T) + 5), replace=False).tolist()),
             "disjoint": sorted(rng.choice(outside, min(len(outside), len(T)), replace=False).tolist()),
             "superset": sorted(set(T) | set(rng.choice(outside, 7, replace=False).tolist())),
-            "half": sorted(T[::2] + rng.choice(outside, 3, replace=False).tolist())}
+            "half": sorted(T[::2] + rng.choice(outside, 3, replace=False).tolist()),
+            "unsorted": list(rng.permutation(T[::2] + rng.choice(outside, 3, replace=False).tolist()))}
     return sets
 
 
@@ -208,22 +209,29 @@ def test_repair_merge_forced_predictions(name):
                 pool = [n for n in range(N) if n not in set(p) and n not in set(sel_np[b, g])]
                 while len(p) < kp:
                     p.append(pool.pop())
-                pred_np[b, g, :kp] = np.sort(p)
+                pred_np[b, g, :kp] = p if kind == "unsorted" else np.sort(p)
         pred = torch.as_tensor(pred_np, device="cuda")
         part = torch.zeros((max(L.partials_bytes(s, kp), 16) // 4,), dtype=torch.float32, device="cuda")
         L.speculate(s, q, inp.k_cache, inp.v_cache, inp.table, pred, kp, part)
         L.repair_merge(s, q, inp.k_cache, inp.v_cache, inp.table, sel, K, pred if kp else None, kp,
                        part if kp else None, out, nm, ws)
         torch.cuda.synchronize()
-        got = np64(out)
-        nmn = nm.cpu().numpy()
-        for b in range(B):
-            for g in range(Hkv):
-                e = max_abs(got[b, g * G:(g + 1) * G], ref[(b, g)])
-                worst = max(worst, e)
-                assert e <= TOL[w.dtype], (kind, b, g, e)
-                missed = len(set(sel_np[b, g]) - set(pred_np[b, g, :kp]))
-                assert nmn[b, g] == missed, (kind, b, g, nmn[b, g], missed)
+        # the same repair inside the selection launch (two-launch step)
+        out2 = torch.zeros_like(out)
+        nm2 = torch.full_like(nm, -1)
+        sel2 = torch.zeros_like(sel)
+        L.select_repair(s, scores, K, sel2, q, inp.k_cache, inp.v_cache, inp.table, out2, nm2,
+                        pred_idx=pred if kp else None, k_spec=kp, partials=part if kp else None)
+        torch.cuda.synchronize()
+        assert torch.equal(sel, sel2)
+        for got, nmn in ((np64(out), nm.cpu().numpy()), (np64(out2), nm2.cpu().numpy())):
+            for b in range(B):
+                for g in range(Hkv):
+                    e = max_abs(got[b, g * G:(g + 1) * G], ref[(b, g)])
+                    worst = max(worst, e)
+                    assert e <= TOL[w.dtype], (kind, b, g, e)
+                    missed = len(set(sel_np[b, g]) - set(pred_np[b, g, :kp]))
+                    assert nmn[b, g] == missed, (kind, b, g, nmn[b, g], missed)
     print(f"[result] {name}: worst forced-P output error {worst:.3e}")
 
 
@@ -315,6 +323,7 @@ def test_fused_launches_match_separate(name):
     pb = L.partials_bytes(s, Kp) // 4
     pa_a, pa_b = (torch.zeros((pb,), dtype=torch.float32, device=dev) for _ in range(2))
     rng = np.random.default_rng(11)
+    em_prev = None
     for t in range(3):
         q = inp.q[t].contiguous()
         cur = torch.as_tensor(np.stack([np.sort(rng.choice(N, Kp, replace=False)) for _ in range(B * Hkv)])
@@ -330,3 +339,14 @@ def test_fused_launches_match_separate(name):
         assert torch.equal(sel_a, sel_b), t
         assert torch.equal(pn_a, pn_b), t
         assert torch.equal(pa_a.view(torch.int32), pa_b.view(torch.int32)), t
+        # scores + EMA + speculation in one launch: the same bits again
+        sc_c, em_c = torch.zeros_like(sc_a), em_b.clone()
+        pa_c = torch.zeros_like(pa_a)
+        if t > 0:
+            em_c.copy_(em_prev)
+        L.score_speculate(s, q, summ, sc_c, em_c, w.alpha, t == 0, inp.k_cache, inp.v_cache, inp.table, cur, Kp,
+                          pa_c)
+        torch.cuda.synchronize()
+        assert torch.equal(sc_a, sc_c) and torch.equal(em_a.view(torch.int32), em_c.view(torch.int32)), t
+        assert torch.equal(pa_a.view(torch.int32), pa_c.view(torch.int32)), t
+        em_prev = em_a.clone()
