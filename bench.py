@@ -23,6 +23,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs per decode step per layer (select+speculate+repair); KV GB/s vs HBM peak"
 HBM_PEAK_GBS = 8000.0
+# HIP kernels behind each traced launch
+HIP_KERNELS = {("prr_fused", "score"): "score_kernel (with the EMA update)",
+               ("prr_fused", "select_topk"): "select_spec_kernel (true top-K, next top-K', speculation)",
+               ("prr_fused", "repair"): "repair_kernel + finalize_kernel",
+               ("serialized", "repair"): "repair_kernel + finalize_kernel",
+               ("prr_1stream", "repair"): "repair_kernel + finalize_kernel",
+               ("prr_2stream", "repair"): "repair_kernel + finalize_kernel"}
 
 
 def parse():
@@ -39,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--detail-out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--calibrate-mib", type=int, default=0,
+                    help="before timing, stream-read and then stream-write a buffer of this many MiB once each (a "
+                         "known byte count for scaling hardware traffic counters)")
     ap.add_argument("--other-modes", default="all",
                     help="comma list of further modes to time beside --mode ('all' or 'none')")
     return ap.parse_args()
@@ -58,6 +68,15 @@ def main():
     from dynamic_sparse_attention_decode_amd.runtime import PRRLayer
 
     L.lib()   # fail loudly without the native library
+    if a.calibrate_mib:
+        buf = torch.empty((a.calibrate_mib << 20,), dtype=torch.uint8, device="cuda:0")
+        sink = torch.zeros((65536,), dtype=torch.float32, device="cuda:0")
+        L.flush_write(buf)          # first touch, not counted
+        torch.cuda.synchronize()
+        L.stream_read(buf, sink)
+        L.flush_write(buf)
+        torch.cuda.synchronize()
+        del buf, sink
     w = WORKLOADS[a.workload]
     kspec = max(w.k_spec) if a.kspec is None else a.kspec
     dev = torch.device("cuda:0")
@@ -113,10 +132,10 @@ def main():
         spec = rows * kspec * blk_kv
         rep = rows * (w.top_k if mode.startswith("serialized") else mean_missed) * blk_kv
         if mode == "prr_fused":
-            # two launches: scores + EMA update + speculation, then selection (true and next predicted sets) with the
-            # row-wise repair and merge
-            return {"score": summ_b + 3 * row_f32 + spec, "repair": 2 * row_f32 + rep}
-        if mode == "serialized_fused":
+            # scoring also updates the EMA; the selection launch reads scores and EMA and speculates
+            return {"score": summ_b + 3 * row_f32, "select_topk": 2 * row_f32 + spec, "repair": rep}
+        if mode == "serialized_fused" and rows >= 128:
+            # two launches: scores, then selection with the row-wise attention and merge
             return {"score": summ_b + row_f32, "repair": row_f32 + rep}
         d = {"score": summ_b + row_f32, "select_topk": row_f32, "repair": rep}
         if mode != "serialized":
@@ -172,20 +191,75 @@ def main():
             lay.close()
         return us_, durs
 
-    # per-kernel breakdown (traced), then the headline timed replay with only the dominant kernel traced
+    def isolated(mode, kernel):
+        """Average duration (µs) of `kernel` alone: a HIP graph of a.steps x layers back-to-back launches of the one
+        entry point that runs it, each with its layer's state after the warm-up steps, timed with HIP events on the
+        stream the graph runs on. None when no entry point launches that kernel alone."""
+        if mode == "serialized_fused" and rows >= 128:   # its repair launch is the selection launch too
+            return None
+        ls = make_layers(mode)
+        run(ls, a.warmup)
+        torch.cuda.synchronize()
+        calls = []
+        K = w.top_k
+        for lay in ls:
+            par, nxt = lay.t % 2, (lay.t + 1) % 2
+            q = qs[lay.t % w.steps]
+            kc = lay.k_spec if lay.t > 0 else 0
+            if kernel == "score":
+                e = lay.ema.clone() if mode == "prr_fused" else None
+                calls.append(lambda lay=lay, q=q, e=e, par=par: L.score(
+                    shape, q, lay.summaries, lay.scores[par], e, w.alpha, False, stream=streams[0]))
+            elif kernel == "select_topk" and mode == "prr_fused":
+                calls.append(lambda lay=lay, q=q, par=par, nxt=nxt, kc=kc: L.select_speculate(
+                    shape, lay.scores[par], K, lay.sel_idx, lay.ema, lay.k_spec, lay.pred[nxt], q, lay.k_cache,
+                    lay.v_cache, lay.table, lay.pred[par], kc, lay.partials[par], stream=streams[0]))
+            elif kernel == "speculate" and lay.k_spec:
+                calls.append(lambda lay=lay, q=q, par=par: L.speculate(
+                    shape, q, lay.k_cache, lay.v_cache, lay.table, lay.pred[par], lay.k_spec, lay.partials[par],
+                    stream=streams[0]))
+            elif kernel == "repair":   # the repair launch and its merge launch (one entry point)
+                calls.append(lambda lay=lay, q=q, par=par, kc=kc: L.repair_merge(
+                    shape, q, lay.k_cache, lay.v_cache, lay.table, lay.sel_idx, K, lay.pred[par] if kc else None, kc,
+                    lay.partials[par] if kc else None, lay.out[par], lay.n_missed, lay.workspace, stream=streams[0]))
+            else:
+                break
+        us_ = None
+        if len(calls) == len(ls):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=streams[0]):
+                for _ in range(a.steps):
+                    for c in calls:
+                        c()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            cur = torch.cuda.current_stream()   # replay() launches the graph on the current stream
+            e0.record(cur)
+            g.replay()
+            e1.record(cur)
+            torch.cuda.synchronize()
+            us_ = e0.elapsed_time(e1) * 1e3 / (a.steps * len(calls))
+        for lay in ls:
+            lay.close()
+        return us_
+
+    # per-kernel breakdown: HIP events around every launch in an eager pass of the same steps (PyTorch's HIP runtime
+    # does not record timing events inside a captured graph); then the headline timed replay; then the dominant
+    # kernel alone in a graph of back-to-back launches
+    eager_flag, a.eager = a.eager, True
     _, per_kernel = measure(a.mode, kern)
-    if not per_kernel:
-        eager_flag, a.eager = a.eager, True
-        _, per_kernel = measure(a.mode, kern)
-        a.eager = eager_flag
+    a.eager = eager_flag
     dominant = max((k for k in per_kernel if k in alg), key=lambda k: per_kernel[k])
-    us, dom = measure(a.mode, [dominant])
-    dom_where = "timed region"
-    if dominant not in dom:   # events could not be recorded inside the graph: time that kernel in an eager pass
-        eager_flag, a.eager = a.eager, True
-        _, dom = measure(a.mode, [dominant])
-        a.eager = eager_flag
-        dom_where = "eager pass of the same steps"
+    us, _ = measure(a.mode)
+    iso = isolated(a.mode, dominant)
+    if iso is not None:
+        dom = {dominant: iso}
+        dom_where = ("graph of back-to-back launches of its entry point" +
+                     (" (repair and merge launches)" if dominant == "repair" else ""))
+    else:
+        dom = {dominant: per_kernel[dominant]}
+        dom_where = "events around each launch in an eager pass of the same steps"
     dom_us = dom.get(dominant, float("nan"))
     achieved = alg[dominant] / (dom_us * 1e-6) / 1e9
     other = {}
@@ -199,11 +273,15 @@ def main():
     # selected-KV attention path: speculation + repair in the PRR modes, attend(T) (the repair launch with an empty
     # prediction) in the serialized mode; the fused mode speculates inside the selection launch, so its path time is
     # the whole selection launch
-    if a.mode in ("prr_fused", "serialized_fused"):   # the repair launch also selects; speculation is in "score"
+    if a.mode == "prr_fused":   # speculation runs inside the selection launch
+        attn_us = per_kernel.get("select_topk", 0.0) + per_kernel.get("repair", 0.0)
+        attn_bytes = alg["select_topk"] + alg["repair"]
+    elif a.mode == "serialized_fused" and rows >= 128:   # the repair launch also selects
         attn_us = per_kernel.get("repair", 0.0)
+        attn_bytes = alg["repair"]
     else:
         attn_us = per_kernel.get("speculate", 0.0) + per_kernel.get("repair", 0.0)
-    attn_bytes = alg.get("speculate", 0) + alg["repair"]
+        attn_bytes = alg.get("speculate", 0) + alg["repair"]
     detail = {
         "us_per_step": {a.mode: us, **other},
         "timing": "eager" if a.eager else "hip graph of all timed steps",
@@ -229,8 +307,10 @@ def main():
                    "head_dim": w.head_dim, "ctx": w.ctx, "block_size": w.block_size, "page_size": w.page_size,
                    "top_k": w.top_k, "k_spec": kspec, "alpha": w.alpha, "mode": a.mode,
                    "layers_rotated": n_layers, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "roofline": {"bound": "hbm", "kernel": dominant, "hip_kernels": HIP_KERNELS.get((a.mode, dominant), dominant),
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(w.name, a.mode, dominant),
                      "alg_bytes_per_launch": alg[dominant], "avg_launch_us": round(dom_us, 3)},
         "cpu_baseline": cpu,
         "detail": detail,
@@ -240,6 +320,35 @@ def main():
     if a.detail_out:
         with open(a.detail_out, "a") as f:
             f.write(s + "\n")
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources and the C header: a recorded counter value is valid only for the same kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dynamic_sparse_attention_decode_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "prr.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, mode: str, kernel: str):
+    """HBM bytes per launch of `kernel` from profiles/pmc_traffic.txt (FETCH_SIZE + WRITE_SIZE per dispatch, each
+    scaled by the same counter's reading for a copy kernel of known size), or None when no entry matches the current
+    kernel sources."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    digest = source_digest()
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 5 and not line.startswith("#") and parts[:4] == [workload, mode, kernel, digest]:
+                return float(parts[4])
+    return None
 
 
 def cpu_baseline(w, inp, kspec, seconds):

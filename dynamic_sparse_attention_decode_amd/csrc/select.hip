@@ -17,12 +17,11 @@ __global__ __launch_bounds__(256) void score_kernel(const uint8_t* __restrict__ 
   score_chunk<DT, G, EMA>(blockIdx.x, blockIdx.y, q, summ, scores, Hq, Hkv, N, chunk, ema, alpha, first);
 }
 
-template <int KPT, bool EMA>
-__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ vals, float* __restrict__ ema,
-                                                    float alpha, int first, int N, int K,
-                                                    int32_t* __restrict__ out) {
+template <int NT, int KPT, bool EMA>
+__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ vals, float* __restrict__ ema,
+                                                  float alpha, int first, int N, int K, int32_t* __restrict__ out) {
   const int64_t row = blockIdx.x;
-  topk_row<1024, KPT, EMA>(vals + row * N, EMA ? ema + row * N : nullptr, alpha, first, N, K, out + row * K);
+  topk_row<NT, KPT, EMA>(vals + row * N, EMA ? ema + row * N : nullptr, alpha, first, N, K, out + row * K);
 }
 
 // ---- launchers -----------------------------------------------------------------------------------------------------
@@ -54,17 +53,15 @@ prr_status launch_score(const prr_shape& s, const void* q, const void* summ, flo
 template <bool EMA>
 static void topk_dispatch(int kpt, dim3 grid, const float* vals, float* ema, float alpha, int first, int N, int K,
                           int32_t* out, hipStream_t st) {
-  const dim3 blk(1024);
   switch (kpt) {
-    case 1: topk_kernel<1, EMA><<<grid, blk, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
-    case 2: topk_kernel<2, EMA><<<grid, blk, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
-    case 4: topk_kernel<4, EMA><<<grid, blk, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
-    case 8: topk_kernel<8, EMA><<<grid, blk, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
-    case 16: topk_kernel<16, EMA><<<grid, blk, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
-    default: topk_kernel<32, EMA><<<grid, blk, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
+    case 1: topk_kernel<1024, 1, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
+    case 2: topk_kernel<1024, 2, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
+    case 4: topk_kernel<1024, 4, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
+    case 8: topk_kernel<1024, 8, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
+    case 16: topk_kernel<1024, 16, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
+    default: topk_kernel<1024, 32, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
   }
 }
-
 
 prr_status launch_topk(const prr_shape& s, const float* values, float* ema, float alpha, int first, int k,
                        int32_t* out_idx, hipStream_t stream) {

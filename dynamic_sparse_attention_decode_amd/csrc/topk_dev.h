@@ -13,7 +13,7 @@
 
 namespace prr {
 
-// ---- workgroup helpers for the 1024-thread top-K kernel ----------------------------------------------------------
+// ---- workgroup helpers ------------------------------------------------------------------------------------------
 
 __device__ inline uint32_t wave_incl_scan(uint32_t x, int lane) {
 #pragma unroll
@@ -35,6 +35,126 @@ __device__ inline uint32_t wave_suffix_incl(uint32_t x, int lane) {
 
 __device__ inline uint32_t shr(uint32_t x, int s) { return s >= 32 ? 0u : x >> s; }
 
+// Shared LDS of the top-K routine (one per workgroup).
+struct TopkLds {
+  uint32_t hist[256];
+  float red_f[2][16];
+  uint32_t red_u[16];
+  uint32_t bc[3];
+  int flag;
+};
+
+// Radix state: the K-th largest counted key lies in {x : x >> shift == prefix >> shift}; keys above that class are
+// all taken, and krem keys of the class (the lowest-index ones).
+struct Radix {
+  uint32_t prefix;
+  int shift;
+  uint32_t krem;
+};
+
+// MSD radix select over keys held NK per thread (bit k of `valid` marks key[k] counted): 8-bit digits from the
+// highest bit in which kmax and kmin differ, LDS histogram, early exit when a whole digit bin is taken.
+template <int NT, int NK>
+__device__ inline Radix radix_select(const uint32_t (&key)[NK], uint64_t valid, uint32_t kmax, uint32_t kmin,
+                                     uint32_t k, TopkLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  Radix R{kmax, 0, k};
+  if (kmax != kmin) {
+    R.shift = 32 - __clz(kmax ^ kmin);
+    R.prefix = R.shift >= 32 ? 0u : (kmax >> R.shift) << R.shift;
+  }
+  while (R.shift > 0) {
+    const int db = R.shift < 8 ? R.shift : 8;
+    const int ns = R.shift - db;
+    if (tid < 256) L.hist[tid] = 0u;
+    __syncthreads();
+    const uint32_t pk = shr(R.prefix, R.shift);
+    const uint32_t dmask = (1u << db) - 1u;
+#pragma unroll
+    for (int j = 0; j < NK; ++j)
+      if (((valid >> j) & 1ull) && shr(key[j], R.shift) == pk) atomicAdd(&L.hist[(key[j] >> ns) & dmask], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t c[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = L.hist[4 * lane + j];
+      const uint32_t lsum = c[0] + c[1] + c[2] + c[3];
+      uint32_t above = wave_suffix_incl(lsum, lane) - lsum;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        if (above < R.krem && R.krem <= above + c[j]) { L.bc[0] = 4 * lane + j; L.bc[1] = above; L.bc[2] = c[j]; }
+        above += c[j];
+      }
+    }
+    __syncthreads();
+    const uint32_t bin = L.bc[0];
+    R.krem -= L.bc[1];
+    R.prefix |= bin << ns;
+    R.shift = ns;
+    if (L.bc[2] == R.krem) break;   // the whole bin is selected: no further digits needed
+  }
+  return R;
+}
+
+// Exclusive workgroup scan of x; total receives the sum.
+template <int NT>
+__device__ inline uint32_t block_scan(uint32_t x, uint32_t& total, TopkLds& L) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan(x, lane);
+  if (lane == 63) L.red_u[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t c = L.red_u[w];
+    before += w < wave ? c : 0u;
+    tot += c;
+  }
+  total = tot;
+  __syncthreads();
+  return before + incl - x;
+}
+
+// Writes the selected indices (all keys above the radix class, and the first krem keys of the class in order)
+// in ascending order. Thread t holds keys NK per thread in index order; idx_of(j) gives key j's index.
+template <int NT, int NK, typename IdxFn>
+__device__ inline void write_selected(const uint32_t (&key)[NK], uint64_t valid, const Radix& R, int K,
+                                      int32_t* __restrict__ orow, int32_t* lds_out, TopkLds& L, IdxFn&& idx_of) {
+  const uint32_t pk = shr(R.prefix, R.shift);
+  uint32_t cg = 0, ce = 0;
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    if ((valid >> j) & 1ull) {
+      const uint32_t hk = shr(key[j], R.shift);
+      cg += hk > pk;
+      ce += hk == pk;
+    }
+  }
+  const uint32_t packed = (cg << 16) | ce;   // both totals stay below 65536
+  uint32_t total;
+  const uint32_t excl = block_scan<NT>(packed, total, L);
+  const uint32_t pre_g = excl >> 16, pre_e = excl & 0xffffu;
+  uint32_t pos = pre_g + (pre_e < R.krem ? pre_e : R.krem);
+  uint32_t le = pre_e;
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    if ((valid >> j) & 1ull) {
+      const uint32_t hk = shr(key[j], R.shift);
+      bool take = hk > pk;
+      if (hk == pk) take = le++ < R.krem;
+      if (take) {
+        if (pos < (uint32_t)K) {   // pos < K always holds; the guard keeps a logic error in bounds
+          const int32_t i = idx_of(j);
+          orow[pos] = i;
+          if (lds_out) lds_out[pos] = i;
+        }
+        ++pos;
+      }
+    }
+  }
+}
+
 // Top-K of one row of N <= NT * KPT values (optionally after the EMA update e = alpha e + (1 - alpha) v, written
 // back), by one workgroup of NT threads (256 <= NT <= 1024); orow (and lds_out, an LDS copy, when given) receives K
 // ascending indices.
@@ -43,10 +163,7 @@ __device__ void topk_row(const float* __restrict__ v, float* __restrict__ e_row,
                          int32_t* __restrict__ orow, int32_t* lds_out = nullptr) {
   static_assert(NT >= 256 && NT <= 1024 && NT % 64 == 0, "workgroup size");
   constexpr int NW = NT / 64;
-  __shared__ uint32_t hist[256];
-  __shared__ float red_f[2][NW];
-  __shared__ uint32_t red_u[NW];
-  __shared__ uint32_t bc[3];
+  __shared__ TopkLds L;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i0 = tid * KPT;
 
@@ -91,109 +208,28 @@ __device__ void topk_row(const float* __restrict__ v, float* __restrict__ e_row,
     }
   }
 
-  // ---- row range of the keys --------------------------------------------------------------------------------
+  // ---- keys and the row range ---------------------------------------------------------------------------------
   float lmax = -__builtin_huge_valf(), lmin = __builtin_huge_valf();
   uint32_t key[KPT];
+  uint64_t valid = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const bool ok = i0 + k < N;
     key[k] = ok ? f2key(x[k]) : 0u;
+    valid |= (uint64_t)ok << k;
     if (ok) { lmax = fmaxf(lmax, x[k]); lmin = fminf(lmin, x[k]); }
   }
   lmax = wave_max(lmax);
   lmin = -wave_max(-lmin);
-  if (lane == 0) { red_f[0][wave] = lmax; red_f[1][wave] = lmin; }
+  if (lane == 0) { L.red_f[0][wave] = lmax; L.red_f[1][wave] = lmin; }
   __syncthreads();
-  float gmax = red_f[0][0], gmin = red_f[1][0];
+  float gmax = L.red_f[0][0], gmin = L.red_f[1][0];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) { gmax = fmaxf(gmax, red_f[0][w]); gmin = fminf(gmin, red_f[1][w]); }
+  for (int w = 1; w < NW; ++w) { gmax = fmaxf(gmax, L.red_f[0][w]); gmin = fminf(gmin, L.red_f[1][w]); }
   const uint32_t kmax = f2key(gmax), kmin = f2key(gmin);
 
-  // ---- MSD radix select ---------------------------------------------------------------------------------------
-  uint32_t prefix = kmax;
-  int shift = 0;
-  uint32_t krem = (uint32_t)K;
-  if (kmax != kmin) {
-    const int hb = 31 - __clz(kmax ^ kmin);
-    shift = hb + 1;
-    prefix = shift >= 32 ? 0u : (kmax >> shift) << shift;
-  }
-  while (shift > 0) {
-    const int db = shift < 8 ? shift : 8;
-    const int ns = shift - db;
-    if (tid < 256) hist[tid] = 0u;
-    __syncthreads();
-    const uint32_t pk = shr(prefix, shift);
-    const uint32_t dmask = (1u << db) - 1u;
-#pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-      if (i0 + k < N && shr(key[k], shift) == pk) atomicAdd(&hist[(key[k] >> ns) & dmask], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t c[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) c[j] = hist[4 * lane + j];
-      const uint32_t lsum = c[0] + c[1] + c[2] + c[3];
-      uint32_t above = wave_suffix_incl(lsum, lane) - lsum;
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (above < krem && krem <= above + c[j]) { bc[0] = 4 * lane + j; bc[1] = above; bc[2] = c[j]; }
-        above += c[j];
-      }
-    }
-    __syncthreads();
-    const uint32_t bin = bc[0];
-    krem -= bc[1];
-    prefix |= bin << ns;
-    shift = ns;
-    if (bc[2] == krem) break;   // the whole bin is selected: no further digits needed
-  }
-
-  // ---- compaction in ascending index order ---------------------------------------------------------------------
-  const uint32_t pk = shr(prefix, shift);
-  uint32_t cg = 0, ce = 0;
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    if (i0 + k < N) {
-      const uint32_t hk = shr(key[k], shift);
-      cg += hk > pk;
-      ce += hk == pk;
-    }
-  }
-  const uint32_t packed = (cg << 16) | ce;
-  const uint32_t incl = wave_incl_scan(packed, lane);
-  if (lane == 63) red_u[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int w = 0; w < wave; ++w) before += red_u[w];
-  const uint32_t excl = before + incl - packed;
-  const uint32_t pre_g = excl >> 16, pre_e = excl & 0xffffu;
-  uint32_t pos = pre_g + (pre_e < krem ? pre_e : krem);
-  uint32_t le = pre_e;
-#pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const int i = i0 + k;
-    if (i < N) {
-      const uint32_t hk = shr(key[k], shift);
-      if (hk > pk) {
-        if (pos < (uint32_t)K) {   // pos < K always holds; the guard keeps a logic error in bounds
-          orow[pos] = i;
-          if (lds_out) lds_out[pos] = i;
-        }
-        ++pos;
-      } else if (hk == pk) {
-        if (le < krem) {
-          if (pos < (uint32_t)K) {
-            orow[pos] = i;
-            if (lds_out) lds_out[pos] = i;
-          }
-          ++pos;
-        }
-        ++le;
-      }
-    }
-  }
+  const Radix R = radix_select<NT, KPT>(key, valid, kmax, kmin, (uint32_t)K, L);
+  write_selected<NT, KPT>(key, valid, R, K, orow, lds_out, L, [&](int k) { return i0 + k; });
 }
 
 // Values per thread of a 1024-thread workgroup for a row of N values (N <= 32768).
