@@ -52,10 +52,10 @@ struct Radix {
   uint32_t krem;
 };
 
-// MSD radix select over keys held NK per thread (bit k of `valid` marks key[k] counted): 8-bit digits from the
+// MSD radix select over keys held NK per thread (valid(j) tells whether key[j] is counted): 8-bit digits from the
 // highest bit in which kmax and kmin differ, LDS histogram, early exit when a whole digit bin is taken.
-template <int NT, int NK>
-__device__ inline Radix radix_select(const uint32_t (&key)[NK], uint64_t valid, uint32_t kmax, uint32_t kmin,
+template <int NT, int NK, typename ValidFn>
+__device__ inline Radix radix_select(const uint32_t (&key)[NK], ValidFn&& valid, uint32_t kmax, uint32_t kmin,
                                      uint32_t k, TopkLds& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Radix R{kmax, 0, k};
@@ -72,7 +72,7 @@ __device__ inline Radix radix_select(const uint32_t (&key)[NK], uint64_t valid, 
     const uint32_t dmask = (1u << db) - 1u;
 #pragma unroll
     for (int j = 0; j < NK; ++j)
-      if (((valid >> j) & 1ull) && shr(key[j], R.shift) == pk) atomicAdd(&L.hist[(key[j] >> ns) & dmask], 1u);
+      if (valid(j) && shr(key[j], R.shift) == pk) atomicAdd(&L.hist[(key[j] >> ns) & dmask], 1u);
     __syncthreads();
     if (wave == 0) {
       uint32_t c[4];
@@ -118,14 +118,14 @@ __device__ inline uint32_t block_scan(uint32_t x, uint32_t& total, TopkLds& L) {
 
 // Writes the selected indices (all keys above the radix class, and the first krem keys of the class in order)
 // in ascending order. Thread t holds keys NK per thread in index order; idx_of(j) gives key j's index.
-template <int NT, int NK, typename IdxFn>
-__device__ inline void write_selected(const uint32_t (&key)[NK], uint64_t valid, const Radix& R, int K,
+template <int NT, int NK, typename ValidFn, typename IdxFn>
+__device__ inline void write_selected(const uint32_t (&key)[NK], ValidFn&& valid, const Radix& R, int K,
                                       int32_t* __restrict__ orow, int32_t* lds_out, TopkLds& L, IdxFn&& idx_of) {
   const uint32_t pk = shr(R.prefix, R.shift);
   uint32_t cg = 0, ce = 0;
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
-    if ((valid >> j) & 1ull) {
+    if (valid(j)) {
       const uint32_t hk = shr(key[j], R.shift);
       cg += hk > pk;
       ce += hk == pk;
@@ -139,7 +139,7 @@ __device__ inline void write_selected(const uint32_t (&key)[NK], uint64_t valid,
   uint32_t le = pre_e;
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
-    if ((valid >> j) & 1ull) {
+    if (valid(j)) {
       const uint32_t hk = shr(key[j], R.shift);
       bool take = hk > pk;
       if (hk == pk) take = le++ < R.krem;
@@ -211,12 +211,10 @@ __device__ void topk_row(const float* __restrict__ v, float* __restrict__ e_row,
   // ---- keys and the row range ---------------------------------------------------------------------------------
   float lmax = -__builtin_huge_valf(), lmin = __builtin_huge_valf();
   uint32_t key[KPT];
-  uint64_t valid = 0;
 #pragma unroll
   for (int k = 0; k < KPT; ++k) {
     const bool ok = i0 + k < N;
     key[k] = ok ? f2key(x[k]) : 0u;
-    valid |= (uint64_t)ok << k;
     if (ok) { lmax = fmaxf(lmax, x[k]); lmin = fminf(lmin, x[k]); }
   }
   lmax = wave_max(lmax);
@@ -228,6 +226,7 @@ __device__ void topk_row(const float* __restrict__ v, float* __restrict__ e_row,
   for (int w = 1; w < NW; ++w) { gmax = fmaxf(gmax, L.red_f[0][w]); gmin = fminf(gmin, L.red_f[1][w]); }
   const uint32_t kmax = f2key(gmax), kmin = f2key(gmin);
 
+  auto valid = [&](int k) { return i0 + k < N; };
   const Radix R = radix_select<NT, KPT>(key, valid, kmax, kmin, (uint32_t)K, L);
   write_selected<NT, KPT>(key, valid, R, K, orow, lds_out, L, [&](int k) { return i0 + k; });
 }
