@@ -25,8 +25,10 @@ METRIC = "µs per decode step per layer (select+speculate+repair); KV GB/s vs HB
 HBM_PEAK_GBS = 8000.0
 # HIP kernels behind each traced launch
 HIP_KERNELS = {("prr_fused", "score"): "score_kernel (with the EMA update)",
-               ("prr_fused", "select_topk"): "select_spec_kernel (true top-K, next top-K', speculation)",
+               ("prr_fused", "select_topk"): "select_spec_kernel or select_missed_kernel (true top-K, next top-K', "
+                                             "speculation over P_t; the latter also the missed blocks)",
                ("prr_fused", "repair"): "repair_kernel + finalize_kernel",
+               ("prr_fused", "finalize"): "merge_hits_kernel",
                ("serialized", "repair"): "repair_kernel + finalize_kernel",
                ("prr_1stream", "repair"): "repair_kernel + finalize_kernel",
                ("prr_2stream", "repair"): "repair_kernel + finalize_kernel"}
@@ -49,6 +51,9 @@ def parse():
     ap.add_argument("--calibrate-mib", type=int, default=0,
                     help="before timing, stream-read and then stream-write a buffer of this many MiB once each (a "
                          "known byte count for scaling hardware traffic counters)")
+    ap.add_argument("--budget-profile", action="store_true",
+                    help="instead of the step benchmark: measure the selection time over a grid of block counts and "
+                         "the speculation time over a grid of budgets K', and print the profiled budget K'*")
     ap.add_argument("--other-modes", default="all",
                     help="comma list of further modes to time beside --mode ('all' or 'none')")
     return ap.parse_args()
@@ -78,6 +83,9 @@ def main():
         torch.cuda.synchronize()
         del buf, sink
     w = WORKLOADS[a.workload]
+    if a.budget_profile:
+        budget_profile(w)
+        return
     kspec = max(w.k_spec) if a.kspec is None else a.kspec
     dev = torch.device("cuda:0")
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
@@ -131,8 +139,12 @@ def main():
         """Algorithmic bytes per launch of each traced kernel in `mode`."""
         spec = rows * kspec * blk_kv
         rep = rows * (w.top_k if mode.startswith("serialized") else mean_missed) * blk_kv
+        if mode == "prr_fused" and (rows >= 128 or w.top_k <= 32):
+            # scoring also updates the EMA; the selection launch reads scores and EMA, speculates over P_t and attends
+            # the missed blocks; the merge launch (traced as "finalize") only reads partial records
+            return {"score": summ_b + 3 * row_f32, "select_topk": 2 * row_f32 + spec + rep}
         if mode == "prr_fused":
-            # scoring also updates the EMA; the selection launch reads scores and EMA and speculates
+            # scoring also updates the EMA; the selection launch reads scores and EMA and speculates; then repair
             return {"score": summ_b + 3 * row_f32, "select_topk": 2 * row_f32 + spec, "repair": rep}
         if mode == "serialized_fused" and rows >= 128:
             # two launches: scores, then selection with the row-wise attention and merge
@@ -210,7 +222,7 @@ def main():
                 e = lay.ema.clone() if mode == "prr_fused" else None
                 calls.append(lambda lay=lay, q=q, e=e, par=par: L.score(
                     shape, q, lay.summaries, lay.scores[par], e, w.alpha, False, stream=streams[0]))
-            elif kernel == "select_topk" and mode == "prr_fused":
+            elif kernel == "select_topk" and mode == "prr_fused" and "repair" in alg:   # the select_spec launch
                 calls.append(lambda lay=lay, q=q, par=par, nxt=nxt, kc=kc: L.select_speculate(
                     shape, lay.scores[par], K, lay.sel_idx, lay.ema, lay.k_spec, lay.pred[nxt], q, lay.k_cache,
                     lay.v_cache, lay.table, lay.pred[par], kc, lay.partials[par], stream=streams[0]))
@@ -273,9 +285,12 @@ def main():
     # selected-KV attention path: speculation + repair in the PRR modes, attend(T) (the repair launch with an empty
     # prediction) in the serialized mode; the fused mode speculates inside the selection launch, so its path time is
     # the whole selection launch
-    if a.mode == "prr_fused":   # speculation runs inside the selection launch
+    if a.mode == "prr_fused" and "repair" not in alg:   # speculation and missed blocks in the selection launch
+        attn_us = per_kernel.get("select_topk", 0.0) + per_kernel.get("finalize", 0.0)
+        attn_bytes = alg["select_topk"] - 2 * row_f32
+    elif a.mode == "prr_fused":   # speculation in the selection launch, then the repair launch
         attn_us = per_kernel.get("select_topk", 0.0) + per_kernel.get("repair", 0.0)
-        attn_bytes = alg["select_topk"] + alg["repair"]
+        attn_bytes = alg["select_topk"] - 2 * row_f32 + alg["repair"]
     elif a.mode == "serialized_fused" and rows >= 128:   # the repair launch also selects
         attn_us = per_kernel.get("repair", 0.0)
         attn_bytes = alg["repair"]
@@ -320,6 +335,75 @@ def main():
     if a.detail_out:
         with open(a.detail_out, "a") as f:
             f.write(s + "\n")
+
+
+def budget_profile(w):
+    """Profiling-guided speculation budget (PRR abstract; PRR summary page, Limitations): the selection time t_sel(N)
+    (scores + top-K) on a grid of block counts that leaves out the workload's own N, the speculation time t_spec(K')
+    on a grid of budgets, both as graph replays of back-to-back calls timed with HIP events; K'* from prr_choose_budget
+    with a degree-2 polynomial for the off-grid N. Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    from dynamic_sparse_attention_decode_amd import _lib as L
+    from dynamic_sparse_attention_decode_amd.inputs import make_inputs
+
+    dev = torch.device("cuda:0")
+    dt = {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[w.dtype]
+    rows = w.batch * w.n_kv_heads
+    reps = 50
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream(device=dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(reps):
+                fn(s)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    N0 = w.n_blocks
+    n_grid = sorted({n for n in (N0 // 8, N0 // 4, N0 // 2, N0 * 2, N0 * 4) if 64 <= n <= 32768} - {N0})
+    g_ = torch.Generator(device=dev).manual_seed(w.seed)
+    t_sel = []
+    for n in n_grid:
+        s = L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, n, dt, w.scale)
+        summ = torch.randn((w.batch, w.n_kv_heads, n, 2, w.head_dim), generator=g_, device=dev).to(w.torch_dtype)
+        q = torch.randn((w.batch, w.n_q_heads, w.head_dim), generator=g_, device=dev).to(w.torch_dtype)
+        sc = torch.zeros((w.batch, w.n_kv_heads, n), dtype=torch.float32, device=dev)
+        sel = torch.zeros((w.batch, w.n_kv_heads, min(w.top_k, n)), dtype=torch.int32, device=dev)
+        t_sel.append(timed(lambda st=None, s=s, q=q, summ=summ, sc=sc, sel=sel: L.score_select(
+            s, q, summ, sel.shape[-1], sc, sel, stream=st)))
+    inp = make_inputs(w, device=dev, steps=2)
+    s = L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, N0, dt, w.scale)
+    k_grid = sorted({0, w.top_k // 4, w.top_k // 2, w.top_k, (3 * w.top_k) // 2, 2 * w.top_k} | set(w.k_spec))
+    k_grid = [k for k in k_grid if k <= N0]
+    rng = np.random.default_rng(w.seed)
+    t_spec = []
+    for k in k_grid:
+        if k == 0:
+            t_spec.append(0.0)
+            continue
+        pred = torch.as_tensor(np.stack([np.sort(rng.choice(N0, k, replace=False)) for _ in range(rows)])
+                               .reshape(w.batch, w.n_kv_heads, k).astype(np.int32), device=dev)
+        part = torch.zeros((L.partials_bytes(s, k) // 4,), dtype=torch.float32, device=dev)
+        q = inp.q[1].contiguous()
+        t_spec.append(timed(lambda st=None, pred=pred, part=part, k=k, q=q: L.speculate(
+            s, q, inp.k_cache, inp.v_cache, inp.table, pred, k, part, stream=st)))
+    kstar = L.choose_budget(n_grid, t_sel, k_grid, t_spec, float(N0), 2)
+    fit = float(np.polyval(np.polyfit(n_grid, t_sel, 2), N0))
+    print(json.dumps({"budget_profile": {"workload": w.name, "n_target": N0, "n_grid": n_grid,
+                                         "t_sel_us": [round(x, 2) for x in t_sel], "t_sel_fit_us": round(fit, 2),
+                                         "kspec_grid": k_grid, "t_spec_us": [round(x, 2) for x in t_spec],
+                                         "kspec_star": kstar}}), flush=True)
 
 
 def source_digest() -> str:

@@ -88,7 +88,7 @@ def lib():
         "prr_score": (i32, [sp, vp, vp, vp, vp, f32, i32, vp]),
         "prr_select_speculate": (i32, [sp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
         "prr_score_speculate": (i32, [sp, vp, vp, vp, vp, f32, i32, vp, vp, vp, vp, i32, vp, vp]),
-        "prr_select_repair": (i32, [sp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]),
+        "prr_select_repair": (i32, [sp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
         "prr_partials_bytes": (sz, [sp, i32]),
         "prr_workspace_bytes": (sz, [sp, i32]),
         "prr_step_ctx_create": (i32, [ctypes.POINTER(vp)]),
@@ -213,8 +213,8 @@ def score_speculate(shape: Shape, q, summaries, scores, ema=None, alpha: float =
 
 
 def select_repair(shape: Shape, scores, top_k: int, sel_idx, q, k_cache, v_cache, block_table, out, n_missed,
-                  ema=None, k_spec_next: int = 0, pred_idx_next=None, pred_idx=None, k_spec: int = 0, partials=None,
-                  stream=None) -> None:
+                  workspace, ema=None, k_spec_next: int = 0, pred_idx_next=None, pred_idx=None, k_spec: int = 0,
+                  partials=None, stream=None) -> None:
     dt = shape.torch_dtype
     _check(lib().prr_select_repair(ctypes.byref(shape), _p(scores, torch.float32, "scores"), top_k,
                                    _p(sel_idx, torch.int32, "sel_idx"), _p(ema, torch.float32, "ema"), k_spec_next,
@@ -222,7 +222,8 @@ def select_repair(shape: Shape, scores, top_k: int, sel_idx, q, k_cache, v_cache
                                    _p(k_cache, dt, "k_cache"), _p(v_cache, dt, "v_cache"),
                                    _p(block_table, torch.int32, "block_table"), _p(pred_idx, torch.int32, "pred_idx"),
                                    k_spec, _p(partials, torch.float32, "partials"), _p(out, torch.float32, "out"),
-                                   _p(n_missed, torch.int32, "n_missed"), _s(stream)), "select_repair")
+                                   _p(n_missed, torch.int32, "n_missed"), _p(workspace, None, "workspace"),
+                                   _s(stream)), "select_repair")
 
 
 def partials_bytes(shape: Shape, k_spec: int) -> int:

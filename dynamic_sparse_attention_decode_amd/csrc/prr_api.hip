@@ -291,10 +291,10 @@ prr_status prr_select_repair(const prr_shape* shape, const float* scores, int32_
                              const float* ema, int32_t k_spec_next, int32_t* pred_idx_next, const void* q,
                              const void* k_cache, const void* v_cache, const int32_t* block_table,
                              const int32_t* pred_idx, int32_t k_spec, const float* partials, float* out,
-                             int32_t* n_missed, void* stream) {
+                             int32_t* n_missed, void* workspace, void* stream) {
   PRR_TRY(check_shape(shape));
   PRR_TRY(check_topk_n(shape));
-  PRR_REQUIRE(scores && sel_idx && q && k_cache && v_cache && block_table && out && n_missed,
+  PRR_REQUIRE(scores && sel_idx && q && k_cache && v_cache && block_table && out && n_missed && workspace,
               "select_repair: null pointer");
   PRR_REQUIRE(top_k >= 1 && top_k <= shape->n_blocks, "select_repair: top_k %d not in [1, %d]", top_k,
               shape->n_blocks);
@@ -312,9 +312,9 @@ prr_status prr_select_repair(const prr_shape* shape, const float* scores, int32_
     set_error("select_repair: needs page_size %% 16 == 0, block_size <= 128 and top_k, k_spec, k_spec_next <= 2048");
     return PRR_EUNSUPPORTED;
   }
-  return launch_select_repair(*shape, scores, top_k, sel_idx, ema, k_spec_next, pred_idx_next, q, k_cache, v_cache,
-                              block_table, k_spec ? pred_idx : nullptr, k_spec, k_spec ? partials : nullptr, out,
-                              n_missed, as_stream(stream));
+  return launch_select_missed(*shape, scores, top_k, sel_idx, ema, k_spec_next, pred_idx_next, q, k_cache, v_cache,
+                              block_table, k_spec ? pred_idx : nullptr, k_spec, k_spec ? const_cast<float*>(partials)
+                              : nullptr, false, out, n_missed, workspace, as_stream(stream));
 }
 
 size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec) {
@@ -326,7 +326,8 @@ size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec) {
 
 size_t prr_workspace_bytes(const prr_shape* shape, int32_t top_k) {
   if (check_shape(shape) != PRR_OK || top_k <= 0) return 0;
-  return repair_workspace_bytes(*shape, top_k);
+  const size_t a = repair_workspace_bytes(*shape, top_k), b = select_missed_ws_bytes(*shape, top_k);
+  return a > b ? a : b;
 }
 
 prr_status prr_step_ctx_create(prr_step_ctx** out) {
@@ -382,9 +383,24 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
     if (two_launch_supported(*shape, a->top_k, 0, 0) && (int64_t)shape->batch * shape->n_kv_heads >= 128) {
       PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, nullptr, 0.f, 0, s1));
       return prr_select_repair(shape, a->scores, a->top_k, a->sel_idx, nullptr, 0, nullptr, a->q, a->k_cache,
-                               a->v_cache, a->block_table, nullptr, 0, nullptr, a->out, a->n_missed, s1);
+                               a->v_cache, a->block_table, nullptr, 0, nullptr, a->out, a->n_missed, a->workspace,
+                               s1);
     }
     mode = PRR_MODE_SERIALIZED;
+  }
+  const int64_t rows = (int64_t)shape->batch * shape->n_kv_heads;
+  if (mode == PRR_MODE_FUSED && two_launch_supported(*shape, a->top_k, kc, kn) && (rows >= 128 || a->top_k <= 32)) {
+    // scores + EMA; then selection of T and P_{t+1}, speculation over P_t and the missed blocks T \ P_t in one
+    // launch; then the merge of the missed-block records with the speculated records of T ∩ P_t. One workgroup per
+    // row attends that row's missed blocks after its selection, which pays off when the rows alone fill the chip or
+    // the rows are short; otherwise the missed blocks are spread over a separate repair launch (below).
+    PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step, s1));
+    PRR_REQUIRE(a->workspace && a->sel_idx && a->out && a->n_missed, "decode_step: null pointer");
+    if (kc > 0) PRR_REQUIRE(a->pred_cur && a->partials, "decode_step: null predicted set or partials");
+    if (kn > 0) PRR_REQUIRE(a->ema && a->pred_next && a->pred_next != a->pred_cur, "decode_step: bad prediction buffers");
+    return launch_select_missed(*shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,
+                                a->v_cache, a->block_table, kc ? a->pred_cur : nullptr, kc,
+                                kc ? a->partials : nullptr, true, a->out, a->n_missed, a->workspace, s1);
   }
   if (mode == PRR_MODE_FUSED) {
     PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step, s1));

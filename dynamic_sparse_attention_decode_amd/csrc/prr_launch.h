@@ -72,10 +72,13 @@ bool two_launch_supported(const prr_shape& s, int top_k, int k_spec, int k_spec_
 prr_status launch_score_spec(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema,
                              float alpha, int first, const void* kc, const void* vc, const int32_t* table,
                              const int32_t* pred, int k_spec, float* partials, hipStream_t stream);
-prr_status launch_select_repair(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
+// Selection launch that also attends the missed blocks (T \ P_t) per row, and optionally speculates over P_t, then
+// the merge launch (missed-block record + speculated records of the hits -> out).
+prr_status launch_select_missed(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
                                 int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
-                                const int32_t* table, const int32_t* pred, int k_spec, const float* partials,
-                                float* out, int32_t* n_missed, hipStream_t stream);
+                                const int32_t* table, const int32_t* pred, int k_spec, float* partials,
+                                bool speculate, float* out, int32_t* n_missed, void* workspace, hipStream_t stream);
+size_t select_missed_ws_bytes(const prr_shape& s, int top_k);
 prr_status launch_flush(void* buf, size_t bytes, hipStream_t stream);
 prr_status launch_stream_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);
 

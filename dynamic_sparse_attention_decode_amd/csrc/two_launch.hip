@@ -44,17 +44,46 @@ __global__ __launch_bounds__(256, 3) void score_spec_kernel(const uint8_t* __res
 constexpr int kSRThreads = 512;   // 8 waves: the attention tile keeps its full register budget
 constexpr int kSRMaxK = 2048;     // largest top-K and predicted set handled in LDS
 
+// Per-row workspace of the selection-and-repair launch: the slots of the hits (blocks of T found in P_t), their
+// count, and the partial record of the missed blocks.
+struct MissedWs {
+  int32_t* hits;    // [rows][Kp]
+  int32_t* cnt;     // [rows]
+  float* mrec;      // [rows][RF]
+  int Kp;
+};
+
+__host__ __device__ inline size_t missed_ws_layout(int64_t rows, int K, int RF, void* base, MissedWs* out) {
+  const int Kp = (K + 3) & ~3;
+  const size_t hits_b = (size_t)rows * Kp * 4;
+  const size_t cnt_b = ((size_t)rows * 4 + 255) / 256 * 256;
+  const size_t rec_b = (size_t)rows * RF * 4;
+  if (out) {
+    char* p = static_cast<char*>(base);
+    out->hits = reinterpret_cast<int32_t*>(p);
+    out->cnt = reinterpret_cast<int32_t*>(p + hits_b);
+    out->mrec = reinterpret_cast<float*>(p + hits_b + cnt_b);
+    out->Kp = Kp;
+  }
+  return hits_b + cnt_b + rec_b;
+}
+
+// Workgroup r < rows: true top-K of row r, then (same workgroup) the blocks of T missing from P_t are attended from
+// the KV cache by the 8 waves and merged into one partial record of the row; the hits' slots go to the workspace for
+// the merge launch. Workgroups [rows, rows + n_pwg): next predicted set (top-K' of the updated EMA). The rest:
+// speculation over P_t (one wave per slot) when spec_total > 0.
 template <int KPT, int DT, int G>
-__global__ __launch_bounds__(kSRThreads) void select_repair_kernel(
+__global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
     const float* __restrict__ scores, int K, int32_t* __restrict__ sel, const float* __restrict__ ema, int Kp_next,
     int32_t* __restrict__ pred_next, const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, const int32_t* __restrict__ pred, int k_spec,
-    const float* __restrict__ partials, float* __restrict__ out, int32_t* __restrict__ n_missed, int Hq, int Hkv,
-    int N, int bs, int page, int pps, float qscale, int rows) {
+    float* __restrict__ partials, int64_t spec_total, MissedWs ws, int32_t* __restrict__ n_missed, int Hq, int Hkv,
+    int N, int bs, int page, int pps, float qscale, int rows, int n_pwg) {
   using W = Tile<DT, G>;
   constexpr int NW = kSRThreads / 64;
   constexpr int D = W::D;
   constexpr int RF = rec_floats(G, D);
+  constexpr int ML = rec_ml(G);
   __shared__ int32_t s_T[kSRMaxK];
   __shared__ int32_t s_P[kSRMaxK];
   __shared__ int32_t s_list[kSRMaxK];   // slots of the hits, then ids of the missed blocks
@@ -64,6 +93,12 @@ __global__ __launch_bounds__(kSRThreads) void select_repair_kernel(
   __shared__ float s_o[NW][G * D];
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (r >= rows + n_pwg) {   // speculation over P_t
+    const int64_t s = (r - rows - n_pwg) * NW + wave;
+    if (s < spec_total)
+      speculate_slot<DT, G>(s, lane, q, kc, vc, table, pred, k_spec, partials, Hq, Hkv, N, bs, page, pps, qscale);
+    return;
+  }
   if (r >= rows) {   // next step's predicted set
     const int64_t rr = r - rows;
     topk_row<kSRThreads, KPT, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp_next, pred_next + rr * Kp_next);
@@ -71,7 +106,7 @@ __global__ __launch_bounds__(kSRThreads) void select_repair_kernel(
   }
   topk_row<kSRThreads, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, s_T);
 
-  // ---- T against P_t: slot of every entry of T in P_t (binary search when P_t is ascending) --------------------
+  // ---- T against P_t: slot of every entry of T in P_t (bisection when P_t is ascending) -------------------------
   const int b = (int)(r / Hkv), g = (int)(r % Hkv);
   const int32_t* prow = k_spec ? pred + r * k_spec : nullptr;
   if (tid == 0) s_unsorted = 0;
@@ -104,7 +139,6 @@ __global__ __launch_bounds__(kSRThreads) void select_repair_kernel(
     }
     nh_local += slot[u] >= 0;
   }
-  // exclusive scan of the hit counts over the workgroup
   uint32_t incl = nh_local;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -121,12 +155,14 @@ __global__ __launch_bounds__(kSRThreads) void select_repair_kernel(
     nh += c;
   }
   uint32_t ph = before + incl - nh_local;   // hits before this thread's entries
+  int32_t* hrow = ws.hits + r * ws.Kp;
 #pragma unroll
   for (int u = 0; u < EPT; ++u) {
     const int j = tid * EPT + u;
     if (j < K) {
       if (slot[u] >= 0) {
-        s_list[ph++] = slot[u];
+        hrow[ph] = slot[u];
+        ++ph;
       } else {
         s_list[nh + (uint32_t)j - ph] = s_T[j];   // misses before entry j = j - hits before j
       }
@@ -135,15 +171,10 @@ __global__ __launch_bounds__(kSRThreads) void select_repair_kernel(
   __syncthreads();
   const int nm = K - (int)nh;
 
-  // ---- the row's attention: each wave merges a share of the hits and computes a share of the misses ------------
+  // ---- the missed blocks, shared among the waves, merged into one record --------------------------------------
   W st;
   st.init(lane);
   st.load_q(q + ((int64_t)b * Hq + (int64_t)g * G) * kRowBytes, qscale);
-  const float* part_row = partials ? partials + r * k_spec * (int64_t)RF : nullptr;
-  const int h0 = (int)((int64_t)nh * wave / NW), h1 = (int)((int64_t)nh * (wave + 1) / NW);
-  run_records(st, h1 - h0, [&](int i) {
-    return part_row + (int64_t)__builtin_amdgcn_readfirstlane(s_list[h0 + i]) * RF;   // uniform: scalar m, l loads
-  });
   const int m0 = (int)((int64_t)nm * wave / NW), m1 = (int)((int64_t)nm * (wave + 1) / NW);
   const int32_t* trow = table + (int64_t)b * pps;
   const int cap = 64 / ((bs + 15) >> 4);   // blocks per pipelined call
@@ -161,22 +192,111 @@ __global__ __launch_bounds__(kSRThreads) void select_repair_kernel(
     s_o[wave][(f / W::VE) * D + st.col * W::VE + (f % W::VE)] = folded[i];
   }
   __syncthreads();
-  float* orow = out + ((int64_t)b * Hq + (int64_t)g * G) * D;
+  float* rec = ws.mrec + r * (int64_t)RF;
   for (int f = tid; f < G * D; f += kSRThreads) {
     const int h = f / D;
     float M = s_ml[0][h];
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h]);
-    float o = 0.f, l = 0.f;
+    float o = 0.f;
+    if (M > -__builtin_huge_valf()) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float c = exp2f(s_ml[w][h] - M);
-      o += s_o[w][f] * c;
-      l += s_ml[w][G + h] * c;
+      for (int w = 0; w < NW; ++w) o += s_o[w][f] * exp2f(s_ml[w][h] - M);
     }
-    orow[f] = o / l;
+    rec[ML + f] = o;
   }
-  if (tid == 0) n_missed[r] = nm;
+  if (tid < G) {
+    const int h = tid;
+    float M = s_ml[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h]);
+    float l = 0.f;
+    if (M > -__builtin_huge_valf()) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) l += s_ml[w][G + h] * exp2f(s_ml[w][h] - M);
+    }
+    rec[h] = M;   // -inf and l = 0 when nothing was missed: the record then carries no weight
+    rec[G + h] = l;
+  }
+  if (tid == 0) {
+    ws.cnt[r] = (int)nh;
+    n_missed[r] = nm;
+  }
+}
+
+// out[b, g*G + h] = merge of the row's missed-block record and the speculated records of its hits, normalised. One
+// 256-thread workgroup per (row, head): the weights exp2(m_i - M) go to LDS, then 256 / (D/4) record groups
+// accumulate float4 slices of O with 8 loads in flight per thread.
+template <int G, int D>
+__global__ __launch_bounds__(256) void merge_hits_kernel(const float* __restrict__ partials, int k_spec, MissedWs ws,
+                                                         float* __restrict__ out, int Hq, int Hkv) {
+  constexpr int RF = rec_floats(G, D), ML = rec_ml(G);
+  constexpr int S = D / 4, P = 256 / S, U = 8;
+  __shared__ float s_w[kSRMaxK + 1];
+  __shared__ const float* s_rec[kSRMaxK + 1];
+  __shared__ float s_red[2][4];
+  __shared__ float4 s_acc[P][S];
+  const int64_t r = blockIdx.x;
+  const int h = blockIdx.y;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int b = (int)(r / Hkv), g = (int)(r % Hkv);
+  const int nh = ws.cnt[r];
+  const int n = nh + 1;   // record 0: the missed blocks; records 1..nh: speculated hits
+  const float* mrec = ws.mrec + r * (int64_t)RF;
+  const float* part_row = partials ? partials + r * k_spec * (int64_t)RF : nullptr;
+  float mx = -__builtin_huge_valf();
+  for (int i = t; i < n; i += 256) {
+    const float* rec = i == 0 ? mrec : part_row + (int64_t)ws.hits[r * ws.Kp + i - 1] * RF;
+    s_rec[i] = rec;
+    const float m = rec[h];
+    s_w[i] = m;
+    mx = fmaxf(mx, m);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) s_red[0][wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  float ls = 0.f;
+  for (int i = t; i < n; i += 256) {
+    const float w = exp2f(s_w[i] - M);
+    s_w[i] = w;
+    ls += s_rec[i][G + h] * w;
+  }
+  ls = wave_sum(ls);
+  if (lane == 0) s_red[1][wave] = ls;
+  __syncthreads();
+  const float L = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
+  const int slot = t % S, p = t / S;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = p; i0 < n; i0 += U * P) {
+    float4 o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * P;
+      o[u] = i < n ? *reinterpret_cast<const float4*>(s_rec[i] + ML + h * D + slot * 4)
+                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * P;
+      const float wr = i < n ? s_w[i] : 0.f;
+      acc.x = fmaf(o[u].x, wr, acc.x); acc.y = fmaf(o[u].y, wr, acc.y);
+      acc.z = fmaf(o[u].z, wr, acc.z); acc.w = fmaf(o[u].w, wr, acc.w);
+    }
+  }
+  s_acc[p][slot] = acc;
+  __syncthreads();
+  if (t < S) {
+    float4 a = s_acc[0][t];
+#pragma unroll
+    for (int p2 = 1; p2 < P; ++p2) {
+      const float4 c = s_acc[p2][t];
+      a.x += c.x; a.y += c.y; a.z += c.z; a.w += c.w;
+    }
+    const float il = 1.f / L;
+    float* o = out + ((int64_t)b * Hq + (int64_t)g * G + h) * D;
+    *reinterpret_cast<float4*>(o + t * 4) = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+  }
 }
 
 // ---- launchers -----------------------------------------------------------------------------------------------------
@@ -234,39 +354,55 @@ prr_status launch_score_spec(const prr_shape& s, const void* q, const void* summ
   return check_launch("score_speculate");
 }
 
+size_t select_missed_ws_bytes(const prr_shape& s, int top_k) {
+  const int G = s.n_q_heads / s.n_kv_heads;
+  return missed_ws_layout((int64_t)s.batch * s.n_kv_heads, top_k, (int)rec_floats(G, s.head_dim), nullptr, nullptr);
+}
+
 template <int DT, int G>
-static void select_repair_launch(const prr_shape& s, const float* scores, int K, int32_t* sel, const float* ema,
+static void select_missed_launch(const prr_shape& s, const float* scores, int K, int32_t* sel, const float* ema,
                                  int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
-                                 const int32_t* table, const int32_t* pred, int k_spec, const float* partials,
-                                 float* out, int32_t* n_missed, hipStream_t st) {
+                                 const int32_t* table, const int32_t* pred, int k_spec, float* partials,
+                                 bool speculate, float* out, int32_t* n_missed, void* workspace, hipStream_t st) {
+  constexpr int D = 16 * Vec<DT>::n;
   const int rows = s.batch * s.n_kv_heads;
-  const dim3 grid((unsigned)(kp_next > 0 ? 2 * rows : rows)), blk(kSRThreads);
+  MissedWs ws;
+  missed_ws_layout(rows, K, (int)rec_floats(G, D), workspace, &ws);
+  const int n_pwg = kp_next > 0 ? rows : 0;
+  const int64_t spec_total = speculate ? (int64_t)rows * k_spec : 0;
+  constexpr int WPG = kSRThreads / 64;
+  const int n_spec_wg = (int)((spec_total + WPG - 1) / WPG);
+  const dim3 grid((unsigned)(rows + n_pwg + n_spec_wg)), blk(kSRThreads);
   const auto* qq = static_cast<const uint8_t*>(q);
   const auto* kk = static_cast<const uint8_t*>(kc);
   const auto* vv = static_cast<const uint8_t*>(vc);
   const float qs = s.softmax_scale * kLog2e;
-#define PRR_SELREP(KPT)                                                                                            \
-  select_repair_kernel<KPT, DT, G><<<grid, blk, 0, st>>>(scores, K, sel, ema, kp_next, pred_next, qq, kk, vv,       \
-                                                         table, pred, k_spec, partials, out, n_missed, s.n_q_heads, \
-                                                         s.n_kv_heads, s.n_blocks, s.block_size, s.page_size,       \
-                                                         s.pages_per_seq, qs, rows)
+#define PRR_SELMISS(KPT)                                                                                           \
+  select_missed_kernel<KPT, DT, G><<<grid, blk, 0, st>>>(scores, K, sel, ema, kp_next, pred_next, qq, kk, vv,       \
+                                                         table, pred, k_spec, partials, spec_total, ws, n_missed,   \
+                                                         s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size,       \
+                                                         s.page_size, s.pages_per_seq, qs, rows, n_pwg)
+  trace_begin(PRR_KERNEL_SELECT_TOPK, st);
   if (s.n_blocks <= 4 * kSRThreads)
-    PRR_SELREP(4);
+    PRR_SELMISS(4);
   else if (s.n_blocks <= 16 * kSRThreads)
-    PRR_SELREP(16);
+    PRR_SELMISS(16);
   else
-    PRR_SELREP(64);
-#undef PRR_SELREP
+    PRR_SELMISS(64);
+#undef PRR_SELMISS
+  trace_end(PRR_KERNEL_SELECT_TOPK, st);
+  trace_begin(PRR_KERNEL_FINALIZE, st);
+  merge_hits_kernel<G, D><<<dim3((unsigned)rows, (unsigned)G), dim3(256), 0, st>>>(partials, k_spec, ws, out,
+                                                                                   s.n_q_heads, s.n_kv_heads);
+  trace_end(PRR_KERNEL_FINALIZE, st);
 }
 
-prr_status launch_select_repair(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
+prr_status launch_select_missed(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
                                 int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
-                                const int32_t* table, const int32_t* pred, int k_spec, const float* partials,
-                                float* out, int32_t* n_missed, hipStream_t stream) {
-  trace_begin(PRR_KERNEL_REPAIR, stream);
-  PRR_DISPATCH_DT_G(select_repair_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
-                    partials, out, n_missed, stream);
-  trace_end(PRR_KERNEL_REPAIR, stream);
+                                const int32_t* table, const int32_t* pred, int k_spec, float* partials,
+                                bool speculate, float* out, int32_t* n_missed, void* workspace, hipStream_t stream) {
+  PRR_DISPATCH_DT_G(select_missed_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
+                    partials, speculate, out, n_missed, workspace, stream);
   return check_launch("select_repair");
 }
 

@@ -136,24 +136,26 @@ prr_status prr_score_speculate(const prr_shape* shape, const void* q, const void
                                const int32_t* block_table, const int32_t* pred_idx, int32_t k_spec, float* partials,
                                void* stream);
 
-/* In ONE launch, per (b, g) row: the true top-K of `scores` into sel_idx (as prr_score_select), then in the same
- * workgroup the row's repaired attention (PRR abstract: repair the missed blocks once the true set is known):
- * blocks of T in P = pred_idx[b,g,:k_spec] merge their records from `partials` (written by prr_score_speculate or
- * prr_speculate), blocks of T \ P are computed from the KV cache, blocks of P \ T never enter; out = O / l and
- * n_missed = |T \ P| as prr_repair_merge writes them. When k_spec_next > 0 other workgroups also write
- * pred_idx_next = top-k_spec_next of `ema` (already updated). k_spec == 0 attends over all of T (select-then-attend
- * in one launch). Needs no workspace. Returns PRR_EUNSUPPORTED unless page_size is a multiple of 16,
- * block_size <= 128, top_k, k_spec, k_spec_next <= 2048 (the separate calls cover the rest). pred_idx is searched
+/* Selection with repair (PRR abstract: repair the missed blocks once the true set is known), in two launches. Per
+ * (b, g) row: the true top-K of `scores` into sel_idx (as prr_score_select); then, in the same workgroup, the blocks
+ * of T missing from P = pred_idx[b,g,:k_spec] are attended from the KV cache and merged into one partial state;
+ * a second launch merges that state with the records of the blocks of T ∩ P found in `partials` (written before by
+ * prr_score_speculate or prr_speculate) — blocks of P outside T never enter — and writes out = O / l and
+ * n_missed = |T minus P| as prr_repair_merge does. When k_spec_next > 0 other workgroups of the first launch also
+ * write pred_idx_next = top-k_spec_next of `ema` (already updated). k_spec == 0 attends over all of T
+ * (select-then-attend). `workspace` holds prr_workspace_bytes(shape, top_k) bytes (no initialisation needed; calls
+ * sharing one workspace must not overlap). Returns PRR_EUNSUPPORTED unless page_size is a multiple of 16,
+ * block_size <= 128 and top_k, k_spec, k_spec_next <= 2048 (the separate calls cover the rest). pred_idx is searched
  * by bisection when ascending (as the top-K calls write it), linearly otherwise. */
 prr_status prr_select_repair(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
                              const float* ema, int32_t k_spec_next, int32_t* pred_idx_next, const void* q,
                              const void* k_cache, const void* v_cache, const int32_t* block_table,
                              const int32_t* pred_idx, int32_t k_spec, const float* partials, float* out,
-                             int32_t* n_missed, void* stream);
+                             int32_t* n_missed, void* workspace, void* stream);
 
 /* Bytes of the partials buffer for a speculation budget k_spec (0 for k_spec == 0). */
 size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec);
-/* Bytes of the repair workspace for top_k. */
+/* Bytes of the workspace of prr_repair_merge, prr_select_repair and prr_decode_step for top_k. */
 size_t prr_workspace_bytes(const prr_shape* shape, int32_t top_k);
 
 /* ---- one decode step on two streams (the runtime around the calls above) ------------------------------------ */
@@ -163,8 +165,11 @@ typedef enum {
   PRR_MODE_ONE_STREAM = 1,  /* stream_sel: speculate -> score_select -> repair_merge -> ema_predict                */
   PRR_MODE_TWO_STREAM = 2,  /* stream_spec: speculate || stream_sel: score_select; then repair_merge on stream_sel
                                while ema_predict runs on stream_spec                                            */
-  PRR_MODE_FUSED = 3,       /* stream_sel only: score (+ EMA update) -> select_speculate (T, P_{t+1} and the
-                               speculation over P_t in one launch) -> repair_merge                              */
+  PRR_MODE_FUSED = 3,       /* stream_sel only, 3 or 4 launches. When batch * n_kv_heads >= 128 or top_k <= 32
+                               (and select_repair supports the shape): score (+ EMA update) -> one launch
+                               selecting T and P_{t+1}, speculating over P_t and attending the missed blocks
+                               T minus P_t -> one merge launch. Otherwise: score (+ EMA update) ->
+                               select_speculate (T, P_{t+1}, speculation over P_t) -> repair_merge            */
   PRR_MODE_SERIALIZED_FUSED = 4  /* stream_sel only: score -> select_repair with no prediction (select-then-attend
                                     in two launches) when select_repair supports the shape and batch * n_kv_heads
                                     >= 128; otherwise as PRR_MODE_SERIALIZED                                    */

@@ -75,13 +75,15 @@ def test_argument_validation_without_launch():
     assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, nz, 8, nz, nz, nz, nz, nz, nz, 8, nz, None) == -1
     # select_repair: argument checks, then the supported-shape rule (page size multiple of 16, K <= 2048)
     assert lib.prr_select_repair(ctypes.byref(s), nz, 8, nz, None, 0, None, nz, nz, nz, nz, None, 4, None, nz, nz,
-                                 None) == -1                                                  # k_spec > 0, no P
+                                 nz, None) == -1                                              # k_spec > 0, no P
+    assert lib.prr_select_repair(ctypes.byref(s), nz, 8, nz, None, 0, None, nz, nz, nz, nz, None, 0, None, nz, nz,
+                                 None, None) == -1                                            # no workspace
     s8 = _shape(block_size=16, page_size=8, n_blocks=2048)
     assert lib.prr_select_repair(ctypes.byref(s8), nz, 8, nz, None, 0, None, nz, nz, nz, nz, None, 0, None, nz, nz,
-                                 None) == -2                                                  # page 8: unsupported
+                                 nz, None) == -2                                              # page 8: unsupported
     s4 = _shape(n_blocks=4096)
     assert lib.prr_select_repair(ctypes.byref(s4), nz, 2049, nz, None, 0, None, nz, nz, nz, nz, None, 0, None, nz,
-                                 nz, None) == -2                                              # K > 2048
+                                 nz, nz, None) == -2                                          # K > 2048
     assert lib.prr_score_speculate(ctypes.byref(s), nz, nz, nz, None, 0.5, 0, None, None, None, None, 4, None,
                                    None) == -1                                                # k_spec > 0, no KV
     assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 0.9, 0, 0, nz, None) == -1        # K' < 1

@@ -220,7 +220,7 @@ def test_repair_merge_forced_predictions(name):
         out2 = torch.zeros_like(out)
         nm2 = torch.full_like(nm, -1)
         sel2 = torch.zeros_like(sel)
-        L.select_repair(s, scores, K, sel2, q, inp.k_cache, inp.v_cache, inp.table, out2, nm2,
+        L.select_repair(s, scores, K, sel2, q, inp.k_cache, inp.v_cache, inp.table, out2, nm2, ws,
                         pred_idx=pred if kp else None, k_spec=kp, partials=part if kp else None)
         torch.cuda.synchronize()
         assert torch.equal(sel, sel2)
