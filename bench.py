@@ -7,7 +7,7 @@ consecutive steps do not run out of the 256 MB Infinity Cache, the timed loop ro
 KV cache (distinct memory, like the layers of a model), with L (at most 8) chosen so the working set exceeds
 512 MiB where 8 copies suffice; the reported time is per (step, layer).
 
-Prints ONE JSON line. `python bench.py --gpus N` with N > 1 exits: this build runs on one GPU only.
+Prints ONE JSON line. `python bench.py --gpus N` with N > 1 exits: the benchmark runs on one GPU only.
 """
 from __future__ import annotations
 
