@@ -100,10 +100,11 @@ def main():
     streams = (torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev))
     qs = [inp.q[t].contiguous() for t in range(w.steps)]
 
-    def make_layers(mode):
+    def make_layers(mode, k_spec=None):
         ls = []
         for k, v in kvs:
-            lay = PRRLayer(shape, w.top_k, kspec, w.alpha, mode=mode, device=dev, streams=streams)
+            lay = PRRLayer(shape, w.top_k, kspec if k_spec is None else k_spec, w.alpha, mode=mode, device=dev,
+                           streams=streams)
             lay.build(k, v, inp.table)
             ls.append(lay)
         torch.cuda.synchronize()
@@ -157,10 +158,10 @@ def main():
     alg = alg_bytes(a.mode)
     kern = list(alg) + ["finalize"]
 
-    def measure(mode, trace_kernels=None):
+    def measure(mode, trace_kernels=None, k_spec=None):
         """Warm up eagerly, capture exactly a.steps steps (x layers) in a HIP graph, replay once untimed and once
         timed. Returns (us per step, per-kernel launch durations from the timed replay)."""
-        ls = make_layers(mode)
+        ls = make_layers(mode, k_spec)
         run(ls, a.warmup)
         torch.cuda.synchronize()
         tr = None
@@ -311,6 +312,21 @@ def main():
         "working_set_MiB": n_layers * (kv_layer + summ_layer) / 2 ** 20,
     }
     detail["step_GBps"] = detail["step_alg_bytes"] / (us * 1e-6) / 1e9
+    if len(w.k_spec) > 1 and a.mode != "serialized":   # the workload sweeps its speculation budget
+        detail["us_per_step_by_kspec"] = {str(k): measure(a.mode, k_spec=k)[0] for k in w.k_spec}
+    if w.drift_every:   # rebuilding the summaries of the blocks whose keys changed (not part of the step)
+        lay = make_layers(a.mode)[0]
+        ids = torch.as_tensor(inp.drift(w.drift_every), device=dev)
+        lay.rebuild_blocks(ids)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            lay.rebuild_blocks(ids)
+        e1.record()
+        torch.cuda.synchronize()
+        detail["summary_rebuild_us"] = {"blocks": int(ids.numel()), "us": e0.elapsed_time(e1) * 1e3 / 20}
+        lay.close()
     print(f"[bench] {json.dumps(detail)}", file=sys.stderr, flush=True)
 
     cpu = None if a.no_cpu else cpu_baseline(w, inp, kspec, a.cpu_seconds)
