@@ -170,3 +170,38 @@ def test_graph_replay_matches_eager(mode):
         assert np.array_equal(lay.n_missed.cpu().numpy(), ref[base + 3][2])
         del scratch
     lay.close()
+
+
+def _variant(dtype, G, page, k):
+    """A small layer of the given storage dtype and group size (two KV heads, two sequences), with pages shuffled."""
+    from dynamic_sparse_attention_decode_amd.inputs import Workload
+    D = 64 if dtype == "f32" else 128
+    return Workload(f"variant_{dtype}_g{G}_p{page}", 2, 2 * G, 2, D, 32 * 70, 32, page, k, (k + 5,), 0.8, 0.9, 4, 6,
+                    shuffle_pages=True, dtype=dtype, seed=20261203 + 17 * G + page)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_dtypes_and_group_sizes(dtype, G):
+    """Every storage dtype and group size the library supports, through the fused PRR step (page-aligned chunks)
+    and the serialized step on 8-token pages (chunks straddling pages), against the oracle at every step."""
+    for page, mode, k in ((16, "prr_fused", 13), (8, "serialized", 11), (16, "prr_fused", 40), (8, "prr_fused", 13)):
+        w = _variant(dtype, G, page, k)
+        print(f"[case] {w.name} {mode} K={k}", flush=True)
+        inp = make_inputs(w, device="cuda")
+        ov = OracleView(inp)
+        run_layer(w, inp, max(w.k_spec), mode, ov=ov)
+
+
+def test_all_blocks_selected_is_dense_attention():
+    """K = N (every block selected) equals dense attention over the whole context, in the fused PRR step."""
+    w = small("tiny_f32_4k").replace(top_k=128, k_spec=(128,), steps=3)
+    inp = make_inputs(w, device="cuda")
+    ov = OracleView(inp)
+    hist = run_layer(w, inp, 128, "prr_fused", ov=ov)
+    G = w.group
+    for t, h in enumerate(hist):
+        qg = ov.q_group(t, 0, 0)
+        ref = O.attention_over_blocks(qg, ov.keys(0, 0), ov.values(0, 0), np.arange(128), w.block_size, w.scale)
+        assert max_abs(h["out"][0, :G], ref) <= TOL[w.dtype]
+        assert list(h["sel"][0, 0]) == list(range(128))
