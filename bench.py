@@ -354,10 +354,12 @@ def main():
 
 
 def budget_profile(w):
-    """Profiling-guided speculation budget (PRR abstract; PRR summary page, Limitations): the selection time t_sel(N)
-    (scores + top-K) on a grid of block counts that leaves out the workload's own N, the speculation time t_spec(K')
-    on a grid of budgets, both as graph replays of back-to-back calls timed with HIP events; K'* from prr_choose_budget
-    with a degree-2 polynomial for the off-grid N. Prints one JSON line."""
+    """Profiling-guided speculation budget (PRR abstract; PRR summary page, Limitations): selection times on a grid of
+    block counts that leaves out the workload's own N, and the speculation time t_spec(K') on a grid of budgets, all
+    as graph replays of back-to-back calls timed with HIP events; K'* from prr_choose_budget with a degree-2
+    polynomial for the off-grid N. Two windows: the whole selection (scores + top-K), which speculation on a second
+    stream overlaps, and the selection launch alone, which the fused step's speculation overlaps. Prints one JSON
+    line."""
     import numpy as np
     import torch
 
@@ -389,15 +391,19 @@ def budget_profile(w):
     N0 = w.n_blocks
     n_grid = sorted({n for n in (N0 // 8, N0 // 4, N0 // 2, N0 * 2, N0 * 4) if 64 <= n <= 32768} - {N0})
     g_ = torch.Generator(device=dev).manual_seed(w.seed)
-    t_sel = []
+    t_sel, t_topk = [], []
     for n in n_grid:
         s = L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, n, dt, w.scale)
         summ = torch.randn((w.batch, w.n_kv_heads, n, 2, w.head_dim), generator=g_, device=dev).to(w.torch_dtype)
         q = torch.randn((w.batch, w.n_q_heads, w.head_dim), generator=g_, device=dev).to(w.torch_dtype)
         sc = torch.zeros((w.batch, w.n_kv_heads, n), dtype=torch.float32, device=dev)
         sel = torch.zeros((w.batch, w.n_kv_heads, min(w.top_k, n)), dtype=torch.int32, device=dev)
+        # the whole selection (scores + top-K): the window a second stream can overlap
         t_sel.append(timed(lambda st=None, s=s, q=q, summ=summ, sc=sc, sel=sel: L.score_select(
             s, q, summ, sel.shape[-1], sc, sel, stream=st)))
+        # the selection launch alone: the window the fused step's speculation overlaps
+        t_topk.append(timed(lambda st=None, s=s, sc=sc, sel=sel: L.select_speculate(
+            s, sc, sel.shape[-1], sel, stream=st)))
     inp = make_inputs(w, device=dev, steps=2)
     s = L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, N0, dt, w.scale)
     k_grid = sorted({0, w.top_k // 4, w.top_k // 2, w.top_k, (3 * w.top_k) // 2, 2 * w.top_k} | set(w.k_spec))
@@ -415,11 +421,15 @@ def budget_profile(w):
         t_spec.append(timed(lambda st=None, pred=pred, part=part, k=k, q=q: L.speculate(
             s, q, inp.k_cache, inp.v_cache, inp.table, pred, k, part, stream=st)))
     kstar = L.choose_budget(n_grid, t_sel, k_grid, t_spec, float(N0), 2)
+    kstar_fused = L.choose_budget(n_grid, t_topk, k_grid, t_spec, float(N0), 2)
     fit = float(np.polyval(np.polyfit(n_grid, t_sel, 2), N0))
-    print(json.dumps({"budget_profile": {"workload": w.name, "n_target": N0, "n_grid": n_grid,
-                                         "t_sel_us": [round(x, 2) for x in t_sel], "t_sel_fit_us": round(fit, 2),
-                                         "kspec_grid": k_grid, "t_spec_us": [round(x, 2) for x in t_spec],
-                                         "kspec_star": kstar}}), flush=True)
+    fit_topk = float(np.polyval(np.polyfit(n_grid, t_topk, 2), N0))
+    print(json.dumps({"budget_profile": {
+        "workload": w.name, "n_target": N0, "n_grid": n_grid,
+        "t_sel_us": [round(x, 2) for x in t_sel], "t_sel_fit_us": round(fit, 2),
+        "t_select_launch_us": [round(x, 2) for x in t_topk], "t_select_launch_fit_us": round(fit_topk, 2),
+        "kspec_grid": k_grid, "t_spec_us": [round(x, 2) for x in t_spec],
+        "kspec_star_two_stream": kstar, "kspec_star_fused": kstar_fused}}), flush=True)
 
 
 def source_digest() -> str:
