@@ -95,14 +95,21 @@ def main():
     e = w.elem_bytes
     kv_layer = 2 * w.n_pages * w.n_kv_heads * w.page_size * w.head_dim * e
     summ_layer = w.batch * w.n_kv_heads * w.n_blocks * 2 * w.head_dim * e
-    n_layers = a.layers or min(8, max(1, math.ceil(512 * 2 ** 20 / (kv_layer + summ_layer))))
+    # Layers to rotate over: a real model visits every other layer between two visits of one layer, so the bytes one
+    # step touches (summaries, scores and EMA, the true set's and the predicted set's KV) times the layers rotated
+    # must exceed twice the 256 MB Infinity Cache, or later steps would read this layer's data from it. Capped at
+    # 32 layers and 48 GiB of KV (the tiny workload stays cache-resident whatever the count).
+    touched = (w.batch * w.n_kv_heads * (w.n_blocks * (2 * w.head_dim * e + 12)
+                                         + (w.top_k + max(w.k_spec)) * w.block_size * 2 * w.head_dim * e))
+    n_layers = a.layers or int(min(32, max(1, 48 * 2 ** 30 // (kv_layer + summ_layer)),
+                                   max(1, math.ceil(512 * 2 ** 20 / touched))))
     kvs = [(inp.k_cache, inp.v_cache)] + [(inp.k_cache.clone(), inp.v_cache.clone()) for _ in range(n_layers - 1)]
     streams = (torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev))
     qs = [inp.q[t].contiguous() for t in range(w.steps)]
 
-    def make_layers(mode, k_spec=None):
+    def make_layers(mode, k_spec=None, n_kv=None):
         ls = []
-        for k, v in kvs:
+        for k, v in kvs[:n_kv]:
             lay = PRRLayer(shape, w.top_k, kspec if k_spec is None else k_spec, w.alpha, mode=mode, device=dev,
                            streams=streams)
             lay.build(k, v, inp.table)
@@ -158,10 +165,10 @@ def main():
     alg = alg_bytes(a.mode)
     kern = list(alg) + ["finalize"]
 
-    def measure(mode, trace_kernels=None, k_spec=None):
+    def measure(mode, trace_kernels=None, k_spec=None, n_kv=None):
         """Warm up eagerly, capture exactly a.steps steps (x layers) in a HIP graph, replay once untimed and once
         timed. Returns (us per step, per-kernel launch durations from the timed replay)."""
-        ls = make_layers(mode, k_spec)
+        ls = make_layers(mode, k_spec, n_kv)
         run(ls, a.warmup)
         torch.cuda.synchronize()
         tr = None
@@ -226,7 +233,8 @@ def main():
             elif kernel == "select_topk" and mode == "prr_fused" and "repair" in alg:   # the select_spec launch
                 calls.append(lambda lay=lay, q=q, par=par, nxt=nxt, kc=kc: L.select_speculate(
                     shape, lay.scores[par], K, lay.sel_idx, lay.ema, lay.k_spec, lay.pred[nxt], q, lay.k_cache,
-                    lay.v_cache, lay.table, lay.pred[par], kc, lay.partials[par], stream=streams[0]))
+                    lay.v_cache, lay.table, lay.pred[par], kc, lay.partials[par], workspace=lay.workspace,
+                    stream=streams[0]))
             elif kernel == "speculate" and lay.k_spec:
                 calls.append(lambda lay=lay, q=q, par=par: L.speculate(
                     shape, q, lay.k_cache, lay.v_cache, lay.table, lay.pred[par], lay.k_spec, lay.partials[par],
@@ -309,9 +317,12 @@ def main():
         "predictor_overlap": float(np.mean(overlap)) if overlap else None,
         "repaired_blocks_mean": mean_missed,
         "layers_rotated": n_layers,
+        "touched_MiB_per_step": touched / 2 ** 20,
         "working_set_MiB": n_layers * (kv_layer + summ_layer) / 2 ** 20,
     }
     detail["step_GBps"] = detail["step_alg_bytes"] / (us * 1e-6) / 1e9
+    if n_layers > 1:   # the same step with one layer only: its data stays in the Infinity Cache between steps
+        detail["us_per_step_one_layer_cache_warm"] = measure(a.mode, n_kv=1)[0]
     if len(w.k_spec) > 1 and a.mode != "serialized":   # the workload sweeps its speculation budget
         detail["us_per_step_by_kspec"] = {str(k): measure(a.mode, k_spec=k)[0] for k in w.k_spec}
     if w.drift_every:   # rebuilding the summaries of the blocks whose keys changed (not part of the step)
@@ -398,12 +409,13 @@ def budget_profile(w):
         q = torch.randn((w.batch, w.n_q_heads, w.head_dim), generator=g_, device=dev).to(w.torch_dtype)
         sc = torch.zeros((w.batch, w.n_kv_heads, n), dtype=torch.float32, device=dev)
         sel = torch.zeros((w.batch, w.n_kv_heads, min(w.top_k, n)), dtype=torch.int32, device=dev)
+        ws = torch.zeros((L.workspace_bytes(s, sel.shape[-1]) // 4 + 1,), dtype=torch.float32, device=dev)
         # the whole selection (scores + top-K): the window a second stream can overlap
-        t_sel.append(timed(lambda st=None, s=s, q=q, summ=summ, sc=sc, sel=sel: L.score_select(
-            s, q, summ, sel.shape[-1], sc, sel, stream=st)))
+        t_sel.append(timed(lambda st=None, s=s, q=q, summ=summ, sc=sc, sel=sel, ws=ws: L.score_select(
+            s, q, summ, sel.shape[-1], sc, sel, workspace=ws, stream=st)))
         # the selection launch alone: the window the fused step's speculation overlaps
-        t_topk.append(timed(lambda st=None, s=s, sc=sc, sel=sel: L.select_speculate(
-            s, sc, sel.shape[-1], sel, stream=st)))
+        t_topk.append(timed(lambda st=None, s=s, sc=sc, sel=sel, ws=ws: L.select_speculate(
+            s, sc, sel.shape[-1], sel, workspace=ws, stream=st)))
     inp = make_inputs(w, device=dev, steps=2)
     s = L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, N0, dt, w.scale)
     k_grid = sorted({0, w.top_k // 4, w.top_k // 2, w.top_k, (3 * w.top_k) // 2, 2 * w.top_k} | set(w.k_spec))

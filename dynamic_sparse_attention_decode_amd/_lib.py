@@ -81,12 +81,12 @@ def lib():
     sp = ctypes.POINTER(Shape)
     sig = {
         "prr_build_summaries": (i32, [sp, vp, vp, vp, i32, vp, vp]),
-        "prr_score_select": (i32, [sp, vp, vp, i32, vp, vp, vp]),
-        "prr_ema_predict": (i32, [sp, vp, vp, f32, i32, i32, vp, vp]),
+        "prr_score_select": (i32, [sp, vp, vp, i32, vp, vp, vp, vp]),
+        "prr_ema_predict": (i32, [sp, vp, vp, f32, i32, i32, vp, vp, vp]),
         "prr_speculate": (i32, [sp, vp, vp, vp, vp, vp, i32, vp, vp]),
         "prr_repair_merge": (i32, [sp, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp]),
         "prr_score": (i32, [sp, vp, vp, vp, vp, f32, i32, vp]),
-        "prr_select_speculate": (i32, [sp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp]),
+        "prr_select_speculate": (i32, [sp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]),
         "prr_score_speculate": (i32, [sp, vp, vp, vp, vp, f32, i32, vp, vp, vp, vp, i32, vp, vp]),
         "prr_select_repair": (i32, [sp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
         "prr_partials_bytes": (sz, [sp, i32]),
@@ -148,18 +148,19 @@ def build_summaries(shape: Shape, k_cache, block_table, summaries, block_ids=Non
                                      _s(stream)), "build_summaries")
 
 
-def score_select(shape: Shape, q, summaries, top_k: int, scores, sel_idx, stream=None) -> None:
+def score_select(shape: Shape, q, summaries, top_k: int, scores, sel_idx, workspace=None, stream=None) -> None:
     dt = shape.torch_dtype
     _check(lib().prr_score_select(ctypes.byref(shape), _p(q, dt, "q"), _p(summaries, dt, "summaries"), top_k,
                                   _p(scores, torch.float32, "scores"), _p(sel_idx, torch.int32, "sel_idx"),
-                                  _s(stream)), "score_select")
+                                  _p(workspace, None, "workspace"), _s(stream)), "score_select")
 
 
 def ema_predict(shape: Shape, scores, ema, alpha: float, first_step: bool, k_spec: int, pred_idx_next,
-                stream=None) -> None:
+                workspace=None, stream=None) -> None:
     _check(lib().prr_ema_predict(ctypes.byref(shape), _p(scores, torch.float32, "scores"),
                                  _p(ema, torch.float32, "ema"), alpha, int(bool(first_step)), k_spec,
-                                 _p(pred_idx_next, torch.int32, "pred_idx_next"), _s(stream)), "ema_predict")
+                                 _p(pred_idx_next, torch.int32, "pred_idx_next"), _p(workspace, None, "workspace"),
+                                 _s(stream)), "ema_predict")
 
 
 def speculate(shape: Shape, q, k_cache, v_cache, block_table, pred_idx, k_spec: int, partials, stream=None) -> None:
@@ -191,14 +192,15 @@ def score(shape: Shape, q, summaries, scores, ema=None, alpha: float = 0.0, firs
 
 def select_speculate(shape: Shape, scores, top_k: int, sel_idx, ema=None, k_spec_next: int = 0, pred_idx_next=None,
                      q=None, k_cache=None, v_cache=None, block_table=None, pred_idx=None, k_spec: int = 0,
-                     partials=None, stream=None) -> None:
+                     partials=None, workspace=None, stream=None) -> None:
     dt = shape.torch_dtype
     _check(lib().prr_select_speculate(ctypes.byref(shape), _p(scores, torch.float32, "scores"), top_k,
                                       _p(sel_idx, torch.int32, "sel_idx"), _p(ema, torch.float32, "ema"), k_spec_next,
                                       _p(pred_idx_next, torch.int32, "pred_idx_next"), _p(q, dt, "q"),
                                       _p(k_cache, dt, "k_cache"), _p(v_cache, dt, "v_cache"),
                                       _p(block_table, torch.int32, "block_table"), _p(pred_idx, torch.int32, "pred_idx"),
-                                      k_spec, _p(partials, torch.float32, "partials"), _s(stream)), "select_speculate")
+                                      k_spec, _p(partials, torch.float32, "partials"), _p(workspace, None, "workspace"),
+                                      _s(stream)), "select_speculate")
 
 
 def score_speculate(shape: Shape, q, summaries, scores, ema=None, alpha: float = 0.0, first_step=False,

@@ -252,10 +252,10 @@ size_t repair_workspace_bytes(const prr_shape& s, int top_k) { return ws_layout(
 
 // The resolved-page pipelined path: 16-token chunks never straddle a page, and a wave's group of at most 8 entries
 // (or 4 speculation slots) spans at most 64 chunks.
-static bool p16_path(const prr_shape& s) { return (s.page_size & 15) == 0 && s.block_size <= 128; }
+bool p16_path(const prr_shape& s) { return (s.page_size & 15) == 0 && s.block_size <= 128; }
 
 // Slots per speculation wave: about four 16-token chunks per wave, while keeping at least 4096 waves in flight.
-static int spec_spw(const prr_shape& s, int k_spec) {
+int spec_slots_per_wave(const prr_shape& s, int k_spec) {
   const int cpb = (s.block_size + 15) / 16;
   int spw = cpb >= 4 ? 1 : 4 / cpb;
   const int64_t rows = (int64_t)s.batch * s.n_kv_heads;
@@ -266,7 +266,7 @@ static int spec_spw(const prr_shape& s, int k_spec) {
 template <int DT, int G>
 static void spec_launch(const prr_shape& s, const void* q, const void* kc, const void* vc, const int32_t* table,
                         const int32_t* pred, int k_spec, float* partials, hipStream_t st) {
-  const int spw = spec_spw(s, k_spec);
+  const int spw = spec_slots_per_wave(s, k_spec);
   const int wpr = (k_spec + spw - 1) / spw;
   const int64_t total = (int64_t)s.batch * s.n_kv_heads * wpr;
   const float qscale = s.softmax_scale * kLog2e;

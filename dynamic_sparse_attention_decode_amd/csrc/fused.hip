@@ -5,6 +5,11 @@
 // [rows, 2 rows) the next step's predicted set (top-K' of the EMA, which the scoring launch has already updated), and
 // the rest run speculation over the current predicted set, one wave per slot. Selection keeps one workgroup per row
 // busy and is bound by latency, so the speculative loads use bandwidth that would otherwise sit idle.
+//
+// Long rows (given candidate regions): seg_spec_kernel's first workgroups select the top-K of each segment of 2048
+// scores and the top-K' of each segment of the EMA, the rest speculate as the standalone speculation kernel does
+// (256-thread workgroups, several slots per wave); merge2_kernel then selects each row's T and P_{t+1} from the
+// segments' candidates (topk_dev.h).
 #include "attn_wave.h"
 #include "topk_dev.h"
 
@@ -37,6 +42,87 @@ __global__ __launch_bounds__(kSelSpecThreads) void select_spec_kernel(const floa
   if (s < spec_total)
     speculate_slot<DT, G>(s, threadIdx.x & 63, q, kc, vc, table, pred, k_spec, partials, Hq, Hkv, N, bs, page, pps,
                           qscale);
+}
+
+constexpr int kSegSpecThreads = 256;                // the standalone speculation kernel's workgroup
+constexpr int kSelSpecSeg = 8 * kSegSpecThreads;    // segment of one workgroup: 2048 values, 8 per thread
+
+template <int DT, int G, bool P16>
+__global__ __launch_bounds__(kSegSpecThreads, 3) void seg_spec_kernel(const float* __restrict__ scores, int K,
+                                                           const float* __restrict__ ema, int Kp_next, int S,
+                                                           int n_seg_wg, TopkCand ct, TopkCand cp,
+                                                           const uint8_t* __restrict__ q,
+                                                           const uint8_t* __restrict__ kc,
+                                                           const uint8_t* __restrict__ vc,
+                                                           const int32_t* __restrict__ table,
+                                                           const int32_t* __restrict__ pred, int k_spec,
+                                                           float* __restrict__ partials, int spw, int wpr,
+                                                           int64_t spec_waves, int Hq, int Hkv, int N, int bs,
+                                                           int page, int pps, float qscale, int rows) {
+  const int64_t r = blockIdx.x;
+  if (r < n_seg_wg) {
+    const int64_t job = r / S;
+    const int seg = (int)(r % S);
+    if (job < rows)
+      topk_segment<kSegSpecThreads, 8, false>(scores + job * N, nullptr, 0.f, 0, N, K, kSelSpecSeg, seg,
+                                              ct.key + job * ct.cap, ct.idx + job * ct.cap);
+    else
+      topk_segment<kSegSpecThreads, 8, false>(ema + (job - rows) * N, nullptr, 0.f, 0, N, Kp_next, kSelSpecSeg, seg,
+                                              cp.key + (job - rows) * cp.cap, cp.idx + (job - rows) * cp.cap);
+    return;
+  }
+  // speculation as the standalone kernel does it: spw consecutive slots per wave
+  const int64_t w = (r - n_seg_wg) * (kSegSpecThreads / 64) + (threadIdx.x >> 6);
+  if (w >= spec_waves) return;
+  const int64_t rowid = w / wpr;
+  const int j0 = (int)(w - rowid * wpr) * spw;
+  speculate_slots<DT, G, P16>(rowid, j0, min(k_spec, j0 + spw), threadIdx.x & 63, q, kc, vc, table, pred, k_spec,
+                              partials, Hq, Hkv, N, bs, page, pps, qscale);
+}
+
+template <int KPT>
+__global__ __launch_bounds__(1024) void merge2_kernel(TopkCand ct, int Ct, int K, int32_t* __restrict__ sel,
+                                                      TopkCand cp, int Cp, int Kp_next,
+                                                      int32_t* __restrict__ pred_next, int rows) {
+  const int64_t r = blockIdx.x;
+  if (r < rows)
+    topk_merge_row<1024, KPT>(ct.key + r * ct.cap, ct.idx + r * ct.cap, Ct, K, sel + r * K);
+  else
+    topk_merge_row<1024, KPT>(cp.key + (r - rows) * cp.cap, cp.idx + (r - rows) * cp.cap, Cp, Kp_next,
+                              pred_next + (r - rows) * Kp_next);
+}
+
+template <int DT, int G>
+static void seg_spec_launch(const prr_shape& s, const float* scores, int K, int32_t* sel, const float* ema,
+                            int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
+                            const int32_t* table, const int32_t* pred, int k_spec, float* partials,
+                            const TopkCand& ct, const TopkCand& cp, hipStream_t st) {
+  const int rows = s.batch * s.n_kv_heads;
+  const TopkSplit pt = topk_split(s.n_blocks, K, kSelSpecSeg);
+  const TopkSplit pp = topk_split(s.n_blocks, kp_next > 0 ? kp_next : 1, kSelSpecSeg);
+  const int n_seg_wg = (kp_next > 0 ? 2 : 1) * rows * pt.S;
+  const int spw = k_spec > 0 ? spec_slots_per_wave(s, k_spec) : 1;
+  const int wpr = (k_spec + spw - 1) / spw;
+  const int64_t spec_waves = (int64_t)rows * wpr;
+  constexpr int WPG = kSegSpecThreads / 64;
+  const int n_spec_wg = (int)((spec_waves + WPG - 1) / WPG);
+  auto kern = p16_path(s) ? seg_spec_kernel<DT, G, true> : seg_spec_kernel<DT, G, false>;
+  kern<<<dim3((unsigned)(n_seg_wg + n_spec_wg)), kSegSpecThreads, 0, st>>>(
+      scores, K, ema, kp_next, pt.S, n_seg_wg, ct, cp, static_cast<const uint8_t*>(q),
+      static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, pred, k_spec, partials, spw, wpr,
+      spec_waves, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size, s.pages_per_seq,
+      s.softmax_scale * kLog2e, rows);
+  const int cmax = kp_next > 0 && pp.C > pt.C ? pp.C : pt.C;
+  const dim3 grid((unsigned)((kp_next > 0 ? 2 : 1) * rows));
+#define PRR_MERGE2(KPT) \
+  merge2_kernel<KPT><<<grid, 1024, 0, st>>>(ct, pt.C, K, sel, cp, pp.C, kp_next, pred_next, rows)
+  switch (topk_kpt(cmax)) {
+    case 1: case 2: PRR_MERGE2(2); break;
+    case 4: PRR_MERGE2(4); break;
+    case 8: PRR_MERGE2(8); break;
+    default: PRR_MERGE2(16); break;   // C <= 16384 (topk_split_on)
+  }
+#undef PRR_MERGE2
 }
 
 template <int DT, int G>
@@ -72,10 +158,17 @@ static void select_spec_launch(const prr_shape& s, const float* scores, int K, i
 prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
                               int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                               const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                              hipStream_t stream) {
+                              hipStream_t stream, void* cand_t, void* cand_p) {
   trace_begin(PRR_KERNEL_SELECT_TOPK, stream);
-  PRR_DISPATCH_DT_G(select_spec_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
-                    partials, stream);
+  if (cand_t && cand_p && topk_split_on(s.n_blocks, k, kSelSpecSeg) &&
+      (kp_next == 0 || topk_split_on(s.n_blocks, kp_next, kSelSpecSeg))) {
+    const TopkCand ct = topk_cand_at(s, cand_t), cp = topk_cand_at(s, cand_p);
+    PRR_DISPATCH_DT_G(seg_spec_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
+                      partials, ct, cp, stream);
+  } else {
+    PRR_DISPATCH_DT_G(select_spec_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
+                      partials, stream);
+  }
   trace_end(PRR_KERNEL_SELECT_TOPK, stream);
   return check_launch("select_speculate");
 }

@@ -177,6 +177,20 @@ struct prr_step_ctx {
   hipEvent_t q_ready, spec_done, sel_done, spec_tail;
 };
 
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// The workspace: two top-K candidate regions for long rows (the true set's and the predicted set's), then the
+// repair's part (spread-out or row-wise repair). The three parts are disjoint, so the true-set selection, the
+// predicted-set selection and the repair may run at once.
+static size_t cand_part_bytes(const prr_shape& s) { return round256(topk_cand_bytes(s)); }
+
+static void* cand_region(const prr_shape& s, void* ws, int which) {
+  if (!ws || topk_cand_bytes(s) == 0) return nullptr;
+  return static_cast<char*>(ws) + (size_t)which * cand_part_bytes(s);
+}
+
+static void* repair_ws(const prr_shape& s, void* ws) { return static_cast<char*>(ws) + 2 * cand_part_bytes(s); }
+
 extern "C" {
 
 prr_status prr_build_summaries(const prr_shape* shape, const void* k_cache, const int32_t* block_table,
@@ -192,25 +206,27 @@ prr_status prr_build_summaries(const prr_shape* shape, const void* k_cache, cons
 }
 
 prr_status prr_score_select(const prr_shape* shape, const void* q, const void* summaries, int32_t top_k,
-                            float* scores, int32_t* sel_idx, void* stream) {
+                            float* scores, int32_t* sel_idx, void* workspace, void* stream) {
   PRR_TRY(check_shape(shape));
   PRR_TRY(check_topk_n(shape));
   PRR_REQUIRE(q && summaries && scores && sel_idx, "score_select: null pointer");
   PRR_REQUIRE(top_k >= 1 && top_k <= shape->n_blocks, "score_select: top_k %d not in [1, %d]", top_k,
               shape->n_blocks);
   PRR_TRY(launch_score(*shape, q, summaries, scores, nullptr, 0.f, 0, as_stream(stream)));
-  return launch_topk(*shape, scores, nullptr, 0.f, 0, top_k, sel_idx, as_stream(stream));
+  return launch_topk(*shape, scores, nullptr, 0.f, 0, top_k, sel_idx, as_stream(stream),
+                     cand_region(*shape, workspace, 0));
 }
 
 prr_status prr_ema_predict(const prr_shape* shape, const float* scores, float* ema, float alpha, int32_t first_step,
-                           int32_t k_spec, int32_t* pred_idx_next, void* stream) {
+                           int32_t k_spec, int32_t* pred_idx_next, void* workspace, void* stream) {
   PRR_TRY(check_shape(shape));
   PRR_TRY(check_topk_n(shape));
   PRR_REQUIRE(scores && ema && pred_idx_next, "ema_predict: null pointer");
   PRR_REQUIRE(k_spec >= 1 && k_spec <= shape->n_blocks, "ema_predict: k_spec %d not in [1, %d]", k_spec,
               shape->n_blocks);
   PRR_REQUIRE(alpha >= 0.f && alpha <= 1.f, "ema_predict: alpha not in [0, 1]");
-  return launch_topk(*shape, scores, ema, alpha, first_step ? 1 : 0, k_spec, pred_idx_next, as_stream(stream));
+  return launch_topk(*shape, scores, ema, alpha, first_step ? 1 : 0, k_spec, pred_idx_next, as_stream(stream),
+                     cand_region(*shape, workspace, 1));
 }
 
 prr_status prr_speculate(const prr_shape* shape, const void* q, const void* k_cache, const void* v_cache,
@@ -237,7 +253,8 @@ prr_status prr_repair_merge(const prr_shape* shape, const void* q, const void* k
               shape->n_blocks);
   if (k_spec > 0) PRR_REQUIRE(pred_idx && partials, "repair_merge: k_spec > 0 needs pred_idx and partials");
   return launch_repair(*shape, q, k_cache, v_cache, block_table, sel_idx, top_k, k_spec ? pred_idx : nullptr,
-                       k_spec, k_spec ? partials : nullptr, out, n_missed, workspace, as_stream(stream));
+                       k_spec, k_spec ? partials : nullptr, out, n_missed, repair_ws(*shape, workspace),
+                       as_stream(stream));
 }
 
 prr_status prr_score(const prr_shape* shape, const void* q, const void* summaries, float* scores, float* ema,
@@ -251,7 +268,8 @@ prr_status prr_score(const prr_shape* shape, const void* q, const void* summarie
 prr_status prr_select_speculate(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
                                 const float* ema, int32_t k_spec_next, int32_t* pred_idx_next, const void* q,
                                 const void* k_cache, const void* v_cache, const int32_t* block_table,
-                                const int32_t* pred_idx, int32_t k_spec, float* partials, void* stream) {
+                                const int32_t* pred_idx, int32_t k_spec, float* partials, void* workspace,
+                                void* stream) {
   PRR_TRY(check_shape(shape));
   PRR_TRY(check_topk_n(shape));
   PRR_REQUIRE(scores && sel_idx, "select_speculate: null pointer");
@@ -269,7 +287,8 @@ prr_status prr_select_speculate(const prr_shape* shape, const float* scores, int
     return PRR_EINVAL;
   }
   return launch_select_spec(*shape, scores, top_k, sel_idx, ema, k_spec_next, pred_idx_next, q, k_cache, v_cache,
-                            block_table, pred_idx, k_spec, partials, as_stream(stream));
+                            block_table, pred_idx, k_spec, partials, as_stream(stream),
+                            cand_region(*shape, workspace, 0), cand_region(*shape, workspace, 1));
 }
 
 prr_status prr_score_speculate(const prr_shape* shape, const void* q, const void* summaries, float* scores, float* ema,
@@ -314,7 +333,7 @@ prr_status prr_select_repair(const prr_shape* shape, const float* scores, int32_
   }
   return launch_select_missed(*shape, scores, top_k, sel_idx, ema, k_spec_next, pred_idx_next, q, k_cache, v_cache,
                               block_table, k_spec ? pred_idx : nullptr, k_spec, k_spec ? const_cast<float*>(partials)
-                              : nullptr, false, out, n_missed, workspace, as_stream(stream));
+                              : nullptr, false, out, n_missed, repair_ws(*shape, workspace), as_stream(stream));
 }
 
 size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec) {
@@ -327,7 +346,7 @@ size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec) {
 size_t prr_workspace_bytes(const prr_shape* shape, int32_t top_k) {
   if (check_shape(shape) != PRR_OK || top_k <= 0) return 0;
   const size_t a = repair_workspace_bytes(*shape, top_k), b = select_missed_ws_bytes(*shape, top_k);
-  return a > b ? a : b;
+  return 2 * cand_part_bytes(*shape) + (a > b ? a : b);
 }
 
 prr_status prr_step_ctx_create(prr_step_ctx** out) {
@@ -400,22 +419,30 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
     if (kn > 0) PRR_REQUIRE(a->ema && a->pred_next && a->pred_next != a->pred_cur, "decode_step: bad prediction buffers");
     return launch_select_missed(*shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,
                                 a->v_cache, a->block_table, kc ? a->pred_cur : nullptr, kc,
-                                kc ? a->partials : nullptr, true, a->out, a->n_missed, a->workspace, s1);
+                                kc ? a->partials : nullptr, true, a->out, a->n_missed,
+                                repair_ws(*shape, a->workspace), s1);
   }
+  // long rows select in two launches (segments, then a merge) through the workspace's candidate regions
   if (mode == PRR_MODE_FUSED) {
     PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step, s1));
     PRR_TRY(prr_select_speculate(shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,
-                                 a->v_cache, a->block_table, a->pred_cur, kc, a->partials, s1));
+                                 a->v_cache, a->block_table, a->pred_cur, kc, a->partials, a->workspace, s1));
     return prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
                             kc, a->partials, a->out, a->n_missed, a->workspace, s1);
   }
+  auto score_select = [&](hipStream_t st) {
+    return prr_score_select(shape, a->q, a->summaries, a->top_k, a->scores, a->sel_idx, a->workspace, st);
+  };
+  auto ema_predict = [&](hipStream_t st) {
+    return prr_ema_predict(shape, a->scores, a->ema, a->alpha, a->first_step, kn, a->pred_next, a->workspace, st);
+  };
   if (mode != PRR_MODE_TWO_STREAM) {
     if (kc > 0) PRR_TRY(prr_speculate(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->pred_cur, kc,
                                       a->partials, s1));
-    PRR_TRY(prr_score_select(shape, a->q, a->summaries, a->top_k, a->scores, a->sel_idx, s1));
+    PRR_TRY(score_select(s1));
     PRR_TRY(prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
                              kc, a->partials, a->out, a->n_missed, a->workspace, s1));
-    if (kn > 0) PRR_TRY(prr_ema_predict(shape, a->scores, a->ema, a->alpha, a->first_step, kn, a->pred_next, s1));
+    if (kn > 0) PRR_TRY(ema_predict(s1));
     return PRR_OK;
   }
   PRR_TRY(hip_ok(hipEventRecord(ctx->q_ready, s1), "decode_step: record q_ready"));
@@ -423,14 +450,14 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
   if (kc > 0) PRR_TRY(prr_speculate(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->pred_cur, kc,
                                     a->partials, s2));
   PRR_TRY(hip_ok(hipEventRecord(ctx->spec_done, s2), "decode_step: record spec_done"));
-  PRR_TRY(prr_score_select(shape, a->q, a->summaries, a->top_k, a->scores, a->sel_idx, s1));
+  PRR_TRY(score_select(s1));
   PRR_TRY(hip_ok(hipEventRecord(ctx->sel_done, s1), "decode_step: record sel_done"));
   PRR_TRY(hip_ok(hipStreamWaitEvent(s1, ctx->spec_done, 0), "decode_step: wait spec_done"));
   PRR_TRY(prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
                            kc, a->partials, a->out, a->n_missed, a->workspace, s1));
   if (kn > 0) {
     PRR_TRY(hip_ok(hipStreamWaitEvent(s2, ctx->sel_done, 0), "decode_step: wait sel_done"));
-    PRR_TRY(prr_ema_predict(shape, a->scores, a->ema, a->alpha, a->first_step, kn, a->pred_next, s2));
+    PRR_TRY(ema_predict(s2));
   }
   if (join) {
     PRR_TRY(hip_ok(hipEventRecord(ctx->spec_tail, s2), "decode_step: record spec_tail"));

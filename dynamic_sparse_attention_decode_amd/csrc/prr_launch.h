@@ -54,8 +54,21 @@ prr_status launch_summaries(const prr_shape& s, const void* k_cache, const int32
 // Scores; with ema != nullptr also the EMA update (first != 0: ema = scores).
 prr_status launch_score(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema, float alpha,
                         int first, hipStream_t stream);
+// Top-K of each row (with ema != nullptr: of the EMA after its update). With cand != nullptr (a candidate region of
+// topk_cand_bytes) rows longer than kTopkSplitMinN are split into segments, then merged.
 prr_status launch_topk(const prr_shape& s, const float* values, float* ema, float alpha, int first, int k,
-                       int32_t* out_idx, hipStream_t stream);
+                       int32_t* out_idx, hipStream_t stream, void* cand = nullptr);
+constexpr int kTopkSplitMinN = 8192;   // shorter rows take one workgroup each
+constexpr int kTopkSeg1024 = 4096;     // segment of a 1024-thread workgroup (4 values per thread)
+struct TopkCand {
+  uint32_t* key;
+  int32_t* idx;
+  int64_t cap;   // candidate slots per row
+};
+size_t topk_cand_row_capacity(int N);
+size_t topk_cand_bytes(const prr_shape& s);   // one candidate region (0 when rows are never split)
+bool topk_split_on(int N, int K, int seg);
+TopkCand topk_cand_at(const prr_shape& s, void* region);
 prr_status launch_speculate(const prr_shape& s, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* table, const int32_t* pred, int k_spec, float* partials,
                             hipStream_t stream);
@@ -63,10 +76,15 @@ prr_status launch_repair(const prr_shape& s, const void* q, const void* k_cache,
                          const int32_t* table, const int32_t* sel, int top_k, const int32_t* pred, int k_spec,
                          const float* partials, float* out, int32_t* n_missed, void* workspace, hipStream_t stream);
 size_t repair_workspace_bytes(const prr_shape& s, int top_k);
+// The resolved-page pipelined attention path: 16-token chunks never straddle a page, and a wave's group of at most
+// 8 entries (or 4 speculation slots) spans at most 64 chunks.
+bool p16_path(const prr_shape& s);
+// Predicted slots per speculation wave: about four 16-token chunks per wave, while keeping >= 4096 waves in flight.
+int spec_slots_per_wave(const prr_shape& s, int k_spec);
 prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
                               int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                               const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                              hipStream_t stream);
+                              hipStream_t stream, void* cand_t = nullptr, void* cand_p = nullptr);
 // The two-launch step: scores (+ EMA) with speculation, then selection with the row-wise repair and merge.
 bool two_launch_supported(const prr_shape& s, int top_k, int k_spec, int k_spec_next);
 prr_status launch_score_spec(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema,

@@ -5,6 +5,8 @@
 // score_kernel: Quest's group-summed block score as a streaming GEMV over all CUs (score_dev.h); optionally updates
 //   the EMA in the same pass.
 // topk_kernel: one 1024-thread workgroup per (b, g) row (topk_dev.h); optionally updates the EMA first.
+// topk_seg_kernel + topk_merge_kernel: the same top-K for long rows when a candidate workspace is given: one
+//   workgroup per segment of 4096 values, then one per row over the segments' candidates.
 #include "score_dev.h"
 #include "topk_dev.h"
 
@@ -22,6 +24,23 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ vals
                                                   float alpha, int first, int N, int K, int32_t* __restrict__ out) {
   const int64_t row = blockIdx.x;
   topk_row<NT, KPT, EMA>(vals + row * N, EMA ? ema + row * N : nullptr, alpha, first, N, K, out + row * K);
+}
+
+template <int KPT, bool EMA>
+__global__ __launch_bounds__(1024) void topk_seg_kernel(const float* __restrict__ vals, float* __restrict__ ema,
+                                                        float alpha, int first, int N, int K, int seg, int64_t cap,
+                                                        uint32_t* __restrict__ ckey, int32_t* __restrict__ cidx) {
+  const int64_t row = blockIdx.y;
+  topk_segment<1024, KPT, EMA>(vals + row * N, EMA ? ema + row * N : nullptr, alpha, first, N, K, seg, blockIdx.x,
+                               ckey + row * cap, cidx + row * cap);
+}
+
+template <int KPT>
+__global__ __launch_bounds__(1024) void topk_merge_kernel(const uint32_t* __restrict__ ckey,
+                                                          const int32_t* __restrict__ cidx, int64_t cap, int C, int K,
+                                                          int32_t* __restrict__ out) {
+  const int64_t row = blockIdx.x;
+  topk_merge_row<1024, KPT>(ckey + row * cap, cidx + row * cap, C, K, out + row * K);
 }
 
 // ---- launchers -----------------------------------------------------------------------------------------------------
@@ -63,16 +82,59 @@ static void topk_dispatch(int kpt, dim3 grid, const float* vals, float* ema, flo
   }
 }
 
+size_t topk_cand_row_capacity(int N) {
+  return N > kTopkSplitMinN ? (size_t)((N / 2 + 2048 + 3) & ~3) : 0;
+}
+
+size_t topk_cand_bytes(const prr_shape& s) {
+  return (size_t)s.batch * s.n_kv_heads * topk_cand_row_capacity(s.n_blocks) * (sizeof(uint32_t) + sizeof(int32_t));
+}
+
+bool topk_split_on(int N, int K, int seg) {
+  // the merge holds at most 16 candidates per thread of a 1024-thread workgroup
+  return N > kTopkSplitMinN && K <= seg / 2 && topk_split(N, K, seg).C <= 16 * 1024;
+}
+
+TopkCand topk_cand_at(const prr_shape& s, void* region) {
+  const int64_t cap = (int64_t)topk_cand_row_capacity(s.n_blocks);
+  auto* k = static_cast<uint32_t*>(region);
+  return TopkCand{k, reinterpret_cast<int32_t*>(k + (int64_t)s.batch * s.n_kv_heads * cap), cap};
+}
+
+template <bool EMA>
+static void topk_split_launch(const prr_shape& s, const float* vals, float* ema, float alpha, int first, int K,
+                              int32_t* out, const TopkCand& c, hipStream_t st) {
+  const int rows = s.batch * s.n_kv_heads;
+  const TopkSplit p = topk_split(s.n_blocks, K, kTopkSeg1024);
+  topk_seg_kernel<4, EMA><<<dim3((unsigned)p.S, (unsigned)rows), 1024, 0, st>>>(vals, ema, alpha, first, s.n_blocks,
+                                                                                K, p.seg, c.cap, c.key, c.idx);
+  const dim3 grid((unsigned)rows);
+  switch (topk_kpt(p.C)) {
+    case 1: case 2: topk_merge_kernel<2><<<grid, 1024, 0, st>>>(c.key, c.idx, c.cap, p.C, K, out); break;
+    case 4: topk_merge_kernel<4><<<grid, 1024, 0, st>>>(c.key, c.idx, c.cap, p.C, K, out); break;
+    case 8: topk_merge_kernel<8><<<grid, 1024, 0, st>>>(c.key, c.idx, c.cap, p.C, K, out); break;
+    default: topk_merge_kernel<16><<<grid, 1024, 0, st>>>(c.key, c.idx, c.cap, p.C, K, out); break;   // C <= 16384
+  }
+}
+
 prr_status launch_topk(const prr_shape& s, const float* values, float* ema, float alpha, int first, int k,
-                       int32_t* out_idx, hipStream_t stream) {
-  const int kpt = topk_kpt(s.n_blocks);
-  const dim3 grid((unsigned)(s.batch * s.n_kv_heads));
+                       int32_t* out_idx, hipStream_t stream, void* cand) {
   const int kid = ema ? PRR_KERNEL_EMA_TOPK : PRR_KERNEL_SELECT_TOPK;
   trace_begin(kid, stream);
-  if (ema)
-    topk_dispatch<true>(kpt, grid, values, ema, alpha, first, s.n_blocks, k, out_idx, stream);
-  else
-    topk_dispatch<false>(kpt, grid, values, nullptr, alpha, first, s.n_blocks, k, out_idx, stream);
+  if (cand && topk_split_on(s.n_blocks, k, kTopkSeg1024)) {
+    const TopkCand c = topk_cand_at(s, cand);
+    if (ema)
+      topk_split_launch<true>(s, values, ema, alpha, first, k, out_idx, c, stream);
+    else
+      topk_split_launch<false>(s, values, nullptr, alpha, first, k, out_idx, c, stream);
+  } else {
+    const int kpt = topk_kpt(s.n_blocks);
+    const dim3 grid((unsigned)(s.batch * s.n_kv_heads));
+    if (ema)
+      topk_dispatch<true>(kpt, grid, values, ema, alpha, first, s.n_blocks, k, out_idx, stream);
+    else
+      topk_dispatch<false>(kpt, grid, values, nullptr, alpha, first, s.n_blocks, k, out_idx, stream);
+  }
   trace_end(kid, stream);
   return check_launch(ema ? "ema_predict" : "select_topk");
 }

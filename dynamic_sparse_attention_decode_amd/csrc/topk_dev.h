@@ -8,6 +8,12 @@
 // every key above the threshold class and the lowest-index keys of the threshold class; one workgroup-wide scan
 // gives each thread its output offset, so the output comes out in ascending block order. Optionally updates the EMA
 // in the same pass.
+//
+// Long rows split: a row cut into segments has its top-K among the union of the segments' top-K sets (a key with
+// fewer than K keys ahead of it in the row has fewer than K ahead of it in its segment, under the same order of
+// value then index). One workgroup per segment writes its top-K as (key, index) candidates in ascending index order,
+// the segments one after another, so the candidate list is in ascending block order; one workgroup per row then
+// selects the top-K of the candidates with the same tie rule by position.
 #pragma once
 #include "prr_device.h"
 
@@ -38,11 +44,45 @@ __device__ inline uint32_t shr(uint32_t x, int s) { return s >= 32 ? 0u : x >> s
 // Shared LDS of the top-K routine (one per workgroup).
 struct TopkLds {
   uint32_t hist[256];
-  float red_f[2][16];
+  uint32_t red_k[2][16];
   uint32_t red_u[16];
   uint32_t bc[3];
   int flag;
 };
+
+__device__ inline uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, d));
+  return x;
+}
+
+__device__ inline uint32_t wave_min_u32(uint32_t x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, d));
+  return x;
+}
+
+// Largest and smallest counted key of the workgroup (integer order, so +0 and -0 stay apart as the keys do).
+template <int NT, int NK, typename ValidFn>
+__device__ inline void block_key_range(const uint32_t (&key)[NK], ValidFn&& valid, uint32_t& kmax, uint32_t& kmin,
+                                       TopkLds& L) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t hi = 0u, lo = 0xffffffffu;
+#pragma unroll
+  for (int j = 0; j < NK; ++j)
+    if (valid(j)) { hi = max(hi, key[j]); lo = min(lo, key[j]); }
+  hi = wave_max_u32(hi);
+  lo = wave_min_u32(lo);
+  if (lane == 0) { L.red_k[0][wave] = hi; L.red_k[1][wave] = lo; }
+  __syncthreads();
+  hi = L.red_k[0][0];
+  lo = L.red_k[1][0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) { hi = max(hi, L.red_k[0][w]); lo = min(lo, L.red_k[1][w]); }
+  kmax = hi;
+  kmin = lo;
+}
 
 // Radix state: the K-th largest counted key lies in {x : x >> shift == prefix >> shift}; keys above that class are
 // all taken, and krem keys of the class (the lowest-index ones).
@@ -116,11 +156,12 @@ __device__ inline uint32_t block_scan(uint32_t x, uint32_t& total, TopkLds& L) {
   return before + incl - x;
 }
 
-// Writes the selected indices (all keys above the radix class, and the first krem keys of the class in order)
-// in ascending order. Thread t holds keys NK per thread in index order; idx_of(j) gives key j's index.
-template <int NT, int NK, typename ValidFn, typename IdxFn>
-__device__ inline void write_selected(const uint32_t (&key)[NK], ValidFn&& valid, const Radix& R, int K,
-                                      int32_t* __restrict__ orow, int32_t* lds_out, TopkLds& L, IdxFn&& idx_of) {
+// Emits the selected keys (all keys above the radix class, and the first krem keys of the class in order) in
+// ascending order: emit(pos, j) for this thread's key j at output slot pos. Thread t holds keys NK per thread in
+// index order.
+template <int NT, int NK, typename ValidFn, typename EmitFn>
+__device__ inline void write_selected(const uint32_t (&key)[NK], ValidFn&& valid, const Radix& R, int K, TopkLds& L,
+                                      EmitFn&& emit) {
   const uint32_t pk = shr(R.prefix, R.shift);
   uint32_t cg = 0, ce = 0;
 #pragma unroll
@@ -144,32 +185,35 @@ __device__ inline void write_selected(const uint32_t (&key)[NK], ValidFn&& valid
       bool take = hk > pk;
       if (hk == pk) take = le++ < R.krem;
       if (take) {
-        if (pos < (uint32_t)K) {   // pos < K always holds; the guard keeps a logic error in bounds
-          const int32_t i = idx_of(j);
-          orow[pos] = i;
-          if (lds_out) lds_out[pos] = i;
-        }
+        if (pos < (uint32_t)K) emit(pos, j);   // pos < K always holds; the guard keeps a logic error in bounds
         ++pos;
       }
     }
   }
 }
 
+// Top-K of the counted keys, emitted in ascending order (see write_selected).
+template <int NT, int NK, typename ValidFn, typename EmitFn>
+__device__ inline void select_top(const uint32_t (&key)[NK], ValidFn&& valid, int K, TopkLds& L, EmitFn&& emit) {
+  uint32_t kmax, kmin;
+  block_key_range<NT>(key, valid, kmax, kmin, L);
+  const Radix R = radix_select<NT, NK>(key, valid, kmax, kmin, (uint32_t)K, L);
+  write_selected<NT, NK>(key, valid, R, K, L, emit);
+}
+
 // Top-K of one row of N <= NT * KPT values (optionally after the EMA update e = alpha e + (1 - alpha) v, written
-// back), by one workgroup of NT threads (256 <= NT <= 1024); orow (and lds_out, an LDS copy, when given) receives K
-// ascending indices.
-template <int NT, int KPT, bool EMA>
-__device__ void topk_row(const float* __restrict__ v, float* __restrict__ e_row, float alpha, int first, int N, int K,
-                         int32_t* __restrict__ orow, int32_t* lds_out = nullptr) {
+// back), by one workgroup of NT threads (256 <= NT <= 1024): emit(pos, i, key) receives the K selected row
+// positions i in ascending order, with their keys.
+template <int NT, int KPT, bool EMA, typename EmitFn>
+__device__ void topk_row_emit(const float* __restrict__ v, float* __restrict__ e_row, float alpha, int first, int N,
+                              int K, EmitFn&& emit) {
   static_assert(NT >= 256 && NT <= 1024 && NT % 64 == 0, "workgroup size");
-  constexpr int NW = NT / 64;
   __shared__ TopkLds L;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i0 = tid * KPT;
+  const int i0 = threadIdx.x * KPT;
 
   // ---- load (and EMA update) --------------------------------------------------------------------------------
   float x[KPT];
-  if (KPT % 4 == 0 && (N & 3) == 0 && i0 + KPT <= N) {
+  if (KPT % 4 == 0 && ((uintptr_t)v & 15) == 0 && (!EMA || ((uintptr_t)e_row & 15) == 0) && i0 + KPT <= N) {
 #pragma unroll
     for (int k = 0; k < KPT; k += 4) {
       const float4 a = *reinterpret_cast<const float4*>(v + i0 + k);
@@ -208,27 +252,82 @@ __device__ void topk_row(const float* __restrict__ v, float* __restrict__ e_row,
     }
   }
 
-  // ---- keys and the row range ---------------------------------------------------------------------------------
-  float lmax = -__builtin_huge_valf(), lmin = __builtin_huge_valf();
   uint32_t key[KPT];
 #pragma unroll
-  for (int k = 0; k < KPT; ++k) {
-    const bool ok = i0 + k < N;
-    key[k] = ok ? f2key(x[k]) : 0u;
-    if (ok) { lmax = fmaxf(lmax, x[k]); lmin = fminf(lmin, x[k]); }
-  }
-  lmax = wave_max(lmax);
-  lmin = -wave_max(-lmin);
-  if (lane == 0) { L.red_f[0][wave] = lmax; L.red_f[1][wave] = lmin; }
-  __syncthreads();
-  float gmax = L.red_f[0][0], gmin = L.red_f[1][0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) { gmax = fmaxf(gmax, L.red_f[0][w]); gmin = fminf(gmin, L.red_f[1][w]); }
-  const uint32_t kmax = f2key(gmax), kmin = f2key(gmin);
-
+  for (int k = 0; k < KPT; ++k) key[k] = f2key(x[k]);
   auto valid = [&](int k) { return i0 + k < N; };
-  const Radix R = radix_select<NT, KPT>(key, valid, kmax, kmin, (uint32_t)K, L);
-  write_selected<NT, KPT>(key, valid, R, K, orow, lds_out, L, [&](int k) { return i0 + k; });
+  select_top<NT, KPT>(key, valid, K, L, [&](uint32_t pos, int j) { emit(pos, i0 + j, key[j]); });
+}
+
+// Top-K of one row into orow (and lds_out, an LDS copy, when given) as K ascending indices.
+template <int NT, int KPT, bool EMA>
+__device__ inline void topk_row(const float* __restrict__ v, float* __restrict__ e_row, float alpha, int first, int N,
+                                int K, int32_t* __restrict__ orow, int32_t* lds_out = nullptr) {
+  topk_row_emit<NT, KPT, EMA>(v, e_row, alpha, first, N, K, [&](uint32_t pos, int i, uint32_t) {
+    orow[pos] = i;
+    if (lds_out) lds_out[pos] = i;
+  });
+}
+
+// ---- long rows: segments, then a merge ---------------------------------------------------------------------------
+
+// Segment s (seg values from s * seg) of a row of N values: its top-min(K, length) as (key, index) candidates at
+// ckey_row / cidx_row + s * min(K, seg), ascending by index.
+template <int NT, int KPT, bool EMA>
+__device__ inline void topk_segment(const float* __restrict__ v_row, float* __restrict__ e_row, float alpha, int first,
+                                    int N, int K, int seg, int s, uint32_t* __restrict__ ckey_row,
+                                    int32_t* __restrict__ cidx_row) {
+  const int base = s * seg;
+  const int n = min(seg, N - base);
+  const int kc = min(K, seg);
+  uint32_t* ok = ckey_row + (int64_t)s * kc;
+  int32_t* oi = cidx_row + (int64_t)s * kc;
+  topk_row_emit<NT, KPT, EMA>(v_row + base, EMA ? e_row + base : nullptr, alpha, first, n, min(K, n),
+                              [&](uint32_t pos, int i, uint32_t key) {
+                                ok[pos] = key;
+                                oi[pos] = base + i;
+                              });
+}
+
+// Top-K of a row's C candidates (C <= NT * KPT) into orow (and lds_out) as K ascending block indices.
+template <int NT, int KPT>
+__device__ void topk_merge_row(const uint32_t* __restrict__ ckey_row, const int32_t* __restrict__ cidx_row, int C,
+                               int K, int32_t* __restrict__ orow, int32_t* lds_out = nullptr) {
+  __shared__ TopkLds L;
+  const int i0 = threadIdx.x * KPT;
+  uint32_t key[KPT];
+  if (KPT % 4 == 0 && ((uintptr_t)ckey_row & 15) == 0 && i0 + KPT <= C) {
+#pragma unroll
+    for (int k = 0; k < KPT; k += 4) {
+      const uint4 a = *reinterpret_cast<const uint4*>(ckey_row + i0 + k);
+      key[k] = a.x; key[k + 1] = a.y; key[k + 2] = a.z; key[k + 3] = a.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) key[k] = i0 + k < C ? ckey_row[i0 + k] : 0u;
+  }
+  auto valid = [&](int k) { return i0 + k < C; };
+  select_top<NT, KPT>(key, valid, K, L, [&](uint32_t pos, int j) {
+    const int32_t b = cidx_row[i0 + j];
+    orow[pos] = b;
+    if (lds_out) lds_out[pos] = b;
+  });
+}
+
+// Split of a row of N values into segments of seg for a top-K: S segments, kc candidate slots per segment, C
+// candidates in all (the last segment may hold fewer).
+struct TopkSplit {
+  int S, seg, kc, C;
+};
+
+__host__ __device__ inline TopkSplit topk_split(int N, int K, int seg) {
+  TopkSplit p;
+  p.seg = seg;
+  p.S = (N + seg - 1) / seg;
+  p.kc = K < seg ? K : seg;
+  const int last = N - (p.S - 1) * seg;
+  p.C = (p.S - 1) * p.kc + (p.kc < last ? p.kc : last);
+  return p;
 }
 
 // Values per thread of a 1024-thread workgroup for a row of N values (N <= 32768).

@@ -306,14 +306,6 @@ bool two_launch_supported(const prr_shape& s, int top_k, int k_spec, int k_spec_
          k_spec_next <= kSRMaxK && s.n_blocks <= 64 * kSRThreads;
 }
 
-static int spec_spw2(const prr_shape& s, int k_spec) {
-  const int cpb = (s.block_size + 15) / 16;
-  int spw = cpb >= 4 ? 1 : 4 / cpb;
-  const int64_t rows = (int64_t)s.batch * s.n_kv_heads;
-  while (spw > 1 && rows * ((k_spec + spw - 1) / spw) < 4096) spw >>= 1;
-  return spw;
-}
-
 template <int DT, int G>
 static void score_spec_launch(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema,
                               float alpha, int first, const void* kc, const void* vc, const int32_t* table,
@@ -321,7 +313,7 @@ static void score_spec_launch(const prr_shape& s, const void* q, const void* sum
   const int rows = s.batch * s.n_kv_heads;
   const int chunk = score_chunk_size(s);
   const int gx = (s.n_blocks + chunk - 1) / chunk;
-  const int spw = k_spec > 0 ? spec_spw2(s, k_spec) : 1;
+  const int spw = k_spec > 0 ? spec_slots_per_wave(s, k_spec) : 1;
   const int wpr = (k_spec + spw - 1) / spw;
   const int64_t spec_waves = (int64_t)rows * wpr;
   const int n_spec_wg = (int)((spec_waves + 3) / 4);

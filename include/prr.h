@@ -82,15 +82,19 @@ prr_status prr_build_summaries(const prr_shape* shape, const void* k_cache, cons
 /* Query-aware block scores and exact top-K selection (PRR abstract: attend only to the top-K blocks relevant to
  * each query). scores[b,g,n] = sum over the query heads h of KV head g and dims d of
  * max(q[b,h,d]*kmin[d], q[b,h,d]*kmax[d]) (fp32); sel_idx[b,g,:] = the top_k largest scores, ties to the lower
- * block index, ascending. Requires 1 <= top_k <= N. */
+ * block index, ascending. Requires 1 <= top_k <= N. `workspace` (prr_workspace_bytes bytes, no initialisation
+ * needed) or NULL: with it, rows of more than 8192 blocks select in two launches (the top-K of each segment of 4096
+ * scores, then the top-K of those candidates), much faster on long rows than one workgroup per row; the result is
+ * the same. The selection uses the workspace's true-set candidate region only. */
 prr_status prr_score_select(const prr_shape* shape, const void* q, const void* summaries, int32_t top_k,
-                            float* scores, int32_t* sel_idx, void* stream);
+                            float* scores, int32_t* sel_idx, void* workspace, void* stream);
 
 /* EMA score predictor (PRR abstract: "lightweight EMA-based predictor"): ema = scores when first_step != 0, else
  * ema = alpha * ema + (1 - alpha) * scores (in place); then pred_idx_next[b,g,:] = top-k_spec of ema, ties to the
- * lower index, ascending — the predicted set for the next decode step. Requires 1 <= k_spec <= N. */
+ * lower index, ascending — the predicted set for the next decode step. Requires 1 <= k_spec <= N. `workspace` as in
+ * prr_score_select (its predicted-set candidate region only, so the two selections may run at once). */
 prr_status prr_ema_predict(const prr_shape* shape, const float* scores, float* ema, float alpha, int32_t first_step,
-                           int32_t k_spec, int32_t* pred_idx_next, void* stream);
+                           int32_t k_spec, int32_t* pred_idx_next, void* workspace, void* stream);
 
 /* Speculative attention (PRR abstract: speculate the attention over the predicted blocks while selection is in
  * flight): for every (b, g) and predicted slot j < k_spec, with n = pred_idx[b,g,j] and each query head h of the
@@ -106,7 +110,8 @@ prr_status prr_speculate(const prr_shape* shape, const void* q, const void* k_ca
  * P = pred_idx[b,g,:k_spec] reuse their speculated partials; the missed blocks M = T \ P are computed here; blocks of
  * P \ T never enter. out[b,h] = O / l of the merged state; n_missed[b,g] = |M|. k_spec == 0 (or pred_idx NULL)
  * computes attention over all of T (the serialized select-then-attend path). `workspace` holds
- * prr_workspace_bytes() bytes of scratch (no initialisation needed); calls sharing one workspace must not overlap. */
+ * prr_workspace_bytes() bytes of scratch (no initialisation needed); it uses the workspace's repair region, so it
+ * may overlap a selection call on the same workspace, but not another repair. */
 prr_status prr_repair_merge(const prr_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_table, const int32_t* sel_idx, int32_t top_k,
                             const int32_t* pred_idx, int32_t k_spec, const float* partials, float* out,
@@ -122,11 +127,14 @@ prr_status prr_score(const prr_shape* shape, const void* q, const void* summarie
  * step's predicted set pred_idx_next = top-k_spec_next of `ema` (already updated by prr_score; ties to the lower
  * index, ascending); and the speculation of prr_speculate over pred_idx (k_spec slots) into `partials`.
  * Selection occupies one workgroup per row and is bound by latency, so speculation runs in its shadow (PRR
- * abstract: speculation overlaps selection). pred_idx and pred_idx_next must be different buffers. */
+ * abstract: speculation overlaps selection). pred_idx and pred_idx_next must be different buffers. `workspace`
+ * (prr_workspace_bytes bytes) or NULL: with it, rows of more than 8192 blocks (with top_k and k_spec_next <= 1024)
+ * select by segments of 2048 values in this launch and merge the candidates in a second one. */
 prr_status prr_select_speculate(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
                                 const float* ema, int32_t k_spec_next, int32_t* pred_idx_next, const void* q,
                                 const void* k_cache, const void* v_cache, const int32_t* block_table,
-                                const int32_t* pred_idx, int32_t k_spec, float* partials, void* stream);
+                                const int32_t* pred_idx, int32_t k_spec, float* partials, void* workspace,
+                                void* stream);
 
 /* Scores (+ the EMA update when ema != NULL, as prr_score) and the speculation of prr_speculate over pred_idx
  * (k_spec slots), in ONE launch whose workgroups of the two roles run concurrently (PRR abstract: speculation runs
@@ -143,8 +151,8 @@ prr_status prr_score_speculate(const prr_shape* shape, const void* q, const void
  * prr_score_speculate or prr_speculate) — blocks of P outside T never enter — and writes out = O / l and
  * n_missed = |T minus P| as prr_repair_merge does. When k_spec_next > 0 other workgroups of the first launch also
  * write pred_idx_next = top-k_spec_next of `ema` (already updated). k_spec == 0 attends over all of T
- * (select-then-attend). `workspace` holds prr_workspace_bytes(shape, top_k) bytes (no initialisation needed; calls
- * sharing one workspace must not overlap). Returns PRR_EUNSUPPORTED unless page_size is a multiple of 16,
+ * (select-then-attend). `workspace` holds prr_workspace_bytes(shape, top_k) bytes (no initialisation needed; it uses
+ * the repair region, as prr_repair_merge). Returns PRR_EUNSUPPORTED unless page_size is a multiple of 16,
  * block_size <= 128 and top_k, k_spec, k_spec_next <= 2048 (the separate calls cover the rest). pred_idx is searched
  * by bisection when ascending (as the top-K calls write it), linearly otherwise. */
 prr_status prr_select_repair(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
@@ -155,7 +163,8 @@ prr_status prr_select_repair(const prr_shape* shape, const float* scores, int32_
 
 /* Bytes of the partials buffer for a speculation budget k_spec (0 for k_spec == 0). */
 size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec);
-/* Bytes of the workspace of prr_repair_merge, prr_select_repair and prr_decode_step for top_k. */
+/* Bytes of the workspace of the selection calls, prr_repair_merge, prr_select_repair and prr_decode_step for top_k:
+ * two top-K candidate regions (true set, predicted set; empty unless N > 8192), then the repair region. */
 size_t prr_workspace_bytes(const prr_shape* shape, int32_t top_k);
 
 /* ---- one decode step on two streams (the runtime around the calls above) ------------------------------------ */

@@ -53,7 +53,7 @@ def test_shape_validation(bad, code):
     lib = L.lib()
     s = _shape(**bad)
     nz = ctypes.c_void_p(16)
-    st = lib.prr_score_select(ctypes.byref(s), nz, nz, 8, nz, nz, None)
+    st = lib.prr_score_select(ctypes.byref(s), nz, nz, 8, nz, nz, None, None)
     assert st == code, (bad, st, lib.prr_last_error())
     assert lib.prr_last_error()
 
@@ -62,17 +62,18 @@ def test_argument_validation_without_launch():
     lib = L.lib()
     s = _shape()
     nz = ctypes.c_void_p(16)
-    assert lib.prr_score_select(ctypes.byref(s), None, nz, 8, nz, nz, None) == -1          # null q
-    assert lib.prr_score_select(ctypes.byref(s), nz, nz, 0, nz, nz, None) == -1            # K < 1
-    assert lib.prr_score_select(ctypes.byref(s), nz, nz, 2049, nz, nz, None) == -1         # K > N
+    assert lib.prr_score_select(ctypes.byref(s), None, nz, 8, nz, nz, None, None) == -1          # null q
+    assert lib.prr_score_select(ctypes.byref(s), nz, nz, 0, nz, nz, None, None) == -1            # K < 1
+    assert lib.prr_score_select(ctypes.byref(s), nz, nz, 2049, nz, nz, None, None) == -1         # K > N
     assert lib.prr_score(ctypes.byref(s), nz, None, nz, None, 0.5, 0, None) == -1         # null summaries
     assert lib.prr_score(ctypes.byref(s), nz, nz, nz, nz, -0.5, 0, None) == -1            # alpha < 0 with an EMA
     # select_speculate: prediction needs the EMA; speculation needs its buffers; P_t and P_{t+1} buffers differ
     assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, None, 8, nz, None, None, None, None, None, 0, None,
-                                    None) == -1
+                                    None, None) == -1
     assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, None, 0, None, nz, None, nz, nz, nz, 4, nz,
+                                    None, None) == -1
+    assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, nz, 8, nz, nz, nz, nz, nz, nz, 8, nz, None,
                                     None) == -1
-    assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, nz, 8, nz, nz, nz, nz, nz, nz, 8, nz, None) == -1
     # select_repair: argument checks, then the supported-shape rule (page size multiple of 16, K <= 2048)
     assert lib.prr_select_repair(ctypes.byref(s), nz, 8, nz, None, 0, None, nz, nz, nz, nz, None, 4, None, nz, nz,
                                  nz, None) == -1                                              # k_spec > 0, no P
@@ -86,8 +87,8 @@ def test_argument_validation_without_launch():
                                  nz, nz, None) == -2                                          # K > 2048
     assert lib.prr_score_speculate(ctypes.byref(s), nz, nz, nz, None, 0.5, 0, None, None, None, None, 4, None,
                                    None) == -1                                                # k_spec > 0, no KV
-    assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 0.9, 0, 0, nz, None) == -1        # K' < 1
-    assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 1.5, 0, 8, nz, None) == -1        # alpha > 1
+    assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 0.9, 0, 0, nz, None, None) == -1        # K' < 1
+    assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 1.5, 0, 8, nz, None, None) == -1        # alpha > 1
     assert lib.prr_speculate(ctypes.byref(s), nz, nz, nz, nz, nz, -1, nz, None) == -1      # K' < 0
     assert lib.prr_speculate(ctypes.byref(s), None, None, None, None, None, 0, None, None) == 0   # K' = 0: no-op
     assert lib.prr_repair_merge(ctypes.byref(s), nz, nz, nz, nz, nz, 8, None, 4, None, nz, nz, nz, None) == -1

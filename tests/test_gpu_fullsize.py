@@ -18,17 +18,22 @@ pytestmark = [pytest.mark.gpu, requires_gpu]
 STEPS = 3
 
 
-@pytest.mark.parametrize("name", list(WORKLOADS))
-def test_full_size_sampled_rows(name):
+# every workload in the benchmark's mode; the million-token row (32768 blocks, selected by segments) in the other
+# modes' selection paths too
+CASES = [(n, "prr_fused") for n in WORKLOADS] + [("million_token", "serialized"), ("million_token", "prr_2stream")]
+
+
+@pytest.mark.parametrize("name,mode", CASES)
+def test_full_size_sampled_rows(name, mode):
     w = WORKLOADS[name]
     k_spec = max(w.k_spec)
     rng = np.random.default_rng(5)
     rows = sorted({(0, 0), (w.batch - 1, w.n_kv_heads - 1),
                    (int(rng.integers(w.batch)), int(rng.integers(w.n_kv_heads)))})
-    print(f"[case] full-size {name} K={w.top_k} K'={k_spec} rows {rows}", flush=True)
+    print(f"[case] full-size {name} {mode} K={w.top_k} K'={k_spec} rows {rows}", flush=True)
     inp = make_inputs(w, device="cuda", steps=STEPS)
     ov = OracleView(inp)
-    layer = PRRLayer(shape_of(w), w.top_k, k_spec, w.alpha, mode="prr_fused")
+    layer = PRRLayer(shape_of(w), w.top_k, k_spec, w.alpha, mode=mode)
     layer.build(inp.k_cache, inp.v_cache, inp.table)
     ema = {}
     G = w.group
@@ -41,7 +46,8 @@ def test_full_size_sampled_rows(name):
         out = layer.step(inp.q[t].contiguous())
         torch.cuda.synchronize()
         out_h, sel, nm = np64(out), layer.sel_idx.cpu().numpy(), layer.n_missed.cpu().numpy()
-        pred = layer.pred_current.cpu().numpy() if t > 0 else None
+        kp = layer.k_spec
+        pred = layer.pred_current.cpu().numpy() if t > 0 and kp > 0 else None
         for (b, g) in rows:
             qg = ov.q_group(t, b, g)
             keys = ov.keys(b, g)
@@ -52,8 +58,8 @@ def test_full_size_sampled_rows(name):
             e = max_abs(out_h[b, g * G:(g + 1) * G], ref)
             worst = max(worst, e)
             assert e <= TOL[w.dtype], (t, b, g, e)
-            if t > 0:
-                check_selection(pred[b, g], ema[(b, g)], k_spec)
+            if pred is not None:
+                check_selection(pred[b, g], ema[(b, g)], kp)
                 assert nm[b, g] == len(set(sel[b, g]) - set(pred[b, g])), (t, b, g)
             else:
                 assert nm[b, g] == w.top_k

@@ -308,6 +308,112 @@ def test_topk_large_rows(n_blocks):
                 assert np.array_equal(got[r], ref), (name, k, r)
 
 
+def _tie_cases(rng, rows, N):
+    stride = max(1, N // 1024)
+    cases = {
+        "normal": rng.standard_normal((rows, N)),
+        "constant": np.full((rows, N), 3.5),
+        "few_levels": rng.integers(0, 3, size=(rows, N)).astype(np.float64),
+        "rounded": np.round(rng.standard_normal((rows, N)) * 4),
+        "signed_zeros": np.where(rng.random((rows, N)) < 0.5, -0.0, 0.0),
+    }
+    hi = rng.standard_normal((rows, N))
+    hi[:, ::stride] = 100.0 + rng.random((rows, len(range(0, N, stride))))
+    cases["strided_high"] = hi
+    # the largest values all in the last (short) segment, then all in the first
+    tail = rng.standard_normal((rows, N))
+    tail[:, -min(N, 3000):] += 50.0
+    cases["tail_high"] = tail
+    cases["head_high"] = tail[:, ::-1].copy()
+    return cases
+
+
+def _ref_top_k(v32, k):
+    """The tie rule on the fp32 keys: larger value first, then lower index (-0.0 ranks below +0.0, as the device
+    keys order them)."""
+    key = v32.view(np.uint32).astype(np.int64)
+    key = np.where(key & 0x80000000, 0xFFFFFFFF - key, key | 0x80000000)
+    order = np.lexsort((np.arange(len(v32)), -key))
+    return np.sort(order[:k]).astype(np.int32)
+
+
+@pytest.mark.parametrize("n_blocks", [8193, 20001, 32768])
+def test_topk_split_rows(n_blocks):
+    """Long rows with a workspace: prr_ema_predict and prr_score_select's top-K run by segments of 4096 values and a
+    merge. The selection equals the tie rule on every case (ties, constant rows, signed zeros, the largest values in
+    the short last segment or in the first), for K up to the largest split size and beyond it (one workgroup per
+    row), and equals the call without a workspace; the EMA written is the same bits."""
+    s = L.make_shape(1, 16, 2, 128, 16, 16, n_blocks, L.BF16)
+    N, rows = n_blocks, 2
+    print(f"[case] split top-K N={N}", flush=True)
+    rng = np.random.default_rng(23)
+    ws = torch.zeros((L.workspace_bytes(s, 64) // 4 + 1,), dtype=torch.float32, device="cuda")
+    for name, vals in _tie_cases(rng, rows, N).items():
+        v32 = vals.astype(np.float32)
+        vd = torch.as_tensor(v32[None], device="cuda").contiguous()
+        for k in sorted({1, 64, 256, 1000, 2048, min(N, 3000)}):
+            out_a = torch.full((1, rows, k), -1, dtype=torch.int32, device="cuda")
+            out_b = torch.full((1, rows, k), -1, dtype=torch.int32, device="cuda")
+            em_a = torch.as_tensor(np.float32(0.25) * v32[None], device="cuda").contiguous()
+            em_b = em_a.clone()
+            L.ema_predict(s, vd, em_a, 0.5, False, k, out_a, workspace=ws)
+            L.ema_predict(s, vd, em_b, 0.5, False, k, out_b)
+            torch.cuda.synchronize()
+            assert torch.equal(em_a.view(torch.int32), em_b.view(torch.int32)), (name, k)
+            assert torch.equal(out_a, out_b), (name, k)
+            e32 = em_a.cpu().numpy()[0]
+            got = out_a.cpu().numpy()[0]
+            for r in range(rows):
+                assert np.array_equal(got[r], _ref_top_k(e32[r], k)), (name, k, r)
+            if name == "rounded":
+                # first step: ema = values, so the selection is the values' own top-K
+                L.ema_predict(s, vd, em_a, 0.5, True, k, out_a, workspace=ws)
+                torch.cuda.synchronize()
+                for r in range(rows):
+                    assert np.array_equal(out_a.cpu().numpy()[0][r], O.top_k(v32[r].astype(np.float64), k)), (k, r)
+
+
+@pytest.mark.parametrize("n_blocks", [20001, 32768])
+def test_select_speculate_split_rows(n_blocks):
+    """prr_select_speculate on long rows with a workspace (selection by segments of 2048 values inside the
+    speculation launch, then the merge launch) writes the same true set, predicted set and partial records, bit for
+    bit, as without it, and the sets follow the tie rule, for K and K' on both sides of the segments' candidate
+    count."""
+    s = L.make_shape(1, 8, 2, 128, 16, 16, n_blocks, L.BF16)
+    N, B, Hkv, bs = n_blocks, 1, 2, 16
+    print(f"[case] split select_speculate N={N}", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(31)
+    n_pages = N + 17
+    kc = torch.randn((n_pages, Hkv, bs, 128), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((n_pages, Hkv, bs, 128), generator=g, device="cuda").to(torch.bfloat16)
+    rng = np.random.default_rng(37)
+    table = torch.as_tensor(rng.permutation(n_pages)[:N].astype(np.int32)[None], device="cuda").contiguous()
+    q = torch.randn((B, 8, 128), generator=g, device="cuda").to(torch.bfloat16)
+    ws = torch.zeros((L.workspace_bytes(s, 64) // 4 + 1,), dtype=torch.float32, device="cuda")
+    for name, vals in list(_tie_cases(rng, B * Hkv, N).items())[:6]:
+        sc = torch.as_tensor(vals.astype(np.float32).reshape(B, Hkv, N), device="cuda").contiguous()
+        em = torch.as_tensor(np.round(rng.standard_normal((B, Hkv, N)) * 3).astype(np.float32), device="cuda")
+        for K, Kp, kspec in [(256, 384, 300), (1024, 64, 0), (7, 1024, 64)]:
+            cur = torch.as_tensor(np.stack([np.sort(rng.choice(N, max(kspec, 1), replace=False))
+                                            for _ in range(B * Hkv)]).reshape(B, Hkv, -1).astype(np.int32),
+                                  device="cuda")
+            res = []
+            for w_ in (ws, None):
+                sel = torch.full((B, Hkv, K), -1, dtype=torch.int32, device="cuda")
+                pn = torch.full((B, Hkv, Kp), -1, dtype=torch.int32, device="cuda")
+                pa = torch.zeros((max(L.partials_bytes(s, kspec), 4) // 4,), dtype=torch.float32, device="cuda")
+                L.select_speculate(s, sc, K, sel, em, Kp, pn, q, kc, vc, table, cur, kspec, pa, workspace=w_)
+                torch.cuda.synchronize()
+                res.append((sel, pn, pa))
+            (sel_a, pn_a, pa_a), (sel_b, pn_b, pa_b) = res
+            assert torch.equal(sel_a, sel_b) and torch.equal(pn_a, pn_b), (name, K, Kp)
+            assert torch.equal(pa_a.view(torch.int32), pa_b.view(torch.int32)), (name, K, Kp)
+            s32, e32 = sc.cpu().numpy().reshape(-1, N), em.cpu().numpy().reshape(-1, N)
+            for r in range(B * Hkv):
+                assert np.array_equal(sel_a.cpu().numpy().reshape(-1, K)[r], _ref_top_k(s32[r], K)), (name, K, r)
+                assert np.array_equal(pn_a.cpu().numpy().reshape(-1, Kp)[r], _ref_top_k(e32[r], Kp)), (name, Kp, r)
+
+
 @pytest.mark.parametrize("name", SMALL)
 def test_fused_launches_match_separate(name):
     """prr_score (with the EMA update) followed by prr_select_speculate produce, bit for bit, the scores, EMA, true
