@@ -90,11 +90,11 @@ struct AttnWaveM {
       const uint8_t* base_v = vc + ((phys * Hkv + g) * page + tc % page) * (int64_t)kRowBytes;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        c.ka[kk] = kok ? ld16(base_k + col * kRowBytes + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
+        c.ka[kk] = kok ? ld16_stream(base_k + col * kRowBytes + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tt = 4 * row + r;
-        c.vv[r] = t0 + tt < bs ? ld16(base_v + tt * kRowBytes + 16 * col) : make_uint4(0, 0, 0, 0);
+        c.vv[r] = t0 + tt < bs ? ld16_stream(base_v + tt * kRowBytes + 16 * col) : make_uint4(0, 0, 0, 0);
       }
     } else {
       const int64_t tk = tok0 + t0 + col;
@@ -102,14 +102,14 @@ struct AttnWaveM {
       const uint8_t* base_k = kc + ((pk * Hkv + g) * page + tk % page) * (int64_t)kRowBytes;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        c.ka[kk] = kok ? ld16(base_k + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
+        c.ka[kk] = kok ? ld16_stream(base_k + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tt = 4 * row + r;
         const int64_t tv = tok0 + t0 + tt;
         if (t0 + tt < bs) {
           const int64_t pv = trow[tv / page];
-          c.vv[r] = ld16(vc + ((pv * Hkv + g) * page + tv % page) * (int64_t)kRowBytes + 16 * col);
+          c.vv[r] = ld16_stream(vc + ((pv * Hkv + g) * page + tv % page) * (int64_t)kRowBytes + 16 * col);
         } else {
           c.vv[r] = make_uint4(0, 0, 0, 0);
         }
@@ -122,11 +122,11 @@ struct AttnWaveM {
                                 int nvalid) const {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      c.ka[kk] = col < nvalid ? ld16(base_k + col * kRowBytes + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
+      c.ka[kk] = col < nvalid ? ld16_stream(base_k + col * kRowBytes + 16 * row + 64 * kk) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int tt = 4 * row + r;
-      c.vv[r] = tt < nvalid ? ld16(base_v + tt * kRowBytes + 16 * col) : make_uint4(0, 0, 0, 0);
+      c.vv[r] = tt < nvalid ? ld16_stream(base_v + tt * kRowBytes + 16 * col) : make_uint4(0, 0, 0, 0);
     }
   }
 

@@ -75,8 +75,8 @@ struct AttnWave {
       if (t0 + 4 * j < bs) {
         const int64_t phys = trow[tok / page];
         const int64_t off = ((phys * Hkv + g) * page + tok % page) * (int64_t)kRowBytes + col * 16;
-        c.kv[j] = ld16(kc + off);
-        c.vv[j] = ld16(vc + off);
+        c.kv[j] = ld16_stream(kc + off);
+        c.vv[j] = ld16_stream(vc + off);
       } else {
         c.kv[j] = make_uint4(0, 0, 0, 0);
         c.vv[j] = make_uint4(0, 0, 0, 0);
@@ -90,8 +90,8 @@ struct AttnWave {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int off = (4 * j + row) * kRowBytes + col * 16;
-      c.kv[j] = 4 * j < nvalid ? ld16(base_k + off) : make_uint4(0, 0, 0, 0);
-      c.vv[j] = 4 * j < nvalid ? ld16(base_v + off) : make_uint4(0, 0, 0, 0);
+      c.kv[j] = 4 * j < nvalid ? ld16_stream(base_k + off) : make_uint4(0, 0, 0, 0);
+      c.vv[j] = 4 * j < nvalid ? ld16_stream(base_v + off) : make_uint4(0, 0, 0, 0);
     }
   }
 

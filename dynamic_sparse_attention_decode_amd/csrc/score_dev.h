@@ -47,7 +47,7 @@ __device__ inline void score_chunk(int bx, int bg, const uint8_t* __restrict__ q
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int n = n0 + 8 * u;
-      v[u] = n < c1 ? ld16(base + (int64_t)n * (2 * kRowBytes)) : make_uint4(0, 0, 0, 0);
+      v[u] = n < c1 ? ld16_stream(base + (int64_t)n * (2 * kRowBytes)) : make_uint4(0, 0, 0, 0);
       e_old[u] = (EMA && !first && owner && n < c1) ? erow[n] : 0.f;
     }
 #pragma unroll

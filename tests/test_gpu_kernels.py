@@ -15,7 +15,11 @@ pytestmark = [pytest.mark.gpu, requires_gpu]
 
 
 def _setup(name, seed_shift=0):
-    w = small(name)
+    if name == "paged_wide":   # a wide batch of short rows
+        w = small("paged_b32_64k")
+        w = w.replace(batch=17, ctx=w.block_size * 70, top_k=12, k_spec=(12,), steps=4)
+    else:
+        w = small(name)
     if seed_shift:
         w = w.replace(seed=w.seed + seed_shift)
     print(f"[case] {name} B={w.batch} N={w.n_blocks} K={w.top_k} K'={w.k_spec}", flush=True)
@@ -171,10 +175,11 @@ def _forced_sets(rng, T, N, Kp_list):
     return sets
 
 
-@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("name", SMALL + ["paged_wide"])
 def test_repair_merge_forced_predictions(name):
-    """Whatever the predicted set (empty, equal, random, disjoint, superset, partial), the repaired output equals
-    attention over the true set and the missed count is |T \\ P| (PRR summary page, Key findings)."""
+    """Whatever the predicted set (empty, equal, random, disjoint, superset, partial, unsorted), the repaired output
+    equals attention over the true set and the missed count is |T \\ P| (PRR summary page, Key findings); also on a
+    wide batch of 17 sequences (136 rows) with short rows."""
     w, inp, s, summ, ov = _setup(name)
     B, Hkv, N, K, G = w.batch, w.n_kv_heads, w.n_blocks, w.top_k, w.group
     t = 2
