@@ -3,9 +3,9 @@ achieved HBM bandwidth of the dominant kernel against the 8 TB/s peak.
 
 A "step" is one decode step of one attention layer: score_select, speculate over the predicted blocks, repair and
 merge, and the EMA prediction for the next step (the whole hot path), on synthetic inputs resident in HBM. So that
-consecutive steps do not run out of the 256 MB Infinity Cache, the timed loop rotates over L copies of the layer's
-KV cache (distinct memory, like the layers of a model), with L (at most 8) chosen so the working set exceeds
-512 MiB where 8 copies suffice; the reported time is per (step, layer).
+consecutive steps do not run out of the 256 MB Infinity Cache, the timed loop rotates over L layers (copies of the
+KV cache, distinct memory, like the layers of a model), with L chosen so that the bytes one step touches times L
+exceed 512 MiB (at most 32 layers and 48 GiB); the reported time is per (step, layer).
 
 Prints ONE JSON line. `python bench.py --gpus N` with N > 1 exits: the benchmark runs on one GPU only.
 """
@@ -445,15 +445,22 @@ def budget_profile(w):
 
 
 def source_digest() -> str:
-    """sha256 over the HIP sources and the C header: a recorded counter value is valid only for the same kernels."""
+    """sha256 over the HIP sources and the C header with comments and whitespace removed: a recorded counter value
+    is valid only for the same kernels."""
     import hashlib
+    import re
+
+    def code(path):
+        src = open(path).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        return " ".join(src.split()).encode()
+
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "dynamic_sparse_attention_decode_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
-    with open(os.path.join(ROOT, "include", "prr.h"), "rb") as f:
-        h.update(f.read())
+        h.update(name.encode() + b"\0" + code(os.path.join(csrc, name)))
+    h.update(code(os.path.join(ROOT, "include", "prr.h")))
     return h.hexdigest()[:16]
 
 

@@ -1,5 +1,5 @@
 // score_dev.h — Quest block scoring as a streaming GEMV (PRR reference list, Quest), optionally fused with the EMA
-// predictor's update (PRR abstract: "lightweight EMA-based predictor").
+// predictor's update (PRR abstract: a light predictor built on an exponential moving average).
 //
 // s[b,g,n] = sum_d Qpos_d * kmax[n,d] + Qneg_d * kmin[n,d] with Qpos_d = sum_h max(q_hd, 0) and
 // Qneg_d = sum_h min(q_hd, 0) over the group's query heads. Because kmin <= kmax, max(q*kmin, q*kmax) equals

@@ -1,6 +1,6 @@
 // Query-aware block scoring and exact top-K selection (PRR abstract: attend only to the top-K KV blocks of each
 // query; PRR reference list, Quest: block scores from per-block key min/max), and the EMA predictor's update and
-// top-K' (PRR abstract: "lightweight EMA-based predictor").
+// top-K' (PRR abstract: a light predictor built on an exponential moving average).
 //
 // score_kernel: Quest's group-summed block score as a streaming GEMV over all CUs (score_dev.h); optionally updates
 //   the EMA in the same pass.

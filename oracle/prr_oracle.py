@@ -182,7 +182,7 @@ def prr_output(q_group, keys, values, true_set, pred_set, block_size: int, scale
 
 
 # ------------------------------------------------------------------------------------------------------------------
-# EMA score predictor (PRR abstract: "lightweight EMA-based predictor"; summary page: forecasts the top-K blocks)
+# EMA score predictor (PRR abstract: a light predictor built on an exponential moving average; summary page: it forecasts the top-K blocks)
 # ------------------------------------------------------------------------------------------------------------------
 
 
