@@ -134,12 +134,19 @@ def test_ema_state_save_restore():
     fresh.close()
 
 
-@pytest.mark.parametrize("mode", ["prr_2stream", "prr_fused"])
-def test_graph_replay_matches_eager(mode):
+@pytest.mark.parametrize("rows,mode", [("short", "prr_2stream"), ("short", "prr_fused"), ("long", "prr_fused"),
+                                       ("long", "serialized"), ("long", "prr_2stream")])
+def test_graph_replay_matches_eager(rows, mode):
     """Steps captured in a HIP graph and replayed several times (with eager work and synchronisation between the
-    replays) give the same outputs, selections and missed counts as the same steps run eagerly."""
-    w = small("llama3_8b_32k")
-    kp = w.k_spec[0]
+    replays) give the same outputs, selections and missed counts as the same steps run eagerly; also with rows of
+    12000 blocks, which select by segments through the workspace's candidate regions."""
+    if rows == "short":
+        w = small("llama3_8b_32k")
+        kp = w.k_spec[0]
+    else:
+        w = small("million_token").replace(ctx=32 * 12000, top_k=61, k_spec=(93,), steps=6)
+        kp = 93
+    print(f"[case] graph replay {rows} rows N={w.n_blocks} {mode}", flush=True)
     inp = make_inputs(w, device="cuda")
     qs = [inp.q[t].contiguous() for t in range(w.steps)]
     seq = [0] + [1, 2, 3, 4] * 3
