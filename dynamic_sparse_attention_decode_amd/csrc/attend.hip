@@ -187,9 +187,9 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8
 }
 
 // Merge each row's records into the normalised output: one workgroup per (row, head); the head-0 workgroup also sums
-// the missed count. A kernel boundary separates it from repair_kernel: cross-workgroup visibility through
-// device-scope fences (an L2 write-back and invalidate per workgroup on this multi-XCD part) cost far more than one
-// extra launch.
+// the missed count. A kernel boundary separates it from repair_kernel: publishing each workgroup's record with an
+// agent-scope release fence (an L2 write-back on this multi-XCD part; the fences serialise) costs about 5.5 us over
+// 256 workgroups, against 1.6-2.1 us for a launch in a graph.
 template <int G, int D>
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ ws_rec,
                                                        const int32_t* __restrict__ ws_miss, int n_rec,
