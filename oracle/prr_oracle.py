@@ -53,10 +53,21 @@ def logical_tokens(cache: np.ndarray, table: np.ndarray, b: int, g: int, n_token
 
 
 def block_summaries(keys: np.ndarray, block_size: int):
-    """Elementwise min and max of the keys of each block: kmin, kmax [N, D] (exact: comparisons only)."""
+    """Elementwise min and max of the keys of each block: kmin, kmax [N, D] (exact: comparisons only). Block n holds
+    tokens [n * block_size, (n + 1) * block_size) of the sequence; when the sequence ends inside a block (decode
+    appends one token at a time), the last block's summary covers the tokens it holds."""
     n_tok, d = keys.shape
-    kb = keys.reshape(n_tok // block_size, block_size, d)
-    return kb.min(axis=1), kb.max(axis=1)
+    if n_tok % block_size == 0:   # whole blocks: the same min and max, vectorised
+        kb = keys.reshape(n_tok // block_size, block_size, d)
+        return kb.min(axis=1), kb.max(axis=1)
+    n_blk = -(-n_tok // block_size)
+    kmin = np.empty((n_blk, d), dtype=keys.dtype)
+    kmax = np.empty((n_blk, d), dtype=keys.dtype)
+    for n in range(n_blk):
+        blk = keys[n * block_size:(n + 1) * block_size]
+        kmin[n] = blk.min(axis=0)
+        kmax[n] = blk.max(axis=0)
+    return kmin, kmax
 
 
 def quest_scores(q_group: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> np.ndarray:
@@ -104,15 +115,16 @@ def boundary_gap(values: np.ndarray, k: int):
 # ------------------------------------------------------------------------------------------------------------------
 
 
-def block_tokens(blocks, block_size: int) -> np.ndarray:
-    return np.concatenate([np.arange(n * block_size, (n + 1) * block_size) for n in blocks]) if len(blocks) else \
-        np.zeros((0,), dtype=np.int64)
+def block_tokens(blocks, block_size: int, n_tokens: int) -> np.ndarray:
+    """Token indices of ``blocks`` in a sequence of n_tokens tokens (a last, partly filled block holds fewer)."""
+    parts = [np.arange(n * block_size, min((n + 1) * block_size, n_tokens)) for n in blocks]
+    return np.concatenate(parts) if parts else np.zeros((0,), dtype=np.int64)
 
 
 def attention_over_blocks(q_group, keys, values, blocks, block_size: int, scale: float) -> np.ndarray:
-    """o[h] = softmax(scale * q_h . k_i) weighted sum of v_i over the tokens of ``blocks``; two-pass softmax
-    (max first, then the sum), float64. Returns [G, D]."""
-    idx = block_tokens(blocks, block_size)
+    """o[h] = softmax(scale * q_h . k_i) weighted sum of v_i over the tokens of ``blocks`` (keys and values hold the
+    sequence's tokens); two-pass softmax (max first, then the sum), float64. Returns [G, D]."""
+    idx = block_tokens(blocks, block_size, len(keys))
     k = keys[idx]
     v = values[idx]
     out = np.empty((q_group.shape[0], keys.shape[1]), dtype=np.float64)
@@ -179,6 +191,18 @@ def prr_output(q_group, keys, values, true_set, pred_set, block_size: int, scale
         out[h] = finalize(state)
     wasted = sorted(P - set(T))
     return out, np.asarray(missed, dtype=np.int64), np.asarray(wasted, dtype=np.int64)
+
+
+# ------------------------------------------------------------------------------------------------------------------
+# decode-time append: the sequence gains one token per step (its key and value); the summaries and every later
+# quantity are the definitions above applied to the longer sequence
+# ------------------------------------------------------------------------------------------------------------------
+
+
+def append_token(keys: np.ndarray, values: np.ndarray, k_new, v_new):
+    """The sequence's keys and values after one decode step appends (k_new, v_new): [n + 1, D] each."""
+    return (np.concatenate([keys, np.asarray(k_new, dtype=np.float64)[None]]),
+            np.concatenate([values, np.asarray(v_new, dtype=np.float64)[None]]))
 
 
 # ------------------------------------------------------------------------------------------------------------------

@@ -255,6 +255,54 @@ def pin_paged_gather(o):
             assert np.array_equal(got, ref)
 
 
+def pin_partial_last_block(o):
+    """A sequence that ends inside a block (decode appends one token at a time): with every block selected the output
+    is dense attention over the tokens that exist (torch SDPA, fp64), through the speculate-reuse-repair pipeline
+    too; a one-token last block's summary is that token's key; the Quest score of the partial block bounds the exact
+    largest q.k over its tokens; appending tokens one by one gives, at every length, the summaries of that prefix
+    and dense attention over it."""
+    rng = np.random.default_rng(19)
+    for (n_tok, bs, d, g) in [(13, 4, 6, 2), (17, 8, 5, 1), (33, 32, 16, 4), (9, 3, 4, 3)]:
+        q = rng.standard_normal((g, d))
+        k = rng.standard_normal((n_tok, d))
+        v = rng.standard_normal((n_tok, d))
+        scale = 1.0 / math.sqrt(d)
+        nb = -(-n_tok // bs)
+        kmin, kmax = o.block_summaries(k, bs)
+        assert kmin.shape == (nb, d) and kmax.shape == (nb, d)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, :, None, :], torch.from_numpy(k)[None, None].expand(1, g, -1, -1),
+            torch.from_numpy(v)[None, None].expand(1, g, -1, -1), scale=scale)[0, :, 0, :].numpy()
+        got = o.attention_over_blocks(q, k, v, np.arange(nb), bs, scale)
+        assert np.allclose(got, ref, rtol=0, atol=1e-13), np.abs(got - ref).max()
+        got2, missed, _ = o.prr_output(q, k, v, np.arange(nb), [nb - 1, 0], bs, scale)
+        assert np.allclose(got2, ref, rtol=0, atol=1e-13) and nb - 1 not in set(missed)
+        s = o.quest_scores(q[:1], kmin, kmax)
+        last = k[(nb - 1) * bs:]
+        assert s[nb - 1] >= (last @ q[0]).max() - 1e-12
+    # one-token last block
+    k = rng.standard_normal((9, 4))
+    kmin, kmax = o.block_summaries(k, 4)
+    assert np.array_equal(kmin[2], k[8]) and np.array_equal(kmax[2], k[8])
+    # appending one token at a time
+    bs, d, g = 4, 5, 2
+    q = rng.standard_normal((g, d))
+    k = rng.standard_normal((6, d))
+    v = rng.standard_normal((6, d))
+    for step in range(9):
+        k_new, v_new = rng.standard_normal(d), rng.standard_normal(d)
+        k, v = o.append_token(k, v, k_new, v_new)
+        assert len(k) == 7 + step and np.array_equal(k[-1], k_new) and np.array_equal(v[-1], v_new)
+        kmin, kmax = o.block_summaries(k, bs)
+        n_last = (len(k) - 1) // bs
+        assert np.array_equal(kmax[n_last], np.max(k[n_last * bs:], axis=0))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None, :, None, :], torch.from_numpy(k)[None, None].expand(1, g, -1, -1),
+            torch.from_numpy(v)[None, None].expand(1, g, -1, -1), scale=0.5)[0, :, 0, :].numpy()
+        got = o.attention_over_blocks(q, k, v, np.arange(n_last + 1), bs, 0.5)
+        assert np.allclose(got, ref, rtol=0, atol=1e-13)
+
+
 ALL_PINS = [pin_dense_equivalence, pin_brute_force_selection, pin_quest_upper_bound, pin_signsplit,
             pin_merge_order_free, pin_repair_invariants, pin_closed_forms, pin_hand_example, pin_ema_closed_form,
-            pin_budget_closed_form, pin_paged_gather]
+            pin_budget_closed_form, pin_paged_gather, pin_partial_last_block]

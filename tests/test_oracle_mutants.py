@@ -35,6 +35,23 @@ def _summaries_swapped(keys, bs):
     return kb.max(axis=1), kb.min(axis=1)
 
 
+def _summaries_last_window(keys, bs):
+    """Partial last block summarised over the last bs tokens of the sequence (reaching into the previous block)."""
+    n_tok = len(keys)
+    kmin, kmax = _orig["block_summaries"](keys, bs)
+    if n_tok % bs:
+        tail = keys[max(0, n_tok - bs):]
+        kmin[-1], kmax[-1] = tail.min(axis=0), tail.max(axis=0)
+    return kmin, kmax
+
+
+def _attn_whole_last_block(q_group, keys, values, blocks, block_size, scale):
+    """Attention that drops the tokens of a partial last block (only whole blocks attended)."""
+    n_whole = len(keys) // block_size
+    blocks = [n for n in blocks if n < n_whole] or list(blocks)
+    return _orig["attention_over_blocks"](q_group, keys, values, blocks, block_size, scale)
+
+
 def _topk_high_ties(values, k):
     n = len(values)
     order = np.lexsort((-np.arange(n), -np.asarray(values, dtype=np.float64)))
@@ -136,7 +153,8 @@ def _gather_identity(cache, table, b, g, n_tokens):
     return np.asarray(cache[b * table.shape[1] + i // page, g, i % page], dtype=np.float64)
 
 
-_orig = {k: getattr(O, k) for k in ["attention_over_blocks", "prr_output", "ema_update", "choose_budget"]}
+_orig = {k: getattr(O, k) for k in ["attention_over_blocks", "prr_output", "ema_update", "choose_budget",
+                                    "block_summaries"]}
 
 MUTANTS = {
     "quest_drop_kmin": ("quest_scores", _quest_drop_kmin),
@@ -144,6 +162,8 @@ MUTANTS = {
     "quest_first_head_only": ("quest_scores", _quest_first_head_only),
     "signsplit_swapped": ("quest_scores_signsplit", _signsplit_swapped),
     "summaries_swapped": ("block_summaries", _summaries_swapped),
+    "summaries_last_window": ("block_summaries", _summaries_last_window),
+    "attn_drops_partial_block": ("attention_over_blocks", _attn_whole_last_block),
     "topk_high_ties": ("top_k", _topk_high_ties),
     "topk_off_by_one": ("top_k", _topk_off_by_one),
     "topk_unsorted": ("top_k", _topk_unsorted),
