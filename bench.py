@@ -91,7 +91,8 @@ def main():
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
     inp = make_inputs(w, device=dev)
     shape = L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, w.n_blocks,
-                         {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[w.dtype], w.scale)
+                         {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[w.dtype], w.scale,
+                         ctx_len=w.ctx if w.ctx % w.block_size else 0)
     e = w.elem_bytes
     kv_layer = 2 * w.n_pages * w.n_kv_heads * w.page_size * w.head_dim * e
     summ_layer = w.batch * w.n_kv_heads * w.n_blocks * 2 * w.head_dim * e
@@ -338,6 +339,28 @@ def main():
         torch.cuda.synchronize()
         detail["summary_rebuild_us"] = {"blocks": int(ids.numel()), "us": e0.elapsed_time(e1) * 1e3 / 20}
         lay.close()
+    # decode-time append (the step before selection in a decoder; not part of the timed step): one new token per
+    # (sequence, KV head) written at the last slot of the sequences and its block's summary updated, as a graph of
+    # 200 launches timed with HIP events on the stream the graph runs on (last, since it rewrites that slot)
+    lay = make_layers(a.mode, n_kv=1)[0]
+    gk = torch.Generator(device=dev).manual_seed(w.seed + 7)
+    kn = torch.randn((w.batch, w.n_kv_heads, w.head_dim), generator=gk, device=dev).to(w.torch_dtype)
+    vn = torch.randn((w.batch, w.n_kv_heads, w.head_dim), generator=gk, device=dev).to(w.torch_dtype)
+    s_app = L.Shape.from_buffer_copy(shape)
+    s_app.ctx_len = w.n_blocks * w.block_size
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=streams[0]):
+        for _ in range(200):
+            L.append_kv(s_app, kn, vn, lay.k_cache, lay.v_cache, lay.table, lay.summaries, stream=streams[0])
+    gr.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    detail["append_us"] = e0.elapsed_time(e1) * 1e3 / 200
+    lay.close()
     print(f"[bench] {json.dumps(detail)}", file=sys.stderr, flush=True)
 
     cpu = None if a.no_cpu else cpu_baseline(w, inp, kspec, a.cpu_seconds)

@@ -18,7 +18,7 @@ MODE_SERIALIZED, MODE_ONE_STREAM, MODE_TWO_STREAM, MODE_FUSED, MODE_SERIALIZED_F
 _DT_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 # every entry point of include/prr.h
-EXPORTS = ["prr_build_summaries", "prr_score_select", "prr_ema_predict", "prr_speculate", "prr_repair_merge",
+EXPORTS = ["prr_build_summaries", "prr_append_kv", "prr_score_select", "prr_ema_predict", "prr_speculate", "prr_repair_merge",
            "prr_score", "prr_select_speculate", "prr_score_speculate", "prr_select_repair",
            "prr_partials_bytes", "prr_workspace_bytes", "prr_step_ctx_create", "prr_step_ctx_destroy",
            "prr_decode_step", "prr_choose_budget", "prr_trace_create", "prr_trace_destroy", "prr_trace_enable",
@@ -36,7 +36,7 @@ class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("n_blocks", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("ctx_len", ctypes.c_int32)]
 
     @property
     def group(self) -> int:
@@ -58,12 +58,13 @@ class StepArgs(ctypes.Structure):
 
 
 def make_shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, page_size, n_blocks, dtype,
-               softmax_scale=None) -> Shape:
+               softmax_scale=None, ctx_len=0) -> Shape:
+    """ctx_len: tokens per sequence when the last block is partly filled (0: n_blocks * block_size)."""
     if isinstance(dtype, torch.dtype):
         dtype = _DT_CODE[dtype]
     pps = n_blocks * block_size // page_size
     scale = head_dim ** -0.5 if softmax_scale is None else softmax_scale
-    return Shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, page_size, n_blocks, pps, dtype, scale)
+    return Shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, page_size, n_blocks, pps, dtype, scale, ctx_len)
 
 
 _lib = None
@@ -81,6 +82,7 @@ def lib():
     sp = ctypes.POINTER(Shape)
     sig = {
         "prr_build_summaries": (i32, [sp, vp, vp, vp, i32, vp, vp]),
+        "prr_append_kv": (i32, [sp, vp, vp, vp, vp, vp, vp, vp]),
         "prr_score_select": (i32, [sp, vp, vp, i32, vp, vp, vp, vp]),
         "prr_ema_predict": (i32, [sp, vp, vp, f32, i32, i32, vp, vp, vp]),
         "prr_speculate": (i32, [sp, vp, vp, vp, vp, vp, i32, vp, vp]),
@@ -146,6 +148,15 @@ def build_summaries(shape: Shape, k_cache, block_table, summaries, block_ids=Non
                                      _p(block_table, torch.int32, "block_table"),
                                      _p(block_ids, torch.int32, "block_ids"), n_ids, _p(summaries, dt, "summaries"),
                                      _s(stream)), "build_summaries")
+
+
+def append_kv(shape: Shape, k_new, v_new, k_cache, v_cache, block_table, summaries, stream=None) -> None:
+    """Write the token at position shape.ctx_len - 1 (k_new, v_new: [B, Hkv, D]) and update its block's summary."""
+    dt = shape.torch_dtype
+    _check(lib().prr_append_kv(ctypes.byref(shape), _p(k_new, dt, "k_new"), _p(v_new, dt, "v_new"),
+                               _p(k_cache, dt, "k_cache"), _p(v_cache, dt, "v_cache"),
+                               _p(block_table, torch.int32, "block_table"), _p(summaries, dt, "summaries"),
+                               _s(stream)), "append_kv")
 
 
 def score_select(shape: Shape, q, summaries, top_k: int, scores, sel_idx, workspace=None, stream=None) -> None:

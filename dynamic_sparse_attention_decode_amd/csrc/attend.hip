@@ -22,14 +22,14 @@ __global__ __launch_bounds__(256, 3) void speculate_kernel(const uint8_t* __rest
                                                         const int32_t* __restrict__ pred, int k_spec,
                                                         float* __restrict__ partials, int Hq, int Hkv, int N, int bs,
                                                         int page, int pps, float qscale, int spw, int wpr,
-                                                        int64_t total_waves) {
+                                                        int64_t total_waves, int last_len) {
   const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (w >= total_waves) return;
   const int64_t rowid = w / wpr;
   const int j0 = (int)(w - rowid * wpr) * spw;
   const int j1 = min(k_spec, j0 + spw);
   speculate_slots<DT, G, P16>(rowid, j0, j1, threadIdx.x & 63, q, kc, vc, table, pred, k_spec, partials, Hq, Hkv, N, bs,
-                         page, pps, qscale);
+                              page, pps, qscale, last_len);
 }
 
 constexpr int kMaxRecords = 256;   // records per row (bounded through entries per wave)
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8
                                                      const int32_t* __restrict__ pred, int k_spec,
                                                      const float* __restrict__ partials, float* __restrict__ ws_rec,
                                                      int32_t* __restrict__ ws_miss, int Hq, int Hkv, int N, int bs,
-                                                     int page, int pps, float qscale, int epw) {
+                                                     int page, int pps, float qscale, int epw, int last_len) {
   using W = Tile<DT, G>;
   constexpr int D = W::D;
   constexpr int RF = rec_floats(G, D);
@@ -152,7 +152,8 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8
     }
     misses += nm;
     // compute the missed blocks with the next chunk's loads in flight
-    run_blocks<P16>(st, nm, [&](int i) { return s_mid[wave][i]; }, [](int) {}, kc, vc, trow, bs, page, Hkv, g);
+    run_blocks<P16>(st, nm, [&](int i) { return s_mid[wave][i]; }, [](int) {}, kc, vc, trow, bs, page, Hkv, g, N,
+                    last_len);
   }
   float folded[W::NK];
   st.fold(folded);
@@ -275,7 +276,7 @@ static void spec_launch(const prr_shape& s, const void* q, const void* kc, const
   kern<<<dim3((unsigned)((total + 3) / 4)), dim3(256), 0, st>>>(
       static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, pred,
       k_spec, partials, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size, s.pages_per_seq, qscale,
-      spw, wpr, total);
+      spw, wpr, total, last_block_len(s));
   trace_end(PRR_KERNEL_SPECULATE, st);
 }
 
@@ -294,7 +295,7 @@ static void repair_launch(const prr_shape& s, const void* q, const void* kc, con
   kern<<<dim3((unsigned)nrec, (unsigned)rows), dim3(256), 0, st>>>(
       static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, sel,
       top_k, pred, k_spec, partials, ws.rec, ws.miss, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size,
-      s.page_size, s.pages_per_seq, qscale, epw);
+      s.page_size, s.pages_per_seq, qscale, epw, last_block_len(s));
   trace_end(PRR_KERNEL_REPAIR, st);
   constexpr int D = 16 * Vec<DT>::n;
   trace_begin(PRR_KERNEL_FINALIZE, st);

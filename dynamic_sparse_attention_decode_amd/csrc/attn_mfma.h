@@ -78,11 +78,12 @@ struct AttnWaveM {
     uint4 ka[4], vv[4];
   };
 
+  // len: tokens the block holds (bs, or fewer in a sequence's last block).
   __device__ void load_chunk(Chunk& c, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
-                             const int32_t* __restrict__ trow, int n, int t0, int bs, int page, int Hkv,
+                             const int32_t* __restrict__ trow, int n, int t0, int bs, int len, int page, int Hkv,
                              int g) const {
     const int64_t tok0 = (int64_t)n * bs;
-    const bool kok = t0 + col < bs;
+    const bool kok = t0 + col < len;
     if ((page & 15) == 0) {   // the 16 tokens share one page
       const int64_t tc = tok0 + t0;
       const int64_t phys = trow[tc / page];
@@ -94,7 +95,7 @@ struct AttnWaveM {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tt = 4 * row + r;
-        c.vv[r] = t0 + tt < bs ? ld16_stream(base_v + tt * kRowBytes + 16 * col) : make_uint4(0, 0, 0, 0);
+        c.vv[r] = t0 + tt < len ? ld16_stream(base_v + tt * kRowBytes + 16 * col) : make_uint4(0, 0, 0, 0);
       }
     } else {
       const int64_t tk = tok0 + t0 + col;
@@ -107,7 +108,7 @@ struct AttnWaveM {
       for (int r = 0; r < 4; ++r) {
         const int tt = 4 * row + r;
         const int64_t tv = tok0 + t0 + tt;
-        if (t0 + tt < bs) {
+        if (t0 + tt < len) {
           const int64_t pv = trow[tv / page];
           c.vv[r] = ld16_stream(vc + ((pv * Hkv + g) * page + tv % page) * (int64_t)kRowBytes + 16 * col);
         } else {
@@ -130,15 +131,15 @@ struct AttnWaveM {
     }
   }
 
-  // Fold one loaded chunk (tokens t0 .. t0 + 15 of a block of bs tokens) into the running state.
-  __device__ void compute_chunk(const Chunk& c, int t0, int bs) {
+  // Fold one loaded chunk (tokens t0 .. t0 + 15 of a block holding len tokens) into the running state.
+  __device__ void compute_chunk(const Chunk& c, int t0, int len) {
     // ---- logits on the matrix cores --------------------------------------------------------------------------
     floatx4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) s = mfma16x16x32<DT>(c.ka[kk], qb[kk], s);
     float z[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) z[r] = t0 + 4 * row + r < bs ? s[r] * qscale : -__builtin_huge_valf();
+    for (int r = 0; r < 4; ++r) z[r] = t0 + 4 * row + r < len ? s[r] * qscale : -__builtin_huge_valf();
     // ---- online softmax for head col --------------------------------------------------------------------------
     float mc = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
     mc = max_xor32(max_xor16(mc));
@@ -159,13 +160,13 @@ struct AttnWaveM {
     }
   }
 
-  // Fold one block of bs tokens into the running state.
+  // Fold block n (bs tokens apart, holding len of them) into the running state.
   __device__ void block(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
-                        const int32_t* __restrict__ trow, int n, int bs, int page, int Hkv, int g) {
-    for (int t0 = 0; t0 < bs; t0 += 16) {
+                        const int32_t* __restrict__ trow, int n, int bs, int len, int page, int Hkv, int g) {
+    for (int t0 = 0; t0 < len; t0 += 16) {
       Chunk c;
-      load_chunk(c, kc, vc, trow, n, t0, bs, page, Hkv, g);
-      compute_chunk(c, t0, bs);
+      load_chunk(c, kc, vc, trow, n, t0, bs, len, page, Hkv, g);
+      compute_chunk(c, t0, len);
     }
   }
 

@@ -65,14 +65,15 @@ struct AttnWave {
     uint4 kv[4], vv[4];
   };
 
+  // len: tokens the block holds (bs, or fewer in a sequence's last block).
   __device__ void load_chunk(Chunk& c, const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
-                             const int32_t* __restrict__ trow, int n, int t0, int bs, int page, int Hkv,
+                             const int32_t* __restrict__ trow, int n, int t0, int bs, int len, int page, int Hkv,
                              int g) const {
     const int64_t tok0 = (int64_t)n * bs;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t tok = tok0 + t0 + 4 * j + row;
-      if (t0 + 4 * j < bs) {
+      if (t0 + 4 * j + row < len) {
         const int64_t phys = trow[tok / page];
         const int64_t off = ((phys * Hkv + g) * page + tok % page) * (int64_t)kRowBytes + col * 16;
         c.kv[j] = ld16_stream(kc + off);
@@ -90,17 +91,17 @@ struct AttnWave {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int off = (4 * j + row) * kRowBytes + col * 16;
-      c.kv[j] = 4 * j < nvalid ? ld16_stream(base_k + off) : make_uint4(0, 0, 0, 0);
-      c.vv[j] = 4 * j < nvalid ? ld16_stream(base_v + off) : make_uint4(0, 0, 0, 0);
+      c.kv[j] = 4 * j + row < nvalid ? ld16_stream(base_k + off) : make_uint4(0, 0, 0, 0);
+      c.vv[j] = 4 * j + row < nvalid ? ld16_stream(base_v + off) : make_uint4(0, 0, 0, 0);
     }
   }
 
-  // Fold one loaded chunk (tokens t0 .. t0 + 15 of a block of bs tokens, bs % 4 == 0) into the running state.
-  __device__ void compute_chunk(const Chunk& c, int t0, int bs) {
+  // Fold one loaded chunk (tokens t0 .. t0 + 15 of a block holding len tokens) into the running state.
+  __device__ void compute_chunk(const Chunk& c, int t0, int len) {
     float z[4][G];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool ok = t0 + 4 * j < bs;
+      const bool ok = t0 + 4 * j + row < len;
       float x[VE];
       V::to_f32(c.kv[j], x);
 #pragma unroll
@@ -140,13 +141,13 @@ struct AttnWave {
     }
   }
 
-  // Fold one block of bs tokens (bs % 4 == 0) into the running state.
+  // Fold block n (bs tokens apart, holding len of them) into the running state.
   __device__ void block(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
-                        const int32_t* __restrict__ trow, int n, int bs, int page, int Hkv, int g) {
-    for (int t0 = 0; t0 < bs; t0 += 16) {
+                        const int32_t* __restrict__ trow, int n, int bs, int len, int page, int Hkv, int g) {
+    for (int t0 = 0; t0 < len; t0 += 16) {
       Chunk c;
-      load_chunk(c, kc, vc, trow, n, t0, bs, page, Hkv, g);
-      compute_chunk(c, t0, bs);
+      load_chunk(c, kc, vc, trow, n, t0, bs, len, page, Hkv, g);
+      compute_chunk(c, t0, len);
     }
   }
 
@@ -255,38 +256,42 @@ using Tile = std::conditional_t<DT == kF32, AttnWave<DT, G>, AttnWaveM<(DT == kF
 template <bool P16, typename W, typename IdFn, typename DoneFn>
 __device__ inline void run_blocks(W& st, int cnt, IdFn&& id_of, DoneFn&& done, const uint8_t* __restrict__ kc,
                                   const uint8_t* __restrict__ vc, const int32_t* __restrict__ trow, int bs,
-                                  int page, int Hkv, int g) {
+                                  int page, int Hkv, int g, int N, int last_len) {
   const int cpb = (bs + 15) >> 4;   // chunks per block
   const int total = cnt * cpb;
   if (total <= 0) return;
   if constexpr (!P16) {   // general path (pages smaller than 16 tokens, or large blocks): one chunk at a time
     for (int i = 0; i < cnt; ++i) {
-      st.block(kc, vc, trow, id_of(i), bs, page, Hkv, g);
+      const int n = id_of(i);
+      st.block(kc, vc, trow, n, bs, block_len(n, N, bs, last_len), page, Hkv, g);
       done(i);
     }
     return;
   }
-  // P16: the page size is a multiple of 16 and the caller keeps cnt * chunks per block <= 64
+  // P16: the page size is a multiple of 16 and the caller keeps cnt * chunks per block <= 64; lane k also keeps the
+  // number of tokens chunk k holds (16, fewer at the end of a block, none past the end of a sequence)
   const int lane = threadIdx.x & 63;
-  int my_phys = 0, my_off = 0;
+  int my_phys = 0, my_off = 0, my_nv = 0;
   if (lane < total) {
     const int i = lane / cpb;
-    const int64_t tc = (int64_t)id_of(i) * bs + ((lane - i * cpb) << 4);
+    const int n = id_of(i);
+    const int part = (lane - i * cpb) << 4;
+    const int64_t tc = (int64_t)n * bs + part;
     my_phys = trow[tc / page];
     my_off = (int)(tc % page);
+    my_nv = block_len(n, N, bs, last_len) - part;
   }
   // two register buffers used alternately (no copies, so the loads of one stay in flight while the other is used)
   typename W::Chunk ca, cb;
   auto load = [&](typename W::Chunk& c, int k) {
     const int phys = __builtin_amdgcn_readlane(my_phys, k);
     const int off = __builtin_amdgcn_readlane(my_off, k);
-    const int t0 = (k - (k / cpb) * cpb) << 4;
     const int64_t r = ((int64_t)phys * Hkv + g) * page + off;
-    st.load_chunk_at(c, kc + r * kRowBytes, vc + r * kRowBytes, bs - t0);
+    st.load_chunk_at(c, kc + r * kRowBytes, vc + r * kRowBytes, __builtin_amdgcn_readlane(my_nv, k));
   };
   auto compute = [&](const typename W::Chunk& c, int k) {
     const int i = k / cpb, t0 = (k - i * cpb) << 4;
-    st.compute_chunk(c, t0, bs);
+    st.compute_chunk(c, 0, __builtin_amdgcn_readlane(my_nv, k));
     if (t0 + 16 >= bs) done(i);
   };
   if constexpr (W::kPipelined) {
@@ -329,7 +334,7 @@ __device__ inline void speculate_slots(int64_t rowid, int j0, int j1, int lane, 
                                        const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                                        const int32_t* __restrict__ table, const int32_t* __restrict__ pred,
                                        int k_spec, float* __restrict__ partials, int Hq, int Hkv, int N, int bs,
-                                       int page, int pps, float qscale) {
+                                       int page, int pps, float qscale, int last_len) {
   using W = Tile<DT, G>;
   const int b = (int)(rowid / Hkv), g = (int)(rowid % Hkv);
   const int32_t* prow = pred + rowid * k_spec;
@@ -345,7 +350,7 @@ __device__ inline void speculate_slots(int64_t rowid, int j0, int j1, int lane, 
         st.write_record(partials + (rowid * k_spec + j0 + i) * rec_floats(G, W::D), folded);
         st.init(lane);
       },
-      kc, vc, table + (int64_t)b * pps, bs, page, Hkv, g);
+      kc, vc, table + (int64_t)b * pps, bs, page, Hkv, g, N, last_len);
 }
 
 // Speculation of one predicted slot s = (b * Hkv + g) * k_spec + j by one wave: the block's partial record.
@@ -354,7 +359,7 @@ __device__ inline void speculate_slot(int64_t s, int lane, const uint8_t* __rest
                                       const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                                       const int32_t* __restrict__ table, const int32_t* __restrict__ pred, int k_spec,
                                       float* __restrict__ partials, int Hq, int Hkv, int N, int bs, int page, int pps,
-                                      float qscale) {
+                                      float qscale, int last_len) {
   using W = Tile<DT, G>;
   const int64_t rowid = s / k_spec;
   const int b = (int)(rowid / Hkv), g = (int)(rowid % Hkv);
@@ -362,7 +367,7 @@ __device__ inline void speculate_slot(int64_t s, int lane, const uint8_t* __rest
   W st;
   st.init(lane);
   st.load_q(q + ((int64_t)b * Hq + (int64_t)g * G) * kRowBytes, qscale);
-  st.block(kc, vc, table + (int64_t)b * pps, n, bs, page, Hkv, g);
+  st.block(kc, vc, table + (int64_t)b * pps, n, bs, block_len(n, N, bs, last_len), page, Hkv, g);
   float folded[W::NK];
   st.fold(folded);
   st.write_record(partials + s * rec_floats(G, W::D), folded);

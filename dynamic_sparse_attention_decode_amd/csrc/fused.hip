@@ -28,7 +28,7 @@ __global__ __launch_bounds__(kSelSpecThreads) void select_spec_kernel(const floa
                                                            const int32_t* __restrict__ pred, int k_spec,
                                                            float* __restrict__ partials, int64_t spec_total, int Hq,
                                                            int Hkv, int N, int bs, int page, int pps, float qscale,
-                                                           int rows) {
+                                                           int rows, int last_len) {
   const int64_t r = blockIdx.x;
   if (r < n_sel_wg) {
     if (r < rows)
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kSelSpecThreads) void select_spec_kernel(const floa
   const int64_t s = (r - n_sel_wg) * (kSelSpecThreads / 64) + (threadIdx.x >> 6);
   if (s < spec_total)
     speculate_slot<DT, G>(s, threadIdx.x & 63, q, kc, vc, table, pred, k_spec, partials, Hq, Hkv, N, bs, page, pps,
-                          qscale);
+                          qscale, last_len);
 }
 
 constexpr int kSegSpecThreads = 256;                // the standalone speculation kernel's workgroup
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kSegSpecThreads, 3) void seg_spec_kernel(const floa
                                                            const int32_t* __restrict__ pred, int k_spec,
                                                            float* __restrict__ partials, int spw, int wpr,
                                                            int64_t spec_waves, int Hq, int Hkv, int N, int bs,
-                                                           int page, int pps, float qscale, int rows) {
+                                                           int page, int pps, float qscale, int rows, int last_len) {
   const int64_t r = blockIdx.x;
   if (r < n_seg_wg) {
     const int64_t job = r / S;
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kSegSpecThreads, 3) void seg_spec_kernel(const floa
   const int64_t rowid = w / wpr;
   const int j0 = (int)(w - rowid * wpr) * spw;
   speculate_slots<DT, G, P16>(rowid, j0, min(k_spec, j0 + spw), threadIdx.x & 63, q, kc, vc, table, pred, k_spec,
-                              partials, Hq, Hkv, N, bs, page, pps, qscale);
+                              partials, Hq, Hkv, N, bs, page, pps, qscale, last_len);
 }
 
 template <int KPT>
@@ -111,7 +111,7 @@ static void seg_spec_launch(const prr_shape& s, const float* scores, int K, int3
       scores, K, ema, kp_next, pt.S, n_seg_wg, ct, cp, static_cast<const uint8_t*>(q),
       static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, pred, k_spec, partials, spw, wpr,
       spec_waves, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size, s.pages_per_seq,
-      s.softmax_scale * kLog2e, rows);
+      s.softmax_scale * kLog2e, rows, last_block_len(s));
   const int cmax = kp_next > 0 && pp.C > pt.C ? pp.C : pt.C;
   const dim3 grid((unsigned)((kp_next > 0 ? 2 : 1) * rows));
 #define PRR_MERGE2(KPT) \
@@ -144,7 +144,7 @@ static void select_spec_launch(const prr_shape& s, const float* scores, int K, i
   select_spec_kernel<KPT, DT, G><<<grid, blk, 0, st>>>(scores, K, sel, ema, kp_next, pred_next, n_sel_wg, qq, kk, vv, \
                                                        table, pred, k_spec, partials, spec_total, s.n_q_heads,       \
                                                        s.n_kv_heads, s.n_blocks, s.block_size, s.page_size,          \
-                                                       s.pages_per_seq, qs, rows)
+                                                       s.pages_per_seq, qs, rows, last_block_len(s))
   // values per thread: a few register sizes cover every row length (larger than needed is correct, just slower)
   if (s.n_blocks <= 4 * kSelSpecThreads)
     PRR_SELSPEC(4);

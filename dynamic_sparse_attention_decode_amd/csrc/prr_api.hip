@@ -144,6 +144,11 @@ static prr_status check_shape(const prr_shape* s) {
     return PRR_EINVAL;
   }
   if (s->n_blocks > 65536) { set_error("n_blocks > 65536"); return PRR_EUNSUPPORTED; }
+  if (s->ctx_len != 0 && ((int64_t)s->ctx_len <= (int64_t)(s->n_blocks - 1) * s->block_size ||
+                           (int64_t)s->ctx_len > (int64_t)s->n_blocks * s->block_size)) {
+    set_error("ctx_len %d not in ((n_blocks - 1) * block_size, n_blocks * block_size]", s->ctx_len);
+    return PRR_EINVAL;
+  }
   if (!(s->softmax_scale > 0.f) || !isfinite(s->softmax_scale)) { set_error("softmax_scale must be finite and > 0"); return PRR_EINVAL; }
   return PRR_OK;
 }
@@ -203,6 +208,13 @@ prr_status prr_build_summaries(const prr_shape* shape, const void* k_cache, cons
     jobs = n_block_ids;
   }
   return launch_summaries(*shape, k_cache, block_table, block_ids, jobs, summaries, as_stream(stream));
+}
+
+prr_status prr_append_kv(const prr_shape* shape, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                         const int32_t* block_table, void* summaries, void* stream) {
+  PRR_TRY(check_shape(shape));
+  PRR_REQUIRE(k_new && v_new && k_cache && v_cache && block_table && summaries, "append_kv: null pointer");
+  return launch_append(*shape, k_new, v_new, k_cache, v_cache, block_table, summaries, as_stream(stream));
 }
 
 prr_status prr_score_select(const prr_shape* shape, const void* q, const void* summaries, int32_t top_k,

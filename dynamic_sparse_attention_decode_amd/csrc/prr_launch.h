@@ -49,6 +49,15 @@ void trace_end(int kid, hipStream_t stream);
     }                                                                   \
   } while (0)
 
+// Tokens of the last block (block_size unless the sequence ends inside it).
+inline int last_block_len(const prr_shape& s) {
+  return s.ctx_len > 0 ? s.ctx_len - (s.n_blocks - 1) * s.block_size : s.block_size;
+}
+// Tokens of block n of a sequence whose last block N - 1 holds last_len tokens.
+__host__ __device__ inline int block_len(int n, int N, int bs, int last_len) { return n == N - 1 ? last_len : bs; }
+
+prr_status launch_append(const prr_shape& s, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                         const int32_t* table, void* summ, hipStream_t stream);
 prr_status launch_summaries(const prr_shape& s, const void* k_cache, const int32_t* table, const int32_t* ids,
                             int64_t n_jobs, void* summ, hipStream_t stream);
 // Scores; with ema != nullptr also the EMA update (first != 0: ema = scores).

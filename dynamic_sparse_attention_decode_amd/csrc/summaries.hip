@@ -3,7 +3,11 @@
 //
 // One wave per block: each load instruction reads 4 token rows (16 lanes x 16 B per 256-byte row); lanes keep
 // running min/max, then fold the 4 rows with permlane swaps. Rows 0 and 1 of the wave write the min and max rows.
-// Pure HBM streaming: reads bs * 256 B per block, writes 512 B.
+// Pure HBM streaming: reads bs * 256 B per block, writes 512 B. A last block that the sequence ends inside is
+// summarised over the tokens it holds.
+//
+// append_kernel: the decode step's new token (position ctx_len - 1) into the K and V caches and its block's summary
+// updated in place, 16 lanes per (b, g).
 #include "prr_device.h"
 #include "prr_launch.h"
 
@@ -14,7 +18,7 @@ __global__ __launch_bounds__(256) void summaries_kernel(const uint8_t* __restric
                                                         const int32_t* __restrict__ table,
                                                         const int32_t* __restrict__ ids, int64_t n_jobs,
                                                         int64_t n_total, uint8_t* __restrict__ summ, int Hkv, int N,
-                                                        int bs, int page, int pps) {
+                                                        int bs, int page, int pps, int last_len) {
   using V = Vec<DT>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t job = (int64_t)blockIdx.x * 4 + wave;
@@ -33,8 +37,10 @@ __global__ __launch_bounds__(256) void summaries_kernel(const uint8_t* __restric
   for (int e = 0; e < V::n; ++e) { mn[e] = __builtin_huge_valf(); mx[e] = -__builtin_huge_valf(); }
 
   const int tok0 = n * bs;
+  const int len = block_len(n, N, bs, last_len);
 #pragma unroll 4
-  for (int t = 0; t < bs; t += 4) {
+  for (int t = 0; t < len; t += 4) {
+    if (t + row >= len) break;   // rows past the sequence's end (only in its last block)
     const int tok = tok0 + t + row;
     const int64_t phys = trow[tok / page];
     const uint8_t* p = k_cache + ((phys * Hkv + g) * page + (tok % page)) * (int64_t)kRowBytes + col * 16;
@@ -56,6 +62,61 @@ __global__ __launch_bounds__(256) void summaries_kernel(const uint8_t* __restric
   }
 }
 
+template <int DT>
+__global__ __launch_bounds__(256) void append_kernel(const uint8_t* __restrict__ k_new,
+                                                     const uint8_t* __restrict__ v_new, uint8_t* __restrict__ k_cache,
+                                                     uint8_t* __restrict__ v_cache, const int32_t* __restrict__ table,
+                                                     uint8_t* __restrict__ summ, int rows, int Hkv, int N, int bs,
+                                                     int page, int pps, int pos) {
+  using V = Vec<DT>;
+  const int r = (int)((blockIdx.x * 256 + threadIdx.x) >> 4);   // (b, g) row
+  if (r >= rows) return;
+  const int col = threadIdx.x & 15;
+  const int b = r / Hkv, g = r % Hkv;
+  const int64_t phys = table[(int64_t)b * pps + pos / page];
+  const int64_t off = ((phys * Hkv + g) * page + pos % page) * (int64_t)kRowBytes + col * 16;
+  const uint4 k = ld16(k_new + (int64_t)r * kRowBytes + col * 16);
+  st16(k_cache + off, k);
+  st16(v_cache + off, ld16(v_new + (int64_t)r * kRowBytes + col * 16));
+  uint8_t* smin = summ + (((int64_t)r * N + pos / bs) * 2) * kRowBytes + col * 16;
+  uint8_t* smax = smin + kRowBytes;
+  if (pos % bs == 0) {   // the token opens its block
+    st16(smin, k);
+    st16(smax, k);
+    return;
+  }
+  float x[V::n], lo[V::n], hi[V::n];
+  V::to_f32(k, x);
+  V::to_f32(ld16(smin), lo);
+  V::to_f32(ld16(smax), hi);
+#pragma unroll
+  for (int e = 0; e < V::n; ++e) { lo[e] = fminf(lo[e], x[e]); hi[e] = fmaxf(hi[e], x[e]); }
+  st16(smin, V::from_f32(lo));
+  st16(smax, V::from_f32(hi));
+}
+
+prr_status launch_append(const prr_shape& s, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                         const int32_t* table, void* summ, hipStream_t stream) {
+  const int rows = s.batch * s.n_kv_heads;
+  const int pos = (s.ctx_len > 0 ? s.ctx_len : s.n_blocks * s.block_size) - 1;
+  const dim3 grid((unsigned)((rows * 16 + 255) / 256)), block(256);
+  const auto* kn = static_cast<const uint8_t*>(k_new);
+  const auto* vn = static_cast<const uint8_t*>(v_new);
+  auto* kc = static_cast<uint8_t*>(k_cache);
+  auto* vc = static_cast<uint8_t*>(v_cache);
+  auto* sm = static_cast<uint8_t*>(summ);
+#define PRR_APPEND(DT)                                                                                             \
+  append_kernel<DT><<<grid, block, 0, stream>>>(kn, vn, kc, vc, table, sm, rows, s.n_kv_heads, s.n_blocks,           \
+                                                s.block_size, s.page_size, s.pages_per_seq, pos)
+  switch (s.dtype) {
+    case kF32: PRR_APPEND(kF32); break;
+    case kBF16: PRR_APPEND(kBF16); break;
+    default: PRR_APPEND(kF16); break;
+  }
+#undef PRR_APPEND
+  return check_launch("append_kv");
+}
+
 prr_status launch_summaries(const prr_shape& s, const void* k_cache, const int32_t* table, const int32_t* ids,
                             int64_t n_jobs, void* summ, hipStream_t stream) {
   if (n_jobs == 0) return PRR_OK;
@@ -66,12 +127,13 @@ prr_status launch_summaries(const prr_shape& s, const void* k_cache, const int32
   trace_begin(PRR_KERNEL_SUMMARIES, stream);
   switch (s.dtype) {
     case kF32: summaries_kernel<kF32><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads, s.n_blocks,
-                                                                  s.block_size, s.page_size, s.pages_per_seq); break;
+                                                                  s.block_size, s.page_size, s.pages_per_seq, last_block_len(s)); break;
     case kBF16: summaries_kernel<kBF16><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads,
                                                                     s.n_blocks, s.block_size, s.page_size,
-                                                                    s.pages_per_seq); break;
+                                                                    s.pages_per_seq, last_block_len(s)); break;
     default: summaries_kernel<kF16><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads, s.n_blocks,
-                                                                s.block_size, s.page_size, s.pages_per_seq); break;
+                                                                s.block_size, s.page_size, s.pages_per_seq,
+                                                                last_block_len(s)); break;
   }
   trace_end(PRR_KERNEL_SUMMARIES, stream);
   return check_launch("build_summaries");

@@ -26,14 +26,14 @@ __global__ __launch_bounds__(256, 3) void score_spec_kernel(const uint8_t* __res
                                                          const int32_t* __restrict__ pred, int k_spec,
                                                          float* __restrict__ partials, int n_spec_wg, int spw, int wpr,
                                                          int64_t spec_waves, int Hq, int Hkv, int N, int bs, int page,
-                                                         int pps, float qscale) {
+                                                         int pps, float qscale, int last_len) {
   if ((int)blockIdx.x < n_spec_wg) {
     const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (w < spec_waves) {
       const int64_t rowid = w / wpr;
       const int j0 = (int)(w - rowid * wpr) * spw;
       speculate_slots<DT, G, P16>(rowid, j0, min(k_spec, j0 + spw), threadIdx.x & 63, q, kc, vc, table, pred,
-                                  k_spec, partials, Hq, Hkv, N, bs, page, pps, qscale);
+                                  k_spec, partials, Hq, Hkv, N, bs, page, pps, qscale, last_len);
     }
     return;
   }
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
     int32_t* __restrict__ pred_next, const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, const int32_t* __restrict__ pred, int k_spec,
     float* __restrict__ partials, int64_t spec_total, MissedWs ws, int32_t* __restrict__ n_missed, int Hq, int Hkv,
-    int N, int bs, int page, int pps, float qscale, int rows, int n_pwg) {
+    int N, int bs, int page, int pps, float qscale, int rows, int n_pwg, int last_len) {
   using W = Tile<DT, G>;
   constexpr int NW = kSRThreads / 64;
   constexpr int D = W::D;
@@ -96,7 +96,8 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
   if (r >= rows + n_pwg) {   // speculation over P_t
     const int64_t s = (r - rows - n_pwg) * NW + wave;
     if (s < spec_total)
-      speculate_slot<DT, G>(s, lane, q, kc, vc, table, pred, k_spec, partials, Hq, Hkv, N, bs, page, pps, qscale);
+      speculate_slot<DT, G>(s, lane, q, kc, vc, table, pred, k_spec, partials, Hq, Hkv, N, bs, page, pps, qscale,
+                            last_len);
     return;
   }
   if (r >= rows) {   // next step's predicted set
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
   for (int i0 = m0; i0 < m1; i0 += cap) {
     const int base = nh + i0;
     run_blocks<true>(st, min(cap, m1 - i0), [&](int i) { return s_list[base + i]; }, [](int) {}, kc, vc, trow, bs,
-                     page, Hkv, g);
+                     page, Hkv, g, N, last_len);
   }
   float folded[W::NK];
   st.fold(folded);
@@ -327,7 +328,8 @@ static void score_spec_launch(const prr_shape& s, const void* q, const void* sum
 #define PRR_SCORESPEC(EMA_, P16_)                                                                                   \
   score_spec_kernel<DT, G, EMA_, P16_><<<dim3(grid), dim3(256), 0, st>>>(                                          \
       qq, sm, scores, chunk, gx, ema, alpha, first, kk, vv, table, pred, k_spec, partials, n_spec_wg, spw, wpr,    \
-      spec_waves, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size, s.pages_per_seq, qs)
+      spec_waves, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size, s.pages_per_seq, qs,          \
+      last_block_len(s))
   if (ema) {
     if (p16) PRR_SCORESPEC(true, true); else PRR_SCORESPEC(true, false);
   } else {
@@ -373,7 +375,8 @@ static void select_missed_launch(const prr_shape& s, const float* scores, int K,
   select_missed_kernel<KPT, DT, G><<<grid, blk, 0, st>>>(scores, K, sel, ema, kp_next, pred_next, qq, kk, vv,       \
                                                          table, pred, k_spec, partials, spec_total, ws, n_missed,   \
                                                          s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size,       \
-                                                         s.page_size, s.pages_per_seq, qs, rows, n_pwg)
+                                                         s.page_size, s.pages_per_seq, qs, rows, n_pwg,             \
+                                                         last_block_len(s))
   trace_begin(PRR_KERNEL_SELECT_TOPK, st);
   if (s.n_blocks <= 4 * kSRThreads)
     PRR_SELMISS(4);

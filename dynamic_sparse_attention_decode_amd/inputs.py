@@ -19,6 +19,8 @@ Recipe (per workload, master seed ``seed``):
   moves from one uniformly chosen hot block to one uniformly chosen non-hot block.
 * Paged KV: ``page_size`` tokens per page; the page table is the identity, or a seeded permutation of all pages of
   the batch when ``shuffle_pages`` is set.
+* A context that ends inside a block (``ctx`` not a multiple of ``block_size``): the cache holds whole blocks, and
+  the slots past the end hold poison (keys +50, values 1e4), which no result may depend on.
 
 Every random draw is keyed by (seed, purpose, indices) through numpy's SeedSequence, so any part can be regenerated
 independently. Bulk K/V draws use torch's generator on the target device; within one device the bytes are
@@ -66,11 +68,16 @@ class Workload:
 
     @property
     def n_blocks(self) -> int:
-        return self.ctx // self.block_size
+        return -(-self.ctx // self.block_size)   # the last block may be partly filled
+
+    @property
+    def capacity(self) -> int:
+        """Token slots per sequence in the paged cache (whole blocks)."""
+        return self.n_blocks * self.block_size
 
     @property
     def pages_per_seq(self) -> int:
-        return self.ctx // self.page_size
+        return self.capacity // self.page_size
 
     @property
     def n_pages(self) -> int:
@@ -93,7 +100,7 @@ class Workload:
 
     def validate(self) -> None:
         assert self.n_q_heads % self.n_kv_heads == 0
-        assert self.ctx % self.block_size == 0 and self.block_size % self.page_size == 0
+        assert self.ctx >= 1 and self.block_size % self.page_size == 0
         assert 1 <= self.top_k <= self.n_blocks
         assert all(0 <= k <= self.n_blocks for k in self.k_spec)
         assert 0 <= self.hot_blocks <= self.n_blocks
@@ -255,13 +262,16 @@ def make_inputs(w: Workload, device="cpu", steps: int | None = None) -> DecodeIn
     k_cache = torch.empty((w.n_pages, Hkv, page, D), dtype=dt, device=device)
     v_cache = torch.empty_like(k_cache)
     saved = {}
+    cap = w.capacity
     for b in range(B):
         phys = torch.as_tensor(table_np[b], device=device, dtype=torch.long)
         for g in range(Hkv):
-            k = torch.randn((ctx, D), generator=_torch_gen(device, w.seed, _P_K, b, g), device=device,
+            k = torch.randn((cap, D), generator=_torch_gen(device, w.seed, _P_K, b, g), device=device,
                             dtype=torch.float32)
-            v = torch.randn((ctx, D), generator=_torch_gen(device, w.seed, _P_V, b, g), device=device,
+            v = torch.randn((cap, D), generator=_torch_gen(device, w.seed, _P_V, b, g), device=device,
                             dtype=torch.float32)
+            k[ctx:] = 50.0   # slots past the end of the sequence
+            v[ctx:] = 1e4
             if w.hot_blocks:
                 kb = k.view(w.n_blocks, w.block_size, D)
                 idx = torch.as_tensor(hot[b, g], device=device, dtype=torch.long)

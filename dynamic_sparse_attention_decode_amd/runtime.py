@@ -28,7 +28,8 @@ class PRRLayer:
                  device="cuda", streams=None):
         if mode not in MODES:
             raise ValueError(f"mode must be one of {list(MODES)}")
-        self.shape = shape
+        self.shape = L.Shape.from_buffer_copy(shape)   # own copy: append() advances its ctx_len
+        shape = self.shape
         self.top_k = int(top_k)
         self.k_spec = int(k_spec) if mode not in ("serialized", "serialized_fused") else 0
         self.alpha = float(alpha)
@@ -85,6 +86,19 @@ class PRRLayer:
         self.s_sel.wait_stream(cur)
         L.build_summaries(self.shape, self.k_cache, self.table, self.summaries, block_ids=flat_ids,
                           stream=self.s_sel)
+        cur.wait_stream(self.s_sel)
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+        """Decode-time append of one token per sequence (k_new, v_new: [B, Hkv, D]) at the end of the layer's
+        sequences, on the selection stream, ahead of the next step; the last block must have room for it."""
+        s = self.shape
+        n_tok = s.ctx_len or s.n_blocks * s.block_size
+        if n_tok >= s.n_blocks * s.block_size:
+            raise L.PRRError("append: the last block is full (the block count is fixed for this layer)")
+        s.ctx_len = n_tok + 1
+        cur = torch.cuda.current_stream(self.device)
+        self.s_sel.wait_stream(cur)
+        L.append_kv(s, k_new, v_new, self.k_cache, self.v_cache, self.table, self.summaries, stream=self.s_sel)
         cur.wait_stream(self.s_sel)
 
     def reset(self) -> None:

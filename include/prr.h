@@ -63,13 +63,17 @@ typedef enum { PRR_F32 = 0, PRR_BF16 = 1, PRR_F16 = 2 } prr_dtype;
 
 /* Shape of one attention layer's decode state. Supported: (dtype F32, head_dim 64) and (dtype BF16 or F16,
  * head_dim 128) — one 256-byte row per token; group size G in {1, 2, 4, 8}; block_size a multiple of page_size and
- * of 4; 1 <= n_blocks <= 65536 (and n_blocks <= 32768 for the top-K kernels). */
+ * of 4; 1 <= n_blocks <= 65536 (and n_blocks <= 32768 for the top-K kernels).
+ * ctx_len: tokens of every sequence. 0 means n_blocks * block_size; otherwise (n_blocks - 1) * block_size < ctx_len
+ * <= n_blocks * block_size, and the last block holds ctx_len - (n_blocks - 1) * block_size tokens: its summary covers
+ * those tokens and attention never reads past them (decode appends one token at a time, prr_append_kv). */
 typedef struct {
   int32_t batch, n_q_heads, n_kv_heads, head_dim;
   int32_t block_size, page_size;
   int32_t n_blocks, pages_per_seq;
   int32_t dtype;        /* prr_dtype */
   float softmax_scale;  /* typically 1/sqrt(head_dim) */
+  int32_t ctx_len;      /* tokens per sequence (0: n_blocks * block_size) */
 } prr_shape;
 
 /* Quest block summaries (PRR reference list, Quest): for every (b, kv head g, block n), the elementwise min and max
@@ -78,6 +82,15 @@ typedef struct {
  * whose keys changed) are rebuilt and the rest of `summaries` is left untouched. */
 prr_status prr_build_summaries(const prr_shape* shape, const void* k_cache, const int32_t* block_table,
                                const int32_t* block_ids, int32_t n_block_ids, void* summaries, void* stream);
+
+/* Decode-time append (the step before selection in a decoder): with ctx_len the length after the append, the token
+ * at position p = ctx_len - 1 of every (b, kv head g) is written from k_new, v_new [B, Hkv, D] (the cache dtype) into
+ * the K and V caches through the block table, and the summary of its block n = p / block_size is updated in place:
+ * (k, k) when p starts the block, else the elementwise (min, max) with k — exact, and equal to rebuilding the
+ * block's summary over its tokens. Requires ctx_len >= 1 (a shape with ctx_len 0 appends at n_blocks * block_size - 1,
+ * the last slot). Enqueues one small launch; the next step's shape carries the same ctx_len. */
+prr_status prr_append_kv(const prr_shape* shape, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                         const int32_t* block_table, void* summaries, void* stream);
 
 /* Query-aware block scores and exact top-K selection (PRR abstract: attend only to the top-K blocks relevant to
  * each query). scores[b,g,n] = sum over the query heads h of KV head g and dims d of

@@ -33,7 +33,13 @@ SMALL = ["tiny_f32_4k", "llama3_8b_32k", "long_ctx_131k_b4", "paged_b32_64k", "m
 
 def shape_of(w: Workload) -> L.Shape:
     return L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, w.n_blocks,
-                        {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[w.dtype], w.scale)
+                        {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[w.dtype], w.scale,
+                        ctx_len=w.ctx if w.ctx % w.block_size else 0)
+
+
+def ragged(w: Workload, short: int) -> Workload:
+    """The workload with its sequences ending `short` tokens before the end of the last block."""
+    return w.replace(name=w.name + f"_short{short}", ctx=w.ctx - short)
 
 
 def np64(t: torch.Tensor) -> np.ndarray:

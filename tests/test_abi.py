@@ -48,6 +48,8 @@ def _status(fn, *args):
     (dict(block_size=16, page_size=32), -1),      # block_size % page_size != 0
     (dict(n_blocks=0), -1),
     (dict(n_blocks=40000), -2),                   # top-K kernels support N <= 32768
+    (dict(ctx_len=2047 * 16), -1),                # ctx_len must end inside the last block
+    (dict(ctx_len=2048 * 16 + 1), -1),
 ])
 def test_shape_validation(bad, code):
     lib = L.lib()
@@ -56,6 +58,16 @@ def test_shape_validation(bad, code):
     st = lib.prr_score_select(ctypes.byref(s), nz, nz, 8, nz, nz, None, None)
     assert st == code, (bad, st, lib.prr_last_error())
     assert lib.prr_last_error()
+
+
+def test_append_validation_without_launch():
+    lib = L.lib()
+    nz = ctypes.c_void_p(16)
+    s = _shape(ctx_len=2047 * 16 + 5)
+    assert lib.prr_append_kv(ctypes.byref(s), None, nz, nz, nz, nz, nz, None) == -1       # null k_new
+    assert lib.prr_append_kv(ctypes.byref(s), nz, nz, nz, nz, nz, None, None) == -1       # null summaries
+    bad = _shape(ctx_len=2047 * 16)
+    assert lib.prr_append_kv(ctypes.byref(bad), nz, nz, nz, nz, nz, nz, None) == -1       # ctx_len out of range
 
 
 def test_argument_validation_without_launch():

@@ -9,7 +9,7 @@ from dynamic_sparse_attention_decode_amd.inputs import make_inputs
 from dynamic_sparse_attention_decode_amd.runtime import PRRLayer
 from oracle import prr_oracle as O
 from tests.checker import TOL, check_selection, max_abs
-from tests.gpu_common import SMALL, OracleView, np64, requires_gpu, shape_of, small
+from tests.gpu_common import SMALL, OracleView, np64, ragged, requires_gpu, shape_of, small
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -139,12 +139,13 @@ def test_ema_state_save_restore():
 def test_graph_replay_matches_eager(rows, mode):
     """Steps captured in a HIP graph and replayed several times (with eager work and synchronisation between the
     replays) give the same outputs, selections and missed counts as the same steps run eagerly; also with rows of
-    12000 blocks, which select by segments through the workspace's candidate regions."""
+    12000 blocks, which select by segments through the workspace's candidate regions (the last block partly
+    filled)."""
     if rows == "short":
         w = small("llama3_8b_32k")
         kp = w.k_spec[0]
     else:
-        w = small("million_token").replace(ctx=32 * 12000, top_k=61, k_spec=(93,), steps=6)
+        w = small("million_token").replace(ctx=32 * 12000 - 7, top_k=61, k_spec=(93,), steps=6)
         kp = 93
     print(f"[case] graph replay {rows} rows N={w.n_blocks} {mode}", flush=True)
     inp = make_inputs(w, device="cuda")
@@ -212,3 +213,77 @@ def test_all_blocks_selected_is_dense_attention():
         ref = O.attention_over_blocks(qg, ov.keys(0, 0), ov.values(0, 0), np.arange(128), w.block_size, w.scale)
         assert max_abs(h["out"][0, :G], ref) <= TOL[w.dtype]
         assert list(h["sel"][0, 0]) == list(range(128))
+
+
+PARTIAL = [("tiny_f32_4k", 31, "prr_fused"), ("llama3_8b_32k", 5, "prr_fused"), ("llama3_8b_32k", 9, "serialized"),
+           ("long_ctx_131k_b4", 40, "prr_2stream"), ("paged_b32_64k", 15, "prr_fused"),
+           ("paged_b32_64k", 7, "serialized_fused"), ("million_token", 3, "prr_fused"),
+           ("million_token", 20, "prr_1stream")]
+
+
+@pytest.mark.parametrize("name,short,mode", PARTIAL)
+def test_partial_last_block_decode(name, short, mode):
+    """Sequences that end inside their last block (the slots past the end hold poison): every step's selection,
+    output, missed count and predicted set against the oracle over the tokens that exist."""
+    w = ragged(small(name), short).replace(steps=4)
+    print(f"[case] partial decode {w.name} ctx={w.ctx} {mode}", flush=True)
+    inp = make_inputs(w, device="cuda")
+    ov = OracleView(inp)
+    kp = max(w.k_spec) or w.top_k
+    run_layer(w, inp, kp, mode, ov=ov)
+
+
+class _Grown:
+    """Oracle view of sequences that grow by one appended token per step (host copies of what was appended)."""
+
+    def __init__(self, ov):
+        self.ov = ov
+        self.k = {}
+        self.v = {}
+
+    def keys(self, b, g):
+        return self.k.setdefault((b, g), self.ov.keys(b, g))
+
+    def values(self, b, g):
+        return self.v.setdefault((b, g), self.ov.values(b, g))
+
+    def append(self, b, g, kn, vn):
+        self.k[(b, g)], self.v[(b, g)] = O.append_token(self.keys(b, g), self.values(b, g), kn, vn)
+
+    def q_group(self, t, b, g):
+        return self.ov.q_group(t, b, g)
+
+
+@pytest.mark.parametrize("name,mode", [("llama3_8b_32k", "prr_fused"), ("paged_b32_64k", "prr_2stream"),
+                                       ("tiny_f32_4k", "serialized"), ("million_token", "prr_fused")])
+def test_decode_with_appends(name, mode):
+    """A decoder's loop: before every step after the first, one new token per sequence is appended (prr_append_kv
+    through PRRLayer.append); the step then selects, speculates and repairs over the longer sequences. Checked at
+    every step against the oracle over the sequences with the same appended tokens."""
+    w = ragged(small(name), 7).replace(steps=6)
+    print(f"[case] decode with appends {w.name} {mode}", flush=True)
+    inp = make_inputs(w, device="cuda")
+    view = _Grown(OracleView(inp))
+    kp = max(w.k_spec) or w.top_k
+    layer = PRRLayer(shape_of(w), w.top_k, kp, w.alpha, mode=mode)
+    layer.build(inp.k_cache, inp.v_cache, inp.table)
+    rng = np.random.default_rng(43)
+    ema_ref = {}
+    for t in range(w.steps):
+        if t > 0:
+            kn = torch.as_tensor(rng.standard_normal((w.batch, w.n_kv_heads, w.head_dim)),
+                                 dtype=torch.float32).to(w.torch_dtype)
+            vn = torch.as_tensor(rng.standard_normal((w.batch, w.n_kv_heads, w.head_dim)),
+                                 dtype=torch.float32).to(w.torch_dtype)
+            layer.append(kn.cuda(), vn.cuda())
+            for b in range(w.batch):
+                for g in range(w.n_kv_heads):
+                    view.append(b, g, kn[b, g].double().numpy(), vn[b, g].double().numpy())
+        out = layer.step(inp.q[t].contiguous())
+        torch.cuda.synchronize()
+        h = dict(out=np64(out), sel=layer.sel_idx.cpu().numpy().copy(),
+                 pred=None if (t == 0 or layer.k_spec == 0) else layer.pred_current.cpu().numpy().copy(),
+                 nm=layer.n_missed.cpu().numpy().copy())
+        _check_step(w, view, t, h, layer.k_spec, ema_ref)
+    assert layer.shape.ctx_len == w.ctx + w.steps - 1
+    layer.close()

@@ -9,7 +9,7 @@ from dynamic_sparse_attention_decode_amd import _lib as L
 from dynamic_sparse_attention_decode_amd.inputs import make_inputs
 from oracle import prr_oracle as O
 from tests.checker import TOL, check_selection, max_abs
-from tests.gpu_common import SMALL, OracleView, np64, requires_gpu, shape_of, small
+from tests.gpu_common import SMALL, OracleView, np64, ragged, requires_gpu, shape_of, small
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -461,3 +461,52 @@ def test_fused_launches_match_separate(name):
         assert torch.equal(sc_a, sc_c) and torch.equal(em_a.view(torch.int32), em_c.view(torch.int32)), t
         assert torch.equal(pa_a.view(torch.int32), pa_c.view(torch.int32)), t
         em_prev = em_a.clone()
+
+
+@pytest.mark.parametrize("name,short", [("tiny_f32_4k", 31), ("llama3_8b_32k", 5), ("paged_b32_64k", 15),
+                                        ("long_ctx_131k_b4", 40), ("million_token", 3)])
+def test_partial_last_block_summaries_and_append(name, short):
+    """Sequences that end inside their last block: the summaries cover the tokens that exist (the slots past the end
+    hold poison that must never enter). Then tokens are appended one at a time through prr_append_kv (when the last
+    block holds a single token, the first append rewrites it and so opens the block): the cache rows written equal the
+    appended tokens, and after every append each summary equals the oracle's over the longer sequence, exactly."""
+    w = ragged(small(name), short)
+    print(f"[case] partial last block {w.name} ctx={w.ctx} N={w.n_blocks}", flush=True)
+    inp = make_inputs(w, device="cuda")
+    s = shape_of(w)
+    B, Hkv, N, D, bs, page = w.batch, w.n_kv_heads, w.n_blocks, w.head_dim, w.block_size, w.page_size
+    summ = torch.zeros((B, Hkv, N, 2, D), dtype=w.torch_dtype, device="cuda")
+    L.build_summaries(s, inp.k_cache, inp.table, summ)
+    torch.cuda.synchronize()
+    ov = OracleView(inp)
+    keys = {(b, g): ov.keys(b, g) for b in range(B) for g in range(Hkv)}
+    vals = {(b, g): ov.values(b, g) for b in range(B) for g in range(Hkv)}
+
+    def check_summaries(tag):
+        got = np64(summ)
+        for (b, g), k in keys.items():
+            kmin, kmax = O.block_summaries(k, bs)
+            assert np.array_equal(got[b, g, :, 0], kmin) and np.array_equal(got[b, g, :, 1], kmax), (tag, b, g)
+
+    check_summaries("built")
+    rng = np.random.default_rng(41)
+    n_tok = w.ctx
+    if (n_tok - 1) % bs == 0:   # rewrite the last block's only token: the append opens the block
+        n_tok -= 1
+        for key in keys:
+            keys[key], vals[key] = keys[key][:-1], vals[key][:-1]
+    for i in range(min(6, w.n_blocks * bs - n_tok)):
+        kn = torch.as_tensor(rng.standard_normal((B, Hkv, D)), dtype=torch.float32).to(w.torch_dtype)
+        vn = torch.as_tensor(rng.standard_normal((B, Hkv, D)), dtype=torch.float32).to(w.torch_dtype)
+        n_tok += 1
+        s.ctx_len = n_tok
+        L.append_kv(s, kn.cuda(), vn.cuda(), inp.k_cache, inp.v_cache, inp.table, summ)
+        torch.cuda.synchronize()
+        pos = n_tok - 1
+        for (b, g) in keys:
+            keys[(b, g)], vals[(b, g)] = O.append_token(keys[(b, g)], vals[(b, g)], kn[b, g].double().numpy(),
+                                                         vn[b, g].double().numpy())
+            phys = int(inp.table_np[b, pos // page])
+            assert torch.equal(inp.k_cache[phys, g, pos % page].cpu(), kn[b, g]), (i, b, g)
+            assert torch.equal(inp.v_cache[phys, g, pos % page].cpu(), vn[b, g]), (i, b, g)
+        check_summaries(f"append {i}")
