@@ -18,7 +18,8 @@ LLM Decoding", arXiv 2606.30389):
 Readings where the pages are silent (each is listed in the design notes):
   * score: Quest's per-head upper bound sum_d max(q_d * kmin_d, q_d * kmax_d), summed over the query heads of the
     KV group (one selection per sequence and KV head);
-  * top-K ties go to the lower block index; index lists are reported in ascending order;
+  * top-K ties go to the lower block index; index lists are reported in ascending order; optional forced blocks
+    (the first n_sink and last n_local) rank first;
   * the EMA averages block scores: e_0 = s_0, e_t = alpha * e_{t-1} + (1 - alpha) * s_t; step 0 has no prediction;
     the prediction for step t is the top-K' of e_{t-1} with the same tie rule;
   * softmax scale 1/sqrt(D);
@@ -94,10 +95,17 @@ def quest_scores_signsplit(q_group: np.ndarray, kmin: np.ndarray, kmax: np.ndarr
 # ------------------------------------------------------------------------------------------------------------------
 
 
-def top_k(values: np.ndarray, k: int) -> np.ndarray:
-    """Indices of the k largest values, ties to the lower index; returned ascending (int64)."""
+def top_k(values: np.ndarray, k: int, n_sink: int = 0, n_local: int = 0) -> np.ndarray:
+    """Indices of the k largest values, ties to the lower index; returned ascending (int64).
+
+    Forced blocks (attention sinks and a local window; StreamingLLM in the PRR reference list): the first n_sink and
+    the last n_local blocks rank above every other block, among themselves by index, so they are always selected
+    when k covers them."""
     n = len(values)
-    order = np.lexsort((np.arange(n), -np.asarray(values, dtype=np.float64)))
+    idx = np.arange(n)
+    forced = (idx < n_sink) | (idx >= n - n_local)
+    rank_value = np.where(forced, 0.0, -np.asarray(values, dtype=np.float64))   # forced: by index alone
+    order = np.lexsort((idx, rank_value, ~forced))
     return np.sort(order[:k])
 
 
@@ -217,9 +225,10 @@ def ema_update(ema_prev, scores, alpha: float, first: bool) -> np.ndarray:
     return alpha * np.asarray(ema_prev, dtype=np.float64) + (1.0 - alpha) * s
 
 
-def predict(ema, k_spec: int) -> np.ndarray:
-    """Predicted set for the next step: top-K' of the EMA with the selection's tie rule (ascending)."""
-    return top_k(ema, k_spec)
+def predict(ema, k_spec: int, n_sink: int = 0, n_local: int = 0) -> np.ndarray:
+    """Predicted set for the next step: top-K' of the EMA with the selection's tie rule and forced blocks
+    (ascending)."""
+    return top_k(ema, k_spec, n_sink, n_local)
 
 
 # ------------------------------------------------------------------------------------------------------------------
@@ -286,11 +295,16 @@ def decode_row(q_steps, keys_at, values, block_size: int, top_k_blocks: int, k_s
 # ------------------------------------------------------------------------------------------------------------------
 
 
-def brute_force_top_k(values, k: int):
-    """Among all k-subsets, the one with the largest sum; ties to the lexicographically smallest ascending tuple."""
+def brute_force_top_k(values, k: int, forced=()):
+    """Among all k-subsets that contain the forced blocks (or, when k is smaller than their number, that lie inside
+    them), the one with the largest sum; ties to the lexicographically smallest ascending tuple."""
+    forced = set(forced)
     best, best_sum = None, -math.inf
     for c in combinations(range(len(values)), k):
-        s = float(sum(values[i] for i in c))
+        cs = set(c)
+        if (len(forced) <= k and not forced <= cs) or (len(forced) > k and not cs <= forced):
+            continue
+        s = float(sum(values[i] for i in c)) if len(forced) <= k else -float(sum(c))
         if s > best_sum or (s == best_sum and c < best):
             best, best_sum = c, s
     return np.asarray(best, dtype=np.int64)

@@ -303,6 +303,33 @@ def pin_partial_last_block(o):
         assert np.allclose(got, ref, rtol=0, atol=1e-13)
 
 
+def pin_forced_blocks(o):
+    """Forced blocks (attention sinks and a local window): against brute force over every K-subset that contains
+    them (or lies inside them when K is smaller), with integer ties included; no forced blocks is the plain top-K;
+    K equal to their number selects exactly them, even when they hold the lowest scores; the prediction forces them
+    too."""
+    rng = np.random.default_rng(21)
+    for trial in range(80):
+        nb = int(rng.integers(3, 10))
+        sink = int(rng.integers(0, 3))
+        local = int(rng.integers(0, 3))
+        if sink + local > nb:
+            continue
+        k = int(rng.integers(1, nb + 1))
+        vals = rng.standard_normal(nb)
+        if trial % 3 == 0:
+            vals = np.round(vals * 2)
+        forced = [i for i in range(nb) if i < sink or i >= nb - local]
+        got = o.top_k(vals, k, sink, local)
+        ref = o.brute_force_top_k(list(vals), k, forced)
+        assert list(got) == list(ref), (vals, k, sink, local, got, ref)
+        assert list(o.top_k(vals, k, 0, 0)) == list(o.brute_force_top_k(list(vals), k))
+    vals = np.array([-5.0, 3.0, 2.0, 9.0, 1.0, -7.0, -6.0])
+    assert o.top_k(vals, 3, 1, 2).tolist() == [0, 5, 6]
+    assert o.top_k(vals, 4, 1, 2).tolist() == [0, 3, 5, 6]
+    assert o.predict(vals, 2, 1, 2).tolist() == [0, 5]
+
+
 ALL_PINS = [pin_dense_equivalence, pin_brute_force_selection, pin_quest_upper_bound, pin_signsplit,
             pin_merge_order_free, pin_repair_invariants, pin_closed_forms, pin_hand_example, pin_ema_closed_form,
-            pin_budget_closed_form, pin_paged_gather, pin_partial_last_block]
+            pin_budget_closed_form, pin_paged_gather, pin_partial_last_block, pin_forced_blocks]

@@ -52,6 +52,18 @@ def _attn_whole_last_block(q_group, keys, values, blocks, block_size, scale):
     return _orig["attention_over_blocks"](q_group, keys, values, blocks, block_size, scale)
 
 
+def _topk_ignores_forced(values, k, n_sink=0, n_local=0):
+    return _orig["top_k"](values, k)
+
+
+def _topk_local_off_by_one(values, k, n_sink=0, n_local=0):
+    n = len(values)
+    idx = np.arange(n)
+    forced = (idx < n_sink) | (idx > n - n_local)
+    rank_value = np.where(forced, 0.0, -np.asarray(values, dtype=np.float64))
+    return np.sort(np.lexsort((idx, rank_value, ~forced))[:k])
+
+
 def _topk_high_ties(values, k):
     n = len(values)
     order = np.lexsort((-np.arange(n), -np.asarray(values, dtype=np.float64)))
@@ -154,7 +166,7 @@ def _gather_identity(cache, table, b, g, n_tokens):
 
 
 _orig = {k: getattr(O, k) for k in ["attention_over_blocks", "prr_output", "ema_update", "choose_budget",
-                                    "block_summaries"]}
+                                    "block_summaries", "top_k"]}
 
 MUTANTS = {
     "quest_drop_kmin": ("quest_scores", _quest_drop_kmin),
@@ -165,6 +177,8 @@ MUTANTS = {
     "summaries_last_window": ("block_summaries", _summaries_last_window),
     "attn_drops_partial_block": ("attention_over_blocks", _attn_whole_last_block),
     "topk_high_ties": ("top_k", _topk_high_ties),
+    "topk_ignores_forced": ("top_k", _topk_ignores_forced),
+    "topk_local_off_by_one": ("top_k", _topk_local_off_by_one),
     "topk_off_by_one": ("top_k", _topk_off_by_one),
     "topk_unsorted": ("top_k", _topk_unsorted),
     "attn_no_scale": ("attention_over_blocks", _attn_no_scale),
