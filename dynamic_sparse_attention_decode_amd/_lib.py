@@ -36,7 +36,8 @@ class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("n_blocks", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("ctx_len", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("ctx_len", ctypes.c_int32), ("sink_blocks", ctypes.c_int32),
+                ("local_blocks", ctypes.c_int32)]
 
     @property
     def group(self) -> int:
@@ -58,13 +59,15 @@ class StepArgs(ctypes.Structure):
 
 
 def make_shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, page_size, n_blocks, dtype,
-               softmax_scale=None, ctx_len=0) -> Shape:
-    """ctx_len: tokens per sequence when the last block is partly filled (0: n_blocks * block_size)."""
+               softmax_scale=None, ctx_len=0, sink_blocks=0, local_blocks=0) -> Shape:
+    """ctx_len: tokens per sequence when the last block is partly filled (0: n_blocks * block_size); sink_blocks,
+    local_blocks: blocks every selection keeps (the first and the last of each sequence)."""
     if isinstance(dtype, torch.dtype):
         dtype = _DT_CODE[dtype]
     pps = n_blocks * block_size // page_size
     scale = head_dim ** -0.5 if softmax_scale is None else softmax_scale
-    return Shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, page_size, n_blocks, pps, dtype, scale, ctx_len)
+    return Shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, page_size, n_blocks, pps, dtype, scale, ctx_len,
+                 sink_blocks, local_blocks)
 
 
 _lib = None

@@ -28,14 +28,15 @@ __global__ __launch_bounds__(kSelSpecThreads) void select_spec_kernel(const floa
                                                            const int32_t* __restrict__ pred, int k_spec,
                                                            float* __restrict__ partials, int64_t spec_total, int Hq,
                                                            int Hkv, int N, int bs, int page, int pps, float qscale,
-                                                           int rows, int last_len) {
+                                                           int rows, int last_len, int sink, int local) {
   const int64_t r = blockIdx.x;
   if (r < n_sel_wg) {
     if (r < rows)
-      topk_row<kSelSpecThreads, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K);
+      topk_row<kSelSpecThreads, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, nullptr,
+                                            Force{0, N, sink, local});
     else
       topk_row<kSelSpecThreads, KPT, false>(ema + (r - rows) * N, nullptr, 0.f, 0, N, Kp_next,
-                                            pred_next + (r - rows) * Kp_next);
+                                            pred_next + (r - rows) * Kp_next, nullptr, Force{0, N, sink, local});
     return;
   }
   const int64_t s = (r - n_sel_wg) * (kSelSpecThreads / 64) + (threadIdx.x >> 6);
@@ -58,17 +59,19 @@ __global__ __launch_bounds__(kSegSpecThreads, 3) void seg_spec_kernel(const floa
                                                            const int32_t* __restrict__ pred, int k_spec,
                                                            float* __restrict__ partials, int spw, int wpr,
                                                            int64_t spec_waves, int Hq, int Hkv, int N, int bs,
-                                                           int page, int pps, float qscale, int rows, int last_len) {
+                                                           int page, int pps, float qscale, int rows, int last_len,
+                                                           int sink, int local) {
   const int64_t r = blockIdx.x;
   if (r < n_seg_wg) {
     const int64_t job = r / S;
     const int seg = (int)(r % S);
     if (job < rows)
       topk_segment<kSegSpecThreads, 8, false>(scores + job * N, nullptr, 0.f, 0, N, K, kSelSpecSeg, seg,
-                                              ct.key + job * ct.cap, ct.idx + job * ct.cap);
+                                              ct.key + job * ct.cap, ct.idx + job * ct.cap, sink, local);
     else
       topk_segment<kSegSpecThreads, 8, false>(ema + (job - rows) * N, nullptr, 0.f, 0, N, Kp_next, kSelSpecSeg, seg,
-                                              cp.key + (job - rows) * cp.cap, cp.idx + (job - rows) * cp.cap);
+                                              cp.key + (job - rows) * cp.cap, cp.idx + (job - rows) * cp.cap, sink,
+                                              local);
     return;
   }
   // speculation as the standalone kernel does it: spw consecutive slots per wave
@@ -111,7 +114,7 @@ static void seg_spec_launch(const prr_shape& s, const float* scores, int K, int3
       scores, K, ema, kp_next, pt.S, n_seg_wg, ct, cp, static_cast<const uint8_t*>(q),
       static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, pred, k_spec, partials, spw, wpr,
       spec_waves, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size, s.pages_per_seq,
-      s.softmax_scale * kLog2e, rows, last_block_len(s));
+      s.softmax_scale * kLog2e, rows, last_block_len(s), s.sink_blocks, s.local_blocks);
   const int cmax = kp_next > 0 && pp.C > pt.C ? pp.C : pt.C;
   const dim3 grid((unsigned)((kp_next > 0 ? 2 : 1) * rows));
 #define PRR_MERGE2(KPT) \
@@ -144,7 +147,8 @@ static void select_spec_launch(const prr_shape& s, const float* scores, int K, i
   select_spec_kernel<KPT, DT, G><<<grid, blk, 0, st>>>(scores, K, sel, ema, kp_next, pred_next, n_sel_wg, qq, kk, vv, \
                                                        table, pred, k_spec, partials, spec_total, s.n_q_heads,       \
                                                        s.n_kv_heads, s.n_blocks, s.block_size, s.page_size,          \
-                                                       s.pages_per_seq, qs, rows, last_block_len(s))
+                                                       s.pages_per_seq, qs, rows, last_block_len(s),            \
+                                                       s.sink_blocks, s.local_blocks)
   // values per thread: a few register sizes cover every row length (larger than needed is correct, just slower)
   if (s.n_blocks <= 4 * kSelSpecThreads)
     PRR_SELSPEC(4);

@@ -21,18 +21,21 @@ __global__ __launch_bounds__(256) void score_kernel(const uint8_t* __restrict__ 
 
 template <int NT, int KPT, bool EMA>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ vals, float* __restrict__ ema,
-                                                  float alpha, int first, int N, int K, int32_t* __restrict__ out) {
+                                                  float alpha, int first, int N, int K, int32_t* __restrict__ out,
+                                                  int sink, int local) {
   const int64_t row = blockIdx.x;
-  topk_row<NT, KPT, EMA>(vals + row * N, EMA ? ema + row * N : nullptr, alpha, first, N, K, out + row * K);
+  topk_row<NT, KPT, EMA>(vals + row * N, EMA ? ema + row * N : nullptr, alpha, first, N, K, out + row * K, nullptr,
+                         Force{0, N, sink, local});
 }
 
 template <int KPT, bool EMA>
 __global__ __launch_bounds__(1024) void topk_seg_kernel(const float* __restrict__ vals, float* __restrict__ ema,
                                                         float alpha, int first, int N, int K, int seg, int64_t cap,
-                                                        uint32_t* __restrict__ ckey, int32_t* __restrict__ cidx) {
+                                                        uint32_t* __restrict__ ckey, int32_t* __restrict__ cidx,
+                                                        int sink, int local) {
   const int64_t row = blockIdx.y;
   topk_segment<1024, KPT, EMA>(vals + row * N, EMA ? ema + row * N : nullptr, alpha, first, N, K, seg, blockIdx.x,
-                               ckey + row * cap, cidx + row * cap);
+                               ckey + row * cap, cidx + row * cap, sink, local);
 }
 
 template <int KPT>
@@ -71,14 +74,14 @@ prr_status launch_score(const prr_shape& s, const void* q, const void* summ, flo
 
 template <bool EMA>
 static void topk_dispatch(int kpt, dim3 grid, const float* vals, float* ema, float alpha, int first, int N, int K,
-                          int32_t* out, hipStream_t st) {
+                          int sink, int local, int32_t* out, hipStream_t st) {
   switch (kpt) {
-    case 1: topk_kernel<1024, 1, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
-    case 2: topk_kernel<1024, 2, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
-    case 4: topk_kernel<1024, 4, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
-    case 8: topk_kernel<1024, 8, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
-    case 16: topk_kernel<1024, 16, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
-    default: topk_kernel<1024, 32, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out); break;
+    case 1: topk_kernel<1024, 1, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local); break;
+    case 2: topk_kernel<1024, 2, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local); break;
+    case 4: topk_kernel<1024, 4, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local); break;
+    case 8: topk_kernel<1024, 8, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local); break;
+    case 16: topk_kernel<1024, 16, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local); break;
+    default: topk_kernel<1024, 32, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local); break;
   }
 }
 
@@ -107,7 +110,8 @@ static void topk_split_launch(const prr_shape& s, const float* vals, float* ema,
   const int rows = s.batch * s.n_kv_heads;
   const TopkSplit p = topk_split(s.n_blocks, K, kTopkSeg1024);
   topk_seg_kernel<4, EMA><<<dim3((unsigned)p.S, (unsigned)rows), 1024, 0, st>>>(vals, ema, alpha, first, s.n_blocks,
-                                                                                K, p.seg, c.cap, c.key, c.idx);
+                                                                                K, p.seg, c.cap, c.key, c.idx,
+                                                                                s.sink_blocks, s.local_blocks);
   const dim3 grid((unsigned)rows);
   switch (topk_kpt(p.C)) {
     case 1: case 2: topk_merge_kernel<2><<<grid, 1024, 0, st>>>(c.key, c.idx, c.cap, p.C, K, out); break;
@@ -131,9 +135,11 @@ prr_status launch_topk(const prr_shape& s, const float* values, float* ema, floa
     const int kpt = topk_kpt(s.n_blocks);
     const dim3 grid((unsigned)(s.batch * s.n_kv_heads));
     if (ema)
-      topk_dispatch<true>(kpt, grid, values, ema, alpha, first, s.n_blocks, k, out_idx, stream);
+      topk_dispatch<true>(kpt, grid, values, ema, alpha, first, s.n_blocks, k, s.sink_blocks, s.local_blocks,
+                          out_idx, stream);
     else
-      topk_dispatch<false>(kpt, grid, values, nullptr, alpha, first, s.n_blocks, k, out_idx, stream);
+      topk_dispatch<false>(kpt, grid, values, nullptr, alpha, first, s.n_blocks, k, s.sink_blocks, s.local_blocks,
+                           out_idx, stream);
   }
   trace_end(kid, stream);
   return check_launch(ema ? "ema_predict" : "select_topk");

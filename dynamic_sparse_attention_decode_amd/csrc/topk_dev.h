@@ -201,12 +201,21 @@ __device__ inline void select_top(const uint32_t (&key)[NK], ValidFn&& valid, in
   write_selected<NT, NK>(key, valid, R, K, L, emit);
 }
 
+// Forced blocks of a row of n blocks: the first `sink` and the last `local` (attention sinks and the local window,
+// StreamingLLM in the PRR reference list) take the largest key, so they rank above every score (an fp32 score's key
+// is below 0xFFFFFFFF, which only a NaN would reach) and among themselves by index. base: the row position of the
+// values at hand (a segment's offset).
+struct Force {
+  int base = 0, n = 0, sink = 0, local = 0;
+  __device__ bool operator()(int i) const { return base + i < sink || base + i >= n - local; }
+};
+
 // Top-K of one row of N <= NT * KPT values (optionally after the EMA update e = alpha e + (1 - alpha) v, written
 // back), by one workgroup of NT threads (256 <= NT <= 1024): emit(pos, i, key) receives the K selected row
 // positions i in ascending order, with their keys.
 template <int NT, int KPT, bool EMA, typename EmitFn>
 __device__ void topk_row_emit(const float* __restrict__ v, float* __restrict__ e_row, float alpha, int first, int N,
-                              int K, EmitFn&& emit) {
+                              int K, EmitFn&& emit, Force force = Force{}) {
   static_assert(NT >= 256 && NT <= 1024 && NT % 64 == 0, "workgroup size");
   __shared__ TopkLds L;
   const int i0 = threadIdx.x * KPT;
@@ -254,7 +263,7 @@ __device__ void topk_row_emit(const float* __restrict__ v, float* __restrict__ e
 
   uint32_t key[KPT];
 #pragma unroll
-  for (int k = 0; k < KPT; ++k) key[k] = f2key(x[k]);
+  for (int k = 0; k < KPT; ++k) key[k] = force(i0 + k) ? 0xFFFFFFFFu : f2key(x[k]);
   auto valid = [&](int k) { return i0 + k < N; };
   select_top<NT, KPT>(key, valid, K, L, [&](uint32_t pos, int j) { emit(pos, i0 + j, key[j]); });
 }
@@ -262,11 +271,11 @@ __device__ void topk_row_emit(const float* __restrict__ v, float* __restrict__ e
 // Top-K of one row into orow (and lds_out, an LDS copy, when given) as K ascending indices.
 template <int NT, int KPT, bool EMA>
 __device__ inline void topk_row(const float* __restrict__ v, float* __restrict__ e_row, float alpha, int first, int N,
-                                int K, int32_t* __restrict__ orow, int32_t* lds_out = nullptr) {
+                                int K, int32_t* __restrict__ orow, int32_t* lds_out, Force force) {
   topk_row_emit<NT, KPT, EMA>(v, e_row, alpha, first, N, K, [&](uint32_t pos, int i, uint32_t) {
     orow[pos] = i;
     if (lds_out) lds_out[pos] = i;
-  });
+  }, force);
 }
 
 // ---- long rows: segments, then a merge ---------------------------------------------------------------------------
@@ -276,7 +285,7 @@ __device__ inline void topk_row(const float* __restrict__ v, float* __restrict__
 template <int NT, int KPT, bool EMA>
 __device__ inline void topk_segment(const float* __restrict__ v_row, float* __restrict__ e_row, float alpha, int first,
                                     int N, int K, int seg, int s, uint32_t* __restrict__ ckey_row,
-                                    int32_t* __restrict__ cidx_row) {
+                                    int32_t* __restrict__ cidx_row, int sink, int local) {
   const int base = s * seg;
   const int n = min(seg, N - base);
   const int kc = min(K, seg);
@@ -286,7 +295,8 @@ __device__ inline void topk_segment(const float* __restrict__ v_row, float* __re
                               [&](uint32_t pos, int i, uint32_t key) {
                                 ok[pos] = key;
                                 oi[pos] = base + i;
-                              });
+                              },
+                              Force{base, N, sink, local});
 }
 
 // Top-K of a row's C candidates (C <= NT * KPT) into orow (and lds_out) as K ascending block indices.

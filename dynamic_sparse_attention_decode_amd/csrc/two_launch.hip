@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
     int32_t* __restrict__ pred_next, const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, const int32_t* __restrict__ pred, int k_spec,
     float* __restrict__ partials, int64_t spec_total, MissedWs ws, int32_t* __restrict__ n_missed, int Hq, int Hkv,
-    int N, int bs, int page, int pps, float qscale, int rows, int n_pwg, int last_len) {
+    int N, int bs, int page, int pps, float qscale, int rows, int n_pwg, int last_len, int sink, int local) {
   using W = Tile<DT, G>;
   constexpr int NW = kSRThreads / 64;
   constexpr int D = W::D;
@@ -102,10 +102,11 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
   }
   if (r >= rows) {   // next step's predicted set
     const int64_t rr = r - rows;
-    topk_row<kSRThreads, KPT, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp_next, pred_next + rr * Kp_next);
+    topk_row<kSRThreads, KPT, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp_next, pred_next + rr * Kp_next, nullptr,
+                                     Force{0, N, sink, local});
     return;
   }
-  topk_row<kSRThreads, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, s_T);
+  topk_row<kSRThreads, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, s_T, Force{0, N, sink, local});
 
   // ---- T against P_t: slot of every entry of T in P_t (bisection when P_t is ascending) -------------------------
   const int b = (int)(r / Hkv), g = (int)(r % Hkv);
@@ -376,7 +377,7 @@ static void select_missed_launch(const prr_shape& s, const float* scores, int K,
                                                          table, pred, k_spec, partials, spec_total, ws, n_missed,   \
                                                          s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size,       \
                                                          s.page_size, s.pages_per_seq, qs, rows, n_pwg,             \
-                                                         last_block_len(s))
+                                                         last_block_len(s), s.sink_blocks, s.local_blocks)
   trace_begin(PRR_KERNEL_SELECT_TOPK, st);
   if (s.n_blocks <= 4 * kSRThreads)
     PRR_SELMISS(4);

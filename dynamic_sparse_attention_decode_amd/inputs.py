@@ -60,6 +60,8 @@ class Workload:
     dtype: str = "bf16"          # storage dtype of q, K, V and the block summaries: "f32" | "bf16" | "f16"
     hot_bias: float = 2.0
     seed: int = 20261203
+    sink_blocks: int = 0         # forced blocks of every selection: the first sink_blocks and the last local_blocks
+    local_blocks: int = 0
 
     # ---- derived sizes -------------------------------------------------------------------------------------------
     @property

@@ -74,6 +74,9 @@ typedef struct {
   int32_t dtype;        /* prr_dtype */
   float softmax_scale;  /* typically 1/sqrt(head_dim) */
   int32_t ctx_len;      /* tokens per sequence (0: n_blocks * block_size) */
+  int32_t sink_blocks;  /* forced blocks: the first sink_blocks and the last local_blocks of every sequence rank   */
+  int32_t local_blocks; /* above all others in every top-K (true set and prediction), among themselves by index; */
+                        /* sink_blocks + local_blocks <= n_blocks (0, 0: plain top-K)                            */
 } prr_shape;
 
 /* Quest block summaries (PRR reference list, Quest): for every (b, kv head g, block n), the elementwise min and max

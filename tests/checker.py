@@ -18,13 +18,27 @@ REL_GAP = 1e-4
 TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2e-2}
 
 
-def check_selection(gpu_idx, oracle_scores, k: int, rel: float = REL_GAP):
-    """Returns (exact_required, banded_ok). Raises AssertionError if the GPU set is invalid."""
+def check_selection(gpu_idx, oracle_scores, k: int, rel: float = REL_GAP, n_sink: int = 0, n_local: int = 0):
+    """Returns whether exact equality was required. Raises AssertionError if the GPU set is invalid. Forced blocks
+    (the first n_sink and last n_local) must all be in the set (or, when k is smaller, the set is the first k of
+    them); the rest of the set is judged among the other blocks by the rule above."""
     g = np.asarray(gpu_idx, dtype=np.int64)
     s = np.asarray(oracle_scores, dtype=np.float64)
     assert g.shape == (k,), g.shape
     assert np.all(np.diff(g) > 0), "indices not strictly ascending"
     assert g.min() >= 0 and g.max() < len(s), "index out of range"
+    if n_sink or n_local:
+        n = len(s)
+        forced = np.array([i < n_sink or i >= n - n_local for i in range(n)])
+        f_idx = np.flatnonzero(forced)
+        if k <= len(f_idx):
+            assert np.array_equal(g, f_idx[:k]), (g, f_idx[:k])
+            return True
+        assert set(f_idx) <= set(g.tolist()), "a forced block is missing"
+        rest = np.flatnonzero(~forced)
+        pos = {int(b): i for i, b in enumerate(rest)}
+        g_rest = np.asarray([pos[int(b)] for b in g if not forced[b]], dtype=np.int64)
+        return check_selection(g_rest, s[rest], k - len(f_idx), rel)
     ref = O.top_k(s, k)
     _, _, gap = O.boundary_gap(s, k)
     if gap > rel:

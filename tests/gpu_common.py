@@ -34,7 +34,8 @@ SMALL = ["tiny_f32_4k", "llama3_8b_32k", "long_ctx_131k_b4", "paged_b32_64k", "m
 def shape_of(w: Workload) -> L.Shape:
     return L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, w.n_blocks,
                         {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[w.dtype], w.scale,
-                        ctx_len=w.ctx if w.ctx % w.block_size else 0)
+                        ctx_len=w.ctx if w.ctx % w.block_size else 0, sink_blocks=w.sink_blocks,
+                        local_blocks=w.local_blocks)
 
 
 def ragged(w: Workload, short: int) -> Workload:

@@ -46,14 +46,14 @@ def _check_step(w, ov, t, h, k_spec, ema_ref):
             keys = ov.keys(b, g)
             kmin, kmax = O.block_summaries(keys, w.block_size)
             s = O.quest_scores(qg, kmin, kmax)
-            check_selection(h["sel"][b, g], s, w.top_k)
+            check_selection(h["sel"][b, g], s, w.top_k, n_sink=w.sink_blocks, n_local=w.local_blocks)
             ref = O.attention_over_blocks(qg, keys, ov.values(b, g), h["sel"][b, g], w.block_size, w.scale)
             e = max_abs(h["out"][b, g * G:(g + 1) * G], ref)
             assert e <= TOL[w.dtype], (t, b, g, e)
             # oracle EMA over the oracle's scores; the GPU's predicted set must be valid for it
             prev = ema_ref.get((b, g)) if t > 0 else None
             if t > 0 and k_spec:
-                check_selection(h["pred"][b, g], prev, k_spec)
+                check_selection(h["pred"][b, g], prev, k_spec, n_sink=w.sink_blocks, n_local=w.local_blocks)
                 missed = len(set(h["sel"][b, g]) - set(h["pred"][b, g]))
                 assert h["nm"][b, g] == missed
             elif t == 0 or not k_spec:
@@ -287,3 +287,16 @@ def test_decode_with_appends(name, mode):
         _check_step(w, view, t, h, layer.k_spec, ema_ref)
     assert layer.shape.ctx_len == w.ctx + w.steps - 1
     layer.close()
+
+
+@pytest.mark.parametrize("name,mode", [("tiny_f32_4k", "prr_fused"), ("llama3_8b_32k", "prr_2stream"),
+                                       ("paged_b32_64k", "prr_fused"), ("million_token", "serialized"),
+                                       ("long_ctx_131k_b4", "prr_1stream")])
+def test_forced_blocks_decode(name, mode):
+    """Attention sinks and a local window (one sink block, three local blocks) forced into every selection and
+    prediction: each step against the oracle with the same forced blocks."""
+    w = small(name).replace(sink_blocks=1, local_blocks=3, steps=4)
+    print(f"[case] forced blocks decode {name} {mode}", flush=True)
+    inp = make_inputs(w, device="cuda")
+    kp = max(w.k_spec) or w.top_k
+    run_layer(w, inp, kp, mode, ov=OracleView(inp))

@@ -510,3 +510,32 @@ def test_partial_last_block_summaries_and_append(name, short):
             assert torch.equal(inp.k_cache[phys, g, pos % page].cpu(), kn[b, g]), (i, b, g)
             assert torch.equal(inp.v_cache[phys, g, pos % page].cpu(), vn[b, g]), (i, b, g)
         check_summaries(f"append {i}")
+
+
+@pytest.mark.parametrize("n_blocks", [300, 20001])
+def test_topk_forced_blocks(n_blocks):
+    """Forced blocks (the first sink_blocks and last local_blocks) in every top-K launch: prr_ema_predict and
+    prr_select_speculate (one workgroup per row, and by segments on long rows with a workspace), for K below, at and
+    above the number of forced blocks, on values with many ties: equal to the oracle's rule."""
+    N, rows = n_blocks, 2
+    rng = np.random.default_rng(47)
+    print(f"[case] forced blocks N={N}", flush=True)
+    for sink, local in [(1, 0), (0, 3), (2, 5)]:
+        s = L.make_shape(1, 8, rows, 128, 16, 16, N, L.BF16, sink_blocks=sink, local_blocks=local)
+        ws = torch.zeros((L.workspace_bytes(s, 64) // 4 + 1,), dtype=torch.float32, device="cuda")
+        vals = (np.round(rng.standard_normal((rows, N)) * 4) + 0.25).astype(np.float32)
+        vd = torch.as_tensor(vals[None], device="cuda").contiguous()
+        em = torch.zeros_like(vd)
+        for k in sorted({1, sink + local, sink + local + 1, 64, 300}):
+            if k < 1 or k > N:
+                continue
+            ref = np.stack([O.top_k(vals[r].astype(np.float64), k, sink, local) for r in range(rows)])
+            for w_ in (None, ws):
+                out = torch.full((1, rows, k), -1, dtype=torch.int32, device="cuda")
+                L.ema_predict(s, vd, em, 0.5, True, k, out, workspace=w_)
+                sel = torch.full((1, rows, k), -1, dtype=torch.int32, device="cuda")
+                pn = torch.full((1, rows, k), -1, dtype=torch.int32, device="cuda")
+                L.select_speculate(s, vd, k, sel, em, k, pn, workspace=w_)
+                torch.cuda.synchronize()
+                for name, got in (("ema_predict", out), ("select T", sel), ("select P", pn)):
+                    assert np.array_equal(got.cpu().numpy()[0], ref), (name, sink, local, k, w_ is not None)
