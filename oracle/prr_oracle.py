@@ -90,6 +90,22 @@ def quest_scores_signsplit(q_group: np.ndarray, kmin: np.ndarray, kmax: np.ndarr
     return kmax @ qp + kmin @ qn
 
 
+def block_means(keys: np.ndarray, block_size: int) -> np.ndarray:
+    """Mean key of each block over the tokens it holds: [N, D] (float64)."""
+    n_tok = len(keys)
+    n_blk = -(-n_tok // block_size)
+    return np.stack([np.asarray(keys[n * block_size:(n + 1) * block_size], dtype=np.float64).mean(axis=0)
+                     for n in range(n_blk)])
+
+
+def mean_key_scores(q_group: np.ndarray, keys: np.ndarray, block_size: int) -> np.ndarray:
+    """A second scorer (representative-key block scores; the PRR abstract speaks of representative DSA methods):
+    s[n] = sum over the group's heads h of q_h . mean of the block's keys, i.e. the block's average group-summed
+    logit before scaling."""
+    means = block_means(keys, block_size)
+    return means @ np.asarray(q_group, dtype=np.float64).sum(axis=0)
+
+
 # ------------------------------------------------------------------------------------------------------------------
 # top-K block selection (PRR abstract: attend only to the top-K blocks)
 # ------------------------------------------------------------------------------------------------------------------

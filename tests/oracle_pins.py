@@ -330,6 +330,29 @@ def pin_forced_blocks(o):
     assert o.predict(vals, 2, 1, 2).tolist() == [0, 5]
 
 
+def pin_mean_key_scores(o):
+    """The mean-key scorer: equal to the average over each block's tokens of the group-summed exact logits q . k
+    (per token, a different order of summation); constant keys give that key's dot product; one-token blocks give
+    the exact dot product; a partial last block averages over the tokens it holds; the Quest bound is never below
+    it (a mean of dot products cannot exceed their maximum, which the bound covers)."""
+    rng = np.random.default_rng(23)
+    for (n_tok, bs, d, g) in [(24, 4, 6, 2), (19, 8, 5, 3), (7, 1, 4, 1)]:
+        q = rng.standard_normal((g, d))
+        k = rng.standard_normal((n_tok, d))
+        s = o.mean_key_scores(q, k, bs)
+        per_tok = np.array([sum(float(q[h] @ k[i]) for h in range(g)) for i in range(n_tok)])
+        nb = -(-n_tok // bs)
+        ref = np.array([per_tok[n * bs:(n + 1) * bs].mean() for n in range(nb)])
+        assert np.allclose(s, ref, rtol=0, atol=1e-12)
+        kmin, kmax = o.block_summaries(k, bs)
+        assert np.all(o.quest_scores(q, kmin, kmax) >= s - 1e-12)
+    c = rng.standard_normal(5)
+    q = rng.standard_normal((2, 5))
+    s = o.mean_key_scores(q, np.tile(c, (12, 1)), 4)
+    assert np.allclose(s, q.sum(axis=0) @ c, rtol=0, atol=1e-13)
+
+
 ALL_PINS = [pin_dense_equivalence, pin_brute_force_selection, pin_quest_upper_bound, pin_signsplit,
             pin_merge_order_free, pin_repair_invariants, pin_closed_forms, pin_hand_example, pin_ema_closed_form,
-            pin_budget_closed_form, pin_paged_gather, pin_partial_last_block, pin_forced_blocks]
+            pin_budget_closed_form, pin_paged_gather, pin_partial_last_block, pin_forced_blocks,
+            pin_mean_key_scores]

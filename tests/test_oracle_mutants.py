@@ -64,6 +64,14 @@ def _topk_local_off_by_one(values, k, n_sink=0, n_local=0):
     return np.sort(np.lexsort((idx, rank_value, ~forced))[:k])
 
 
+def _mean_scores_first_head(q_group, keys, block_size):
+    return _orig["mean_key_scores"](q_group[:1], keys, block_size)
+
+
+def _mean_scores_sum_not_mean(q_group, keys, block_size):
+    return _orig["mean_key_scores"](q_group, keys, block_size) * block_size
+
+
 def _topk_high_ties(values, k):
     n = len(values)
     order = np.lexsort((-np.arange(n), -np.asarray(values, dtype=np.float64)))
@@ -166,7 +174,7 @@ def _gather_identity(cache, table, b, g, n_tokens):
 
 
 _orig = {k: getattr(O, k) for k in ["attention_over_blocks", "prr_output", "ema_update", "choose_budget",
-                                    "block_summaries", "top_k"]}
+                                    "block_summaries", "top_k", "mean_key_scores"]}
 
 MUTANTS = {
     "quest_drop_kmin": ("quest_scores", _quest_drop_kmin),
@@ -178,6 +186,8 @@ MUTANTS = {
     "attn_drops_partial_block": ("attention_over_blocks", _attn_whole_last_block),
     "topk_high_ties": ("top_k", _topk_high_ties),
     "topk_ignores_forced": ("top_k", _topk_ignores_forced),
+    "mean_scores_first_head": ("mean_key_scores", _mean_scores_first_head),
+    "mean_scores_sum_not_mean": ("mean_key_scores", _mean_scores_sum_not_mean),
     "topk_local_off_by_one": ("top_k", _topk_local_off_by_one),
     "topk_off_by_one": ("top_k", _topk_off_by_one),
     "topk_unsorted": ("top_k", _topk_unsorted),
