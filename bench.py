@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--budget-profile", action="store_true",
                     help="instead of the step benchmark: measure the selection time over a grid of block counts and "
                          "the speculation time over a grid of budgets K', and print the profiled budget K'*")
+    ap.add_argument("--scorer", default="quest", choices=["quest", "mean"], help="block scorer")
     ap.add_argument("--sink", type=int, default=0, help="attention-sink blocks forced into every selection")
     ap.add_argument("--local", type=int, default=0, help="local-window blocks (the last ones) forced likewise")
     ap.add_argument("--other-modes", default="all",
@@ -85,8 +86,8 @@ def main():
         torch.cuda.synchronize()
         del buf, sink
     w = WORKLOADS[a.workload]
-    if a.sink or a.local:
-        w = w.replace(sink_blocks=a.sink, local_blocks=a.local)
+    if a.sink or a.local or a.scorer != "quest":
+        w = w.replace(sink_blocks=a.sink, local_blocks=a.local, scorer=a.scorer)
     if a.budget_profile:
         budget_profile(w)
         return
@@ -97,7 +98,7 @@ def main():
     shape = L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, w.n_blocks,
                          {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[w.dtype], w.scale,
                          ctx_len=w.ctx if w.ctx % w.block_size else 0, sink_blocks=w.sink_blocks,
-                         local_blocks=w.local_blocks)
+                         local_blocks=w.local_blocks, scorer=L.SCORER_MEAN if w.scorer == "mean" else L.SCORER_QUEST)
     e = w.elem_bytes
     kv_layer = 2 * w.n_pages * w.n_kv_heads * w.page_size * w.head_dim * e
     summ_layer = w.batch * w.n_kv_heads * w.n_blocks * 2 * w.head_dim * e
@@ -376,7 +377,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "ctx": w.ctx, "block_size": w.block_size, "page_size": w.page_size,
                    "top_k": w.top_k, "k_spec": kspec, "alpha": w.alpha, "mode": a.mode,
-                   "sink_blocks": w.sink_blocks, "local_blocks": w.local_blocks,
+                   "sink_blocks": w.sink_blocks, "local_blocks": w.local_blocks, "scorer": w.scorer,
                    "layers_rotated": n_layers, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": dominant, "hip_kernels": HIP_KERNELS.get((a.mode, dominant), dominant),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,

@@ -14,6 +14,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libprr.so")
 
 F32, BF16, F16 = 0, 1, 2
+SCORER_QUEST, SCORER_MEAN = 0, 1
 MODE_SERIALIZED, MODE_ONE_STREAM, MODE_TWO_STREAM, MODE_FUSED, MODE_SERIALIZED_FUSED = 0, 1, 2, 3, 4
 _DT_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
@@ -37,7 +38,7 @@ class Shape(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("n_blocks", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("ctx_len", ctypes.c_int32), ("sink_blocks", ctypes.c_int32),
-                ("local_blocks", ctypes.c_int32)]
+                ("local_blocks", ctypes.c_int32), ("scorer", ctypes.c_int32)]
 
     @property
     def group(self) -> int:
@@ -59,15 +60,16 @@ class StepArgs(ctypes.Structure):
 
 
 def make_shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, page_size, n_blocks, dtype,
-               softmax_scale=None, ctx_len=0, sink_blocks=0, local_blocks=0) -> Shape:
+               softmax_scale=None, ctx_len=0, sink_blocks=0, local_blocks=0, scorer=0) -> Shape:
     """ctx_len: tokens per sequence when the last block is partly filled (0: n_blocks * block_size); sink_blocks,
-    local_blocks: blocks every selection keeps (the first and the last of each sequence)."""
+    local_blocks: blocks every selection keeps (the first and the last of each sequence); scorer: SCORER_QUEST or
+    SCORER_MEAN."""
     if isinstance(dtype, torch.dtype):
         dtype = _DT_CODE[dtype]
     pps = n_blocks * block_size // page_size
     scale = head_dim ** -0.5 if softmax_scale is None else softmax_scale
     return Shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, page_size, n_blocks, pps, dtype, scale, ctx_len,
-                 sink_blocks, local_blocks)
+                 sink_blocks, local_blocks, scorer)
 
 
 _lib = None

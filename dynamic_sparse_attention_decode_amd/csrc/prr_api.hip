@@ -149,6 +149,7 @@ static prr_status check_shape(const prr_shape* s) {
     set_error("ctx_len %d not in ((n_blocks - 1) * block_size, n_blocks * block_size]", s->ctx_len);
     return PRR_EINVAL;
   }
+  if (s->scorer != 0 && s->scorer != 1) { set_error("unknown scorer %d", s->scorer); return PRR_EINVAL; }
   if (s->sink_blocks < 0 || s->local_blocks < 0 || (int64_t)s->sink_blocks + s->local_blocks > s->n_blocks) {
     set_error("sink_blocks %d, local_blocks %d: need both >= 0 and their sum <= n_blocks", s->sink_blocks,
               s->local_blocks);

@@ -49,6 +49,8 @@ void trace_end(int kid, hipStream_t stream);
     }                                                                   \
   } while (0)
 
+constexpr int kScorerQuest = 0, kScorerMean = 1;
+
 // Tokens of the last block (block_size unless the sequence ends inside it).
 inline int last_block_len(const prr_shape& s) {
   return s.ctx_len > 0 ? s.ctx_len - (s.n_blocks - 1) * s.block_size : s.block_size;

@@ -1,5 +1,5 @@
-// score_dev.h — Quest block scoring as a streaming GEMV (PRR reference list, Quest), optionally fused with the EMA
-// predictor's update (PRR abstract: a light predictor built on an exponential moving average).
+// score_dev.h — Quest block scoring as a streaming GEMV (PRR reference list, Quest), or mean-key scoring, optionally
+// fused with the EMA predictor's update (PRR abstract: a light predictor built on an exponential moving average).
 //
 // s[b,g,n] = sum_d Qpos_d * kmax[n,d] + Qneg_d * kmin[n,d] with Qpos_d = sum_h max(q_hd, 0) and
 // Qneg_d = sum_h min(q_hd, 0) over the group's query heads. Because kmin <= kmax, max(q*kmin, q*kmax) equals
@@ -65,6 +65,79 @@ __device__ inline void score_chunk(int bx, int bg, const uint8_t* __restrict__ q
       }
     }
   }
+}
+
+// Mean-key scores (the second scorer) of blocks [bx * chunk, (bx + 1) * chunk) of row bg: s[n] = <sum_h q_h, mean_n>
+// with the block's mean key stored in fp32 in its summary slot (dims 64 * half + 4 * col .. + 3 at byte
+// 256 * half + 16 * col; with fp32 storage D = 64 and only the first half is used). Same wave layout, fold and EMA
+// update as score_chunk.
+template <int DT, int G, bool EMA>
+__device__ inline void score_chunk_mean(int bx, int bg, const uint8_t* __restrict__ q,
+                                        const uint8_t* __restrict__ summ, float* __restrict__ scores, int Hq, int Hkv,
+                                        int N, int chunk, float* __restrict__ ema, float alpha, int first) {
+  constexpr int U = 8;   // wave loads in flight per lane
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int col = lane & 15, half = (lane >> 4) & 1, pair = lane >> 5;
+  const bool used = DT != kF32 || half == 0;
+
+  float coef[4] = {0.f, 0.f, 0.f, 0.f};
+  if (used) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint8_t* qh = q + ((int64_t)b * Hq + g * G + h) * kRowBytes;
+      float x[Vec<DT>::n];
+      if constexpr (DT == kF32) {
+        Vec<DT>::to_f32(ld16(qh + col * 16), x);
+      } else {   // the 4 16-bit values at dims 64 * half + 4 * col
+        const uint2 w = *reinterpret_cast<const uint2*>(qh + (64 * half + 4 * col) * 2);
+        Vec<DT>::to_f32(make_uint4(w.x, w.y, 0u, 0u), x);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) coef[e] += x[e];
+    }
+  }
+
+  const int c0 = bx * chunk;
+  const int c1 = min(N, c0 + chunk);
+  const uint8_t* base = summ + (int64_t)bg * N * (2 * kRowBytes) + half * kRowBytes + col * 16;
+  float* srow = scores + (int64_t)bg * N;
+  float* erow = EMA ? ema + (int64_t)bg * N : nullptr;
+  const bool owner = (lane & 31) == 0;
+  for (int n0 = c0 + wave * 2 + pair; n0 < c1; n0 += 8 * U) {
+    uint4 v[U];
+    float e_old[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int n = n0 + 8 * u;
+      v[u] = (used && n < c1) ? ld16_stream(base + (int64_t)n * (2 * kRowBytes)) : make_uint4(0, 0, 0, 0);
+      e_old[u] = (EMA && !first && owner && n < c1) ? erow[n] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float s = coef[0] * __uint_as_float(v[u].x);
+      s = fmaf(coef[1], __uint_as_float(v[u].y), s);
+      s = fmaf(coef[2], __uint_as_float(v[u].z), s);
+      s = fmaf(coef[3], __uint_as_float(v[u].w), s);
+      s = sum_xor16(row_sum16(s));
+      const int n = n0 + 8 * u;
+      if (owner && n < c1) {
+        srow[n] = s;
+        if (EMA) erow[n] = first ? s : fmaf(alpha, e_old[u], (1.f - alpha) * s);
+      }
+    }
+  }
+}
+
+// The shape's scorer over one chunk of a row.
+template <int DT, int G, bool EMA>
+__device__ inline void score_any(int scorer, int bx, int bg, const uint8_t* __restrict__ q,
+                                 const uint8_t* __restrict__ summ, float* __restrict__ scores, int Hq, int Hkv, int N,
+                                 int chunk, float* __restrict__ ema, float alpha, int first) {
+  if (scorer == kScorerMean)
+    score_chunk_mean<DT, G, EMA>(bx, bg, q, summ, scores, Hq, Hkv, N, chunk, ema, alpha, first);
+  else
+    score_chunk<DT, G, EMA>(bx, bg, q, summ, scores, Hq, Hkv, N, chunk, ema, alpha, first);
 }
 
 // Blocks per scoring workgroup: a multiple of 64 (one unrolled wave round), sized for about 2048 workgroups.

@@ -15,8 +15,8 @@ namespace prr {
 template <int DT, int G, bool EMA>
 __global__ __launch_bounds__(256) void score_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ summ,
                                                     float* __restrict__ scores, int Hq, int Hkv, int N, int chunk,
-                                                    float* __restrict__ ema, float alpha, int first) {
-  score_chunk<DT, G, EMA>(blockIdx.x, blockIdx.y, q, summ, scores, Hq, Hkv, N, chunk, ema, alpha, first);
+                                                    float* __restrict__ ema, float alpha, int first, int scorer) {
+  score_any<DT, G, EMA>(scorer, blockIdx.x, blockIdx.y, q, summ, scores, Hq, Hkv, N, chunk, ema, alpha, first);
 }
 
 template <int NT, int KPT, bool EMA>
@@ -58,10 +58,10 @@ static void score_launch(const prr_shape& s, const void* q, const void* summ, fl
   const auto* sm = static_cast<const uint8_t*>(summ);
   if (ema)
     score_kernel<DT, G, true><<<grid, blk, 0, st>>>(qq, sm, scores, s.n_q_heads, s.n_kv_heads, s.n_blocks, chunk,
-                                                    ema, alpha, first);
+                                                    ema, alpha, first, s.scorer);
   else
     score_kernel<DT, G, false><<<grid, blk, 0, st>>>(qq, sm, scores, s.n_q_heads, s.n_kv_heads, s.n_blocks, chunk,
-                                                     nullptr, 0.f, 0);
+                                                     nullptr, 0.f, 0, s.scorer);
 }
 
 prr_status launch_score(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema, float alpha,

@@ -18,7 +18,7 @@ __global__ __launch_bounds__(256) void summaries_kernel(const uint8_t* __restric
                                                         const int32_t* __restrict__ table,
                                                         const int32_t* __restrict__ ids, int64_t n_jobs,
                                                         int64_t n_total, uint8_t* __restrict__ summ, int Hkv, int N,
-                                                        int bs, int page, int pps, int last_len) {
+                                                        int bs, int page, int pps, int last_len, int scorer) {
   using V = Vec<DT>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t job = (int64_t)blockIdx.x * 4 + wave;
@@ -32,12 +32,38 @@ __global__ __launch_bounds__(256) void summaries_kernel(const uint8_t* __restric
   const int row = lane >> 4, col = lane & 15;
   const int32_t* trow = table + (int64_t)b * pps;
 
+  const int tok0 = n * bs;
+  const int len = block_len(n, N, bs, last_len);
+  uint8_t* slot = summ + flat * 2 * kRowBytes;
+  if (scorer == kScorerMean) {   // fp32 mean key: lane col sums dims VE * col .. over its row's tokens, then folds
+    float sm[V::n];
+#pragma unroll
+    for (int e = 0; e < V::n; ++e) sm[e] = 0.f;
+    for (int t = 0; t < len; t += 4) {
+      if (t + row >= len) break;
+      const int tok = tok0 + t + row;
+      const int64_t phys = trow[tok / page];
+      float x[V::n];
+      V::to_f32(ld16(k_cache + ((phys * Hkv + g) * page + (tok % page)) * (int64_t)kRowBytes + col * 16), x);
+#pragma unroll
+      for (int e = 0; e < V::n; ++e) sm[e] += x[e];
+    }
+    const float inv = 1.f / (float)len;
+#pragma unroll
+    for (int e = 0; e < V::n; ++e) sm[e] = sum_xor32(sum_xor16(sm[e])) * inv;
+    if (row == 0) {
+#pragma unroll
+      for (int e = 0; e < V::n; e += 4)
+        st16(slot + (col * V::n + e) * 4, make_uint4(__float_as_uint(sm[e]), __float_as_uint(sm[e + 1]),
+                                                     __float_as_uint(sm[e + 2]), __float_as_uint(sm[e + 3])));
+    } else if (row == 1 && V::n * 16 * 4 < 2 * kRowBytes) {   // fp32 storage: the second half of the slot is unused
+      st16(slot + kRowBytes + col * 16, make_uint4(0u, 0u, 0u, 0u));
+    }
+    return;
+  }
   float mn[V::n], mx[V::n];
 #pragma unroll
   for (int e = 0; e < V::n; ++e) { mn[e] = __builtin_huge_valf(); mx[e] = -__builtin_huge_valf(); }
-
-  const int tok0 = n * bs;
-  const int len = block_len(n, N, bs, last_len);
 #pragma unroll 4
   for (int t = 0; t < len; t += 4) {
     if (t + row >= len) break;   // rows past the sequence's end (only in its last block)
@@ -67,7 +93,7 @@ __global__ __launch_bounds__(256) void append_kernel(const uint8_t* __restrict__
                                                      const uint8_t* __restrict__ v_new, uint8_t* __restrict__ k_cache,
                                                      uint8_t* __restrict__ v_cache, const int32_t* __restrict__ table,
                                                      uint8_t* __restrict__ summ, int rows, int Hkv, int N, int bs,
-                                                     int page, int pps, int pos) {
+                                                     int page, int pps, int pos, int scorer) {
   using V = Vec<DT>;
   const int r = (int)((blockIdx.x * 256 + threadIdx.x) >> 4);   // (b, g) row
   if (r >= rows) return;
@@ -78,7 +104,34 @@ __global__ __launch_bounds__(256) void append_kernel(const uint8_t* __restrict__
   const uint4 k = ld16(k_new + (int64_t)r * kRowBytes + col * 16);
   st16(k_cache + off, k);
   st16(v_cache + off, ld16(v_new + (int64_t)r * kRowBytes + col * 16));
-  uint8_t* smin = summ + (((int64_t)r * N + pos / bs) * 2) * kRowBytes + col * 16;
+  uint8_t* slot = summ + (((int64_t)r * N + pos / bs) * 2) * kRowBytes;
+  if (scorer == kScorerMean) {   // running fp32 mean: m' = k when the token opens the block, else m + (k - m) / c
+    float x[V::n], m[V::n];
+    V::to_f32(k, x);
+    uint8_t* dst = slot + col * V::n * 4;
+    const int c = pos % bs;   // tokens already in the block
+    if (c == 0) {
+#pragma unroll
+      for (int e = 0; e < V::n; ++e) m[e] = x[e];
+      if (V::n * 16 * 4 < 2 * kRowBytes) st16(slot + kRowBytes + col * 16, make_uint4(0u, 0u, 0u, 0u));
+    } else {
+      const float inv = 1.f / (float)(c + 1);
+#pragma unroll
+      for (int e = 0; e < V::n; e += 4) {
+        const uint4 w = ld16(dst + e * 4);
+        m[e] = __uint_as_float(w.x); m[e + 1] = __uint_as_float(w.y);
+        m[e + 2] = __uint_as_float(w.z); m[e + 3] = __uint_as_float(w.w);
+      }
+#pragma unroll
+      for (int e = 0; e < V::n; ++e) m[e] = fmaf(x[e] - m[e], inv, m[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < V::n; e += 4)
+      st16(dst + e * 4, make_uint4(__float_as_uint(m[e]), __float_as_uint(m[e + 1]), __float_as_uint(m[e + 2]),
+                                   __float_as_uint(m[e + 3])));
+    return;
+  }
+  uint8_t* smin = slot + col * 16;
   uint8_t* smax = smin + kRowBytes;
   if (pos % bs == 0) {   // the token opens its block
     st16(smin, k);
@@ -107,7 +160,7 @@ prr_status launch_append(const prr_shape& s, const void* k_new, const void* v_ne
   auto* sm = static_cast<uint8_t*>(summ);
 #define PRR_APPEND(DT)                                                                                             \
   append_kernel<DT><<<grid, block, 0, stream>>>(kn, vn, kc, vc, table, sm, rows, s.n_kv_heads, s.n_blocks,           \
-                                                s.block_size, s.page_size, s.pages_per_seq, pos)
+                                                s.block_size, s.page_size, s.pages_per_seq, pos, s.scorer)
   switch (s.dtype) {
     case kF32: PRR_APPEND(kF32); break;
     case kBF16: PRR_APPEND(kBF16); break;
@@ -127,13 +180,14 @@ prr_status launch_summaries(const prr_shape& s, const void* k_cache, const int32
   trace_begin(PRR_KERNEL_SUMMARIES, stream);
   switch (s.dtype) {
     case kF32: summaries_kernel<kF32><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads, s.n_blocks,
-                                                                  s.block_size, s.page_size, s.pages_per_seq, last_block_len(s)); break;
+                                                                  s.block_size, s.page_size, s.pages_per_seq, last_block_len(s),
+                                                                  s.scorer); break;
     case kBF16: summaries_kernel<kBF16><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads,
                                                                     s.n_blocks, s.block_size, s.page_size,
-                                                                    s.pages_per_seq, last_block_len(s)); break;
+                                                                    s.pages_per_seq, last_block_len(s), s.scorer); break;
     default: summaries_kernel<kF16><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads, s.n_blocks,
                                                                 s.block_size, s.page_size, s.pages_per_seq,
-                                                                last_block_len(s)); break;
+                                                                last_block_len(s), s.scorer); break;
   }
   trace_end(PRR_KERNEL_SUMMARIES, stream);
   return check_launch("build_summaries");

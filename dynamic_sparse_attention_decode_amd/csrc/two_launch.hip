@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256, 3) void score_spec_kernel(const uint8_t* __res
                                                          const int32_t* __restrict__ pred, int k_spec,
                                                          float* __restrict__ partials, int n_spec_wg, int spw, int wpr,
                                                          int64_t spec_waves, int Hq, int Hkv, int N, int bs, int page,
-                                                         int pps, float qscale, int last_len) {
+                                                         int pps, float qscale, int last_len, int scorer) {
   if ((int)blockIdx.x < n_spec_wg) {
     const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (w < spec_waves) {
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256, 3) void score_spec_kernel(const uint8_t* __res
     return;
   }
   const int sb = (int)blockIdx.x - n_spec_wg;
-  score_chunk<DT, G, EMA>(sb % score_gx, sb / score_gx, q, summ, scores, Hq, Hkv, N, chunk, ema, alpha, first);
+  score_any<DT, G, EMA>(scorer, sb % score_gx, sb / score_gx, q, summ, scores, Hq, Hkv, N, chunk, ema, alpha, first);
 }
 
 constexpr int kSRThreads = 512;   // 8 waves: the attention tile keeps its full register budget
@@ -330,7 +330,7 @@ static void score_spec_launch(const prr_shape& s, const void* q, const void* sum
   score_spec_kernel<DT, G, EMA_, P16_><<<dim3(grid), dim3(256), 0, st>>>(                                          \
       qq, sm, scores, chunk, gx, ema, alpha, first, kk, vv, table, pred, k_spec, partials, n_spec_wg, spw, wpr,    \
       spec_waves, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size, s.pages_per_seq, qs,          \
-      last_block_len(s))
+      last_block_len(s), s.scorer)
   if (ema) {
     if (p16) PRR_SCORESPEC(true, true); else PRR_SCORESPEC(true, false);
   } else {

@@ -62,6 +62,7 @@ class Workload:
     seed: int = 20261203
     sink_blocks: int = 0         # forced blocks of every selection: the first sink_blocks and the last local_blocks
     local_blocks: int = 0
+    scorer: str = "quest"        # block scorer: "quest" (key min/max bound) or "mean" (mean key)
 
     # ---- derived sizes -------------------------------------------------------------------------------------------
     @property

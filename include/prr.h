@@ -61,6 +61,13 @@ typedef enum {
 
 typedef enum { PRR_F32 = 0, PRR_BF16 = 1, PRR_F16 = 2 } prr_dtype;
 
+/* Block scorer. QUEST: the summary slot of a block holds its elementwise key min and max (2 rows of D elements of the
+ * cache dtype) and the score is Quest's bound (PRR reference list, Quest). MEAN: the same 2 * D * elem-size bytes hold
+ * the block's mean key in fp32 (D floats; with fp32 storage the second half of the slot is unused) and the score is
+ * the group-summed query against it — a representative-key scorer (the PRR abstract evaluates representative DSA
+ * methods). */
+typedef enum { PRR_SCORER_QUEST = 0, PRR_SCORER_MEAN = 1 } prr_scorer;
+
 /* Shape of one attention layer's decode state. Supported: (dtype F32, head_dim 64) and (dtype BF16 or F16,
  * head_dim 128) — one 256-byte row per token; group size G in {1, 2, 4, 8}; block_size a multiple of page_size and
  * of 4; 1 <= n_blocks <= 65536 (and n_blocks <= 32768 for the top-K kernels).
@@ -77,10 +84,12 @@ typedef struct {
   int32_t sink_blocks;  /* forced blocks: the first sink_blocks and the last local_blocks of every sequence rank   */
   int32_t local_blocks; /* above all others in every top-K (true set and prediction), among themselves by index; */
                         /* sink_blocks + local_blocks <= n_blocks (0, 0: plain top-K)                            */
+  int32_t scorer;       /* prr_scorer                                                                            */
 } prr_shape;
 
 /* Quest block summaries (PRR reference list, Quest): for every (b, kv head g, block n), the elementwise min and max
- * over the block's tokens of the keys, read through the page table; exact in every dtype.
+ * over the block's tokens of the keys, read through the page table; exact in every dtype. With the MEAN scorer the
+ * slot receives the block's mean key in fp32 instead (summed in fp32, divided by the block's token count).
  * block_ids: NULL rebuilds every block; otherwise n_block_ids flat ids f = (b * Hkv + g) * N + n (e.g. the blocks
  * whose keys changed) are rebuilt and the rest of `summaries` is left untouched. */
 prr_status prr_build_summaries(const prr_shape* shape, const void* k_cache, const int32_t* block_table,

@@ -35,7 +35,16 @@ def shape_of(w: Workload) -> L.Shape:
     return L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, w.n_blocks,
                         {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[w.dtype], w.scale,
                         ctx_len=w.ctx if w.ctx % w.block_size else 0, sink_blocks=w.sink_blocks,
-                        local_blocks=w.local_blocks)
+                        local_blocks=w.local_blocks, scorer=L.SCORER_MEAN if w.scorer == "mean" else L.SCORER_QUEST)
+
+
+def oracle_scores(w: Workload, q_group, keys):
+    """The oracle's block scores of one (sequence, KV head) under the workload's scorer."""
+    from oracle import prr_oracle as O
+    if w.scorer == "mean":
+        return O.mean_key_scores(q_group, keys, w.block_size)
+    kmin, kmax = O.block_summaries(keys, w.block_size)
+    return O.quest_scores(q_group, kmin, kmax)
 
 
 def ragged(w: Workload, short: int) -> Workload:

@@ -9,7 +9,7 @@ from dynamic_sparse_attention_decode_amd.inputs import make_inputs
 from dynamic_sparse_attention_decode_amd.runtime import PRRLayer
 from oracle import prr_oracle as O
 from tests.checker import TOL, check_selection, max_abs
-from tests.gpu_common import SMALL, OracleView, np64, ragged, requires_gpu, shape_of, small
+from tests.gpu_common import SMALL, OracleView, np64, oracle_scores, ragged, requires_gpu, shape_of, small
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -44,8 +44,7 @@ def _check_step(w, ov, t, h, k_spec, ema_ref):
         for g in range(w.n_kv_heads):
             qg = ov.q_group(t, b, g)
             keys = ov.keys(b, g)
-            kmin, kmax = O.block_summaries(keys, w.block_size)
-            s = O.quest_scores(qg, kmin, kmax)
+            s = oracle_scores(w, qg, keys)
             check_selection(h["sel"][b, g], s, w.top_k, n_sink=w.sink_blocks, n_local=w.local_blocks)
             ref = O.attention_over_blocks(qg, keys, ov.values(b, g), h["sel"][b, g], w.block_size, w.scale)
             e = max_abs(h["out"][b, g * G:(g + 1) * G], ref)
@@ -297,6 +296,24 @@ def test_forced_blocks_decode(name, mode):
     prediction: each step against the oracle with the same forced blocks."""
     w = small(name).replace(sink_blocks=1, local_blocks=3, steps=4)
     print(f"[case] forced blocks decode {name} {mode}", flush=True)
+    inp = make_inputs(w, device="cuda")
+    kp = max(w.k_spec) or w.top_k
+    run_layer(w, inp, kp, mode, ov=OracleView(inp))
+
+
+@pytest.mark.parametrize("name,mode,extra", [("tiny_f32_4k", "prr_fused", {}), ("llama3_8b_32k", "serialized", {}),
+                                             ("llama3_8b_32k", "prr_2stream", {"sink_blocks": 1, "local_blocks": 2}),
+                                             ("paged_b32_64k", "prr_fused", {}),
+                                             ("million_token", "prr_fused", {"ctx_short": 11})])
+def test_mean_scorer_decode(name, mode, extra):
+    """The whole decode with the mean-key scorer (with forced blocks, and with a partly filled last block): every
+    step against the oracle's mean-key selection and attention."""
+    extra = dict(extra)
+    short = extra.pop("ctx_short", 0)
+    w = small(name).replace(scorer="mean", steps=4, **extra)
+    if short:
+        w = ragged(w, short)
+    print(f"[case] mean scorer decode {w.name} {mode} {extra}", flush=True)
     inp = make_inputs(w, device="cuda")
     kp = max(w.k_spec) or w.top_k
     run_layer(w, inp, kp, mode, ov=OracleView(inp))

@@ -539,3 +539,56 @@ def test_topk_forced_blocks(n_blocks):
                 torch.cuda.synchronize()
                 for name, got in (("ema_predict", out), ("select T", sel), ("select P", pn)):
                     assert np.array_equal(got.cpu().numpy()[0], ref), (name, sink, local, k, w_ is not None)
+
+
+@pytest.mark.parametrize("name,short", [("tiny_f32_4k", 9), ("llama3_8b_32k", 0), ("paged_b32_64k", 15),
+                                        ("million_token", 5)])
+def test_mean_scorer_summaries_scores_append(name, short):
+    """The mean-key scorer: each block's fp32 mean key (a partial last block over the tokens it holds), the scores
+    against the oracle's mean-key scores, and the running mean after appends against the mean recomputed over the
+    longer sequence; all within fp32 rounding of the fp64 values."""
+    from tests.gpu_common import oracle_scores
+    w = small(name).replace(scorer="mean")
+    if short:
+        w = ragged(w, short)
+    print(f"[case] mean scorer {w.name} ctx={w.ctx}", flush=True)
+    inp = make_inputs(w, device="cuda")
+    s = shape_of(w)
+    B, Hkv, N, D, bs = w.batch, w.n_kv_heads, w.n_blocks, w.head_dim, w.block_size
+    summ = torch.zeros((B, Hkv, N, 2, D), dtype=w.torch_dtype, device="cuda")
+    L.build_summaries(s, inp.k_cache, inp.table, summ)
+    ov = OracleView(inp)
+    keys = {(b, g): ov.keys(b, g) for b in range(B) for g in range(Hkv)}
+
+    def means_gpu():
+        raw = summ.view(torch.uint8).reshape(B, Hkv, N, -1)[..., :D * 4].contiguous().view(torch.float32)
+        return raw.cpu().numpy().astype(np.float64)
+
+    def check_means(tag):
+        got = means_gpu()
+        for (b, g), k in keys.items():
+            ref = O.block_means(k, bs)
+            assert np.allclose(got[b, g], ref, rtol=0, atol=2e-6 * max(1.0, np.abs(k).max())), (tag, b, g)
+
+    torch.cuda.synchronize()
+    check_means("built")
+    scores = torch.zeros((B, Hkv, N), dtype=torch.float32, device="cuda")
+    q = inp.q[1].contiguous()
+    L.score(s, q, summ, scores)
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy().astype(np.float64)
+    for (b, g), k in keys.items():
+        ref = oracle_scores(w, ov.q_group(1, b, g), k)
+        assert np.allclose(sc[b, g], ref, rtol=0, atol=1e-5 * max(1.0, np.abs(ref).max())), (b, g)
+    rng = np.random.default_rng(53)
+    n_tok = w.ctx
+    for i in range(min(4, w.n_blocks * bs - n_tok)):
+        kn = torch.as_tensor(rng.standard_normal((B, Hkv, D)), dtype=torch.float32).to(w.torch_dtype)
+        vn = torch.as_tensor(rng.standard_normal((B, Hkv, D)), dtype=torch.float32).to(w.torch_dtype)
+        n_tok += 1
+        s.ctx_len = n_tok
+        L.append_kv(s, kn.cuda(), vn.cuda(), inp.k_cache, inp.v_cache, inp.table, summ)
+        torch.cuda.synchronize()
+        for (b, g) in keys:
+            keys[(b, g)] = np.concatenate([keys[(b, g)], kn[b, g].double().numpy()[None]])
+        check_means(f"append {i}")
