@@ -158,18 +158,19 @@ __device__ inline uint32_t block_scan(uint32_t x, uint32_t& total, TopkLds& L) {
 
 // Emits the selected keys (all keys above the radix class, and the first krem keys of the class in order) in
 // ascending order: emit(pos, j) for this thread's key j at output slot pos. Thread t holds keys NK per thread in
-// index order.
-template <int NT, int NK, typename ValidFn, typename EmitFn>
+// index order. Keys for which taken(j) holds are selected whatever the class (forced blocks).
+template <int NT, int NK, typename ValidFn, typename EmitFn, typename TakenFn>
 __device__ inline void write_selected(const uint32_t (&key)[NK], ValidFn&& valid, const Radix& R, int K, TopkLds& L,
-                                      EmitFn&& emit) {
+                                      EmitFn&& emit, TakenFn&& taken) {
   const uint32_t pk = shr(R.prefix, R.shift);
   uint32_t cg = 0, ce = 0;
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
     if (valid(j)) {
       const uint32_t hk = shr(key[j], R.shift);
-      cg += hk > pk;
-      ce += hk == pk;
+      const bool t = taken(j);
+      cg += t || hk > pk;
+      ce += !t && hk == pk;
     }
   }
   const uint32_t packed = (cg << 16) | ce;   // both totals stay below 65536
@@ -182,8 +183,8 @@ __device__ inline void write_selected(const uint32_t (&key)[NK], ValidFn&& valid
   for (int j = 0; j < NK; ++j) {
     if (valid(j)) {
       const uint32_t hk = shr(key[j], R.shift);
-      bool take = hk > pk;
-      if (hk == pk) take = le++ < R.krem;
+      bool take = taken(j) || hk > pk;
+      if (!taken(j) && hk == pk) take = le++ < R.krem;
       if (take) {
         if (pos < (uint32_t)K) emit(pos, j);   // pos < K always holds; the guard keeps a logic error in bounds
         ++pos;
@@ -198,7 +199,19 @@ __device__ inline void select_top(const uint32_t (&key)[NK], ValidFn&& valid, in
   uint32_t kmax, kmin;
   block_key_range<NT>(key, valid, kmax, kmin, L);
   const Radix R = radix_select<NT, NK>(key, valid, kmax, kmin, (uint32_t)K, L);
-  write_selected<NT, NK>(key, valid, R, K, L, emit);
+  write_selected<NT, NK>(key, valid, R, K, L, emit, [](int) { return false; });
+}
+
+// Top-K when F < K of the counted keys are forced (taken(j)): the other K - F are chosen by the radix select among
+// the unforced keys alone, so the forced keys' extreme value does not widen its digit range.
+template <int NT, int NK, typename ValidFn, typename TakenFn, typename EmitFn>
+__device__ inline void select_top_forced(const uint32_t (&key)[NK], ValidFn&& valid, TakenFn&& taken, int K, int F,
+                                         TopkLds& L, EmitFn&& emit) {
+  auto free_key = [&](int j) { return valid(j) && !taken(j); };
+  uint32_t kmax, kmin;
+  block_key_range<NT>(key, free_key, kmax, kmin, L);
+  const Radix R = radix_select<NT, NK>(key, free_key, kmax, kmin, (uint32_t)(K - F), L);
+  write_selected<NT, NK>(key, valid, R, K, L, emit, taken);
 }
 
 // Forced blocks of a row of n blocks: the first `sink` and the last `local` (attention sinks and the local window,
@@ -208,6 +221,12 @@ __device__ inline void select_top(const uint32_t (&key)[NK], ValidFn&& valid, in
 struct Force {
   int base = 0, n = 0, sink = 0, local = 0;
   __device__ bool operator()(int i) const { return base + i < sink || base + i >= n - local; }
+  // forced positions among [base, base + len)
+  __device__ int count(int len) const {
+    const int a = max(0, min(sink, base + len) - base);
+    const int b = max(0, base + len - max(n - local, base));
+    return a + b;
+  }
 };
 
 // Top-K of one row of N <= NT * KPT values (optionally after the EMA update e = alpha e + (1 - alpha) v, written
@@ -265,7 +284,12 @@ __device__ void topk_row_emit(const float* __restrict__ v, float* __restrict__ e
 #pragma unroll
   for (int k = 0; k < KPT; ++k) key[k] = force(i0 + k) ? 0xFFFFFFFFu : f2key(x[k]);
   auto valid = [&](int k) { return i0 + k < N; };
-  select_top<NT, KPT>(key, valid, K, L, [&](uint32_t pos, int j) { emit(pos, i0 + j, key[j]); });
+  auto out = [&](uint32_t pos, int j) { emit(pos, i0 + j, key[j]); };
+  const int F = force.count(N);
+  if (F > 0 && F < K)
+    select_top_forced<NT, KPT>(key, valid, [&](int k) { return force(i0 + k); }, K, F, L, out);
+  else   // no forced block, or K of them at most: the forced keys take the first places by index
+    select_top<NT, KPT>(key, valid, K, L, out);
 }
 
 // Top-K of one row into orow (and lds_out, an LDS copy, when given) as K ascending indices.
