@@ -93,7 +93,8 @@ __device__ void finalize_head(const float* __restrict__ recs, int n_rec, int h, 
 }
 
 template <int DT, int G, bool P16>
-__global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
+__global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8_t* __restrict__ q,
+                                                     const uint8_t* __restrict__ kc,
                                                      const uint8_t* __restrict__ vc,
                                                      const int32_t* __restrict__ table,
                                                      const int32_t* __restrict__ sel, int top_k,

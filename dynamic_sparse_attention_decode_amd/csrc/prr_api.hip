@@ -155,7 +155,10 @@ static prr_status check_shape(const prr_shape* s) {
               s->local_blocks);
     return PRR_EINVAL;
   }
-  if (!(s->softmax_scale > 0.f) || !isfinite(s->softmax_scale)) { set_error("softmax_scale must be finite and > 0"); return PRR_EINVAL; }
+  if (!(s->softmax_scale > 0.f) || !isfinite(s->softmax_scale)) {
+    set_error("softmax_scale must be finite and > 0");
+    return PRR_EINVAL;
+  }
   return PRR_OK;
 }
 

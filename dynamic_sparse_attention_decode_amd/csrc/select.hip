@@ -2,8 +2,8 @@
 // query; PRR reference list, Quest: block scores from per-block key min/max), and the EMA predictor's update and
 // top-K' (PRR abstract: a light predictor built on an exponential moving average).
 //
-// score_kernel: Quest's group-summed block score as a streaming GEMV over all CUs (score_dev.h); optionally updates
-//   the EMA in the same pass.
+// score_kernel: Quest's group-summed block score (or the mean-key score) as a streaming GEMV over all CUs
+//   (score_dev.h); optionally updates the EMA in the same pass.
 // topk_kernel: one 1024-thread workgroup per (b, g) row (topk_dev.h); optionally updates the EMA first.
 // topk_seg_kernel + topk_merge_kernel: the same top-K for long rows when a candidate workspace is given: one
 //   workgroup per segment of 4096 values, then one per row over the segments' candidates.

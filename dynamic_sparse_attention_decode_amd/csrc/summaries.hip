@@ -4,10 +4,11 @@
 // One wave per block: each load instruction reads 4 token rows (16 lanes x 16 B per 256-byte row); lanes keep
 // running min/max, then fold the 4 rows with permlane swaps. Rows 0 and 1 of the wave write the min and max rows.
 // Pure HBM streaming: reads bs * 256 B per block, writes 512 B. A last block that the sequence ends inside is
-// summarised over the tokens it holds.
+// summarised over the tokens it holds. With the mean-key scorer the same pass sums the rows in fp32 and row 0 of the
+// wave writes the block's mean key in fp32 into the slot.
 //
 // append_kernel: the decode step's new token (position ctx_len - 1) into the K and V caches and its block's summary
-// updated in place, 16 lanes per (b, g).
+// updated in place (min/max, or the running mean), 16 lanes per (b, g).
 #include "prr_device.h"
 #include "prr_launch.h"
 
@@ -178,17 +179,16 @@ prr_status launch_summaries(const prr_shape& s, const void* k_cache, const int32
   auto* sm = static_cast<uint8_t*>(summ);
   const int64_t n_total = (int64_t)s.batch * s.n_kv_heads * s.n_blocks;
   trace_begin(PRR_KERNEL_SUMMARIES, stream);
+#define PRR_SUMMARIES(DT)                                                                                          \
+  summaries_kernel<DT><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads, s.n_blocks,   \
+                                                   s.block_size, s.page_size, s.pages_per_seq, last_block_len(s),   \
+                                                   s.scorer)
   switch (s.dtype) {
-    case kF32: summaries_kernel<kF32><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads, s.n_blocks,
-                                                                  s.block_size, s.page_size, s.pages_per_seq, last_block_len(s),
-                                                                  s.scorer); break;
-    case kBF16: summaries_kernel<kBF16><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads,
-                                                                    s.n_blocks, s.block_size, s.page_size,
-                                                                    s.pages_per_seq, last_block_len(s), s.scorer); break;
-    default: summaries_kernel<kF16><<<grid, block, 0, stream>>>(kc, table, ids, n_jobs, n_total, sm, s.n_kv_heads, s.n_blocks,
-                                                                s.block_size, s.page_size, s.pages_per_seq,
-                                                                last_block_len(s), s.scorer); break;
+    case kF32: PRR_SUMMARIES(kF32); break;
+    case kBF16: PRR_SUMMARIES(kBF16); break;
+    default: PRR_SUMMARIES(kF16); break;
   }
+#undef PRR_SUMMARIES
   trace_end(PRR_KERNEL_SUMMARIES, stream);
   return check_launch("build_summaries");
 }

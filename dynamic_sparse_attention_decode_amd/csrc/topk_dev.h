@@ -7,7 +7,8 @@
 // the row's keys differ, 8-bit digits, LDS histogram, early exit when a whole digit bin is taken. Compaction takes
 // every key above the threshold class and the lowest-index keys of the threshold class; one workgroup-wide scan
 // gives each thread its output offset, so the output comes out in ascending block order. Optionally updates the EMA
-// in the same pass.
+// in the same pass. Forced blocks (attention sinks, a local window) carry the largest key; when fewer than K of them
+// are present, the radix select runs over the other keys for the remaining places.
 //
 // Long rows split: a row cut into segments has its top-K among the union of the segments' top-K sets (a key with
 // fewer than K keys ahead of it in the row has fewer than K ahead of it in its segment, under the same order of

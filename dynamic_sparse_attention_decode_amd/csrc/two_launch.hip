@@ -4,12 +4,14 @@
 // score_spec_kernel: workgroups [0, n_spec_wg) speculate over P_t (per-block partial records, one wave per few
 //   slots); the rest compute the block scores (and update the EMA). Scoring reads the summaries and speculation reads
 //   the predicted blocks, concurrently, so the speculative loads fill bandwidth that selection leaves unused.
-// select_repair_kernel (512 threads): workgroup r < rows selects the true top-K of row r and then, in the same
-//   workgroup, merges that row's attention: blocks of T found in P_t merge their speculated records, missed blocks
-//   are computed from the KV cache, blocks of P_t outside T never enter. The 8 wave states merge in LDS and the
-//   normalised output is written directly, so no separate merge launch follows. Workgroups [rows, 2 rows) compute
-//   the next predicted set (top-K' of the updated EMA).
-// With P_t empty the same launch is select-then-attend (the serialized path in two launches).
+// select_missed_kernel (512 threads): workgroup r < rows selects the true top-K of row r and then, in the same
+//   workgroup, finds each entry of T in P_t; its 8 waves attend the missed blocks (T minus P_t) from the KV cache
+//   and merge them in LDS into one partial record, and the slots of the hits go to the workspace; blocks of P_t
+//   outside T never enter. Workgroups [rows, 2 rows) compute the next predicted set (top-K' of the updated EMA); the
+//   rest, when asked, speculate over P_t.
+// merge_hits_kernel: one workgroup per (row, head) merges the missed-block record with the speculated records of
+//   the hits and writes out = O / l.
+// With P_t empty the two launches are select-then-attend (the serialized path in two launches).
 #include "attn_wave.h"
 #include "score_dev.h"
 #include "topk_dev.h"

@@ -114,10 +114,11 @@ prr_status prr_append_kv(const prr_shape* shape, const void* k_new, const void* 
 prr_status prr_score_select(const prr_shape* shape, const void* q, const void* summaries, int32_t top_k,
                             float* scores, int32_t* sel_idx, void* workspace, void* stream);
 
-/* EMA score predictor (PRR abstract: a light predictor built on an exponential moving average): ema = scores when first_step != 0, else
- * ema = alpha * ema + (1 - alpha) * scores (in place); then pred_idx_next[b,g,:] = top-k_spec of ema, ties to the
- * lower index, ascending — the predicted set for the next decode step. Requires 1 <= k_spec <= N. `workspace` as in
- * prr_score_select (its predicted-set candidate region only, so the two selections may run at once). */
+/* EMA score predictor (PRR abstract: a light predictor built on an exponential moving average): ema = scores when
+ * first_step != 0, else ema = alpha * ema + (1 - alpha) * scores (in place); then pred_idx_next[b,g,:] = top-k_spec
+ * of ema, ties to the lower index, forced blocks first (as the selection), ascending — the predicted set for the next
+ * decode step. Requires 1 <= k_spec <= N. `workspace` as in prr_score_select (its predicted-set candidate region
+ * only, so the two selections may run at once). */
 prr_status prr_ema_predict(const prr_shape* shape, const float* scores, float* ema, float alpha, int32_t first_step,
                            int32_t k_spec, int32_t* pred_idx_next, void* workspace, void* stream);
 

@@ -230,7 +230,8 @@ def append_token(keys: np.ndarray, values: np.ndarray, k_new, v_new):
 
 
 # ------------------------------------------------------------------------------------------------------------------
-# EMA score predictor (PRR abstract: a light predictor built on an exponential moving average; summary page: it forecasts the top-K blocks)
+# EMA score predictor (PRR abstract: a light predictor built on an exponential moving average; summary page: it
+# forecasts the top-K blocks)
 # ------------------------------------------------------------------------------------------------------------------
 
 
