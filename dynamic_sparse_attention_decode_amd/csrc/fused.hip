@@ -83,16 +83,16 @@ __global__ __launch_bounds__(kSegSpecThreads, 3) void seg_spec_kernel(const floa
                               partials, Hq, Hkv, N, bs, page, pps, qscale, last_len);
 }
 
-template <int KPT>
-__global__ __launch_bounds__(1024) void merge2_kernel(TopkCand ct, int Ct, int K, int32_t* __restrict__ sel,
-                                                      TopkCand cp, int Cp, int Kp_next,
-                                                      int32_t* __restrict__ pred_next, int rows) {
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void merge2_kernel(TopkCand ct, int Ct, int K, int32_t* __restrict__ sel,
+                                                    TopkCand cp, int Cp, int Kp_next, int32_t* __restrict__ pred_next,
+                                                    int rows) {
   const int64_t r = blockIdx.x;
   if (r < rows)
-    topk_merge_row<1024, KPT>(ct.key + r * ct.cap, ct.idx + r * ct.cap, Ct, K, sel + r * K);
+    topk_merge_row<NT, KPT>(ct.key + r * ct.cap, ct.idx + r * ct.cap, Ct, K, sel + r * K);
   else
-    topk_merge_row<1024, KPT>(cp.key + (r - rows) * cp.cap, cp.idx + (r - rows) * cp.cap, Cp, Kp_next,
-                              pred_next + (r - rows) * Kp_next);
+    topk_merge_row<NT, KPT>(cp.key + (r - rows) * cp.cap, cp.idx + (r - rows) * cp.cap, Cp, Kp_next,
+                            pred_next + (r - rows) * Kp_next);
 }
 
 template <int DT, int G>
@@ -117,13 +117,18 @@ static void seg_spec_launch(const prr_shape& s, const float* scores, int K, int3
       s.softmax_scale * kLog2e, rows, last_block_len(s), s.sink_blocks, s.local_blocks);
   const int cmax = kp_next > 0 && pp.C > pt.C ? pp.C : pt.C;
   const dim3 grid((unsigned)((kp_next > 0 ? 2 : 1) * rows));
-#define PRR_MERGE2(KPT) \
-  merge2_kernel<KPT><<<grid, 1024, 0, st>>>(ct, pt.C, K, sel, cp, pp.C, kp_next, pred_next, rows)
-  switch (topk_kpt(cmax)) {
-    case 1: case 2: PRR_MERGE2(2); break;
-    case 4: PRR_MERGE2(4); break;
-    case 8: PRR_MERGE2(8); break;
-    default: PRR_MERGE2(16); break;   // C <= 16384 (topk_split_on)
+#define PRR_MERGE2(NT, KPT) \
+  merge2_kernel<NT, KPT><<<grid, NT, 0, st>>>(ct, pt.C, K, sel, cp, pp.C, kp_next, pred_next, rows)
+  if (cmax <= 4096) {   // 512 threads, as for short rows
+    switch (topk_kpt_nt(cmax, 512)) {
+      case 1: case 2: case 4: PRR_MERGE2(512, 4); break;
+      default: PRR_MERGE2(512, 8); break;
+    }
+  } else {
+    switch (topk_kpt(cmax)) {
+      case 1: case 2: case 4: case 8: PRR_MERGE2(1024, 8); break;
+      default: PRR_MERGE2(1024, 16); break;   // C <= 16384 (topk_split_on)
+    }
   }
 #undef PRR_MERGE2
 }

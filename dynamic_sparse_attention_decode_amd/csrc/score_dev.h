@@ -24,16 +24,10 @@ __device__ inline void score_chunk(int bx, int bg, const uint8_t* __restrict__ q
   const int b = bg / Hkv, g = bg % Hkv;
   const int col = lane & 15, half = (lane >> 4) & 1, pair = lane >> 5;
 
-  float coef[V::n];
+  // the query rows and the first round of summary loads are issued together (one memory round trip, not two)
+  uint4 qraw[G];
 #pragma unroll
-  for (int e = 0; e < V::n; ++e) coef[e] = 0.f;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float x[V::n];
-    V::to_f32(ld16(q + ((int64_t)b * Hq + g * G + h) * kRowBytes + col * 16), x);
-#pragma unroll
-    for (int e = 0; e < V::n; ++e) coef[e] += half ? fmaxf(x[e], 0.f) : fminf(x[e], 0.f);
-  }
+  for (int h = 0; h < G; ++h) qraw[h] = ld16(q + ((int64_t)b * Hq + g * G + h) * kRowBytes + col * 16);
 
   const int c0 = bx * chunk;
   const int c1 = min(N, c0 + chunk);
@@ -41,15 +35,32 @@ __device__ inline void score_chunk(int bx, int bg, const uint8_t* __restrict__ q
   float* srow = scores + (int64_t)bg * N;
   float* erow = EMA ? ema + (int64_t)bg * N : nullptr;
   const bool owner = (lane & 31) == 0;   // lanes 0 and 32 hold their block's score after the fold
-  for (int n0 = c0 + wave * 2 + pair; n0 < c1; n0 += 8 * U) {
-    uint4 v[U];
-    float e_old[U];
+  uint4 v[U];
+  float e_old[U];
+  auto issue = [&](int m0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int n = n0 + 8 * u;
+      const int n = m0 + 8 * u;
       v[u] = n < c1 ? ld16_stream(base + (int64_t)n * (2 * kRowBytes)) : make_uint4(0, 0, 0, 0);
       e_old[u] = (EMA && !first && owner && n < c1) ? erow[n] : 0.f;
     }
+  };
+  int n0 = c0 + wave * 2 + pair;
+  issue(n0);
+
+  float coef[V::n];
+#pragma unroll
+  for (int e = 0; e < V::n; ++e) coef[e] = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float x[V::n];
+    V::to_f32(qraw[h], x);
+#pragma unroll
+    for (int e = 0; e < V::n; ++e) coef[e] += half ? fmaxf(x[e], 0.f) : fminf(x[e], 0.f);
+  }
+
+  for (; n0 < c1; n0 += 8 * U) {
+    if (n0 > c0 + 7) issue(n0);   // rounds after the first
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float x[V::n];
@@ -81,20 +92,18 @@ __device__ inline void score_chunk_mean(int bx, int bg, const uint8_t* __restric
   const int col = lane & 15, half = (lane >> 4) & 1, pair = lane >> 5;
   const bool used = DT != kF32 || half == 0;
 
-  float coef[4] = {0.f, 0.f, 0.f, 0.f};
-  if (used) {
+  // the query values and the first round of summary loads are issued together, as in score_chunk
+  uint4 qraw[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const uint8_t* qh = q + ((int64_t)b * Hq + g * G + h) * kRowBytes;
-      float x[Vec<DT>::n];
-      if constexpr (DT == kF32) {
-        Vec<DT>::to_f32(ld16(qh + col * 16), x);
-      } else {   // the 4 16-bit values at dims 64 * half + 4 * col
-        const uint2 w = *reinterpret_cast<const uint2*>(qh + (64 * half + 4 * col) * 2);
-        Vec<DT>::to_f32(make_uint4(w.x, w.y, 0u, 0u), x);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) coef[e] += x[e];
+  for (int h = 0; h < G; ++h) {
+    const uint8_t* qh = q + ((int64_t)b * Hq + g * G + h) * kRowBytes;
+    if (!used) {
+      qraw[h] = make_uint4(0u, 0u, 0u, 0u);
+    } else if constexpr (DT == kF32) {
+      qraw[h] = ld16(qh + col * 16);
+    } else {   // the 4 16-bit values at dims 64 * half + 4 * col
+      const uint2 w = *reinterpret_cast<const uint2*>(qh + (64 * half + 4 * col) * 2);
+      qraw[h] = make_uint4(w.x, w.y, 0u, 0u);
     }
   }
 
@@ -104,15 +113,30 @@ __device__ inline void score_chunk_mean(int bx, int bg, const uint8_t* __restric
   float* srow = scores + (int64_t)bg * N;
   float* erow = EMA ? ema + (int64_t)bg * N : nullptr;
   const bool owner = (lane & 31) == 0;
-  for (int n0 = c0 + wave * 2 + pair; n0 < c1; n0 += 8 * U) {
-    uint4 v[U];
-    float e_old[U];
+  uint4 v[U];
+  float e_old[U];
+  auto issue = [&](int m0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int n = n0 + 8 * u;
+      const int n = m0 + 8 * u;
       v[u] = (used && n < c1) ? ld16_stream(base + (int64_t)n * (2 * kRowBytes)) : make_uint4(0, 0, 0, 0);
       e_old[u] = (EMA && !first && owner && n < c1) ? erow[n] : 0.f;
     }
+  };
+  int n0 = c0 + wave * 2 + pair;
+  issue(n0);
+
+  float coef[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float x[Vec<DT>::n];
+    Vec<DT>::to_f32(qraw[h], x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) coef[e] += x[e];
+  }
+
+  for (; n0 < c1; n0 += 8 * U) {
+    if (n0 > c0 + 7) issue(n0);   // rounds after the first
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float s = coef[0] * __uint_as_float(v[u].x);

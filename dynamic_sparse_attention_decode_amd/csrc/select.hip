@@ -38,12 +38,12 @@ __global__ __launch_bounds__(1024) void topk_seg_kernel(const float* __restrict_
                                ckey + row * cap, cidx + row * cap, sink, local);
 }
 
-template <int KPT>
-__global__ __launch_bounds__(1024) void topk_merge_kernel(const uint32_t* __restrict__ ckey,
-                                                          const int32_t* __restrict__ cidx, int64_t cap, int C, int K,
-                                                          int32_t* __restrict__ out) {
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_merge_kernel(const uint32_t* __restrict__ ckey,
+                                                        const int32_t* __restrict__ cidx, int64_t cap, int C, int K,
+                                                        int32_t* __restrict__ out) {
   const int64_t row = blockIdx.x;
-  topk_merge_row<1024, KPT>(ckey + row * cap, cidx + row * cap, C, K, out + row * K);
+  topk_merge_row<NT, KPT>(ckey + row * cap, cidx + row * cap, C, K, out + row * K);
 }
 
 // ---- launchers -----------------------------------------------------------------------------------------------------
@@ -72,17 +72,28 @@ prr_status launch_score(const prr_shape& s, const void* q, const void* summ, flo
   return check_launch("score");
 }
 
+// Rows of up to 4096 values take a 512-thread workgroup (fewer waves at each of the select's barriers), longer
+// rows 1024 threads.
 template <bool EMA>
-static void topk_dispatch(int kpt, dim3 grid, const float* vals, float* ema, float alpha, int first, int N, int K,
-                          int sink, int local, int32_t* out, hipStream_t st) {
-  switch (kpt) {
-    case 1: topk_kernel<1024, 1, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local); break;
-    case 2: topk_kernel<1024, 2, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local); break;
-    case 4: topk_kernel<1024, 4, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local); break;
-    case 8: topk_kernel<1024, 8, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local); break;
-    case 16: topk_kernel<1024, 16, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local); break;
-    default: topk_kernel<1024, 32, EMA><<<grid, 1024, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local); break;
+static void topk_dispatch(int N, dim3 grid, const float* vals, float* ema, float alpha, int first, int K, int sink,
+                          int local, int32_t* out, hipStream_t st) {
+#define PRR_TOPK(NT, KPT) \
+  topk_kernel<NT, KPT, EMA><<<grid, NT, 0, st>>>(vals, ema, alpha, first, N, K, out, sink, local)
+  if (N <= 4096) {
+    switch (topk_kpt_nt(N, 512)) {
+      case 1: PRR_TOPK(512, 1); break;
+      case 2: PRR_TOPK(512, 2); break;
+      case 4: PRR_TOPK(512, 4); break;
+      default: PRR_TOPK(512, 8); break;
+    }
+    return;
   }
+  switch (topk_kpt(N)) {
+    case 1: case 2: case 4: case 8: PRR_TOPK(1024, 8); break;
+    case 16: PRR_TOPK(1024, 16); break;
+    default: PRR_TOPK(1024, 32); break;
+  }
+#undef PRR_TOPK
 }
 
 size_t topk_cand_row_capacity(int N) {
@@ -113,12 +124,19 @@ static void topk_split_launch(const prr_shape& s, const float* vals, float* ema,
                                                                                 K, p.seg, c.cap, c.key, c.idx,
                                                                                 s.sink_blocks, s.local_blocks);
   const dim3 grid((unsigned)rows);
-  switch (topk_kpt(p.C)) {
-    case 1: case 2: topk_merge_kernel<2><<<grid, 1024, 0, st>>>(c.key, c.idx, c.cap, p.C, K, out); break;
-    case 4: topk_merge_kernel<4><<<grid, 1024, 0, st>>>(c.key, c.idx, c.cap, p.C, K, out); break;
-    case 8: topk_merge_kernel<8><<<grid, 1024, 0, st>>>(c.key, c.idx, c.cap, p.C, K, out); break;
-    default: topk_merge_kernel<16><<<grid, 1024, 0, st>>>(c.key, c.idx, c.cap, p.C, K, out); break;   // C <= 16384
+#define PRR_MERGE(NT, KPT) topk_merge_kernel<NT, KPT><<<grid, NT, 0, st>>>(c.key, c.idx, c.cap, p.C, K, out)
+  if (p.C <= 4096) {   // 512 threads, as for short rows
+    switch (topk_kpt_nt(p.C, 512)) {
+      case 1: case 2: case 4: PRR_MERGE(512, 4); break;
+      default: PRR_MERGE(512, 8); break;
+    }
+  } else {
+    switch (topk_kpt(p.C)) {
+      case 1: case 2: case 4: case 8: PRR_MERGE(1024, 8); break;
+      default: PRR_MERGE(1024, 16); break;   // C <= 16384
+    }
   }
+#undef PRR_MERGE
 }
 
 prr_status launch_topk(const prr_shape& s, const float* values, float* ema, float alpha, int first, int k,
@@ -132,13 +150,12 @@ prr_status launch_topk(const prr_shape& s, const float* values, float* ema, floa
     else
       topk_split_launch<false>(s, values, nullptr, alpha, first, k, out_idx, c, stream);
   } else {
-    const int kpt = topk_kpt(s.n_blocks);
     const dim3 grid((unsigned)(s.batch * s.n_kv_heads));
     if (ema)
-      topk_dispatch<true>(kpt, grid, values, ema, alpha, first, s.n_blocks, k, s.sink_blocks, s.local_blocks,
-                          out_idx, stream);
+      topk_dispatch<true>(s.n_blocks, grid, values, ema, alpha, first, k, s.sink_blocks, s.local_blocks, out_idx,
+                          stream);
     else
-      topk_dispatch<false>(kpt, grid, values, nullptr, alpha, first, s.n_blocks, k, s.sink_blocks, s.local_blocks,
+      topk_dispatch<false>(s.n_blocks, grid, values, nullptr, alpha, first, k, s.sink_blocks, s.local_blocks,
                            out_idx, stream);
   }
   trace_end(kid, stream);

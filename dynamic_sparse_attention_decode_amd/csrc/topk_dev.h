@@ -365,11 +365,14 @@ __host__ __device__ inline TopkSplit topk_split(int N, int K, int seg) {
   return p;
 }
 
-// Values per thread of a 1024-thread workgroup for a row of N values (N <= 32768).
-inline int topk_kpt(int n) {
+// Values per thread (a power of two) of an nt-thread workgroup for a row of n values.
+inline int topk_kpt_nt(int n, int nt) {
   int kpt = 1;
-  while (kpt * 1024 < n) kpt *= 2;
+  while (kpt * nt < n) kpt *= 2;
   return kpt;
 }
+
+// Values per thread of a 1024-thread workgroup for a row of N values (N <= 32768).
+inline int topk_kpt(int n) { return topk_kpt_nt(n, 1024); }
 
 }  // namespace prr
