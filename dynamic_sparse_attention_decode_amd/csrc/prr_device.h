@@ -151,8 +151,10 @@ __device__ inline float fold32(float lo, float hi) { const Pair p = swap32(lo, h
 __device__ inline float fold16(float lo, float hi) { const Pair p = swap16(lo, hi); return p.a + p.b; }
 
 // ---- order-preserving float -> uint32 keys (larger float -> larger key) -----------------------------------------
+// -0 and +0 are one value and take one key (+0's), so equal scores tie by index whatever their sign bit.
 __device__ inline uint32_t f2key(float f) {
-  const uint32_t u = __float_as_uint(f);
+  uint32_t u = __float_as_uint(f);
+  u = u == 0x80000000u ? 0u : u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

@@ -279,11 +279,12 @@ def test_poison_block_excluded():
     assert int(nm.sum()) == 0
 
 
-@pytest.mark.parametrize("n_blocks", [32768, 5000, 1000])
+@pytest.mark.parametrize("n_blocks", [32768, 5000, 4096, 3000, 2048, 1000, 129])
 def test_topk_large_rows(n_blocks):
-    """Rows up to 32768 values (the largest row the top-K kernels take): random values, massive ties, constant rows,
-    a few distinct levels, and rows whose evenly spaced entries hold the extremes. For every K the selection equals
-    the oracle's tie rule (lowest index first among equal values, ascending output)."""
+    """Rows up to 32768 values (the largest row the top-K kernels take), across the workgroup shapes (512 threads
+    with 1 to 8 values each up to 4096 values, 1024 threads beyond, full and ragged): random values, massive ties,
+    constant rows, a few distinct levels, and rows whose evenly spaced entries hold the extremes. For every K the
+    selection equals the oracle's tie rule (lowest index first among equal values, ascending output)."""
     s = L.make_shape(1, 16, 2, 128, 16, 16, n_blocks, L.BF16)
     N, rows = n_blocks, 2
     rng = np.random.default_rng(21)
@@ -303,7 +304,7 @@ def test_topk_large_rows(n_blocks):
     ema = torch.zeros((1, rows, N), dtype=torch.float32, device="cuda")
     for name, vals in cases.items():
         v32 = vals.astype(np.float32)
-        for k in sorted({1, 64, 256, min(N, 2000), N}):
+        for k in sorted({k for k in (1, 64, 256, 2000, N) if k <= N}):
             out = torch.full((1, rows, k), -1, dtype=torch.int32, device="cuda")
             L.ema_predict(s, torch.as_tensor(v32[None], device="cuda").contiguous(), ema, 0.5, True, k, out)
             torch.cuda.synchronize()
@@ -334,12 +335,8 @@ def _tie_cases(rng, rows, N):
 
 
 def _ref_top_k(v32, k):
-    """The tie rule on the fp32 keys: larger value first, then lower index (-0.0 ranks below +0.0, as the device
-    keys order them)."""
-    key = v32.view(np.uint32).astype(np.int64)
-    key = np.where(key & 0x80000000, 0xFFFFFFFF - key, key | 0x80000000)
-    order = np.lexsort((np.arange(len(v32)), -key))
-    return np.sort(order[:k]).astype(np.int32)
+    """The oracle's selection over the fp32 values (larger value first, then lower index; -0.0 equals +0.0)."""
+    return O.top_k(v32.astype(np.float64), k).astype(np.int32)
 
 
 @pytest.mark.parametrize("n_blocks", [8193, 20001, 32768])
