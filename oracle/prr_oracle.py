@@ -249,6 +249,57 @@ def predict(ema, k_spec: int, n_sink: int = 0, n_local: int = 0) -> np.ndarray:
 
 
 # ------------------------------------------------------------------------------------------------------------------
+# per-row budgets of the predicted set (PRR summary page: speculative work is held to a dynamic budget; Future work:
+# adaptive budgeting, and confidence measures for the EMA predictor). The pages give no formula for either; both
+# rules below are readings. The device takes their integer decisions in fp32, so these functions do too.
+# ------------------------------------------------------------------------------------------------------------------
+
+
+def budget_from_misses(missed_prev, k_top: int, k_cap: int, beta: float, k_min: int) -> np.ndarray:
+    """Size of each row's next predicted set from the blocks the row missed at its last completed step:
+    k = K + ceil(beta * m), clamped to [k_min, k_cap]. A row whose prediction missed more blocks speculates more.
+    beta * m is an fp32 product."""
+    m = np.asarray(missed_prev).astype(np.float32)
+    grow = np.ceil(np.float32(beta) * m).astype(np.int64)
+    return np.minimum(np.maximum(k_top + grow, k_min), k_cap)
+
+
+def confidence_bound(scores, ema, c: float) -> np.ndarray:
+    """u = e + c * |s - e| per block, every operation rounded to fp32: the EMA raised by c times its disagreement
+    with the step's score, an optimistic score for blocks whose scores move."""
+    s = np.asarray(scores, dtype=np.float32)
+    e = np.asarray(ema, dtype=np.float32)
+    return e + np.float32(c) * np.abs(s - e)
+
+
+def budget_from_confidence(scores, ema, k_top: int, k_cap: int, c: float, k_min: int, n_sink: int = 0,
+                           n_local: int = 0):
+    """(k, u): k counts the blocks whose optimistic score u reaches the K-th entry of the EMA in the selection order
+    (forced blocks first, then larger value, then lower index), clamped to [k_min, k_cap]. A forced block reaches
+    every value; when the K-th entry is itself forced, only forced blocks reach it."""
+    e = np.asarray(ema, dtype=np.float32)
+    u = confidence_bound(scores, e, c)
+    n = len(e)
+    idx = np.arange(n)
+    forced = (idx < n_sink) | (idx >= n - n_local)
+    order = np.lexsort((idx, -e.astype(np.float64), ~forced))   # the selection order of the EMA
+    kth = order[k_top - 1]
+    if forced[kth]:
+        count = int(forced.sum())
+    else:
+        count = int(forced.sum()) + int(np.count_nonzero(~forced & (u >= e[kth])))
+    return int(min(max(count, k_min), k_cap)), u
+
+
+def predict_confident(scores, ema, k_top: int, k_cap: int, c: float, k_min: int, n_sink: int = 0,
+                      n_local: int = 0) -> np.ndarray:
+    """Confidence-aware prediction: the k blocks with the largest optimistic scores u (forced first, ties to the
+    lower index), k from budget_from_confidence; ascending."""
+    k, u = budget_from_confidence(scores, ema, k_top, k_cap, c, k_min, n_sink, n_local)
+    return top_k(u, k, n_sink, n_local)
+
+
+# ------------------------------------------------------------------------------------------------------------------
 # profiling-guided speculation budget (PRR abstract; summary page, Limitations: polynomial regression off the grid)
 # ------------------------------------------------------------------------------------------------------------------
 

@@ -352,7 +352,58 @@ def pin_mean_key_scores(o):
     assert np.allclose(s, q.sum(axis=0) @ c, rtol=0, atol=1e-13)
 
 
+def pin_adaptive_budgets(o):
+    """Per-row budgets of the predicted set (two readings of the pages' adaptive budget and confidence measures).
+    Misses: worked values of K + ceil(beta * m) with clamping, no growth at beta = 0 or m = 0, and an fp32 decision
+    where fp64 would round the other way (0.3f * 50 is 15.000001 in fp32 but 15.0 in fp64; 1.1f * 50 is 55.0 in
+    fp32 but 55.00000000000001 in fp64). Confidence: against a
+    plain loop over every block in fp32 plus brute force over every k-subset on tiny rows (forced blocks and integer
+    ties included); c = 0 on distinct values is the plain top-K of the EMA; a huge c fills the cap."""
+    assert o.budget_from_misses([0, 3, 10, 100], 8, 20, 0.5, 4).tolist() == [8, 10, 13, 20]
+    assert o.budget_from_misses([0, 5], 8, 20, 0.0, 4).tolist() == [8, 8]
+    assert o.budget_from_misses([0, 1], 3, 20, 0.5, 6).tolist() == [6, 6]     # k_min lifts small budgets
+    assert o.budget_from_misses([50], 4, 64, 0.3, 1).tolist() == [20]          # fp32: 0.3f * 50 = 15.000001
+    assert o.budget_from_misses([50], 4, 64, 1.1, 1).tolist() == [59]          # fp32: 1.1f * 50 = 55.0
+    assert o.budget_from_misses([1], 4, 64, 0.25, 1).tolist() == [5]           # ceil(0.25) = 1
+
+    f32 = np.float32
+    rng = np.random.default_rng(29)
+    for trial in range(120):
+        n = int(rng.integers(3, 9))
+        sink = int(rng.integers(0, 2)) if trial % 2 else 0
+        local = int(rng.integers(0, 2)) if trial % 3 == 0 else 0
+        if sink + local >= n:
+            continue
+        kt = int(rng.integers(1, n + 1))
+        cap = int(rng.integers(kt, n + 1))
+        kmin = int(rng.integers(1, cap + 1))
+        c = float(rng.choice([0.0, 0.5, 1.0, 3.0]))
+        s = rng.standard_normal(n).astype(np.float32)
+        e = rng.standard_normal(n).astype(np.float32)
+        if trial % 4 == 0:
+            s, e = np.round(s * 2).astype(np.float32), np.round(e * 2).astype(np.float32)
+        forced = [i < sink or i >= n - local for i in range(n)]
+        u = [f32(e[i]) + f32(c) * f32(abs(f32(s[i]) - f32(e[i]))) for i in range(n)]
+        rank = sorted(range(n), key=lambda i: (not forced[i], -float(e[i]), i))
+        kth = rank[kt - 1]
+        if forced[kth]:
+            count = sum(forced)
+        else:
+            count = sum(1 for i in range(n) if forced[i] or u[i] >= e[kth])
+        k = min(max(count, kmin), cap)
+        got_k, got_u = o.budget_from_confidence(s, e, kt, cap, c, kmin, sink, local)
+        assert got_k == k, (trial, got_k, k)
+        assert np.array_equal(np.asarray(got_u, dtype=np.float32), np.asarray(u, dtype=np.float32))
+        ref = o.brute_force_top_k([float(x) for x in u], k, [i for i in range(n) if forced[i]])
+        got = o.predict_confident(s, e, kt, cap, c, kmin, sink, local)
+        assert list(got) == list(ref), (trial, got, ref)
+    e = rng.permutation(40).astype(np.float32)
+    s = e + rng.standard_normal(40).astype(np.float32)
+    assert o.predict_confident(s, e, 7, 20, 0.0, 1).tolist() == o.top_k(e, 7).tolist()
+    assert len(o.predict_confident(s, e, 7, 20, 1e30, 1)) == 20
+
+
 ALL_PINS = [pin_dense_equivalence, pin_brute_force_selection, pin_quest_upper_bound, pin_signsplit,
             pin_merge_order_free, pin_repair_invariants, pin_closed_forms, pin_hand_example, pin_ema_closed_form,
             pin_budget_closed_form, pin_paged_gather, pin_partial_last_block, pin_forced_blocks,
-            pin_mean_key_scores]
+            pin_mean_key_scores, pin_adaptive_budgets]

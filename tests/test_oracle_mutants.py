@@ -173,8 +173,34 @@ def _gather_identity(cache, table, b, g, n_tokens):
     return np.asarray(cache[b * table.shape[1] + i // page, g, i % page], dtype=np.float64)
 
 
+def _budget_misses_floor(missed_prev, k_top, k_cap, beta, k_min):
+    m = np.asarray(missed_prev).astype(np.float32)
+    return np.minimum(np.maximum(k_top + np.floor(np.float32(beta) * m).astype(np.int64), k_min), k_cap)
+
+
+def _budget_misses_fp64(missed_prev, k_top, k_cap, beta, k_min):
+    m = np.asarray(missed_prev).astype(np.float64)
+    return np.minimum(np.maximum(k_top + np.ceil(beta * m).astype(np.int64), k_min), k_cap)
+
+
+def _bound_minus(scores, ema, c):
+    s = np.asarray(scores, dtype=np.float32)
+    e = np.asarray(ema, dtype=np.float32)
+    return e - np.float32(c) * np.abs(s - e)
+
+
+def _confidence_theta_from_u(scores, ema, k_top, k_cap, c, k_min, n_sink=0, n_local=0):
+    u = O.confidence_bound(scores, ema, c)
+    return _orig["budget_from_confidence"](scores, u, k_top, k_cap, 0.0, k_min, n_sink, n_local)[0], u
+
+
+def _predict_confident_by_ema(scores, ema, k_top, k_cap, c, k_min, n_sink=0, n_local=0):
+    k, _ = O.budget_from_confidence(scores, ema, k_top, k_cap, c, k_min, n_sink, n_local)
+    return O.top_k(np.asarray(ema, dtype=np.float32), k, n_sink, n_local)
+
+
 _orig = {k: getattr(O, k) for k in ["attention_over_blocks", "prr_output", "ema_update", "choose_budget",
-                                    "block_summaries", "top_k", "mean_key_scores"]}
+                                    "block_summaries", "top_k", "mean_key_scores", "budget_from_confidence"]}
 
 MUTANTS = {
     "quest_drop_kmin": ("quest_scores", _quest_drop_kmin),
@@ -204,6 +230,11 @@ MUTANTS = {
     "budget_linear_fit": ("choose_budget", _budget_linear),
     "budget_smallest": ("choose_budget", _budget_smallest),
     "gather_ignores_table": ("logical_tokens", _gather_identity),
+    "budget_misses_floor": ("budget_from_misses", _budget_misses_floor),
+    "budget_misses_fp64": ("budget_from_misses", _budget_misses_fp64),
+    "confidence_bound_minus": ("confidence_bound", _bound_minus),
+    "confidence_theta_from_u": ("budget_from_confidence", _confidence_theta_from_u),
+    "predict_confident_by_ema": ("predict_confident", _predict_confident_by_ema),
 }
 
 
