@@ -49,6 +49,28 @@ class Shape(ctypes.Structure):
         return {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[self.dtype]
 
 
+BUDGET_FIXED, BUDGET_MISSES, BUDGET_CONFIDENCE = 0, 1, 2
+
+
+class Budget(ctypes.Structure):
+    """prr_budget: a per-row budget of the predicted set (policy BUDGET_MISSES or BUDGET_CONFIDENCE)."""
+    _fields_ = [("policy", ctypes.c_int32), ("top_k", ctypes.c_int32), ("k_min", ctypes.c_int32),
+                ("beta", ctypes.c_float), ("c", ctypes.c_float), ("missed_prev", ctypes.c_void_p)]
+
+
+def make_budget(policy: int, top_k: int, k_min: int = 1, beta: float = 0.0, c: float = 0.0, missed_prev=None):
+    """A Budget; missed_prev (int32 [B, Hkv] on the device) for BUDGET_MISSES. Keep the returned object (and the
+    tensor) alive while calls that use it are pending."""
+    mp = _p(missed_prev, torch.int32, "missed_prev")
+    b = Budget(policy, top_k, k_min, beta, c, mp.value if mp is not None else None)
+    b._keep = missed_prev
+    return b
+
+
+def _b(budget):
+    return ctypes.byref(budget) if budget is not None else None
+
+
 class StepArgs(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("summaries", ctypes.c_void_p), ("scores", ctypes.c_void_p),
@@ -56,7 +78,7 @@ class StepArgs(ctypes.Structure):
                 ("pred_next", ctypes.c_void_p), ("partials", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("n_missed", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("top_k", ctypes.c_int32),
                 ("k_spec_cur", ctypes.c_int32), ("k_spec_next", ctypes.c_int32), ("first_step", ctypes.c_int32),
-                ("alpha", ctypes.c_float)]
+                ("alpha", ctypes.c_float), ("budget", ctypes.c_void_p)]
 
 
 def make_shape(batch, n_q_heads, n_kv_heads, head_dim, block_size, page_size, n_blocks, dtype,
@@ -85,15 +107,16 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     sp = ctypes.POINTER(Shape)
+    bp = ctypes.POINTER(Budget)
     sig = {
         "prr_build_summaries": (i32, [sp, vp, vp, vp, i32, vp, vp]),
         "prr_append_kv": (i32, [sp, vp, vp, vp, vp, vp, vp, vp]),
         "prr_score_select": (i32, [sp, vp, vp, i32, vp, vp, vp, vp]),
-        "prr_ema_predict": (i32, [sp, vp, vp, f32, i32, i32, vp, vp, vp]),
+        "prr_ema_predict": (i32, [sp, vp, vp, f32, i32, i32, vp, bp, vp, vp]),
         "prr_speculate": (i32, [sp, vp, vp, vp, vp, vp, i32, vp, vp]),
         "prr_repair_merge": (i32, [sp, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp, vp, vp, vp]),
         "prr_score": (i32, [sp, vp, vp, vp, vp, f32, i32, vp]),
-        "prr_select_speculate": (i32, [sp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp]),
+        "prr_select_speculate": (i32, [sp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, bp, vp, vp]),
         "prr_score_speculate": (i32, [sp, vp, vp, vp, vp, f32, i32, vp, vp, vp, vp, i32, vp, vp]),
         "prr_select_repair": (i32, [sp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]),
         "prr_partials_bytes": (sz, [sp, i32]),
@@ -172,11 +195,11 @@ def score_select(shape: Shape, q, summaries, top_k: int, scores, sel_idx, worksp
 
 
 def ema_predict(shape: Shape, scores, ema, alpha: float, first_step: bool, k_spec: int, pred_idx_next,
-                workspace=None, stream=None) -> None:
+                workspace=None, stream=None, budget: Budget | None = None) -> None:
     _check(lib().prr_ema_predict(ctypes.byref(shape), _p(scores, torch.float32, "scores"),
                                  _p(ema, torch.float32, "ema"), alpha, int(bool(first_step)), k_spec,
-                                 _p(pred_idx_next, torch.int32, "pred_idx_next"), _p(workspace, None, "workspace"),
-                                 _s(stream)), "ema_predict")
+                                 _p(pred_idx_next, torch.int32, "pred_idx_next"), _b(budget),
+                                 _p(workspace, None, "workspace"), _s(stream)), "ema_predict")
 
 
 def speculate(shape: Shape, q, k_cache, v_cache, block_table, pred_idx, k_spec: int, partials, stream=None) -> None:
@@ -208,15 +231,15 @@ def score(shape: Shape, q, summaries, scores, ema=None, alpha: float = 0.0, firs
 
 def select_speculate(shape: Shape, scores, top_k: int, sel_idx, ema=None, k_spec_next: int = 0, pred_idx_next=None,
                      q=None, k_cache=None, v_cache=None, block_table=None, pred_idx=None, k_spec: int = 0,
-                     partials=None, workspace=None, stream=None) -> None:
+                     partials=None, workspace=None, stream=None, budget: Budget | None = None) -> None:
     dt = shape.torch_dtype
     _check(lib().prr_select_speculate(ctypes.byref(shape), _p(scores, torch.float32, "scores"), top_k,
                                       _p(sel_idx, torch.int32, "sel_idx"), _p(ema, torch.float32, "ema"), k_spec_next,
                                       _p(pred_idx_next, torch.int32, "pred_idx_next"), _p(q, dt, "q"),
                                       _p(k_cache, dt, "k_cache"), _p(v_cache, dt, "v_cache"),
                                       _p(block_table, torch.int32, "block_table"), _p(pred_idx, torch.int32, "pred_idx"),
-                                      k_spec, _p(partials, torch.float32, "partials"), _p(workspace, None, "workspace"),
-                                      _s(stream)), "select_speculate")
+                                      k_spec, _p(partials, torch.float32, "partials"), _b(budget),
+                                      _p(workspace, None, "workspace"), _s(stream)), "select_speculate")
 
 
 def score_speculate(shape: Shape, q, summaries, scores, ema=None, alpha: float = 0.0, first_step=False,

@@ -328,7 +328,8 @@ __device__ inline void run_records(W& st, int cnt, RecFn&& rec_of) {
   }
 }
 
-// Speculation of the predicted slots [j0, j1) of row `rowid` by one wave: one partial record per slot.
+// Speculation of the predicted slots [j0, j1) of row `rowid` by one wave: one partial record per slot. Slots from
+// the first empty one (a negative id: a budgeted set's padding, which follows every id of its row) are skipped.
 template <int DT, int G, bool P16>
 __device__ inline void speculate_slots(int64_t rowid, int j0, int j1, int lane, const uint8_t* __restrict__ q,
                                        const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
@@ -338,12 +339,20 @@ __device__ inline void speculate_slots(int64_t rowid, int j0, int j1, int lane, 
   using W = Tile<DT, G>;
   const int b = (int)(rowid / Hkv), g = (int)(rowid % Hkv);
   const int32_t* prow = pred + rowid * k_spec;
+  for (int c = j0; c < j1; c += 64) {   // the wave's slots end at the first empty one
+    const unsigned long long empty = __ballot(c + lane < j1 && prow[c + lane] < 0);
+    if (empty) {
+      j1 = c + __ffsll(empty) - 1;
+      break;
+    }
+  }
+  if (j1 <= j0) return;
   W st;
   st.init(lane);
   st.load_q(q + ((int64_t)b * Hq + (int64_t)g * G) * kRowBytes, qscale);
   run_blocks<P16>(
       st, j1 - j0,
-      [&](int i) { return min(max(prow[j0 + i], 0), N - 1); },   // ids outside [0, N) are clamped, never a fault
+      [&](int i) { return min(max(prow[j0 + i], 0), N - 1); },   // ids beyond the row are clamped, never a fault
       [&](int i) {
         float folded[W::NK];
         st.fold(folded);
@@ -363,7 +372,9 @@ __device__ inline void speculate_slot(int64_t s, int lane, const uint8_t* __rest
   using W = Tile<DT, G>;
   const int64_t rowid = s / k_spec;
   const int b = (int)(rowid / Hkv), g = (int)(rowid % Hkv);
-  const int n = min(max(pred[s], 0), N - 1);   // ids outside [0, N) are clamped: wrong output, never a fault
+  const int32_t id = pred[s];
+  if (id < 0) return;              // an empty slot (a budgeted set's padding)
+  const int n = min(id, N - 1);    // ids beyond the row are clamped: wrong output, never a fault
   W st;
   st.init(lane);
   st.load_q(q + ((int64_t)b * Hq + (int64_t)g * G) * kRowBytes, qscale);

@@ -28,15 +28,25 @@ __global__ __launch_bounds__(kSelSpecThreads) void select_spec_kernel(const floa
                                                            const int32_t* __restrict__ pred, int k_spec,
                                                            float* __restrict__ partials, int64_t spec_total, int Hq,
                                                            int Hkv, int N, int bs, int page, int pps, float qscale,
-                                                           int rows, int last_len, int sink, int local) {
+                                                           int rows, int last_len, int sink, int local,
+                                                           BudgetDev bp) {
   const int64_t r = blockIdx.x;
   if (r < n_sel_wg) {
-    if (r < rows)
+    const int64_t rr = r - rows;
+    if (r < rows) {
       topk_row<kSelSpecThreads, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, nullptr,
                                             Force{0, N, sink, local});
-    else
-      topk_row<kSelSpecThreads, KPT, false>(ema + (r - rows) * N, nullptr, 0.f, 0, N, Kp_next,
-                                            pred_next + (r - rows) * Kp_next, nullptr, Force{0, N, sink, local});
+    } else if constexpr (KPT <= 16) {   // budgeted rows are routed elsewhere beyond 8192 blocks
+      if (bp.policy != 0)
+        predict_row<kSelSpecThreads, KPT, false>(scores + rr * N, const_cast<float*>(ema) + rr * N, 0.f, 0, N,
+                                                 Kp_next, bp, rr, pred_next + rr * Kp_next, Force{0, N, sink, local});
+      else
+        topk_row<kSelSpecThreads, KPT, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp_next, pred_next + rr * Kp_next,
+                                              nullptr, Force{0, N, sink, local});
+    } else {
+      topk_row<kSelSpecThreads, KPT, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp_next, pred_next + rr * Kp_next,
+                                            nullptr, Force{0, N, sink, local});
+    }
     return;
   }
   const int64_t s = (r - n_sel_wg) * (kSelSpecThreads / 64) + (threadIdx.x >> 6);
@@ -137,7 +147,7 @@ template <int DT, int G>
 static void select_spec_launch(const prr_shape& s, const float* scores, int K, int32_t* sel, const float* ema,
                                int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                                const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                               hipStream_t st) {
+                               const BudgetDev& bp, hipStream_t st) {
   const int rows = s.batch * s.n_kv_heads;
   const int n_sel_wg = kp_next > 0 ? 2 * rows : rows;
   const int64_t spec_total = (int64_t)rows * k_spec;
@@ -153,7 +163,7 @@ static void select_spec_launch(const prr_shape& s, const float* scores, int K, i
                                                        table, pred, k_spec, partials, spec_total, s.n_q_heads,       \
                                                        s.n_kv_heads, s.n_blocks, s.block_size, s.page_size,          \
                                                        s.pages_per_seq, qs, rows, last_block_len(s),            \
-                                                       s.sink_blocks, s.local_blocks)
+                                                       s.sink_blocks, s.local_blocks, bp)
   // values per thread: a few register sizes cover every row length (larger than needed is correct, just slower)
   if (s.n_blocks <= 4 * kSelSpecThreads)
     PRR_SELSPEC(4);
@@ -167,16 +177,23 @@ static void select_spec_launch(const prr_shape& s, const float* scores, int K, i
 prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
                               int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                               const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                              hipStream_t stream, void* cand_t, void* cand_p) {
+                              hipStream_t stream, void* cand_t, void* cand_p, const BudgetDev& bp) {
+  if (bp.policy != 0 && kp_next > 0 && s.n_blocks > 16 * kSelSpecThreads) {
+    // budgeted rows this long take their own launch of 1024-thread workgroups, which reads the EMA as it stands
+    const prr_status st = launch_select_spec(s, scores, k, sel, nullptr, 0, nullptr, q, kc, vc, table, pred, k_spec,
+                                             partials, stream, cand_t, cand_p, BudgetDev{});
+    if (st != PRR_OK) return st;
+    return launch_predict_budget(s, scores, const_cast<float*>(ema), 0.f, 0, kp_next, bp, pred_next, false, stream);
+  }
   trace_begin(PRR_KERNEL_SELECT_TOPK, stream);
-  if (cand_t && cand_p && topk_split_on(s.n_blocks, k, kSelSpecSeg) &&
+  if (bp.policy == 0 && cand_t && cand_p && topk_split_on(s.n_blocks, k, kSelSpecSeg) &&
       (kp_next == 0 || topk_split_on(s.n_blocks, kp_next, kSelSpecSeg))) {
     const TopkCand ct = topk_cand_at(s, cand_t), cp = topk_cand_at(s, cand_p);
     PRR_DISPATCH_DT_G(seg_spec_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
                       partials, ct, cp, stream);
   } else {
     PRR_DISPATCH_DT_G(select_spec_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
-                      partials, stream);
+                      partials, bp, stream);
   }
   trace_end(PRR_KERNEL_SELECT_TOPK, stream);
   return check_launch("select_speculate");

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <cmath>
 #include <new>
 
 #include "prr_device.h"
@@ -183,6 +184,23 @@ static prr_status check_topk_n(const prr_shape* s) {
 
 static inline hipStream_t as_stream(void* p) { return static_cast<hipStream_t>(p); }
 
+// A budget for a predicted set of k_spec slots (NULL or PRR_BUDGET_FIXED: nothing to check).
+static prr_status check_budget(const prr_shape* s, const prr_budget* b, int k_spec, const char* who) {
+  if (!b || b->policy == PRR_BUDGET_FIXED) return PRR_OK;
+  PRR_REQUIRE(b->policy == PRR_BUDGET_MISSES || b->policy == PRR_BUDGET_CONFIDENCE, "%s: unknown budget policy %d",
+              who, b->policy);
+  PRR_REQUIRE(b->top_k >= 1 && b->top_k <= s->n_blocks, "%s: budget top_k %d not in [1, %d]", who, b->top_k,
+              s->n_blocks);
+  PRR_REQUIRE(b->k_min >= 1 && b->k_min <= k_spec, "%s: budget k_min %d not in [1, %d]", who, b->k_min, k_spec);
+  if (b->policy == PRR_BUDGET_MISSES) {
+    PRR_REQUIRE(std::isfinite(b->beta) && b->beta >= 0.f, "%s: budget beta must be finite and >= 0", who);
+    PRR_REQUIRE(b->missed_prev, "%s: the misses budget needs missed_prev", who);
+  } else {
+    PRR_REQUIRE(std::isfinite(b->c) && b->c >= 0.f, "%s: budget c must be finite and >= 0", who);
+  }
+  return PRR_OK;
+}
+
 }  // namespace prr
 
 using namespace prr;
@@ -239,13 +257,19 @@ prr_status prr_score_select(const prr_shape* shape, const void* q, const void* s
 }
 
 prr_status prr_ema_predict(const prr_shape* shape, const float* scores, float* ema, float alpha, int32_t first_step,
-                           int32_t k_spec, int32_t* pred_idx_next, void* workspace, void* stream) {
+                           int32_t k_spec, int32_t* pred_idx_next, const prr_budget* budget, void* workspace,
+                           void* stream) {
   PRR_TRY(check_shape(shape));
   PRR_TRY(check_topk_n(shape));
   PRR_REQUIRE(scores && ema && pred_idx_next, "ema_predict: null pointer");
   PRR_REQUIRE(k_spec >= 1 && k_spec <= shape->n_blocks, "ema_predict: k_spec %d not in [1, %d]", k_spec,
               shape->n_blocks);
   PRR_REQUIRE(alpha >= 0.f && alpha <= 1.f, "ema_predict: alpha not in [0, 1]");
+  PRR_TRY(check_budget(shape, budget, k_spec, "ema_predict"));
+  const BudgetDev bp = budget_dev(budget);
+  if (bp.policy != 0)
+    return launch_predict_budget(*shape, scores, ema, alpha, first_step ? 1 : 0, k_spec, bp, pred_idx_next, true,
+                                 as_stream(stream));
   return launch_topk(*shape, scores, ema, alpha, first_step ? 1 : 0, k_spec, pred_idx_next, as_stream(stream),
                      cand_region(*shape, workspace, 1));
 }
@@ -289,8 +313,8 @@ prr_status prr_score(const prr_shape* shape, const void* q, const void* summarie
 prr_status prr_select_speculate(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
                                 const float* ema, int32_t k_spec_next, int32_t* pred_idx_next, const void* q,
                                 const void* k_cache, const void* v_cache, const int32_t* block_table,
-                                const int32_t* pred_idx, int32_t k_spec, float* partials, void* workspace,
-                                void* stream) {
+                                const int32_t* pred_idx, int32_t k_spec, float* partials, const prr_budget* budget,
+                                void* workspace, void* stream) {
   PRR_TRY(check_shape(shape));
   PRR_TRY(check_topk_n(shape));
   PRR_REQUIRE(scores && sel_idx, "select_speculate: null pointer");
@@ -307,9 +331,11 @@ prr_status prr_select_speculate(const prr_shape* shape, const float* scores, int
     set_error("select_speculate: pred_idx and pred_idx_next must be different buffers");
     return PRR_EINVAL;
   }
+  if (k_spec_next > 0) PRR_TRY(check_budget(shape, budget, k_spec_next, "select_speculate"));
   return launch_select_spec(*shape, scores, top_k, sel_idx, ema, k_spec_next, pred_idx_next, q, k_cache, v_cache,
                             block_table, pred_idx, k_spec, partials, as_stream(stream),
-                            cand_region(*shape, workspace, 0), cand_region(*shape, workspace, 1));
+                            cand_region(*shape, workspace, 0), cand_region(*shape, workspace, 1),
+                            k_spec_next > 0 ? budget_dev(budget) : BudgetDev{});
 }
 
 prr_status prr_score_speculate(const prr_shape* shape, const void* q, const void* summaries, float* scores, float* ema,
@@ -429,7 +455,14 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
     mode = PRR_MODE_SERIALIZED;
   }
   const int64_t rows = (int64_t)shape->batch * shape->n_kv_heads;
-  if (mode == PRR_MODE_FUSED && two_launch_supported(*shape, a->top_k, kc, kn) && (rows >= 128 || a->top_k <= 32)) {
+  const prr_budget* budget = kn > 0 ? a->budget : nullptr;
+  const bool budgeted = budget && budget->policy != PRR_BUDGET_FIXED;
+  if (budgeted)
+    PRR_REQUIRE(budget->top_k == a->top_k, "decode_step: the budget's top_k %d differs from the step's %d",
+                budget->top_k, a->top_k);
+  // budgeted predictions are written by the selection launches of the paths below (one workgroup per row)
+  if (mode == PRR_MODE_FUSED && !budgeted && two_launch_supported(*shape, a->top_k, kc, kn) &&
+      (rows >= 128 || a->top_k <= 32)) {
     // scores + EMA; then selection of T and P_{t+1}, speculation over P_t and the missed blocks T \ P_t in one
     // launch; then the merge of the missed-block records with the speculated records of T ∩ P_t. One workgroup per
     // row attends that row's missed blocks after its selection, which pays off when the rows alone fill the chip or
@@ -447,7 +480,8 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
   if (mode == PRR_MODE_FUSED) {
     PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step, s1));
     PRR_TRY(prr_select_speculate(shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,
-                                 a->v_cache, a->block_table, a->pred_cur, kc, a->partials, a->workspace, s1));
+                                 a->v_cache, a->block_table, a->pred_cur, kc, a->partials, budget, a->workspace,
+                                 s1));
     return prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
                             kc, a->partials, a->out, a->n_missed, a->workspace, s1);
   }
@@ -455,7 +489,8 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
     return prr_score_select(shape, a->q, a->summaries, a->top_k, a->scores, a->sel_idx, a->workspace, st);
   };
   auto ema_predict = [&](hipStream_t st) {
-    return prr_ema_predict(shape, a->scores, a->ema, a->alpha, a->first_step, kn, a->pred_next, a->workspace, st);
+    return prr_ema_predict(shape, a->scores, a->ema, a->alpha, a->first_step, kn, a->pred_next, budget, a->workspace,
+                           st);
   };
   if (mode != PRR_MODE_TWO_STREAM) {
     if (kc > 0) PRR_TRY(prr_speculate(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->pred_cur, kc,

@@ -51,6 +51,29 @@ void trace_end(int kid, hipStream_t stream);
 
 constexpr int kScorerQuest = 0, kScorerMean = 1;
 
+// A predicted set's per-row budget as the kernels take it (policy 0: fixed).
+struct BudgetDev {
+  int policy = 0, top_k = 0, k_min = 1;
+  float beta = 0.f, c = 0.f;
+  const int32_t* missed_prev = nullptr;
+};
+inline BudgetDev budget_dev(const prr_budget* b) {
+  BudgetDev d;
+  if (b && b->policy != PRR_BUDGET_FIXED) {
+    d.policy = b->policy;
+    d.top_k = b->top_k;
+    d.k_min = b->k_min;
+    d.beta = b->beta;
+    d.c = b->c;
+    d.missed_prev = b->missed_prev;
+  }
+  return d;
+}
+// Standalone budgeted prediction (with update: the EMA update first; then the per-row size, the top-k_r and the -1
+// padding): one workgroup per row, rows of at most 32768 blocks.
+prr_status launch_predict_budget(const prr_shape& s, const float* scores, float* ema, float alpha, int first, int cap,
+                                 const BudgetDev& bp, int32_t* pred_next, bool update, hipStream_t stream);
+
 // Tokens of the last block (block_size unless the sequence ends inside it).
 inline int last_block_len(const prr_shape& s) {
   return s.ctx_len > 0 ? s.ctx_len - (s.n_blocks - 1) * s.block_size : s.block_size;
@@ -95,7 +118,8 @@ int spec_slots_per_wave(const prr_shape& s, int k_spec);
 prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
                               int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                               const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                              hipStream_t stream, void* cand_t = nullptr, void* cand_p = nullptr);
+                              hipStream_t stream, void* cand_t = nullptr, void* cand_p = nullptr,
+                              const BudgetDev& bp = BudgetDev{});
 // The two-launch step: scores (+ EMA) with speculation, then selection with the row-wise repair and merge.
 bool two_launch_supported(const prr_shape& s, int top_k, int k_spec, int k_spec_next);
 prr_status launch_score_spec(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema,

@@ -46,6 +46,15 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const uint32_t* __restri
   topk_merge_row<NT, KPT>(ckey + row * cap, cidx + row * cap, C, K, out + row * K);
 }
 
+template <int NT, int KPT, bool EMA>
+__global__ __launch_bounds__(NT) void predict_budget_kernel(const float* __restrict__ scores, float* __restrict__ ema,
+                                                            float alpha, int first, int N, int cap, BudgetDev bp,
+                                                            int32_t* __restrict__ out, int sink, int local) {
+  const int64_t row = blockIdx.x;
+  predict_row<NT, KPT, EMA>(scores + row * N, ema + row * N, alpha, first, N, cap, bp, row, out + row * cap,
+                            Force{0, N, sink, local});
+}
+
 // ---- launchers -----------------------------------------------------------------------------------------------------
 
 template <int DT, int G>
@@ -137,6 +146,42 @@ static void topk_split_launch(const prr_shape& s, const float* vals, float* ema,
     }
   }
 #undef PRR_MERGE
+}
+
+template <bool EMA>
+static void predict_budget_dispatch(const prr_shape& s, const float* scores, float* ema, float alpha, int first,
+                                    int cap, const BudgetDev& bp, int32_t* pred_next, hipStream_t st) {
+  const int N = s.n_blocks;
+  const dim3 grid((unsigned)(s.batch * s.n_kv_heads));
+#define PRR_PREDICT(NT, KPT)                                                                                       \
+  predict_budget_kernel<NT, KPT, EMA><<<grid, NT, 0, st>>>(scores, ema, alpha, first, N, cap, bp, pred_next,       \
+                                                           s.sink_blocks, s.local_blocks)
+  if (N <= 4096) {
+    switch (topk_kpt_nt(N, 512)) {
+      case 1: PRR_PREDICT(512, 1); break;
+      case 2: PRR_PREDICT(512, 2); break;
+      case 4: PRR_PREDICT(512, 4); break;
+      default: PRR_PREDICT(512, 8); break;
+    }
+  } else {
+    switch (topk_kpt(N)) {
+      case 1: case 2: case 4: case 8: PRR_PREDICT(1024, 8); break;
+      case 16: PRR_PREDICT(1024, 16); break;
+      default: PRR_PREDICT(1024, 32); break;   // N <= 32768
+    }
+  }
+#undef PRR_PREDICT
+}
+
+prr_status launch_predict_budget(const prr_shape& s, const float* scores, float* ema, float alpha, int first, int cap,
+                                 const BudgetDev& bp, int32_t* pred_next, bool update, hipStream_t st) {
+  trace_begin(PRR_KERNEL_EMA_TOPK, st);
+  if (update)
+    predict_budget_dispatch<true>(s, scores, ema, alpha, first, cap, bp, pred_next, st);
+  else
+    predict_budget_dispatch<false>(s, scores, ema, alpha, first, cap, bp, pred_next, st);
+  trace_end(PRR_KERNEL_EMA_TOPK, st);
+  return check_launch("ema_predict (budget)");
 }
 
 prr_status launch_topk(const prr_shape& s, const float* values, float* ema, float alpha, int first, int k,

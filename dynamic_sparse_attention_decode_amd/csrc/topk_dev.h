@@ -17,6 +17,7 @@
 // selects the top-K of the candidates with the same tie rule by position.
 #pragma once
 #include "prr_device.h"
+#include "prr_launch.h"
 
 namespace prr {
 
@@ -291,6 +292,92 @@ __device__ void topk_row_emit(const float* __restrict__ v, float* __restrict__ e
     select_top_forced<NT, KPT>(key, valid, [&](int k) { return force(i0 + k); }, K, F, L, out);
   else   // no forced block, or K of them at most: the forced keys take the first places by index
     select_top<NT, KPT>(key, valid, K, L, out);
+}
+
+// Smallest key of the workgroup (0xffffffff when no thread holds one).
+template <int NT>
+__device__ inline uint32_t block_min_u32(uint32_t x, TopkLds& L) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  x = wave_min_u32(x);
+  if (lane == 0) L.red_k[1][wave] = x;
+  __syncthreads();
+  uint32_t r = L.red_k[1][0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) r = min(r, L.red_k[1][w]);
+  __syncthreads();
+  return r;
+}
+
+// The next step's predicted set of one row under a per-row budget (BudgetDev; the host has validated it), by one
+// workgroup of NT threads, N <= NT * KPT. With EMA the row's average is updated first (e = s on the first step, else
+// alpha e + (1 - alpha) s, written back), otherwise e_row already holds it. The row's size k_r is cap (fixed),
+// K + ceil(beta m) clamped to [k_min, cap] (misses: m the row's missed blocks at its last completed step, an fp32
+// product), or the number of blocks whose optimistic score u = e + c |s - e| (fp32) reaches the K-th EMA key in the
+// selection order, clamped (confidence). orow[0, k_r) receives the top-k_r of the EMA (fixed, misses) or of u
+// (confidence), forced blocks first, ascending; orow[k_r, cap) = -1.
+template <int NT, int KPT, bool EMA>
+__device__ void predict_row(const float* __restrict__ s_row, float* e_row, float alpha, int first, int N, int cap,
+                            const BudgetDev& bp, int64_t row, int32_t* __restrict__ orow, Force force) {
+  static_assert(NT >= 256 && NT <= 1024 && NT % 64 == 0, "workgroup size");
+  __shared__ TopkLds L;
+  const int i0 = threadIdx.x * KPT;
+  const bool conf = bp.policy == 2;
+  // keys of the EMA (key) and, for the confidence rule, of the optimistic score u (ukey); forced blocks the largest
+  uint32_t key[KPT], ukey[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) {
+    const int i = i0 + k;
+    float e = 0.f, sv = 0.f;
+    if (i < N) {
+      if (EMA || conf) sv = s_row[i];
+      if (EMA) {
+        e = first ? sv : fmaf(alpha, e_row[i], (1.f - alpha) * sv);
+        e_row[i] = e;
+      } else {
+        e = e_row[i];
+      }
+    }
+    const bool f = force(i);
+    key[k] = f ? 0xFFFFFFFFu : f2key(e);
+    ukey[k] = f ? 0xFFFFFFFFu : f2key(__fadd_rn(e, __fmul_rn(bp.c, fabsf(__fsub_rn(sv, e)))));
+  }
+  auto valid = [&](int k) { return i0 + k < N; };
+  int kr = cap;
+  if (bp.policy == 1) {
+    const float grow = fminf(ceilf(bp.beta * (float)bp.missed_prev[row]), (float)cap);   // cap bounds k_r anyway
+    kr = min(max(bp.top_k + (int)grow, bp.k_min), cap);
+  } else if (conf) {
+    // theta: the K-th largest EMA key
+    uint32_t kmax, kmin;
+    block_key_range<NT>(key, valid, kmax, kmin, L);
+    const Radix R = radix_select<NT, KPT>(key, valid, kmax, kmin, (uint32_t)bp.top_k, L);
+    uint32_t theta = R.prefix;
+    if (R.shift > 0) {   // the selection took its last digit class whole: theta is that class's smallest key
+      const uint32_t pk = shr(R.prefix, R.shift);
+      uint32_t lo = 0xffffffffu;
+#pragma unroll
+      for (int k = 0; k < KPT; ++k)
+        if (valid(k) && shr(key[k], R.shift) == pk) lo = min(lo, key[k]);
+      theta = block_min_u32<NT>(lo, L);
+    }
+    uint32_t cnt = 0;   // optimistic scores reaching theta
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      cnt += valid(k) && ukey[k] >= theta;
+      key[k] = ukey[k];
+    }
+    uint32_t total;
+    block_scan<NT>(cnt, total, L);
+    kr = min(max((int)total, bp.k_min), cap);
+  }
+  auto out = [&](uint32_t pos, int j) { orow[pos] = i0 + j; };
+  const int F = force.count(N);
+  if (F > 0 && F < kr)
+    select_top_forced<NT, KPT>(key, valid, [&](int k) { return force(i0 + k); }, kr, F, L, out);
+  else
+    select_top<NT, KPT>(key, valid, kr, L, out);
+  for (int j = kr + (int)threadIdx.x; j < cap; j += NT) orow[j] = -1;
 }
 
 // Top-K of one row into orow (and lds_out, an LDS copy, when given) as K ascending indices.

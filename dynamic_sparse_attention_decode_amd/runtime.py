@@ -7,6 +7,8 @@ one decode step through the library's ``prr_decode_step``:
   stream_sel:  score_select(t) -> [wait speculation] -> repair_merge(t)                      -> out_t
   stream_spec: speculate(P_t)  -> [wait selection]   -> ema_predict(t) -> P_{t+1}
 
+A per-row budget (prr_budget) may size each row's predicted set below k_spec; its rows then end in -1 slots.
+
 PRR abstract: speculation over the predicted blocks runs while selection is in flight; the missed blocks are
 repaired once the true set is known. Step 0 has no prediction (full repair). Buffers that the two streams share
 across steps alternate by step parity, so step t+1's speculation never overwrites what step t's repair reads.
@@ -23,9 +25,15 @@ MODES = {"serialized": L.MODE_SERIALIZED, "prr_1stream": L.MODE_ONE_STREAM, "prr
          "prr_fused": L.MODE_FUSED, "serialized_fused": L.MODE_SERIALIZED_FUSED}
 
 
+BUDGETS = {"fixed": L.BUDGET_FIXED, "misses": L.BUDGET_MISSES, "confidence": L.BUDGET_CONFIDENCE}
+
+
 class PRRLayer:
     def __init__(self, shape: L.Shape, top_k: int, k_spec: int, alpha: float, mode: str = "prr_2stream",
-                 device="cuda", streams=None):
+                 device="cuda", streams=None, budget: dict | None = None):
+        """budget: None (every row predicts k_spec blocks) or {"policy": "misses" | "confidence", "k_min": int,
+        "beta": float, "c": float}: per-row sizes of the predicted set, at most k_spec (prr_budget); the missed
+        counts that the misses policy reads are double-buffered here."""
         if mode not in MODES:
             raise ValueError(f"mode must be one of {list(MODES)}")
         self.shape = L.Shape.from_buffer_copy(shape)   # own copy: append() advances its ctx_len
@@ -47,7 +55,13 @@ class PRRLayer:
         pb = max(L.partials_bytes(shape, kp), 16)
         self.partials = [torch.zeros((pb // 4,), dtype=torch.float32, device=dev) for _ in range(2)]
         self.out = [torch.zeros((B, shape.n_q_heads, D), dtype=torch.float32, device=dev) for _ in range(2)]
-        self.n_missed = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+        self.missed = [torch.zeros((B, Hkv), dtype=torch.int32, device=dev) for _ in range(2)]   # by step parity
+        self.budgets = None
+        if budget is not None and BUDGETS[budget.get("policy", "fixed")] != L.BUDGET_FIXED and self.k_spec > 0:
+            pol = BUDGETS[budget["policy"]]
+            # step t writes P_{t+1} under the budget whose missed counts are step t-1's (the other parity)
+            self.budgets = [L.make_budget(pol, self.top_k, int(budget.get("k_min", 1)), float(budget.get("beta", 0.0)),
+                                          float(budget.get("c", 0.0)), self.missed[1 - par]) for par in range(2)]
         self.workspace = torch.zeros((L.workspace_bytes(shape, self.top_k) // 4 + 1,), dtype=torch.float32,
                                      device=dev)
         if streams is None:
@@ -102,8 +116,10 @@ class PRRLayer:
         cur.wait_stream(self.s_sel)
 
     def reset(self) -> None:
-        """Forget the prediction state: the next step is a first step (no speculation)."""
+        """Forget the prediction state: the next step is a first step (no speculation, no missed counts)."""
         self.t = 0
+        for m in self.missed:
+            m.zero_()
 
     # ---- one decode step -----------------------------------------------------------------------------------------
     def _args(self, q: torch.Tensor) -> L.StepArgs:
@@ -111,10 +127,11 @@ class PRRLayer:
         par, nxt = t % 2, (t + 1) % 2
         kc = self.k_spec if t > 0 else 0
         vp = lambda x: ctypes.c_void_p(x.data_ptr())
+        bud = ctypes.addressof(self.budgets[par]) if self.budgets else None
         return L.StepArgs(vp(q), vp(self.k_cache), vp(self.v_cache), vp(self.table), vp(self.summaries),
                           vp(self.scores[par]), vp(self.sel_idx), vp(self.ema), vp(self.pred[par]),
-                          vp(self.pred[nxt]), vp(self.partials[par]), vp(self.out[par]), vp(self.n_missed),
-                          vp(self.workspace), self.top_k, kc, self.k_spec, int(t == 0), self.alpha)
+                          vp(self.pred[nxt]), vp(self.partials[par]), vp(self.out[par]), vp(self.missed[par]),
+                          vp(self.workspace), self.top_k, kc, self.k_spec, int(t == 0), self.alpha, bud)
 
     def enqueue(self, q: torch.Tensor, join: bool = False) -> torch.Tensor:
         """Enqueue one step on the layer's streams without touching the caller's stream (for timing loops and graph
@@ -148,6 +165,11 @@ class PRRLayer:
     @property
     def pred_next(self) -> torch.Tensor:
         return self.pred[self.t % 2][..., :self.k_spec]
+
+    @property
+    def n_missed(self) -> torch.Tensor:
+        """Missed blocks per row of the last step (|T minus P|; all of T when nothing was predicted)."""
+        return self.missed[(self.t - 1) % 2]
 
     @property
     def scores_last(self) -> torch.Tensor:

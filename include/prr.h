@@ -114,19 +114,47 @@ prr_status prr_append_kv(const prr_shape* shape, const void* k_new, const void* 
 prr_status prr_score_select(const prr_shape* shape, const void* q, const void* summaries, int32_t top_k,
                             float* scores, int32_t* sel_idx, void* workspace, void* stream);
 
+/* Per-row budgets of the predicted set (PRR summary page: speculative work is held to a dynamic budget; its future
+ * work: adaptive budgeting, and confidence measures for the EMA predictor). The pages give no formula; these two
+ * rules are readings. With a budget, row r of a predicted set holds k_r <= k_spec ascending block ids followed by
+ * k_spec - k_r entries of -1 (empty slots, which speculation skips and repair never matches):
+ *   PRR_BUDGET_MISSES:     k_r = K + ceil(beta * m_r), m_r = missed_prev[r], the blocks row r missed at its last
+ *                          completed step (fp32 product), clamped to [k_min, k_spec]; the set is the top-k_r of the
+ *                          EMA (forced blocks first).
+ *   PRR_BUDGET_CONFIDENCE: with u_n = e_n + c * |s_n - e_n| (fp32; e the updated EMA, s the step's scores), k_r is
+ *                          the number of blocks whose u reaches the K-th entry of the EMA in the selection order
+ *                          (forced blocks first; a forced block reaches every value, and when the K-th entry is
+ *                          forced only forced blocks reach it), clamped to [k_min, k_spec]; the set is the top-k_r
+ *                          of u (forced blocks first, ties to the lower index).
+ * K = top_k, the decode step's true-set size. A NULL budget, or policy PRR_BUDGET_FIXED, keeps k_r = k_spec. */
+typedef enum { PRR_BUDGET_FIXED = 0, PRR_BUDGET_MISSES = 1, PRR_BUDGET_CONFIDENCE = 2 } prr_budget_policy;
+typedef struct {
+  int32_t policy;               /* prr_budget_policy                                                              */
+  int32_t top_k;                /* K, 1 <= top_k <= N                                                             */
+  int32_t k_min;                /* 1 <= k_min <= k_spec                                                           */
+  float beta;                   /* PRR_BUDGET_MISSES: blocks added per missed block, finite, >= 0                */
+  float c;                      /* PRR_BUDGET_CONFIDENCE: weight of |s - e|, finite, >= 0                         */
+  const int32_t* missed_prev;   /* PRR_BUDGET_MISSES: int32 [B, Hkv] on the device (a buffer the step did not
+                                   just write: double-buffer the missed counts across steps)                      */
+} prr_budget;
+
 /* EMA score predictor (PRR abstract: a light predictor built on an exponential moving average): ema = scores when
  * first_step != 0, else ema = alpha * ema + (1 - alpha) * scores (in place); then pred_idx_next[b,g,:] = top-k_spec
  * of ema, ties to the lower index, forced blocks first (as the selection), ascending — the predicted set for the next
  * decode step. Requires 1 <= k_spec <= N. `workspace` as in prr_score_select (its predicted-set candidate region
- * only, so the two selections may run at once). */
+ * only, so the two selections may run at once). `budget` (NULL: fixed) sizes each row's set as described above; a
+ * budgeted row selects in one workgroup (rows of at most 32768 blocks) and does not use the workspace. */
 prr_status prr_ema_predict(const prr_shape* shape, const float* scores, float* ema, float alpha, int32_t first_step,
-                           int32_t k_spec, int32_t* pred_idx_next, void* workspace, void* stream);
+                           int32_t k_spec, int32_t* pred_idx_next, const prr_budget* budget, void* workspace,
+                           void* stream);
 
 /* Speculative attention (PRR abstract: speculate the attention over the predicted blocks while selection is in
  * flight): for every (b, g) and predicted slot j < k_spec, with n = pred_idx[b,g,j] and each query head h of the
  * group, z_i = softmax_scale * q[b,h] . k_i over the block's tokens; the block's partial state m = max z,
  * l = sum exp(z - m), O = sum exp(z - m) v_i is stored as the record (b, g, j) of `partials`, in the base-2 form
- * given under Layouts (m2 = m * log2 e, the same l and O). k_spec == 0 enqueues nothing. */
+ * given under Layouts (m2 = m * log2 e, the same l and O). k_spec == 0 enqueues nothing. A negative id marks an
+ * empty slot (a budgeted prediction's padding): nothing is computed or written for it; empty slots must follow every
+ * id of their row. Ids >= N are clamped to N - 1 (a wrong result, never an out-of-bounds read). */
 prr_status prr_speculate(const prr_shape* shape, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_table, const int32_t* pred_idx, int32_t k_spec, float* partials,
                          void* stream);
@@ -155,12 +183,14 @@ prr_status prr_score(const prr_shape* shape, const void* q, const void* summarie
  * Selection occupies one workgroup per row and is bound by latency, so speculation runs in its shadow (PRR
  * abstract: speculation overlaps selection). pred_idx and pred_idx_next must be different buffers. `workspace`
  * (prr_workspace_bytes bytes) or NULL: with it, rows of more than 8192 blocks (with top_k and k_spec_next <= 1024)
- * select by segments of 2048 values in this launch and merge the candidates in a second one. */
+ * select by segments of 2048 values in this launch and merge the candidates in a second one. `budget` (NULL: fixed)
+ * sizes each row of pred_idx_next as in prr_ema_predict (`scores` are the step's s, `ema` the updated e); budgeted
+ * rows select in one workgroup per row. */
 prr_status prr_select_speculate(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
                                 const float* ema, int32_t k_spec_next, int32_t* pred_idx_next, const void* q,
                                 const void* k_cache, const void* v_cache, const int32_t* block_table,
-                                const int32_t* pred_idx, int32_t k_spec, float* partials, void* workspace,
-                                void* stream);
+                                const int32_t* pred_idx, int32_t k_spec, float* partials, const prr_budget* budget,
+                                void* workspace, void* stream);
 
 /* Scores (+ the EMA update when ema != NULL, as prr_score) and the speculation of prr_speculate over pred_idx
  * (k_spec slots), in ONE launch whose workgroups of the two roles run concurrently (PRR abstract: speculation runs
@@ -221,6 +251,8 @@ typedef struct {
   float* out; int32_t* n_missed; void* workspace;
   int32_t top_k, k_spec_cur, k_spec_next, first_step;
   float alpha;
+  const prr_budget* budget;    /* NULL: fixed k_spec_next per row; else per-row budgets (prr_ema_predict). pred_cur
+                                  may then hold empty (-1) slots. Its top_k must equal this step's top_k. */
 } prr_step_args;
 
 /* Opaque host object holding the events that order the two streams (no device memory). */

@@ -81,10 +81,10 @@ def test_argument_validation_without_launch():
     assert lib.prr_score(ctypes.byref(s), nz, nz, nz, nz, -0.5, 0, None) == -1            # alpha < 0 with an EMA
     # select_speculate: prediction needs the EMA; speculation needs its buffers; P_t and P_{t+1} buffers differ
     assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, None, 8, nz, None, None, None, None, None, 0, None,
-                                    None, None) == -1
+                                    None, None, None) == -1
     assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, None, 0, None, nz, None, nz, nz, nz, 4, nz,
-                                    None, None) == -1
-    assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, nz, 8, nz, nz, nz, nz, nz, nz, 8, nz, None,
+                                    None, None, None) == -1
+    assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, nz, 8, nz, nz, nz, nz, nz, nz, 8, nz, None, None,
                                     None) == -1
     # select_repair: argument checks, then the supported-shape rule (page size multiple of 16, K <= 2048)
     assert lib.prr_select_repair(ctypes.byref(s), nz, 8, nz, None, 0, None, nz, nz, nz, nz, None, 4, None, nz, nz,
@@ -99,8 +99,18 @@ def test_argument_validation_without_launch():
                                  nz, nz, None) == -2                                          # K > 2048
     assert lib.prr_score_speculate(ctypes.byref(s), nz, nz, nz, None, 0.5, 0, None, None, None, None, 4, None,
                                    None) == -1                                                # k_spec > 0, no KV
-    assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 0.9, 0, 0, nz, None, None) == -1        # K' < 1
-    assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 1.5, 0, 8, nz, None, None) == -1        # alpha > 1
+    assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 0.9, 0, 0, nz, None, None, None) == -1   # K' < 1
+    assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 1.5, 0, 8, nz, None, None, None) == -1   # alpha > 1
+    # per-row budgets: policy, K, k_min, beta / c and the missed counts are checked before any launch
+    for bad in (L.Budget(7, 8, 1, 0.5, 0.0, 16), L.Budget(L.BUDGET_MISSES, 0, 1, 0.5, 0.0, 16),
+                L.Budget(L.BUDGET_MISSES, 8, 0, 0.5, 0.0, 16), L.Budget(L.BUDGET_MISSES, 8, 9, 0.5, 0.0, 16),
+                L.Budget(L.BUDGET_MISSES, 8, 1, -0.5, 0.0, 16), L.Budget(L.BUDGET_MISSES, 8, 1, float("nan"), 0.0, 16),
+                L.Budget(L.BUDGET_MISSES, 8, 1, 0.5, 0.0, None), L.Budget(L.BUDGET_CONFIDENCE, 8, 1, 0.0, -1.0, None),
+                L.Budget(L.BUDGET_CONFIDENCE, 8, 1, 0.0, float("inf"), None),
+                L.Budget(L.BUDGET_CONFIDENCE, s.n_blocks + 1, 1, 0.0, 1.0, None)):
+        assert lib.prr_ema_predict(ctypes.byref(s), nz, nz, 0.9, 0, 8, nz, ctypes.byref(bad), None, None) == -1, bad
+        assert lib.prr_select_speculate(ctypes.byref(s), nz, 8, nz, nz, 8, nz, None, None, None, None, None, 0, None,
+                                        ctypes.byref(bad), None, None) == -1, bad
     assert lib.prr_speculate(ctypes.byref(s), nz, nz, nz, nz, nz, -1, nz, None) == -1      # K' < 0
     assert lib.prr_speculate(ctypes.byref(s), None, None, None, None, None, 0, None, None) == 0   # K' = 0: no-op
     assert lib.prr_repair_merge(ctypes.byref(s), nz, nz, nz, nz, nz, 8, None, 4, None, nz, nz, nz, None) == -1

@@ -1,0 +1,190 @@
+"""Per-row budgets of the predicted set (prr_budget: the misses rule and the confidence rule) against the oracle.
+
+The budgets are integer decisions taken in fp32 from fp32 inputs, so the device must match the oracle exactly once
+both start from the same fp32 values: the tests hand the oracle the device's own EMA (itself checked against the
+oracle's update within fp32 rounding) and the scores the device read. Each row's set is its first k_r entries
+(ascending block ids) followed by -1 up to the capacity; speculation skips the -1 slots and repair never matches
+them, so the step's output stays the oracle's attention over the true set."""
+import numpy as np
+import pytest
+import torch
+
+from dynamic_sparse_attention_decode_amd import _lib as L
+from dynamic_sparse_attention_decode_amd.inputs import make_inputs
+from dynamic_sparse_attention_decode_amd.runtime import PRRLayer
+from oracle import prr_oracle as O
+from tests.checker import TOL, check_selection, max_abs
+from tests.gpu_common import OracleView, np64, oracle_scores, requires_gpu, shape_of, small
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+POLICIES = {"misses": L.BUDGET_MISSES, "confidence": L.BUDGET_CONFIDENCE}
+
+
+def _expected_row(policy, s_row, e_row, m, K, cap, k_min, beta, c, sink, local):
+    """The oracle's predicted set of one row (ascending ids, then -1 up to cap)."""
+    if policy == "misses":
+        k = int(O.budget_from_misses([m], K, cap, beta, k_min)[0])
+        ids = O.top_k(e_row.astype(np.float64), k, sink, local)
+    else:
+        ids = O.predict_confident(s_row, e_row, K, cap, c, k_min, sink, local)
+    out = np.full(cap, -1, dtype=np.int64)
+    out[:len(ids)] = ids
+    return out
+
+
+def _rows(rng, rows, N, kind):
+    if kind == "normal":
+        s = rng.standard_normal((rows, N)) * 3 + 20
+        e = s + rng.standard_normal((rows, N)) * 2
+    else:   # many equal values: ties resolved by index on both sides
+        s = np.round(rng.standard_normal((rows, N)) * 2)
+        e = np.round(s + rng.standard_normal((rows, N)))
+    return s.astype(np.float32), e.astype(np.float32)
+
+
+@pytest.mark.parametrize("policy", ["misses", "confidence"])
+@pytest.mark.parametrize("n_blocks", [129, 2048, 4096, 6000, 20001])
+def test_ema_predict_budget(policy, n_blocks):
+    """prr_ema_predict with a budget: the EMA update, each row's size and set (forced blocks included) against the
+    oracle, for row lengths across the workgroup shapes (512 threads up to 4096 blocks, 1024 beyond), random and
+    tie-heavy values, first and later steps."""
+    rng = np.random.default_rng(n_blocks)
+    rows, N = 6, n_blocks
+    K = min(N, 40)
+    cap = min(N, 90)
+    for kind in ("normal", "ties"):
+        for first in (False, True):
+            for (sink, local) in ((0, 0), (1, 3)):
+                print(f"[case] ema_predict budget {policy} N={N} {kind} first={first} sink={sink} local={local}",
+                      flush=True)
+                s = L.make_shape(1, 4 * rows, rows, 128, 16, 16, N, L.BF16, sink_blocks=sink, local_blocks=local)
+                s32, e32 = _rows(rng, rows, N, kind)
+                m = rng.integers(0, K + 1, size=rows).astype(np.int32)
+                k_min = int(rng.integers(1, K + 1))
+                beta, c = 0.7, 0.4
+                scores = torch.as_tensor(s32[None], device="cuda").contiguous()
+                ema = torch.as_tensor(e32[None], device="cuda").contiguous()
+                missed = torch.as_tensor(m[None], device="cuda").contiguous()
+                pred = torch.full((1, rows, cap), -7, dtype=torch.int32, device="cuda")
+                bud = L.make_budget(POLICIES[policy], K, k_min, beta, c, missed)
+                L.ema_predict(s, scores, ema, 0.8, first, cap, pred, budget=bud)
+                torch.cuda.synchronize()
+                e_gpu = ema.cpu().numpy()[0]
+                ref_e = np.stack([O.ema_update(e32[r], s32[r], 0.8, first) for r in range(rows)])
+                assert np.allclose(e_gpu, ref_e, rtol=1e-6, atol=1e-5)
+                got = pred.cpu().numpy()[0]
+                for r in range(rows):
+                    ref = _expected_row(policy, s32[r], e_gpu[r], int(m[r]), K, cap, k_min, beta, c, sink, local)
+                    assert np.array_equal(got[r], ref), (r, got[r][:12], ref[:12])
+
+
+@pytest.mark.parametrize("policy", ["misses", "confidence"])
+@pytest.mark.parametrize("n_blocks", [2048, 20001])
+def test_select_speculate_budget(policy, n_blocks):
+    """prr_select_speculate with a budget: T as without one; P_{t+1} from the already updated EMA by the budget
+    (in the selection launch up to 8192 blocks, in a launch of its own beyond); speculation over a padded P_t writes
+    the records of its filled slots exactly as prr_speculate does and leaves the -1 slots untouched."""
+    rng = np.random.default_rng(7 + n_blocks)
+    N = n_blocks
+    s = L.make_shape(1, 32, 8, 128, 16, 16, N, L.BF16)
+    rows, K, cap = 8, 30, 45
+    inp_k = torch.randn((N, 8, 16, 128), device="cuda").to(torch.bfloat16)
+    inp_v = torch.randn((N, 8, 16, 128), device="cuda").to(torch.bfloat16)
+    table = torch.arange(N, dtype=torch.int32, device="cuda")[None].contiguous()
+    q = torch.randn((1, 32, 128), device="cuda").to(torch.bfloat16)
+    s32, e32 = _rows(rng, rows, N, "normal")
+    scores = torch.as_tensor(s32[None], device="cuda").contiguous()
+    ema = torch.as_tensor(e32[None], device="cuda").contiguous()
+    m = rng.integers(0, K + 1, size=rows).astype(np.int32)
+    missed = torch.as_tensor(m[None], device="cuda").contiguous()
+    # P_t: filled prefixes of various lengths, then -1
+    p_cur = np.full((rows, cap), -1, dtype=np.int32)
+    for r in range(rows):
+        n_fill = int(rng.integers(0, cap + 1))
+        p_cur[r, :n_fill] = np.sort(rng.choice(N, size=n_fill, replace=False))
+    pred_cur = torch.as_tensor(p_cur[None], device="cuda").contiguous()
+    pb = L.partials_bytes(s, cap) // 4
+    part = torch.full((pb,), 12345.0, dtype=torch.float32, device="cuda")
+    part_ref = torch.full((pb,), 12345.0, dtype=torch.float32, device="cuda")
+    sel = torch.zeros((1, rows, K), dtype=torch.int32, device="cuda")
+    pred_next = torch.full((1, rows, cap), -7, dtype=torch.int32, device="cuda")
+    ws = torch.zeros((L.workspace_bytes(s, K) // 4 + 1,), dtype=torch.float32, device="cuda")
+    bud = L.make_budget(POLICIES[policy], K, 5, 0.7, 0.4, missed)
+    L.select_speculate(s, scores, K, sel, ema, cap, pred_next, q, inp_k, inp_v, table, pred_cur, cap, part,
+                       workspace=ws, budget=bud)
+    L.speculate(s, q, inp_k, inp_v, table, pred_cur, cap, part_ref)
+    torch.cuda.synchronize()
+    got_sel = sel.cpu().numpy()[0]
+    for r in range(rows):
+        assert np.array_equal(got_sel[r], O.top_k(s32[r].astype(np.float64), K))
+    got_p = pred_next.cpu().numpy()[0]
+    for r in range(rows):
+        ref = _expected_row(policy, s32[r], e32[r], int(m[r]), K, cap, 5, 0.7, 0.4, 0, 0)
+        assert np.array_equal(got_p[r], ref), (r, got_p[r][:12], ref[:12])
+    # the records: equal to the standalone speculation's where filled; untouched where empty
+    rf = ((2 * 4 + 3) & ~3) + 4 * 128   # a record: m[G], l[G], padding to 4 floats, O[G][D] (G = 4, D = 128)
+    a = part.cpu().numpy()[:rows * cap * rf].reshape(rows, cap, rf)
+    b = part_ref.cpu().numpy()[:rows * cap * rf].reshape(rows, cap, rf)
+    filled = p_cur >= 0
+    assert np.allclose(a[filled], b[filled], rtol=1e-6, atol=1e-6)
+    assert np.all(a[~filled] == 12345.0) and np.all(b[~filled] == 12345.0)
+
+
+@pytest.mark.parametrize("mode", ["prr_fused", "prr_1stream", "prr_2stream"])
+@pytest.mark.parametrize("policy", ["misses", "confidence"])
+@pytest.mark.parametrize("name", ["tiny_f32_4k", "llama3_8b_32k", "paged_b32_64k", "million_token"])
+def test_decode_with_budget(name, policy, mode):
+    """Whole decode runs with a budget: every step's selection and output against the oracle (the output is
+    attention over the true set whatever was predicted), the missed count = |T minus the filled part of P_t|, and
+    P_{t+1} equal to the oracle's budgeted prediction from the step's scores and EMA and the previous step's missed
+    counts; the sets' sizes vary by row within [k_min, k_spec]."""
+    w = small(name)
+    kp = min(w.n_blocks, max(max(w.k_spec), w.top_k + w.top_k // 2))   # room above K for the sizes to vary
+    k_min = max(1, w.top_k // 2)
+    cfg = {"policy": policy, "k_min": k_min, "beta": 0.5, "c": 0.3}
+    print(f"[case] decode budget {name} {policy} {mode} K'={kp}", flush=True)
+    inp = make_inputs(w, device="cuda")
+    ov = OracleView(inp)
+    layer = PRRLayer(shape_of(w), w.top_k, kp, w.alpha, mode=mode, budget=cfg)
+    layer.build(inp.k_cache, inp.v_cache, inp.table)
+    G = w.group
+    prev_missed = np.zeros((w.batch, w.n_kv_heads), dtype=np.int64)
+    pred_t = None
+    sizes = []
+    for t in range(w.steps):
+        ids = inp.drift(t)
+        if len(ids):
+            layer.rebuild_blocks(torch.as_tensor(ids, device="cuda"))
+            ov.invalidate_keys()
+        out = layer.step(inp.q[t].contiguous())
+        layer.sync_spec()
+        torch.cuda.synchronize()
+        out_h, sel = np64(out), layer.sel_idx.cpu().numpy()
+        nm = layer.n_missed.cpu().numpy()
+        s_gpu = layer.scores_last.cpu().numpy()
+        e_gpu = layer.ema.cpu().numpy()
+        p_next = layer.pred_next.cpu().numpy()
+        for b in range(w.batch):
+            for g in range(w.n_kv_heads):
+                qg = ov.q_group(t, b, g)
+                keys = ov.keys(b, g)
+                check_selection(sel[b, g], oracle_scores(w, qg, keys), w.top_k, n_sink=w.sink_blocks,
+                                n_local=w.local_blocks)
+                ref = O.attention_over_blocks(qg, keys, ov.values(b, g), sel[b, g], w.block_size, w.scale)
+                assert max_abs(out_h[b, g * G:(g + 1) * G], ref) <= TOL[w.dtype], (t, b, g)
+                if pred_t is None:
+                    assert nm[b, g] == w.top_k
+                else:
+                    filled = pred_t[b, g][pred_t[b, g] >= 0]
+                    assert nm[b, g] == len(set(sel[b, g]) - set(filled))
+                exp = _expected_row(policy, s_gpu[b, g], e_gpu[b, g], int(prev_missed[b, g]), w.top_k, kp, k_min,
+                                    0.5, 0.3, w.sink_blocks, w.local_blocks)
+                assert np.array_equal(p_next[b, g], exp), (t, b, g, p_next[b, g][:10], exp[:10])
+                sizes.append(int((p_next[b, g] >= 0).sum()))
+        prev_missed = nm.astype(np.int64)
+        pred_t = p_next.copy()
+    layer.close()
+    assert min(sizes) >= min(k_min, kp) and max(sizes) <= kp
+    print(f"[result] {name} {policy} {mode}: predicted-set sizes {min(sizes)}..{max(sizes)} "
+          f"(mean {np.mean(sizes):.1f}, cap {kp})")
