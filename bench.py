@@ -57,6 +57,12 @@ def parse():
     ap.add_argument("--scorer", default="quest", choices=["quest", "mean"], help="block scorer")
     ap.add_argument("--sink", type=int, default=0, help="attention-sink blocks forced into every selection")
     ap.add_argument("--local", type=int, default=0, help="local-window blocks (the last ones) forced likewise")
+    ap.add_argument("--budget", default="fixed", choices=["fixed", "misses", "confidence"],
+                    help="per-row size of the predicted set (at most --kspec): fixed, K + ceil(beta * missed), or "
+                         "the blocks whose optimistic score e + c|s - e| reaches the K-th EMA entry")
+    ap.add_argument("--budget-beta", type=float, default=1.0, help="misses budget: blocks added per missed block")
+    ap.add_argument("--budget-c", type=float, default=0.5, help="confidence budget: weight of |s - e|")
+    ap.add_argument("--budget-kmin", type=int, default=0, help="smallest per-row budget (0: K, capped at --kspec)")
     ap.add_argument("--other-modes", default="all",
                     help="comma list of further modes to time beside --mode ('all' or 'none')")
     return ap.parse_args()
@@ -114,11 +120,19 @@ def main():
     streams = (torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev))
     qs = [inp.q[t].contiguous() for t in range(w.steps)]
 
+    budget_cfg = None
+    if a.budget != "fixed":
+        budget_cfg = {"policy": a.budget, "beta": a.budget_beta, "c": a.budget_c,
+                      "k_min": a.budget_kmin or min(w.top_k, kspec)}
+
     def make_layers(mode, k_spec=None, n_kv=None):
         ls = []
+        kp = kspec if k_spec is None else k_spec
         for k, v in kvs[:n_kv]:
-            lay = PRRLayer(shape, w.top_k, kspec if k_spec is None else k_spec, w.alpha, mode=mode, device=dev,
-                           streams=streams)
+            bud = budget_cfg if kp > 0 else None
+            if bud is not None and bud["k_min"] > kp:
+                bud = dict(bud, k_min=kp)
+            lay = PRRLayer(shape, w.top_k, kp, w.alpha, mode=mode, device=dev, streams=streams, budget=bud)
             lay.build(k, v, inp.table)
             ls.append(lay)
         torch.cuda.synchronize()
@@ -138,21 +152,25 @@ def main():
 
     # ---- statistics pass: overlap, missed blocks (untimed, per-step syncs) ---------------------------------------
     stat = make_layers(a.mode)[0]
-    missed, overlap = [], []
+    missed, overlap, pred_size = [], [], []
     for i in range(min(w.steps, 32)):
         stat.step(qs[stat.t % w.steps])
+        stat.sync_spec()
         torch.cuda.synchronize()
         if stat.t > 1 and stat.k_spec:
             nm = stat.n_missed.cpu().numpy()
             missed.append(float(nm.mean()))
             overlap.append(float(1.0 - nm.mean() / w.top_k))
+        if stat.k_spec:
+            pred_size.append(float((stat.pred_next >= 0).sum(-1).float().mean()))
     stat.close()
     mean_missed = float(np.mean(missed)) if missed else float(w.top_k)
+    mean_pred = float(np.mean(pred_size)) if pred_size else float(kspec)   # filled slots of a predicted set
     prr_mode = not a.mode.startswith("serialized")
 
     def alg_bytes(mode):
         """Algorithmic bytes per launch of each traced kernel in `mode`."""
-        spec = rows * kspec * blk_kv
+        spec = rows * mean_pred * blk_kv
         rep = rows * (w.top_k if mode.startswith("serialized") else mean_missed) * blk_kv
         if mode == "prr_fused" and (rows >= 128 or w.top_k <= 32):
             # scoring also updates the EMA; the selection launch reads scores and EMA, speculates over P_t and attends
@@ -241,7 +259,7 @@ def main():
                 calls.append(lambda lay=lay, q=q, par=par, nxt=nxt, kc=kc: L.select_speculate(
                     shape, lay.scores[par], K, lay.sel_idx, lay.ema, lay.k_spec, lay.pred[nxt], q, lay.k_cache,
                     lay.v_cache, lay.table, lay.pred[par], kc, lay.partials[par], workspace=lay.workspace,
-                    stream=streams[0]))
+                    stream=streams[0], budget=lay.budgets[par] if lay.budgets else None))
             elif kernel == "speculate" and lay.k_spec:
                 calls.append(lambda lay=lay, q=q, par=par: L.speculate(
                     shape, q, lay.k_cache, lay.v_cache, lay.table, lay.pred[par], lay.k_spec, lay.partials[par],
@@ -322,6 +340,8 @@ def main():
         "attention_path_frac": (attn_bytes / (attn_us * 1e-6) / 1e9) / HBM_PEAK_GBS if attn_us else None,
         "step_alg_bytes": summ_b + attn_bytes,
         "predictor_overlap": float(np.mean(overlap)) if overlap else None,
+        "budget": {"policy": a.budget, **({k: budget_cfg[k] for k in ("beta", "c", "k_min")} if budget_cfg else {}),
+                   "k_spec_cap": kspec, "predicted_blocks_mean": mean_pred},
         "repaired_blocks_mean": mean_missed,
         "layers_rotated": n_layers,
         "touched_MiB_per_step": touched / 2 ** 20,
@@ -378,7 +398,7 @@ def main():
                    "head_dim": w.head_dim, "ctx": w.ctx, "block_size": w.block_size, "page_size": w.page_size,
                    "top_k": w.top_k, "k_spec": kspec, "alpha": w.alpha, "mode": a.mode,
                    "sink_blocks": w.sink_blocks, "local_blocks": w.local_blocks, "scorer": w.scorer,
-                   "layers_rotated": n_layers, "parallelism": "none (1 GPU)"},
+                   "budget": a.budget, "layers_rotated": n_layers, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": dominant, "hip_kernels": HIP_KERNELS.get((a.mode, dominant), dominant),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

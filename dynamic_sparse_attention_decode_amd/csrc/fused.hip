@@ -70,18 +70,24 @@ __global__ __launch_bounds__(kSegSpecThreads, 3) void seg_spec_kernel(const floa
                                                            float* __restrict__ partials, int spw, int wpr,
                                                            int64_t spec_waves, int Hq, int Hkv, int N, int bs,
                                                            int page, int pps, float qscale, int rows, int last_len,
-                                                           int sink, int local) {
+                                                           int sink, int local, int Ke, TopkCand cu, float conf_c) {
   const int64_t r = blockIdx.x;
   if (r < n_seg_wg) {
     const int64_t job = r / S;
     const int seg = (int)(r % S);
-    if (job < rows)
+    if (job < rows) {
       topk_segment<kSegSpecThreads, 8, false>(scores + job * N, nullptr, 0.f, 0, N, K, kSelSpecSeg, seg,
                                               ct.key + job * ct.cap, ct.idx + job * ct.cap, sink, local);
-    else
-      topk_segment<kSegSpecThreads, 8, false>(ema + (job - rows) * N, nullptr, 0.f, 0, N, Kp_next, kSelSpecSeg, seg,
-                                              cp.key + (job - rows) * cp.cap, cp.idx + (job - rows) * cp.cap, sink,
-                                              local);
+    } else if (job < 2 * rows) {   // the EMA's top-Ke of the segment (Ke = K' or, for a confidence budget, K)
+      const int64_t rr = job - rows;
+      topk_segment<kSegSpecThreads, 8, false>(ema + rr * N, nullptr, 0.f, 0, N, Ke, kSelSpecSeg, seg,
+                                              cp.key + rr * cp.cap, cp.idx + rr * cp.cap, sink, local);
+    } else {   // a confidence budget's optimistic scores: the segment's top-K'
+      const int64_t rr = job - 2 * rows;
+      topk_segment<kSegSpecThreads, 8, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp_next, kSelSpecSeg, seg,
+                                              cu.key + rr * cu.cap, cu.idx + rr * cu.cap, sink, local,
+                                              scores + rr * N, conf_c);
+    }
     return;
   }
   // speculation as the standalone kernel does it: spw consecutive slots per wave
@@ -96,24 +102,33 @@ __global__ __launch_bounds__(kSegSpecThreads, 3) void seg_spec_kernel(const floa
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void merge2_kernel(TopkCand ct, int Ct, int K, int32_t* __restrict__ sel,
                                                     TopkCand cp, int Cp, int Kp_next, int32_t* __restrict__ pred_next,
-                                                    int rows) {
+                                                    int rows, BudgetDev bp, TopkCand cu, int Cu) {
   const int64_t r = blockIdx.x;
-  if (r < rows)
+  if (r < rows) {
     topk_merge_row<NT, KPT>(ct.key + r * ct.cap, ct.idx + r * ct.cap, Ct, K, sel + r * K);
+    return;
+  }
+  const int64_t rr = r - rows;
+  if (bp.policy != 0)
+    topk_merge_budget_row<NT, KPT>(cp.key + rr * cp.cap, cp.idx + rr * cp.cap, Cp, cu.key + rr * cu.cap,
+                                   cu.idx + rr * cu.cap, Cu, Kp_next, bp, rr, pred_next + rr * Kp_next);
   else
-    topk_merge_row<NT, KPT>(cp.key + (r - rows) * cp.cap, cp.idx + (r - rows) * cp.cap, Cp, Kp_next,
-                            pred_next + (r - rows) * Kp_next);
+    topk_merge_row<NT, KPT>(cp.key + rr * cp.cap, cp.idx + rr * cp.cap, Cp, Kp_next, pred_next + rr * Kp_next);
 }
 
 template <int DT, int G>
 static void seg_spec_launch(const prr_shape& s, const float* scores, int K, int32_t* sel, const float* ema,
                             int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                             const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                            const TopkCand& ct, const TopkCand& cp, hipStream_t st) {
+                            const TopkCand& ct, const TopkCand& cp, const TopkCand& cu, const BudgetDev& bp,
+                            hipStream_t st) {
   const int rows = s.batch * s.n_kv_heads;
+  const bool conf = kp_next > 0 && bp.policy == 2;
+  const int ke = conf ? bp.top_k : kp_next;   // EMA candidates per segment: K for the confidence rule's theta
   const TopkSplit pt = topk_split(s.n_blocks, K, kSelSpecSeg);
-  const TopkSplit pp = topk_split(s.n_blocks, kp_next > 0 ? kp_next : 1, kSelSpecSeg);
-  const int n_seg_wg = (kp_next > 0 ? 2 : 1) * rows * pt.S;
+  const TopkSplit pp = topk_split(s.n_blocks, kp_next > 0 ? ke : 1, kSelSpecSeg);
+  const TopkSplit pu = topk_split(s.n_blocks, kp_next > 0 ? kp_next : 1, kSelSpecSeg);
+  const int n_seg_wg = (kp_next > 0 ? (conf ? 3 : 2) : 1) * rows * pt.S;
   const int spw = k_spec > 0 ? spec_slots_per_wave(s, k_spec) : 1;
   const int wpr = (k_spec + spw - 1) / spw;
   const int64_t spec_waves = (int64_t)rows * wpr;
@@ -124,11 +139,13 @@ static void seg_spec_launch(const prr_shape& s, const float* scores, int K, int3
       scores, K, ema, kp_next, pt.S, n_seg_wg, ct, cp, static_cast<const uint8_t*>(q),
       static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, pred, k_spec, partials, spw, wpr,
       spec_waves, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size, s.pages_per_seq,
-      s.softmax_scale * kLog2e, rows, last_block_len(s), s.sink_blocks, s.local_blocks);
-  const int cmax = kp_next > 0 && pp.C > pt.C ? pp.C : pt.C;
+      s.softmax_scale * kLog2e, rows, last_block_len(s), s.sink_blocks, s.local_blocks, ke, cu, bp.c);
+  int cmax = pt.C;
+  if (kp_next > 0) cmax = max(cmax, max(pp.C, conf ? pu.C : 0));
   const dim3 grid((unsigned)((kp_next > 0 ? 2 : 1) * rows));
-#define PRR_MERGE2(NT, KPT) \
-  merge2_kernel<NT, KPT><<<grid, NT, 0, st>>>(ct, pt.C, K, sel, cp, pp.C, kp_next, pred_next, rows)
+#define PRR_MERGE2(NT, KPT)                                                                                        \
+  merge2_kernel<NT, KPT><<<grid, NT, 0, st>>>(ct, pt.C, K, sel, cp, pp.C, kp_next, pred_next, rows,               \
+                                              kp_next > 0 ? bp : BudgetDev{}, cu, pu.C)
   if (cmax <= 4096) {   // 512 threads, as for short rows
     switch (topk_kpt_nt(cmax, 512)) {
       case 1: case 2: case 4: PRR_MERGE2(512, 4); break;
@@ -177,20 +194,26 @@ static void select_spec_launch(const prr_shape& s, const float* scores, int K, i
 prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
                               int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                               const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                              hipStream_t stream, void* cand_t, void* cand_p, const BudgetDev& bp) {
-  if (bp.policy != 0 && kp_next > 0 && s.n_blocks > 16 * kSelSpecThreads) {
+                              hipStream_t stream, void* cand_t, void* cand_p, void* cand_u, const BudgetDev& bp) {
+  // long rows by segments (with the candidate regions): T, the EMA's candidates and, for a confidence budget, the
+  // optimistic scores' candidates; the merge launch applies the budget
+  const int ke = bp.policy == 2 ? bp.top_k : kp_next;
+  const bool split = cand_t && cand_p && (bp.policy != 2 || cand_u) && topk_split_on(s.n_blocks, k, kSelSpecSeg) &&
+                     (kp_next == 0 || (topk_split_on(s.n_blocks, kp_next, kSelSpecSeg) &&
+                                       topk_split_on(s.n_blocks, ke, kSelSpecSeg)));
+  if (bp.policy != 0 && kp_next > 0 && !split && s.n_blocks > 16 * kSelSpecThreads) {
     // budgeted rows this long take their own launch of 1024-thread workgroups, which reads the EMA as it stands
     const prr_status st = launch_select_spec(s, scores, k, sel, nullptr, 0, nullptr, q, kc, vc, table, pred, k_spec,
-                                             partials, stream, cand_t, cand_p, BudgetDev{});
+                                             partials, stream, cand_t, cand_p, cand_u, BudgetDev{});
     if (st != PRR_OK) return st;
     return launch_predict_budget(s, scores, const_cast<float*>(ema), 0.f, 0, kp_next, bp, pred_next, false, stream);
   }
   trace_begin(PRR_KERNEL_SELECT_TOPK, stream);
-  if (bp.policy == 0 && cand_t && cand_p && topk_split_on(s.n_blocks, k, kSelSpecSeg) &&
-      (kp_next == 0 || topk_split_on(s.n_blocks, kp_next, kSelSpecSeg))) {
+  if (split) {
     const TopkCand ct = topk_cand_at(s, cand_t), cp = topk_cand_at(s, cand_p);
+    const TopkCand cu = cand_u ? topk_cand_at(s, cand_u) : TopkCand{nullptr, nullptr, 0};
     PRR_DISPATCH_DT_G(seg_spec_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
-                      partials, ct, cp, stream);
+                      partials, ct, cp, cu, bp, stream);
   } else {
     PRR_DISPATCH_DT_G(select_spec_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
                       partials, bp, stream);

@@ -211,9 +211,9 @@ struct prr_step_ctx {
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// The workspace: two top-K candidate regions for long rows (the true set's and the predicted set's), then the
-// repair's part (spread-out or row-wise repair). The three parts are disjoint, so the true-set selection, the
-// predicted-set selection and the repair may run at once.
+// The workspace: three top-K candidate regions for long rows (the true set's, the predicted set's, and the
+// optimistic scores' of a confidence budget), then the repair's part (spread-out or row-wise repair). The parts are
+// disjoint, so the true-set selection, the predicted-set selection and the repair may run at once.
 static size_t cand_part_bytes(const prr_shape& s) { return round256(topk_cand_bytes(s)); }
 
 static void* cand_region(const prr_shape& s, void* ws, int which) {
@@ -221,7 +221,7 @@ static void* cand_region(const prr_shape& s, void* ws, int which) {
   return static_cast<char*>(ws) + (size_t)which * cand_part_bytes(s);
 }
 
-static void* repair_ws(const prr_shape& s, void* ws) { return static_cast<char*>(ws) + 2 * cand_part_bytes(s); }
+static void* repair_ws(const prr_shape& s, void* ws) { return static_cast<char*>(ws) + 3 * cand_part_bytes(s); }
 
 extern "C" {
 
@@ -335,6 +335,7 @@ prr_status prr_select_speculate(const prr_shape* shape, const float* scores, int
   return launch_select_spec(*shape, scores, top_k, sel_idx, ema, k_spec_next, pred_idx_next, q, k_cache, v_cache,
                             block_table, pred_idx, k_spec, partials, as_stream(stream),
                             cand_region(*shape, workspace, 0), cand_region(*shape, workspace, 1),
+                            cand_region(*shape, workspace, 2),
                             k_spec_next > 0 ? budget_dev(budget) : BudgetDev{});
 }
 
@@ -393,7 +394,7 @@ size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec) {
 size_t prr_workspace_bytes(const prr_shape* shape, int32_t top_k) {
   if (check_shape(shape) != PRR_OK || top_k <= 0) return 0;
   const size_t a = repair_workspace_bytes(*shape, top_k), b = select_missed_ws_bytes(*shape, top_k);
-  return 2 * cand_part_bytes(*shape) + (a > b ? a : b);
+  return 3 * cand_part_bytes(*shape) + (a > b ? a : b);
 }
 
 prr_status prr_step_ctx_create(prr_step_ctx** out) {
@@ -460,9 +461,9 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
   if (budgeted)
     PRR_REQUIRE(budget->top_k == a->top_k, "decode_step: the budget's top_k %d differs from the step's %d",
                 budget->top_k, a->top_k);
-  // budgeted predictions are written by the selection launches of the paths below (one workgroup per row)
-  if (mode == PRR_MODE_FUSED && !budgeted && two_launch_supported(*shape, a->top_k, kc, kn) &&
-      (rows >= 128 || a->top_k <= 32)) {
+  // budgeted predictions are written by the selection launches (one workgroup per row up to 8192 blocks)
+  if (mode == PRR_MODE_FUSED && two_launch_supported(*shape, a->top_k, kc, kn) && (rows >= 128 || a->top_k <= 32) &&
+      !(budgeted && shape->n_blocks > 8192)) {
     // scores + EMA; then selection of T and P_{t+1}, speculation over P_t and the missed blocks T \ P_t in one
     // launch; then the merge of the missed-block records with the speculated records of T ∩ P_t. One workgroup per
     // row attends that row's missed blocks after its selection, which pays off when the rows alone fill the chip or
@@ -474,7 +475,7 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
     return launch_select_missed(*shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,
                                 a->v_cache, a->block_table, kc ? a->pred_cur : nullptr, kc,
                                 kc ? a->partials : nullptr, true, a->out, a->n_missed,
-                                repair_ws(*shape, a->workspace), s1);
+                                repair_ws(*shape, a->workspace), s1, budget_dev(budget));
   }
   // long rows select in two launches (segments, then a merge) through the workspace's candidate regions
   if (mode == PRR_MODE_FUSED) {

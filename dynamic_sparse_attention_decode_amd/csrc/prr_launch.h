@@ -119,7 +119,7 @@ prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, in
                               int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                               const int32_t* table, const int32_t* pred, int k_spec, float* partials,
                               hipStream_t stream, void* cand_t = nullptr, void* cand_p = nullptr,
-                              const BudgetDev& bp = BudgetDev{});
+                              void* cand_u = nullptr, const BudgetDev& bp = BudgetDev{});
 // The two-launch step: scores (+ EMA) with speculation, then selection with the row-wise repair and merge.
 bool two_launch_supported(const prr_shape& s, int top_k, int k_spec, int k_spec_next);
 prr_status launch_score_spec(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema,
@@ -130,7 +130,8 @@ prr_status launch_score_spec(const prr_shape& s, const void* q, const void* summ
 prr_status launch_select_missed(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
                                 int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                                 const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                                bool speculate, float* out, int32_t* n_missed, void* workspace, hipStream_t stream);
+                                bool speculate, float* out, int32_t* n_missed, void* workspace, hipStream_t stream,
+                                const BudgetDev& bp = BudgetDev{});
 size_t select_missed_ws_bytes(const prr_shape& s, int top_k);
 prr_status launch_flush(void* buf, size_t bytes, hipStream_t stream);
 prr_status launch_stream_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);

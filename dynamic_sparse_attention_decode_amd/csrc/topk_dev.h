@@ -236,7 +236,8 @@ struct Force {
 // positions i in ascending order, with their keys.
 template <int NT, int KPT, bool EMA, typename EmitFn>
 __device__ void topk_row_emit(const float* __restrict__ v, float* __restrict__ e_row, float alpha, int first, int N,
-                              int K, EmitFn&& emit, Force force = Force{}) {
+                              int K, EmitFn&& emit, Force force = Force{}, const float* __restrict__ conf_s = nullptr,
+                              float conf_c = 0.f) {
   static_assert(NT >= 256 && NT <= 1024 && NT % 64 == 0, "workgroup size");
   __shared__ TopkLds L;
   const int i0 = threadIdx.x * KPT;
@@ -282,6 +283,13 @@ __device__ void topk_row_emit(const float* __restrict__ v, float* __restrict__ e
     }
   }
 
+  if (conf_s) {   // the values are an EMA row: rank its optimistic scores u = e + c |s - e| instead
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      const float sv = i0 + k < N ? conf_s[i0 + k] : 0.f;
+      x[k] = __fadd_rn(x[k], __fmul_rn(conf_c, fabsf(__fsub_rn(sv, x[k]))));
+    }
+  }
   uint32_t key[KPT];
 #pragma unroll
   for (int k = 0; k < KPT; ++k) key[k] = force(i0 + k) ? 0xFFFFFFFFu : f2key(x[k]);
@@ -397,7 +405,8 @@ __device__ inline void topk_row(const float* __restrict__ v, float* __restrict__
 template <int NT, int KPT, bool EMA>
 __device__ inline void topk_segment(const float* __restrict__ v_row, float* __restrict__ e_row, float alpha, int first,
                                     int N, int K, int seg, int s, uint32_t* __restrict__ ckey_row,
-                                    int32_t* __restrict__ cidx_row, int sink, int local) {
+                                    int32_t* __restrict__ cidx_row, int sink, int local,
+                                    const float* __restrict__ conf_s_row = nullptr, float conf_c = 0.f) {
   const int base = s * seg;
   const int n = min(seg, N - base);
   const int kc = min(K, seg);
@@ -408,7 +417,7 @@ __device__ inline void topk_segment(const float* __restrict__ v_row, float* __re
                                 ok[pos] = key;
                                 oi[pos] = base + i;
                               },
-                              Force{base, N, sink, local});
+                              Force{base, N, sink, local}, conf_s_row ? conf_s_row + base : nullptr, conf_c);
 }
 
 // Top-K of a row's C candidates (C <= NT * KPT) into orow (and lds_out) as K ascending block indices.
@@ -434,6 +443,54 @@ __device__ void topk_merge_row(const uint32_t* __restrict__ ckey_row, const int3
     orow[pos] = b;
     if (lds_out) lds_out[pos] = b;
   });
+}
+
+// The next predicted set of a long row under a budget, from segment candidates (ascending block order): misses:
+// the top-k_r of the EMA candidates (ekey/eidx, C_e of them, at least cap per segment); confidence: theta = the K-th
+// largest EMA candidate key (the segments' top-K, so the row's K-th is among them), k_r = the optimistic-score
+// candidates (ukey/uidx: each segment's top-cap of u) at or above theta, clamped, which equals the count over the
+// whole row clamped to cap, then their top-k_r. Writes orow[0, k_r) and -1 up to cap.
+template <int NT, int KPT>
+__device__ void topk_merge_budget_row(const uint32_t* __restrict__ ekey, const int32_t* __restrict__ eidx, int Ce,
+                                      const uint32_t* __restrict__ ukey, const int32_t* __restrict__ uidx, int Cu,
+                                      int cap, const BudgetDev& bp, int64_t row, int32_t* __restrict__ orow) {
+  __shared__ TopkLds L;
+  const int i0 = threadIdx.x * KPT;
+  int kr = cap;
+  if (bp.policy == 1) {
+    const float grow = fminf(ceilf(bp.beta * (float)bp.missed_prev[row]), (float)cap);
+    kr = min(max(bp.top_k + (int)grow, bp.k_min), cap);
+    topk_merge_row<NT, KPT>(ekey, eidx, Ce, kr, orow);
+  } else {
+    uint32_t key[KPT];
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) key[k] = i0 + k < Ce ? ekey[i0 + k] : 0u;
+    auto valid_e = [&](int k) { return i0 + k < Ce; };
+    uint32_t kmax, kmin;
+    block_key_range<NT>(key, valid_e, kmax, kmin, L);
+    const Radix R = radix_select<NT, KPT>(key, valid_e, kmax, kmin, (uint32_t)bp.top_k, L);
+    uint32_t theta = R.prefix;
+    if (R.shift > 0) {
+      const uint32_t pk = shr(R.prefix, R.shift);
+      uint32_t lo = 0xffffffffu;
+#pragma unroll
+      for (int k = 0; k < KPT; ++k)
+        if (valid_e(k) && shr(key[k], R.shift) == pk) lo = min(lo, key[k]);
+      theta = block_min_u32<NT>(lo, L);
+    }
+    auto valid_u = [&](int k) { return i0 + k < Cu; };
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int k = 0; k < KPT; ++k) {
+      key[k] = i0 + k < Cu ? ukey[i0 + k] : 0u;
+      cnt += valid_u(k) && key[k] >= theta;
+    }
+    uint32_t total;
+    block_scan<NT>(cnt, total, L);
+    kr = min(max((int)total, bp.k_min), cap);
+    select_top<NT, KPT>(key, valid_u, kr, L, [&](uint32_t pos, int j) { orow[pos] = uidx[i0 + j]; });
+  }
+  for (int j = kr + (int)threadIdx.x; j < cap; j += NT) orow[j] = -1;
 }
 
 // Split of a row of N values into segments of seg for a top-K: S segments, kc candidate slots per segment, C

@@ -80,7 +80,8 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
     int32_t* __restrict__ pred_next, const uint8_t* __restrict__ q, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, const int32_t* __restrict__ pred, int k_spec,
     float* __restrict__ partials, int64_t spec_total, MissedWs ws, int32_t* __restrict__ n_missed, int Hq, int Hkv,
-    int N, int bs, int page, int pps, float qscale, int rows, int n_pwg, int last_len, int sink, int local) {
+    int N, int bs, int page, int pps, float qscale, int rows, int n_pwg, int last_len, int sink, int local,
+    BudgetDev bp) {
   using W = Tile<DT, G>;
   constexpr int NW = kSRThreads / 64;
   constexpr int D = W::D;
@@ -91,6 +92,7 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
   __shared__ int32_t s_list[kSRMaxK];   // slots of the hits, then ids of the missed blocks
   __shared__ uint32_t s_scan[NW];
   __shared__ int s_unsorted;
+  __shared__ int s_kf;   // filled slots of P_t (a budgeted set ends in -1 slots)
   __shared__ float s_ml[NW][2 * G];
   __shared__ float s_o[NW][G * D];
   const int64_t r = blockIdx.x;
@@ -104,6 +106,13 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
   }
   if (r >= rows) {   // next step's predicted set
     const int64_t rr = r - rows;
+    if constexpr (KPT <= 16) {   // budgeted rows are routed elsewhere beyond 8192 blocks
+      if (bp.policy != 0) {
+        predict_row<kSRThreads, KPT, false>(scores + rr * N, const_cast<float*>(ema) + rr * N, 0.f, 0, N, Kp_next,
+                                            bp, rr, pred_next + rr * Kp_next, Force{0, N, sink, local});
+        return;
+      }
+    }
     topk_row<kSRThreads, KPT, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp_next, pred_next + rr * Kp_next, nullptr,
                                      Force{0, N, sink, local});
     return;
@@ -113,10 +122,14 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
   // ---- T against P_t: slot of every entry of T in P_t (bisection when P_t is ascending) -------------------------
   const int b = (int)(r / Hkv), g = (int)(r % Hkv);
   const int32_t* prow = k_spec ? pred + r * k_spec : nullptr;
-  if (tid == 0) s_unsorted = 0;
+  if (tid == 0) { s_unsorted = 0; s_kf = k_spec; }
   for (int i = tid; i < k_spec; i += kSRThreads) s_P[i] = prow[i];
   __syncthreads();
-  for (int i = tid; i + 1 < k_spec; i += kSRThreads)
+  for (int i = tid; i < k_spec; i += kSRThreads)
+    if (s_P[i] < 0) atomicMin(&s_kf, i);
+  __syncthreads();
+  const int kf = s_kf;   // the slots from the first empty one on never match
+  for (int i = tid; i + 1 < kf; i += kSRThreads)
     if (s_P[i] >= s_P[i + 1]) s_unsorted = 1;
   __syncthreads();
   const bool sorted = s_unsorted == 0;
@@ -127,17 +140,17 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
   for (int u = 0; u < EPT; ++u) {
     const int j = tid * EPT + u;
     slot[u] = -1;
-    if (j < K && k_spec > 0) {
+    if (j < K && kf > 0) {
       const int n = s_T[j];
       if (sorted) {
-        int lo = 0, hi = k_spec;   // first index with s_P[idx] >= n
+        int lo = 0, hi = kf;   // first index with s_P[idx] >= n
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
           if (s_P[mid] < n) lo = mid + 1; else hi = mid;
         }
-        if (lo < k_spec && s_P[lo] == n) slot[u] = lo;
+        if (lo < kf && s_P[lo] == n) slot[u] = lo;
       } else {
-        for (int i = 0; i < k_spec; ++i)
+        for (int i = 0; i < kf; ++i)
           if (s_P[i] == n) { slot[u] = i; break; }
       }
     }
@@ -360,7 +373,8 @@ template <int DT, int G>
 static void select_missed_launch(const prr_shape& s, const float* scores, int K, int32_t* sel, const float* ema,
                                  int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                                  const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                                 bool speculate, float* out, int32_t* n_missed, void* workspace, hipStream_t st) {
+                                 bool speculate, float* out, int32_t* n_missed, void* workspace, const BudgetDev& bp,
+                                 hipStream_t st) {
   constexpr int D = 16 * Vec<DT>::n;
   const int rows = s.batch * s.n_kv_heads;
   MissedWs ws;
@@ -379,7 +393,7 @@ static void select_missed_launch(const prr_shape& s, const float* scores, int K,
                                                          table, pred, k_spec, partials, spec_total, ws, n_missed,   \
                                                          s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size,       \
                                                          s.page_size, s.pages_per_seq, qs, rows, n_pwg,             \
-                                                         last_block_len(s), s.sink_blocks, s.local_blocks)
+                                                         last_block_len(s), s.sink_blocks, s.local_blocks, bp)
   trace_begin(PRR_KERNEL_SELECT_TOPK, st);
   if (s.n_blocks <= 4 * kSRThreads)
     PRR_SELMISS(4);
@@ -398,9 +412,10 @@ static void select_missed_launch(const prr_shape& s, const float* scores, int K,
 prr_status launch_select_missed(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
                                 int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                                 const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                                bool speculate, float* out, int32_t* n_missed, void* workspace, hipStream_t stream) {
+                                bool speculate, float* out, int32_t* n_missed, void* workspace, hipStream_t stream,
+                                const BudgetDev& bp) {
   PRR_DISPATCH_DT_G(select_missed_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
-                    partials, speculate, out, n_missed, workspace, stream);
+                    partials, speculate, out, n_missed, workspace, bp, stream);
   return check_launch("select_repair");
 }
 

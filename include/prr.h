@@ -184,8 +184,8 @@ prr_status prr_score(const prr_shape* shape, const void* q, const void* summarie
  * abstract: speculation overlaps selection). pred_idx and pred_idx_next must be different buffers. `workspace`
  * (prr_workspace_bytes bytes) or NULL: with it, rows of more than 8192 blocks (with top_k and k_spec_next <= 1024)
  * select by segments of 2048 values in this launch and merge the candidates in a second one. `budget` (NULL: fixed)
- * sizes each row of pred_idx_next as in prr_ema_predict (`scores` are the step's s, `ema` the updated e); budgeted
- * rows select in one workgroup per row. */
+ * sizes each row of pred_idx_next as in prr_ema_predict (`scores` are the step's s, `ema` the updated e); with the
+ * workspace, budgeted long rows select by segments too (a confidence budget uses the third candidate region). */
 prr_status prr_select_speculate(const prr_shape* shape, const float* scores, int32_t top_k, int32_t* sel_idx,
                                 const float* ema, int32_t k_spec_next, int32_t* pred_idx_next, const void* q,
                                 const void* k_cache, const void* v_cache, const int32_t* block_table,
@@ -220,7 +220,8 @@ prr_status prr_select_repair(const prr_shape* shape, const float* scores, int32_
 /* Bytes of the partials buffer for a speculation budget k_spec (0 for k_spec == 0). */
 size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec);
 /* Bytes of the workspace of the selection calls, prr_repair_merge, prr_select_repair and prr_decode_step for top_k:
- * two top-K candidate regions (true set, predicted set; empty unless N > 8192), then the repair region. */
+ * three top-K candidate regions (true set, predicted set, a confidence budget's optimistic scores; empty unless
+ * N > 8192), then the repair region. */
 size_t prr_workspace_bytes(const prr_shape* shape, int32_t top_k);
 
 /* ---- one decode step on two streams (the runtime around the calls above) ------------------------------------ */

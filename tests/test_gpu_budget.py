@@ -79,15 +79,19 @@ def test_ema_predict_budget(policy, n_blocks):
                     assert np.array_equal(got[r], ref), (r, got[r][:12], ref[:12])
 
 
+@pytest.mark.parametrize("forced", [(0, 0), (2, 3)])
+@pytest.mark.parametrize("with_ws", [True, False])
 @pytest.mark.parametrize("policy", ["misses", "confidence"])
 @pytest.mark.parametrize("n_blocks", [2048, 20001])
-def test_select_speculate_budget(policy, n_blocks):
+def test_select_speculate_budget(policy, n_blocks, with_ws, forced):
     """prr_select_speculate with a budget: T as without one; P_{t+1} from the already updated EMA by the budget
-    (in the selection launch up to 8192 blocks, in a launch of its own beyond); speculation over a padded P_t writes
-    the records of its filled slots exactly as prr_speculate does and leaves the -1 slots untouched."""
+    (in the selection launch up to 8192 blocks; beyond, by segments whose candidates the merge launch budgets when a
+    workspace is given, else in a launch of its own), forced blocks included; speculation over a padded P_t writes
+    the records of its filled slots as prr_speculate does and leaves the -1 slots untouched."""
     rng = np.random.default_rng(7 + n_blocks)
     N = n_blocks
-    s = L.make_shape(1, 32, 8, 128, 16, 16, N, L.BF16)
+    sink, local = forced
+    s = L.make_shape(1, 32, 8, 128, 16, 16, N, L.BF16, sink_blocks=sink, local_blocks=local)
     rows, K, cap = 8, 30, 45
     inp_k = torch.randn((N, 8, 16, 128), device="cuda").to(torch.bfloat16)
     inp_v = torch.randn((N, 8, 16, 128), device="cuda").to(torch.bfloat16)
@@ -111,16 +115,17 @@ def test_select_speculate_budget(policy, n_blocks):
     pred_next = torch.full((1, rows, cap), -7, dtype=torch.int32, device="cuda")
     ws = torch.zeros((L.workspace_bytes(s, K) // 4 + 1,), dtype=torch.float32, device="cuda")
     bud = L.make_budget(POLICIES[policy], K, 5, 0.7, 0.4, missed)
+    print(f"[case] select_speculate budget {policy} N={N} workspace={with_ws} sink={sink} local={local}", flush=True)
     L.select_speculate(s, scores, K, sel, ema, cap, pred_next, q, inp_k, inp_v, table, pred_cur, cap, part,
-                       workspace=ws, budget=bud)
+                       workspace=ws if with_ws else None, budget=bud)
     L.speculate(s, q, inp_k, inp_v, table, pred_cur, cap, part_ref)
     torch.cuda.synchronize()
     got_sel = sel.cpu().numpy()[0]
     for r in range(rows):
-        assert np.array_equal(got_sel[r], O.top_k(s32[r].astype(np.float64), K))
+        assert np.array_equal(got_sel[r], O.top_k(s32[r].astype(np.float64), K, sink, local))
     got_p = pred_next.cpu().numpy()[0]
     for r in range(rows):
-        ref = _expected_row(policy, s32[r], e32[r], int(m[r]), K, cap, 5, 0.7, 0.4, 0, 0)
+        ref = _expected_row(policy, s32[r], e32[r], int(m[r]), K, cap, 5, 0.7, 0.4, sink, local)
         assert np.array_equal(got_p[r], ref), (r, got_p[r][:12], ref[:12])
     # the records: equal to the standalone speculation's where filled; untouched where empty
     rf = ((2 * 4 + 3) & ~3) + 4 * 128   # a record: m[G], l[G], padding to 4 floats, O[G][D] (G = 4, D = 128)
