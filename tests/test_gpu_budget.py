@@ -193,3 +193,58 @@ def test_decode_with_budget(name, policy, mode):
     assert min(sizes) >= min(k_min, kp) and max(sizes) <= kp
     print(f"[result] {name} {policy} {mode}: predicted-set sizes {min(sizes)}..{max(sizes)} "
           f"(mean {np.mean(sizes):.1f}, cap {kp})")
+
+
+@pytest.mark.parametrize("rows,mode,policy", [("short", "prr_fused", "misses"), ("short", "prr_fused", "confidence"),
+                                              ("short", "prr_2stream", "misses"),
+                                              ("long", "prr_fused", "confidence"), ("long", "prr_fused", "misses")])
+def test_budget_graph_replay_matches_eager(rows, mode, policy):
+    """Budgeted steps captured in a HIP graph and replayed several times (eager work and synchronisation between the
+    replays) give the same outputs, selections, missed counts and predicted sets as the same steps run eagerly: the
+    budgets read their missed counts through device pointers, so a captured graph keeps adapting. Long rows (12000
+    blocks) select and predict by segments through the workspace's three candidate regions."""
+    if rows == "short":
+        w = small("llama3_8b_32k")
+    else:
+        w = small("million_token").replace(ctx=32 * 12000 - 7, top_k=61, k_spec=(93,), steps=6)
+    kp = min(w.n_blocks, max(max(w.k_spec), w.top_k + w.top_k // 2))
+    cfg = {"policy": policy, "k_min": max(1, w.top_k // 2), "beta": 0.5, "c": 0.3}
+    print(f"[case] budget graph replay {rows} rows N={w.n_blocks} {mode} {policy}", flush=True)
+    inp = make_inputs(w, device="cuda")
+    qs = [inp.q[t].contiguous() for t in range(w.steps)]
+    seq = [0] + [1, 2, 3, 4] * 3
+    eager = PRRLayer(shape_of(w), w.top_k, kp, w.alpha, mode=mode, budget=cfg)
+    eager.build(inp.k_cache, inp.v_cache, inp.table)
+    ref = []
+    for t in seq:
+        out = eager.step(qs[t])
+        eager.sync_spec()
+        torch.cuda.synchronize()
+        ref.append((np64(out), eager.sel_idx.cpu().numpy().copy(), eager.n_missed.cpu().numpy().copy(),
+                    eager.pred_next.cpu().numpy().copy()))
+    eager.close()
+    lay = PRRLayer(shape_of(w), w.top_k, kp, w.alpha, mode=mode, budget=cfg)
+    lay.build(inp.k_cache, inp.v_cache, inp.table)
+    lay.step(qs[0])
+    lay.sync_spec()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=lay.s_sel):
+        outs = [lay.enqueue(qs[t], join=(t == 4)) for t in (1, 2, 3, 4)]
+    sizes = set()
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        scratch = torch.randn(1 << 16, device="cuda").sum()   # unrelated eager work between replays
+        torch.cuda.synchronize()
+        base = 1 + 4 * r
+        for i in (2, 3):   # the two output buffers hold the last two steps of the replay
+            assert np.array_equal(np64(outs[i]), ref[base + i][0]), (r, i)
+        assert np.array_equal(lay.sel_idx.cpu().numpy(), ref[base + 3][1])
+        assert np.array_equal(lay.n_missed.cpu().numpy(), ref[base + 3][2])
+        p = lay.pred_next.cpu().numpy()
+        assert np.array_equal(p, ref[base + 3][3])
+        sizes.update((p >= 0).sum(-1).ravel().tolist())
+        del scratch
+    lay.close()
+    print(f"[result] predicted-set sizes seen after replays: {sorted(sizes)}")
