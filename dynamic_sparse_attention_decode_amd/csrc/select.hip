@@ -4,9 +4,11 @@
 //
 // score_kernel: Quest's group-summed block score (or the mean-key score) as a streaming GEMV over all CUs
 //   (score_dev.h); optionally updates the EMA in the same pass.
-// topk_kernel: one 1024-thread workgroup per (b, g) row (topk_dev.h); optionally updates the EMA first.
+// topk_kernel: one workgroup per (b, g) row, 512 threads up to 4096 values and 1024 beyond (topk_dev.h);
+//   optionally updates the EMA first.
 // topk_seg_kernel + topk_merge_kernel: the same top-K for long rows when a candidate workspace is given: one
 //   workgroup per segment of 4096 values, then one per row over the segments' candidates.
+// predict_budget_kernel: the next predicted set of each row under a per-row budget (topk_dev.h predict_row).
 #include "score_dev.h"
 #include "topk_dev.h"
 
