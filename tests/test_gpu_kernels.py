@@ -18,6 +18,9 @@ def _setup(name, seed_shift=0):
     if name == "paged_wide":   # a wide batch of short rows
         w = small("paged_b32_64k")
         w = w.replace(batch=17, ctx=w.block_size * 70, top_k=12, k_spec=(12,), steps=4)
+    elif name == "paged_many":   # 512 rows: the spread-out repair takes 8 entries of T per wave (a ragged last one)
+        w = small("paged_b32_64k")
+        w = w.replace(batch=64, ctx=w.block_size * 160, top_k=61, k_spec=(61,), steps=4)
     else:
         w = small(name)
     if seed_shift:
@@ -175,11 +178,12 @@ def _forced_sets(rng, T, N, Kp_list):
     return sets
 
 
-@pytest.mark.parametrize("name", SMALL + ["paged_wide"])
+@pytest.mark.parametrize("name", SMALL + ["paged_wide", "paged_many"])
 def test_repair_merge_forced_predictions(name):
     """Whatever the predicted set (empty, equal, random, disjoint, superset, partial, unsorted), the repaired output
     equals attention over the true set and the missed count is |T \\ P| (PRR summary page, Key findings); also on a
-    wide batch of 17 sequences (136 rows) with short rows."""
+    wide batch of 17 sequences (136 rows) with short rows, and on 512 rows, where each repair wave takes several
+    entries of the true set."""
     w, inp, s, summ, ov = _setup(name)
     B, Hkv, N, K, G = w.batch, w.n_kv_heads, w.n_blocks, w.top_k, w.group
     t = 2
