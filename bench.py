@@ -152,7 +152,8 @@ def main():
 
     # ---- statistics pass: overlap, missed blocks (untimed, per-step syncs) ---------------------------------------
     stat = make_layers(a.mode)[0]
-    missed, overlap, pred_size = [], [], []
+    missed, missed_max, overlap, pred_size = [], 0, [], []
+    banded, instances = 0, 0
     for i in range(min(w.steps, 32)):
         stat.step(qs[stat.t % w.steps])
         stat.sync_spec()
@@ -160,9 +161,16 @@ def main():
         if stat.t > 1 and stat.k_spec:
             nm = stat.n_missed.cpu().numpy()
             missed.append(float(nm.mean()))
+            missed_max = max(missed_max, int(nm.max()))
             overlap.append(float(1.0 - nm.mean() / w.top_k))
         if stat.k_spec:
             pred_size.append(float((stat.pred_next >= 0).sum(-1).float().mean()))
+        if w.top_k < w.n_blocks:   # rows whose relative gap at the K-th score is within 1e-4 (several valid sets)
+            srt = np.sort(stat.scores_last.cpu().numpy().reshape(-1, w.n_blocks), axis=1)[:, ::-1]
+            sk, sk1 = srt[:, w.top_k - 1].astype(np.float64), srt[:, w.top_k].astype(np.float64)
+            gap = (sk - sk1) / np.maximum(np.abs(sk), 1e-30)
+            banded += int((gap <= 1e-4).sum())
+            instances += len(gap)
     stat.close()
     mean_missed = float(np.mean(missed)) if missed else float(w.top_k)
     mean_pred = float(np.mean(pred_size)) if pred_size else float(kspec)   # filled slots of a predicted set
@@ -343,11 +351,31 @@ def main():
         "budget": {"policy": a.budget, **({k: budget_cfg[k] for k in ("beta", "c", "k_min")} if budget_cfg else {}),
                    "k_spec_cap": kspec, "predicted_blocks_mean": mean_pred},
         "repaired_blocks_mean": mean_missed,
+        "repaired_blocks_max": missed_max if missed else w.top_k,
+        "banded_instances": {"count": banded, "of": instances,
+                             "rule": "relative gap at the K-th score <= 1e-4 (from the device's scores)"},
         "layers_rotated": n_layers,
         "touched_MiB_per_step": touched / 2 ** 20,
         "working_set_MiB": n_layers * (kv_layer + summ_layer) / 2 ** 20,
     }
     detail["step_GBps"] = detail["step_alg_bytes"] / (us * 1e-6) / 1e9
+    # the achievable streaming-read bandwidth of this GPU (2 GiB, beyond the Infinity Cache), for a second fraction
+    rd = torch.empty((2 << 30,), dtype=torch.uint8, device=dev)
+    rd_sink = torch.zeros((65536,), dtype=torch.float32, device=dev)
+    L.flush_write(rd)
+    L.stream_read(rd, rd_sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        L.stream_read(rd, rd_sink)
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = 5 * rd.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del rd, rd_sink
+    detail["hbm_read_GBps_measured"] = read_gbs
+    detail["attention_path_frac_of_measured"] = (detail["attention_path_GBps"] / read_gbs
+                                                 if detail["attention_path_GBps"] else None)
     if n_layers > 1:   # the same step with one layer only: its data stays in the Infinity Cache between steps
         detail["us_per_step_one_layer_cache_warm"] = measure(a.mode, n_kv=1)[0]
     if len(w.k_spec) > 1 and a.mode != "serialized":   # the workload sweeps its speculation budget
