@@ -260,8 +260,8 @@ def budget_from_misses(missed_prev, k_top: int, k_cap: int, beta: float, k_min: 
     k = K + ceil(beta * m), clamped to [k_min, k_cap]. A row whose prediction missed more blocks speculates more.
     beta * m is an fp32 product."""
     m = np.asarray(missed_prev).astype(np.float32)
-    grow = np.ceil(np.float32(beta) * m).astype(np.int64)
-    return np.minimum(np.maximum(k_top + grow, k_min), k_cap)
+    grow = np.minimum(np.ceil(np.float32(beta) * m), np.float32(k_cap))   # k_cap bounds k anyway; keeps the cast exact
+    return np.minimum(np.maximum(k_top + grow.astype(np.int64), k_min), k_cap)
 
 
 def confidence_bound(scores, ema, c: float) -> np.ndarray:

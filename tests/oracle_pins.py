@@ -365,6 +365,7 @@ def pin_adaptive_budgets(o):
     assert o.budget_from_misses([50], 4, 64, 0.3, 1).tolist() == [20]          # fp32: 0.3f * 50 = 15.000001
     assert o.budget_from_misses([50], 4, 64, 1.1, 1).tolist() == [59]          # fp32: 1.1f * 50 = 55.0
     assert o.budget_from_misses([1], 4, 64, 0.25, 1).tolist() == [5]           # ceil(0.25) = 1
+    assert o.budget_from_misses([5, 0], 8, 20, 1e30, 1).tolist() == [20, 8]    # a huge product stays at the cap
 
     f32 = np.float32
     rng = np.random.default_rng(29)
