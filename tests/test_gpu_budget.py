@@ -248,3 +248,31 @@ def test_budget_graph_replay_matches_eager(rows, mode, policy):
         del scratch
     lay.close()
     print(f"[result] predicted-set sizes seen after replays: {sorted(sizes)}")
+
+
+@pytest.mark.parametrize("policy", ["misses", "confidence"])
+def test_budget_edge_parameters(policy):
+    """Budget parameters at their edges, against the oracle: a cap below K (every row at the cap), k_min equal to the
+    cap, beta = 0 and c = 0 (the plain top-K of the EMA, with ties), a huge beta or c (every row at the cap), missed
+    counts of 0 and above K, K = 1 and K = N."""
+    rng = np.random.default_rng(77)
+    rows, N = 5, 700
+    s32, e32 = _rows(rng, rows, N, "ties")
+    cases = [(40, 30, 1, 0.5, 0.5), (40, 90, 90, 0.5, 0.5), (40, 90, 1, 0.0, 0.0), (40, 90, 1, 1e30, 1e30),
+             (1, 90, 1, 2.0, 1.0), (N, N, 1, 1.0, 1.0), (40, N, 40, 3.0, 0.25)]
+    for (K, cap, k_min, beta, c) in cases:
+        print(f"[case] budget edges {policy} K={K} cap={cap} k_min={k_min} beta={beta} c={c}", flush=True)
+        s = L.make_shape(1, 4 * rows, rows, 128, 16, 16, N, L.BF16)
+        m = np.array([0, K, 3 * K + 5, 1, 2], dtype=np.int32)
+        scores = torch.as_tensor(s32[None], device="cuda").contiguous()
+        ema = torch.as_tensor(e32[None], device="cuda").contiguous()
+        missed = torch.as_tensor(m[None], device="cuda").contiguous()
+        pred = torch.full((1, rows, cap), -7, dtype=torch.int32, device="cuda")
+        bud = L.make_budget(POLICIES[policy], K, k_min, beta, c, missed)
+        L.ema_predict(s, scores, ema, 0.5, False, cap, pred, budget=bud)
+        torch.cuda.synchronize()
+        e_gpu = ema.cpu().numpy()[0]
+        got = pred.cpu().numpy()[0]
+        for r in range(rows):
+            ref = _expected_row(policy, s32[r], e_gpu[r], int(m[r]), K, cap, k_min, beta, c, 0, 0)
+            assert np.array_equal(got[r], ref), (K, cap, r, got[r][:12], ref[:12])
