@@ -458,9 +458,11 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
   const int64_t rows = (int64_t)shape->batch * shape->n_kv_heads;
   const prr_budget* budget = kn > 0 ? a->budget : nullptr;
   const bool budgeted = budget && budget->policy != PRR_BUDGET_FIXED;
-  if (budgeted)
+  if (budgeted) {
+    PRR_TRY(check_budget(shape, budget, kn, "decode_step"));
     PRR_REQUIRE(budget->top_k == a->top_k, "decode_step: the budget's top_k %d differs from the step's %d",
                 budget->top_k, a->top_k);
+  }
   // budgeted predictions are written by the selection launches (one workgroup per row up to 8192 blocks)
   if (mode == PRR_MODE_FUSED && two_launch_supported(*shape, a->top_k, kc, kn) && (rows >= 128 || a->top_k <= 32) &&
       !(budgeted && shape->n_blocks > 8192)) {

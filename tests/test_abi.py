@@ -116,6 +116,13 @@ def test_argument_validation_without_launch():
     assert lib.prr_repair_merge(ctypes.byref(s), nz, nz, nz, nz, nz, 8, None, 4, None, nz, nz, nz, None) == -1
     assert lib.prr_build_summaries(None, nz, nz, None, 0, nz, None) == -1
     assert lib.prr_decode_step(None, ctypes.byref(s), None, 2, 0, None, None) == -1
+    # a decode step checks its budget before any launch (also on the two-launch path), and its K against the step's
+    for bad in (L.Budget(L.BUDGET_MISSES, 8, 0, 0.5, 0.0, 16), L.Budget(L.BUDGET_MISSES, 8, 1, 0.5, 0.0, None),
+                L.Budget(L.BUDGET_CONFIDENCE, 9, 1, 0.0, 1.0, None)):
+        args = L.StepArgs(nz, nz, nz, nz, nz, nz, nz, nz, nz, nz, nz, nz, nz, nz, 8, 8, 8, 0, 0.9,
+                          ctypes.addressof(bad))
+        for mode in (L.MODE_FUSED, L.MODE_ONE_STREAM):
+            assert lib.prr_decode_step(None, ctypes.byref(s), ctypes.byref(args), mode, 0, None, None) == -1, bad
     assert lib.prr_flush_write(nz, 17, None) == -1
     assert b"null" in lib.prr_status_string(-1).lower() or lib.prr_status_string(-1)
 
