@@ -317,3 +317,18 @@ def test_mean_scorer_decode(name, mode, extra):
     inp = make_inputs(w, device="cuda")
     kp = max(w.k_spec) or w.top_k
     run_layer(w, inp, kp, mode, ov=OracleView(inp))
+
+
+@pytest.mark.parametrize("mode", ["prr_fused", "serialized", "prr_2stream"])
+@pytest.mark.parametrize("ctx,bs,page,k,kp", [(5, 32, 32, 1, 1), (32, 32, 32, 1, 1), (40, 16, 16, 2, 3),
+                                               (17, 16, 8, 1, 2), (3, 16, 16, 1, 1)])
+def test_degenerate_contexts(ctx, bs, page, k, kp, mode):
+    """The smallest layers: one block (partly or wholly filled), a few blocks with K and K' near N, pages smaller
+    than a 16-token chunk; every step against the oracle (selection, output, missed count, predicted set)."""
+    from dynamic_sparse_attention_decode_amd.inputs import Workload
+    w = Workload(f"degenerate_{ctx}_{bs}_{page}", 2, 8, 2, 128, ctx, bs, page, k, (kp,), 0.8, 0.9, 4, 0,
+                 shuffle_pages=True, seed=20261203 + ctx + bs + page)
+    print(f"[case] degenerate ctx={ctx} bs={bs} page={page} N={w.n_blocks} K={k} K'={kp} {mode}", flush=True)
+    inp = make_inputs(w, device="cuda")
+    ov = OracleView(inp)
+    run_layer(w, inp, kp if mode != "serialized" else 0, mode, ov=ov)
