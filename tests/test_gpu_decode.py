@@ -321,10 +321,12 @@ def test_mean_scorer_decode(name, mode, extra):
 
 @pytest.mark.parametrize("mode", ["prr_fused", "serialized", "prr_2stream"])
 @pytest.mark.parametrize("ctx,bs,page,k,kp", [(5, 32, 32, 1, 1), (32, 32, 32, 1, 1), (40, 16, 16, 2, 3),
-                                               (17, 16, 8, 1, 2), (3, 16, 16, 1, 1)])
+                                               (17, 16, 8, 1, 2), (3, 16, 16, 1, 1), (5100, 256, 256, 4, 6),
+                                               (200, 4, 4, 5, 7), (301, 12, 4, 6, 8), (1000, 128, 32, 3, 5)])
 def test_degenerate_contexts(ctx, bs, page, k, kp, mode):
-    """The smallest layers: one block (partly or wholly filled), a few blocks with K and K' near N, pages smaller
-    than a 16-token chunk; every step against the oracle (selection, output, missed count, predicted set)."""
+    """The smallest layers and the block-size extremes: one block (partly or wholly filled), a few blocks with K and
+    K' near N, pages smaller than a 16-token chunk, blocks of 4 and 12 tokens, blocks of 128 and 256 tokens (chunks
+    beyond one pipelined call); every step against the oracle (selection, output, missed count, predicted set)."""
     from dynamic_sparse_attention_decode_amd.inputs import Workload
     w = Workload(f"degenerate_{ctx}_{bs}_{page}", 2, 8, 2, 128, ctx, bs, page, k, (kp,), 0.8, 0.9, 4, 0,
                  shuffle_pages=True, seed=20261203 + ctx + bs + page)
