@@ -367,6 +367,15 @@ def pin_adaptive_budgets(o):
     assert o.budget_from_misses([1], 4, 64, 0.25, 1).tolist() == [5]           # ceil(0.25) = 1
     assert o.budget_from_misses([5, 0], 8, 20, 1e30, 1).tolist() == [20, 8]    # a huge product stays at the cap
 
+    # worked by hand: e = [2, 4, 3, 1, 7, 3, 1], s = [1, 5, 3, 2, 8, 0.5, 4], c = 1 gives u = e + |s - e| =
+    # [3, 5, 3, 2, 8, 5.5, 4]; the 2nd largest EMA entry is 4 (block 1), four blocks have u >= 4 (1, 4, 5, 6)
+    s_h = np.array([1, 5, 3, 2, 8, 0.5, 4], dtype=np.float32)
+    e_h = np.array([2, 4, 3, 1, 7, 3, 1], dtype=np.float32)
+    k_h, u_h = o.budget_from_confidence(s_h, e_h, 2, 6, 1.0, 1)
+    assert k_h == 4 and u_h.tolist() == [3, 5, 3, 2, 8, 5.5, 4]
+    assert o.predict_confident(s_h, e_h, 2, 6, 1.0, 1).tolist() == [1, 4, 5, 6]
+    assert o.predict_confident(s_h, e_h, 2, 3, 1.0, 1).tolist() == [1, 4, 5]          # capped at 3
+    assert o.predict_confident(s_h, e_h, 2, 6, 1.0, 5).tolist() == [0, 1, 4, 5, 6]    # k_min 5: next is block 0
     f32 = np.float32
     rng = np.random.default_rng(29)
     for trial in range(120):
