@@ -195,6 +195,8 @@ prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, in
                               int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                               const int32_t* table, const int32_t* pred, int k_spec, float* partials,
                               hipStream_t stream, void* cand_t, void* cand_p, void* cand_u, const BudgetDev& bp) {
+  // nothing to speculate or predict: the selection alone, exactly as the serialized step runs it
+  if (k_spec == 0 && kp_next == 0) return launch_topk(s, scores, nullptr, 0.f, 0, k, sel, stream, cand_t);
   // long rows by segments (with the candidate regions): T, the EMA's candidates and, for a confidence budget, the
   // optimistic scores' candidates; the merge launch applies the budget
   const int ke = bp.policy == 2 ? bp.top_k : kp_next;
