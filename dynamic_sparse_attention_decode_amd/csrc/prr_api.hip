@@ -464,8 +464,9 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
                 budget->top_k, a->top_k);
   }
   // budgeted predictions are written by the selection launches (one workgroup per row up to 8192 blocks)
-  if (mode == PRR_MODE_FUSED && two_launch_supported(*shape, a->top_k, kc, kn) && (rows >= 128 || a->top_k <= 32) &&
-      !(budgeted && shape->n_blocks > 8192)) {
+  // (with nothing predicted or to predict the fused step runs the serialized launches, below)
+  if (mode == PRR_MODE_FUSED && (kc > 0 || kn > 0) && two_launch_supported(*shape, a->top_k, kc, kn) &&
+      (rows >= 128 || a->top_k <= 32) && !(budgeted && shape->n_blocks > 8192)) {
     // scores + EMA; then selection of T and P_{t+1}, speculation over P_t and the missed blocks T \ P_t in one
     // launch; then the merge of the missed-block records with the speculated records of T ∩ P_t. One workgroup per
     // row attends that row's missed blocks after its selection, which pays off when the rows alone fill the chip or
