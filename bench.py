@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--budget-beta", type=float, default=1.0, help="misses budget: blocks added per missed block")
     ap.add_argument("--budget-c", type=float, default=0.5, help="confidence budget: weight of |s - e|")
     ap.add_argument("--budget-kmin", type=int, default=0, help="smallest per-row budget (0: K, capped at --kspec)")
+    ap.add_argument("--no-kspec-sweep", action="store_true",
+                    help="skip the workload's speculation-budget sweep (e.g. for counter passes of one K')")
     ap.add_argument("--other-modes", default="all",
                     help="comma list of further modes to time beside --mode ('all' or 'none')")
     return ap.parse_args()
@@ -378,7 +380,7 @@ def main():
                                                  if detail["attention_path_GBps"] else None)
     if n_layers > 1:   # the same step with one layer only: its data stays in the Infinity Cache between steps
         detail["us_per_step_one_layer_cache_warm"] = measure(a.mode, n_kv=1)[0]
-    if len(w.k_spec) > 1 and a.mode != "serialized":   # the workload sweeps its speculation budget
+    if len(w.k_spec) > 1 and a.mode != "serialized" and not a.no_kspec_sweep:   # the workload sweeps its budget
         detail["us_per_step_by_kspec"] = {str(k): measure(a.mode, k_spec=k)[0] for k in w.k_spec}
     if w.drift_every:   # rebuilding the summaries of the blocks whose keys changed (not part of the step)
         lay = make_layers(a.mode)[0]
