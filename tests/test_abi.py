@@ -161,3 +161,35 @@ def test_budget_chooser_matches_oracle_and_closed_forms():
                 tt = np.polyval(np.polyfit(n_grid, ts, deg), nt)
                 k = max(a, b)
                 assert abs(tp[ks.index(k)] - tt) < 1e-9 * max(1, abs(tt))
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors of prr_shape, prr_budget and prr_step_args have the C header's size and field offsets
+    (a C program built with the host compiler against include/prr.h prints them)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    structs = {"prr_shape": L.Shape, "prr_budget": L.Budget, "prr_step_args": L.StepArgs}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "prr.h"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-std=c11", "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line:
+            parts = line.split()
+            got[tuple(parts[:-1])] = int(parts[-1])
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)
