@@ -18,9 +18,10 @@ pytestmark = [pytest.mark.gpu, requires_gpu]
 STEPS = 3
 
 
-# every workload in the benchmark's mode; the million-token row (32768 blocks, selected by segments) in the other
-# modes' selection paths too
-CASES = [(n, "prr_fused") for n in WORKLOADS] + [("million_token", "serialized"), ("million_token", "prr_2stream")]
+# every workload in the benchmark's mode and in the serialized step; the million-token row (32768 blocks, selected
+# by segments) in the two-stream step too
+CASES = ([(n, "prr_fused") for n in WORKLOADS] + [(n, "serialized") for n in WORKLOADS]
+         + [("million_token", "prr_2stream")])
 
 
 @pytest.mark.parametrize("name,mode", CASES)
