@@ -126,7 +126,10 @@ def top_k(values: np.ndarray, k: int, n_sink: int = 0, n_local: int = 0) -> np.n
 
 
 def boundary_gap(values: np.ndarray, k: int):
-    """(v_(k), v_(k+1), relative gap (v_(k) - v_(k+1)) / |v_(k)|) of the sorted values; gap = inf when k == n."""
+    """(v_(k), v_(k+1), relative gap (v_(k) - v_(k+1)) / |v_(k)|), v_(i) the i-th largest value.
+
+    gap = inf when k == n (nothing is left out). When v_(k) = 0 the relative gap is inf if v_(k+1) < 0 and 0 if the
+    two are equal. A positive gap means the top-k set is the only k-set of largest sum."""
     v = np.sort(np.asarray(values, dtype=np.float64))[::-1]
     if k >= len(v):
         return float(v[k - 1]), -math.inf, math.inf
@@ -322,40 +325,6 @@ def choose_budget(n_grid, t_sel, kspec_grid, t_spec, n_target: float, degree: in
         if t <= t_target and k > best:
             best = int(k)
     return best
-
-
-# ------------------------------------------------------------------------------------------------------------------
-# one (sequence, KV head) through a whole decode run: selection, prediction, output, statistics
-# ------------------------------------------------------------------------------------------------------------------
-
-
-def select_row(q_group, keys, block_size: int, top_k_blocks: int):
-    """(scores [N], T ascending, gap) for one (sequence, KV head) and one query group."""
-    kmin, kmax = block_summaries(keys, block_size)
-    s = quest_scores(q_group, kmin, kmax)
-    return s, top_k(s, top_k_blocks), boundary_gap(s, top_k_blocks)[2]
-
-
-def decode_row(q_steps, keys_at, values, block_size: int, top_k_blocks: int, k_spec: int, alpha: float,
-               scale: float, steps=None):
-    """Run the PRR reference pipeline over decode steps for one (sequence, KV head).
-
-    q_steps: [steps, G, D] queries; keys_at(t) -> [ctx, D] keys in force at step t (drift may change them).
-    Yields per step a dict with scores, T, P (None at step 0), output, missed, wasted, gaps."""
-    ema = None
-    P = None
-    n_steps = len(q_steps) if steps is None else steps
-    for t in range(n_steps):
-        keys = keys_at(t)
-        s, T, gap = select_row(q_steps[t], keys, block_size, top_k_blocks)
-        Pt = np.zeros((0,), dtype=np.int64) if (P is None or k_spec == 0) else P
-        o, missed, wasted = prr_output(q_steps[t], keys, values, T, Pt, block_size, scale)
-        ema = ema_update(ema, s, alpha, first=(t == 0))
-        ema_gap = boundary_gap(ema, k_spec)[2] if k_spec else math.inf
-        P_next = predict(ema, k_spec) if k_spec else np.zeros((0,), dtype=np.int64)
-        yield dict(t=t, scores=s, T=T, P=None if P is None else Pt, out=o, missed=missed, wasted=wasted, gap=gap,
-                   ema=ema.copy(), ema_gap_next=ema_gap, P_next=P_next)
-        P = P_next
 
 
 # ------------------------------------------------------------------------------------------------------------------

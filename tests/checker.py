@@ -55,3 +55,15 @@ def check_selection(gpu_idx, oracle_scores, k: int, rel: float = REL_GAP, n_sink
 
 def max_abs(a, b) -> float:
     return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64))))
+
+
+def check_output(got, ref, dtype: str) -> float:
+    """Element-by-element comparison of an output with the oracle's: raises AssertionError when any element differs
+    by more than the storage dtype's max-abs tolerance. Returns the largest difference."""
+    a = np.asarray(got, dtype=np.float64)
+    b = np.asarray(ref, dtype=np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    assert np.all(np.isfinite(a)), "non-finite output"
+    err = max_abs(a, b)
+    assert err <= TOL[dtype], f"max |gpu - oracle| = {err:.3e} > {TOL[dtype]:.0e} ({dtype})"
+    return err

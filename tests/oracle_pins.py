@@ -16,6 +16,8 @@ import json
 import math
 import os
 
+from itertools import combinations
+
 import numpy as np
 import torch
 
@@ -413,7 +415,48 @@ def pin_adaptive_budgets(o):
     assert len(o.predict_confident(s, e, 7, 20, 1e30, 1)) == 20
 
 
+def _maximising_k_sets(values, k):
+    """Number of k-subsets whose summed value is the largest (brute force)."""
+    sums = [sum(values[i] for i in c) for c in combinations(range(len(values)), k)]
+    best = max(sums)
+    return sum(1 for x in sums if x == best)
+
+
+def pin_boundary_gap(o):
+    """The relative gap at the K-th/(K+1)-th boundary on hand-worked vectors (distinct values, an exact tie, k = n,
+    a negative K-th value, a zero K-th value above and equal to the next), and what it means: on integer-valued
+    vectors a positive gap leaves exactly one k-set of largest sum, a zero gap at least two (brute force)."""
+    inf = math.inf
+    cases = [
+        ([5.0, 3.0, 9.0, 1.0], 2, 5.0, 3.0, 0.4),          # sorted 9 5 | 3 1: (5 - 3) / 5
+        ([4.0, 1.0, 3.0, 2.0], 1, 4.0, 3.0, 0.25),
+        ([4.0, 1.0, 3.0, 2.0], 3, 2.0, 1.0, 0.5),
+        ([2.0, 7.0, 2.0, 1.0], 2, 2.0, 2.0, 0.0),          # exact tie at the boundary
+        ([1.0, 2.0, 3.0], 3, 1.0, -inf, inf),             # k = n: nothing left out
+        ([-1.0, -4.0, -2.0, -8.0], 2, -2.0, -4.0, 1.0),    # negative K-th value: (-2 - -4) / |-2|
+        ([-3.0, -3.5, 10.0], 2, -3.0, -3.5, 0.5 / 3.0),
+        ([3.0, 0.0, -1.0], 2, 0.0, -1.0, inf),            # K-th value 0 above the next
+        ([0.0, 5.0, 0.0], 2, 0.0, 0.0, 0.0),              # K-th and next both 0
+        ([10.0, 9.999, 1.0], 1, 10.0, 9.999, 1e-4),
+    ]
+    for vals, k, a, b, gap in cases:
+        ga, gb, gg = o.boundary_gap(np.asarray(vals), k)
+        assert ga == a and gb == b, (vals, k, ga, gb)
+        if math.isinf(gap):
+            assert math.isinf(gg) and gg > 0, (vals, k, gg)
+        else:
+            assert math.isclose(gg, gap, rel_tol=1e-9, abs_tol=0.0), (vals, k, gg, gap)
+    rng = np.random.default_rng(21)
+    for _ in range(80):
+        n = int(rng.integers(2, 8))
+        vals = [float(x) for x in rng.integers(-4, 5, size=n)]
+        k = int(rng.integers(1, n))
+        gap = o.boundary_gap(np.asarray(vals), k)[2]
+        count = _maximising_k_sets(vals, k)
+        assert (count == 1) == (gap > 0), (vals, k, gap, count)
+
+
 ALL_PINS = [pin_dense_equivalence, pin_brute_force_selection, pin_quest_upper_bound, pin_signsplit,
             pin_merge_order_free, pin_repair_invariants, pin_closed_forms, pin_hand_example, pin_ema_closed_form,
             pin_budget_closed_form, pin_paged_gather, pin_partial_last_block, pin_forced_blocks,
-            pin_mean_key_scores, pin_adaptive_budgets]
+            pin_mean_key_scores, pin_adaptive_budgets, pin_boundary_gap]

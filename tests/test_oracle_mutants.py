@@ -8,6 +8,8 @@ import numpy as np
 import pytest
 
 from oracle import prr_oracle as O
+from tests import checker as C
+from tests.checker_cases import ALL_CASES
 from tests.oracle_pins import ALL_PINS
 
 
@@ -199,8 +201,44 @@ def _predict_confident_by_ema(scores, ema, k_top, k_cap, c, k_min, n_sink=0, n_l
     return O.top_k(np.asarray(ema, dtype=np.float32), k, n_sink, n_local)
 
 
+def _gap_off_by_one(values, k):
+    v = np.sort(np.asarray(values, dtype=np.float64))[::-1]
+    if k + 1 >= len(v):
+        return float(v[-1]), -math.inf, math.inf
+    a, b = float(v[k]), float(v[k + 1])
+    return a, b, (a - b) / abs(a) if a != 0 else (math.inf if a > b else 0.0)
+
+
+def _gap_sign(values, k):
+    a, b, _ = _orig["boundary_gap"](values, k)
+    if math.isinf(b):
+        return a, b, math.inf
+    return a, b, (b - a) / abs(a) if a != 0 else (math.inf if a > b else 0.0)
+
+
+def _gap_zero_branch(values, k):
+    a, b, g = _orig["boundary_gap"](values, k)
+    return a, b, 0.0 if a == 0 else g
+
+
+def _gap_over_next(values, k):
+    a, b, g = _orig["boundary_gap"](values, k)
+    if math.isinf(b) or a == 0 or b == 0:
+        return a, b, g
+    return a, b, (a - b) / abs(b)
+
+
+def _gap_ascending(values, k):
+    v = np.sort(np.asarray(values, dtype=np.float64))
+    if k >= len(v):
+        return float(v[k - 1]), -math.inf, math.inf
+    a, b = float(v[k - 1]), float(v[k])
+    return a, b, abs(a - b) / abs(a) if a != 0 else math.inf
+
+
 _orig = {k: getattr(O, k) for k in ["attention_over_blocks", "prr_output", "ema_update", "choose_budget",
-                                    "block_summaries", "top_k", "mean_key_scores", "budget_from_confidence"]}
+                                    "block_summaries", "top_k", "mean_key_scores", "budget_from_confidence",
+                                    "boundary_gap"]}
 
 MUTANTS = {
     "quest_drop_kmin": ("quest_scores", _quest_drop_kmin),
@@ -235,6 +273,11 @@ MUTANTS = {
     "confidence_bound_minus": ("confidence_bound", _bound_minus),
     "confidence_theta_from_u": ("budget_from_confidence", _confidence_theta_from_u),
     "predict_confident_by_ema": ("predict_confident", _predict_confident_by_ema),
+    "gap_off_by_one": ("boundary_gap", _gap_off_by_one),
+    "gap_sign": ("boundary_gap", _gap_sign),
+    "gap_zero_branch": ("boundary_gap", _gap_zero_branch),
+    "gap_over_next": ("boundary_gap", _gap_over_next),
+    "gap_ascending": ("boundary_gap", _gap_ascending),
 }
 
 
@@ -251,3 +294,107 @@ def test_mutant_is_caught(name, monkeypatch):
         except Exception:   # a crash inside a pin also counts as caught
             failures += 1
     assert failures > 0, f"mutant {name} passed every pin"
+
+
+# ---- planted mistakes in the comparison rules (tests/checker.py), caught by tests/checker_cases.py -----------------
+_check_selection = C.check_selection
+_check_output = C.check_output
+
+
+def _band(g, s, k, eps):
+    mask = np.zeros(len(s), dtype=bool)
+    mask[g] = True
+    outside = s[~mask].max() if (~mask).any() else -np.inf
+    assert s[mask].min() >= outside - eps
+
+
+def _sel_eps_absolute(gpu_idx, oracle_scores, k, rel=C.REL_GAP, n_sink=0, n_local=0):
+    """The band taken as an absolute 1e-4 instead of relative to |s_(K)|."""
+    if n_sink or n_local:
+        return _check_selection(gpu_idx, oracle_scores, k, rel, n_sink, n_local)
+    g, s = np.asarray(gpu_idx), np.asarray(oracle_scores, dtype=np.float64)
+    assert g.shape == (k,) and np.all(np.diff(g) > 0) and g.min() >= 0 and g.max() < len(s)
+    if O.boundary_gap(s, k)[2] > rel:
+        assert np.array_equal(g, O.top_k(s, k))
+        return True
+    _band(g, s, k, rel)
+    return False
+
+
+def _sel_threshold_inverted(gpu_idx, oracle_scores, k, rel=C.REL_GAP, n_sink=0, n_local=0):
+    """Exactness demanded where the gap is small (and the band used where it is large)."""
+    if n_sink or n_local:
+        return _check_selection(gpu_idx, oracle_scores, k, rel, n_sink, n_local)
+    g, s = np.asarray(gpu_idx), np.asarray(oracle_scores, dtype=np.float64)
+    assert g.shape == (k,) and np.all(np.diff(g) > 0) and g.min() >= 0 and g.max() < len(s)
+    if O.boundary_gap(s, k)[2] <= rel:
+        assert np.array_equal(g, O.top_k(s, k))
+        return True
+    _band(g, s, k, rel * abs(O.boundary_gap(s, k)[0]))
+    return False
+
+
+def _sel_band_wrong_side(gpu_idx, oracle_scores, k, rel=C.REL_GAP, n_sink=0, n_local=0):
+    """The band added on the wrong side (inside minimum >= outside maximum + eps)."""
+    if n_sink or n_local:
+        return _check_selection(gpu_idx, oracle_scores, k, rel, n_sink, n_local)
+    g, s = np.asarray(gpu_idx), np.asarray(oracle_scores, dtype=np.float64)
+    assert g.shape == (k,) and np.all(np.diff(g) > 0) and g.min() >= 0 and g.max() < len(s)
+    if O.boundary_gap(s, k)[2] > rel:
+        assert np.array_equal(g, O.top_k(s, k))
+        return True
+    _band(g, s, k, -rel * abs(O.boundary_gap(s, k)[0]))
+    return False
+
+
+def _sel_no_order_check(gpu_idx, oracle_scores, k, rel=C.REL_GAP, n_sink=0, n_local=0):
+    """Ids compared as a set: an unsorted or repeated list passes."""
+    g = np.unique(np.asarray(gpu_idx))
+    if len(g) != k:
+        g = np.sort(np.asarray(gpu_idx))
+        return True
+    return _check_selection(g, oracle_scores, k, rel, n_sink, n_local)
+
+
+def _sel_forced_last(gpu_idx, oracle_scores, k, rel=C.REL_GAP, n_sink=0, n_local=0):
+    """K below the number of forced blocks compared with the last K of them."""
+    n = len(oracle_scores)
+    f_idx = [i for i in range(n) if i < n_sink or i >= n - n_local]
+    if (n_sink or n_local) and k <= len(f_idx):
+        assert np.array_equal(np.asarray(gpu_idx), np.asarray(f_idx[-k:]))
+        return True
+    return _check_selection(gpu_idx, oracle_scores, k, rel, n_sink, n_local)
+
+
+def _out_mean_abs(got, ref, dtype):
+    err = float(np.mean(np.abs(np.asarray(got, dtype=np.float64) - np.asarray(ref, dtype=np.float64))))
+    assert not np.isnan(err) and err <= C.TOL[dtype]
+    return err
+
+
+def _out_bf16_tol(got, ref, dtype):
+    return _check_output(got, ref, "bf16")
+
+
+CHECKER_MUTANTS = {
+    "sel_eps_absolute": ("check_selection", _sel_eps_absolute),
+    "sel_threshold_inverted": ("check_selection", _sel_threshold_inverted),
+    "sel_band_wrong_side": ("check_selection", _sel_band_wrong_side),
+    "sel_no_order_check": ("check_selection", _sel_no_order_check),
+    "sel_forced_last": ("check_selection", _sel_forced_last),
+    "out_mean_abs": ("check_output", _out_mean_abs),
+    "out_bf16_tolerance_for_f32": ("check_output", _out_bf16_tol),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CHECKER_MUTANTS))
+def test_checker_mutant_is_caught(name, monkeypatch):
+    attr, fn = CHECKER_MUTANTS[name]
+    monkeypatch.setattr(C, attr, fn)
+    failures = 0
+    for case in ALL_CASES:
+        try:
+            case(C)
+        except Exception:   # AssertionError or a crash inside a case
+            failures += 1
+    assert failures > 0, f"checker mutant {name} passed every case"
