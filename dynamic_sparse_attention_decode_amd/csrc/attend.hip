@@ -112,6 +112,7 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8
   __shared__ int s_miss[4];
   __shared__ int32_t s_pred[kPredLds];
   __shared__ int32_t s_mid[4][8];   // missed block ids of the current group of entries, per wave
+  __shared__ int s_kf[4];           // per wave: the first empty (negative) slot of P it saw
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t rowid = blockIdx.y;
   const int rec = blockIdx.x;
@@ -122,13 +123,22 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8
   const float* part_row = partials ? partials + rowid * k_spec * (int64_t)RF : nullptr;
 
   const bool pred_lds = k_spec <= kPredLds;
-  if (prow && pred_lds)
-    for (int i = threadIdx.x; i < k_spec; i += 256) s_pred[i] = prow[i];
+  int kneg = k_spec;
+  if (prow)
+    for (int i = threadIdx.x; i < k_spec; i += 256) {
+      const int32_t v = prow[i];
+      if (pred_lds) s_pred[i] = v;
+      if (v < 0) kneg = min(kneg, i);
+    }
+  kneg = -(int)wave_max(-(float)kneg);   // exact: slot counts are far below 2^24
+  if (lane == 0) s_kf[wave] = kneg;
   W st;
   st.init(lane);
   st.load_q(q + ((int64_t)b * Hq + (int64_t)g * G) * kRowBytes, qscale);
   const int32_t* trow = table + (int64_t)b * pps;
   __syncthreads();
+  // slots from the first empty one on never match (speculation may have skipped them), as in the row-wise repair
+  const int kf = min(min(s_kf[0], s_kf[1]), min(s_kf[2], s_kf[3]));
   int misses = 0;
   const int j0 = (rec * 4 + wave) * epw;
   const int j1 = min(top_k, j0 + epw);
@@ -138,9 +148,9 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8
     for (int j = jb; j < min(j1, jb + 8); ++j) {
       const int n = min(max(srow[j], 0), N - 1);
       int slot = -1;
-      for (int c = 0; c < k_spec; c += 64) {
+      for (int c = 0; c < kf; c += 64) {
         const int i = c + lane;
-        const int pv = i < k_spec ? (pred_lds ? s_pred[i] : prow[i]) : -1;
+        const int pv = i < kf ? (pred_lds ? s_pred[i] : prow[i]) : -1;
         const unsigned long long hit = __ballot(pv == n);
         if (hit) { slot = c + __ffsll(hit) - 1; break; }
       }

@@ -442,7 +442,30 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
   const bool serial = mode == PRR_MODE_SERIALIZED || mode == PRR_MODE_SERIALIZED_FUSED;
   const int kc = serial ? 0 : a->k_spec_cur;
   const int kn = serial ? 0 : a->k_spec_next;
-  PRR_REQUIRE(kc >= 0 && kn >= 0, "decode_step: negative k_spec");
+  const int N = shape->n_blocks;
+  // every argument of every mode is checked here, before the first launch: a rejected call enqueues nothing (and so
+  // leaves the EMA and every other buffer as it was)
+  PRR_TRY(check_topk_n(shape));
+  PRR_REQUIRE(a->top_k >= 1 && a->top_k <= N, "decode_step: top_k %d not in [1, %d]", a->top_k, N);
+  PRR_REQUIRE(kc >= 0 && kc <= N && kn >= 0 && kn <= N, "decode_step: k_spec_cur %d, k_spec_next %d not in [0, %d]",
+              kc, kn, N);
+  PRR_REQUIRE(a->q && a->k_cache && a->v_cache && a->block_table && a->summaries && a->scores && a->sel_idx &&
+              a->out && a->n_missed && a->workspace, "decode_step: null pointer");
+  if (kc > 0) PRR_REQUIRE(a->pred_cur && a->partials, "decode_step: k_spec_cur > 0 needs pred_cur and partials");
+  if (kn > 0) {
+    PRR_REQUIRE(a->ema && a->pred_next, "decode_step: k_spec_next > 0 needs ema and pred_next");
+    PRR_REQUIRE(kc == 0 || a->pred_next != a->pred_cur, "decode_step: pred_cur and pred_next must differ");
+    PRR_REQUIRE(a->alpha >= 0.f && a->alpha <= 1.f, "decode_step: alpha not in [0, 1]");
+  }
+
+  const int64_t rows = (int64_t)shape->batch * shape->n_kv_heads;
+  const prr_budget* budget = kn > 0 ? a->budget : nullptr;
+  const bool budgeted = budget && budget->policy != PRR_BUDGET_FIXED;
+  if (budgeted) {
+    PRR_TRY(check_budget(shape, budget, kn, "decode_step"));
+    PRR_REQUIRE(budget->top_k == a->top_k, "decode_step: the budget's top_k %d differs from the step's %d",
+                budget->top_k, a->top_k);
+  }
 
   // select-then-attend in two launches pays off only when the rows alone fill the chip (one workgroup per row
   // attends over the row's whole true set); otherwise the spread-out attention launches are faster
@@ -455,14 +478,6 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
     }
     mode = PRR_MODE_SERIALIZED;
   }
-  const int64_t rows = (int64_t)shape->batch * shape->n_kv_heads;
-  const prr_budget* budget = kn > 0 ? a->budget : nullptr;
-  const bool budgeted = budget && budget->policy != PRR_BUDGET_FIXED;
-  if (budgeted) {
-    PRR_TRY(check_budget(shape, budget, kn, "decode_step"));
-    PRR_REQUIRE(budget->top_k == a->top_k, "decode_step: the budget's top_k %d differs from the step's %d",
-                budget->top_k, a->top_k);
-  }
   // budgeted predictions are written by the selection launches (one workgroup per row up to 8192 blocks)
   // (with nothing predicted or to predict the fused step runs the serialized launches, below)
   if (mode == PRR_MODE_FUSED && (kc > 0 || kn > 0) && two_launch_supported(*shape, a->top_k, kc, kn) &&
@@ -472,9 +487,6 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
     // row attends that row's missed blocks after its selection, which pays off when the rows alone fill the chip or
     // the rows are short; otherwise the missed blocks are spread over a separate repair launch (below).
     PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step, s1));
-    PRR_REQUIRE(a->workspace && a->sel_idx && a->out && a->n_missed, "decode_step: null pointer");
-    if (kc > 0) PRR_REQUIRE(a->pred_cur && a->partials, "decode_step: null predicted set or partials");
-    if (kn > 0) PRR_REQUIRE(a->ema && a->pred_next && a->pred_next != a->pred_cur, "decode_step: bad prediction buffers");
     return launch_select_missed(*shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,
                                 a->v_cache, a->block_table, kc ? a->pred_cur : nullptr, kc,
                                 kc ? a->partials : nullptr, true, a->out, a->n_missed,

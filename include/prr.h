@@ -162,7 +162,8 @@ prr_status prr_speculate(const prr_shape* shape, const void* q, const void* k_ca
 /* Repair and merge (PRR abstract: repair the missed blocks once the true set is known; folds them into the partial
  * state with online-softmax statistics). For every (b, g): the blocks of T = sel_idx[b,g,:] that are in
  * P = pred_idx[b,g,:k_spec] reuse their speculated partials; the missed blocks M = T \ P are computed here; blocks of
- * P \ T never enter. out[b,h] = O / l of the merged state; n_missed[b,g] = |M|. k_spec == 0 (or pred_idx NULL)
+ * P \ T never enter. P ends at its first negative (empty) slot: ids after it are never matched, so a block of T
+ * listed there is computed as missed. out[b,h] = O / l of the merged state; n_missed[b,g] = |M|. k_spec == 0 (or pred_idx NULL)
  * computes attention over all of T (the serialized select-then-attend path). `workspace` holds
  * prr_workspace_bytes() bytes of scratch (no initialisation needed); it uses the workspace's repair region, so it
  * may overlap a selection call on the same workspace, but not another repair. */

@@ -123,6 +123,34 @@ def test_argument_validation_without_launch():
                           ctypes.addressof(bad))
         for mode in (L.MODE_FUSED, L.MODE_ONE_STREAM):
             assert lib.prr_decode_step(None, ctypes.byref(s), ctypes.byref(args), mode, 0, None, None) == -1, bad
+    # top_k and the budgets of P_t and P_{t+1} are checked before any launch in every mode, including the fused
+    # two-launch path (B * Hkv >= 128): a rejected call has enqueued nothing, so the EMA is left as it was. Distinct
+    # non-null pointers, so that only the value under test is wrong (no call here may reach a launch).
+    ptrs = [ctypes.c_void_p(256 * (i + 1)) for i in range(14)]
+    s_many = _shape(batch=16, n_blocks=2048)
+    for shp in (s, s_many):
+        n = shp.n_blocks
+        for top_k, kc, kn in ((0, 8, 8), (-1, 8, 8), (n + 1, 8, 8), (8, n + 1, 8), (8, 8, n + 1), (8, -1, 8)):
+            args = L.StepArgs(*ptrs, top_k, kc, kn, 0, 0.9, None)
+            bad_k = top_k < 1 or top_k > n
+            for mode in (L.MODE_FUSED, L.MODE_ONE_STREAM, L.MODE_SERIALIZED, L.MODE_SERIALIZED_FUSED):
+                if not bad_k and mode in (L.MODE_SERIALIZED, L.MODE_SERIALIZED_FUSED):
+                    continue   # the serialized modes ignore both budgets: this call would be valid
+                st = lib.prr_decode_step(None, ctypes.byref(shp), ctypes.byref(args), mode, 0, None, None)
+                assert st == -1, (shp.batch, top_k, kc, kn, mode, st, lib.prr_last_error())
+    # each null buffer, equal P_t and P_{t+1} buffers, and alpha outside [0, 1] are rejected before the scoring launch
+    for i in range(14):
+        bad = list(ptrs)
+        bad[i] = None
+        args = L.StepArgs(*bad, 8, 8, 8, 0, 0.9, None)
+        assert lib.prr_decode_step(None, ctypes.byref(s_many), ctypes.byref(args), L.MODE_FUSED, 0, None,
+                                   None) == -1, i
+    same = list(ptrs)
+    same[9] = same[8]   # pred_next = pred_cur
+    args = L.StepArgs(*same, 8, 8, 8, 0, 0.9, None)
+    assert lib.prr_decode_step(None, ctypes.byref(s_many), ctypes.byref(args), L.MODE_FUSED, 0, None, None) == -1
+    args = L.StepArgs(*ptrs, 8, 8, 8, 0, 1.5, None)
+    assert lib.prr_decode_step(None, ctypes.byref(s_many), ctypes.byref(args), L.MODE_FUSED, 0, None, None) == -1
     assert lib.prr_flush_write(nz, 17, None) == -1
     assert b"null" in lib.prr_status_string(-1).lower() or lib.prr_status_string(-1)
 

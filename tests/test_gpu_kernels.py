@@ -244,6 +244,46 @@ def test_repair_merge_forced_predictions(name):
     print(f"[result] {name}: worst forced-P output error {worst:.3e}")
 
 
+@pytest.mark.parametrize("name", ["llama3_8b_32k", "paged_wide"])
+def test_repair_empty_slot_inside_prediction(name):
+    """A predicted set with an empty (-1) slot before valid ids: ids after the first empty slot are never matched
+    (speculation may have skipped them), so their blocks of T are repaired. The output is attention over T and the
+    missed count is |T minus the ids before the empty slot|, in the spread-out and the row-wise repair alike."""
+    w, inp, s, summ, ov = _setup(name)
+    B, Hkv, N, K, G = w.batch, w.n_kv_heads, w.n_blocks, w.top_k, w.group
+    t = 1
+    q = inp.q[t].contiguous()
+    scores = torch.zeros((B, Hkv, N), dtype=torch.float32, device="cuda")
+    sel = torch.zeros((B, Hkv, K), dtype=torch.int32, device="cuda")
+    L.score_select(s, q, summ, K, scores, sel)
+    torch.cuda.synchronize()
+    sel_np = sel.cpu().numpy()
+    cut = K // 2
+    pred_np = np.sort(sel_np, axis=-1).astype(np.int32)
+    pred_np[:, :, cut] = -1                      # T with one empty slot in the middle: the ids after it are in T too
+    pred = torch.as_tensor(pred_np, device="cuda")
+    part = torch.zeros((L.partials_bytes(s, K) // 4,), dtype=torch.float32, device="cuda")
+    L.speculate(s, q, inp.k_cache, inp.v_cache, inp.table, pred, K, part)
+    ws = torch.zeros((L.workspace_bytes(s, K) // 4 + 1,), dtype=torch.float32, device="cuda")
+    out = torch.zeros((B, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    nm = torch.full((B, Hkv), -1, dtype=torch.int32, device="cuda")
+    L.repair_merge(s, q, inp.k_cache, inp.v_cache, inp.table, sel, K, pred, K, part, out, nm, ws)
+    out2 = torch.zeros_like(out)
+    nm2 = torch.full_like(nm, -1)
+    sel2 = torch.zeros_like(sel)
+    L.select_repair(s, scores, K, sel2, q, inp.k_cache, inp.v_cache, inp.table, out2, nm2, ws, pred_idx=pred,
+                    k_spec=K, partials=part)
+    torch.cuda.synchronize()
+    for got, nmn in ((np64(out), nm.cpu().numpy()), (np64(out2), nm2.cpu().numpy())):
+        for b in range(B):
+            for g in range(Hkv):
+                ref = O.attention_over_blocks(ov.q_group(t, b, g), ov.keys(b, g), ov.values(b, g), sel_np[b, g],
+                                              w.block_size, w.scale)
+                e = max_abs(got[b, g * G:(g + 1) * G], ref)
+                assert e <= TOL[w.dtype], (b, g, e)
+                assert nmn[b, g] == K - cut, (b, g, nmn[b, g], K - cut)
+
+
 def test_poison_block_excluded():
     """A predicted block outside the true set whose keys align with the queries (logits far above every selected
     token) must not leak into the output."""
