@@ -1,12 +1,15 @@
 """Shared helpers of the GPU parity tests: reduced workloads, oracle views of the generated inputs."""
 from __future__ import annotations
 
+import functools
+import os
+
 import numpy as np
 import pytest
 import torch
 
 from dynamic_sparse_attention_decode_amd import _lib as L
-from dynamic_sparse_attention_decode_amd.inputs import WORKLOADS, Workload
+from dynamic_sparse_attention_decode_amd.inputs import WORKLOADS, Workload, load_attempts, make_inputs
 
 requires_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
 
@@ -89,3 +92,28 @@ class OracleView:
     def q_group(self, t: int, b: int, g: int) -> np.ndarray:
         G = self.w.group
         return np64(self.inp.q[t, b, g * G:(g + 1) * G])
+
+
+GAP_TABLES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "gap_attempts")
+
+
+@functools.lru_cache(maxsize=64)
+def _searched_attempts(w: Workload, steps: int) -> np.ndarray:
+    from tests.gap_search import search
+    return search(w, steps)[0]
+
+
+def gap_attempts(w: Workload, steps: int | None = None) -> np.ndarray:
+    """Query-draw attempts that keep the selection's relative score gap above 1e-4 on every (step, row): the stored
+    table of a full-size workload, else a search with the oracle (reduced workloads take seconds)."""
+    steps = w.steps if steps is None else steps
+    full = WORKLOADS.get(w.name)
+    if full is not None and full.key() == w.key():
+        return load_attempts(os.path.join(GAP_TABLES, f"{w.name}.json"), w, steps)
+    return _searched_attempts(w, steps)
+
+
+def gap_inputs(w: Workload, device="cuda", steps: int | None = None) -> "object":
+    """make_inputs with the gap-keeping query draws (so the selection is checked for exact equality everywhere)."""
+    steps = w.steps if steps is None else steps
+    return make_inputs(w, device=device, steps=steps, attempts=gap_attempts(w, steps))

@@ -10,11 +10,10 @@ import pytest
 import torch
 
 from dynamic_sparse_attention_decode_amd import _lib as L
-from dynamic_sparse_attention_decode_amd.inputs import make_inputs
 from dynamic_sparse_attention_decode_amd.runtime import PRRLayer
 from oracle import prr_oracle as O
 from tests.checker import TOL, check_selection, max_abs
-from tests.gpu_common import OracleView, np64, oracle_scores, requires_gpu, shape_of, small
+from tests.gpu_common import OracleView, gap_inputs, np64, oracle_scores, requires_gpu, shape_of, small
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -149,7 +148,7 @@ def test_decode_with_budget(name, policy, mode):
     k_min = max(1, w.top_k // 2)
     cfg = {"policy": policy, "k_min": k_min, "beta": 0.5, "c": 0.3}
     print(f"[case] decode budget {name} {policy} {mode} K'={kp}", flush=True)
-    inp = make_inputs(w, device="cuda")
+    inp = gap_inputs(w)
     ov = OracleView(inp)
     layer = PRRLayer(shape_of(w), w.top_k, kp, w.alpha, mode=mode, budget=cfg)
     layer.build(inp.k_cache, inp.v_cache, inp.table)
@@ -174,8 +173,8 @@ def test_decode_with_budget(name, policy, mode):
             for g in range(w.n_kv_heads):
                 qg = ov.q_group(t, b, g)
                 keys = ov.keys(b, g)
-                check_selection(sel[b, g], oracle_scores(w, qg, keys), w.top_k, n_sink=w.sink_blocks,
-                                n_local=w.local_blocks)
+                assert check_selection(sel[b, g], oracle_scores(w, qg, keys), w.top_k, n_sink=w.sink_blocks,
+                                       n_local=w.local_blocks), (t, b, g)
                 ref = O.attention_over_blocks(qg, keys, ov.values(b, g), sel[b, g], w.block_size, w.scale)
                 assert max_abs(out_h[b, g * G:(g + 1) * G], ref) <= TOL[w.dtype], (t, b, g)
                 if pred_t is None:
@@ -210,7 +209,7 @@ def test_budget_graph_replay_matches_eager(rows, mode, policy):
     kp = min(w.n_blocks, max(max(w.k_spec), w.top_k + w.top_k // 2))
     cfg = {"policy": policy, "k_min": max(1, w.top_k // 2), "beta": 0.5, "c": 0.3}
     print(f"[case] budget graph replay {rows} rows N={w.n_blocks} {mode} {policy}", flush=True)
-    inp = make_inputs(w, device="cuda")
+    inp = gap_inputs(w)
     qs = [inp.q[t].contiguous() for t in range(w.steps)]
     seq = [0] + [1, 2, 3, 4] * 3
     eager = PRRLayer(shape_of(w), w.top_k, kp, w.alpha, mode=mode, budget=cfg)

@@ -5,11 +5,11 @@ import numpy as np
 import pytest
 import torch
 
-from dynamic_sparse_attention_decode_amd.inputs import make_inputs
 from dynamic_sparse_attention_decode_amd.runtime import PRRLayer
 from oracle import prr_oracle as O
 from tests.checker import TOL, check_selection, max_abs
-from tests.gpu_common import SMALL, OracleView, np64, oracle_scores, ragged, requires_gpu, shape_of, small
+from tests.gpu_common import (SMALL, OracleView, gap_inputs, np64, oracle_scores, ragged, requires_gpu, shape_of,
+                              small)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -45,7 +45,9 @@ def _check_step(w, ov, t, h, k_spec, ema_ref):
             qg = ov.q_group(t, b, g)
             keys = ov.keys(b, g)
             s = oracle_scores(w, qg, keys)
-            check_selection(h["sel"][b, g], s, w.top_k, n_sink=w.sink_blocks, n_local=w.local_blocks)
+            exact = check_selection(h["sel"][b, g], s, w.top_k, n_sink=w.sink_blocks, n_local=w.local_blocks)
+            # the inputs keep the oracle's relative gap above 1e-4 at every step, so the set must be the oracle's
+            assert exact, (t, b, g, "banded instance: the inputs did not keep the gap")
             ref = O.attention_over_blocks(qg, keys, ov.values(b, g), h["sel"][b, g], w.block_size, w.scale)
             e = max_abs(h["out"][b, g * G:(g + 1) * G], ref)
             assert e <= TOL[w.dtype], (t, b, g, e)
@@ -66,7 +68,7 @@ def test_decode_vs_oracle(name, mode):
     w = small(name)
     for kp in (w.k_spec if mode != "serialized_fused" else (0,)):
         print(f"[case] decode {name} {mode} K'={kp}", flush=True)
-        inp = make_inputs(w, device="cuda")
+        inp = gap_inputs(w)
         ov = OracleView(inp)
         hist = run_layer(w, inp, kp, mode, ov=ov)
         if kp:
@@ -85,7 +87,7 @@ def test_modes_agree(name):
     kp = max(w.k_spec)
     runs = {}
     for mode in ("prr_2stream", "prr_fused", "prr_1stream", "serialized", "serialized_fused"):
-        inp = make_inputs(w, device="cuda")
+        inp = gap_inputs(w)
         runs[mode] = run_layer(w, inp, kp, mode, check=False)
     for a, b in zip(runs["prr_2stream"], runs["prr_1stream"]):
         assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["sel"], b["sel"])
@@ -109,9 +111,9 @@ def test_ema_state_save_restore():
     reproduces the remaining predicted sets and outputs exactly."""
     w = small("llama3_8b_32k")
     kp = w.k_spec[0]
-    inp = make_inputs(w, device="cuda")
+    inp = gap_inputs(w)
     full = run_layer(w, inp, kp, "prr_2stream", check=False)
-    inp = make_inputs(w, device="cuda")
+    inp = gap_inputs(w)
     layer = PRRLayer(shape_of(w), w.top_k, kp, w.alpha)
     layer.build(inp.k_cache, inp.v_cache, inp.table)
     cut = 4
@@ -147,7 +149,7 @@ def test_graph_replay_matches_eager(rows, mode):
         w = small("million_token").replace(ctx=32 * 12000 - 7, top_k=61, k_spec=(93,), steps=6)
         kp = 93
     print(f"[case] graph replay {rows} rows N={w.n_blocks} {mode}", flush=True)
-    inp = make_inputs(w, device="cuda")
+    inp = gap_inputs(w)
     qs = [inp.q[t].contiguous() for t in range(w.steps)]
     seq = [0] + [1, 2, 3, 4] * 3
     eager = PRRLayer(shape_of(w), w.top_k, kp, w.alpha, mode=mode)
@@ -195,7 +197,7 @@ def test_dtypes_and_group_sizes(dtype, G):
     for page, mode, k in ((16, "prr_fused", 13), (8, "serialized", 11), (16, "prr_fused", 40), (8, "prr_fused", 13)):
         w = _variant(dtype, G, page, k)
         print(f"[case] {w.name} {mode} K={k}", flush=True)
-        inp = make_inputs(w, device="cuda")
+        inp = gap_inputs(w)
         ov = OracleView(inp)
         run_layer(w, inp, max(w.k_spec), mode, ov=ov)
 
@@ -203,7 +205,7 @@ def test_dtypes_and_group_sizes(dtype, G):
 def test_all_blocks_selected_is_dense_attention():
     """K = N (every block selected) equals dense attention over the whole context, in the fused PRR step."""
     w = small("tiny_f32_4k").replace(top_k=128, k_spec=(128,), steps=3)
-    inp = make_inputs(w, device="cuda")
+    inp = gap_inputs(w)
     ov = OracleView(inp)
     hist = run_layer(w, inp, 128, "prr_fused", ov=ov)
     G = w.group
@@ -226,7 +228,7 @@ def test_partial_last_block_decode(name, short, mode):
     output, missed count and predicted set against the oracle over the tokens that exist."""
     w = ragged(small(name), short).replace(steps=4)
     print(f"[case] partial decode {w.name} ctx={w.ctx} {mode}", flush=True)
-    inp = make_inputs(w, device="cuda")
+    inp = gap_inputs(w)
     ov = OracleView(inp)
     kp = max(w.k_spec) or w.top_k
     run_layer(w, inp, kp, mode, ov=ov)
@@ -261,7 +263,7 @@ def test_decode_with_appends(name, mode):
     every step against the oracle over the sequences with the same appended tokens."""
     w = ragged(small(name), 7).replace(steps=6)
     print(f"[case] decode with appends {w.name} {mode}", flush=True)
-    inp = make_inputs(w, device="cuda")
+    inp = gap_inputs(w)
     view = _Grown(OracleView(inp))
     kp = max(w.k_spec) or w.top_k
     layer = PRRLayer(shape_of(w), w.top_k, kp, w.alpha, mode=mode)
@@ -296,7 +298,7 @@ def test_forced_blocks_decode(name, mode):
     prediction: each step against the oracle with the same forced blocks."""
     w = small(name).replace(sink_blocks=1, local_blocks=3, steps=4)
     print(f"[case] forced blocks decode {name} {mode}", flush=True)
-    inp = make_inputs(w, device="cuda")
+    inp = gap_inputs(w)
     kp = max(w.k_spec) or w.top_k
     run_layer(w, inp, kp, mode, ov=OracleView(inp))
 
@@ -314,7 +316,7 @@ def test_mean_scorer_decode(name, mode, extra):
     if short:
         w = ragged(w, short)
     print(f"[case] mean scorer decode {w.name} {mode} {extra}", flush=True)
-    inp = make_inputs(w, device="cuda")
+    inp = gap_inputs(w)
     kp = max(w.k_spec) or w.top_k
     run_layer(w, inp, kp, mode, ov=OracleView(inp))
 
@@ -331,6 +333,6 @@ def test_degenerate_contexts(ctx, bs, page, k, kp, mode):
     w = Workload(f"degenerate_{ctx}_{bs}_{page}", 2, 8, 2, 128, ctx, bs, page, k, (kp,), 0.8, 0.9, 4, 0,
                  shuffle_pages=True, seed=20261203 + ctx + bs + page)
     print(f"[case] degenerate ctx={ctx} bs={bs} page={page} N={w.n_blocks} K={k} K'={kp} {mode}", flush=True)
-    inp = make_inputs(w, device="cuda")
+    inp = gap_inputs(w)
     ov = OracleView(inp)
     run_layer(w, inp, kp if mode != "serialized" else 0, mode, ov=ov)

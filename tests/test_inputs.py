@@ -1,5 +1,6 @@
 """The seeded input generator: determinism, hot-block planting, drift, paging (CPU)."""
 import numpy as np
+import pytest
 import torch
 
 from dynamic_sparse_attention_decode_amd.inputs import WORKLOADS, make_inputs, query_stream, block_table
@@ -106,3 +107,65 @@ def test_drift_moves_one_block_per_row():
 def _keys(cache, inp, b, g, n):
     pages = torch.as_tensor(inp._pages_of_block(b, n), dtype=torch.long)
     return cache[pages, g].reshape(inp.w.block_size, inp.w.head_dim)
+
+
+def test_bytes_do_not_depend_on_thread_count():
+    w = _small("paged_b32_64k", batch=3)
+    a = make_inputs(w, threads=1)
+    b = make_inputs(w, threads=5)
+    assert torch.equal(a.k_cache.view(torch.int16), b.k_cache.view(torch.int16))
+    assert torch.equal(a.v_cache.view(torch.int16), b.v_cache.view(torch.int16))
+
+
+def test_cache_rows_follow_the_host_recipe():
+    """Through the page table, each row of the cache is the host draw (bias planted on the hot blocks) cast to the
+    storage dtype; slots past the context hold the poison values."""
+    from dynamic_sparse_attention_decode_amd import inputs as I
+    w = _small("paged_b32_64k", batch=2, hot_blocks=5, ctx=16 * 64 - 7)
+    inp = make_inputs(w)
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            pages = torch.as_tensor(inp.table_np[b], dtype=torch.long)
+            k = inp.k_cache[pages, g].reshape(w.capacity, w.head_dim)
+            v = inp.v_cache[pages, g].reshape(w.capacity, w.head_dim)
+            kr = I.key_row(w, b, g)
+            I.plant_hot(kr, inp.hot[b, g], w.hot_bias * inp.qhat[b, g], w.block_size)
+            assert torch.equal(k.view(torch.int16), I.to_storage(kr, w.dtype).view(torch.int16))
+            assert torch.equal(v.view(torch.int16), I.to_storage(I.value_row(w, b, g), w.dtype).view(torch.int16))
+            # poison past the end (a hot last block carries the bias there too)
+            assert torch.all(k[w.ctx:].float() > 45.0) and torch.all(v[w.ctx:].float() > 9000.0)
+
+
+def test_attempts_redraw_only_their_group_step():
+    w = _small("llama3_8b_32k", batch=2, steps=6)
+    base = query_stream(w)
+    att = np.zeros((w.steps, w.batch, w.n_kv_heads), dtype=np.int64)
+    att[3, 1, 5] = 2
+    q = query_stream(w, attempts=att)
+    G = w.group
+    diff = np.argwhere(np.any(q != base, axis=-1))
+    assert len(diff) > 0
+    for t, b, h in diff:
+        assert t >= 3 and b == 1 and h // G == 5, (t, b, h)
+    assert np.all(np.any(q[3:, 1, 5 * G:6 * G] != base[3:, 1, 5 * G:6 * G], axis=-1))
+    att0 = att.copy()
+    att0[0, 0, 2] = 1   # a redrawn first query moves that group's hot-block bias direction too
+    inp_a = make_inputs(w.replace(steps=2), attempts=att0[:2])
+    inp_b = make_inputs(w.replace(steps=2))
+    assert not np.array_equal(inp_a.qhat[0, 2], inp_b.qhat[0, 2])
+    assert np.array_equal(inp_a.qhat[0, 1], inp_b.qhat[0, 1])
+
+
+def test_load_attempts_checks_the_workload(tmp_path):
+    import json
+    from dynamic_sparse_attention_decode_amd.inputs import load_attempts
+    w = _small("tiny_f32_4k", steps=3)
+    a = np.arange(3 * w.batch * w.n_kv_heads).reshape(3, w.batch, w.n_kv_heads)
+    p = tmp_path / "t.json"
+    p.write_text(json.dumps({"workload": w.key(), "shape": list(a.shape), "attempts": a.ravel().tolist()}))
+    assert np.array_equal(load_attempts(str(p), w), a)
+    assert np.array_equal(load_attempts(str(p), w, steps=2), a[:2])
+    with pytest.raises(ValueError):
+        load_attempts(str(p), w.replace(seed=1))
+    with pytest.raises(ValueError):
+        load_attempts(str(p), w.replace(steps=4))
