@@ -22,7 +22,7 @@ _DT_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 EXPORTS = ["prr_build_summaries", "prr_append_kv", "prr_score_select", "prr_ema_predict", "prr_speculate", "prr_repair_merge",
            "prr_score", "prr_select_speculate", "prr_score_speculate", "prr_select_repair",
            "prr_partials_bytes", "prr_workspace_bytes", "prr_step_ctx_create", "prr_step_ctx_destroy",
-           "prr_decode_step", "prr_choose_budget", "prr_trace_create", "prr_trace_destroy", "prr_trace_enable",
+           "prr_decode_step", "prr_decode_step_noalloc", "prr_choose_budget", "prr_trace_create", "prr_trace_destroy", "prr_trace_enable",
            "prr_trace_read", "prr_flush_write", "prr_stream_read", "prr_status_string", "prr_last_error",
            "prr_version"]
 
@@ -124,6 +124,7 @@ def lib():
         "prr_step_ctx_create": (i32, [ctypes.POINTER(vp)]),
         "prr_step_ctx_destroy": (None, [vp]),
         "prr_decode_step": (i32, [vp, sp, ctypes.POINTER(StepArgs), i32, i32, vp, vp]),
+        "prr_decode_step_noalloc": (i32, [vp, sp, ctypes.POINTER(StepArgs), i32, i32, vp, vp]),
         "prr_choose_budget": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), i32,
                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), i32,
                                     ctypes.c_double, i32]),
@@ -288,6 +289,15 @@ def step_ctx_destroy(h) -> None:
 def decode_step(ctx, shape: Shape, args: StepArgs, mode: int, join: bool, stream_sel, stream_spec) -> None:
     _check(lib().prr_decode_step(ctx, ctypes.byref(shape), ctypes.byref(args), mode, int(bool(join)),
                                  _s(stream_sel), _s(stream_spec)), "decode_step")
+
+
+def decode_step_noalloc(ctx, shape: Shape, args: StepArgs, mode: int, join: bool, stream_sel, stream_spec) -> None:
+    """prr_decode_step with the library's static scratch as the workspace (args.workspace must be None)."""
+    _check(lib().prr_decode_step_noalloc(ctx, ctypes.byref(shape), ctypes.byref(args), mode, int(bool(join)),
+                                         _s(stream_sel), _s(stream_spec)), "decode_step_noalloc")
+
+
+SCRATCH_MAX_BYTES = 32 << 20   # PRR_SCRATCH_MAX_BYTES in include/prr.h
 
 
 def choose_budget(n_grid, t_sel, kspec_grid, t_spec, n_target: float, degree: int = 2) -> int:

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <new>
 
 #include "prr_device.h"
@@ -210,6 +211,60 @@ struct prr_step_ctx {
 };
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---- the allocation-free step's scratch ------------------------------------------------------------------------------
+// A file-scope device array stands in for the caller's workspace in prr_decode_step_noalloc. Each GPU the library
+// runs on holds its own copy (module-load time, until the process ends). In host code its name is only a host-side
+// stand-in: the device address comes from hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever passed to kernels. The workspace needs no initialisation, so nothing is cleared.
+constexpr size_t kScratchBytes = (size_t)PRR_SCRATCH_MAX_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_addr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The scratch's device address for the device of `stream` (the null stream: the current device), which must be the
+// current device.
+static prr_status scratch_of_stream(hipStream_t stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) {
+    set_error("decode_step_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    (void)hipGetLastError();
+    return PRR_ELAUNCH;
+  }
+  int dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) {
+      set_error("decode_step_noalloc: hipStreamGetDevice: %s", hipGetErrorString(e));
+      (void)hipGetLastError();
+      return PRR_ELAUNCH;
+    }
+  }
+  PRR_REQUIRE(dev == cur, "decode_step_noalloc: the stream is on device %d, make it current (device %d is)", dev, cur);
+  PRR_REQUIRE(dev >= 0 && dev < kMaxDevices, "decode_step_noalloc: device %d out of range", dev);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) {
+        set_error("decode_step_noalloc: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        (void)hipGetLastError();
+        return PRR_ELAUNCH;
+      }
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PRR_OK;
+}
+
+static prr_status decode_step_impl(prr_step_ctx* ctx, const prr_shape* shape, const prr_step_args* a, int32_t mode,
+                                   int32_t join, void* stream_sel, void* stream_spec);
 
 // The workspace: three top-K candidate regions for long rows (the true set's, the predicted set's, and the
 // optimistic scores' of a confidence budget), then the repair's part (spread-out or row-wise repair). The parts are
@@ -433,6 +488,34 @@ static prr_status hip_ok(hipError_t e, const char* what) {
 
 prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_step_args* a, int32_t mode,
                            int32_t join, void* stream_sel, void* stream_spec) {
+  return decode_step_impl(ctx, shape, a, mode, join, stream_sel, stream_spec);
+}
+
+prr_status prr_decode_step_noalloc(prr_step_ctx* ctx, const prr_shape* shape, const prr_step_args* a, int32_t mode,
+                                   int32_t join, void* stream_sel, void* stream_spec) {
+  PRR_TRY(check_shape(shape));
+  PRR_REQUIRE(a, "decode_step_noalloc: args is NULL");
+  PRR_REQUIRE(!a->workspace, "decode_step_noalloc: args->workspace must be NULL (the library's scratch is used)");
+  PRR_REQUIRE(a->top_k >= 1 && a->top_k <= shape->n_blocks, "decode_step_noalloc: top_k %d not in [1, %d]",
+              a->top_k, shape->n_blocks);
+  const size_t need = prr_workspace_bytes(shape, a->top_k);
+  PRR_REQUIRE(need <= kScratchBytes, "decode_step_noalloc: this shape needs %zu bytes of workspace, more than the "
+              "library's %zu-byte scratch (use prr_decode_step with a workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  PRR_TRY(scratch_of_stream(as_stream(stream_sel), &ws));
+  if (mode == PRR_MODE_TWO_STREAM) {   // both streams must be on the scratch's device
+    void* ws2 = nullptr;
+    PRR_TRY(scratch_of_stream(as_stream(stream_spec), &ws2));
+  }
+  prr_step_args with_ws = *a;
+  with_ws.workspace = ws;
+  return decode_step_impl(ctx, shape, &with_ws, mode, join, stream_sel, stream_spec);
+}
+
+}  // extern "C"
+
+static prr_status decode_step_impl(prr_step_ctx* ctx, const prr_shape* shape, const prr_step_args* a, int32_t mode,
+                                   int32_t join, void* stream_sel, void* stream_spec) {
   PRR_TRY(check_shape(shape));
   PRR_REQUIRE(a, "decode_step: args is NULL");
   PRR_REQUIRE(mode >= PRR_MODE_SERIALIZED && mode <= PRR_MODE_SERIALIZED_FUSED, "decode_step: unknown mode %d", mode);
@@ -537,6 +620,8 @@ prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_
   }
   return PRR_OK;
 }
+
+extern "C" {
 
 prr_status prr_trace_create(prr_trace** out, int32_t capacity) {
   if (!out || capacity < 1) { set_error("trace_create: null pointer or capacity < 1"); return PRR_EINVAL; }

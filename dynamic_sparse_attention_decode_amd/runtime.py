@@ -30,10 +30,11 @@ BUDGETS = {"fixed": L.BUDGET_FIXED, "misses": L.BUDGET_MISSES, "confidence": L.B
 
 class PRRLayer:
     def __init__(self, shape: L.Shape, top_k: int, k_spec: int, alpha: float, mode: str = "prr_2stream",
-                 device="cuda", streams=None, budget: dict | None = None):
+                 device="cuda", streams=None, budget: dict | None = None, static_workspace: bool = False):
         """budget: None (every row predicts k_spec blocks) or {"policy": "misses" | "confidence", "k_min": int,
         "beta": float, "c": float}: per-row sizes of the predicted set, at most k_spec (prr_budget); the missed
-        counts that the misses policy reads are double-buffered here."""
+        counts that the misses policy reads are double-buffered here. static_workspace: step through
+        prr_decode_step_noalloc (the library's scratch; no workspace buffer here)."""
         if mode not in MODES:
             raise ValueError(f"mode must be one of {list(MODES)}")
         self.shape = L.Shape.from_buffer_copy(shape)   # own copy: append() advances its ctx_len
@@ -62,8 +63,9 @@ class PRRLayer:
             # step t writes P_{t+1} under the budget whose missed counts are step t-1's (the other parity)
             self.budgets = [L.make_budget(pol, self.top_k, int(budget.get("k_min", 1)), float(budget.get("beta", 0.0)),
                                           float(budget.get("c", 0.0)), self.missed[1 - par]) for par in range(2)]
-        self.workspace = torch.zeros((L.workspace_bytes(shape, self.top_k) // 4 + 1,), dtype=torch.float32,
-                                     device=dev)
+        self.static_workspace = bool(static_workspace)
+        self.workspace = None if self.static_workspace else torch.zeros(
+            (L.workspace_bytes(shape, self.top_k) // 4 + 1,), dtype=torch.float32, device=dev)
         if streams is None:
             streams = (torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev))
         self.s_sel, self.s_spec = streams
@@ -126,7 +128,7 @@ class PRRLayer:
         t = self.t
         par, nxt = t % 2, (t + 1) % 2
         kc = self.k_spec if t > 0 else 0
-        vp = lambda x: ctypes.c_void_p(x.data_ptr())
+        vp = lambda x: None if x is None else ctypes.c_void_p(x.data_ptr())
         bud = ctypes.addressof(self.budgets[par]) if self.budgets else None
         return L.StepArgs(vp(q), vp(self.k_cache), vp(self.v_cache), vp(self.table), vp(self.summaries),
                           vp(self.scores[par]), vp(self.sel_idx), vp(self.ema), vp(self.pred[par]),
@@ -141,7 +143,8 @@ class PRRLayer:
         if tuple(q.shape) != (self.shape.batch, self.shape.n_q_heads, self.shape.head_dim):
             raise L.PRRError(f"q has shape {tuple(q.shape)}")
         out = self.out[self.t % 2]
-        L.decode_step(self.ctx, self.shape, self._args(q), MODES[self.mode], join, self.s_sel, self.s_spec)
+        step = L.decode_step_noalloc if self.static_workspace else L.decode_step
+        step(self.ctx, self.shape, self._args(q), MODES[self.mode], join, self.s_sel, self.s_spec)
         self.t += 1
         return out
 

@@ -271,6 +271,23 @@ void prr_step_ctx_destroy(prr_step_ctx* ctx);
 prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_step_args* args, int32_t mode,
                            int32_t join, void* stream_sel, void* stream_spec);
 
+/* ---- the same step without a caller workspace ---------------------------------------------------------------- */
+
+/* Bytes of the library's static scratch that prr_decode_step_noalloc uses as its workspace. */
+#define PRR_SCRATCH_MAX_BYTES (32u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): prr_decode_step with the workspace taken from a file-scope device array of
+ * PRR_SCRATCH_MAX_BYTES bytes that the library holds on every GPU it runs on until the process ends. args->workspace
+ * must be NULL; every other argument, mode and result is as in prr_decode_step (same kernels, same order, so the
+ * same bits). Calls nothing that allocates. Returns PRR_EINVAL when prr_workspace_bytes(shape, args->top_k) exceeds
+ * PRR_SCRATCH_MAX_BYTES, or when a stream is not on the current device; PRR_ELAUNCH when the scratch's device address
+ * cannot be taken (first call on a device). All calls on one GPU share its scratch, which keeps the last call's
+ * contents (the workspace needs no initialisation): calls that overlap on one GPU (two streams, two threads, two
+ * layers in flight) race; order them. */
+prr_status prr_decode_step_noalloc(prr_step_ctx* ctx, const prr_shape* shape, const prr_step_args* args,
+                                   int32_t mode, int32_t join, void* stream_sel, void* stream_spec);
+
 /* Profiling-guided speculation budget (PRR abstract; PRR summary page, Limitations: polynomial regression outside
  * the profiled grid). Returns the largest kspec_grid[i] with t_spec[i] <= t_sel(n_target), where t_sel(n_target)
  * is t_sel[j] if n_grid[j] == n_target, else a least-squares polynomial of degree poly_degree (clamped to
