@@ -78,6 +78,16 @@ def test_decode_vs_oracle(name, mode):
                   f"mean missed {np.mean([h['nm'].mean() for h in hist[1:]]):.2f}")
 
 
+@pytest.mark.parametrize("k_spec", [12, 20])
+def test_decode_many_rows_vs_oracle(k_spec):
+    """A batch of 136 rows (17 sequences x 8 KV heads): the fused step speculates inside the scoring launch and
+    attends the missed blocks per row after their selection; every step against the oracle."""
+    w = small("paged_b32_64k").replace(batch=17, ctx=16 * 70 - 3, top_k=12, k_spec=(k_spec,), steps=5)
+    print(f"[case] decode many rows B={w.batch} K'={k_spec}", flush=True)
+    inp = gap_inputs(w)
+    run_layer(w, inp, k_spec, "prr_fused", ov=OracleView(inp))
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_32k", "paged_b32_64k", "tiny_f32_4k", "million_token"])
 def test_modes_agree(name):
     """Two-stream and one-stream runs are bitwise identical (same kernels, same order). The two-launch fused run
