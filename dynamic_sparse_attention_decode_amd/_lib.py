@@ -22,6 +22,7 @@ _DT_CODE = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 EXPORTS = ["prr_build_summaries", "prr_append_kv", "prr_score_select", "prr_ema_predict", "prr_speculate", "prr_repair_merge",
            "prr_score", "prr_select_speculate", "prr_score_speculate", "prr_select_repair",
            "prr_partials_bytes", "prr_workspace_bytes", "prr_step_ctx_create", "prr_step_ctx_destroy",
+           "prr_step_ctx_set_delays",
            "prr_decode_step", "prr_decode_step_noalloc", "prr_choose_budget", "prr_trace_create", "prr_trace_destroy", "prr_trace_enable",
            "prr_trace_read", "prr_flush_write", "prr_stream_read", "prr_status_string", "prr_last_error",
            "prr_version"]
@@ -123,6 +124,7 @@ def lib():
         "prr_workspace_bytes": (sz, [sp, i32]),
         "prr_step_ctx_create": (i32, [ctypes.POINTER(vp)]),
         "prr_step_ctx_destroy": (None, [vp]),
+        "prr_step_ctx_set_delays": (i32, [vp, i32, i32]),
         "prr_decode_step": (i32, [vp, sp, ctypes.POINTER(StepArgs), i32, i32, vp, vp]),
         "prr_decode_step_noalloc": (i32, [vp, sp, ctypes.POINTER(StepArgs), i32, i32, vp, vp]),
         "prr_choose_budget": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), i32,
@@ -289,6 +291,11 @@ def step_ctx_destroy(h) -> None:
 def decode_step(ctx, shape: Shape, args: StepArgs, mode: int, join: bool, stream_sel, stream_spec) -> None:
     _check(lib().prr_decode_step(ctx, ctypes.byref(shape), ctypes.byref(args), mode, int(bool(join)),
                                  _s(stream_sel), _s(stream_spec)), "decode_step")
+
+
+def step_ctx_set_delays(ctx, delay_sel: int, delay_spec: int) -> None:
+    """Race check: sleep iterations before the repair (stream_sel) and before the speculation (stream_spec)."""
+    _check(lib().prr_step_ctx_set_delays(ctx, int(delay_sel), int(delay_spec)), "step_ctx_set_delays")
 
 
 def decode_step_noalloc(ctx, shape: Shape, args: StepArgs, mode: int, join: bool, stream_sel, stream_spec) -> None:

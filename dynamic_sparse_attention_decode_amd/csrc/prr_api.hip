@@ -207,8 +207,20 @@ static prr_status check_budget(const prr_shape* s, const prr_budget* b, int k_sp
 using namespace prr;
 
 struct prr_step_ctx {
-  hipEvent_t q_ready, spec_done, sel_done, spec_tail;
+  hipEvent_t q_ready, spec_done;   // the fork and the join of the two-stream step
+  int32_t delay_sel = 0, delay_spec = 0;   // race check: sleep iterations before the repair / the speculation
 };
+
+// A bounded sleep of `iters` s_sleep(127) instructions (about 8000 shader clocks each) by one wave: a kernel that
+// only takes time, for checking that results do not depend on the timing of the two streams.
+__global__ __launch_bounds__(64) void delay_kernel(int32_t iters) {
+  for (int32_t i = 0; i < iters; ++i) __builtin_amdgcn_s_sleep(127);
+}
+
+static prr_status launch_delay(int32_t iters, hipStream_t st) {
+  delay_kernel<<<dim3(1), dim3(64), 0, st>>>(iters);
+  return check_launch("step delay");
+}
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -456,8 +468,8 @@ prr_status prr_step_ctx_create(prr_step_ctx** out) {
   if (!out) { set_error("step_ctx_create: null pointer"); return PRR_EINVAL; }
   auto* c = new (std::nothrow) prr_step_ctx{};
   if (!c) { set_error("step_ctx_create: out of host memory"); return PRR_EINVAL; }
-  hipEvent_t* ev[4] = {&c->q_ready, &c->spec_done, &c->sel_done, &c->spec_tail};
-  for (int i = 0; i < 4; ++i) {
+  hipEvent_t* ev[2] = {&c->q_ready, &c->spec_done};
+  for (int i = 0; i < 2; ++i) {
     if (hipEventCreateWithFlags(ev[i], hipEventDisableTiming) != hipSuccess) {
       for (int j = 0; j < i; ++j) (void)hipEventDestroy(*ev[j]);
       delete c;
@@ -469,12 +481,19 @@ prr_status prr_step_ctx_create(prr_step_ctx** out) {
   return PRR_OK;
 }
 
+prr_status prr_step_ctx_set_delays(prr_step_ctx* ctx, int32_t delay_sel, int32_t delay_spec) {
+  PRR_REQUIRE(ctx, "step_ctx_set_delays: null context");
+  PRR_REQUIRE(delay_sel >= 0 && delay_sel <= 100000 && delay_spec >= 0 && delay_spec <= 100000,
+              "step_ctx_set_delays: delays must be in [0, 100000] sleep iterations");
+  ctx->delay_sel = delay_sel;
+  ctx->delay_spec = delay_spec;
+  return PRR_OK;
+}
+
 void prr_step_ctx_destroy(prr_step_ctx* ctx) {
   if (!ctx) return;
   (void)hipEventDestroy(ctx->q_ready);
   (void)hipEventDestroy(ctx->spec_done);
-  (void)hipEventDestroy(ctx->sel_done);
-  (void)hipEventDestroy(ctx->spec_tail);
   delete ctx;
 }
 
@@ -600,24 +619,23 @@ static prr_status decode_step_impl(prr_step_ctx* ctx, const prr_shape* shape, co
     if (kn > 0) PRR_TRY(ema_predict(s1));
     return PRR_OK;
   }
-  PRR_TRY(hip_ok(hipEventRecord(ctx->q_ready, s1), "decode_step: record q_ready"));
-  PRR_TRY(hip_ok(hipStreamWaitEvent(s2, ctx->q_ready, 0), "decode_step: wait q_ready"));
+  // One fork and one join per step: speculation over P_t runs on stream_spec while stream_sel scores and selects;
+  // the repair waits for it; the next prediction follows the repair on stream_sel, so the next step's fork (recorded
+  // after it) orders the next speculation after P_{t+1}. Every edge between the streams costs an idle gap when a
+  // graph runs the two branches on different hardware queues, so the step keeps only these two.
+  (void)join;   // stream_spec's work always ends in the join below
+  PRR_TRY(hip_ok(hipEventRecord(ctx->q_ready, s1), "decode_step: record fork"));
+  PRR_TRY(hip_ok(hipStreamWaitEvent(s2, ctx->q_ready, 0), "decode_step: wait fork"));
+  if (ctx->delay_spec > 0) PRR_TRY(launch_delay(ctx->delay_spec, s2));
   if (kc > 0) PRR_TRY(prr_speculate(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->pred_cur, kc,
                                     a->partials, s2));
-  PRR_TRY(hip_ok(hipEventRecord(ctx->spec_done, s2), "decode_step: record spec_done"));
+  PRR_TRY(hip_ok(hipEventRecord(ctx->spec_done, s2), "decode_step: record join"));
   PRR_TRY(score_select(s1));
-  PRR_TRY(hip_ok(hipEventRecord(ctx->sel_done, s1), "decode_step: record sel_done"));
-  PRR_TRY(hip_ok(hipStreamWaitEvent(s1, ctx->spec_done, 0), "decode_step: wait spec_done"));
+  PRR_TRY(hip_ok(hipStreamWaitEvent(s1, ctx->spec_done, 0), "decode_step: wait join"));
+  if (ctx->delay_sel > 0) PRR_TRY(launch_delay(ctx->delay_sel, s1));
   PRR_TRY(prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
                            kc, a->partials, a->out, a->n_missed, a->workspace, s1));
-  if (kn > 0) {
-    PRR_TRY(hip_ok(hipStreamWaitEvent(s2, ctx->sel_done, 0), "decode_step: wait sel_done"));
-    PRR_TRY(ema_predict(s2));
-  }
-  if (join) {
-    PRR_TRY(hip_ok(hipEventRecord(ctx->spec_tail, s2), "decode_step: record spec_tail"));
-    PRR_TRY(hip_ok(hipStreamWaitEvent(s1, ctx->spec_tail, 0), "decode_step: wait spec_tail"));
-  }
+  if (kn > 0) PRR_TRY(ema_predict(s1));
   return PRR_OK;
 }
 

@@ -261,13 +261,21 @@ typedef struct {
 typedef struct prr_step_ctx prr_step_ctx;
 prr_status prr_step_ctx_create(prr_step_ctx** out);
 void prr_step_ctx_destroy(prr_step_ctx* ctx);
+/* Race check of the two-stream step: every later PRR_MODE_TWO_STREAM step with this context enqueues a bounded sleep
+ * kernel of delay_spec iterations on stream_spec before the speculation and one of delay_sel iterations on
+ * stream_sel between the join and the repair (one iteration is about 8000 shader clocks; 0 = none; each in
+ * [0, 100000]). The results must not change: a step whose streams were wrongly ordered would read partial records
+ * or predicted sets that are not yet written, or that the other stream overwrites. Test instrumentation. */
+prr_status prr_step_ctx_set_delays(prr_step_ctx* ctx, int32_t delay_sel, int32_t delay_spec);
 
-/* Enqueue one PRR decode step. Two-stream order (PRR abstract: speculation runs while selection is in flight):
- *   stream_sel:  [record q-ready] score_select [record sel-done] [wait spec-done] repair_merge
- *   stream_spec: [wait q-ready] speculate(P_t) [record spec-done] [wait sel-done] ema_predict -> P_{t+1}
- * `out` is complete on stream_sel when the call's work there finishes; P_{t+1} is complete on stream_spec, and the
- * next call's speculation is ordered after it. Pass join != 0 to make stream_sel also wait for stream_spec's work
- * (needed at the end of a graph capture). In PRR_MODE_ONE_STREAM and PRR_MODE_SERIALIZED only stream_sel is used. */
+/* Enqueue one PRR decode step. Two-stream order (PRR abstract: speculation runs while selection is in flight), one
+ * fork and one join per step:
+ *   stream_sel:  [record fork] score_select [wait join] repair_merge ema_predict -> P_{t+1}
+ *   stream_spec: [wait fork] speculate(P_t) [record join]
+ * `out` and P_{t+1} are complete on stream_sel when the call's work there finishes; the next call's speculation is
+ * ordered after them by its fork. stream_spec's work always ends in the join, so a graph capture of steps on
+ * stream_sel is closed; `join` is accepted and has no further effect. In PRR_MODE_ONE_STREAM and PRR_MODE_SERIALIZED
+ * only stream_sel is used. */
 prr_status prr_decode_step(prr_step_ctx* ctx, const prr_shape* shape, const prr_step_args* args, int32_t mode,
                            int32_t join, void* stream_sel, void* stream_spec);
 

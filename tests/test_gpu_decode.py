@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 import torch
 
+from dynamic_sparse_attention_decode_amd import _lib as L
 from dynamic_sparse_attention_decode_amd.runtime import PRRLayer
 from oracle import prr_oracle as O
 from tests.checker import TOL, check_selection, max_abs
@@ -76,6 +77,40 @@ def test_decode_vs_oracle(name, mode):
                         for h in hist[1:] for b in range(w.batch) for g in range(w.n_kv_heads)]
             print(f"[result] {name} K'={kp}: mean overlap {np.mean(ov_steps):.3f}, "
                   f"mean missed {np.mean([h['nm'].mean() for h in hist[1:]]):.2f}")
+
+
+def _run_unsynced(w, inp, k_spec, mode, delays=None):
+    """All steps enqueued without a host synchronisation between them; each step's results are copied on the
+    caller's stream (ordered after the step's stream_sel work)."""
+    layer = PRRLayer(shape_of(w), w.top_k, k_spec, w.alpha, mode=mode)
+    if delays:
+        L.step_ctx_set_delays(layer.ctx, *delays)
+    layer.build(inp.k_cache, inp.v_cache, inp.table)
+    qs = [inp.q[t].contiguous() for t in range(w.steps)]
+    res = []
+    for t in range(w.steps):
+        out = layer.step(qs[t])
+        res.append((out.clone(), layer.sel_idx.clone(), layer.n_missed.clone(), layer.pred_next.clone()))
+    torch.cuda.synchronize()
+    layer.close()
+    return [tuple(x.cpu().numpy() for x in r) for r in res]
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_32k", "paged_b32_64k", "million_token"])
+def test_two_stream_delays_do_not_change_results(name):
+    """Race check: a bounded sleep kernel (about 100 us) on stream_spec before the speculation, on stream_sel before
+    the repair, or on both, leaves every step's output, selection, missed count and next predicted set bitwise equal
+    to the one-stream run: the two streams are ordered by their fork and join, not by timing."""
+    w = small(name)
+    kp = max(w.k_spec)
+    inp = gap_inputs(w)
+    ref = _run_unsynced(w, inp, kp, "prr_1stream")
+    for delays in ((0, 30), (30, 0), (30, 30)):
+        print(f"[case] two-stream delays {name} (sel, spec) = {delays}", flush=True)
+        got = _run_unsynced(w, inp, kp, "prr_2stream", delays)
+        for t, (a, b) in enumerate(zip(ref, got)):
+            for x, y, what in zip(a, b, ("out", "sel_idx", "n_missed", "pred_next")):
+                assert np.array_equal(x, y), (delays, t, what)
 
 
 @pytest.mark.parametrize("k_spec", [12, 20])
