@@ -327,6 +327,21 @@ def choose_budget(n_grid, t_sel, kspec_grid, t_spec, n_target: float, degree: in
     return best
 
 
+def choose_budget_fused(kspec_grid, t_step) -> int:
+    """Budget of the fused single-stream step, where the speculation shares the selection launch: both its cost (the
+    launch grows) and its saving (fewer missed blocks to repair) show only in the step's own time, so the profile
+    measures the step at each grid budget (the grid holds 0, the step without speculation). K'* is the largest
+    profiled K' whose step time is at most the step time without speculation: the largest budget that keeps the
+    speculative work off the step's critical path."""
+    ks = [int(k) for k in kspec_grid]
+    t0 = float(t_step[ks.index(0)])
+    best = 0
+    for k, t in zip(ks, t_step):
+        if float(t) <= t0 and k > best:
+            best = k
+    return best
+
+
 # ------------------------------------------------------------------------------------------------------------------
 # brute force (tiny inputs only): used by the pins
 # ------------------------------------------------------------------------------------------------------------------

@@ -456,7 +456,20 @@ def pin_boundary_gap(o):
         assert (count == 1) == (gap > 0), (vals, k, gap, count)
 
 
+def pin_budget_fused_closed_form(o):
+    """The fused-step budget on hand-made step-time tables: the largest K' whose step time is at most the time
+    without speculation (a tie with it qualifies), whatever the order of the grid; 0 when every budget lengthens the
+    step; the grid's largest K' when speculation never costs more."""
+    ks = [0, 32, 64, 128, 192]
+    assert o.choose_budget_fused(ks, [20.0, 19.0, 19.5, 20.0, 21.0]) == 128     # 128 ties t(0)
+    assert o.choose_budget_fused(ks, [20.0, 19.0, 20.5, 19.9, 24.0]) == 128     # not monotone: 64 fails, 128 fits
+    assert o.choose_budget_fused(ks, [20.0, 20.1, 21.0, 22.0, 25.0]) == 0
+    assert o.choose_budget_fused(ks, [20.0, 18.0, 17.0, 16.0, 15.0]) == 192
+    assert o.choose_budget_fused([64, 0, 128, 32], [19.0, 20.0, 19.5, 25.0]) == 128   # grid in any order
+
+
 ALL_PINS = [pin_dense_equivalence, pin_brute_force_selection, pin_quest_upper_bound, pin_signsplit,
             pin_merge_order_free, pin_repair_invariants, pin_closed_forms, pin_hand_example, pin_ema_closed_form,
             pin_budget_closed_form, pin_paged_gather, pin_partial_last_block, pin_forced_blocks,
-            pin_mean_key_scores, pin_adaptive_budgets, pin_boundary_gap]
+            pin_mean_key_scores, pin_adaptive_budgets, pin_boundary_gap,
+            pin_budget_fused_closed_form]

@@ -236,9 +236,30 @@ def _gap_ascending(values, k):
     return a, b, abs(a - b) / abs(a) if a != 0 else math.inf
 
 
+def _fused_strict(kspec_grid, t_step):
+    ks = list(kspec_grid)
+    t0 = t_step[ks.index(0)]
+    return max([0] + [k for k, t in zip(ks, t_step) if t < t0])
+
+
+def _fused_argmin(kspec_grid, t_step):
+    return int(list(kspec_grid)[int(np.argmin(t_step))])
+
+
+def _fused_smallest(kspec_grid, t_step):
+    best = _orig["choose_budget_fused"](kspec_grid, t_step)
+    ok = [k for k, t in zip(kspec_grid, t_step) if 0 < k and t <= t_step[list(kspec_grid).index(0)]]
+    return min(ok) if ok else best
+
+
+def _fused_first_entry(kspec_grid, t_step):
+    """Compares with the grid's first entry instead of the step without speculation."""
+    return max([0] + [k for k, t in zip(kspec_grid, t_step) if t <= t_step[0]])
+
+
 _orig = {k: getattr(O, k) for k in ["attention_over_blocks", "prr_output", "ema_update", "choose_budget",
                                     "block_summaries", "top_k", "mean_key_scores", "budget_from_confidence",
-                                    "boundary_gap"]}
+                                    "boundary_gap", "choose_budget_fused"]}
 
 MUTANTS = {
     "quest_drop_kmin": ("quest_scores", _quest_drop_kmin),
@@ -278,6 +299,10 @@ MUTANTS = {
     "gap_zero_branch": ("boundary_gap", _gap_zero_branch),
     "gap_over_next": ("boundary_gap", _gap_over_next),
     "gap_ascending": ("boundary_gap", _gap_ascending),
+    "fused_strict": ("choose_budget_fused", _fused_strict),
+    "fused_argmin": ("choose_budget_fused", _fused_argmin),
+    "fused_smallest": ("choose_budget_fused", _fused_smallest),
+    "fused_first_entry": ("choose_budget_fused", _fused_first_entry),
 }
 
 
