@@ -381,7 +381,7 @@ def main():
     del rd, rd_sink
     detail["hbm_read_GBps_measured"] = read_gbs
     if not a.no_budget_profile:   # the profiled budget K'* beside the fixed K' of the line
-        detail["budget_profile"] = budget_profile(w, inp)
+        detail["budget_profile"] = budget_profile(w, inp, kvs, qs, steps=min(a.steps, 32))
     detail["attention_path_frac_of_measured"] = (detail["attention_path_GBps"] / read_gbs
                                                  if detail["attention_path_GBps"] else None)
     if n_layers > 1:   # the same step with one layer only: its data stays in the Infinity Cache between steps
@@ -469,81 +469,36 @@ def workload_inputs(w, dev):
     return make_inputs(w, device=dev, attempts=attempts), info
 
 
-def budget_profile(w, inp):
-    """Profiling-guided speculation budget (PRR abstract; PRR summary page, Limitations): selection times on a grid of
-    block counts that leaves out the workload's own N, and the speculation time t_spec(K') on a grid of budgets, all
-    as graph replays of back-to-back calls timed with HIP events; K'* from prr_choose_budget with a degree-2
-    polynomial for the off-grid N. Two windows: the whole selection (scores + top-K), which speculation on a second
-    stream overlaps, and the selection launch alone, which the fused step's speculation overlaps. Prints one JSON
-    line."""
-    import numpy as np
+def budget_profile(w, inp, kvs=None, qs=None, steps=20):
+    """The profiling-guided speculation budget of the workload (dynamic_sparse_attention_decode_amd.profiling): the
+    two-stream rule's tables (selection over a grid of block counts, speculation over a grid of budgets) and the
+    fused step's table (whole steps at each grid budget, rotated over the same layers as the timed step), with K'*
+    from each."""
     import torch
 
     from dynamic_sparse_attention_decode_amd import _lib as L
+    from dynamic_sparse_attention_decode_amd import profiling as P
 
-    dev = torch.device("cuda:0")
+    dev = inp.k_cache.device
     dt = {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[w.dtype]
-    rows = w.batch * w.n_kv_heads
-    reps = 50
-
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        s = torch.cuda.Stream(device=dev)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            for _ in range(reps):
-                fn(s)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
-
-    N0 = w.n_blocks
-    n_grid = sorted({n for n in (N0 // 8, N0 // 4, N0 // 2, N0 * 2, N0 * 4) if 64 <= n <= 32768} - {N0})
-    g_ = torch.Generator(device=dev).manual_seed(w.seed)
-    t_sel, t_topk = [], []
-    for n in n_grid:
-        s = L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, n, dt, w.scale)
-        summ = torch.randn((w.batch, w.n_kv_heads, n, 2, w.head_dim), generator=g_, device=dev).to(w.torch_dtype)
-        q = torch.randn((w.batch, w.n_q_heads, w.head_dim), generator=g_, device=dev).to(w.torch_dtype)
-        sc = torch.zeros((w.batch, w.n_kv_heads, n), dtype=torch.float32, device=dev)
-        sel = torch.zeros((w.batch, w.n_kv_heads, min(w.top_k, n)), dtype=torch.int32, device=dev)
-        ws = torch.zeros((L.workspace_bytes(s, sel.shape[-1]) // 4 + 1,), dtype=torch.float32, device=dev)
-        # the whole selection (scores + top-K): the window a second stream can overlap
-        t_sel.append(timed(lambda st=None, s=s, q=q, summ=summ, sc=sc, sel=sel, ws=ws: L.score_select(
-            s, q, summ, sel.shape[-1], sc, sel, workspace=ws, stream=st)))
-        # the selection launch alone: the window the fused step's speculation overlaps
-        t_topk.append(timed(lambda st=None, s=s, sc=sc, sel=sel, ws=ws: L.select_speculate(
-            s, sc, sel.shape[-1], sel, workspace=ws, stream=st)))
-    s = L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, N0, dt, w.scale)
-    k_grid = sorted({0, w.top_k // 4, w.top_k // 2, w.top_k, (3 * w.top_k) // 2, 2 * w.top_k} | set(w.k_spec))
-    k_grid = [k for k in k_grid if k <= N0]
-    rng = np.random.default_rng(w.seed)
-    t_spec = []
-    for k in k_grid:
-        if k == 0:
-            t_spec.append(0.0)
-            continue
-        pred = torch.as_tensor(np.stack([np.sort(rng.choice(N0, k, replace=False)) for _ in range(rows)])
-                               .reshape(w.batch, w.n_kv_heads, k).astype(np.int32), device=dev)
-        part = torch.zeros((L.partials_bytes(s, k) // 4,), dtype=torch.float32, device=dev)
-        q = inp.q[1].contiguous()
-        t_spec.append(timed(lambda st=None, pred=pred, part=part, k=k, q=q: L.speculate(
-            s, q, inp.k_cache, inp.v_cache, inp.table, pred, k, part, stream=st)))
-    kstar = L.choose_budget(n_grid, t_sel, k_grid, t_spec, float(N0), 2)
-    kstar_fused = L.choose_budget(n_grid, t_topk, k_grid, t_spec, float(N0), 2)
-    fit = float(np.polyval(np.polyfit(n_grid, t_sel, 2), N0))
-    fit_topk = float(np.polyval(np.polyfit(n_grid, t_topk, 2), N0))
-    return {"workload": w.name, "n_target": N0, "n_grid": n_grid,
-            "t_sel_us": [round(x, 2) for x in t_sel], "t_sel_fit_us": round(fit, 2),
-            "t_select_launch_us": [round(x, 2) for x in t_topk], "t_select_launch_fit_us": round(fit_topk, 2),
-            "kspec_grid": k_grid, "t_spec_us": [round(x, 2) for x in t_spec],
-            "kspec_star_two_stream": kstar, "kspec_star_fused": kstar_fused}
+    shape = L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, w.n_blocks, dt,
+                         w.scale, ctx_len=w.ctx if w.ctx % w.block_size else 0, sink_blocks=w.sink_blocks,
+                         local_blocks=w.local_blocks,
+                         scorer=L.SCORER_MEAN if w.scorer == "mean" else L.SCORER_QUEST)
+    k_grid = P.default_k_grid(w.top_k, w.n_blocks, w.k_spec)
+    qs = qs or [inp.q[t].contiguous() for t in range(w.steps)]
+    two = P.two_stream_tables(shape, w.top_k, qs[1 % len(qs)], inp.k_cache, inp.v_cache, inp.table, k_grid=k_grid,
+                              seed=w.seed)
+    fused = P.fused_step_table(shape, w.top_k, w.alpha, kvs or [(inp.k_cache, inp.v_cache)], inp.table, qs, k_grid,
+                               steps=steps)
+    torch.cuda.synchronize(dev)
+    r2 = lambda xs: [round(x, 2) for x in xs]
+    return {"workload": w.name, "n_target": w.n_blocks, "kspec_grid": k_grid,
+            "two_stream": {"n_grid": two["n_grid"], "t_sel_us": r2(two["t_sel_us"]),
+                           "t_sel_fit_us": round(two["t_sel_fit_us"], 2), "t_spec_us": r2(two["t_spec_us"]),
+                           "kspec_star": two["kspec_star"]},
+            "fused": {"t_step_us": r2(fused["t_step_us"]), "kspec_star": fused["kspec_star"]},
+            "kspec_star_two_stream": two["kspec_star"], "kspec_star_fused": fused["kspec_star"]}
 
 
 def source_digest() -> str:

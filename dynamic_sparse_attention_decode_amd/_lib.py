@@ -23,7 +23,7 @@ EXPORTS = ["prr_build_summaries", "prr_append_kv", "prr_score_select", "prr_ema_
            "prr_score", "prr_select_speculate", "prr_score_speculate", "prr_select_repair",
            "prr_partials_bytes", "prr_workspace_bytes", "prr_step_ctx_create", "prr_step_ctx_destroy",
            "prr_step_ctx_set_delays",
-           "prr_decode_step", "prr_decode_step_noalloc", "prr_choose_budget", "prr_trace_create", "prr_trace_destroy", "prr_trace_enable",
+           "prr_decode_step", "prr_decode_step_noalloc", "prr_choose_budget", "prr_choose_budget_fused", "prr_trace_create", "prr_trace_destroy", "prr_trace_enable",
            "prr_trace_read", "prr_flush_write", "prr_stream_read", "prr_status_string", "prr_last_error",
            "prr_version"]
 
@@ -130,6 +130,7 @@ def lib():
         "prr_choose_budget": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), i32,
                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), i32,
                                     ctypes.c_double, i32]),
+        "prr_choose_budget_fused": (i32, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), i32]),
         "prr_trace_create": (i32, [ctypes.POINTER(vp), i32]),
         "prr_trace_destroy": (None, [vp]),
         "prr_trace_enable": (i32, [vp, ctypes.c_uint32]),
@@ -305,6 +306,18 @@ def decode_step_noalloc(ctx, shape: Shape, args: StepArgs, mode: int, join: bool
 
 
 SCRATCH_MAX_BYTES = 32 << 20   # PRR_SCRATCH_MAX_BYTES in include/prr.h
+
+
+def choose_budget_fused(kspec_grid, t_step) -> int:
+    """The fused step's budget from measured step times at each grid budget (the grid holds 0)."""
+    D = ctypes.c_double
+    if len(kspec_grid) != len(t_step):
+        raise PRRError("choose_budget_fused: kspec_grid and t_step differ in length")
+    r = lib().prr_choose_budget_fused((D * len(kspec_grid))(*kspec_grid), (D * len(t_step))(*t_step),
+                                      len(kspec_grid))
+    if r < 0:
+        raise PRRError("choose_budget_fused: invalid arguments (the grid must hold 0; times must be finite)")
+    return r
 
 
 def choose_budget(n_grid, t_sel, kspec_grid, t_spec, n_target: float, degree: int = 2) -> int:

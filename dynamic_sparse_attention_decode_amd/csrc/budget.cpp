@@ -72,3 +72,21 @@ extern "C" int32_t prr_choose_budget(const double* n_grid, const double* t_sel, 
     if (t_spec[i] <= t_target && kspec_grid[i] > best) best = (int32_t)kspec_grid[i];
   return best;
 }
+
+// The fused single-stream step co-schedules the speculation with the selection launch, so speculation is off the
+// critical path exactly when the step with it is no slower than the step without it: the budget is the largest
+// profiled K' whose measured step time is at most that of K' = 0 (which the grid must hold).
+extern "C" int32_t prr_choose_budget_fused(const double* kspec_grid, const double* t_step, int32_t n_pts) {
+  if (!kspec_grid || !t_step || n_pts < 1) return -1;
+  int zero = -1;
+  for (int i = 0; i < n_pts; ++i) {
+    if (!(kspec_grid[i] >= 0.0) || !isfinite(t_step[i])) return -1;
+    if (kspec_grid[i] == 0.0 && zero < 0) zero = i;
+  }
+  if (zero < 0) return -1;
+  const double t0 = t_step[zero];
+  int32_t best = 0;
+  for (int i = 0; i < n_pts; ++i)
+    if (t_step[i] <= t0 && kspec_grid[i] > best) best = (int32_t)kspec_grid[i];
+  return best;
+}

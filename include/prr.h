@@ -304,6 +304,14 @@ prr_status prr_decode_step_noalloc(prr_step_ctx* ctx, const prr_shape* shape, co
 int32_t prr_choose_budget(const double* n_grid, const double* t_sel, int32_t n_pts_sel, const double* kspec_grid,
                           const double* t_spec, int32_t n_pts_spec, double n_target, int32_t poly_degree);
 
+/* Profiling-guided budget of the fused single-stream step (PRR_MODE_FUSED). There the speculation shares the
+ * selection launch, so its cost (a longer launch) and its saving (fewer missed blocks to repair) show only in the
+ * step's own time: t_step[i] is the measured time of a decode step at budget kspec_grid[i], the grid holding 0 (the
+ * step without speculation). Returns the largest kspec_grid[i] with t_step[i] <= the time at 0, i.e. the largest
+ * budget that keeps speculation off the step's critical path; -1 on invalid arguments (null arrays, n_pts < 1, no
+ * zero entry, a negative budget or a non-finite time). Host-only; safe without a GPU. */
+int32_t prr_choose_budget_fused(const double* kspec_grid, const double* t_step, int32_t n_pts);
+
 /* ---- kernel tracing ------------------------------------------------------------------------------------------ */
 /* Per-kernel launch timing with HIP events recorded on the stream each kernel is launched on, for measuring the
  * achieved bandwidth of one kernel inside a running decode loop. A trace holds `capacity` event pairs per kernel

@@ -191,6 +191,25 @@ def test_budget_chooser_matches_oracle_and_closed_forms():
                 assert abs(tp[ks.index(k)] - tt) < 1e-9 * max(1, abs(tt))
 
 
+def test_fused_budget_chooser_matches_oracle():
+    ks = [0, 32, 64, 128, 192]
+    assert L.choose_budget_fused(ks, [20.0, 19.0, 19.5, 20.0, 21.0]) == 128
+    assert L.choose_budget_fused(ks, [20.0, 20.1, 21.0, 22.0, 25.0]) == 0
+    import numpy as np
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        n = int(rng.integers(1, 9))
+        grid = sorted(set([0] + [int(x) for x in rng.integers(1, 512, size=n)]))
+        rng.shuffle(grid)
+        t = [float(x) for x in np.round(rng.uniform(10, 20, size=len(grid)), 1)]   # rounded: exact ties occur
+        assert L.choose_budget_fused(grid, t) == O.choose_budget_fused(grid, t), (grid, t)
+    lib = L.lib()
+    D = ctypes.c_double
+    assert lib.prr_choose_budget_fused((D * 2)(32, 64), (D * 2)(1.0, 2.0), 2) == -1            # no zero entry
+    assert lib.prr_choose_budget_fused((D * 2)(0, 64), (D * 2)(1.0, float("nan")), 2) == -1     # non-finite time
+    assert lib.prr_choose_budget_fused(None, None, 0) == -1
+
+
 def test_struct_layouts_match_the_header(tmp_path):
     """The ctypes mirrors of prr_shape, prr_budget and prr_step_args have the C header's size and field offsets
     (a C program built with the host compiler against include/prr.h prints them)."""

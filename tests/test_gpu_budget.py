@@ -275,3 +275,35 @@ def test_budget_edge_parameters(policy):
         for r in range(rows):
             ref = _expected_row(policy, s32[r], e_gpu[r], int(m[r]), K, cap, k_min, beta, c, 0, 0)
             assert np.array_equal(got[r], ref), (K, cap, r, got[r][:12], ref[:12])
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_32k", "million_token"])
+def test_budget_chooser_on_profiled_tables(name):
+    """The profiling-guided budget on tables measured here (PRR abstract; PRR summary page, Limitations): the
+    library's two choosers give the oracle's K'* on the same measured tables (the two-stream rule with its off-grid
+    polynomial fit, and the fused step's rule), and the fused K'* is a budget whose measured step is no slower than
+    the step without speculation while every larger grid budget is slower."""
+    from dynamic_sparse_attention_decode_amd import profiling as P
+    w = small(name)
+    print(f"[case] budget profile {name} N={w.n_blocks} K={w.top_k}", flush=True)
+    inp = gap_inputs(w)
+    s = shape_of(w)
+    qs = [inp.q[t].contiguous() for t in range(w.steps)]
+    k_grid = P.default_k_grid(w.top_k, w.n_blocks, w.k_spec)
+    two = P.two_stream_tables(s, w.top_k, qs[1], inp.k_cache, inp.v_cache, inp.table, k_grid=k_grid, reps=20,
+                              seed=w.seed)
+    fused = P.fused_step_table(s, w.top_k, w.alpha, [(inp.k_cache, inp.v_cache)], inp.table, qs, k_grid, steps=8,
+                               warmup=3)
+    print(f"[result] {name}: t_sel {np.round(two['t_sel_us'], 2)} t_spec {np.round(two['t_spec_us'], 2)} "
+          f"t_step {np.round(fused['t_step_us'], 2)} K'* two-stream {two['kspec_star']} fused {fused['kspec_star']}")
+    assert all(t > 0 for t in two["t_sel_us"]) and all(t > 0 for t in fused["t_step_us"])
+    ref = O.choose_budget(two["n_grid"], two["t_sel_us"], k_grid, two["t_spec_us"], float(w.n_blocks), 2)
+    if two["kspec_star"] != ref:   # only a near-tie between the fitted selection time and a table entry may differ
+        tt = np.polyval(np.polyfit(two["n_grid"], two["t_sel_us"], 2), w.n_blocks)
+        k = max(two["kspec_star"], ref)
+        assert abs(two["t_spec_us"][k_grid.index(k)] - tt) < 1e-9 * max(1.0, abs(tt)), (two["kspec_star"], ref)
+    assert fused["kspec_star"] == O.choose_budget_fused(k_grid, fused["t_step_us"])
+    t0 = fused["t_step_us"][k_grid.index(0)]
+    ks = fused["kspec_star"]
+    assert fused["t_step_us"][k_grid.index(ks)] <= t0
+    assert all(t > t0 for k, t in zip(k_grid, fused["t_step_us"]) if k > ks)
