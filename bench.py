@@ -28,7 +28,8 @@ HIP_KERNELS = {("prr_fused", "score"): "score_kernel (with the EMA update)",
                ("prr_fused", "select_topk"): "select_spec_kernel or select_missed_kernel (true top-K, next top-K', "
                                              "speculation over P_t; the latter also the missed blocks)",
                ("prr_fused", "repair"): "repair_kernel + finalize_kernel",
-               ("prr_fused", "finalize"): "merge_hits_kernel",
+               ("prr_fused", "finalize"): "merge_hits_kernel or finalize_kernel",
+               ("prr_fused", "speculate"): "speculate_kernel",
                ("serialized", "repair"): "repair_kernel + finalize_kernel",
                ("prr_1stream", "repair"): "repair_kernel + finalize_kernel",
                ("prr_2stream", "repair"): "repair_kernel + finalize_kernel"}
@@ -185,7 +186,11 @@ def main():
         """Algorithmic bytes per launch of each traced kernel in `mode`."""
         spec = rows * mean_pred * blk_kv
         rep = rows * (w.top_k if mode.startswith("serialized") else mean_missed) * blk_kv
-        if mode == "prr_fused" and (rows >= 128 or w.top_k <= 32):
+        if mode == "prr_fused" and rows >= 128:
+            # speculation over P_t in its own launch; scores with the EMA update; the selection launch (T and
+            # P_{t+1}); the spread-out repair (its merge launch traced as "finalize")
+            return {"speculate": spec, "score": summ_b + 3 * row_f32, "select_topk": 2 * row_f32, "repair": rep}
+        if mode == "prr_fused" and w.top_k <= 32:
             # scoring also updates the EMA; the selection launch reads scores and EMA, speculates over P_t and attends
             # the missed blocks; the merge launch (traced as "finalize") only reads partial records
             return {"score": summ_b + 3 * row_f32, "select_topk": 2 * row_f32 + spec + rep}
@@ -269,6 +274,7 @@ def main():
                 calls.append(lambda lay=lay, q=q, e=e, par=par: L.score(
                     shape, q, lay.summaries, lay.scores[par], e, w.alpha, False, stream=streams[0]))
             elif kernel == "select_topk" and mode == "prr_fused" and "repair" in alg:   # the select_spec launch
+                kc = 0 if "speculate" in alg else kc   # many rows: the speculation has its own launch
                 calls.append(lambda lay=lay, q=q, par=par, nxt=nxt, kc=kc: L.select_speculate(
                     shape, lay.scores[par], K, lay.sel_idx, lay.ema, lay.k_spec, lay.pred[nxt], q, lay.k_cache,
                     lay.v_cache, lay.table, lay.pred[par], kc, lay.partials[par], workspace=lay.workspace,
@@ -332,7 +338,10 @@ def main():
     # selected-KV attention path: speculation + repair in the PRR modes, attend(T) (the repair launch with an empty
     # prediction) in the serialized mode; the fused mode speculates inside the selection launch, so its path time is
     # the whole selection launch
-    if a.mode == "prr_fused" and "repair" not in alg:   # speculation and missed blocks in the selection launch
+    if a.mode == "prr_fused" and "speculate" in alg:   # speculation in its own launch, then the repair
+        attn_us = (per_kernel.get("speculate", 0.0) + per_kernel.get("repair", 0.0) + per_kernel.get("finalize", 0.0))
+        attn_bytes = alg["speculate"] + alg["repair"]
+    elif a.mode == "prr_fused" and "repair" not in alg:   # speculation and missed blocks in the selection launch
         attn_us = per_kernel.get("select_topk", 0.0) + per_kernel.get("finalize", 0.0)
         attn_bytes = alg["select_topk"] - 2 * row_f32
     elif a.mode == "prr_fused":   # speculation in the selection launch, then the repair launch

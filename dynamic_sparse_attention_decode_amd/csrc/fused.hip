@@ -203,6 +203,8 @@ prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, in
   const bool split = cand_t && cand_p && (bp.policy != 2 || cand_u) && topk_split_on(s.n_blocks, k, kSelSpecSeg) &&
                      (kp_next == 0 || (topk_split_on(s.n_blocks, kp_next, kSelSpecSeg) &&
                                        topk_split_on(s.n_blocks, ke, kSelSpecSeg)));
+  // nothing to speculate: the true and predicted sets in one launch of top-K workgroups only
+  if (k_spec == 0 && !split) return launch_topk_pair(s, scores, k, sel, ema, kp_next, pred_next, bp, stream);
   if (bp.policy != 0 && kp_next > 0 && !split && s.n_blocks > 16 * kSelSpecThreads) {
     // budgeted rows this long take their own launch of 1024-thread workgroups, which reads the EMA as it stands
     const prr_status st = launch_select_spec(s, scores, k, sel, nullptr, 0, nullptr, q, kc, vc, table, pred, k_spec,

@@ -137,13 +137,16 @@ def test_select_speculate_budget(policy, n_blocks, with_ws, forced):
 
 @pytest.mark.parametrize("mode", ["prr_fused", "prr_1stream", "prr_2stream"])
 @pytest.mark.parametrize("policy", ["misses", "confidence"])
-@pytest.mark.parametrize("name", ["tiny_f32_4k", "llama3_8b_32k", "paged_b32_64k", "million_token"])
+@pytest.mark.parametrize("name", ["tiny_f32_4k", "llama3_8b_32k", "paged_b32_64k", "million_token", "paged_wide"])
 def test_decode_with_budget(name, policy, mode):
     """Whole decode runs with a budget: every step's selection and output against the oracle (the output is
     attention over the true set whatever was predicted), the missed count = |T minus the filled part of P_t|, and
     P_{t+1} equal to the oracle's budgeted prediction from the step's scores and EMA and the previous step's missed
     counts; the sets' sizes vary by row within [k_min, k_spec]."""
-    w = small(name)
+    if name == "paged_wide":   # 136 rows: the fused step's selection splits T into hits and a missed list
+        w = small("paged_b32_64k").replace(batch=17, ctx=16 * 70 - 3, top_k=12, k_spec=(12,), steps=5)
+    else:
+        w = small(name)
     kp = min(w.n_blocks, max(max(w.k_spec), w.top_k + w.top_k // 2))   # room above K for the sizes to vary
     k_min = max(1, w.top_k // 2)
     cfg = {"policy": policy, "k_min": k_min, "beta": 0.5, "c": 0.3}
