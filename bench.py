@@ -238,6 +238,7 @@ def main():
             g.replay()
             torch.cuda.synchronize()
             us_ = (time.perf_counter() - t0) / (a.steps * len(ls)) * 1e6
+            del g   # a graph captured while tracing refers to the trace's events: release it before the trace
         durs = {}
         if tr:
             tr.disable()

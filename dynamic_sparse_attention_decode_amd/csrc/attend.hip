@@ -120,7 +120,8 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8
   const int b = (int)(rowid / Hkv), g = (int)(rowid % Hkv);
   const int32_t* srow = sel + rowid * top_k;
   const int32_t* prow = pred ? pred + rowid * k_spec : nullptr;
-  const float* part_row = partials ? partials + rowid * k_spec * (int64_t)RF : nullptr;
+  const uint8_t* part_row =
+      partials ? reinterpret_cast<const uint8_t*>(partials) + rowid * k_spec * W::kSpecRecBytes : nullptr;
 
   const bool pred_lds = k_spec <= kPredLds;
   int kneg = k_spec;
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8
         if (hit) { slot = c + __ffsll(hit) - 1; break; }
       }
       if (slot >= 0) {
-        st.merge_record(part_row + (int64_t)slot * RF);
+        st.merge_spec_record(part_row + (int64_t)slot * W::kSpecRecBytes);
       } else {
         if (lane == 0) s_mid[wave][nm] = n;
         ++nm;
@@ -286,14 +287,15 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_list_kernel(const 
 // out[b, g*G + h] = merge of the row's repair records and the speculated records of its hits, normalised: one
 // 256-thread workgroup per (row, head); the weights exp2(m_i - M) go to LDS, then 256 / (D/4) record groups
 // accumulate float4 slices of O with 8 loads in flight per thread. Records of blocks of P outside T are never read.
-template <int G, int D>
+template <int G, int D, int OB>
 __global__ __launch_bounds__(256) void finalize_list_kernel(const float* __restrict__ partials, int k_spec, SplitWs ws,
                                                             float* __restrict__ out, int Hq, int Hkv) {
-  constexpr int RF = rec_floats(G, D), ML = rec_ml(G);
+  constexpr int RF = rec_floats(G, D);
+  constexpr int64_t SRB = spec_rec_bytes(OB == 4 ? 0 : 1, G, D);   // speculation record bytes
   constexpr int S = D / 4, P = 256 / S, U = 8;
   constexpr int kMaxRec = kMaxRecords + kSplitMaxK;
   __shared__ float s_w[kMaxRec];
-  __shared__ const float* s_rec[kMaxRec];
+  __shared__ const uint8_t* s_rec[kMaxRec];
   __shared__ float s_red[2][4];
   __shared__ float4 s_acc[P][S];
   const int64_t r = blockIdx.x;
@@ -303,14 +305,14 @@ __global__ __launch_bounds__(256) void finalize_list_kernel(const float* __restr
   const int nh = ws.cnt[2 * r], nm = ws.cnt[2 * r + 1];
   const int nrep = (nm + 4 * ws.epw - 1) / (4 * ws.epw);   // repair records written
   const int n = nrep + nh;
-  const float* rep_row = ws.rec + r * ws.nrec * (int64_t)RF;
-  const float* part_row = partials ? partials + r * k_spec * (int64_t)RF : nullptr;
+  const uint8_t* rep_row = reinterpret_cast<const uint8_t*>(ws.rec + r * ws.nrec * (int64_t)RF);
+  const uint8_t* part_row = partials ? reinterpret_cast<const uint8_t*>(partials) + r * k_spec * SRB : nullptr;
   const int32_t* hrow = ws.hits + r * ws.Kp;
   float mx = -__builtin_huge_valf();
-  for (int i = t; i < n; i += 256) {
-    const float* rec = i < nrep ? rep_row + (int64_t)i * RF : part_row + (int64_t)hrow[i - nrep] * RF;
+  for (int i = t; i < n; i += 256) {   // records [0, nrep) are the repair's (fp32 O), the rest speculated hits
+    const uint8_t* rec = i < nrep ? rep_row + (int64_t)i * RF * 4 : part_row + (int64_t)hrow[i - nrep] * SRB;
     s_rec[i] = rec;
-    const float m = rec[h];
+    const float m = reinterpret_cast<const float*>(rec)[h];
     s_w[i] = m;
     mx = fmaxf(mx, m);
   }
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(256) void finalize_list_kernel(const float* __restr
   for (int i = t; i < n; i += 256) {
     const float w = exp2f(s_w[i] - M);
     s_w[i] = w;
-    ls += s_rec[i][G + h] * w;
+    ls += reinterpret_cast<const float*>(s_rec[i])[G + h] * w;
   }
   ls = wave_sum(ls);
   if (lane == 0) s_red[1][wave] = ls;
@@ -335,8 +337,7 @@ __global__ __launch_bounds__(256) void finalize_list_kernel(const float* __restr
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u * P;
-      o[u] = i < n ? *reinterpret_cast<const float4*>(s_rec[i] + ML + h * D + slot * 4)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      o[u] = i < n ? rec_o4<G, D>(s_rec[i], OB == 4 || i < nrep, h, slot) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -506,8 +507,8 @@ static void repair_list_launch(const prr_shape& s, const void* q, const void* kc
   trace_end(PRR_KERNEL_REPAIR, st);
   constexpr int D = 16 * Vec<DT>::n;
   trace_begin(PRR_KERNEL_FINALIZE, st);
-  finalize_list_kernel<G, D><<<dim3((unsigned)rows, (unsigned)G), dim3(256), 0, st>>>(partials, k_spec, ws, out,
-                                                                                      s.n_q_heads, s.n_kv_heads);
+  finalize_list_kernel<G, D, spec_o_bytes(DT)><<<dim3((unsigned)rows, (unsigned)G), dim3(256), 0, st>>>(
+      partials, k_spec, ws, out, s.n_q_heads, s.n_kv_heads);
   trace_end(PRR_KERNEL_FINALIZE, st);
 }
 

@@ -47,6 +47,7 @@ struct AttnWaveM {
   static_assert(DT != kF32, "matrix-core tile is for 16-bit storage");
   static constexpr bool kPipelined = G <= 4;   // two chunk buffers fit the register budget
   static constexpr int kRecBatch = G >= 8 ? 2 : 4;   // record loads in flight
+  static constexpr int64_t kSpecRecBytes = spec_rec_bytes(kBF16, G, D);   // speculation records: O in bf16
 
   uint4 qb[4];        // B operand: query head l%16 (zero beyond G), dims 8*(l/16) + 32*kk
   float qscale;
@@ -242,6 +243,56 @@ struct AttnWaveM {
     Rec r;
     load_record(r, rec);
     apply_record(r);
+  }
+
+  // A speculation record (fp16 O / l, m and l in fp32) as one lane needs it: O = (O / l) * l.
+  __device__ void load_spec_record(Rec& r, const uint8_t* __restrict__ rec) const {
+    const float* ml = reinterpret_cast<const float*>(rec);
+    const uint16_t* o = reinterpret_cast<const uint16_t*>(rec + rec_ml(G) * 4);
+#pragma unroll
+    for (int h = 0; h < G; ++h) { r.m[h] = ml[h]; r.l[h] = ml[G + h]; }
+#pragma unroll
+    for (int k = 0; k < (G + 3) / 4; ++k) {
+      const int h = row + 4 * k;
+      const float lh = h < G ? ml[G + h] : 0.f;
+#pragma unroll
+      for (int v = 0; v < VE / 4; ++v) {
+        const float4 t = h < G ? unpack_f16x4(*reinterpret_cast<const uint2*>(o + h * D + col * VE + 4 * v))
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        r.o[k][v] = make_float4(t.x * lh, t.y * lh, t.z * lh, t.w * lh);
+      }
+    }
+  }
+
+  __device__ void merge_spec_record(const uint8_t* __restrict__ rec) {
+    Rec r;
+    load_spec_record(r, rec);
+    apply_record(r);
+  }
+
+  // Write the folded state as a speculation record: m and l in fp32, O / l in fp16 (rounded to nearest even; l >= 1,
+  // since the block's largest logit contributes 2^0).
+  __device__ void write_spec_record(uint8_t* __restrict__ rec, const float* folded) const {
+    store_ml(reinterpret_cast<float*>(rec));
+    uint16_t* o = reinterpret_cast<uint16_t*>(rec + rec_ml(G) * 4);
+    if constexpr (NK % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < NK; i += 4) {
+        const int f = row * NK + i;
+        const int h = f / VE, e = f % VE;
+        const float il = 1.f / __shfl(l_l, h);   // lane h (row 0, column h) holds head h's l
+        *reinterpret_cast<uint2*>(o + h * D + col * VE + e) =
+            make_uint2(pack_f16x2(folded[i] * il, folded[i + 1] * il), pack_f16x2(folded[i + 2] * il,
+                                                                                 folded[i + 3] * il));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const int f = row * NK + i;
+        const float il = 1.f / __shfl(l_l, f / VE);
+        o[(f / VE) * D + col * VE + (f % VE)] = (uint16_t)(pack_f16x2(folded[i] * il, 0.f) & 0xffffu);
+      }
+    }
   }
 
   // Fold the 4 rows: l_l becomes the total of head col; out[i] holds flat accumulator f = row*NK + i.

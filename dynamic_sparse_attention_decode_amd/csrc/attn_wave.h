@@ -29,6 +29,7 @@ struct AttnWave {
   static constexpr int ML = rec_ml(G);  // offset of O in a record (floats)
 
   static constexpr bool kPipelined = G <= 4;   // two chunk buffers fit the register budget
+  static constexpr int64_t kSpecRecBytes = spec_rec_bytes(kF32, G, 16 * Vec<DT>::n);   // fp32 records
   static constexpr int kRecBatch = G >= 8 ? 2 : 4;   // record loads in flight
 
   float q[G][VE];
@@ -200,6 +201,11 @@ struct AttnWave {
     apply_record(r);
   }
 
+  // Speculation records of fp32 storage are fp32 records.
+  __device__ void merge_spec_record(const uint8_t* __restrict__ rec) {
+    merge_record(reinterpret_cast<const float*>(rec));
+  }
+
   // Fold the 4 rows: l becomes the wave total (uniform); out[i] holds flat accumulator f = row*NK + i.
   __device__ void fold(float* out) {
 #pragma unroll
@@ -220,6 +226,10 @@ struct AttnWave {
 #pragma unroll
       for (int h = 0; h < G; ++h) { dst[h] = m[h]; dst[G + h] = l[h]; }
     }
+  }
+
+  __device__ void write_spec_record(uint8_t* __restrict__ rec, const float* folded) {
+    write_record(reinterpret_cast<float*>(rec), folded);
   }
 
   // Write the folded state as a record.
@@ -356,7 +366,8 @@ __device__ inline void speculate_slots(int64_t rowid, int j0, int j1, int lane, 
       [&](int i) {
         float folded[W::NK];
         st.fold(folded);
-        st.write_record(partials + (rowid * k_spec + j0 + i) * rec_floats(G, W::D), folded);
+        st.write_spec_record(reinterpret_cast<uint8_t*>(partials) + (rowid * k_spec + j0 + i) * W::kSpecRecBytes,
+                             folded);
         st.init(lane);
       },
       kc, vc, table + (int64_t)b * pps, bs, page, Hkv, g, N, last_len);
@@ -381,7 +392,7 @@ __device__ inline void speculate_slot(int64_t s, int lane, const uint8_t* __rest
   st.block(kc, vc, table + (int64_t)b * pps, n, bs, block_len(n, N, bs, last_len), page, Hkv, g);
   float folded[W::NK];
   st.fold(folded);
-  st.write_record(partials + s * rec_floats(G, W::D), folded);
+  st.write_spec_record(reinterpret_cast<uint8_t*>(partials) + s * W::kSpecRecBytes, folded);
 }
 
 }  // namespace prr

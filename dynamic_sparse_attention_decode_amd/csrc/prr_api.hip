@@ -454,8 +454,8 @@ prr_status prr_select_repair(const prr_shape* shape, const float* scores, int32_
 size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec) {
   if (check_shape(shape) != PRR_OK || k_spec <= 0) return 0;
   const int G = shape->n_q_heads / shape->n_kv_heads;
-  return (size_t)shape->batch * shape->n_kv_heads * (size_t)k_spec * (size_t)rec_floats(G, shape->head_dim) *
-         sizeof(float);
+  return (size_t)shape->batch * shape->n_kv_heads * (size_t)k_spec *
+         (size_t)spec_rec_bytes(shape->dtype, G, shape->head_dim);
 }
 
 size_t prr_workspace_bytes(const prr_shape* shape, int32_t top_k) {

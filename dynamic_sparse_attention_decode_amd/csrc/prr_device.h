@@ -75,6 +75,18 @@ template <> struct Vec<kF16> {
   }
 };
 
+// Two fp32 values as packed fp16 (the conversion rounds to nearest even), and four packed fp16 widened to fp32.
+__device__ inline uint32_t pack_f16x2(float lo, float hi) {
+  half2_t h;
+  h[0] = (_Float16)lo;
+  h[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ inline float4 unpack_f16x4(uint2 u) {
+  const half2_t a = __builtin_bit_cast(half2_t, u.x), b = __builtin_bit_cast(half2_t, u.y);
+  return make_float4((float)a[0], (float)a[1], (float)b[0], (float)b[1]);
+}
+
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // 16-byte load of data that one step reads once (block summaries, the KV of selected and predicted blocks): a

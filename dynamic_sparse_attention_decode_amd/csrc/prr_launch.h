@@ -16,6 +16,25 @@ prr_status check_launch(const char* what);
 // floats, then O[G][D]. Records are 16-byte aligned.
 __host__ __device__ constexpr int rec_ml(int G) { return (2 * G + 3) & ~3; }
 __host__ __device__ constexpr int64_t rec_floats(int G, int D) { return (int64_t)rec_ml(G) + (int64_t)G * D; }
+// A speculation record (the partials buffer): m[G] and l[G] in fp32, zero padding to a multiple of 4 floats, then
+// O[G][D]: for fp32 storage (dt 0) O itself in fp32; for 16-bit storage (dt 1, 2) O / l (the block's attention
+// output, a weighted average of its values) in fp16, which the reader multiplies back by l. 16-byte aligned. Records
+// inside the workspace keep O in fp32.
+__host__ __device__ constexpr int spec_o_bytes(int dt) { return dt == 0 ? 4 : 2; }
+__host__ __device__ constexpr int64_t spec_rec_bytes(int dt, int G, int D) {
+  return (int64_t)rec_ml(G) * 4 + (int64_t)G * D * spec_o_bytes(dt);
+}
+// Four consecutive O values (dims 4 * slot .. 4 * slot + 3 of head h) of a record: an fp32 record's O when f32, else
+// a compact speculation record's fp16 O / l times its l.
+template <int G, int D>
+__device__ inline float4 rec_o4(const uint8_t* __restrict__ rec, bool f32, int h, int slot) {
+  constexpr int MLB = rec_ml(G) * 4;
+  const int64_t e = (int64_t)h * D + slot * 4;
+  if (f32) return *reinterpret_cast<const float4*>(rec + MLB + e * 4);
+  const float l = reinterpret_cast<const float*>(rec)[G + h];
+  const float4 v = unpack_f16x4(*reinterpret_cast<const uint2*>(rec + MLB + e * 2));
+  return make_float4(v.x * l, v.y * l, v.z * l, v.w * l);
+}
 
 // Kernel tracing hooks: record the armed trace's start/end events around a launch of kernel `kid` on `stream`.
 void trace_begin(int kid, hipStream_t stream);

@@ -244,13 +244,14 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
 // out[b, g*G + h] = merge of the row's missed-block record and the speculated records of its hits, normalised. One
 // 256-thread workgroup per (row, head): the weights exp2(m_i - M) go to LDS, then 256 / (D/4) record groups
 // accumulate float4 slices of O with 8 loads in flight per thread.
-template <int G, int D>
+template <int G, int D, int OB>
 __global__ __launch_bounds__(256) void merge_hits_kernel(const float* __restrict__ partials, int k_spec, MissedWs ws,
                                                          float* __restrict__ out, int Hq, int Hkv) {
-  constexpr int RF = rec_floats(G, D), ML = rec_ml(G);
+  constexpr int RF = rec_floats(G, D);
+  constexpr int64_t SRB = spec_rec_bytes(OB == 4 ? 0 : 1, G, D);   // speculation record bytes
   constexpr int S = D / 4, P = 256 / S, U = 8;
   __shared__ float s_w[kSRMaxK + 1];
-  __shared__ const float* s_rec[kSRMaxK + 1];
+  __shared__ const uint8_t* s_rec[kSRMaxK + 1];
   __shared__ float s_red[2][4];
   __shared__ float4 s_acc[P][S];
   const int64_t r = blockIdx.x;
@@ -259,13 +260,13 @@ __global__ __launch_bounds__(256) void merge_hits_kernel(const float* __restrict
   const int b = (int)(r / Hkv), g = (int)(r % Hkv);
   const int nh = ws.cnt[r];
   const int n = nh + 1;   // record 0: the missed blocks; records 1..nh: speculated hits
-  const float* mrec = ws.mrec + r * (int64_t)RF;
-  const float* part_row = partials ? partials + r * k_spec * (int64_t)RF : nullptr;
+  const uint8_t* mrec = reinterpret_cast<const uint8_t*>(ws.mrec + r * (int64_t)RF);
+  const uint8_t* part_row = partials ? reinterpret_cast<const uint8_t*>(partials) + r * k_spec * SRB : nullptr;
   float mx = -__builtin_huge_valf();
-  for (int i = t; i < n; i += 256) {
-    const float* rec = i == 0 ? mrec : part_row + (int64_t)ws.hits[r * ws.Kp + i - 1] * RF;
+  for (int i = t; i < n; i += 256) {   // record 0 (fp32 O) is the missed blocks', the rest speculated hits
+    const uint8_t* rec = i == 0 ? mrec : part_row + (int64_t)ws.hits[r * ws.Kp + i - 1] * SRB;
     s_rec[i] = rec;
-    const float m = rec[h];
+    const float m = reinterpret_cast<const float*>(rec)[h];
     s_w[i] = m;
     mx = fmaxf(mx, m);
   }
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(256) void merge_hits_kernel(const float* __restrict
   for (int i = t; i < n; i += 256) {
     const float w = exp2f(s_w[i] - M);
     s_w[i] = w;
-    ls += s_rec[i][G + h] * w;
+    ls += reinterpret_cast<const float*>(s_rec[i])[G + h] * w;
   }
   ls = wave_sum(ls);
   if (lane == 0) s_red[1][wave] = ls;
@@ -290,8 +291,7 @@ __global__ __launch_bounds__(256) void merge_hits_kernel(const float* __restrict
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u * P;
-      o[u] = i < n ? *reinterpret_cast<const float4*>(s_rec[i] + ML + h * D + slot * 4)
-                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      o[u] = i < n ? rec_o4<G, D>(s_rec[i], OB == 4 || i == 0, h, slot) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -404,8 +404,8 @@ static void select_missed_launch(const prr_shape& s, const float* scores, int K,
 #undef PRR_SELMISS
   trace_end(PRR_KERNEL_SELECT_TOPK, st);
   trace_begin(PRR_KERNEL_FINALIZE, st);
-  merge_hits_kernel<G, D><<<dim3((unsigned)rows, (unsigned)G), dim3(256), 0, st>>>(partials, k_spec, ws, out,
-                                                                                   s.n_q_heads, s.n_kv_heads);
+  merge_hits_kernel<G, D, spec_o_bytes(DT)><<<dim3((unsigned)rows, (unsigned)G), dim3(256), 0, st>>>(
+      partials, k_spec, ws, out, s.n_q_heads, s.n_kv_heads);
   trace_end(PRR_KERNEL_FINALIZE, st);
 }
 

@@ -35,10 +35,13 @@
  *  ema        f32 [B, Hkv, N]
  *  sel_idx    int32 [B, Hkv, K]   ascending block ids of the true top-K set
  *  pred_idx   int32 [B, Hkv, K']  ascending block ids of the predicted set
- *  partials   f32 buffer of prr_partials_bytes(): one record per (b, kv head, predicted slot), layout
- *             [B, Hkv, K'] x {m[G], l[G], zero padding to a multiple of 4 floats, O[G][D]}; m is the block's
- *             largest logit in log2 units (softmax_scale * q.k * log2 e), l = sum of 2^(z - m), O = sum of
- *             2^(z - m) v (unnormalised); records are 16-byte aligned
+ *  partials   buffer of prr_partials_bytes() (passed as float*): one record per (b, kv head, predicted slot),
+ *             layout [B, Hkv, K'] x {m[G], l[G] fp32, zero padding to a multiple of 4 floats, O[G][D]}; m is the
+ *             block's largest logit in log2 units (softmax_scale * q.k * log2 e), l = sum of 2^(z - m), O = sum of
+ *             2^(z - m) v (unnormalised); O is stored in fp32 for fp32 storage, and as O / l (the block's own
+ *             attention output, a weighted average of its values) in fp16, rounded to nearest even, for bf16 and
+ *             fp16 storage (values beyond the fp16 range, |v| > 65504 in a bf16 cache, are not supported there);
+ *             records are 16-byte aligned
  *  out        f32 [B, Hq, D]      softmax attention over the tokens of the true top-K blocks
  *  n_missed   int32 [B, Hkv]      |T \ P| of the last repair
  */
@@ -318,7 +321,8 @@ int32_t prr_choose_budget_fused(const double* kspec_grid, const double* t_step, 
  * id; while enabled (process-wide, one trace at a time) every launch of a kernel in `kernel_mask` (bit i = kernel
  * id i) records an event immediately before and after it, until that kernel's pool is full. Reading synchronises
  * on the events. Under stream capture the records become external event nodes of the graph (each replay records
- * them again), so a captured decode loop can be traced too. */
+ * them again), so a captured decode loop can be traced too; such a graph refers to the trace's events, so destroy
+ * every graph captured while a trace was enabled before destroying that trace. */
 typedef enum {
   PRR_KERNEL_SUMMARIES = 0, PRR_KERNEL_SCORE = 1, PRR_KERNEL_SELECT_TOPK = 2, PRR_KERNEL_EMA_TOPK = 3,
   PRR_KERNEL_SPECULATE = 4, PRR_KERNEL_REPAIR = 5, PRR_KERNEL_FINALIZE = 6, PRR_KERNEL_COUNT = 7

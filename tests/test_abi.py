@@ -156,14 +156,18 @@ def test_argument_validation_without_launch():
 
 
 def test_buffer_sizes():
+    """Speculation records: m[G] and l[G] fp32 padded to 16 bytes, then O[G][D] in bf16 for 16-bit storage and in
+    fp32 for fp32 storage."""
     s = _shape()
     G, D = 4, 128
-    rec = (2 * G + 3) // 4 * 4 + G * D
-    assert L.partials_bytes(s, 160) == 1 * 8 * 160 * rec * 4
+    ml = (2 * G + 3) // 4 * 4
+    assert L.partials_bytes(s, 160) == 1 * 8 * 160 * (ml * 4 + G * D * 2)
     assert L.partials_bytes(s, 0) == 0
     assert L.workspace_bytes(s, 128) > 0
-    s1 = _shape(n_q_heads=8, n_kv_heads=8)   # G = 1: records padded to 16 bytes
-    assert L.partials_bytes(s1, 3) == 8 * 3 * (4 + 128) * 4
+    s1 = _shape(n_q_heads=8, n_kv_heads=8)   # G = 1: m and l padded to 16 bytes
+    assert L.partials_bytes(s1, 3) == 8 * 3 * (16 + 128 * 2)
+    s2 = _shape(n_q_heads=4, n_kv_heads=1, head_dim=64, dtype=L.F32, block_size=32, page_size=32, n_blocks=128)
+    assert L.partials_bytes(s2, 16) == 16 * (ml * 4 + 4 * 64 * 4)
 
 
 def test_budget_chooser_matches_oracle_and_closed_forms():

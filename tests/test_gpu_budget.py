@@ -126,13 +126,19 @@ def test_select_speculate_budget(policy, n_blocks, with_ws, forced):
     for r in range(rows):
         ref = _expected_row(policy, s32[r], e32[r], int(m[r]), K, cap, 5, 0.7, 0.4, sink, local)
         assert np.array_equal(got_p[r], ref), (r, got_p[r][:12], ref[:12])
-    # the records: equal to the standalone speculation's where filled; untouched where empty
-    rf = ((2 * 4 + 3) & ~3) + 4 * 128   # a record: m[G], l[G], padding to 4 floats, O[G][D] (G = 4, D = 128)
-    a = part.cpu().numpy()[:rows * cap * rf].reshape(rows, cap, rf)
-    b = part_ref.cpu().numpy()[:rows * cap * rf].reshape(rows, cap, rf)
+    # the records (m[G], l[G] fp32 padded to 4 floats, then O / l [G][D] in fp16; G = 4, D = 128): equal to the
+    # standalone speculation's where filled (O / l within one fp16 rounding); untouched where empty
+    words = (8 * 4 + 4 * 128 * 2) // 4
+    a = part.cpu().numpy().view(np.uint32)[:rows * cap * words].reshape(rows, cap, words)
+    b = part_ref.cpu().numpy().view(np.uint32)[:rows * cap * words].reshape(rows, cap, words)
     filled = p_cur >= 0
-    assert np.allclose(a[filled], b[filled], rtol=1e-6, atol=1e-6)
-    assert np.all(a[~filled] == 12345.0) and np.all(b[~filled] == 12345.0)
+    ml_a, ml_b = a[filled][:, :8].view(np.float32), b[filled][:, :8].view(np.float32)
+    assert np.allclose(ml_a, ml_b, rtol=1e-6, atol=1e-6)
+    o_a = a[filled][:, 8:].copy().view(np.float16).astype(np.float64)
+    o_b = b[filled][:, 8:].copy().view(np.float16).astype(np.float64)
+    assert np.all(np.abs(o_a - o_b) <= 2.0 ** -10 * np.abs(o_b) + 1e-7)
+    fill = np.float32(12345.0).view(np.uint32)
+    assert np.all(a[~filled] == fill) and np.all(b[~filled] == fill)
 
 
 @pytest.mark.parametrize("mode", ["prr_fused", "prr_1stream", "prr_2stream"])

@@ -381,3 +381,29 @@ def test_degenerate_contexts(ctx, bs, page, k, kp, mode):
     inp = gap_inputs(w)
     ov = OracleView(inp)
     run_layer(w, inp, kp if mode != "serialized" else 0, mode, ov=ov)
+
+
+def test_kernel_trace_lifecycle():
+    """The per-kernel trace as the benchmark uses it: enabled around eager steps, read (one positive duration per
+    traced launch), disabled and destroyed, three traces in a row; steps after the last one is destroyed run
+    untraced (the library drops a destroyed trace)."""
+    w = small("llama3_8b_32k")
+    inp = gap_inputs(w)
+    lay = PRRLayer(shape_of(w), w.top_k, w.k_spec[0], w.alpha, mode="prr_1stream")
+    lay.build(inp.k_cache, inp.v_cache, inp.table)
+    qs = [inp.q[t].contiguous() for t in range(w.steps)]
+    for rep in range(3):
+        tr = L.Trace(16)
+        tr.enable(["score", "repair", "speculate"])
+        for t in range(4):
+            lay.step(qs[t])
+        torch.cuda.synchronize()
+        tr.disable()
+        for k, n in (("score", 4), ("repair", 4), ("speculate", 3)):   # step 0 of each run has nothing predicted
+            d = tr.read(k)
+            assert len(d) == n and all(x > 0 for x in d), (rep, k, d)
+        tr.close()
+        lay.reset()
+    lay.step(qs[0])
+    torch.cuda.synchronize()
+    lay.close()
