@@ -182,11 +182,15 @@ def main():
     mean_pred = float(np.mean(pred_size)) if pred_size else float(kspec)   # filled slots of a predicted set
     prr_mode = not a.mode.startswith("serialized")
 
+    # the fused step's many-row path (speculation in its own launch, the split into hits and missed lists) serves
+    # batches whose rows alone fill the chip
+    many_row = rows >= 128
+
     def alg_bytes(mode):
         """Algorithmic bytes per launch of each traced kernel in `mode`."""
         spec = rows * mean_pred * blk_kv
         rep = rows * (w.top_k if mode.startswith("serialized") else mean_missed) * blk_kv
-        if mode == "prr_fused" and rows >= 128:
+        if mode == "prr_fused" and many_row:
             # speculation over P_t in its own launch; scores with the EMA update; the selection launch (T and
             # P_{t+1}); the spread-out repair (its merge launch traced as "finalize")
             return {"speculate": spec, "score": summ_b + 3 * row_f32, "select_topk": 2 * row_f32, "repair": rep}
@@ -254,6 +258,36 @@ def main():
         for lay in ls:
             lay.close()
         return us_, durs
+
+    def step_percentiles(mode):
+        """Spread of the step time: the same warm-up and steps as measure(), each step (every layer once) captured as
+        a graph of its own, the graphs replayed in order, each between two HIP events on the stream it runs on.
+        Returns p10 / p50 / p90 of µs per layer-step (a graph launch per step adds its own start-up to each
+        sample, so p50 sits a little above the one-graph average)."""
+        ls = make_layers(mode)
+        run(ls, a.warmup)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(a.steps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=streams[0]):
+                for li, lay in enumerate(ls):
+                    lay.enqueue(qs[lay.t % w.steps], join=(li == len(ls) - 1))
+            graphs.append(g)
+        cur = torch.cuda.current_stream(dev)   # replay() launches a graph on the current stream
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in graphs]
+        for g, (e0, e1) in zip(graphs, ev):
+            e0.record(cur)
+            g.replay()
+            e1.record(cur)
+        torch.cuda.synchronize()
+        t = np.array([e0.elapsed_time(e1) * 1e3 / len(ls) for e0, e1 in ev])
+        del graphs
+        for lay in ls:
+            lay.close()
+        return {"p10": float(np.percentile(t, 10)), "p50": float(np.percentile(t, 50)),
+                "p90": float(np.percentile(t, 90)), "samples": len(t),
+                "how": "one graph per step (all layers), replayed in order between HIP events"}
 
     def isolated(mode, kernel):
         """Average duration (µs) of `kernel` alone: a HIP graph of a.steps x layers back-to-back launches of the one
@@ -394,6 +428,8 @@ def main():
         detail["budget_profile"] = budget_profile(w, inp, kvs, qs, steps=min(a.steps, 32))
     detail["attention_path_frac_of_measured"] = (detail["attention_path_GBps"] / read_gbs
                                                  if detail["attention_path_GBps"] else None)
+    if not a.eager:
+        detail["us_per_step_percentiles"] = step_percentiles(a.mode)
     if n_layers > 1:   # the same step with one layer only: its data stays in the Infinity Cache between steps
         detail["us_per_step_one_layer_cache_warm"] = measure(a.mode, n_kv=1)[0]
     if len(w.k_spec) > 1 and a.mode != "serialized" and not a.no_kspec_sweep:   # the workload sweeps its budget

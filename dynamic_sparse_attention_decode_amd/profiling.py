@@ -7,7 +7,8 @@ context lengths outside them. Two windows are profiled:
 * two-stream step (speculation on its own stream beside the selection): t_sel(N), the time of the whole selection
   (scores and top-K) on a grid of block counts N, and t_spec(K'), the time of the speculation launch alone on a grid
   of budgets; K'* = the largest K' with t_spec(K') <= t_sel at the layer's N (prr_choose_budget, a degree-2
-  least-squares polynomial in N off the grid; the grid leaves out the layer's own N so the fit is exercised).
+  least-squares polynomial in N off the grid; the grid leaves out the layer's own N so the fit is exercised, except
+  at the top-K kernels' largest N, where the fit would have to extrapolate).
 * fused single-stream step (speculation inside the selection launch): t_step(K'), the time of whole decode steps of
   the layer at each grid budget, predicted sets from the layer's own EMA; K'* = the largest K' whose step is no
   slower than the step without speculation (prr_choose_budget_fused).
@@ -45,9 +46,13 @@ def graph_us(fn, reps: int, device) -> float:
 
 
 def default_n_grid(n_blocks: int) -> list:
-    """Block counts around the layer's (left out, so the off-grid fit is used), within the top-K kernels' range."""
-    return sorted({n for n in (n_blocks // 8, n_blocks // 4, n_blocks // 2, n_blocks * 2, n_blocks * 4)
-                   if 64 <= n <= 32768} - {n_blocks})
+    """Block counts around the layer's, within the top-K kernels' range. The layer's own N is left out, so the
+    off-grid fit is used, where the range reaches past it; at the range's end the grid holds the layer's N itself,
+    since a fit could only extrapolate there (a quadratic through concave points turns down past the last one)."""
+    grid = {n for n in (n_blocks // 8, n_blocks // 4, n_blocks // 2, n_blocks * 2, n_blocks * 4) if 64 <= n <= 32768}
+    if any(n > n_blocks for n in grid):
+        return sorted(grid - {n_blocks})
+    return sorted(grid | {n_blocks})
 
 
 def default_k_grid(top_k: int, n_blocks: int, extra=()) -> list:
