@@ -36,11 +36,12 @@ HIP_KERNELS = {("prr_fused", "score"): "score_kernel (with the EMA update)",
 
 
 def parse():
+    from dynamic_sparse_attention_decode_amd.inputs import WORKLOADS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="paged_b32_64k",
+    ap.add_argument("--workload", default="paged_b32_64k", choices=list(WORKLOADS),
                     help="workload (default: the batched paged-KV layer, the largest that one GPU holds)")
     ap.add_argument("--kspec", type=int, default=None, help="speculation budget (default: the workload's largest)")
     ap.add_argument("--layers", type=int, default=0, help="KV copies to rotate over (0 = auto)")
