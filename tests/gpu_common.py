@@ -34,6 +34,15 @@ def small(name: str) -> Workload:
 SMALL = ["tiny_f32_4k", "llama3_8b_32k", "long_ctx_131k_b4", "paged_b32_64k", "million_token"]
 
 
+def wide_paged(**kw) -> Workload:
+    """136 rows (17 sequences x 8 KV heads) of the reduced paged workload, with a partly filled last block: enough
+    rows for the fused step's many-row path (speculation in its own launch, the split of T into hits and a missed
+    list)."""
+    args = dict(batch=17, ctx=16 * 70 - 3, top_k=12, k_spec=(12,), steps=5)
+    args.update(kw)
+    return small("paged_b32_64k").replace(**args)
+
+
 def shape_of(w: Workload) -> L.Shape:
     return L.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.block_size, w.page_size, w.n_blocks,
                         {"f32": L.F32, "bf16": L.BF16, "f16": L.F16}[w.dtype], w.scale,

@@ -13,7 +13,8 @@ from dynamic_sparse_attention_decode_amd import _lib as L
 from dynamic_sparse_attention_decode_amd.runtime import PRRLayer
 from oracle import prr_oracle as O
 from tests.checker import TOL, check_selection, max_abs
-from tests.gpu_common import OracleView, gap_inputs, np64, oracle_scores, requires_gpu, shape_of, small
+from tests.gpu_common import (OracleView, gap_inputs, np64, oracle_scores, requires_gpu, shape_of, small,
+                              wide_paged)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -150,7 +151,7 @@ def test_decode_with_budget(name, policy, mode):
     P_{t+1} equal to the oracle's budgeted prediction from the step's scores and EMA and the previous step's missed
     counts; the sets' sizes vary by row within [k_min, k_spec]."""
     if name == "paged_wide":   # 136 rows: the fused step's selection splits T into hits and a missed list
-        w = small("paged_b32_64k").replace(batch=17, ctx=16 * 70 - 3, top_k=12, k_spec=(12,), steps=5)
+        w = wide_paged()
     else:
         w = small(name)
     kp = min(w.n_blocks, max(max(w.k_spec), w.top_k + w.top_k // 2))   # room above K for the sizes to vary

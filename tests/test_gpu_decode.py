@@ -9,8 +9,8 @@ from dynamic_sparse_attention_decode_amd import _lib as L
 from dynamic_sparse_attention_decode_amd.runtime import PRRLayer
 from oracle import prr_oracle as O
 from tests.checker import TOL, check_selection, max_abs
-from tests.gpu_common import (SMALL, OracleView, gap_inputs, np64, oracle_scores, ragged, requires_gpu, shape_of,
-                              small)
+from tests.gpu_common import (OracleView, SMALL, gap_inputs, np64, oracle_scores, ragged, requires_gpu, shape_of,
+                              small, wide_paged)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -113,12 +113,15 @@ def test_two_stream_delays_do_not_change_results(name):
                 assert np.array_equal(x, y), (delays, t, what)
 
 
-@pytest.mark.parametrize("k_spec", [12, 20])
-def test_decode_many_rows_vs_oracle(k_spec):
-    """A batch of 136 rows (17 sequences x 8 KV heads): the fused step speculates inside the scoring launch and
-    attends the missed blocks per row after their selection; every step against the oracle."""
-    w = small("paged_b32_64k").replace(batch=17, ctx=16 * 70 - 3, top_k=12, k_spec=(k_spec,), steps=5)
-    print(f"[case] decode many rows B={w.batch} K'={k_spec}", flush=True)
+@pytest.mark.parametrize("k_spec,extra", [(12, {}), (20, {}), (20, {"sink_blocks": 1, "local_blocks": 3}),
+                                          (20, {"scorer": "mean"})])
+def test_decode_many_rows_vs_oracle(k_spec, extra):
+    """A batch of 136 rows (17 sequences x 8 KV heads, a partly filled last block): the fused step's many-row path
+    (speculation in its own launch, the selection splitting T into hits and a missed list, the repair of the list, the
+    merge of the records), also with forced sink and local blocks and with the mean-key scorer; every step against
+    the oracle."""
+    w = wide_paged(k_spec=(k_spec,), **extra)
+    print(f"[case] decode many rows B={w.batch} K'={k_spec} {extra}", flush=True)
     inp = gap_inputs(w)
     run_layer(w, inp, k_spec, "prr_fused", ov=OracleView(inp))
 
@@ -301,12 +304,13 @@ class _Grown:
 
 
 @pytest.mark.parametrize("name,mode", [("llama3_8b_32k", "prr_fused"), ("paged_b32_64k", "prr_2stream"),
-                                       ("tiny_f32_4k", "serialized"), ("million_token", "prr_fused")])
+                                       ("tiny_f32_4k", "serialized"), ("million_token", "prr_fused"),
+                                       ("paged_wide", "prr_fused")])
 def test_decode_with_appends(name, mode):
     """A decoder's loop: before every step after the first, one new token per sequence is appended (prr_append_kv
     through PRRLayer.append); the step then selects, speculates and repairs over the longer sequences. Checked at
     every step against the oracle over the sequences with the same appended tokens."""
-    w = ragged(small(name), 7).replace(steps=6)
+    w = ragged(wide_paged() if name == "paged_wide" else small(name), 7).replace(steps=6)
     print(f"[case] decode with appends {w.name} {mode}", flush=True)
     inp = gap_inputs(w)
     view = _Grown(OracleView(inp))
