@@ -2,10 +2,13 @@
 
 PRRLayer owns one attention layer's decode buffers (summaries, scores, EMA, predicted-set and partial double
 buffers, repair workspace) as PyTorch device tensors, and two HIP streams (default priority). ``step(q)`` enqueues
-one decode step through the library's ``prr_decode_step``:
+one decode step through the library's ``prr_decode_step``; in the two-stream mode, with one fork and one join:
 
-  stream_sel:  score_select(t) -> [wait speculation] -> repair_merge(t)                      -> out_t
-  stream_spec: speculate(P_t)  -> [wait selection]   -> ema_predict(t) -> P_{t+1}
+  stream_sel:  [fork] score_select(t) -> [join: wait speculation] -> repair_merge(t) -> ema_predict(t)
+  stream_spec: [wait fork] speculate(P_t)
+
+giving out_t and P_{t+1}. The other modes run on stream_sel alone (``prr_fused``: the same steps in fewer launches,
+speculation inside the selection launch or in a launch of its own).
 
 A per-row budget (prr_budget) may size each row's predicted set below k_spec; its rows then end in -1 slots.
 
