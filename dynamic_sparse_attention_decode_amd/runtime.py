@@ -160,7 +160,7 @@ class PRRLayer:
         return out
 
     def sync_spec(self) -> None:
-        """Make the current stream wait for the speculation stream (the predicted set of the next step)."""
+        """Make the current stream wait for the speculation stream (its last speculation launch)."""
         torch.cuda.current_stream(self.device).wait_stream(self.s_spec)
 
     @property

@@ -233,13 +233,17 @@ size_t prr_workspace_bytes(const prr_shape* shape, int32_t top_k);
 typedef enum {
   PRR_MODE_SERIALIZED = 0,  /* stream_sel: score_select -> repair_merge over all of T (no prediction)            */
   PRR_MODE_ONE_STREAM = 1,  /* stream_sel: speculate -> score_select -> repair_merge -> ema_predict                */
-  PRR_MODE_TWO_STREAM = 2,  /* stream_spec: speculate || stream_sel: score_select; then repair_merge on stream_sel
-                               while ema_predict runs on stream_spec                                            */
-  PRR_MODE_FUSED = 3,       /* stream_sel only, 3 or 4 launches. When batch * n_kv_heads >= 128 or top_k <= 32
-                               (and select_repair supports the shape): score (+ EMA update) -> one launch
-                               selecting T and P_{t+1}, speculating over P_t and attending the missed blocks
-                               T minus P_t -> one merge launch. Otherwise: score (+ EMA update) ->
-                               select_speculate (T, P_{t+1}, speculation over P_t) -> repair_merge            */
+  PRR_MODE_TWO_STREAM = 2,  /* stream_spec: speculate || stream_sel: score_select; after the join, repair_merge
+                               -> ema_predict on stream_sel (one fork and one join per step)                    */
+  PRR_MODE_FUSED = 3,       /* stream_sel only. batch * n_kv_heads >= 128: speculate -> score (+ EMA update) ->
+                               one launch selecting T and P_{t+1} and splitting T into the hits and a list of the
+                               missed blocks -> repair of the listed blocks -> merge. Otherwise, top_k <= 32:
+                               score (+ EMA update) -> one launch selecting T and P_{t+1}, speculating over P_t
+                               and attending T minus P_t per row -> merge. Otherwise: score (+ EMA update) ->
+                               select_speculate (T, P_{t+1}, speculation over P_t; rows of more than 8192
+                               blocks by segments and a merge) -> repair_merge, which with nothing to
+                               speculate or predict are the serialized launches. The shapes each form supports
+                               are the conditions of the separate calls; outside them the next form is taken.  */
   PRR_MODE_SERIALIZED_FUSED = 4  /* stream_sel only: score -> select_repair with no prediction (select-then-attend
                                     in two launches) when select_repair supports the shape and batch * n_kv_heads
                                     >= 128; otherwise as PRR_MODE_SERIALIZED                                    */
