@@ -25,8 +25,11 @@ METRIC = "µs per decode step per layer (select+speculate+repair); KV GB/s vs HB
 HBM_PEAK_GBS = 8000.0
 # HIP kernels behind each traced launch
 HIP_KERNELS = {("prr_fused", "score"): "score_kernel (with the EMA update)",
-               ("prr_fused", "select_topk"): "select_spec_kernel or select_missed_kernel (true top-K, next top-K', "
-                                             "speculation over P_t; the latter also the missed blocks)",
+               ("prr_fused", "select_topk"): "the selection launch(es) by shape: select_spec_kernel (true top-K, "
+                                             "next top-K', speculation over P_t), seg_spec_kernel + merge2_kernel "
+                                             "(rows of more than 8192 blocks), select_missed_kernel (K <= 32, also "
+                                             "the missed blocks), topk_pair_kernel (>= 128 rows; the speculation "
+                                             "has its own launch)",
                ("prr_fused", "repair"): "repair_kernel + finalize_kernel",
                ("prr_fused", "finalize"): "merge_hits_kernel or finalize_kernel",
                ("prr_fused", "speculate"): "speculate_kernel",
@@ -183,7 +186,7 @@ def main():
     mean_pred = float(np.mean(pred_size)) if pred_size else float(kspec)   # filled slots of a predicted set
     prr_mode = not a.mode.startswith("serialized")
 
-    # the fused step's many-row path (speculation in its own launch, the split into hits and missed lists) serves
+    # the fused step's many-row path (speculation in its own launch, a selection launch of top-K workgroups) serves
     # batches whose rows alone fill the chip
     many_row = rows >= 128
 

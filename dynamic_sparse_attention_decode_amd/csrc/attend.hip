@@ -221,147 +221,6 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   }
 }
 
-// The repair by lists: workgroup (rec, row) attends the missed blocks [rec * 4 epw, (rec + 1) * 4 epw) of the row's
-// list (the selection launch wrote it), epw per wave with the next chunk's loads in flight, and merges its 4 wave
-// states in LDS into record rec of the row. A workgroup past the end of the list exits at once: the merge reads only
-// the records of the entries that exist.
-template <int DT, int G, bool P16>
-__global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_list_kernel(const uint8_t* __restrict__ q,
-                                                                        const uint8_t* __restrict__ kc,
-                                                                        const uint8_t* __restrict__ vc,
-                                                                        const int32_t* __restrict__ table, SplitWs ws,
-                                                                        int Hq, int Hkv, int N, int bs, int page,
-                                                                        int pps, float qscale, int last_len) {
-  using W = Tile<DT, G>;
-  constexpr int D = W::D;
-  constexpr int RF = rec_floats(G, D);
-  constexpr int ML = rec_ml(G);
-  __shared__ float s_ml[4][2 * G];
-  __shared__ float s_o[4 * G * D];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t rowid = blockIdx.y;
-  const int rec = blockIdx.x;
-  const int nm = ws.cnt[2 * rowid + 1];
-  const int jw = rec * 4 * ws.epw;
-  if (jw >= nm) return;   // uniform over the workgroup
-  const int b = (int)(rowid / Hkv), g = (int)(rowid % Hkv);
-  const int32_t* mrow = ws.miss + rowid * ws.Kp;
-  W st;
-  st.init(lane);
-  st.load_q(q + ((int64_t)b * Hq + (int64_t)g * G) * kRowBytes, qscale);
-  const int32_t* trow = table + (int64_t)b * pps;
-  const int j0 = jw + wave * ws.epw, j1 = min(nm, j0 + ws.epw);
-  for (int jb = j0; jb < j1; jb += 8)
-    run_blocks<P16>(st, min(8, j1 - jb), [&](int i) { return min(max(mrow[jb + i], 0), N - 1); }, [](int) {}, kc,
-                    vc, trow, bs, page, Hkv, g, N, last_len);
-  float folded[W::NK];
-  st.fold(folded);
-  st.store_ml(&s_ml[wave][0]);
-#pragma unroll
-  for (int i = 0; i < W::NK; ++i) {
-    const int f = st.row * W::NK + i;
-    s_o[wave * G * D + (f / W::VE) * D + st.col * W::VE + (f % W::VE)] = folded[i];
-  }
-  __syncthreads();
-  // merge the 4 wave states (a wave past the list's end holds m = -inf and no weight) into this workgroup's record
-  float* my = ws.rec + (rowid * ws.nrec + rec) * (int64_t)RF;
-  for (int f = threadIdx.x; f < G * D; f += 256) {
-    const int h = f / D;
-    const float M = fmaxf(fmaxf(s_ml[0][h], s_ml[1][h]), fmaxf(s_ml[2][h], s_ml[3][h]));
-    float o = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) o += s_o[w * G * D + f] * exp2f(s_ml[w][h] - M);
-    my[ML + f] = o;
-  }
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    const float M = fmaxf(fmaxf(s_ml[0][h], s_ml[1][h]), fmaxf(s_ml[2][h], s_ml[3][h]));
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) L += s_ml[w][G + h] * exp2f(s_ml[w][h] - M);
-    my[h] = M;
-    my[G + h] = L;
-  }
-}
-
-// out[b, g*G + h] = merge of the row's repair records and the speculated records of its hits, normalised: one
-// 256-thread workgroup per (row, head); the weights exp2(m_i - M) go to LDS, then 256 / (D/4) record groups
-// accumulate float4 slices of O with 8 loads in flight per thread. Records of blocks of P outside T are never read.
-template <int G, int D, int OB>
-__global__ __launch_bounds__(256) void finalize_list_kernel(const float* __restrict__ partials, int k_spec, SplitWs ws,
-                                                            float* __restrict__ out, int Hq, int Hkv) {
-  constexpr int RF = rec_floats(G, D);
-  constexpr int64_t SRB = spec_rec_bytes(OB == 4 ? 0 : 1, G, D);   // speculation record bytes
-  constexpr int S = D / 4, P = 256 / S, U = 8;
-  constexpr int kMaxRec = kMaxRecords + kSplitMaxK;
-  __shared__ float s_w[kMaxRec];
-  __shared__ const uint8_t* s_rec[kMaxRec];
-  __shared__ float s_red[2][4];
-  __shared__ float4 s_acc[P][S];
-  const int64_t r = blockIdx.x;
-  const int h = blockIdx.y;
-  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int b = (int)(r / Hkv), g = (int)(r % Hkv);
-  const int nh = ws.cnt[2 * r], nm = ws.cnt[2 * r + 1];
-  const int nrep = (nm + 4 * ws.epw - 1) / (4 * ws.epw);   // repair records written
-  const int n = nrep + nh;
-  const uint8_t* rep_row = reinterpret_cast<const uint8_t*>(ws.rec + r * ws.nrec * (int64_t)RF);
-  const uint8_t* part_row = partials ? reinterpret_cast<const uint8_t*>(partials) + r * k_spec * SRB : nullptr;
-  const int32_t* hrow = ws.hits + r * ws.Kp;
-  float mx = -__builtin_huge_valf();
-  for (int i = t; i < n; i += 256) {   // records [0, nrep) are the repair's (fp32 O), the rest speculated hits
-    const uint8_t* rec = i < nrep ? rep_row + (int64_t)i * RF * 4 : part_row + (int64_t)hrow[i - nrep] * SRB;
-    s_rec[i] = rec;
-    const float m = reinterpret_cast<const float*>(rec)[h];
-    s_w[i] = m;
-    mx = fmaxf(mx, m);
-  }
-  mx = wave_max(mx);
-  if (lane == 0) s_red[0][wave] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
-  float ls = 0.f;
-  for (int i = t; i < n; i += 256) {
-    const float w = exp2f(s_w[i] - M);
-    s_w[i] = w;
-    ls += reinterpret_cast<const float*>(s_rec[i])[G + h] * w;
-  }
-  ls = wave_sum(ls);
-  if (lane == 0) s_red[1][wave] = ls;
-  __syncthreads();
-  const float L = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
-  const int slot = t % S, p = t / S;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int i0 = p; i0 < n; i0 += U * P) {
-    float4 o[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * P;
-      o[u] = i < n ? rec_o4<G, D>(s_rec[i], OB == 4 || i < nrep, h, slot) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * P;
-      const float wr = i < n ? s_w[i] : 0.f;
-      acc.x = fmaf(o[u].x, wr, acc.x); acc.y = fmaf(o[u].y, wr, acc.y);
-      acc.z = fmaf(o[u].z, wr, acc.z); acc.w = fmaf(o[u].w, wr, acc.w);
-    }
-  }
-  s_acc[p][slot] = acc;
-  __syncthreads();
-  if (t < S) {
-    float4 a = s_acc[0][t];
-#pragma unroll
-    for (int p2 = 1; p2 < P; ++p2) {
-      const float4 c = s_acc[p2][t];
-      a.x += c.x; a.y += c.y; a.z += c.z; a.w += c.w;
-    }
-    const float il = 1.f / L;
-    float* o = out + ((int64_t)b * Hq + (int64_t)g * G + h) * D;
-    *reinterpret_cast<float4*>(o + t * 4) = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
-  }
-}
-
 // ---- launchers -----------------------------------------------------------------------------------------------------
 
 // Entries of T per repair wave: enough to keep records per row <= kMaxRecords; on the pipelined path about eight
@@ -404,41 +263,6 @@ static size_t ws_layout(const prr_shape& s, int top_k, void* base, RepairWs* out
 }
 
 size_t repair_workspace_bytes(const prr_shape& s, int top_k) { return ws_layout(s, top_k, nullptr, nullptr); }
-
-// The repair by lists: per row its records, then the hit slots and missed ids (Kp each), then two counts per row.
-static size_t split_layout(const prr_shape& s, int top_k, void* base, SplitWs* out) {
-  const int G = s.n_q_heads / s.n_kv_heads;
-  const int64_t rows = (int64_t)s.batch * s.n_kv_heads;
-  const int Kp = (top_k + 3) & ~3;
-  const int epw = repair_epw(s, top_k);
-  const int nrec = (top_k + 4 * epw - 1) / (4 * epw);
-  const size_t rec_b = ((size_t)(rows * nrec * rec_floats(G, s.head_dim)) * sizeof(float) + 255) / 256 * 256;
-  const size_t list_b = (size_t)rows * Kp * sizeof(int32_t);
-  const size_t cnt_b = ((size_t)rows * 2 * sizeof(int32_t) + 255) / 256 * 256;
-  if (out) {
-    char* p = static_cast<char*>(base);
-    out->rec = reinterpret_cast<float*>(p);
-    out->hits = reinterpret_cast<int32_t*>(p + rec_b);
-    out->miss = reinterpret_cast<int32_t*>(p + rec_b + list_b);
-    out->cnt = reinterpret_cast<int32_t*>(p + rec_b + 2 * list_b);
-    out->Kp = Kp;
-    out->nrec = nrec;
-    out->epw = epw;
-  }
-  return rec_b + 2 * list_b + cnt_b;
-}
-
-SplitWs split_ws_at(const prr_shape& s, int top_k, void* base) {
-  SplitWs w{};
-  split_layout(s, top_k, base, &w);
-  return w;
-}
-
-size_t split_ws_bytes(const prr_shape& s, int top_k) { return split_layout(s, top_k, nullptr, nullptr); }
-
-bool split_repair_supported(const prr_shape& s, int top_k, int k_spec, int k_spec_next) {
-  return top_k <= kSplitMaxK && k_spec <= kSplitMaxK && k_spec_next <= kSplitMaxK && s.n_blocks <= 32768;
-}
 
 // The resolved-page pipelined path: 16-token chunks never straddle a page, and a wave's group of at most 8 entries
 // (or 4 speculation slots) spans at most 64 chunks.
@@ -492,32 +316,6 @@ static void repair_launch(const prr_shape& s, const void* q, const void* kc, con
                                                                                  n_missed, s.n_q_heads,
                                                                                  s.n_kv_heads);
   trace_end(PRR_KERNEL_FINALIZE, st);
-}
-
-template <int DT, int G>
-static void repair_list_launch(const prr_shape& s, const void* q, const void* kc, const void* vc, const int32_t* table,
-                               const float* partials, int k_spec, float* out, const SplitWs& ws, hipStream_t st) {
-  const int64_t rows = (int64_t)s.batch * s.n_kv_heads;
-  const float qscale = s.softmax_scale * kLog2e;
-  trace_begin(PRR_KERNEL_REPAIR, st);
-  auto kern = p16_path(s) ? repair_list_kernel<DT, G, true> : repair_list_kernel<DT, G, false>;
-  kern<<<dim3((unsigned)ws.nrec, (unsigned)rows), dim3(256), 0, st>>>(
-      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, ws,
-      s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size, s.pages_per_seq, qscale, last_block_len(s));
-  trace_end(PRR_KERNEL_REPAIR, st);
-  constexpr int D = 16 * Vec<DT>::n;
-  trace_begin(PRR_KERNEL_FINALIZE, st);
-  finalize_list_kernel<G, D, spec_o_bytes(DT)><<<dim3((unsigned)rows, (unsigned)G), dim3(256), 0, st>>>(
-      partials, k_spec, ws, out, s.n_q_heads, s.n_kv_heads);
-  trace_end(PRR_KERNEL_FINALIZE, st);
-}
-
-prr_status launch_repair_list(const prr_shape& s, const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* table, const float* partials, int k_spec, float* out, const SplitWs& ws,
-                              hipStream_t stream) {
-  if (!partials) k_spec = 0;
-  PRR_DISPATCH_DT_G(repair_list_launch, s, q, k_cache, v_cache, table, partials, k_spec, out, ws, stream);
-  return check_launch("repair (lists)");
 }
 
 prr_status launch_speculate(const prr_shape& s, const void* q, const void* k_cache, const void* v_cache,

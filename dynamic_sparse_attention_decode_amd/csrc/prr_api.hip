@@ -461,9 +461,7 @@ size_t prr_partials_bytes(const prr_shape* shape, int32_t k_spec) {
 size_t prr_workspace_bytes(const prr_shape* shape, int32_t top_k) {
   if (check_shape(shape) != PRR_OK || top_k <= 0) return 0;
   const size_t a = repair_workspace_bytes(*shape, top_k), b = select_missed_ws_bytes(*shape, top_k);
-  const size_t c = split_ws_bytes(*shape, top_k);
-  const size_t ab = a > b ? a : b;
-  return 3 * cand_part_bytes(*shape) + (ab > c ? ab : c);
+  return 3 * cand_part_bytes(*shape) + (a > b ? a : b);
 }
 
 prr_status prr_step_ctx_create(prr_step_ctx** out) {
@@ -595,20 +593,19 @@ static prr_status decode_step_impl(prr_step_ctx* ctx, const prr_shape* shape, co
                                 kc ? a->partials : nullptr, true, a->out, a->n_missed,
                                 repair_ws(*shape, a->workspace), s1, budget_dev(budget));
   }
-  if (mode == PRR_MODE_FUSED && rows >= 128 && split_repair_supported(*shape, a->top_k, kc, kn)) {
+  if (mode == PRR_MODE_FUSED && rows >= 128) {
     // When the rows alone fill the chip every phase is bound by bandwidth. The speculation over P_t takes its own
     // launch (several slots per wave, pipelined), which moves the gathered blocks faster than speculation roles
-    // beside the selection would; the selection launch splits each row's T into the hits' slots and a list of the
-    // missed blocks; the repair attends only the listed blocks, spread over waves; the merge launch folds their
-    // records and the hits' records, many loads in flight, instead of one dependent record load per hit.
+    // beside the selection would; the selection launch then holds only top-K workgroups (T and P_{t+1}), all
+    // resident at once; the spread-out repair merges the hits' records and attends the missed blocks.
     if (kc > 0)
       PRR_TRY(prr_speculate(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->pred_cur, kc, a->partials, s1));
     PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step, s1));
-    const SplitWs sw = split_ws_at(*shape, a->top_k, repair_ws(*shape, a->workspace));
-    PRR_TRY(launch_select_split(*shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next,
-                                kc ? a->pred_cur : nullptr, kc, sw, a->n_missed, budget_dev(budget), s1));
-    return launch_repair_list(*shape, a->q, a->k_cache, a->v_cache, a->block_table, kc ? a->partials : nullptr, kc,
-                              a->out, sw, s1);
+    PRR_TRY(prr_select_speculate(shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,
+                                 a->v_cache, a->block_table, a->pred_cur, 0, a->partials, budget, a->workspace,
+                                 s1));
+    return prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
+                            kc, a->partials, a->out, a->n_missed, a->workspace, s1);
   }
   if (mode == PRR_MODE_FUSED) {
     // Otherwise the speculation rides in the latency-bound selection launch (long rows select in two launches,

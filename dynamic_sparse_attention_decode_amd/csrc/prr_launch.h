@@ -126,30 +126,6 @@ TopkCand topk_cand_at(const prr_shape& s, void* region);
 // launch of top-K workgroups only (rows of at most 32768 values).
 prr_status launch_topk_pair(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema, int kp,
                             int32_t* pred_next, const BudgetDev& bp, hipStream_t stream);
-// The repair by lists (many-row batches): the selection launch splits each row's true set T against the current
-// predicted set into the slots of the hits (in T order) and the ids of the missed blocks (ascending); the repair
-// launch attends only the missed blocks, spread over waves, into per-workgroup records; the merge launch folds those
-// records and the hits' speculated records into the output.
-constexpr int kSplitMaxK = 2048;   // largest true set and predicted set of the split (held in LDS)
-struct SplitWs {
-  float* rec;       // [rows][nrec][record floats]: the repair launch's records
-  int32_t* hits;    // [rows][Kp] predicted slots of the hits
-  int32_t* miss;    // [rows][Kp] missed block ids
-  int32_t* cnt;     // [rows][2] hits, misses
-  int Kp, nrec, epw;
-};
-SplitWs split_ws_at(const prr_shape& s, int top_k, void* base);
-size_t split_ws_bytes(const prr_shape& s, int top_k);
-bool split_repair_supported(const prr_shape& s, int top_k, int k_spec, int k_spec_next);
-// Selection of T with its split against pred (k_spec slots; none when k_spec == 0), and the next predicted set when
-// kp > 0 (top-K' of the updated EMA, or a budgeted set), in one launch; n_missed = |T minus P|.
-prr_status launch_select_split(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema, int kp,
-                               int32_t* pred_next, const int32_t* pred, int k_spec, const SplitWs& ws,
-                               int32_t* n_missed, const BudgetDev& bp, hipStream_t stream);
-// The missed blocks of each row's list, then the merge of their records with the hits' records into out.
-prr_status launch_repair_list(const prr_shape& s, const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* table, const float* partials, int k_spec, float* out, const SplitWs& ws,
-                              hipStream_t stream);
 prr_status launch_speculate(const prr_shape& s, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* table, const int32_t* pred, int k_spec, float* partials,
                             hipStream_t stream);

@@ -80,108 +80,6 @@ __global__ __launch_bounds__(NT) void topk_pair_kernel(const float* __restrict__
                              Force{0, N, sink, local});
 }
 
-// Workgroup r < rows: the true top-K of row r, then its split against the current predicted set P (k_spec slots,
-// ending at the first empty one): the slots of the entries of T found in P (bisection when P is ascending, as the
-// top-K launches write it; a linear search otherwise) go to ws.hits in T order, the other entries of T to ws.miss,
-// ascending; the counts to ws.cnt and n_missed. Workgroups [rows, 2 rows): the next predicted set, as
-// topk_pair_kernel. Blocks of P outside T are never listed.
-template <int NT, int KPT>
-__global__ __launch_bounds__(NT) void select_split_kernel(const float* __restrict__ scores, int K,
-                                                          int32_t* __restrict__ sel, const float* __restrict__ ema,
-                                                          int Kp, int32_t* __restrict__ pred_next,
-                                                          const int32_t* __restrict__ pred, int k_spec, SplitWs ws,
-                                                          int32_t* __restrict__ n_missed, int rows, int N, int sink,
-                                                          int local, BudgetDev bp) {
-  constexpr int NW = NT / 64;
-  constexpr int EPT = kSplitMaxK / NT;   // entries of T per thread
-  __shared__ int32_t s_T[kSplitMaxK];
-  __shared__ int32_t s_P[kSplitMaxK];
-  __shared__ uint32_t s_scan[NW];
-  __shared__ int s_kf, s_unsorted;
-  const int64_t r = blockIdx.x;
-  if (r >= rows) {
-    const int64_t rr = r - rows;
-    if (bp.policy != 0)
-      predict_row<NT, KPT, false>(scores + rr * N, const_cast<float*>(ema) + rr * N, 0.f, 0, N, Kp, bp, rr,
-                                  pred_next + rr * Kp, Force{0, N, sink, local});
-    else
-      topk_row<NT, KPT, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp, pred_next + rr * Kp, nullptr,
-                               Force{0, N, sink, local});
-    return;
-  }
-  topk_row<NT, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, s_T, Force{0, N, sink, local});
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int32_t* prow = k_spec ? pred + r * k_spec : nullptr;
-  if (tid == 0) { s_kf = k_spec; s_unsorted = 0; }
-  for (int i = tid; i < k_spec; i += NT) s_P[i] = prow[i];
-  __syncthreads();   // T, P and the flags in LDS
-  for (int i = tid; i < k_spec; i += NT)
-    if (s_P[i] < 0) atomicMin(&s_kf, i);
-  __syncthreads();
-  const int kf = s_kf;   // slots from the first empty one on never match
-  for (int i = tid; i + 1 < kf; i += NT)
-    if (s_P[i] >= s_P[i + 1]) s_unsorted = 1;
-  __syncthreads();
-  const bool sorted = s_unsorted == 0;
-  int slot[EPT];
-  uint32_t nh_local = 0;
-#pragma unroll
-  for (int u = 0; u < EPT; ++u) {
-    const int j = tid * EPT + u;
-    slot[u] = -1;
-    if (j < K && kf > 0) {
-      const int n = s_T[j];
-      if (sorted) {
-        int lo = 0, hi = kf;   // first index with s_P[idx] >= n
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (s_P[mid] < n) lo = mid + 1; else hi = mid;
-        }
-        if (lo < kf && s_P[lo] == n) slot[u] = lo;
-      } else {
-        for (int i = 0; i < kf; ++i)
-          if (s_P[i] == n) { slot[u] = i; break; }
-      }
-    }
-    nh_local += slot[u] >= 0;
-  }
-  uint32_t incl = nh_local;   // inclusive scan of the hit counts over the threads, in T order
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(incl, d);
-    if (lane >= d) incl += y;
-  }
-  if (lane == 63) s_scan[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, nh = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t c = s_scan[w];
-    before += w < wave ? c : 0u;
-    nh += c;
-  }
-  uint32_t ph = before + incl - nh_local;   // hits before this thread's entries
-  int32_t* hrow = ws.hits + r * ws.Kp;
-  int32_t* mrow = ws.miss + r * ws.Kp;
-#pragma unroll
-  for (int u = 0; u < EPT; ++u) {
-    const int j = tid * EPT + u;
-    if (j < K) {
-      if (slot[u] >= 0) {
-        hrow[ph] = slot[u];
-        ++ph;
-      } else {
-        mrow[(uint32_t)j - ph] = s_T[j];   // misses before entry j = j - hits before j
-      }
-    }
-  }
-  if (tid == 0) {
-    ws.cnt[2 * r] = (int)nh;
-    ws.cnt[2 * r + 1] = K - (int)nh;
-    n_missed[r] = K - (int)nh;
-  }
-}
-
 // ---- launchers -----------------------------------------------------------------------------------------------------
 
 template <int DT, int G>
@@ -335,33 +233,6 @@ prr_status launch_topk_pair(const prr_shape& s, const float* scores, int k, int3
 #undef PRR_PAIR
   trace_end(PRR_KERNEL_SELECT_TOPK, st);
   return check_launch("select (true and predicted sets)");
-}
-
-prr_status launch_select_split(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema, int kp,
-                               int32_t* pred_next, const int32_t* pred, int k_spec, const SplitWs& ws,
-                               int32_t* n_missed, const BudgetDev& bp, hipStream_t st) {
-  const int N = s.n_blocks, rows = s.batch * s.n_kv_heads;
-  const dim3 grid((unsigned)((kp > 0 ? 2 : 1) * rows));
-#define PRR_SPLIT(NT, KPT)                                                                                         \
-  select_split_kernel<NT, KPT><<<grid, NT, 0, st>>>(scores, k, sel, ema, kp, pred_next, pred, k_spec, ws, n_missed,  \
-                                                    rows, N, s.sink_blocks, s.local_blocks, bp)
-  trace_begin(PRR_KERNEL_SELECT_TOPK, st);
-  if (N <= 4096) {
-    switch (topk_kpt_nt(N, 512)) {
-      case 1: case 2: PRR_SPLIT(512, 2); break;
-      case 4: PRR_SPLIT(512, 4); break;
-      default: PRR_SPLIT(512, 8); break;
-    }
-  } else {
-    switch (topk_kpt(N)) {
-      case 1: case 2: case 4: case 8: PRR_SPLIT(1024, 8); break;
-      case 16: PRR_SPLIT(1024, 16); break;
-      default: PRR_SPLIT(1024, 32); break;   // N <= 32768
-    }
-  }
-#undef PRR_SPLIT
-  trace_end(PRR_KERNEL_SELECT_TOPK, st);
-  return check_launch("select (with the split of T)");
 }
 
 prr_status launch_topk(const prr_shape& s, const float* values, float* ema, float alpha, int first, int k,

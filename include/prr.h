@@ -236,8 +236,8 @@ typedef enum {
   PRR_MODE_TWO_STREAM = 2,  /* stream_spec: speculate || stream_sel: score_select; after the join, repair_merge
                                -> ema_predict on stream_sel (one fork and one join per step)                    */
   PRR_MODE_FUSED = 3,       /* stream_sel only. batch * n_kv_heads >= 128: speculate -> score (+ EMA update) ->
-                               one launch selecting T and P_{t+1} and splitting T into the hits and a list of the
-                               missed blocks -> repair of the listed blocks -> merge. Otherwise, top_k <= 32:
+                               one launch of top-K workgroups selecting T and P_{t+1} -> repair_merge (the
+                               hits' records merged, the missed blocks attended). Otherwise, top_k <= 32:
                                score (+ EMA update) -> one launch selecting T and P_{t+1}, speculating over P_t
                                and attending T minus P_t per row -> merge. Otherwise: score (+ EMA update) ->
                                select_speculate (T, P_{t+1}, speculation over P_t; rows of more than 8192

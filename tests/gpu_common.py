@@ -36,8 +36,8 @@ SMALL = ["tiny_f32_4k", "llama3_8b_32k", "long_ctx_131k_b4", "paged_b32_64k", "m
 
 def wide_paged(**kw) -> Workload:
     """136 rows (17 sequences x 8 KV heads) of the reduced paged workload, with a partly filled last block: enough
-    rows for the fused step's many-row path (speculation in its own launch, the split of T into hits and a missed
-    list)."""
+    rows for the fused step's many-row path (speculation in its own launch, a selection launch of top-K workgroups
+    only, then the spread-out repair)."""
     args = dict(batch=17, ctx=16 * 70 - 3, top_k=12, k_spec=(12,), steps=5)
     args.update(kw)
     return small("paged_b32_64k").replace(**args)

@@ -150,7 +150,7 @@ def test_decode_with_budget(name, policy, mode):
     attention over the true set whatever was predicted), the missed count = |T minus the filled part of P_t|, and
     P_{t+1} equal to the oracle's budgeted prediction from the step's scores and EMA and the previous step's missed
     counts; the sets' sizes vary by row within [k_min, k_spec]."""
-    if name == "paged_wide":   # 136 rows: the fused step's selection splits T into hits and a missed list
+    if name == "paged_wide":   # 136 rows: the fused step's many-row path
         w = wide_paged()
     else:
         w = small(name)

@@ -117,9 +117,8 @@ def test_two_stream_delays_do_not_change_results(name):
                                           (20, {"scorer": "mean"})])
 def test_decode_many_rows_vs_oracle(k_spec, extra):
     """A batch of 136 rows (17 sequences x 8 KV heads, a partly filled last block): the fused step's many-row path
-    (speculation in its own launch, the selection splitting T into hits and a missed list, the repair of the list, the
-    merge of the records), also with forced sink and local blocks and with the mean-key scorer; every step against
-    the oracle."""
+    (speculation in its own launch, then scores with the EMA, the selection of T and P_{t+1}, the repair), also with
+    forced sink and local blocks and with the mean-key scorer; every step against the oracle."""
     w = wide_paged(k_spec=(k_spec,), **extra)
     print(f"[case] decode many rows B={w.batch} K'={k_spec} {extra}", flush=True)
     inp = gap_inputs(w)
