@@ -225,7 +225,9 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
 
 // Entries of T per repair wave: enough to keep records per row <= kMaxRecords; on the pipelined path about eight
 // 16-token chunks per wave while at least 4096 waves remain (on the paged batch, 8 entries per wave against 4:
-// repair 57.5 -> 53.8 us, 4 against 2: 62.1 -> 57.0 us; 16 is slower again).
+// repair 57.5 -> 53.8 us, 4 against 2: 62.1 -> 57.0 us), and sixteen one-chunk entries where eight would leave that
+// many waves: every workgroup is then resident at once, which the PRR step's mix of record merges and missed blocks
+// needs (paged batch, same-box A/B over three runs: PRR step 215.8 -> 213.1 us; serialized 147.8 -> 147.6 us).
 static int repair_epw(const prr_shape& s, int top_k) {
   const int need = (top_k + 4 * kMaxRecords - 1) / (4 * kMaxRecords);
   int e = 1;
@@ -234,6 +236,7 @@ static int repair_epw(const prr_shape& s, int top_k) {
     e = cpb >= 8 ? 1 : 8 / cpb;
     const int64_t rows = (int64_t)s.batch * s.n_kv_heads;
     while (e > 1 && rows * ((top_k + e - 1) / e) < 4096) e >>= 1;
+    if (cpb == 1 && e == 8) e = 16;
   }
   return e > need ? e : need;
 }
