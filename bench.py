@@ -195,9 +195,10 @@ def main():
         spec = rows * mean_pred * blk_kv
         rep = rows * (w.top_k if mode.startswith("serialized") else mean_missed) * blk_kv
         if mode == "prr_fused" and many_row:
-            # speculation over P_t in its own launch; scores with the EMA update; the selection launch (T and
-            # P_{t+1}); the spread-out repair (its merge launch traced as "finalize")
-            return {"speculate": spec, "score": summ_b + 3 * row_f32, "select_topk": 2 * row_f32, "repair": rep}
+            # speculation over P_t in its own launch; scores; the selection launch (T from the scores; P_{t+1} from
+            # the EMA, which its workgroups update from the scores); the spread-out repair (its merge launch traced
+            # as "finalize")
+            return {"speculate": spec, "score": summ_b + row_f32, "select_topk": 4 * row_f32, "repair": rep}
         if mode == "prr_fused" and w.top_k <= 32:
             # scoring also updates the EMA; the selection launch reads scores and EMA, speculates over P_t and attends
             # the missed blocks; the merge launch (traced as "finalize") only reads partial records
@@ -309,7 +310,7 @@ def main():
             q = qs[lay.t % w.steps]
             kc = lay.k_spec if lay.t > 0 else 0
             if kernel == "score":
-                e = lay.ema.clone() if mode == "prr_fused" else None
+                e = lay.ema.clone() if mode == "prr_fused" and not many_row else None   # as the step scores
                 calls.append(lambda lay=lay, q=q, e=e, par=par: L.score(
                     shape, q, lay.summaries, lay.scores[par], e, w.alpha, False, stream=streams[0]))
             elif kernel == "select_topk" and mode == "prr_fused" and "repair" in alg:   # the select_spec launch
@@ -485,7 +486,10 @@ def main():
                    "top_k": w.top_k, "k_spec": kspec, "alpha": w.alpha, "mode": a.mode,
                    "sink_blocks": w.sink_blocks, "local_blocks": w.local_blocks, "scorer": w.scorer,
                    "budget": a.budget, "layers_rotated": n_layers, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": dominant, "hip_kernels": HIP_KERNELS.get((a.mode, dominant), dominant),
+        "roofline": {"bound": "hbm", "kernel": dominant,
+                     "hip_kernels": ("score_kernel (the EMA is updated in the selection launch)"
+                                     if (a.mode, dominant) == ("prr_fused", "score") and many_row
+                                     else HIP_KERNELS.get((a.mode, dominant), dominant)),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(w.name, a.mode, dominant),

@@ -597,13 +597,22 @@ static prr_status decode_step_impl(prr_step_ctx* ctx, const prr_shape* shape, co
     // When the rows alone fill the chip every phase is bound by bandwidth. The speculation over P_t takes its own
     // launch (several slots per wave, pipelined), which moves the gathered blocks faster than speculation roles
     // beside the selection would; the selection launch then holds only top-K workgroups (T and P_{t+1}), all
-    // resident at once; the spread-out repair merges the hits' records and attends the missed blocks.
+    // resident at once, and the workgroups that select P_{t+1} also update the EMA, which they read anyway (the
+    // bandwidth-bound scoring pass then writes the scores alone); the spread-out repair merges the hits' records
+    // and attends the missed blocks.
     if (kc > 0)
       PRR_TRY(prr_speculate(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->pred_cur, kc, a->partials, s1));
-    PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step, s1));
-    PRR_TRY(prr_select_speculate(shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,
-                                 a->v_cache, a->block_table, a->pred_cur, 0, a->partials, budget, a->workspace,
-                                 s1));
+    if (kn > 0 && N <= kTopkSplitMinN) {
+      PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, nullptr, 0.f, 0, s1));
+      PRR_TRY(launch_topk_pair(*shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, budget_dev(budget),
+                               s1, true, a->alpha, a->first_step ? 1 : 0));
+    } else {   // long rows select by segments, from the EMA that the scoring pass updates
+      PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step,
+                        s1));
+      PRR_TRY(prr_select_speculate(shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q,
+                                   a->k_cache, a->v_cache, a->block_table, a->pred_cur, 0, a->partials, budget,
+                                   a->workspace, s1));
+    }
     return prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
                             kc, a->partials, a->out, a->n_missed, a->workspace, s1);
   }

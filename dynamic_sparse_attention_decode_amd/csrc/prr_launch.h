@@ -122,10 +122,12 @@ size_t topk_cand_row_capacity(int N);
 size_t topk_cand_bytes(const prr_shape& s);   // one candidate region (0 when rows are never split)
 bool topk_split_on(int N, int K, int seg);
 TopkCand topk_cand_at(const prr_shape& s, void* region);
-// The true top-K of the scores and the next predicted set (top-K' of the updated EMA, or a budgeted set) in one
-// launch of top-K workgroups only (rows of at most 32768 values).
+// The true top-K of the scores and the next predicted set (top-K' of the EMA, or a budgeted set) in one launch of
+// top-K workgroups only (rows of at most 32768 values). ema_update: the launch updates the EMA from the scores first
+// (alpha, first as for the scoring pass); otherwise the EMA is taken as already updated.
 prr_status launch_topk_pair(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema, int kp,
-                            int32_t* pred_next, const BudgetDev& bp, hipStream_t stream);
+                            int32_t* pred_next, const BudgetDev& bp, hipStream_t stream, bool ema_update = false,
+                            float alpha = 0.f, int first = 0);
 prr_status launch_speculate(const prr_shape& s, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* table, const int32_t* pred, int k_spec, float* partials,
                             hipStream_t stream);

@@ -58,14 +58,15 @@ __global__ __launch_bounds__(NT) void predict_budget_kernel(const float* __restr
 }
 
 // The true set and the next predicted set in one launch, with nothing to speculate: workgroup r < rows selects the
-// true top-K of row r, workgroup rows + r the top-K' of row r's EMA (already updated by the scoring pass) or its
-// budgeted set. The workgroups are sized for the top-K alone (no attention tile beside it), so all of them are
-// resident at once.
-template <int NT, int KPT>
+// true top-K of row r, workgroup rows + r the top-K' of row r's EMA or its budgeted set. With EUP the EMA is updated
+// here (e = s on the first step, else alpha e + (1 - alpha) s, the scoring pass's arithmetic) by the workgroup that
+// selects from it, which reads the scores anyway; without, the scoring pass has updated it. The workgroups are sized
+// for the top-K alone (no attention tile beside it), so all of them are resident at once.
+template <int NT, int KPT, bool EUP>
 __global__ __launch_bounds__(NT) void topk_pair_kernel(const float* __restrict__ scores, int K,
-                                                       int32_t* __restrict__ sel, const float* __restrict__ ema,
-                                                       int Kp, int32_t* __restrict__ pred_next, int rows, int N,
-                                                       int sink, int local, BudgetDev bp) {
+                                                       int32_t* __restrict__ sel, float* __restrict__ ema,
+                                                       float alpha, int first, int Kp, int32_t* __restrict__ pred_next,
+                                                       int rows, int N, int sink, int local, BudgetDev bp) {
   const int64_t r = blockIdx.x;
   if (r < rows) {
     topk_row<NT, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, nullptr, Force{0, N, sink, local});
@@ -73,8 +74,11 @@ __global__ __launch_bounds__(NT) void topk_pair_kernel(const float* __restrict__
   }
   const int64_t rr = r - rows;
   if (bp.policy != 0)
-    predict_row<NT, KPT, false>(scores + rr * N, const_cast<float*>(ema) + rr * N, 0.f, 0, N, Kp, bp, rr,
-                                pred_next + rr * Kp, Force{0, N, sink, local});
+    predict_row<NT, KPT, EUP>(scores + rr * N, ema + rr * N, alpha, first, N, Kp, bp, rr, pred_next + rr * Kp,
+                              Force{0, N, sink, local});
+  else if (EUP)
+    topk_row<NT, KPT, true>(scores + rr * N, ema + rr * N, alpha, first, N, Kp, pred_next + rr * Kp, nullptr,
+                            Force{0, N, sink, local});
   else
     topk_row<NT, KPT, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp, pred_next + rr * Kp, nullptr,
                              Force{0, N, sink, local});
@@ -210,12 +214,14 @@ prr_status launch_predict_budget(const prr_shape& s, const float* scores, float*
 }
 
 prr_status launch_topk_pair(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema, int kp,
-                            int32_t* pred_next, const BudgetDev& bp, hipStream_t st) {
+                            int32_t* pred_next, const BudgetDev& bp, hipStream_t st, bool ema_update, float alpha,
+                            int first) {
   const int N = s.n_blocks, rows = s.batch * s.n_kv_heads;
   const dim3 grid((unsigned)(2 * rows));
+  float* e = const_cast<float*>(ema);   // written only with ema_update
 #define PRR_PAIR(NT, KPT)                                                                                          \
-  topk_pair_kernel<NT, KPT><<<grid, NT, 0, st>>>(scores, k, sel, ema, kp, pred_next, rows, N, s.sink_blocks,      \
-                                                 s.local_blocks, bp)
+  (ema_update ? topk_pair_kernel<NT, KPT, true> : topk_pair_kernel<NT, KPT, false>)<<<grid, NT, 0, st>>>(         \
+      scores, k, sel, e, alpha, first, kp, pred_next, rows, N, s.sink_blocks, s.local_blocks, bp)
   trace_begin(PRR_KERNEL_SELECT_TOPK, st);
   if (N <= 4096) {
     switch (topk_kpt_nt(N, 512)) {
