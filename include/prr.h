@@ -235,9 +235,11 @@ typedef enum {
   PRR_MODE_ONE_STREAM = 1,  /* stream_sel: speculate -> score_select -> repair_merge -> ema_predict                */
   PRR_MODE_TWO_STREAM = 2,  /* stream_spec: speculate || stream_sel: score_select; after the join, repair_merge
                                -> ema_predict on stream_sel (one fork and one join per step)                    */
-  PRR_MODE_FUSED = 3,       /* stream_sel only. batch * n_kv_heads >= 128: speculate -> score (+ EMA update) ->
-                               one launch of top-K workgroups selecting T and P_{t+1} -> repair_merge (the
-                               hits' records merged, the missed blocks attended). Otherwise, top_k <= 32:
+  PRR_MODE_FUSED = 3,       /* stream_sel only. batch * n_kv_heads >= 128: speculate -> score -> one launch of
+                               top-K workgroups selecting T and P_{t+1}, the latter updating the EMA first (up
+                               to 8192 blocks; beyond, the scoring pass updates it and the selection runs by
+                               segments) -> repair_merge (the hits' records merged, the missed blocks
+                               attended). Otherwise, top_k <= 32:
                                score (+ EMA update) -> one launch selecting T and P_{t+1}, speculating over P_t
                                and attending T minus P_t per row -> merge. Otherwise: score (+ EMA update) ->
                                select_speculate (T, P_{t+1}, speculation over P_t; rows of more than 8192
