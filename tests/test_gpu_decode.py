@@ -153,6 +153,21 @@ def test_modes_agree(name):
             assert np.all(b["nm"] == w.top_k)
 
 
+@pytest.mark.parametrize("name", ["paged_wide", "llama3_8b_32k", "million_token", "tiny_f32_4k"])
+def test_ema_identical_in_every_mode(name):
+    """The EMA update runs in the scoring pass, in the selection launch's prediction workgroups (many rows) or in a
+    prediction launch of its own (one and two streams), always as e = fma(alpha, e, (1 - alpha) s): after every step
+    the EMA is bitwise the same in each mode."""
+    w = wide_paged() if name == "paged_wide" else small(name)
+    kp = max(w.k_spec) or w.top_k
+    print(f"[case] EMA across modes {name} K'={kp}", flush=True)
+    ref = run_layer(w, gap_inputs(w), kp, "prr_1stream", check=False)
+    for mode in ("prr_fused", "prr_2stream"):
+        got = run_layer(w, gap_inputs(w), kp, mode, check=False)
+        for t, (a, b) in enumerate(zip(ref, got)):
+            assert np.array_equal(a["ema"], b["ema"]), (mode, t)
+
+
 def test_ema_state_save_restore():
     """The EMA vector and the next predicted set are the only cross-step state: restoring them into a fresh layer
     reproduces the remaining predicted sets and outputs exactly."""
