@@ -30,12 +30,13 @@ HIP_KERNELS = {("prr_fused", "score"): "score_kernel (with the EMA update)",
                                              "(rows of more than 8192 blocks), select_missed_kernel (K <= 32, also "
                                              "the missed blocks), topk_pair_kernel (>= 128 rows; the speculation "
                                              "has its own launch)",
-               ("prr_fused", "repair"): "repair_kernel + finalize_kernel",
+               ("prr_fused", "repair"): "repair_kernel + finalize_kernel (repair_kernel alone where one workgroup "
+                                        "per row writes the output)",
                ("prr_fused", "finalize"): "merge_hits_kernel or finalize_kernel",
                ("prr_fused", "speculate"): "speculate_kernel",
-               ("serialized", "repair"): "repair_kernel + finalize_kernel",
-               ("prr_1stream", "repair"): "repair_kernel + finalize_kernel",
-               ("prr_2stream", "repair"): "repair_kernel + finalize_kernel"}
+               ("serialized", "repair"): "repair_kernel (+ finalize_kernel)",
+               ("prr_1stream", "repair"): "repair_kernel (+ finalize_kernel)",
+               ("prr_2stream", "repair"): "repair_kernel (+ finalize_kernel)"}
 
 
 def parse():

@@ -92,8 +92,8 @@ __device__ void finalize_head(const float* __restrict__ recs, int n_rec, int h, 
   }
 }
 
-template <int DT, int G, bool P16>
-__global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8_t* __restrict__ q,
+template <int DT, int G, bool P16, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : (G >= 8 ? 2 : 3)) void repair_kernel(const uint8_t* __restrict__ q,
                                                      const uint8_t* __restrict__ kc,
                                                      const uint8_t* __restrict__ vc,
                                                      const int32_t* __restrict__ table,
@@ -101,18 +101,20 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8
                                                      const int32_t* __restrict__ pred, int k_spec,
                                                      const float* __restrict__ partials, float* __restrict__ ws_rec,
                                                      int32_t* __restrict__ ws_miss, int Hq, int Hkv, int N, int bs,
-                                                     int page, int pps, float qscale, int epw, int last_len) {
+                                                     int page, int pps, float qscale, int epw, int last_len,
+                                                     float* __restrict__ out, int32_t* __restrict__ n_missed) {
   using W = Tile<DT, G>;
+  constexpr int NT = NW * 64;
   constexpr int D = W::D;
   constexpr int RF = rec_floats(G, D);
   constexpr int ML = rec_ml(G);
   constexpr int kPredLds = 2048;   // predicted sets up to this size are searched in LDS
-  __shared__ float s_ml[4][2 * G];
-  __shared__ float s_o[4 * G * D];
-  __shared__ int s_miss[4];
+  __shared__ float s_ml[NW][2 * G];
+  __shared__ float s_o[NW * G * D];
+  __shared__ int s_miss[NW];
   __shared__ int32_t s_pred[kPredLds];
-  __shared__ int32_t s_mid[4][8];   // missed block ids of the current group of entries, per wave
-  __shared__ int s_kf[4];           // per wave: the first empty (negative) slot of P it saw
+  __shared__ int32_t s_mid[NW][8];   // missed block ids of the current group of entries, per wave
+  __shared__ int s_kf[NW];           // per wave: the first empty (negative) slot of P it saw
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t rowid = blockIdx.y;
   const int rec = blockIdx.x;
@@ -126,7 +128,7 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8
   const bool pred_lds = k_spec <= kPredLds;
   int kneg = k_spec;
   if (prow)
-    for (int i = threadIdx.x; i < k_spec; i += 256) {
+    for (int i = threadIdx.x; i < k_spec; i += NT) {
       const int32_t v = prow[i];
       if (pred_lds) s_pred[i] = v;
       if (v < 0) kneg = min(kneg, i);
@@ -139,9 +141,11 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8
   const int32_t* trow = table + (int64_t)b * pps;
   __syncthreads();
   // slots from the first empty one on never match (speculation may have skipped them), as in the row-wise repair
-  const int kf = min(min(s_kf[0], s_kf[1]), min(s_kf[2], s_kf[3]));
+  int kf = s_kf[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) kf = min(kf, s_kf[w]);
   int misses = 0;
-  const int j0 = (rec * 4 + wave) * epw;
+  const int j0 = (rec * NW + wave) * epw;
   const int j1 = min(top_k, j0 + epw);
   for (int jb = j0; jb < j1; jb += 8) {
     // look up up to 8 entries: merge the speculated ones, collect the missed ones
@@ -177,26 +181,43 @@ __global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8
     s_o[wave * G * D + (f / W::VE) * D + st.col * W::VE + (f % W::VE)] = folded[i];
   }
   __syncthreads();
-  // merge the 4 wave states into this workgroup's record
+  // merge the wave states: into this workgroup's record, or (one workgroup per row) straight into the output
   float* my = ws_rec + (rowid * n_rec + rec) * (int64_t)RF;
-  for (int f = threadIdx.x; f < G * D; f += 256) {
+  for (int f = threadIdx.x; f < G * D; f += NT) {
     const int h = f / D;
-    const float M = fmaxf(fmaxf(s_ml[0][h], s_ml[1][h]), fmaxf(s_ml[2][h], s_ml[3][h]));
+    float M = s_ml[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h]);
     float o = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) o += s_o[w * G * D + f] * exp2f(s_ml[w][h] - M);
-    my[ML + f] = o;
+    for (int w = 0; w < NW; ++w) o += s_o[w * G * D + f] * exp2f(s_ml[w][h] - M);
+    if (out) {
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) L += s_ml[w][G + h] * exp2f(s_ml[w][h] - M);
+      out[((int64_t)b * Hq + (int64_t)g * G) * D + f] = o / L;
+    } else {
+      my[ML + f] = o;
+    }
   }
-  if (threadIdx.x < G) {
+  if (!out && threadIdx.x < G) {
     const int h = threadIdx.x;
-    const float M = fmaxf(fmaxf(s_ml[0][h], s_ml[1][h]), fmaxf(s_ml[2][h], s_ml[3][h]));
+    float M = s_ml[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h]);
     float L = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) L += s_ml[w][G + h] * exp2f(s_ml[w][h] - M);
+    for (int w = 0; w < NW; ++w) L += s_ml[w][G + h] * exp2f(s_ml[w][h] - M);
     my[h] = M;
     my[G + h] = L;
   }
-  if (threadIdx.x == 0) ws_miss[rowid * n_rec + rec] = s_miss[0] + s_miss[1] + s_miss[2] + s_miss[3];
+  if (threadIdx.x == 0) {
+    int m = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m += s_miss[w];
+    if (out) n_missed[rowid] = m;
+    else ws_miss[rowid * n_rec + rec] = m;
+  }
 }
 
 // Merge each row's records into the normalised output: one workgroup per (row, head); the head-0 workgroup also sums
@@ -296,6 +317,12 @@ static void spec_launch(const prr_shape& s, const void* q, const void* kc, const
   trace_end(PRR_KERNEL_SPECULATE, st);
 }
 
+// One 8-wave workgroup per row that writes the output itself (no merge launch) where the row's true set fits it and
+// the rows alone fill the chip: one workgroup per CU at these register counts.
+static bool repair_row_wg(const prr_shape& s, int top_k, int epw) {
+  return (int64_t)s.batch * s.n_kv_heads >= 256 && top_k <= 8 * epw;
+}
+
 template <int DT, int G>
 static void repair_launch(const prr_shape& s, const void* q, const void* kc, const void* vc, const int32_t* table,
                           const int32_t* sel, int top_k, const int32_t* pred, int k_spec, const float* partials,
@@ -306,12 +333,23 @@ static void repair_launch(const prr_shape& s, const void* q, const void* kc, con
   RepairWs ws;
   ws_layout(s, top_k, workspace, &ws);
   const float qscale = s.softmax_scale * kLog2e;
+  const bool p16 = p16_path(s);
+  if (repair_row_wg(s, top_k, epw)) {
+    trace_begin(PRR_KERNEL_REPAIR, st);
+    auto kern = p16 ? repair_kernel<DT, G, true, 8> : repair_kernel<DT, G, false, 8>;
+    kern<<<dim3(1u, (unsigned)rows), dim3(512), 0, st>>>(
+        static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, sel,
+        top_k, pred, k_spec, partials, ws.rec, ws.miss, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size,
+        s.page_size, s.pages_per_seq, qscale, epw, last_block_len(s), out, n_missed);
+    trace_end(PRR_KERNEL_REPAIR, st);
+    return;
+  }
   trace_begin(PRR_KERNEL_REPAIR, st);
-  auto kern = p16_path(s) ? repair_kernel<DT, G, true> : repair_kernel<DT, G, false>;
+  auto kern = p16 ? repair_kernel<DT, G, true, 4> : repair_kernel<DT, G, false, 4>;
   kern<<<dim3((unsigned)nrec, (unsigned)rows), dim3(256), 0, st>>>(
       static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, sel,
       top_k, pred, k_spec, partials, ws.rec, ws.miss, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size,
-      s.page_size, s.pages_per_seq, qscale, epw, last_block_len(s));
+      s.page_size, s.pages_per_seq, qscale, epw, last_block_len(s), nullptr, nullptr);
   trace_end(PRR_KERNEL_REPAIR, st);
   constexpr int D = 16 * Vec<DT>::n;
   trace_begin(PRR_KERNEL_FINALIZE, st);
