@@ -7,7 +7,8 @@
 //
 // repair_kernel: grid (records per row, rows). Each wave walks `epw` consecutive entries of the true set T; an entry
 // found in the predicted set P merges its speculated record, a missed entry is computed from the KV cache; entries
-// of P outside T are never read. The 4 wave states merge in LDS into one record per workgroup.
+// of P outside T are never read. The wave states merge in LDS into one record per 4-wave workgroup, or, with one
+// 8-wave workgroup per row, into the row's normalised output.
 // finalize_kernel: one workgroup per (row, head) merges that head's part of the row's records, normalises, and
 // writes out = O / l; the missed count is summed alongside.
 #include "attn_wave.h"
