@@ -114,11 +114,13 @@ def test_two_stream_delays_do_not_change_results(name):
 
 
 @pytest.mark.parametrize("k_spec,extra", [(12, {}), (20, {}), (20, {"sink_blocks": 1, "local_blocks": 3}),
-                                          (20, {"scorer": "mean"})])
+                                          (20, {"scorer": "mean"}),
+                                          (20, {"batch": 64, "top_k": 64, "ctx": 16 * 100 - 3})])
 def test_decode_many_rows_vs_oracle(k_spec, extra):
     """A batch of 136 rows (17 sequences x 8 KV heads, a partly filled last block): the fused step's many-row path
-    (speculation in its own launch, then scores with the EMA, the selection of T and P_{t+1}, the repair), also with
-    forced sink and local blocks and with the mean-key scorer; every step against the oracle."""
+    (speculation in its own launch, then the scores, the selection of T and of P_{t+1} with the EMA update, the
+    repair), also with forced sink and local blocks and with the mean-key scorer; and 512 rows with K = 64, where one
+    repair workgroup per row writes the output itself; every step against the oracle."""
     w = wide_paged(k_spec=(k_spec,), **extra)
     print(f"[case] decode many rows B={w.batch} K'={k_spec} {extra}", flush=True)
     inp = gap_inputs(w)
