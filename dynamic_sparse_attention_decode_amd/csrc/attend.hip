@@ -7,8 +7,9 @@
 //
 // repair_kernel: grid (records per row, rows). Each wave walks `epw` consecutive entries of the true set T; an entry
 // found in the predicted set P merges its speculated record, a missed entry is computed from the KV cache; entries
-// of P outside T are never read. The wave states merge in LDS into one record per 4-wave workgroup, or, with one
-// 8-wave workgroup per row, into the row's normalised output.
+// of P outside T are never read. The 4 wave states merge in LDS into one record per workgroup.
+// repair_row_kernel: one 8-wave workgroup per row where the rows fill the chip; T is split into hits and missed
+// blocks first, the waves take even shares of both, and the workgroup writes the row's normalised output.
 // finalize_kernel: one workgroup per (row, head) merges that head's part of the row's records, normalises, and
 // writes out = O / l; the missed count is summed alongside.
 #include "attn_wave.h"
@@ -93,8 +94,8 @@ __device__ void finalize_head(const float* __restrict__ recs, int n_rec, int h, 
   }
 }
 
-template <int DT, int G, bool P16, int NW>
-__global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : (G >= 8 ? 2 : 3)) void repair_kernel(const uint8_t* __restrict__ q,
+template <int DT, int G, bool P16>
+__global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8_t* __restrict__ q,
                                                      const uint8_t* __restrict__ kc,
                                                      const uint8_t* __restrict__ vc,
                                                      const int32_t* __restrict__ table,
@@ -102,10 +103,9 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : (G >= 8 ? 2 : 3)) void repai
                                                      const int32_t* __restrict__ pred, int k_spec,
                                                      const float* __restrict__ partials, float* __restrict__ ws_rec,
                                                      int32_t* __restrict__ ws_miss, int Hq, int Hkv, int N, int bs,
-                                                     int page, int pps, float qscale, int epw, int last_len,
-                                                     float* __restrict__ out, int32_t* __restrict__ n_missed) {
+                                                     int page, int pps, float qscale, int epw, int last_len) {
   using W = Tile<DT, G>;
-  constexpr int NT = NW * 64;
+  constexpr int NW = 4, NT = NW * 64;
   constexpr int D = W::D;
   constexpr int RF = rec_floats(G, D);
   constexpr int ML = rec_ml(G);
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : (G >= 8 ? 2 : 3)) void repai
     s_o[wave * G * D + (f / W::VE) * D + st.col * W::VE + (f % W::VE)] = folded[i];
   }
   __syncthreads();
-  // merge the wave states: into this workgroup's record, or (one workgroup per row) straight into the output
+  // merge the wave states into this workgroup's record
   float* my = ws_rec + (rowid * n_rec + rec) * (int64_t)RF;
   for (int f = threadIdx.x; f < G * D; f += NT) {
     const int h = f / D;
@@ -192,16 +192,9 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : (G >= 8 ? 2 : 3)) void repai
     float o = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) o += s_o[w * G * D + f] * exp2f(s_ml[w][h] - M);
-    if (out) {
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) L += s_ml[w][G + h] * exp2f(s_ml[w][h] - M);
-      out[((int64_t)b * Hq + (int64_t)g * G) * D + f] = o / L;
-    } else {
-      my[ML + f] = o;
-    }
+    my[ML + f] = o;
   }
-  if (!out && threadIdx.x < G) {
+  if (threadIdx.x < G) {
     const int h = threadIdx.x;
     float M = s_ml[0][h];
 #pragma unroll
@@ -216,9 +209,127 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : (G >= 8 ? 2 : 3)) void repai
     int m = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) m += s_miss[w];
-    if (out) n_missed[rowid] = m;
-    else ws_miss[rowid * n_rec + rec] = m;
+    ws_miss[rowid * n_rec + rec] = m;
   }
+}
+
+// One 8-wave workgroup per row (K <= kRowMaxK): the row's true set T is looked up in the predicted set P once, by
+// one thread per entry (bisection when P is ascending, as the selection writes it; a linear search otherwise), and
+// split into a list of the hits' slots and a list of the missed blocks with a workgroup prefix count. Each wave then
+// takes an even share of the missed blocks (one pipelined run) and of the hits (record merges), so no wave carries
+// more than its share of either; the wave states merge in LDS into the row's normalised output.
+constexpr int kRowMaxK = 128;
+
+template <int DT, int G, bool P16>
+__global__ __launch_bounds__(512, 1) void repair_row_kernel(const uint8_t* __restrict__ q,
+                                                            const uint8_t* __restrict__ kc,
+                                                            const uint8_t* __restrict__ vc,
+                                                            const int32_t* __restrict__ table,
+                                                            const int32_t* __restrict__ sel, int top_k,
+                                                            const int32_t* __restrict__ pred, int k_spec,
+                                                            const float* __restrict__ partials, int Hq, int Hkv,
+                                                            int N, int bs, int page, int pps, float qscale,
+                                                            int last_len, float* __restrict__ out,
+                                                            int32_t* __restrict__ n_missed) {
+  using W = Tile<DT, G>;
+  constexpr int NW = 8, NT = 512;
+  constexpr int D = W::D;
+  constexpr int kPredLds = 2048;
+  __shared__ float s_ml[NW][2 * G];
+  __shared__ float s_o[NW * G * D];
+  __shared__ int32_t s_pred[kPredLds];
+  __shared__ int32_t s_hit[kRowMaxK];   // predicted slots of the hits, in T order
+  __shared__ int32_t s_mid[kRowMaxK];   // missed block ids, in T order
+  __shared__ int s_cnt[2][2];           // per half of T (waves 0 and 1): hits in it
+  __shared__ int s_kf, s_unsorted;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int64_t rowid = blockIdx.x;
+  const int b = (int)(rowid / Hkv), g = (int)(rowid % Hkv);
+  const int32_t* srow = sel + rowid * top_k;
+  const int32_t* prow = pred ? pred + rowid * k_spec : nullptr;
+  const uint8_t* part_row =
+      partials ? reinterpret_cast<const uint8_t*>(partials) + rowid * k_spec * W::kSpecRecBytes : nullptr;
+  const bool pred_lds = k_spec <= kPredLds;
+  if (t == 0) { s_kf = prow ? k_spec : 0; s_unsorted = 0; }
+  __syncthreads();
+  if (prow)
+    for (int i = t; i < k_spec; i += NT) {
+      const int32_t v = prow[i];
+      if (pred_lds) s_pred[i] = v;
+      if (v < 0) atomicMin(&s_kf, i);
+    }
+  W st;
+  st.init(lane);
+  st.load_q(q + ((int64_t)b * Hq + (int64_t)g * G) * kRowBytes, qscale);
+  const int32_t* trow = table + (int64_t)b * pps;
+  __syncthreads();
+  // slots from the first empty one on never match (speculation may have skipped them)
+  const int kf = s_kf;
+  if (pred_lds)
+    for (int i = t; i + 1 < kf; i += NT)
+      if (s_pred[i] >= s_pred[i + 1]) s_unsorted = 1;
+  __syncthreads();
+  const bool sorted = pred_lds && s_unsorted == 0;
+  // one thread per entry of T (threads 0 .. K-1 are waves 0 and 1)
+  int n = 0, slot = -1;
+  if (t < top_k) {
+    n = min(max(srow[t], 0), N - 1);
+    if (sorted) {
+      int lo = 0, hi = kf;   // first index with s_pred[idx] >= n
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pred[mid] < n) lo = mid + 1; else hi = mid;
+      }
+      if (lo < kf && s_pred[lo] == n) slot = lo;
+    } else {
+      for (int i = 0; i < kf; ++i)
+        if ((pred_lds ? s_pred[i] : prow[i]) == n) { slot = i; break; }
+    }
+  }
+  const unsigned long long hm = __ballot(t < top_k && slot >= 0);
+  const unsigned long long vm = __ballot(t < top_k);
+  if (wave < 2 && lane == 0) { s_cnt[wave][0] = __popcll(hm); s_cnt[wave][1] = __popcll(vm & ~hm); }
+  __syncthreads();
+  const int nh = s_cnt[0][0] + s_cnt[1][0], nm = s_cnt[0][1] + s_cnt[1][1];
+  if (t < top_k) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const int hb = (wave == 1 ? s_cnt[0][0] : 0) + __popcll(hm & below);
+    const int mb = (wave == 1 ? s_cnt[0][1] : 0) + __popcll(vm & ~hm & below);
+    if (slot >= 0) s_hit[hb] = slot; else s_mid[mb] = n;
+  }
+  __syncthreads();
+  // even shares: missed blocks [m0, m1) and hits [h0, h1) of this wave
+  const int m0 = wave * nm / NW, m1 = (wave + 1) * nm / NW;
+  const int h0 = wave * nh / NW, h1 = (wave + 1) * nh / NW;
+  constexpr int kRun = 8;   // missed blocks per pipelined run (at most 64 chunks)
+  for (int mb = m0; mb < m1; mb += kRun)
+    run_blocks<P16>(st, min(kRun, m1 - mb), [&](int i) { return s_mid[mb + i]; }, [](int) {}, kc, vc, trow, bs,
+                    page, Hkv, g, N, last_len);
+  for (int i = h0; i < h1; ++i) st.merge_spec_record(part_row + (int64_t)s_hit[i] * W::kSpecRecBytes);
+  float folded[W::NK];
+  st.fold(folded);
+  st.store_ml(&s_ml[wave][0]);
+#pragma unroll
+  for (int i = 0; i < W::NK; ++i) {
+    const int f = st.row * W::NK + i;
+    s_o[wave * G * D + (f / W::VE) * D + st.col * W::VE + (f % W::VE)] = folded[i];
+  }
+  __syncthreads();
+  for (int f = t; f < G * D; f += NT) {
+    const int h = f / D;
+    float M = s_ml[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_ml[w][h]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float c = exp2f(s_ml[w][h] - M);
+      o += s_o[w * G * D + f] * c;
+      L += s_ml[w][G + h] * c;
+    }
+    out[((int64_t)b * Hq + (int64_t)g * G) * D + f] = o / L;
+  }
+  if (t == 0) n_missed[rowid] = nm;
 }
 
 // Merge each row's records into the normalised output: one workgroup per (row, head); the head-0 workgroup also sums
@@ -319,9 +430,10 @@ static void spec_launch(const prr_shape& s, const void* q, const void* kc, const
 }
 
 // One 8-wave workgroup per row that writes the output itself (no merge launch) where the row's true set fits it and
-// the rows alone fill the chip: one workgroup per CU at these register counts.
+// the rows alone fill the chip: one workgroup per CU at these register counts (paged batch, same-box A/B: with the
+// wave-per-16-entries split 210.1 -> 203.5 us, with even shares of the hits and the missed blocks 203.3 -> 199.0).
 static bool repair_row_wg(const prr_shape& s, int top_k, int epw) {
-  return (int64_t)s.batch * s.n_kv_heads >= 256 && top_k <= 8 * epw;
+  return (int64_t)s.batch * s.n_kv_heads >= 256 && top_k <= 8 * epw && top_k <= kRowMaxK;
 }
 
 template <int DT, int G>
@@ -337,20 +449,20 @@ static void repair_launch(const prr_shape& s, const void* q, const void* kc, con
   const bool p16 = p16_path(s);
   if (repair_row_wg(s, top_k, epw)) {
     trace_begin(PRR_KERNEL_REPAIR, st);
-    auto kern = p16 ? repair_kernel<DT, G, true, 8> : repair_kernel<DT, G, false, 8>;
-    kern<<<dim3(1u, (unsigned)rows), dim3(512), 0, st>>>(
+    auto kern = p16 ? repair_row_kernel<DT, G, true> : repair_row_kernel<DT, G, false>;
+    kern<<<dim3((unsigned)rows), dim3(512), 0, st>>>(
         static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, sel,
-        top_k, pred, k_spec, partials, ws.rec, ws.miss, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size,
-        s.page_size, s.pages_per_seq, qscale, epw, last_block_len(s), out, n_missed);
+        top_k, pred, k_spec, partials, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size,
+        s.pages_per_seq, qscale, last_block_len(s), out, n_missed);
     trace_end(PRR_KERNEL_REPAIR, st);
     return;
   }
   trace_begin(PRR_KERNEL_REPAIR, st);
-  auto kern = p16 ? repair_kernel<DT, G, true, 4> : repair_kernel<DT, G, false, 4>;
+  auto kern = p16 ? repair_kernel<DT, G, true> : repair_kernel<DT, G, false>;
   kern<<<dim3((unsigned)nrec, (unsigned)rows), dim3(256), 0, st>>>(
       static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, sel,
       top_k, pred, k_spec, partials, ws.rec, ws.miss, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size,
-      s.page_size, s.pages_per_seq, qscale, epw, last_block_len(s), nullptr, nullptr);
+      s.page_size, s.pages_per_seq, qscale, epw, last_block_len(s));
   trace_end(PRR_KERNEL_REPAIR, st);
   constexpr int D = 16 * Vec<DT>::n;
   trace_begin(PRR_KERNEL_FINALIZE, st);
