@@ -144,7 +144,8 @@ def test_select_speculate_budget(policy, n_blocks, with_ws, forced):
 
 @pytest.mark.parametrize("mode", ["prr_fused", "prr_1stream", "prr_2stream"])
 @pytest.mark.parametrize("policy", ["misses", "confidence"])
-@pytest.mark.parametrize("name", ["tiny_f32_4k", "llama3_8b_32k", "paged_b32_64k", "million_token", "paged_wide"])
+@pytest.mark.parametrize("name", ["tiny_f32_4k", "llama3_8b_32k", "paged_b32_64k", "million_token", "paged_wide",
+                                  "paged_512"])
 def test_decode_with_budget(name, policy, mode):
     """Whole decode runs with a budget: every step's selection and output against the oracle (the output is
     attention over the true set whatever was predicted), the missed count = |T minus the filled part of P_t|, and
@@ -152,6 +153,8 @@ def test_decode_with_budget(name, policy, mode):
     counts; the sets' sizes vary by row within [k_min, k_spec]."""
     if name == "paged_wide":   # 136 rows: the fused step's many-row path
         w = wide_paged()
+    elif name == "paged_512":   # 512 rows, K = 64: one repair workgroup per row, with -1-padded predicted sets
+        w = wide_paged(batch=64, top_k=64, ctx=16 * 100 - 3, k_spec=(96,))
     else:
         w = small(name)
     kp = min(w.n_blocks, max(max(w.k_spec), w.top_k + w.top_k // 2))   # room above K for the sizes to vary
