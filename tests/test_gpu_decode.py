@@ -266,6 +266,21 @@ def test_dtypes_and_group_sizes(dtype, G):
         run_layer(w, inp, max(w.k_spec), mode, ov=ov)
 
 
+@pytest.mark.parametrize("dtype,G", [("f32", 4), ("f16", 8), ("bf16", 1)])
+def test_row_workgroup_repair_dtypes_and_groups(dtype, G):
+    """256 rows with K = 124 of 140 blocks: the repair takes one 8-wave workgroup per row that splits T into hits and
+    missed blocks and writes the output itself; other storage dtypes and group sizes than the paged batch's, in the
+    fused PRR step and the serialized one, against the oracle at every step."""
+    from dynamic_sparse_attention_decode_amd.inputs import Workload
+    D = 64 if dtype == "f32" else 128
+    w = Workload(f"rows256_{dtype}_g{G}", 128, 2 * G, 2, D, 16 * 140 - 5, 16, 16, 124, (130,), 0.8, 0.9, 3, 6,
+                 shuffle_pages=True, dtype=dtype, seed=20261203 + 29 * G)
+    inp = gap_inputs(w)
+    for mode in ("prr_fused", "serialized"):
+        print(f"[case] {w.name} {mode}", flush=True)
+        run_layer(w, inp, 130, mode, ov=OracleView(inp))
+
+
 def test_all_blocks_selected_is_dense_attention():
     """K = N (every block selected) equals dense attention over the whole context, in the fused PRR step."""
     w = small("tiny_f32_4k").replace(top_k=128, k_spec=(128,), steps=3)
