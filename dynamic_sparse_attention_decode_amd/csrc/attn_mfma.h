@@ -46,7 +46,6 @@ struct AttnWaveM {
   static constexpr int NK = NV / 4;
   static_assert(DT != kF32, "matrix-core tile is for 16-bit storage");
   static constexpr bool kPipelined = G <= 4;   // two chunk buffers fit the register budget
-  static constexpr int kRecBatch = G >= 8 ? 2 : 4;   // record loads in flight
   static constexpr int64_t kSpecRecBytes = spec_rec_bytes(kBF16, G, D);   // speculation records: O in bf16
 
   uint4 qb[4];        // B operand: query head l%16 (zero beyond G), dims 8*(l/16) + 32*kk

@@ -30,7 +30,6 @@ struct AttnWave {
 
   static constexpr bool kPipelined = G <= 4;   // two chunk buffers fit the register budget
   static constexpr int64_t kSpecRecBytes = spec_rec_bytes(kF32, G, 16 * Vec<DT>::n);   // fp32 records
-  static constexpr int kRecBatch = G >= 8 ? 2 : 4;   // record loads in flight
 
   float q[G][VE];
   float m[G];      // running max, log2 units, uniform across the wave
@@ -319,22 +318,6 @@ __device__ inline void run_blocks(W& st, int cnt, IdFn&& id_of, DoneFn&& done, c
       load(ca, k);
       compute(ca, k);
     }
-  }
-}
-
-// Merge `cnt` stored records (wave-uniform addresses from rec_of(i)) into a wave's state, several record loads in
-// flight at a time (four, or two for the 8-head tile).
-template <typename W, typename RecFn>
-__device__ inline void run_records(W& st, int cnt, RecFn&& rec_of) {
-  constexpr int R = W::kRecBatch;
-  for (int i = 0; i < cnt; i += R) {
-    typename W::Rec r[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u)
-      if (i + u < cnt) st.load_record(r[u], rec_of(i + u));
-#pragma unroll
-    for (int u = 0; u < R; ++u)
-      if (i + u < cnt) st.apply_record(r[u]);
   }
 }
 

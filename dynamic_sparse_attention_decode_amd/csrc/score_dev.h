@@ -164,8 +164,13 @@ __device__ inline void score_any(int scorer, int bx, int bg, const uint8_t* __re
     score_chunk<DT, G, EMA>(bx, bg, q, summ, scores, Hq, Hkv, N, chunk, ema, alpha, first);
 }
 
-// Blocks per scoring workgroup: a multiple of 64 (one unrolled wave round), sized for about 2048 workgroups.
-inline int score_chunk_size(const prr_shape& s) {
+// Blocks per scoring workgroup, a multiple of one unrolled wave round (4 waves x 2 blocks x 8 loads in flight = 64).
+// Scores alone: one round per workgroup, so each issues its loads once and the dispatcher balances the many short
+// workgroups across the chip (paged batch, same-box A/B: 16384 workgroups of 64 blocks 81.4 us, against 86.2 us for
+// 2048 resident workgroups of 512 blocks and 85.5 us for 4096 of 256). With the EMA update, which adds a load and a
+// store per block, about 2048 workgroups (million-token layer: 128 blocks each, 25.4 us, against 27.3 us at 64).
+inline int score_chunk_size(const prr_shape& s, bool ema) {
+  if (!ema) return 64;
   const int64_t total = (int64_t)s.batch * s.n_kv_heads * s.n_blocks;
   const int chunk = (int)((total / 2048 + 63) / 64 * 64);
   return chunk < 64 ? 64 : chunk;

@@ -90,7 +90,7 @@ template <int DT, int G>
 static void score_launch(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema, float alpha,
                          int first, hipStream_t st) {
   const int rows = s.batch * s.n_kv_heads;
-  const int chunk = score_chunk_size(s);
+  const int chunk = score_chunk_size(s, ema != nullptr);
   const dim3 grid((unsigned)((s.n_blocks + chunk - 1) / chunk), (unsigned)rows), blk(256);
   const auto* qq = static_cast<const uint8_t*>(q);
   const auto* sm = static_cast<const uint8_t*>(summ);

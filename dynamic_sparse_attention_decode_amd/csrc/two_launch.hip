@@ -328,7 +328,7 @@ static void score_spec_launch(const prr_shape& s, const void* q, const void* sum
                               float alpha, int first, const void* kc, const void* vc, const int32_t* table,
                               const int32_t* pred, int k_spec, float* partials, hipStream_t st) {
   const int rows = s.batch * s.n_kv_heads;
-  const int chunk = score_chunk_size(s);
+  const int chunk = score_chunk_size(s, ema != nullptr);
   const int gx = (s.n_blocks + chunk - 1) / chunk;
   const int spw = k_spec > 0 ? spec_slots_per_wave(s, k_spec) : 1;
   const int wpr = (k_spec + spw - 1) / spw;
