@@ -7,9 +7,10 @@
 // busy and is bound by latency, so the speculative loads use bandwidth that would otherwise sit idle.
 //
 // Long rows (given candidate regions): seg_spec_kernel's first workgroups select the top-K of each segment of 2048
-// scores and the top-K' of each segment of the EMA, the rest speculate as the standalone speculation kernel does
-// (256-thread workgroups, several slots per wave); merge2_kernel then selects each row's T and P_{t+1} from the
-// segments' candidates (topk_dev.h).
+// scores and the top-K' of each segment of the EMA (in the decode step with a fixed budget they update that segment
+// of the EMA from the scores first), the rest speculate as the standalone speculation kernel does (256-thread
+// workgroups, several slots per wave); merge2_kernel then selects each row's T and P_{t+1} from the segments'
+// candidates (topk_dev.h).
 #include "attn_wave.h"
 #include "topk_dev.h"
 
@@ -70,7 +71,8 @@ __global__ __launch_bounds__(kSegSpecThreads, 3) void seg_spec_kernel(const floa
                                                            float* __restrict__ partials, int spw, int wpr,
                                                            int64_t spec_waves, int Hq, int Hkv, int N, int bs,
                                                            int page, int pps, float qscale, int rows, int last_len,
-                                                           int sink, int local, int Ke, TopkCand cu, float conf_c) {
+                                                           int sink, int local, int Ke, TopkCand cu, float conf_c,
+                                                           int ema_upd, float alpha, int first) {
   const int64_t r = blockIdx.x;
   if (r < n_seg_wg) {
     const int64_t job = r / S;
@@ -80,8 +82,13 @@ __global__ __launch_bounds__(kSegSpecThreads, 3) void seg_spec_kernel(const floa
                                               ct.key + job * ct.cap, ct.idx + job * ct.cap, sink, local);
     } else if (job < 2 * rows) {   // the EMA's top-Ke of the segment (Ke = K' or, for a confidence budget, K)
       const int64_t rr = job - rows;
-      topk_segment<kSegSpecThreads, 8, false>(ema + rr * N, nullptr, 0.f, 0, N, Ke, kSelSpecSeg, seg,
-                                              cp.key + rr * cp.cap, cp.idx + rr * cp.cap, sink, local);
+      if (ema_upd)   // update the segment's EMA from the scores first, then rank the updated values
+        topk_segment<kSegSpecThreads, 8, true>(scores + rr * N, const_cast<float*>(ema) + rr * N, alpha, first, N,
+                                               Ke, kSelSpecSeg, seg, cp.key + rr * cp.cap, cp.idx + rr * cp.cap,
+                                               sink, local);
+      else
+        topk_segment<kSegSpecThreads, 8, false>(ema + rr * N, nullptr, 0.f, 0, N, Ke, kSelSpecSeg, seg,
+                                                cp.key + rr * cp.cap, cp.idx + rr * cp.cap, sink, local);
     } else {   // a confidence budget's optimistic scores: the segment's top-K'
       const int64_t rr = job - 2 * rows;
       topk_segment<kSegSpecThreads, 8, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp_next, kSelSpecSeg, seg,
@@ -116,12 +123,13 @@ __global__ __launch_bounds__(NT) void merge2_kernel(TopkCand ct, int Ct, int K, 
     topk_merge_row<NT, KPT>(cp.key + rr * cp.cap, cp.idx + rr * cp.cap, Cp, Kp_next, pred_next + rr * Kp_next);
 }
 
+// ema_upd: the EMA-segment workgroups update the EMA from the scores (alpha, first) before they rank it.
 template <int DT, int G>
 static void seg_spec_launch(const prr_shape& s, const float* scores, int K, int32_t* sel, const float* ema,
                             int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                             const int32_t* table, const int32_t* pred, int k_spec, float* partials,
                             const TopkCand& ct, const TopkCand& cp, const TopkCand& cu, const BudgetDev& bp,
-                            hipStream_t st) {
+                            hipStream_t st, bool ema_upd = false, float alpha = 0.f, int first = 0) {
   const int rows = s.batch * s.n_kv_heads;
   const bool conf = kp_next > 0 && bp.policy == 2;
   const int ke = conf ? bp.top_k : kp_next;   // EMA candidates per segment: K for the confidence rule's theta
@@ -139,7 +147,8 @@ static void seg_spec_launch(const prr_shape& s, const float* scores, int K, int3
       scores, K, ema, kp_next, pt.S, n_seg_wg, ct, cp, static_cast<const uint8_t*>(q),
       static_cast<const uint8_t*>(kc), static_cast<const uint8_t*>(vc), table, pred, k_spec, partials, spw, wpr,
       spec_waves, s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size, s.page_size, s.pages_per_seq,
-      s.softmax_scale * kLog2e, rows, last_block_len(s), s.sink_blocks, s.local_blocks, ke, cu, bp.c);
+      s.softmax_scale * kLog2e, rows, last_block_len(s), s.sink_blocks, s.local_blocks, ke, cu, bp.c,
+      ema_upd ? 1 : 0, alpha, first);
   int cmax = pt.C;
   if (kp_next > 0) cmax = max(cmax, max(pp.C, conf ? pu.C : 0));
   const dim3 grid((unsigned)((kp_next > 0 ? 2 : 1) * rows));
@@ -189,6 +198,27 @@ static void select_spec_launch(const prr_shape& s, const float* scores, int K, i
   else
     PRR_SELSPEC(64);
 #undef PRR_SELSPEC
+}
+
+bool seg_ema_on(const prr_shape& s, int k, int kp_next) {
+  return kp_next > 0 && topk_split_on(s.n_blocks, k, kSelSpecSeg) && topk_split_on(s.n_blocks, kp_next, kSelSpecSeg);
+}
+
+prr_status launch_seg_spec_ema(const prr_shape& s, const float* scores, int k, int32_t* sel, float* ema, float alpha,
+                               int first, int kp_next, int32_t* pred_next, const void* q, const void* kc,
+                               const void* vc, const int32_t* table, const int32_t* pred, int k_spec, float* partials,
+                               void* cand_t, void* cand_p, hipStream_t stream) {
+  if (!seg_ema_on(s, k, kp_next) || !cand_t || !cand_p) {
+    set_error("select_speculate: the EMA update by segments needs rows split into segments");
+    return PRR_EUNSUPPORTED;
+  }
+  const TopkCand ct = topk_cand_at(s, cand_t), cp = topk_cand_at(s, cand_p);
+  const TopkCand cu{nullptr, nullptr, 0};
+  trace_begin(PRR_KERNEL_SELECT_TOPK, stream);
+  PRR_DISPATCH_DT_G(seg_spec_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
+                    partials, ct, cp, cu, BudgetDev{}, stream, true, alpha, first);
+  trace_end(PRR_KERNEL_SELECT_TOPK, stream);
+  return check_launch("select_speculate");
 }
 
 prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,

@@ -230,7 +230,7 @@ static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 // stand-in: the device address comes from hipGetSymbolAddress, taken once per device with that device current, and
 // only that address is ever passed to kernels. The workspace needs no initialisation, so nothing is cleared.
 constexpr size_t kScratchBytes = (size_t)PRR_SCRATCH_MAX_BYTES;
-__device__ __align__(256) uint8_t scratch[kScratchBytes];
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 constexpr int kMaxDevices = 64;
 static std::atomic<void*> g_scratch_addr[kMaxDevices];
@@ -613,6 +613,19 @@ static prr_status decode_step_impl(prr_step_ctx* ctx, const prr_shape* shape, co
                                    a->k_cache, a->v_cache, a->block_table, a->pred_cur, 0, a->partials, budget,
                                    a->workspace, s1));
     }
+    return prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
+                            kc, a->partials, a->out, a->n_missed, a->workspace, s1);
+  }
+  if (mode == PRR_MODE_FUSED && !budgeted && seg_ema_on(*shape, a->top_k, kn)) {
+    // Long rows with a fixed budget: the scoring pass writes the scores alone; the segment launch selects T's and
+    // P_{t+1}'s candidates, updates the EMA in its EMA-segment workgroups (which read it anyway) and speculates over
+    // P_t; then the merge of the candidates and the spread-out repair (million-token layer, same-box A/B over two
+    // runs each: 66.1 -> 65.3 us at K' = 384, 59.7 -> 58.2 us at K' = 128).
+    PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, nullptr, 0.f, 0, s1));
+    PRR_TRY(launch_seg_spec_ema(*shape, a->scores, a->top_k, a->sel_idx, a->ema, a->alpha, a->first_step ? 1 : 0, kn,
+                                a->pred_next, a->q, a->k_cache, a->v_cache, a->block_table,
+                                kc ? a->pred_cur : nullptr, kc, kc ? a->partials : nullptr,
+                                cand_region(*shape, a->workspace, 0), cand_region(*shape, a->workspace, 1), s1));
     return prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
                             kc, a->partials, a->out, a->n_missed, a->workspace, s1);
   }

@@ -145,6 +145,14 @@ prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, in
                               const int32_t* table, const int32_t* pred, int k_spec, float* partials,
                               hipStream_t stream, void* cand_t = nullptr, void* cand_p = nullptr,
                               void* cand_u = nullptr, const BudgetDev& bp = BudgetDev{});
+// Long rows with a fixed budget: the segment launch of the selection also updates the EMA from the scores, in its
+// EMA-segment workgroups (which read the EMA anyway), so the scoring pass writes the scores alone; then the merge
+// launch selects T and P_{t+1} from the candidates. seg_ema_on: whether this form applies (both sets split).
+bool seg_ema_on(const prr_shape& s, int k, int kp_next);
+prr_status launch_seg_spec_ema(const prr_shape& s, const float* scores, int k, int32_t* sel, float* ema, float alpha,
+                               int first, int kp_next, int32_t* pred_next, const void* q, const void* kc,
+                               const void* vc, const int32_t* table, const int32_t* pred, int k_spec, float* partials,
+                               void* cand_t, void* cand_p, hipStream_t stream);
 // The two-launch step: scores (+ EMA) with speculation, then selection with the row-wise repair and merge.
 bool two_launch_supported(const prr_shape& s, int top_k, int k_spec, int k_spec_next);
 prr_status launch_score_spec(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema,

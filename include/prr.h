@@ -243,7 +243,9 @@ typedef enum {
                                score (+ EMA update) -> one launch selecting T and P_{t+1}, speculating over P_t
                                and attending T minus P_t per row -> merge. Otherwise: score (+ EMA update) ->
                                select_speculate (T, P_{t+1}, speculation over P_t; rows of more than 8192
-                               blocks by segments and a merge) -> repair_merge, which with nothing to
+                               blocks by segments and a merge, where with a fixed budget the segments of the
+                               EMA are updated by the segment launch instead of the scoring pass) ->
+                               repair_merge, which with nothing to
                                speculate or predict are the serialized launches. The shapes each form supports
                                are the conditions of the separate calls; outside them the next form is taken.  */
   PRR_MODE_SERIALIZED_FUSED = 4  /* stream_sel only: score -> select_repair with no prediction (select-then-attend

@@ -155,19 +155,28 @@ def test_modes_agree(name):
             assert np.all(b["nm"] == w.top_k)
 
 
-@pytest.mark.parametrize("name", ["paged_wide", "llama3_8b_32k", "million_token", "tiny_f32_4k"])
+@pytest.mark.parametrize("name", ["paged_wide", "llama3_8b_32k", "million_token", "tiny_f32_4k", "million_long"])
 def test_ema_identical_in_every_mode(name):
-    """The EMA update runs in the scoring pass, in the selection launch's prediction workgroups (many rows) or in a
-    prediction launch of its own (one and two streams), always as e = fma(alpha, e, (1 - alpha) s): after every step
-    the EMA is bitwise the same in each mode."""
-    w = wide_paged() if name == "paged_wide" else small(name)
+    """The EMA update runs in the scoring pass, in the selection launch's prediction workgroups (many rows), in the
+    EMA-segment workgroups of the segment launch (long rows) or in a prediction launch of its own (one and two
+    streams), always as e = fma(alpha, e, (1 - alpha) s): after every
+    step the EMA, the selected and predicted sets and the missed counts are bitwise the same in each mode."""
+    if name == "paged_wide":
+        w = wide_paged()
+    elif name == "million_long":   # 12000 blocks per row: selection by segments and a merge
+        w = small("million_token").replace(ctx=32 * 12000 - 7, top_k=61, k_spec=(93,), steps=6)
+    else:
+        w = small(name)
     kp = max(w.k_spec) or w.top_k
-    print(f"[case] EMA across modes {name} K'={kp}", flush=True)
+    print(f"[case] EMA across modes {name} N={w.n_blocks} K'={kp}", flush=True)
     ref = run_layer(w, gap_inputs(w), kp, "prr_1stream", check=False)
     for mode in ("prr_fused", "prr_2stream"):
         got = run_layer(w, gap_inputs(w), kp, mode, check=False)
         for t, (a, b) in enumerate(zip(ref, got)):
             assert np.array_equal(a["ema"], b["ema"]), (mode, t)
+            assert np.array_equal(a["sel"], b["sel"]) and np.array_equal(a["nm"], b["nm"]), (mode, t)
+            if a["pred"] is not None:
+                assert np.array_equal(a["pred"], b["pred"]), (mode, t)
 
 
 def test_ema_state_save_restore():
