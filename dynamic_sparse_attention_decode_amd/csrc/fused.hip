@@ -30,23 +30,25 @@ __global__ __launch_bounds__(kSelSpecThreads) void select_spec_kernel(const floa
                                                            float* __restrict__ partials, int64_t spec_total, int Hq,
                                                            int Hkv, int N, int bs, int page, int pps, float qscale,
                                                            int rows, int last_len, int sink, int local,
-                                                           BudgetDev bp) {
+                                                           BudgetDev bp, int ema_upd, float alpha, int first) {
   const int64_t r = blockIdx.x;
   if (r < n_sel_wg) {
     const int64_t rr = r - rows;
+    const Force force{0, N, sink, local};
+    float* erow = const_cast<float*>(ema) + rr * N;
+    int32_t* prow = pred_next + rr * Kp_next;
     if (r < rows) {
-      topk_row<kSelSpecThreads, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, nullptr,
-                                            Force{0, N, sink, local});
-    } else if constexpr (KPT <= 16) {   // budgeted rows are routed elsewhere beyond 8192 blocks
-      if (bp.policy != 0)
-        predict_row<kSelSpecThreads, KPT, false>(scores + rr * N, const_cast<float*>(ema) + rr * N, 0.f, 0, N,
-                                                 Kp_next, bp, rr, pred_next + rr * Kp_next, Force{0, N, sink, local});
-      else
-        topk_row<kSelSpecThreads, KPT, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp_next, pred_next + rr * Kp_next,
-                                              nullptr, Force{0, N, sink, local});
+      topk_row<kSelSpecThreads, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, nullptr, force);
+    } else if (ema_upd) {   // fixed budget: update the row's EMA from the scores, then take its top-K'
+      topk_row<kSelSpecThreads, KPT, true>(scores + rr * N, erow, alpha, first, N, Kp_next, prow, nullptr, force);
     } else {
-      topk_row<kSelSpecThreads, KPT, false>(ema + rr * N, nullptr, 0.f, 0, N, Kp_next, pred_next + rr * Kp_next,
-                                            nullptr, Force{0, N, sink, local});
+      if constexpr (KPT <= 16) {   // budgeted rows are routed elsewhere beyond 8192 blocks
+        if (bp.policy != 0) {
+          predict_row<kSelSpecThreads, KPT, false>(scores + rr * N, erow, 0.f, 0, N, Kp_next, bp, rr, prow, force);
+          return;
+        }
+      }
+      topk_row<kSelSpecThreads, KPT, false>(erow, nullptr, 0.f, 0, N, Kp_next, prow, nullptr, force);
     }
     return;
   }
@@ -173,7 +175,7 @@ template <int DT, int G>
 static void select_spec_launch(const prr_shape& s, const float* scores, int K, int32_t* sel, const float* ema,
                                int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                                const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                               const BudgetDev& bp, hipStream_t st) {
+                               const BudgetDev& bp, hipStream_t st, bool ema_upd, float alpha, int first) {
   const int rows = s.batch * s.n_kv_heads;
   const int n_sel_wg = kp_next > 0 ? 2 * rows : rows;
   const int64_t spec_total = (int64_t)rows * k_spec;
@@ -189,7 +191,8 @@ static void select_spec_launch(const prr_shape& s, const float* scores, int K, i
                                                        table, pred, k_spec, partials, spec_total, s.n_q_heads,       \
                                                        s.n_kv_heads, s.n_blocks, s.block_size, s.page_size,          \
                                                        s.pages_per_seq, qs, rows, last_block_len(s),            \
-                                                       s.sink_blocks, s.local_blocks, bp)
+                                                       s.sink_blocks, s.local_blocks, bp, ema_upd ? 1 : 0, alpha,    \
+                                                       first)
   // values per thread: a few register sizes cover every row length (larger than needed is correct, just slower)
   if (s.n_blocks <= 4 * kSelSpecThreads)
     PRR_SELSPEC(4);
@@ -200,33 +203,17 @@ static void select_spec_launch(const prr_shape& s, const float* scores, int K, i
 #undef PRR_SELSPEC
 }
 
-bool seg_ema_on(const prr_shape& s, int k, int kp_next) {
-  return kp_next > 0 && topk_split_on(s.n_blocks, k, kSelSpecSeg) && topk_split_on(s.n_blocks, kp_next, kSelSpecSeg);
-}
-
-prr_status launch_seg_spec_ema(const prr_shape& s, const float* scores, int k, int32_t* sel, float* ema, float alpha,
-                               int first, int kp_next, int32_t* pred_next, const void* q, const void* kc,
-                               const void* vc, const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                               void* cand_t, void* cand_p, hipStream_t stream) {
-  if (!seg_ema_on(s, k, kp_next) || !cand_t || !cand_p) {
-    set_error("select_speculate: the EMA update by segments needs rows split into segments");
-    return PRR_EUNSUPPORTED;
-  }
-  const TopkCand ct = topk_cand_at(s, cand_t), cp = topk_cand_at(s, cand_p);
-  const TopkCand cu{nullptr, nullptr, 0};
-  trace_begin(PRR_KERNEL_SELECT_TOPK, stream);
-  PRR_DISPATCH_DT_G(seg_spec_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
-                    partials, ct, cp, cu, BudgetDev{}, stream, true, alpha, first);
-  trace_end(PRR_KERNEL_SELECT_TOPK, stream);
-  return check_launch("select_speculate");
-}
-
 prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
                               int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                               const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                              hipStream_t stream, void* cand_t, void* cand_p, void* cand_u, const BudgetDev& bp) {
+                              hipStream_t stream, void* cand_t, void* cand_p, void* cand_u, const BudgetDev& bp,
+                              bool ema_upd, float alpha, int first) {
   // nothing to speculate or predict: the selection alone, exactly as the serialized step runs it
   if (k_spec == 0 && kp_next == 0) return launch_topk(s, scores, nullptr, 0.f, 0, k, sel, stream, cand_t);
+  if (ema_upd && (kp_next == 0 || !ema || bp.policy != 0)) {
+    set_error("select_speculate: the EMA update in the selection launch needs a predicted set of fixed size");
+    return PRR_EINVAL;
+  }
   // long rows by segments (with the candidate regions): T, the EMA's candidates and, for a confidence budget, the
   // optimistic scores' candidates; the merge launch applies the budget
   const int ke = bp.policy == 2 ? bp.top_k : kp_next;
@@ -234,7 +221,8 @@ prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, in
                      (kp_next == 0 || (topk_split_on(s.n_blocks, kp_next, kSelSpecSeg) &&
                                        topk_split_on(s.n_blocks, ke, kSelSpecSeg)));
   // nothing to speculate: the true and predicted sets in one launch of top-K workgroups only
-  if (k_spec == 0 && !split) return launch_topk_pair(s, scores, k, sel, ema, kp_next, pred_next, bp, stream);
+  if (k_spec == 0 && !split)
+    return launch_topk_pair(s, scores, k, sel, ema, kp_next, pred_next, bp, stream, ema_upd, alpha, first);
   if (bp.policy != 0 && kp_next > 0 && !split && s.n_blocks > 16 * kSelSpecThreads) {
     // budgeted rows this long take their own launch of 1024-thread workgroups, which reads the EMA as it stands
     const prr_status st = launch_select_spec(s, scores, k, sel, nullptr, 0, nullptr, q, kc, vc, table, pred, k_spec,
@@ -247,10 +235,10 @@ prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, in
     const TopkCand ct = topk_cand_at(s, cand_t), cp = topk_cand_at(s, cand_p);
     const TopkCand cu = cand_u ? topk_cand_at(s, cand_u) : TopkCand{nullptr, nullptr, 0};
     PRR_DISPATCH_DT_G(seg_spec_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
-                      partials, ct, cp, cu, bp, stream);
+                      partials, ct, cp, cu, bp, stream, ema_upd, alpha, first);
   } else {
     PRR_DISPATCH_DT_G(select_spec_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
-                      partials, bp, stream);
+                      partials, bp, stream, ema_upd, alpha, first);
   }
   trace_end(PRR_KERNEL_SELECT_TOPK, stream);
   return check_launch("select_speculate");

@@ -606,36 +606,35 @@ static prr_status decode_step_impl(prr_step_ctx* ctx, const prr_shape* shape, co
       PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, nullptr, 0.f, 0, s1));
       PRR_TRY(launch_topk_pair(*shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, budget_dev(budget),
                                s1, true, a->alpha, a->first_step ? 1 : 0));
-    } else {   // long rows select by segments, from the EMA that the scoring pass updates
-      PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step,
-                        s1));
-      PRR_TRY(prr_select_speculate(shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q,
-                                   a->k_cache, a->v_cache, a->block_table, a->pred_cur, 0, a->partials, budget,
-                                   a->workspace, s1));
+    } else {   // long rows select by segments, whose EMA-segment workgroups update the EMA (as below 128 rows)
+      const bool sel_ema = kn > 0 && !budgeted;
+      PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 && !sel_ema ? a->ema : nullptr, a->alpha,
+                        a->first_step, s1));
+      PRR_TRY(launch_select_spec(*shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q,
+                                 a->k_cache, a->v_cache, a->block_table, nullptr, 0, nullptr, s1,
+                                 cand_region(*shape, a->workspace, 0), cand_region(*shape, a->workspace, 1),
+                                 cand_region(*shape, a->workspace, 2), kn > 0 ? budget_dev(budget) : BudgetDev{},
+                                 sel_ema, a->alpha, a->first_step ? 1 : 0));
     }
-    return prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
-                            kc, a->partials, a->out, a->n_missed, a->workspace, s1);
-  }
-  if (mode == PRR_MODE_FUSED && !budgeted && seg_ema_on(*shape, a->top_k, kn)) {
-    // Long rows with a fixed budget: the scoring pass writes the scores alone; the segment launch selects T's and
-    // P_{t+1}'s candidates, updates the EMA in its EMA-segment workgroups (which read it anyway) and speculates over
-    // P_t; then the merge of the candidates and the spread-out repair (million-token layer, same-box A/B over two
-    // runs each: 66.1 -> 65.3 us at K' = 384, 59.7 -> 58.2 us at K' = 128).
-    PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, nullptr, 0.f, 0, s1));
-    PRR_TRY(launch_seg_spec_ema(*shape, a->scores, a->top_k, a->sel_idx, a->ema, a->alpha, a->first_step ? 1 : 0, kn,
-                                a->pred_next, a->q, a->k_cache, a->v_cache, a->block_table,
-                                kc ? a->pred_cur : nullptr, kc, kc ? a->partials : nullptr,
-                                cand_region(*shape, a->workspace, 0), cand_region(*shape, a->workspace, 1), s1));
     return prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
                             kc, a->partials, a->out, a->n_missed, a->workspace, s1);
   }
   if (mode == PRR_MODE_FUSED) {
     // Otherwise the speculation rides in the latency-bound selection launch (long rows select in two launches,
-    // segments then a merge, through the workspace's candidate regions), then the spread-out repair.
-    PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step, s1));
-    PRR_TRY(prr_select_speculate(shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,
-                                 a->v_cache, a->block_table, a->pred_cur, kc, a->partials, budget, a->workspace,
-                                 s1));
+    // segments then a merge, through the workspace's candidate regions), then the spread-out repair. The workgroups
+    // that predict P_{t+1} (or rank the EMA's segments) update the EMA, which they read anyway, so the scoring pass
+    // writes the scores alone (same-box A/B over two runs: million-token layer 66.1 -> 65.3 us at K' = 384, 59.7 ->
+    // 58.2 us at K' = 128, with the update in the segment launch). Under a per-row budget the scoring pass keeps
+    // the update: the confidence rule reads the EMA beside the prediction, and the budgeted prediction roles would
+    // take more registers.
+    const bool sel_ema = kn > 0 && !budgeted;
+    PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 && !sel_ema ? a->ema : nullptr, a->alpha,
+                      a->first_step, s1));
+    PRR_TRY(launch_select_spec(*shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,
+                               a->v_cache, a->block_table, kc ? a->pred_cur : nullptr, kc,
+                               kc ? a->partials : nullptr, s1, cand_region(*shape, a->workspace, 0),
+                               cand_region(*shape, a->workspace, 1), cand_region(*shape, a->workspace, 2),
+                               kn > 0 ? budget_dev(budget) : BudgetDev{}, sel_ema, a->alpha, a->first_step ? 1 : 0));
     return prr_repair_merge(shape, a->q, a->k_cache, a->v_cache, a->block_table, a->sel_idx, a->top_k, a->pred_cur,
                             kc, a->partials, a->out, a->n_missed, a->workspace, s1);
   }

@@ -140,19 +140,15 @@ size_t repair_workspace_bytes(const prr_shape& s, int top_k);
 bool p16_path(const prr_shape& s);
 // Predicted slots per speculation wave: about four 16-token chunks per wave, while keeping >= 4096 waves in flight.
 int spec_slots_per_wave(const prr_shape& s, int k_spec);
+// The true set, the next predicted set and the speculation over pred in the fewest launches the shape allows. With
+// ema_upd (a predicted set of fixed size) the workgroups that predict, or rank the EMA's segments, update the EMA
+// from the scores first (alpha, first as for the scoring pass), so the scoring pass may write the scores alone.
 prr_status launch_select_spec(const prr_shape& s, const float* scores, int k, int32_t* sel, const float* ema,
                               int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                               const int32_t* table, const int32_t* pred, int k_spec, float* partials,
                               hipStream_t stream, void* cand_t = nullptr, void* cand_p = nullptr,
-                              void* cand_u = nullptr, const BudgetDev& bp = BudgetDev{});
-// Long rows with a fixed budget: the segment launch of the selection also updates the EMA from the scores, in its
-// EMA-segment workgroups (which read the EMA anyway), so the scoring pass writes the scores alone; then the merge
-// launch selects T and P_{t+1} from the candidates. seg_ema_on: whether this form applies (both sets split).
-bool seg_ema_on(const prr_shape& s, int k, int kp_next);
-prr_status launch_seg_spec_ema(const prr_shape& s, const float* scores, int k, int32_t* sel, float* ema, float alpha,
-                               int first, int kp_next, int32_t* pred_next, const void* q, const void* kc,
-                               const void* vc, const int32_t* table, const int32_t* pred, int k_spec, float* partials,
-                               void* cand_t, void* cand_p, hipStream_t stream);
+                              void* cand_u = nullptr, const BudgetDev& bp = BudgetDev{}, bool ema_upd = false,
+                              float alpha = 0.f, int first = 0);
 // The two-launch step: scores (+ EMA) with speculation, then selection with the row-wise repair and merge.
 bool two_launch_supported(const prr_shape& s, int top_k, int k_spec, int k_spec_next);
 prr_status launch_score_spec(const prr_shape& s, const void* q, const void* summ, float* scores, float* ema,
