@@ -24,7 +24,8 @@ sys.path.insert(0, ROOT)
 METRIC = "µs per decode step per layer (select+speculate+repair); KV GB/s vs HBM peak"
 HBM_PEAK_GBS = 8000.0
 # HIP kernels behind each traced launch
-HIP_KERNELS = {("prr_fused", "score"): "score_kernel (with the EMA update)",
+HIP_KERNELS = {("prr_fused", "score"): "score_kernel (the scores alone; the EMA is updated by the selection "
+                                       "launch, except where K <= 32 or under a per-row budget)",
                ("prr_fused", "select_topk"): "the selection launch(es) by shape: select_spec_kernel (true top-K, "
                                              "next top-K', speculation over P_t), seg_spec_kernel + merge2_kernel "
                                              "(rows of more than 8192 blocks), select_missed_kernel (K <= 32, also "
@@ -190,6 +191,9 @@ def main():
     # the fused step's many-row path (speculation in its own launch, a selection launch of top-K workgroups) serves
     # batches whose rows alone fill the chip
     many_row = rows >= 128
+    # below 128 rows with K > 32 and a fixed budget, the fused step's selection launch updates the EMA (the workgroups
+    # that predict P_{t+1}); with K <= 32 or a per-row budget the scoring pass does
+    sel_ema = not many_row and w.top_k > 32 and a.budget == "fixed"
 
     def alg_bytes(mode):
         """Algorithmic bytes per launch of each traced kernel in `mode`."""
@@ -204,8 +208,13 @@ def main():
             # scoring also updates the EMA; the selection launch reads scores and EMA, speculates over P_t and attends
             # the missed blocks; the merge launch (traced as "finalize") only reads partial records
             return {"score": summ_b + 3 * row_f32, "select_topk": 2 * row_f32 + spec + rep}
+        if mode == "prr_fused" and sel_ema:
+            # scores alone; the selection launch reads the scores for T, updates the EMA from them in the workgroups
+            # that predict P_{t+1} (scores and EMA read, EMA written) and speculates over P_t; then the repair
+            return {"score": summ_b + row_f32, "select_topk": 4 * row_f32 + spec, "repair": rep}
         if mode == "prr_fused":
-            # scoring also updates the EMA; the selection launch reads scores and EMA and speculates; then repair
+            # per-row budget: scoring also updates the EMA; the selection launch reads scores and EMA and
+            # speculates; then the repair
             return {"score": summ_b + 3 * row_f32, "select_topk": 2 * row_f32 + spec, "repair": rep}
         if mode == "serialized_fused" and rows >= 128:
             # two launches: scores, then selection with the row-wise attention and merge
@@ -311,7 +320,9 @@ def main():
             q = qs[lay.t % w.steps]
             kc = lay.k_spec if lay.t > 0 else 0
             if kernel == "score":
-                e = lay.ema.clone() if mode == "prr_fused" and not many_row else None   # as the step scores
+                # as the step scores: the EMA update rides in the scoring pass only where the selection launch
+                # does not take it
+                e = lay.ema.clone() if mode == "prr_fused" and not many_row and not sel_ema else None
                 calls.append(lambda lay=lay, q=q, e=e, par=par: L.score(
                     shape, q, lay.summaries, lay.scores[par], e, w.alpha, False, stream=streams[0]))
             elif kernel == "select_topk" and mode == "prr_fused" and "repair" in alg:   # the select_spec launch
@@ -367,7 +378,10 @@ def main():
         dom = {dominant: per_kernel[dominant]}
         dom_where = "events around each launch in an eager pass of the same steps"
     dom_us = dom.get(dominant, float("nan"))
-    achieved = alg[dominant] / (dom_us * 1e-6) / 1e9
+    dom_bytes = alg[dominant]
+    if iso is not None and a.mode == "prr_fused" and dominant == "select_topk" and sel_ema:
+        dom_bytes -= 2 * row_f32   # the selection entry point replayed alone reads the EMA without updating it
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     other = {}
     others = ("prr_fused", "prr_2stream", "prr_1stream", "serialized", "serialized_fused") \
         if a.other_modes == "all" else \
@@ -387,7 +401,7 @@ def main():
         attn_bytes = alg["select_topk"] - 2 * row_f32
     elif a.mode == "prr_fused":   # speculation in the selection launch, then the repair launch
         attn_us = per_kernel.get("select_topk", 0.0) + per_kernel.get("repair", 0.0)
-        attn_bytes = alg["select_topk"] - 2 * row_f32 + alg["repair"]
+        attn_bytes = rows * mean_pred * blk_kv + alg["repair"]
     elif a.mode == "serialized_fused" and rows >= 128:   # the repair launch also selects
         attn_us = per_kernel.get("repair", 0.0)
         attn_bytes = alg["repair"]
@@ -488,13 +502,11 @@ def main():
                    "sink_blocks": w.sink_blocks, "local_blocks": w.local_blocks, "scorer": w.scorer,
                    "budget": a.budget, "layers_rotated": n_layers, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": dominant,
-                     "hip_kernels": ("score_kernel (the EMA is updated in the selection launch)"
-                                     if (a.mode, dominant) == ("prr_fused", "score") and many_row
-                                     else HIP_KERNELS.get((a.mode, dominant), dominant)),
+                     "hip_kernels": HIP_KERNELS.get((a.mode, dominant), dominant),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": recorded_traffic(w.name, a.mode, dominant),
-                     "alg_bytes_per_launch": alg[dominant], "avg_launch_us": round(dom_us, 3)},
+                     "alg_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 3)},
         "cpu_baseline": cpu,
         "detail": detail,
     }
