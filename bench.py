@@ -12,6 +12,7 @@ Prints ONE JSON line. `python bench.py --gpus N` with N > 1 exits: the benchmark
 from __future__ import annotations
 
 import argparse
+import copy
 import json
 import math
 import os
@@ -163,10 +164,22 @@ def main():
     row_f32 = rows * w.n_blocks * 4
 
     # ---- statistics pass: overlap, missed blocks (untimed, per-step syncs) ---------------------------------------
-    stat = make_layers(a.mode)[0]
+    # The drifting workload moves its hot blocks as the workload defines it (the stored query draws keep the gap on
+    # the drifted keys): on a copy of the keys, with the summaries of the moved blocks rebuilt before each such step.
+    # The timed passes replay the steps on fixed keys; the rebuild is timed on its own (summary_rebuild_us).
+    stat_inp = inp
+    if w.drift_every:
+        stat_inp = copy.copy(inp)
+        stat_inp.k_cache, stat_inp.hot, stat_inp.saved = inp.k_cache.clone(), inp.hot.copy(), dict(inp.saved)
+    stat = PRRLayer(shape, w.top_k, kspec, w.alpha, mode=a.mode, device=dev, streams=streams,
+                    budget=budget_cfg if kspec > 0 else None)
+    stat.build(stat_inp.k_cache, inp.v_cache, inp.table)
     missed, missed_max, overlap, pred_size = [], 0, [], []
     banded, instances = 0, 0
     for i in range(min(w.steps, 32)):
+        ids = stat_inp.drift(stat.t) if w.drift_every else ()
+        if len(ids):
+            stat.rebuild_blocks(torch.as_tensor(ids, device=dev))
         stat.step(qs[stat.t % w.steps])
         stat.sync_spec()
         torch.cuda.synchronize()
