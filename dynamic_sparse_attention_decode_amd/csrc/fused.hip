@@ -11,6 +11,8 @@
 // of the EMA from the scores first), the rest speculate as the standalone speculation kernel does (256-thread
 // workgroups, several slots per wave); merge2_kernel then selects each row's T and P_{t+1} from the segments'
 // candidates (topk_dev.h).
+#include <atomic>
+
 #include "attn_wave.h"
 #include "topk_dev.h"
 
@@ -18,8 +20,28 @@ namespace prr {
 
 constexpr int kSelSpecThreads = 512;   // 8 waves: room for the speculation tile's registers
 
-template <int KPT, int DT, int G>
-__global__ __launch_bounds__(kSelSpecThreads) void select_spec_kernel(const float* __restrict__ scores, int K,
+// Compute units of the current device (queried once per device; 256 on MI355X).
+static int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cus[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+template <int NT, int KPT, int DT, int G>
+__global__ __launch_bounds__(NT) void select_spec_kernel(const float* __restrict__ scores, int K,
                                                            int32_t* __restrict__ sel, const float* __restrict__ ema,
                                                            int Kp_next, int32_t* __restrict__ pred_next, int n_sel_wg,
                                                            const uint8_t* __restrict__ q,
@@ -38,21 +60,21 @@ __global__ __launch_bounds__(kSelSpecThreads) void select_spec_kernel(const floa
     float* erow = const_cast<float*>(ema) + rr * N;
     int32_t* prow = pred_next + rr * Kp_next;
     if (r < rows) {
-      topk_row<kSelSpecThreads, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, nullptr, force);
+      topk_row<NT, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, nullptr, force);
     } else if (ema_upd) {   // fixed budget: update the row's EMA from the scores, then take its top-K'
-      topk_row<kSelSpecThreads, KPT, true>(scores + rr * N, erow, alpha, first, N, Kp_next, prow, nullptr, force);
+      topk_row<NT, KPT, true>(scores + rr * N, erow, alpha, first, N, Kp_next, prow, nullptr, force);
     } else {
       if constexpr (KPT <= 16) {   // budgeted rows are routed elsewhere beyond 8192 blocks
         if (bp.policy != 0) {
-          predict_row<kSelSpecThreads, KPT, false>(scores + rr * N, erow, 0.f, 0, N, Kp_next, bp, rr, prow, force);
+          predict_row<NT, KPT, false>(scores + rr * N, erow, 0.f, 0, N, Kp_next, bp, rr, prow, force);
           return;
         }
       }
-      topk_row<kSelSpecThreads, KPT, false>(erow, nullptr, 0.f, 0, N, Kp_next, prow, nullptr, force);
+      topk_row<NT, KPT, false>(erow, nullptr, 0.f, 0, N, Kp_next, prow, nullptr, force);
     }
     return;
   }
-  const int64_t s = (r - n_sel_wg) * (kSelSpecThreads / 64) + (threadIdx.x >> 6);
+  const int64_t s = (r - n_sel_wg) * (NT / 64) + (threadIdx.x >> 6);
   if (s < spec_total)
     speculate_slot<DT, G>(s, threadIdx.x & 63, q, kc, vc, table, pred, k_spec, partials, Hq, Hkv, N, bs, page, pps,
                           qscale, last_len);
@@ -179,27 +201,32 @@ static void select_spec_launch(const prr_shape& s, const float* scores, int K, i
   const int rows = s.batch * s.n_kv_heads;
   const int n_sel_wg = kp_next > 0 ? 2 * rows : rows;
   const int64_t spec_total = (int64_t)rows * k_spec;
-  constexpr int WPG = kSelSpecThreads / 64;
-  const int n_spec_wg = (int)((spec_total + WPG - 1) / WPG);
-  const dim3 grid((unsigned)(n_sel_wg + n_spec_wg)), blk(kSelSpecThreads);
   const auto* qq = static_cast<const uint8_t*>(q);
   const auto* kk = static_cast<const uint8_t*>(kc);
   const auto* vv = static_cast<const uint8_t*>(vc);
   const float qs = s.softmax_scale * kLog2e;
-#define PRR_SELSPEC(KPT)                                                                                           \
-  select_spec_kernel<KPT, DT, G><<<grid, blk, 0, st>>>(scores, K, sel, ema, kp_next, pred_next, n_sel_wg, qq, kk, vv, \
+#define PRR_SELSPEC(NT, KPT)                                                                                       \
+  select_spec_kernel<NT, KPT, DT, G><<<dim3((unsigned)(n_sel_wg + (spec_total + NT / 64 - 1) / (NT / 64))), NT, 0,  \
+                                       st>>>(scores, K, sel, ema, kp_next, pred_next, n_sel_wg, qq, kk, vv,           \
                                                        table, pred, k_spec, partials, spec_total, s.n_q_heads,       \
                                                        s.n_kv_heads, s.n_blocks, s.block_size, s.page_size,          \
                                                        s.pages_per_seq, qs, rows, last_block_len(s),            \
                                                        s.sink_blocks, s.local_blocks, bp, ema_upd ? 1 : 0, alpha,    \
                                                        first)
+  // Rows of up to 2048 blocks whose launch of 512-thread workgroups (one per CU at these register counts) would not
+  // be resident at once take 256-thread workgroups (three per CU), so that every speculation wave starts in the
+  // first round (131K batch, same-box A/B over two runs: PRR step 49.5 -> 45.7 us); where the 512-thread launch fits,
+  // it stays, since its top-K workgroups are faster (32K layer: 20.8 against 21.1 us with 256 threads).
+  const int64_t wg512 = n_sel_wg + (spec_total + kSelSpecThreads / 64 - 1) / (kSelSpecThreads / 64);
   // values per thread: a few register sizes cover every row length (larger than needed is correct, just slower)
-  if (s.n_blocks <= 4 * kSelSpecThreads)
-    PRR_SELSPEC(4);
+  if (s.n_blocks <= 2048 && wg512 > device_cus())
+    PRR_SELSPEC(256, 8);
+  else if (s.n_blocks <= 4 * kSelSpecThreads)
+    PRR_SELSPEC(kSelSpecThreads, 4);
   else if (s.n_blocks <= 16 * kSelSpecThreads)
-    PRR_SELSPEC(16);
+    PRR_SELSPEC(kSelSpecThreads, 16);
   else
-    PRR_SELSPEC(64);
+    PRR_SELSPEC(kSelSpecThreads, 64);
 #undef PRR_SELSPEC
 }
 
