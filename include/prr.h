@@ -236,18 +236,16 @@ typedef enum {
   PRR_MODE_TWO_STREAM = 2,  /* stream_spec: speculate || stream_sel: score_select; after the join, repair_merge
                                -> ema_predict on stream_sel (one fork and one join per step)                    */
   PRR_MODE_FUSED = 3,       /* stream_sel only. batch * n_kv_heads >= 128: speculate -> score -> one launch of
-                               top-K workgroups selecting T and P_{t+1}, the latter updating the EMA first (up
-                               to 8192 blocks; beyond, the scoring pass updates it and the selection runs by
-                               segments) -> repair_merge (the hits' records merged, the missed blocks
-                               attended). Otherwise, top_k <= 32:
+                               top-K workgroups selecting T and P_{t+1}, the latter updating the EMA first
+                               (rows of more than 8192 blocks by segments and a merge) -> repair_merge (the
+                               hits' records merged, the missed blocks attended). Otherwise, top_k <= 32:
                                score (+ EMA update) -> one launch selecting T and P_{t+1}, speculating over P_t
-                               and attending T minus P_t per row -> merge. Otherwise: score (+ EMA update) ->
-                               select_speculate (T, P_{t+1}, speculation over P_t; rows of more than 8192
-                               blocks by segments and a merge, where with a fixed budget the segments of the
-                               EMA are updated by the segment launch instead of the scoring pass) ->
-                               repair_merge, which with nothing to
-                               speculate or predict are the serialized launches. The shapes each form supports
-                               are the conditions of the separate calls; outside them the next form is taken.  */
+                               and attending T minus P_t per row -> merge. Otherwise: score -> select_speculate
+                               (T, P_{t+1} after the EMA update, speculation over P_t; rows of more than 8192
+                               blocks by segments and a merge) -> repair_merge, which with nothing to
+                               speculate or predict are the serialized launches. Under a per-row budget the
+                               scoring pass updates the EMA in every form. The shapes each form supports are
+                               the conditions of the separate calls; outside them the next form is taken.      */
   PRR_MODE_SERIALIZED_FUSED = 4  /* stream_sel only: score -> select_repair with no prediction (select-then-attend
                                     in two launches) when select_repair supports the shape and batch * n_kv_heads
                                     >= 128; otherwise as PRR_MODE_SERIALIZED                                    */
