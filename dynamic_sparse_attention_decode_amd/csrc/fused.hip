@@ -55,13 +55,15 @@ __global__ __launch_bounds__(NT) void select_spec_kernel(const float* __restrict
                                                            BudgetDev bp, int ema_upd, float alpha, int first) {
   const int64_t r = blockIdx.x;
   if (r < n_sel_wg) {
-    const int64_t rr = r - rows;
     const Force force{0, N, sink, local};
-    float* erow = const_cast<float*>(ema) + rr * N;
-    int32_t* prow = pred_next + rr * Kp_next;
     if (r < rows) {
       topk_row<NT, KPT, false>(scores + r * N, nullptr, 0.f, 0, N, K, sel + r * K, nullptr, force);
-    } else if (ema_upd) {   // fixed budget: update the row's EMA from the scores, then take its top-K'
+      return;
+    }
+    const int64_t rr = r - rows;   // the next predicted set of row rr
+    float* erow = const_cast<float*>(ema) + rr * N;
+    int32_t* prow = pred_next + rr * Kp_next;
+    if (ema_upd) {   // fixed budget: update the row's EMA from the scores, then take its top-K'
       topk_row<NT, KPT, true>(scores + rr * N, erow, alpha, first, N, Kp_next, prow, nullptr, force);
     } else {
       if constexpr (KPT <= 16) {   // budgeted rows are routed elsewhere beyond 8192 blocks

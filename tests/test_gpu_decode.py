@@ -127,6 +127,23 @@ def test_decode_many_rows_vs_oracle(k_spec, extra):
     run_layer(w, inp, k_spec, "prr_fused", ov=OracleView(inp))
 
 
+def test_decode_wide_selection_launch_vs_oracle():
+    """32 rows of 64-token blocks (drifting hot blocks) with K' = 80: the fused step's selection launch holds 64 top-K
+    workgroups and 2560 speculation waves, more than one 512-thread workgroup per CU can hold at once, so it runs as
+    256-thread workgroups, and each block's four chunks share one page lookup; every step against the oracle, and the
+    EMA, the selected and predicted sets and the missed counts bitwise equal to the one-stream step."""
+    w = small("long_ctx_131k_b4").replace(batch=4, top_k=20, k_spec=(80,), steps=6)
+    print(f"[case] decode wide selection launch B={w.batch} N={w.n_blocks} K={w.top_k} K'=80", flush=True)
+    inp = gap_inputs(w)
+    got = run_layer(w, inp, 80, "prr_fused", ov=OracleView(inp))
+    ref = run_layer(w, gap_inputs(w), 80, "prr_1stream", check=False)
+    for t, (a, b) in enumerate(zip(ref, got)):
+        assert np.array_equal(a["ema"], b["ema"]), t
+        assert np.array_equal(a["sel"], b["sel"]) and np.array_equal(a["nm"], b["nm"]), t
+        if a["pred"] is not None:
+            assert np.array_equal(a["pred"], b["pred"]), t
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_32k", "paged_b32_64k", "tiny_f32_4k", "million_token"])
 def test_modes_agree(name):
     """Two-stream and one-stream runs are bitwise identical (same kernels, same order). The two-launch fused run
