@@ -26,7 +26,7 @@ METRIC = "µs per decode step per layer (select+speculate+repair); KV GB/s vs HB
 HBM_PEAK_GBS = 8000.0
 # HIP kernels behind each traced launch
 HIP_KERNELS = {("prr_fused", "score"): "score_kernel (the scores alone; the EMA is updated by the selection "
-                                       "launch, except where K <= 32 or under a per-row budget)",
+                                       "launch, except under a per-row budget below 128 rows)",
                ("prr_fused", "select_topk"): "the selection launch(es) by shape: select_spec_kernel (true top-K, "
                                              "next top-K', speculation over P_t), seg_spec_kernel + merge2_kernel "
                                              "(rows of more than 8192 blocks), select_missed_kernel (K <= 32, also "
@@ -204,9 +204,9 @@ def main():
     # the fused step's many-row path (speculation in its own launch, a selection launch of top-K workgroups) serves
     # batches whose rows alone fill the chip
     many_row = rows >= 128
-    # below 128 rows with K > 32 and a fixed budget, the fused step's selection launch updates the EMA (the workgroups
-    # that predict P_{t+1}); with K <= 32 or a per-row budget the scoring pass does
-    sel_ema = not many_row and w.top_k > 32 and a.budget == "fixed"
+    # below 128 rows with a fixed budget, the fused step's selection launch updates the EMA (the workgroups that
+    # predict P_{t+1}); under a per-row budget the scoring pass does
+    sel_ema = not many_row and a.budget == "fixed"
 
     def alg_bytes(mode):
         """Algorithmic bytes per launch of each traced kernel in `mode`."""
@@ -218,8 +218,11 @@ def main():
             # as "finalize")
             return {"speculate": spec, "score": summ_b + row_f32, "select_topk": 4 * row_f32, "repair": rep}
         if mode == "prr_fused" and w.top_k <= 32:
-            # scoring also updates the EMA; the selection launch reads scores and EMA, speculates over P_t and attends
-            # the missed blocks; the merge launch (traced as "finalize") only reads partial records
+            # the selection launch reads the scores (and the EMA, which its prediction workgroups update from them
+            # under a fixed budget, else the scoring pass does), speculates over P_t and attends the missed blocks;
+            # the merge launch (traced as "finalize") only reads partial records
+            if sel_ema:
+                return {"score": summ_b + row_f32, "select_topk": 4 * row_f32 + spec + rep}
             return {"score": summ_b + 3 * row_f32, "select_topk": 2 * row_f32 + spec + rep}
         if mode == "prr_fused" and sel_ema:
             # scores alone; the selection launch reads the scores for T, updates the EMA from them in the workgroups
@@ -333,8 +336,7 @@ def main():
             q = qs[lay.t % w.steps]
             kc = lay.k_spec if lay.t > 0 else 0
             if kernel == "score":
-                # as the step scores: the EMA update rides in the scoring pass only where the selection launch
-                # does not take it
+                # as the step scores: the EMA update rides in the scoring pass only under a per-row budget
                 e = lay.ema.clone() if mode == "prr_fused" and not many_row and not sel_ema else None
                 calls.append(lambda lay=lay, q=q, e=e, par=par: L.score(
                     shape, q, lay.summaries, lay.scores[par], e, w.alpha, False, stream=streams[0]))
@@ -411,7 +413,7 @@ def main():
         attn_bytes = alg["speculate"] + alg["repair"]
     elif a.mode == "prr_fused" and "repair" not in alg:   # speculation and missed blocks in the selection launch
         attn_us = per_kernel.get("select_topk", 0.0) + per_kernel.get("finalize", 0.0)
-        attn_bytes = alg["select_topk"] - 2 * row_f32
+        attn_bytes = rows * mean_pred * blk_kv + rows * mean_missed * blk_kv
     elif a.mode == "prr_fused":   # speculation in the selection launch, then the repair launch
         attn_us = per_kernel.get("select_topk", 0.0) + per_kernel.get("repair", 0.0)
         attn_bytes = rows * mean_pred * blk_kv + alg["repair"]

@@ -584,14 +584,18 @@ static prr_status decode_step_impl(prr_step_ctx* ctx, const prr_shape* shape, co
   // (with nothing predicted or to predict the fused step runs the serialized launches, below)
   if (mode == PRR_MODE_FUSED && (kc > 0 || kn > 0) && two_launch_supported(*shape, a->top_k, kc, kn) &&
       a->top_k <= 32 && rows < 128 && !(budgeted && shape->n_blocks > 8192)) {
-    // short true sets: scores + EMA; then selection of T and P_{t+1}, speculation over P_t and the few missed blocks
-    // T \ P_t in one launch (one workgroup per row attends its row's missed blocks right after its selection); then
-    // the merge of the missed-block record with the speculated records of T ∩ P_t
-    PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 ? a->ema : nullptr, a->alpha, a->first_step, s1));
+    // short true sets: scores; then selection of T and of P_{t+1} (whose workgroups update the EMA first, under a
+    // fixed budget), speculation over P_t and the few missed blocks T \ P_t in one launch (one workgroup per row
+    // attends its row's missed blocks right after its selection); then the merge of the missed-block record with the
+    // speculated records of T ∩ P_t
+    const bool sel_ema = kn > 0 && !budgeted;
+    PRR_TRY(prr_score(shape, a->q, a->summaries, a->scores, kn > 0 && !sel_ema ? a->ema : nullptr, a->alpha,
+                      a->first_step, s1));
     return launch_select_missed(*shape, a->scores, a->top_k, a->sel_idx, a->ema, kn, a->pred_next, a->q, a->k_cache,
                                 a->v_cache, a->block_table, kc ? a->pred_cur : nullptr, kc,
                                 kc ? a->partials : nullptr, true, a->out, a->n_missed,
-                                repair_ws(*shape, a->workspace), s1, budget_dev(budget));
+                                repair_ws(*shape, a->workspace), s1, budget_dev(budget), sel_ema, a->alpha,
+                                a->first_step ? 1 : 0);
   }
   if (mode == PRR_MODE_FUSED && rows >= 128) {
     // When the rows alone fill the chip every phase is bound by bandwidth. The speculation over P_t takes its own

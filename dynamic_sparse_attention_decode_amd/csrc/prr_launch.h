@@ -160,7 +160,8 @@ prr_status launch_select_missed(const prr_shape& s, const float* scores, int k, 
                                 int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                                 const int32_t* table, const int32_t* pred, int k_spec, float* partials,
                                 bool speculate, float* out, int32_t* n_missed, void* workspace, hipStream_t stream,
-                                const BudgetDev& bp = BudgetDev{});
+                                const BudgetDev& bp = BudgetDev{}, bool ema_upd = false, float alpha = 0.f,
+                                int first = 0);
 size_t select_missed_ws_bytes(const prr_shape& s, int top_k);
 prr_status launch_flush(void* buf, size_t bytes, hipStream_t stream);
 prr_status launch_stream_read(const void* buf, size_t bytes, float* sink, hipStream_t stream);

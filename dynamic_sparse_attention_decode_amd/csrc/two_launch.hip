@@ -72,7 +72,8 @@ __host__ __device__ inline size_t missed_ws_layout(int64_t rows, int K, int RF, 
 
 // Workgroup r < rows: true top-K of row r, then (same workgroup) the blocks of T missing from P_t are attended from
 // the KV cache by the 8 waves and merged into one partial record of the row; the hits' slots go to the workspace for
-// the merge launch. Workgroups [rows, rows + n_pwg): next predicted set (top-K' of the updated EMA). The rest:
+// the merge launch. Workgroups [rows, rows + n_pwg): next predicted set (top-K' of the EMA, which with ema_upd they
+// update from the scores first). The rest:
 // speculation over P_t (one wave per slot) when spec_total > 0.
 template <int KPT, int DT, int G>
 __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
     const uint8_t* __restrict__ vc, const int32_t* __restrict__ table, const int32_t* __restrict__ pred, int k_spec,
     float* __restrict__ partials, int64_t spec_total, MissedWs ws, int32_t* __restrict__ n_missed, int Hq, int Hkv,
     int N, int bs, int page, int pps, float qscale, int rows, int n_pwg, int last_len, int sink, int local,
-    BudgetDev bp) {
+    BudgetDev bp, int ema_upd, float alpha, int first) {
   using W = Tile<DT, G>;
   constexpr int NW = kSRThreads / 64;
   constexpr int D = W::D;
@@ -106,6 +107,11 @@ __global__ __launch_bounds__(kSRThreads) void select_missed_kernel(
   }
   if (r >= rows) {   // next step's predicted set
     const int64_t rr = r - rows;
+    if (ema_upd) {   // fixed budget: update the row's EMA from the scores, then take its top-K'
+      topk_row<kSRThreads, KPT, true>(scores + rr * N, const_cast<float*>(ema) + rr * N, alpha, first, N, Kp_next,
+                                      pred_next + rr * Kp_next, nullptr, Force{0, N, sink, local});
+      return;
+    }
     if constexpr (KPT <= 16) {   // budgeted rows are routed elsewhere beyond 8192 blocks
       if (bp.policy != 0) {
         predict_row<kSRThreads, KPT, false>(scores + rr * N, const_cast<float*>(ema) + rr * N, 0.f, 0, N, Kp_next,
@@ -374,7 +380,7 @@ static void select_missed_launch(const prr_shape& s, const float* scores, int K,
                                  int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                                  const int32_t* table, const int32_t* pred, int k_spec, float* partials,
                                  bool speculate, float* out, int32_t* n_missed, void* workspace, const BudgetDev& bp,
-                                 hipStream_t st) {
+                                 hipStream_t st, bool ema_upd, float alpha, int first) {
   constexpr int D = 16 * Vec<DT>::n;
   const int rows = s.batch * s.n_kv_heads;
   MissedWs ws;
@@ -393,7 +399,8 @@ static void select_missed_launch(const prr_shape& s, const float* scores, int K,
                                                          table, pred, k_spec, partials, spec_total, ws, n_missed,   \
                                                          s.n_q_heads, s.n_kv_heads, s.n_blocks, s.block_size,       \
                                                          s.page_size, s.pages_per_seq, qs, rows, n_pwg,             \
-                                                         last_block_len(s), s.sink_blocks, s.local_blocks, bp)
+                                                         last_block_len(s), s.sink_blocks, s.local_blocks, bp,      \
+                                                         ema_upd ? 1 : 0, alpha, first)
   trace_begin(PRR_KERNEL_SELECT_TOPK, st);
   if (s.n_blocks <= 4 * kSRThreads)
     PRR_SELMISS(4);
@@ -413,9 +420,13 @@ prr_status launch_select_missed(const prr_shape& s, const float* scores, int k, 
                                 int kp_next, int32_t* pred_next, const void* q, const void* kc, const void* vc,
                                 const int32_t* table, const int32_t* pred, int k_spec, float* partials,
                                 bool speculate, float* out, int32_t* n_missed, void* workspace, hipStream_t stream,
-                                const BudgetDev& bp) {
+                                const BudgetDev& bp, bool ema_upd, float alpha, int first) {
+  if (ema_upd && (kp_next == 0 || !ema || bp.policy != 0)) {
+    set_error("select_repair: the EMA update in the selection launch needs a predicted set of fixed size");
+    return PRR_EINVAL;
+  }
   PRR_DISPATCH_DT_G(select_missed_launch, s, scores, k, sel, ema, kp_next, pred_next, q, kc, vc, table, pred, k_spec,
-                    partials, speculate, out, n_missed, workspace, bp, stream);
+                    partials, speculate, out, n_missed, workspace, bp, stream, ema_upd, alpha, first);
   return check_launch("select_repair");
 }
 

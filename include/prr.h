@@ -239,12 +239,12 @@ typedef enum {
                                top-K workgroups selecting T and P_{t+1}, the latter updating the EMA first
                                (rows of more than 8192 blocks by segments and a merge) -> repair_merge (the
                                hits' records merged, the missed blocks attended). Otherwise, top_k <= 32:
-                               score (+ EMA update) -> one launch selecting T and P_{t+1}, speculating over P_t
-                               and attending T minus P_t per row -> merge. Otherwise: score -> select_speculate
-                               (T, P_{t+1} after the EMA update, speculation over P_t; rows of more than 8192
-                               blocks by segments and a merge) -> repair_merge, which with nothing to
-                               speculate or predict are the serialized launches. Under a per-row budget the
-                               scoring pass updates the EMA in every form. The shapes each form supports are
+                               score -> one launch selecting T and P_{t+1} (after the EMA update), speculating
+                               over P_t and attending T minus P_t per row -> merge. Otherwise: score ->
+                               select_speculate (T, P_{t+1} after the EMA update, speculation over P_t; rows of
+                               more than 8192 blocks by segments and a merge) -> repair_merge, which with nothing
+                               to speculate or predict are the serialized launches. Under a per-row budget below
+                               128 rows the scoring pass updates the EMA. The shapes each form supports are
                                the conditions of the separate calls; outside them the next form is taken.      */
   PRR_MODE_SERIALIZED_FUSED = 4  /* stream_sel only: score -> select_repair with no prediction (select-then-attend
                                     in two launches) when select_repair supports the shape and batch * n_kv_heads
