@@ -94,8 +94,10 @@ __device__ void finalize_head(const float* __restrict__ recs, int n_rec, int h, 
   }
 }
 
+// Two workgroups per CU from G = 4 up: three (168 VGPRs) spilled a register at G = 4 (same-box A/B over two runs:
+// 32K layer PRR step 20.80 -> 20.41 us, serialized 19.95 -> 19.64 us; 131K batch 45.9 -> 45.1 and 33.7 -> 33.5 us).
 template <int DT, int G, bool P16>
-__global__ __launch_bounds__(256, G >= 8 ? 2 : 3) void repair_kernel(const uint8_t* __restrict__ q,
+__global__ __launch_bounds__(256, G >= 4 ? 2 : 3) void repair_kernel(const uint8_t* __restrict__ q,
                                                      const uint8_t* __restrict__ kc,
                                                      const uint8_t* __restrict__ vc,
                                                      const int32_t* __restrict__ table,
